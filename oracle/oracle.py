@@ -1,0 +1,279 @@
+"""ctypes binding of the C oracle (oracle.c) and the bundle pipeline built from it.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product library.  It shares no code
+with the product (decode_gemv_amd) and never imports it.
+
+The functions below chain the oracle's C steps in the order the method runs
+them ("LazyWeights", section "2 . Code them" for the bundle, section "3 . Decode
+on demand" for the decoder; "Unweight", exponent palette and verbatim rows for
+bf16), using numpy only to hold arrays.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+Q4, Q6, BF16 = 1, 2, 3
+KIND = {"q4": Q4, "q6": Q6, "bf16": BF16}
+MAXLEN = 11
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc into oracle/liboracle.so."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-shared", "-fPIC",
+                               "-o", tmp, SRC, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = C.CDLL(LIB)
+        P = C.c_void_p
+        i64, i32 = C.c_int64, C.c_int
+        sig = {
+            "or_symbols_per_lane": (i32, [i32]),
+            "or_alphabet": (i32, [i32]),
+            "or_symbolise_q": (None, [i32, i64, i64, P, P]),
+            "or_unsymbolise_q": (None, [i32, i64, i64, P, P]),
+            "or_histogram": (None, [P, i64, i32, P]),
+            "or_package_merge": (i32, [i32, P, i32, P]),
+            "or_canonical": (i32, [i32, P, P, P, P, P, P, P]),
+            "or_encode_tiles": (i64, [i64, i32, P, P, P, P, P, P]),
+            "or_decode_limit": (i32, [i64, i32, P, P, P, P, P, P, P, P, P]),
+            "or_decode_bitwise": (i32, [i64, i32, P, P, i32, P, P, P]),
+            "or_half_to_double": (C.c_double, [C.c_uint16]),
+            "or_bf16_to_double": (C.c_double, [C.c_uint16]),
+            "or_pack_dm": (None, [i64, i64, P, P, P]),
+            "or_gemv_q": (None, [i64, i64, P, P, P, P, i32, P, i64, P]),
+            "or_gemv_bf16": (None, [i64, i64, P, P, i32, P, i64, P]),
+            "or_bf16_palette": (i32, [i64, P, P]),
+            "or_bf16_verbatim": (i64, [i64, i64, P, P, i32, P, P, P]),
+            "or_bf16_symbolise": (None, [i64, i64, P, P, i32, P, P]),
+            "or_bf16_pack_sm": (None, [i64, i64, P, P]),
+            "or_bf16_reconstruct": (None, [i64, i64, P, P, P, P, P, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(C.c_void_p)
+
+
+# ---------------------------------------------------------------- steps
+
+def symbols_per_lane(kind: int) -> int:
+    return lib().or_symbols_per_lane(kind)
+
+
+def alphabet(kind: int) -> int:
+    return lib().or_alphabet(kind)
+
+
+def symbolise_q(kind: int, codes: np.ndarray) -> np.ndarray:
+    R, Cc = codes.shape
+    nt = (R // 64) * (Cc // 256)
+    syms = np.empty(nt * 32 * symbols_per_lane(kind), dtype=np.uint16)
+    lib().or_symbolise_q(kind, R, Cc, _p(np.ascontiguousarray(codes, np.uint8)), _p(syms))
+    return syms
+
+
+def unsymbolise_q(kind: int, rows: int, cols: int, syms: np.ndarray) -> np.ndarray:
+    q = np.empty((rows, cols), dtype=np.uint8)
+    lib().or_unsymbolise_q(kind, rows, cols, _p(syms), _p(q))
+    return q
+
+
+def histogram(syms: np.ndarray, n_alpha: int) -> np.ndarray:
+    counts = np.zeros(n_alpha, dtype=np.uint64)
+    lib().or_histogram(_p(syms), syms.size, n_alpha, _p(counts))
+    return counts
+
+
+def package_merge(counts, limit: int = MAXLEN) -> np.ndarray:
+    counts = np.ascontiguousarray(counts, dtype=np.uint64)
+    lens = np.zeros(counts.size, dtype=np.uint8)
+    rc = lib().or_package_merge(counts.size, _p(counts), limit, _p(lens))
+    if rc != 0:
+        raise ValueError("alphabet does not fit the length limit")
+    return lens
+
+
+def canonical(lens: np.ndarray) -> dict:
+    lens = np.ascontiguousarray(lens, dtype=np.uint8)
+    n = lens.size
+    codes = np.zeros(n, dtype=np.uint16)
+    arr = {k: np.zeros(MAXLEN + 1, dtype=np.uint16) for k in ("count", "first", "limit", "offset")}
+    sym_sorted = np.zeros(max(n, 1), dtype=np.uint16)
+    k = lib().or_canonical(n, _p(lens), _p(codes), _p(arr["count"]), _p(arr["first"]),
+                           _p(arr["limit"]), _p(arr["offset"]), _p(sym_sorted))
+    if k < 0:
+        raise ValueError("code length above 11")
+    arr.update(codes=codes, lens=lens, sym_sorted=sym_sorted[:k].copy(), n_sym=k)
+    return arr
+
+
+def encode_tiles(syms: np.ndarray, spl: int, lens: np.ndarray, codes: np.ndarray):
+    """-> (tile_off uint32 [T+1], words uint32, lane_bits uint32 [T*32])."""
+    nt = syms.size // (32 * spl)
+    tile_off = np.zeros(nt + 1, dtype=np.uint32)
+    lane_bits = np.zeros(nt * 32, dtype=np.uint32)
+    total = lib().or_encode_tiles(nt, spl, _p(syms), _p(lens), _p(codes), _p(tile_off), None,
+                                  _p(lane_bits))
+    words = np.zeros(max(total, 1), dtype=np.uint32)
+    lib().or_encode_tiles(nt, spl, _p(syms), _p(lens), _p(codes), _p(tile_off), _p(words),
+                          _p(lane_bits))
+    return tile_off, words[:total], lane_bits
+
+
+def decode_limit(tab: dict, tile_off, words, spl: int):
+    """-> (syms, lane_bits) by the limit method."""
+    nt = tile_off.size - 1
+    out = np.zeros(nt * 32 * spl, dtype=np.uint16)
+    bits = np.zeros(nt * 32, dtype=np.uint32)
+    w = words if words.size else np.zeros(1, np.uint32)
+    rc = lib().or_decode_limit(nt, spl, _p(tile_off), _p(w), _p(tab["count"]), _p(tab["first"]),
+                               _p(tab["limit"]), _p(tab["offset"]), _p(tab["sym_sorted"]),
+                               _p(out), _p(bits))
+    if rc != 0:
+        raise ValueError("peek matched no code length")
+    return out, bits
+
+
+def decode_bitwise(tab: dict, tile_off, words, spl: int):
+    nt = tile_off.size - 1
+    out = np.zeros(nt * 32 * spl, dtype=np.uint16)
+    w = words if words.size else np.zeros(1, np.uint32)
+    rc = lib().or_decode_bitwise(nt, spl, _p(tile_off), _p(w), tab["lens"].size,
+                                 _p(tab["lens"]), _p(tab["codes"]), _p(out))
+    if rc != 0:
+        raise ValueError("bitwise decode ran past 11 bits")
+    return out
+
+
+def pack_dm(d: np.ndarray, m: np.ndarray) -> np.ndarray:
+    R, ncb = d.shape
+    dm = np.zeros(R * ncb, dtype=np.uint32)
+    lib().or_pack_dm(R, ncb * 256, _p(np.ascontiguousarray(d, np.uint16)),
+                     _p(np.ascontiguousarray(m, np.uint16)), _p(dm))
+    return dm
+
+
+def gemv_q(codes, d, m, x, batch: int, rows=None) -> np.ndarray:
+    """fp64 y [batch][len(rows) or R] from codes, fp16 d/m and fp16 x bits."""
+    R, Cc = codes.shape
+    x = np.ascontiguousarray(x[:batch], dtype=np.uint16)
+    rl = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nr = R if rl is None else rl.size
+    y = np.zeros((batch, nr), dtype=np.float64)
+    lib().or_gemv_q(R, Cc, _p(np.ascontiguousarray(codes, np.uint8)),
+                    _p(np.ascontiguousarray(d, np.uint16)), _p(np.ascontiguousarray(m, np.uint16)),
+                    _p(x), batch, _p(rl), nr, _p(y))
+    return y
+
+
+def gemv_bf16(w, x, batch: int, rows=None) -> np.ndarray:
+    R, Cc = w.shape
+    x = np.ascontiguousarray(x[:batch], dtype=np.uint16)
+    rl = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nr = R if rl is None else rl.size
+    y = np.zeros((batch, nr), dtype=np.float64)
+    lib().or_gemv_bf16(R, Cc, _p(np.ascontiguousarray(w, np.uint16)), _p(x), batch, _p(rl), nr,
+                       _p(y))
+    return y
+
+
+def half_to_double(h: int) -> float:
+    return lib().or_half_to_double(h)
+
+
+def bf16_to_double(b: int) -> float:
+    return lib().or_bf16_to_double(b)
+
+
+# ---------------------------------------------------------------- bundles
+
+def build_bundle_q(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray) -> dict:
+    """Quantised bundle: per-matrix table, tile offsets, interleaved words, dm."""
+    R, Cc = codes.shape
+    if R % 64 or Cc % 256:
+        raise ValueError("shape must be a multiple of 64x256")
+    spl = symbols_per_lane(kind)
+    syms = symbolise_q(kind, codes)
+    counts = histogram(syms, alphabet(kind))
+    lens = package_merge(counts)
+    tab = canonical(lens)
+    tile_off, words, lane_bits = encode_tiles(syms, spl, lens, tab["codes"])
+    return dict(kind=kind, rows=R, cols=Cc, spl=spl, counts=counts, table=tab,
+                tile_off=tile_off, words=words, lane_bits=lane_bits, dm=pack_dm(d, m))
+
+
+def decode_bundle_q(b: dict, bitwise: bool = False):
+    """-> (codes [R][C], lane_bits or None)."""
+    if bitwise:
+        syms, bits = decode_bitwise(b["table"], b["tile_off"], b["words"], b["spl"]), None
+    else:
+        syms, bits = decode_limit(b["table"], b["tile_off"], b["words"], b["spl"])
+    return unsymbolise_q(b["kind"], b["rows"], b["cols"], syms), bits
+
+
+def build_bundle_bf16(w: np.ndarray) -> dict:
+    R, Cc = w.shape
+    if R % 64 or Cc % 256:
+        raise ValueError("shape must be a multiple of 64x256")
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    L = lib()
+    palette = np.zeros(16, dtype=np.uint8)
+    n_pal = L.or_bf16_palette(w.size, _p(w), _p(palette))
+    nt = (R // 64) * (Cc // 256)
+    vb_bits = np.zeros(nt * 8, dtype=np.uint32)
+    vb_start = np.zeros(nt + 1, dtype=np.uint32)
+    nv = L.or_bf16_verbatim(R, Cc, _p(w), _p(palette), n_pal, _p(vb_bits), _p(vb_start), None)
+    verbatim = np.zeros(max(nv, 1) * 64, dtype=np.uint16)
+    L.or_bf16_verbatim(R, Cc, _p(w), _p(palette), n_pal, _p(vb_bits), _p(vb_start), _p(verbatim))
+    syms = np.zeros(nt * 32 * 512, dtype=np.uint16)
+    L.or_bf16_symbolise(R, Cc, _p(w), _p(palette), n_pal, _p(vb_bits), _p(syms))
+    counts = histogram(syms, 16)
+    lens = package_merge(counts)
+    tab = canonical(lens)
+    tile_off, words, lane_bits = encode_tiles(syms, 512, lens, tab["codes"])
+    sm = np.zeros(nt * 4096, dtype=np.uint32)
+    L.or_bf16_pack_sm(R, Cc, _p(w), _p(sm))
+    return dict(kind=BF16, rows=R, cols=Cc, spl=512, counts=counts, table=tab, palette=palette,
+                n_pal=n_pal, vb_bits=vb_bits, vb_start=vb_start, verbatim=verbatim[:nv * 64],
+                n_verbatim=nv, tile_off=tile_off, words=words, lane_bits=lane_bits, sm=sm)
+
+
+def decode_bundle_bf16(b: dict, bitwise: bool = False):
+    if bitwise:
+        syms, bits = decode_bitwise(b["table"], b["tile_off"], b["words"], 512), None
+    else:
+        syms, bits = decode_limit(b["table"], b["tile_off"], b["words"], 512)
+    R, Cc = b["rows"], b["cols"]
+    out = np.zeros((R, Cc), dtype=np.uint16)
+    verb = b["verbatim"] if b["verbatim"].size else np.zeros(64, np.uint16)
+    lib().or_bf16_reconstruct(R, Cc, _p(syms), _p(b["sm"]), _p(b["palette"]), _p(b["vb_bits"]),
+                              _p(b["vb_start"]), _p(verb), _p(out))
+    return out, bits

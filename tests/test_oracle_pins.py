@@ -1,0 +1,366 @@
+"""Pins of the CPU oracle against facts fixed by the pages or by mathematics.
+
+None of these tests restates the oracle's own code: each checks it against an
+independent definition (Kraft's equality, exhaustive search for optimal
+lengths, the dyadic closed form, a textbook heap Huffman, brute-force bit
+strings, numpy's fp16 conversion, a dense numpy matvec, closed-form special
+cases, a hand-worked example) so that a dropped term, a wrong index or a
+transposed operand anywhere in the oracle fails one of them.
+"""
+import heapq
+import itertools
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def kraft_sum(lens, L=11):
+    return int(sum(1 << (L - int(x)) for x in lens if x))
+
+
+def heap_huffman_cost(counts):
+    """Textbook Huffman (repeatedly merge the two lightest): total cost."""
+    h = [int(c) for c in counts if c > 0]
+    if len(h) == 1:
+        return h[0]
+    heapq.heapify(h)
+    cost = 0
+    while len(h) > 1:
+        a = heapq.heappop(h)
+        b = heapq.heappop(h)
+        cost += a + b
+        heapq.heappush(h, a + b)
+    return cost
+
+
+def heap_huffman_maxlen(counts):
+    h = [(int(c), 0, i) for i, c in enumerate(counts) if c > 0]
+    heapq.heapify(h)
+    uid = len(counts)
+    depth = {}
+    while len(h) > 1:
+        a = heapq.heappop(h)
+        b = heapq.heappop(h)
+        d = max(a[1], b[1]) + 1
+        heapq.heappush(h, (a[0] + b[0], d, uid))
+        uid += 1
+    return h[0][1]
+
+
+def brute_force_opt(counts, L):
+    """Minimum sum(count*len) over all length vectors with Kraft <= 1, max <= L.
+
+    With counts sorted descending an optimal vector is non-decreasing (swapping
+    two lengths onto the heavier symbol never costs more), so the search runs
+    over non-decreasing vectors only, which still contains an optimum."""
+    used = sorted((int(c) for c in counts if c > 0), reverse=True)
+    best = None
+    for lens in itertools.combinations_with_replacement(range(1, L + 1), len(used)):
+        if sum(1 << (L - l) for l in lens) <= (1 << L):
+            cost = sum(c * l for c, l in zip(used, lens))
+            best = cost if best is None else min(best, cost)
+    return best
+
+
+# ------------------------------------------------------------------ lengths
+
+def test_golden_hand_worked_table():
+    rows = {}
+    for line in open(os.path.join(GOLDEN, "canonical_small.txt")):
+        if line.strip() and not line.startswith("#"):
+            k, *v = line.split()
+            rows[k] = [int(t) for t in v]
+    lens = O.package_merge(np.array(rows["counts"], np.uint64))
+    assert lens.tolist() == rows["lens"]
+    tab = O.canonical(lens)
+    assert tab["codes"].tolist() == rows["codes"]
+    for k in ("count", "first", "limit", "offset"):
+        assert tab[k].tolist() == rows[k], k
+    assert tab["sym_sorted"].tolist() == rows["sym_sorted"]
+    assert O.package_merge(np.array(rows["tie_counts"], np.uint64)).tolist() == rows["tie_lens"]
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_package_merge_is_optimal_small(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(2, 8))
+    counts = rng.integers(1, 60, size=n).astype(np.uint64)
+    if seed % 3 == 0:
+        counts = np.array(sorted(counts)[::-1], np.uint64) ** 2  # skewed
+    for L in (3, 4, 11):
+        if (1 << L) < n:
+            continue
+        lens = O.package_merge(counts, L)
+        assert max(lens) <= L
+        assert sum(2.0 ** -int(l) for l in lens) <= 1.0
+        assert int(np.dot(counts, lens.astype(np.uint64))) == brute_force_opt(counts.tolist(), L)
+
+
+def test_dyadic_closed_form():
+    # counts proportional to 2^-k give lengths exactly k (the last two share k)
+    for kmax in range(2, 12):
+        counts = [1 << (kmax - k) for k in range(1, kmax)] + [1]
+        lens = O.package_merge(np.array(counts, np.uint64))
+        expect = list(range(1, kmax)) + [kmax - 1]
+        assert lens.tolist() == expect
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_equals_heap_huffman_when_limit_slack(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(2, 129))
+    counts = rng.integers(20000, 100000, size=n).astype(np.uint64)
+    assert heap_huffman_maxlen(counts) <= 11
+    lens = O.package_merge(counts)
+    assert int(np.dot(counts, lens.astype(np.uint64))) == heap_huffman_cost(counts)
+    assert kraft_sum(lens) == 2048
+
+
+def test_fibonacci_limit_binds():
+    fib = [1, 1]
+    while len(fib) < 25:
+        fib.append(fib[-1] + fib[-2])
+    counts = np.array(fib, np.uint64)
+    assert heap_huffman_maxlen(counts) > 11
+    lens = O.package_merge(counts)
+    assert max(lens) == 11
+    assert kraft_sum(lens) == 2048
+    # optimality against a small limit by brute force on a prefix of the chain
+    small = np.array(fib[:7], np.uint64)
+    assert int(np.dot(small, O.package_merge(small, 4).astype(np.uint64))) == \
+        brute_force_opt(small.tolist(), 4)
+
+
+def test_degenerate_alphabets():
+    one = np.zeros(256, np.uint64); one[37] = 999
+    lens = O.package_merge(one)
+    assert lens[37] == 1 and lens.sum() == 1
+    two = np.zeros(256, np.uint64); two[[3, 200]] = [5, 7]
+    assert sorted(O.package_merge(two)[[3, 200]].tolist()) == [1, 1]
+    uni = np.full(256, 10, np.uint64)
+    assert (O.package_merge(uni) == 8).all()
+    with pytest.raises(ValueError):
+        O.package_merge(np.ones(300, np.uint64), 8)     # 300 symbols cannot fit 8 bits
+
+
+# ------------------------------------------------------------------ canonical
+
+def _bitstr(code, n):
+    return format(int(code), "0%db" % n) if n else ""
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_canonical_prefix_free_and_ordered(seed):
+    rng = np.random.default_rng(200 + seed)
+    counts = rng.integers(0, 5000, size=256).astype(np.uint64) ** 2
+    lens = O.package_merge(counts)
+    tab = O.canonical(lens)
+    words = {s: _bitstr(tab["codes"][s], lens[s]) for s in range(256) if lens[s]}
+    vals = list(words.values())
+    for a in vals:                       # prefix-free, brute force
+        for b in vals:
+            assert a == b or not b.startswith(a)
+    # order: (len, sym) ascending is numeric order of left-justified codes
+    order = sorted(words, key=lambda s: (lens[s], s))
+    lj = [int(words[s], 2) << (11 - int(lens[s])) for s in order]
+    assert lj == sorted(lj) and len(set(lj)) == len(lj)
+    assert tab["sym_sorted"].tolist() == order
+    # limits are non-decreasing and close at 2048 for a complete code
+    lim = tab["limit"][1:].astype(int)
+    assert (np.diff(lim) >= 0).all() and lim[-1] == 2048
+    assert kraft_sum(lens) == 2048
+
+
+# ------------------------------------------------------------------ streams
+
+def _bundle_bits_by_hand(syms, spl, lens, codes, nt):
+    """Each lane's stream as a bit string built from the code table."""
+    out = []
+    s = syms.reshape(nt, 32, spl)
+    for t in range(nt):
+        out.append(["".join(_bitstr(codes[v], lens[v]) for v in s[t, l]) for l in range(32)])
+    return out
+
+
+@pytest.mark.parametrize("kind,law,seed", [(O.Q4, "normal", 1), (O.Q4, "laplace", 2),
+                                            (O.Q6, "normal", 3), (O.Q4, "uniform", 4),
+                                            (O.Q4, "const", 5)])
+def test_interleave_matches_bit_strings(kind, law, seed):
+    qmax = 15 if kind == O.Q4 else 63
+    mu = 31.5 if kind == O.Q6 else 7.5
+    codes, d, m, _ = synth.gen_q_custom(128, 512, seed, qmax=qmax, law=law, mu=mu,
+                                        scale=5.0 if kind == O.Q6 else 1.8)
+    b = O.build_bundle_q(kind, codes, d, m)
+    nt = 4
+    spl = b["spl"]
+    tab = b["table"]
+    syms = O.symbolise_q(kind, codes)
+    hand = _bundle_bits_by_hand(syms, spl, tab["lens"], tab["codes"], nt)
+    toff = b["tile_off"].astype(int)
+    assert toff[0] == 0 and (np.diff(toff) % 32 == 0).all() and (np.diff(toff) > 0).all()
+    for t in range(nt):
+        blk = b["words"][toff[t]:toff[t + 1]].reshape(-1, 32)     # [j][lane]
+        W = blk.shape[0]
+        nwords = [(len(hand[t][l]) + 31) // 32 for l in range(32)]
+        assert W == max(nwords)                      # padded to the longest lane
+        for l in range(32):
+            bits = "".join(format(int(w), "032b") for w in blk[:, l])
+            assert bits[:len(hand[t][l])] == hand[t][l]
+            assert set(bits[len(hand[t][l]):]) <= {"0"}
+            assert b["lane_bits"][t * 32 + l] == len(hand[t][l])
+
+
+def test_symbol_order_by_hand():
+    codes = np.arange(64 * 256, dtype=np.int64).reshape(64, 256) % 16
+    codes = codes.astype(np.uint8)
+    codes[5, 10] = 3
+    syms = O.symbolise_q(O.Q4, codes).reshape(32, 256)
+    # lane 2 holds rows 4 and 5; its symbol 128 + 5 is row 5 columns 10 (low), 11 (high)
+    assert syms[2, 128 + 5] == (codes[5, 10] | (codes[5, 11] << 4))
+    assert syms[7, 3] == (codes[14, 6] | (codes[14, 7] << 4))
+    s6 = O.symbolise_q(O.Q6, codes).reshape(32, 512)
+    assert s6[2, 256 + 10] == codes[5, 10] and s6[31, 255] == codes[62, 255]
+
+
+@pytest.mark.parametrize("kind,rows,cols,law,seed", [
+    (O.Q4, 64, 256, "normal", 11), (O.Q4, 192, 768, "normal", 12),
+    (O.Q4, 128, 1024, "laplace", 13), (O.Q6, 128, 512, "normal", 14),
+    (O.Q4, 64, 512, "uniform", 15), (O.Q4, 64, 256, "const", 16),
+    (O.Q6, 64, 256, "const", 17)])
+def test_round_trip_every_tile_and_bitwise(kind, rows, cols, law, seed):
+    qmax = 15 if kind == O.Q4 else 63
+    codes, d, m, _ = synth.gen_q_custom(rows, cols, seed, qmax=qmax, law=law,
+                                        mu=31.5 if kind == O.Q6 else 7.5,
+                                        scale=5.0 if kind == O.Q6 else 1.8)
+    b = O.build_bundle_q(kind, codes, d, m)
+    q1, bits = O.decode_bundle_q(b)
+    assert np.array_equal(q1, codes)
+    assert np.array_equal(bits, b["lane_bits"])
+    q2, _ = O.decode_bundle_q(b, bitwise=True)
+    assert np.array_equal(q2, codes)
+    # consumed bits equal the sum of code lengths of the lane's symbols
+    syms = O.symbolise_q(kind, codes).reshape(-1, b["spl"])
+    assert np.array_equal(b["table"]["lens"][syms].astype(np.int64).sum(1), bits.astype(np.int64))
+
+
+def test_round_trip_reduced_configs():
+    for cfg, kind in ((2, O.Q4), (3, O.Q4), (5, O.Q6)):
+        mat = synth.CONFIGS[cfg][0]
+        codes, d, m, _ = synth.gen_q(mat, rows=256, cols=2048)
+        b = O.build_bundle_q(kind, codes, d, m)
+        q, _ = O.decode_bundle_q(b)
+        assert np.array_equal(q, codes)
+        assert b["table"]["lens"].max() <= 11
+
+
+def test_dm_layout():
+    _, d, m, _ = synth.gen_q_custom(128, 512, 21)
+    dm = O.pack_dm(d, m).reshape(2, 2, 64)            # [rb][cb][row]
+    assert dm[1, 0, 5] == (int(d[69, 0]) | int(m[69, 0]) << 16)
+    assert dm[0, 1, 63] == (int(d[63, 1]) | int(m[63, 1]) << 16)
+
+
+# ------------------------------------------------------------------ numerics
+
+def test_half_and_bf16_conversions_exact():
+    h = np.arange(65536, dtype=np.uint16)
+    f = h.view(np.float16).astype(np.float64)
+    ok = ~np.isnan(f)
+    got = np.array([O.half_to_double(int(v)) for v in h[ok][::7]])
+    assert np.array_equal(got, f[ok][::7])
+    b = np.arange(0, 65536, 5, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        fb = (b << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    ok = ~np.isnan(fb)
+    got = np.array([O.bf16_to_double(int(v)) for v in b[ok]])
+    assert np.array_equal(got, fb[ok])
+
+
+def _dense_w(codes, d, m):
+    R, Cc = codes.shape
+    dd = np.repeat(d.view(np.float16).astype(np.float64), 256, axis=1)
+    mm = np.repeat(m.view(np.float16).astype(np.float64), 256, axis=1)
+    return dd * codes.astype(np.float64) - mm
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_gemv_vs_dense_numpy(batch):
+    codes, d, m, x = synth.gen_q_custom(128, 768, 31)
+    y = O.gemv_q(codes, d, m, x, batch)
+    ref = x[:batch].view(np.float16).astype(np.float64) @ _dense_w(codes, d, m).T
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+    rows = np.array([0, 5, 127, 64])
+    ys = O.gemv_q(codes, d, m, x, batch, rows=rows)
+    np.testing.assert_array_equal(ys, y[:, rows])
+
+
+def test_gemv_special_cases():
+    codes, d, m, x = synth.gen_q_custom(64, 512, 32)
+    W = _dense_w(codes, d, m)
+    for c in (0, 255, 256, 511):
+        e = np.zeros((1, 512), np.float16); e[0, c] = 1.0
+        y = O.gemv_q(codes, d, m, e.view(np.uint16), 1)
+        assert np.array_equal(y[0], W[:, c])            # exact column
+    eight = np.full_like(codes, 8)
+    assert np.array_equal(O.gemv_q(eight, d, m, x, 2), np.zeros((2, 64)))   # m = 8d
+    # idempotent codec: round((w + m) / d) recovers every code exactly
+    dd = np.repeat(d.view(np.float16).astype(np.float64), 256, axis=1)
+    mm = np.repeat(m.view(np.float16).astype(np.float64), 256, axis=1)
+    assert np.array_equal(np.rint((W + mm) / dd).astype(np.uint8), codes)
+
+
+def test_gemv_bf16_vs_dense():
+    w, x = synth.gen_bf16_custom(64, 512, 41)
+    y = O.gemv_bf16(w, x, 2)
+    wf = (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    xf = (x[:2].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    np.testing.assert_allclose(y, xf @ wf.T, rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------------ bf16
+
+@pytest.mark.parametrize("frac,seed", [(0.0, 51), (0.0005, 52), (0.01, 53)])
+def test_bf16_bit_exact_and_verbatim(frac, seed):
+    w, _ = synth.gen_bf16_custom(128, 512, seed, outlier_frac=frac)
+    b = O.build_bundle_bf16(w)
+    # palette: the 16 most frequent exponents, count desc then exponent asc
+    e = ((w >> 7) & 0xFF).astype(np.int64).ravel()
+    cnt = np.bincount(e, minlength=256)
+    order = np.lexsort((np.arange(256), -cnt))
+    order = [v for v in order if cnt[v] > 0][:16]
+    assert b["palette"][:len(order)].tolist() == order
+    # verbatim segments: exactly the 64-wide row runs with an exponent outside
+    inpal = np.zeros(256, bool); inpal[order] = True
+    seg_out = (~inpal[e.reshape(128, 512)]).reshape(128, 8, 64).any(-1)
+    assert b["n_verbatim"] == int(seg_out.sum())
+    for dec in (False, True):
+        w2, _ = O.decode_bundle_bf16(b, bitwise=dec)
+        assert np.array_equal(w2, w)
+
+
+def test_bf16_exponent_statistics():
+    # "Unweight": the top-16 exponents cover over 99% of a layer's weights and
+    # the exponent distribution needs about 2.6 bits
+    mat = synth.CONFIGS[4][0]
+    w, _ = synth.gen_bf16(mat, rows=512, cols=4096)
+    e = ((w >> 7) & 0xFF).ravel()
+    cnt = np.bincount(e, minlength=256).astype(np.float64)
+    p = np.sort(cnt)[::-1] / cnt.sum()
+    assert p[:16].sum() > 0.99
+    H = -(p[p > 0] * np.log2(p[p > 0])).sum()
+    assert 2.3 < H < 2.9
+    b = O.build_bundle_bf16(w)
+    w2, _ = O.decode_bundle_bf16(b)
+    assert np.array_equal(w2, w)
+
+
+def test_rejects_bad_shapes():
+    codes = np.zeros((65, 256), np.uint8)
+    with pytest.raises(ValueError):
+        O.build_bundle_q(O.Q4, codes, np.zeros((65, 1), np.uint16), np.zeros((65, 1), np.uint16))
