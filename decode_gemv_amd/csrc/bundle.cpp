@@ -1,0 +1,797 @@
+// bundle.cpp -- host-side bundle builder of liblw ("LazyWeights: Decode-on-
+// Demand Edge LLMs", section "2 . Code them"; bf16 variant after "Unweight",
+// "The exponent's exploitable redundancy").
+//
+// A bundle is a flat image (lw_internal.h) holding, for one matrix:
+//   - one length-limited (<= 11 bit) canonical Huffman table,
+//   - the lane words of every 64x256 tile: 32 lanes, each carrying two
+//     adjacent rows as one MSB-first stream of 32-bit words, the lanes' words
+//     interleaved (word j of lane l at 32j + l) and zero-padded to the tile's
+//     longest lane, plus a word offset per tile,
+//   - the raw per-super-block scales (Q4/Q6), or the raw sign+mantissa bytes,
+//     exponent palette and verbatim segments (bf16),
+//   - tables derived for the GPU kernels and a zeroed device workspace.
+// Choices the pages leave open (tie-breaks, bit order, lane rows, pair order)
+// are the ones listed in the design notes; they make the image reproducible.
+#include <algorithm>
+#include <atomic>
+#include <cstring>
+#include <memory>
+#include <new>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "lw_internal.h"
+
+struct lw_bundle {
+    std::vector<uint8_t> image;
+};
+
+// ----------------------------------------------------------------- errors
+static thread_local std::string g_err;
+
+lw_status lw_fail(lw_status s, const std::string &msg)
+{
+    g_err = msg;
+    return s;
+}
+
+extern "C" const char *lw_last_error(void) { return g_err.c_str(); }
+
+extern "C" const char *lw_status_str(lw_status s)
+{
+    switch (s) {
+    case LW_OK: return "ok";
+    case LW_E_ARG: return "invalid argument";
+    case LW_E_SHAPE: return "shape not a multiple of 64x256";
+    case LW_E_TABLE: return "invalid code table";
+    case LW_E_FORMAT: return "corrupt bundle";
+    case LW_E_NOMEM: return "out of host memory";
+    case LW_E_DEVICE: return "HIP error";
+    case LW_E_UNSUPPORTED: return "unsupported";
+    }
+    return "unknown status";
+}
+
+// ----------------------------------------------------------------- helpers
+static int worker_count()
+{
+    unsigned n = std::thread::hardware_concurrency();
+    if (n == 0) n = 4;
+    return (int)std::min(n, 16u);
+}
+
+template <class F>
+static void parallel_for(int64_t n, F f)
+{
+    int nt = (int)std::min<int64_t>(worker_count(), std::max<int64_t>(n, 1));
+    if (nt <= 1) {
+        for (int64_t i = 0; i < n; i++) f(i);
+        return;
+    }
+    std::atomic<int64_t> next(0);
+    std::vector<std::thread> th;
+    for (int t = 0; t < nt; t++)
+        th.emplace_back([&]() {
+            for (;;) {
+                int64_t i = next.fetch_add(1);
+                if (i >= n) break;
+                f(i);
+            }
+        });
+    for (auto &x : th) x.join();
+}
+
+// Optimal code lengths with a length limit (package-merge).  This is the
+// array form of the coin-collector algorithm: each level's list is kept only
+// as (weight, is-leaf) pairs, and the lengths are recovered afterwards from
+// how many leaves each level's selected prefix holds (a selected package of
+// level i always consists of the first items of level i-1, and the leaves of
+// any prefix are the lightest leaves).  Tie rules: leaves ordered by (count,
+// symbol); adjacent pairing; a leaf precedes a package of equal weight; the
+// first 2n-2 items of the last level are selected.
+static bool length_limited_lengths(int n_alpha, const uint64_t *counts, int limit, uint8_t *lens)
+{
+    std::vector<int> order;
+    for (int s = 0; s < n_alpha; s++) {
+        lens[s] = 0;
+        if (counts[s]) order.push_back(s);
+    }
+    int n = (int)order.size();
+    if (n == 0) return true;
+    if (n == 1) {
+        lens[order[0]] = 1;
+        return true;
+    }
+    if ((1 << limit) < n) return false;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int a, int b) { return counts[a] < counts[b]; });
+    std::vector<uint64_t> lw(n);
+    for (int i = 0; i < n; i++) lw[i] = counts[order[i]];
+    // levels[i]: is-leaf flags of level i's merged list (level 0 = leaves)
+    std::vector<std::vector<uint8_t>> leaf(limit);
+    std::vector<uint64_t> cur(lw), nxt;
+    leaf[0].assign(n, 1);
+    for (int lev = 1; lev < limit; lev++) {
+        size_t npk = cur.size() / 2;
+        nxt.clear();
+        leaf[lev].clear();
+        size_t i = 0, p = 0;
+        while (i < (size_t)n || p < npk) {
+            uint64_t pw = p < npk ? cur[2 * p] + cur[2 * p + 1] : 0;
+            bool take_leaf = (p >= npk) || (i < (size_t)n && lw[i] <= pw);
+            if (take_leaf) {
+                nxt.push_back(lw[i++]);
+                leaf[lev].push_back(1);
+            } else {
+                nxt.push_back(pw);
+                p++;
+                leaf[lev].push_back(0);
+            }
+        }
+        cur.swap(nxt);
+    }
+    std::vector<int> depth(n, 0);
+    size_t m = 2 * (size_t)n - 2;
+    for (int lev = limit - 1; lev >= 0; lev--) {
+        size_t nleaf = 0;
+        for (size_t k = 0; k < m && k < leaf[lev].size(); k++) nleaf += leaf[lev][k];
+        for (size_t k = 0; k < nleaf; k++) depth[k]++;
+        m = 2 * (m - nleaf);
+        if (m == 0) break;
+    }
+    for (int i = 0; i < n; i++) lens[order[i]] = (uint8_t)depth[i];
+    return true;
+}
+
+// Canonical code in the RFC 1951 (section 3.2.2) manner, and the decoder
+// arrays of "3 . Decode on demand": per length L, count, first code,
+// limit = (first + count) << (11 - L), and offset into the length-sorted
+// symbol table.
+static int canonical_table(int n_alpha, const uint8_t *lens, uint16_t *codes, lw_table *t)
+{
+    std::memset(t, 0, sizeof(*t));
+    for (int s = 0; s < n_alpha; s++) {
+        if (lens[s] > LW_MAXLEN) return -1;
+        if (lens[s]) t->count[lens[s]]++;
+    }
+    uint32_t next[LW_MAXLEN + 2];
+    uint32_t code = 0;
+    for (int L = 1; L <= LW_MAXLEN; L++) {
+        code = (code + t->count[L - 1]) << 1;
+        next[L] = code;
+        t->first[L] = (uint16_t)code;
+    }
+    uint32_t acc = 0;
+    for (int L = 1; L <= LW_MAXLEN; L++) {
+        t->offset[L] = (uint16_t)acc;
+        acc += t->count[L];
+        t->limit[L] = (uint16_t)(((uint32_t)t->first[L] + t->count[L]) << (LW_MAXLEN - L));
+    }
+    uint32_t fill[LW_MAXLEN + 2];
+    for (int L = 1; L <= LW_MAXLEN; L++) fill[L] = t->offset[L];
+    for (int s = 0; s < n_alpha; s++) {
+        codes[s] = 0;
+        if (!lens[s]) continue;
+        codes[s] = (uint16_t)next[lens[s]]++;
+        t->sym_sorted[fill[lens[s]]++] = (uint16_t)s;
+    }
+    return (int)acc;
+}
+
+// Bit writer into one lane of an interleaved tile block.
+struct LaneWriter {
+    uint32_t *blk;
+    int lane;
+    uint64_t acc = 0;   // pending bits, right-aligned
+    int nacc = 0;
+    int64_t word = 0;
+    void put(uint32_t code, int len)
+    {
+        acc = (acc << len) | code;
+        nacc += len;
+        if (nacc >= 32) {
+            nacc -= 32;
+            blk[32 * word + lane] = (uint32_t)(acc >> nacc);
+            word++;
+            acc &= (nacc ? ((1ull << nacc) - 1) : 0);
+        }
+    }
+    void flush()
+    {
+        if (nacc) blk[32 * word + lane] = (uint32_t)(acc << (32 - nacc));
+    }
+};
+
+struct Shape {
+    int64_t rows, cols, n_rb, n_cb, n_tiles;
+};
+
+// Layout of a new image.  Returns the header with offsets and sizes filled.
+static lw_image_header plan_image(int kind, const Shape &sh, int64_t n_words, int64_t n_verb)
+{
+    lw_image_header h;
+    std::memset(&h, 0, sizeof(h));
+    h.magic = LW_MAGIC;
+    h.version = LW_VERSION;
+    h.kind = kind;
+    h.bits = kind == LW_Q4_PAIR ? 4 : (kind == LW_Q6_SINGLE ? 6 : 16);
+    h.rows = sh.rows;
+    h.cols = sh.cols;
+    h.n_tiles = sh.n_tiles;
+    h.n_rb = (int32_t)sh.n_rb;
+    h.n_cb = (int32_t)sh.n_cb;
+    h.spl = kind == LW_Q4_PAIR ? 256 : 512;
+    h.work_groups = (int32_t)((sh.n_cb + LW_CB_PER_WG - 1) / LW_CB_PER_WG);
+    h.n_verbatim = n_verb;
+    uint64_t bytes[LW_REG_COUNT] = {0};
+    bytes[LW_REG_TABLE] = sizeof(lw_table);
+    bytes[LW_REG_GPUTAB] = sizeof(lw_gputab);
+    bytes[LW_REG_TILE_OFF] = 4u * (uint64_t)(sh.n_tiles + 1);
+    bytes[LW_REG_WORDS] = 4u * (uint64_t)n_words;
+    if (kind == LW_BF16_EXP) {
+        bytes[LW_REG_PALETTE] = 16;
+        bytes[LW_REG_SM] = 4u * 4096u * (uint64_t)sh.n_tiles;
+        bytes[LW_REG_VB_BITS] = 32u * (uint64_t)sh.n_tiles;
+        bytes[LW_REG_VB_START] = 4u * (uint64_t)(sh.n_tiles + 1);
+        bytes[LW_REG_VERBATIM] = 128u * (uint64_t)n_verb;
+    } else {
+        bytes[LW_REG_DM] = 4u * 64u * (uint64_t)sh.n_tiles;
+    }
+    int64_t n_rows_wg = (sh.n_rb + LW_RB_PER_WG - 1) / LW_RB_PER_WG;
+    bytes[LW_REG_WORK] = h.work_groups > 1
+        ? lw_work_partial_bytes(h.work_groups, sh.rows) + 4u * (uint64_t)(n_rows_wg + 64) : 0;
+    uint64_t pos = LW_HEADER_BYTES;
+    for (int r = 0; r < LW_REG_COUNT; r++) {
+        h.off[r] = bytes[r] ? pos : 0;
+        h.bytes[r] = bytes[r];
+        pos = lw_align_up(pos + bytes[r]);
+    }
+    h.coded_bytes = bytes[LW_REG_WORDS] + bytes[LW_REG_TILE_OFF] + bytes[LW_REG_TABLE] +
+                    bytes[LW_REG_DM] + bytes[LW_REG_SM] + bytes[LW_REG_VB_BITS] +
+                    bytes[LW_REG_VB_START] + bytes[LW_REG_VERBATIM] + bytes[LW_REG_PALETTE];
+    h.twin_bytes = kind == LW_BF16_EXP
+        ? 2u * (uint64_t)sh.rows * (uint64_t)sh.cols
+        : (uint64_t)sh.rows * (uint64_t)sh.cols * (uint64_t)h.bits / 8u +
+              (uint64_t)sh.rows * (uint64_t)(sh.cols / 256) * 4u;
+    return h;
+}
+
+template <class T>
+static T *region(std::vector<uint8_t> &img, const lw_image_header &h, int r)
+{
+    return reinterpret_cast<T *>(img.data() + h.off[r]);
+}
+
+// fp16 bit pattern of a small non-negative integer (exact for v < 2048).
+static uint32_t small_int_half(uint32_t v)
+{
+    if (v == 0) return 0;
+    int e = 31 - __builtin_clz(v);
+    return (uint32_t)((e + 15) << 10) | ((v << (10 - e)) & 0x3FFu);
+}
+
+// Derived tables for the kernels (payload per canonical index, limits
+// left-justified to a 32-bit window, length and base per comparison count).
+static void fill_gputab(int kind, const lw_table &t, const uint8_t *palette, lw_image_header &h,
+                        lw_gputab *g)
+{
+    std::memset(g, 0, sizeof(*g));
+    int lmin = 0, lmax = 0;
+    for (int L = 1; L <= LW_MAXLEN; L++)
+        if (t.count[L]) {
+            if (!lmin) lmin = L;
+            lmax = L;
+        }
+    h.min_len = lmin;
+    h.max_len = lmax;
+    for (int i = 0; i < 16; i++) g->limlj[i] = 0xFFFFFFFFu;
+    for (int L = lmin; L < lmax; L++) g->limlj[L - lmin] = (uint32_t)t.limit[L] << 21;
+    for (int r = 0; lmin && r <= lmax - lmin; r++) {
+        int L = lmin + r;
+        g->len[r] = (uint32_t)L;
+        g->base[r] = (int32_t)t.offset[L] - (int32_t)t.first[L];
+    }
+    for (int i = 0; i < h.n_sym; i++) {
+        uint32_t s = t.sym_sorted[i];
+        g->symval[i] = s;
+        if (kind == LW_Q4_PAIR) {
+            g->payload[i] = small_int_half(s & 15) | (small_int_half(s >> 4) << 16);
+        } else if (kind == LW_Q6_SINGLE) {
+            g->payload[i] = small_int_half(s);
+            g->payload_hi[i] = small_int_half(s) << 16;
+        } else {
+            uint32_t e = palette[s];
+            g->payload[i] = e << 7;
+            g->payload_hi[i] = e << 23;
+        }
+    }
+}
+
+// Encode every tile of a symbol source.  sym(t, l, k) gives symbol k of lane
+// l of tile t.  Two passes: lane bit counts (for the tile sizes), then words.
+template <class SymFn>
+static void encode_tiles(const Shape &sh, int spl, const uint8_t *lens, const uint16_t *codes,
+                         SymFn sym, std::vector<uint32_t> &tile_off, int32_t &max_words,
+                         std::vector<uint8_t> *img, const lw_image_header *h)
+{
+    if (!img) {
+        std::vector<uint32_t> wt(sh.n_tiles);
+        parallel_for(sh.n_tiles, [&](int64_t t) {
+            uint32_t wmax = 0;
+            for (int l = 0; l < LW_LANES; l++) {
+                uint64_t bits = 0;
+                for (int k = 0; k < spl; k++) bits += lens[sym(t, l, k)];
+                wmax = std::max<uint32_t>(wmax, (uint32_t)((bits + 31) / 32));
+            }
+            wt[t] = wmax;
+        });
+        tile_off.assign(sh.n_tiles + 1, 0);
+        uint64_t pos = 0;
+        max_words = 0;
+        for (int64_t t = 0; t < sh.n_tiles; t++) {
+            tile_off[t] = (uint32_t)pos;
+            pos += 32u * wt[t];
+            max_words = std::max<int32_t>(max_words, (int32_t)wt[t]);
+        }
+        tile_off[sh.n_tiles] = (uint32_t)pos;
+        return;
+    }
+    uint32_t *words = region<uint32_t>(*img, *h, LW_REG_WORDS);
+    parallel_for(sh.n_tiles, [&](int64_t t) {
+        uint32_t *blk = words + tile_off[t];
+        for (int l = 0; l < LW_LANES; l++) {
+            LaneWriter w{blk, l};
+            for (int k = 0; k < spl; k++) {
+                int s = sym(t, l, k);
+                w.put(codes[s], lens[s]);
+            }
+            w.flush();
+        }
+    });
+}
+
+static lw_status check_shape(int64_t rows, int64_t cols, Shape &sh)
+{
+    if (rows <= 0 || cols <= 0 || rows % LW_TILE_ROWS || cols % LW_TILE_COLS)
+        return lw_fail(LW_E_SHAPE, "rows must be a positive multiple of 64 and cols of 256");
+    if (rows * cols > ((int64_t)1 << 34))
+        return lw_fail(LW_E_ARG, "matrix too large for 32-bit word offsets");
+    sh.rows = rows;
+    sh.cols = cols;
+    sh.n_rb = rows / LW_TILE_ROWS;
+    sh.n_cb = cols / LW_TILE_COLS;
+    sh.n_tiles = sh.n_rb * sh.n_cb;
+    return LW_OK;
+}
+
+static lw_status finish_table(int n_alpha, const std::vector<uint64_t> &hist, uint8_t *lens,
+                              uint16_t *codes, lw_table &tab, int &n_sym)
+{
+    if (!length_limited_lengths(n_alpha, hist.data(), LW_MAXLEN, lens))
+        return lw_fail(LW_E_TABLE, "alphabet does not fit 11-bit codes");
+    n_sym = canonical_table(n_alpha, lens, codes, &tab);
+    if (n_sym < 0) return lw_fail(LW_E_TABLE, "code length above 11");
+    return LW_OK;
+}
+
+extern "C" lw_status lw_bundle_build_q(int kind, int64_t rows, int64_t cols, const uint8_t *q,
+                                       const uint16_t *d, const uint16_t *m, lw_bundle **out)
+{
+    if (!out) return lw_fail(LW_E_ARG, "out is null");
+    *out = nullptr;
+    if (!q || !d || !m) return lw_fail(LW_E_ARG, "null input");
+    if (kind != LW_Q4_PAIR && kind != LW_Q6_SINGLE) return lw_fail(LW_E_ARG, "kind must be Q4 or Q6");
+    Shape sh;
+    lw_status st = check_shape(rows, cols, sh);
+    if (st) return st;
+    const int qmax = kind == LW_Q4_PAIR ? 15 : 63;
+    const int n_alpha = kind == LW_Q4_PAIR ? 256 : 64;
+    const int spl = kind == LW_Q4_PAIR ? 256 : 512;
+    try {
+        // histogram over the whole matrix (one table per matrix), per row band
+        std::vector<std::vector<uint64_t>> part(sh.n_rb, std::vector<uint64_t>(n_alpha, 0));
+        std::atomic<int> bad(0);
+        parallel_for(sh.n_rb, [&](int64_t rb) {
+            auto &hh = part[rb];
+            for (int64_t r = rb * 64; r < rb * 64 + 64; r++) {
+                const uint8_t *row = q + r * cols;
+                if (kind == LW_Q4_PAIR) {
+                    for (int64_t c = 0; c < cols; c += 2) {
+                        if ((row[c] | row[c + 1]) > qmax) bad = 1;
+                        hh[(row[c] | (row[c + 1] << 4)) & 255]++;
+                    }
+                } else {
+                    for (int64_t c = 0; c < cols; c++) {
+                        if (row[c] > qmax) bad = 1;
+                        hh[row[c] & 63]++;
+                    }
+                }
+            }
+        });
+        if (bad) return lw_fail(LW_E_ARG, "code out of range for the kind");
+        std::vector<uint64_t> hist(n_alpha, 0);
+        for (auto &hh : part)
+            for (int s = 0; s < n_alpha; s++) hist[s] += hh[s];
+        uint8_t lens[256];
+        uint16_t codes[256];
+        lw_table tab;
+        int n_sym = 0;
+        if ((st = finish_table(n_alpha, hist, lens, codes, tab, n_sym))) return st;
+
+        auto sym = [&](int64_t t, int l, int k) -> int {
+            int64_t rb = t / sh.n_cb, cb = t % sh.n_cb;
+            int half = k >= spl / 2;
+            int kk = k - half * (spl / 2);
+            const uint8_t *row = q + (rb * 64 + 2 * l + half) * cols + cb * 256;
+            if (kind == LW_Q4_PAIR) return row[2 * kk] | (row[2 * kk + 1] << 4);
+            return row[kk];
+        };
+        std::vector<uint32_t> tile_off;
+        int32_t max_words = 0;
+        encode_tiles(sh, spl, lens, codes, sym, tile_off, max_words, nullptr, nullptr);
+        lw_image_header h = plan_image(kind, sh, tile_off[sh.n_tiles], 0);
+        h.n_sym = n_sym;
+        h.max_words = max_words;
+        std::unique_ptr<lw_bundle> b(new lw_bundle);
+        uint64_t total = lw_align_up(h.off[LW_REG_WORK] + h.bytes[LW_REG_WORK]);
+        for (int r = 0; r < LW_REG_COUNT; r++)
+            if (h.bytes[r]) total = std::max<uint64_t>(total, lw_align_up(h.off[r] + h.bytes[r]));
+        b->image.assign(total, 0);
+        std::memcpy(region<uint32_t>(b->image, h, LW_REG_TILE_OFF), tile_off.data(), 4 * tile_off.size());
+        *region<lw_table>(b->image, h, LW_REG_TABLE) = tab;
+        fill_gputab(kind, tab, nullptr, h, region<lw_gputab>(b->image, h, LW_REG_GPUTAB));
+        encode_tiles(sh, spl, lens, codes, sym, tile_off, max_words, &b->image, &h);
+        uint32_t *dm = region<uint32_t>(b->image, h, LW_REG_DM);
+        parallel_for(sh.n_rb, [&](int64_t rb) {
+            for (int64_t cb = 0; cb < sh.n_cb; cb++)
+                for (int i = 0; i < 64; i++) {
+                    int64_t r = rb * 64 + i;
+                    dm[(rb * sh.n_cb + cb) * 64 + i] =
+                        (uint32_t)d[r * sh.n_cb + cb] | ((uint32_t)m[r * sh.n_cb + cb] << 16);
+                }
+        });
+        std::memcpy(b->image.data(), &h, sizeof(h));
+        *out = b.release();
+        return LW_OK;
+    } catch (const std::bad_alloc &) {
+        return lw_fail(LW_E_NOMEM, "host allocation failed");
+    }
+}
+
+extern "C" lw_status lw_bundle_build_bf16(int64_t rows, int64_t cols, const uint16_t *w, lw_bundle **out)
+{
+    if (!out) return lw_fail(LW_E_ARG, "out is null");
+    *out = nullptr;
+    if (!w) return lw_fail(LW_E_ARG, "null input");
+    Shape sh;
+    lw_status st = check_shape(rows, cols, sh);
+    if (st) return st;
+    try {
+        // exponent histogram -> palette: top 16 by (count desc, exponent asc)
+        std::vector<std::vector<uint64_t>> part(sh.n_rb, std::vector<uint64_t>(256, 0));
+        parallel_for(sh.n_rb, [&](int64_t rb) {
+            for (int64_t i = rb * 64 * cols; i < (rb + 1) * 64 * cols; i++) part[rb][(w[i] >> 7) & 255]++;
+        });
+        uint64_t ecount[256] = {0};
+        for (auto &p : part)
+            for (int e = 0; e < 256; e++) ecount[e] += p[e];
+        int order[256];
+        for (int e = 0; e < 256; e++) order[e] = e;
+        std::stable_sort(order, order + 256, [&](int a, int b) { return ecount[a] > ecount[b]; });
+        uint8_t palette[16] = {0};
+        int n_pal = 0;
+        int8_t pidx[256];
+        std::memset(pidx, -1, sizeof(pidx));
+        for (int k = 0; k < 16 && ecount[order[k]]; k++) {
+            palette[k] = (uint8_t)order[k];
+            pidx[order[k]] = (int8_t)k;
+            n_pal++;
+        }
+        // verbatim segments: any exponent outside the palette in a 64-weight run
+        std::vector<uint32_t> vb_bits(sh.n_tiles * 8, 0), vb_start(sh.n_tiles + 1, 0);
+        std::vector<uint32_t> tile_nv(sh.n_tiles, 0);
+        parallel_for(sh.n_tiles, [&](int64_t t) {
+            int64_t rb = t / sh.n_cb, cb = t % sh.n_cb;
+            uint32_t nv = 0;
+            for (int i = 0; i < 64; i++)
+                for (int s = 0; s < 4; s++) {
+                    const uint16_t *seg = w + (rb * 64 + i) * cols + cb * 256 + 64 * s;
+                    bool outp = false;
+                    for (int c = 0; c < 64; c++) outp |= pidx[(seg[c] >> 7) & 255] < 0;
+                    if (outp) {
+                        vb_bits[t * 8 + (4 * i + s) / 32] |= 1u << ((4 * i + s) % 32);
+                        nv++;
+                    }
+                }
+            tile_nv[t] = nv;
+        });
+        int64_t n_verb = 0;
+        for (int64_t t = 0; t < sh.n_tiles; t++) {
+            vb_start[t] = (uint32_t)n_verb;
+            n_verb += tile_nv[t];
+        }
+        vb_start[sh.n_tiles] = (uint32_t)n_verb;
+        auto is_verb = [&](int64_t t, int i, int c) {
+            int bit = 4 * i + c / 64;
+            return (vb_bits[t * 8 + bit / 32] >> (bit % 32)) & 1u;
+        };
+        auto sym = [&](int64_t t, int l, int k) -> int {
+            int64_t rb = t / sh.n_cb, cb = t % sh.n_cb;
+            int half = k >= 256;
+            int c = k - 256 * half;
+            int i = 2 * l + half;
+            if (is_verb(t, i, c)) return 0;        // placeholder keeps lanes at 512 symbols
+            return pidx[(w[(rb * 64 + i) * cols + cb * 256 + c] >> 7) & 255];
+        };
+        std::vector<uint64_t> hist(16, 0);
+        {
+            std::vector<std::vector<uint64_t>> ht(sh.n_rb);
+            parallel_for(sh.n_rb, [&](int64_t rb) {
+                std::vector<uint64_t> hh(16, 0);
+                for (int64_t cb = 0; cb < sh.n_cb; cb++)
+                    for (int l = 0; l < 32; l++)
+                        for (int k = 0; k < 512; k++) hh[sym(rb * sh.n_cb + cb, l, k)]++;
+                ht[rb] = hh;
+            });
+            for (int64_t rb = 0; rb < sh.n_rb; rb++)
+                for (int s = 0; s < 16; s++) hist[s] += ht[rb][s];
+        }
+        uint8_t lens[16];
+        uint16_t codes[16];
+        lw_table tab;
+        int n_sym = 0;
+        if ((st = finish_table(16, hist, lens, codes, tab, n_sym))) return st;
+        std::vector<uint32_t> tile_off;
+        int32_t max_words = 0;
+        encode_tiles(sh, 512, lens, codes, sym, tile_off, max_words, nullptr, nullptr);
+        lw_image_header h = plan_image(LW_BF16_EXP, sh, tile_off[sh.n_tiles], n_verb);
+        h.n_sym = n_sym;
+        h.max_words = max_words;
+        h.n_pal = n_pal;
+        std::unique_ptr<lw_bundle> b(new lw_bundle);
+        uint64_t total = 0;
+        for (int r = 0; r < LW_REG_COUNT; r++)
+            if (h.bytes[r]) total = std::max<uint64_t>(total, lw_align_up(h.off[r] + h.bytes[r]));
+        b->image.assign(total, 0);
+        std::memcpy(region<uint32_t>(b->image, h, LW_REG_TILE_OFF), tile_off.data(), 4 * tile_off.size());
+        *region<lw_table>(b->image, h, LW_REG_TABLE) = tab;
+        std::memcpy(region<uint8_t>(b->image, h, LW_REG_PALETTE), palette, 16);
+        fill_gputab(LW_BF16_EXP, tab, palette, h, region<lw_gputab>(b->image, h, LW_REG_GPUTAB));
+        encode_tiles(sh, 512, lens, codes, sym, tile_off, max_words, &b->image, &h);
+        std::memcpy(region<uint32_t>(b->image, h, LW_REG_VB_BITS), vb_bits.data(), 4 * vb_bits.size());
+        std::memcpy(region<uint32_t>(b->image, h, LW_REG_VB_START), vb_start.data(), 4 * vb_start.size());
+        uint32_t *sm = region<uint32_t>(b->image, h, LW_REG_SM);
+        uint16_t *verb = n_verb ? region<uint16_t>(b->image, h, LW_REG_VERBATIM) : nullptr;
+        parallel_for(sh.n_tiles, [&](int64_t t) {
+            int64_t rb = t / sh.n_cb, cb = t % sh.n_cb;
+            uint32_t *blk = sm + t * 4096;
+            // sign+mantissa byte of tile row 2l+p, column 4g+b -> byte b of word (p*64+g)*32+l
+            for (int p = 0; p < 2; p++)
+                for (int l = 0; l < 32; l++) {
+                    const uint16_t *row = w + (rb * 64 + 2 * l + p) * cols + cb * 256;
+                    for (int g = 0; g < 64; g++) {
+                        uint32_t v = 0;
+                        for (int bb = 0; bb < 4; bb++) {
+                            uint16_t x = row[4 * g + bb];
+                            v |= (uint32_t)(((x >> 8) & 0x80) | (x & 0x7F)) << (8 * bb);
+                        }
+                        blk[(p * 64 + g) * 32 + l] = v;
+                    }
+                }
+            uint32_t vo = vb_start[t];
+            for (int i = 0; i < 64; i++)
+                for (int s = 0; s < 4; s++)
+                    if (is_verb(t, i, 64 * s)) {
+                        std::memcpy(verb + (uint64_t)vo * 64, w + (rb * 64 + i) * cols + cb * 256 + 64 * s, 128);
+                        vo++;
+                    }
+        });
+        std::memcpy(b->image.data(), &h, sizeof(h));
+        *out = b.release();
+        return LW_OK;
+    } catch (const std::bad_alloc &) {
+        return lw_fail(LW_E_NOMEM, "host allocation failed");
+    }
+}
+
+// ----------------------------------------------------------------- validate
+static lw_status validate_image(const uint8_t *img, size_t bytes)
+{
+    if (bytes < LW_HEADER_BYTES) return lw_fail(LW_E_FORMAT, "image shorter than its header");
+    lw_image_header h;
+    std::memcpy(&h, img, sizeof(h));
+    if (h.magic != LW_MAGIC || h.version != LW_VERSION) return lw_fail(LW_E_FORMAT, "bad magic/version");
+    if (h.kind < LW_Q4_PAIR || h.kind > LW_BF16_EXP) return lw_fail(LW_E_FORMAT, "bad kind");
+    if (h.rows <= 0 || h.cols <= 0 || h.rows % 64 || h.cols % 256) return lw_fail(LW_E_FORMAT, "bad shape");
+    if (h.n_rb != h.rows / 64 || h.n_cb != h.cols / 256 || h.n_tiles != (int64_t)h.n_rb * h.n_cb)
+        return lw_fail(LW_E_FORMAT, "inconsistent tile counts");
+    if (h.spl != (h.kind == LW_Q4_PAIR ? 256 : 512)) return lw_fail(LW_E_FORMAT, "bad symbols per lane");
+    uint64_t prev_end = LW_HEADER_BYTES;
+    for (int r = 0; r < LW_REG_COUNT; r++) {
+        if (!h.bytes[r]) continue;
+        if (h.off[r] % LW_ALIGN || h.off[r] < prev_end || h.off[r] + h.bytes[r] > bytes)
+            return lw_fail(LW_E_FORMAT, "region out of bounds: " + std::to_string(r));
+        prev_end = h.off[r] + h.bytes[r];
+    }
+    bool need[LW_REG_COUNT] = {true, true, true, true, h.kind != LW_BF16_EXP, h.kind == LW_BF16_EXP,
+                               h.kind == LW_BF16_EXP, h.kind == LW_BF16_EXP, h.kind == LW_BF16_EXP,
+                               false, false};
+    for (int r = 0; r < LW_REG_COUNT; r++)
+        if (need[r] && !h.bytes[r]) return lw_fail(LW_E_FORMAT, "missing region " + std::to_string(r));
+    if (h.bytes[LW_REG_TABLE] != sizeof(lw_table) || h.bytes[LW_REG_GPUTAB] != sizeof(lw_gputab))
+        return lw_fail(LW_E_FORMAT, "table region size");
+    if (h.bytes[LW_REG_TILE_OFF] != 4u * (uint64_t)(h.n_tiles + 1)) return lw_fail(LW_E_FORMAT, "tile_off size");
+    if (h.kind != LW_BF16_EXP && h.bytes[LW_REG_DM] != 256u * (uint64_t)h.n_tiles)
+        return lw_fail(LW_E_FORMAT, "dm size");
+    if (h.kind == LW_BF16_EXP &&
+        (h.bytes[LW_REG_SM] != 16384u * (uint64_t)h.n_tiles || h.bytes[LW_REG_VB_BITS] != 32u * (uint64_t)h.n_tiles ||
+         h.bytes[LW_REG_VB_START] != 4u * (uint64_t)(h.n_tiles + 1) || h.bytes[LW_REG_VERBATIM] != 128u * (uint64_t)h.n_verbatim))
+        return lw_fail(LW_E_FORMAT, "bf16 region sizes");
+    // table: lengths <= 11, Kraft sum, consistent canonical arrays
+    lw_table t;
+    std::memcpy(&t, img + h.off[LW_REG_TABLE], sizeof(t));
+    int n_alpha = h.kind == LW_Q4_PAIR ? 256 : (h.kind == LW_Q6_SINGLE ? 64 : 16);
+    uint64_t kraft = 0;
+    int nsym = 0, lmin = 0, lmax = 0;
+    uint32_t code = 0;
+    for (int L = 1; L <= LW_MAXLEN; L++) {
+        code = (code + (L > 1 ? t.count[L - 1] : 0)) << 1;
+        if (t.first[L] != code) return lw_fail(LW_E_TABLE, "first[] not canonical");
+        if (t.offset[L] != nsym) return lw_fail(LW_E_TABLE, "offset[] inconsistent");
+        if (t.limit[L] != (uint16_t)(((uint32_t)t.first[L] + t.count[L]) << (LW_MAXLEN - L)))
+            return lw_fail(LW_E_TABLE, "limit[] inconsistent");
+        kraft += (uint64_t)t.count[L] << (LW_MAXLEN - L);
+        nsym += t.count[L];
+        if (t.count[L]) {
+            if (!lmin) lmin = L;
+            lmax = L;
+        }
+    }
+    if (t.count[0]) return lw_fail(LW_E_TABLE, "count[0] nonzero");
+    if (nsym < 1 || nsym > n_alpha) return lw_fail(LW_E_TABLE, "symbol count");
+    if (kraft > 2048 || (nsym > 1 && kraft != 2048)) return lw_fail(LW_E_TABLE, "Kraft sum violated");
+    if (nsym != h.n_sym || lmin != h.min_len || lmax != h.max_len) return lw_fail(LW_E_TABLE, "header/table mismatch");
+    for (int i = 0; i < nsym; i++)
+        if (t.sym_sorted[i] >= n_alpha) return lw_fail(LW_E_TABLE, "symbol out of alphabet");
+    const lw_gputab *g = reinterpret_cast<const lw_gputab *>(img + h.off[LW_REG_GPUTAB]);
+    for (int r = 0; r <= lmax - lmin; r++) {
+        int L = lmin + r;
+        if ((int)g->len[r] != L || g->base[r] != (int32_t)t.offset[L] - (int32_t)t.first[L])
+            return lw_fail(LW_E_FORMAT, "gpu table mismatch");
+    }
+    for (int L = lmin; L < lmax; L++)
+        if (g->limlj[L - lmin] != ((uint32_t)t.limit[L] << 21)) return lw_fail(LW_E_FORMAT, "gpu limits mismatch");
+    // tile offsets: start at 0, grow by whole word rows, end at the word count
+    const uint32_t *to = reinterpret_cast<const uint32_t *>(img + h.off[LW_REG_TILE_OFF]);
+    if (to[0] != 0) return lw_fail(LW_E_FORMAT, "tile_off[0] != 0");
+    int32_t wmax = 0;
+    for (int64_t i = 0; i < h.n_tiles; i++) {
+        if (to[i + 1] < to[i] || (to[i + 1] - to[i]) % 32) return lw_fail(LW_E_FORMAT, "tile_off not monotone rows");
+        wmax = std::max<int32_t>(wmax, (int32_t)((to[i + 1] - to[i]) / 32));
+    }
+    if ((uint64_t)to[h.n_tiles] * 4u != h.bytes[LW_REG_WORDS]) return lw_fail(LW_E_FORMAT, "words size");
+    if (wmax != h.max_words) return lw_fail(LW_E_FORMAT, "max_words mismatch");
+    // a lane can hold at most symbols_per_lane codes of 11 bits
+    if ((int64_t)wmax * 32 > (int64_t)h.spl * LW_MAXLEN + 31) return lw_fail(LW_E_FORMAT, "tile longer than possible");
+    if (h.kind == LW_BF16_EXP) {
+        const uint32_t *vs = reinterpret_cast<const uint32_t *>(img + h.off[LW_REG_VB_START]);
+        const uint32_t *vb = reinterpret_cast<const uint32_t *>(img + h.off[LW_REG_VB_BITS]);
+        if (vs[0] != 0) return lw_fail(LW_E_FORMAT, "vb_start[0] != 0");
+        for (int64_t i = 0; i < h.n_tiles; i++) {
+            uint32_t pc = 0;
+            for (int j = 0; j < 8; j++) pc += (uint32_t)__builtin_popcount(vb[i * 8 + j]);
+            if (vs[i + 1] != vs[i] + pc) return lw_fail(LW_E_FORMAT, "vb_start inconsistent");
+        }
+        if ((int64_t)vs[h.n_tiles] != h.n_verbatim) return lw_fail(LW_E_FORMAT, "verbatim count");
+        if (h.n_pal < 1 || h.n_pal > 16 || nsym > h.n_pal) return lw_fail(LW_E_FORMAT, "palette size");
+    }
+    int32_t groups = (int32_t)((h.n_cb + LW_CB_PER_WG - 1) / LW_CB_PER_WG);
+    if (h.work_groups != groups) return lw_fail(LW_E_FORMAT, "workspace groups");
+    int64_t n_rows_wg = (h.n_rb + LW_RB_PER_WG - 1) / LW_RB_PER_WG;
+    if (groups > 1 && h.bytes[LW_REG_WORK] < lw_work_partial_bytes(groups, h.rows) + 4u * (uint64_t)n_rows_wg)
+        return lw_fail(LW_E_FORMAT, "workspace too small");
+    return LW_OK;
+}
+
+extern "C" lw_status lw_bundle_validate(const lw_bundle *b)
+{
+    if (!b) return lw_fail(LW_E_ARG, "bundle is null");
+    return validate_image(b->image.data(), b->image.size());
+}
+
+extern "C" lw_status lw_bundle_load(const void *image, size_t bytes, lw_bundle **out)
+{
+    if (!out) return lw_fail(LW_E_ARG, "out is null");
+    *out = nullptr;
+    if (!image) return lw_fail(LW_E_ARG, "image is null");
+    lw_status st = validate_image(static_cast<const uint8_t *>(image), bytes);
+    if (st) return st;
+    try {
+        std::unique_ptr<lw_bundle> b(new lw_bundle);
+        b->image.assign(static_cast<const uint8_t *>(image), static_cast<const uint8_t *>(image) + bytes);
+        // the workspace must start zeroed
+        lw_image_header h;
+        std::memcpy(&h, b->image.data(), sizeof(h));
+        if (h.bytes[LW_REG_WORK]) std::memset(b->image.data() + h.off[LW_REG_WORK], 0, h.bytes[LW_REG_WORK]);
+        *out = b.release();
+        return LW_OK;
+    } catch (const std::bad_alloc &) {
+        return lw_fail(LW_E_NOMEM, "host allocation failed");
+    }
+}
+
+extern "C" lw_status lw_bundle_get_info(const lw_bundle *b, lw_bundle_info *info)
+{
+    if (!b || !info) return lw_fail(LW_E_ARG, "null argument");
+    lw_image_header h;
+    std::memcpy(&h, b->image.data(), sizeof(h));
+    std::memset(info, 0, sizeof(*info));
+    info->kind = h.kind;
+    info->bits = h.bits;
+    info->rows = h.rows;
+    info->cols = h.cols;
+    info->n_tiles = h.n_tiles;
+    info->n_rb = h.n_rb;
+    info->n_cb = h.n_cb;
+    info->symbols_per_lane = h.spl;
+    info->n_symbols = h.n_sym;
+    info->min_len = h.min_len;
+    info->max_len = h.max_len;
+    info->max_words = h.max_words;
+    info->n_palette = h.n_pal;
+    info->n_verbatim = h.n_verbatim;
+    const lw_table *t = reinterpret_cast<const lw_table *>(b->image.data() + h.off[LW_REG_TABLE]);
+    for (int L = 0; L < 12; L++) info->count_per_len[L] = t->count[L];
+    for (int r = 0; r < LW_REG_COUNT; r++) {
+        info->region_offset[r] = h.off[r];
+        info->region_bytes[r] = h.bytes[r];
+    }
+    info->image_bytes = b->image.size();
+    info->coded_bytes = h.coded_bytes;
+    info->twin_bytes = h.twin_bytes;
+    return LW_OK;
+}
+
+extern "C" lw_status lw_bundle_image(const lw_bundle *b, const void **image, size_t *bytes)
+{
+    if (!b || !image || !bytes) return lw_fail(LW_E_ARG, "null argument");
+    *image = b->image.data();
+    *bytes = b->image.size();
+    return LW_OK;
+}
+
+extern "C" lw_status lw_bundle_region(const lw_bundle *b, int r, const void **ptr, size_t *bytes)
+{
+    if (!b || !ptr || !bytes) return lw_fail(LW_E_ARG, "null argument");
+    if (r < 0 || r >= LW_REG_COUNT) return lw_fail(LW_E_ARG, "no such region");
+    lw_image_header h;
+    std::memcpy(&h, b->image.data(), sizeof(h));
+    *ptr = h.bytes[r] ? b->image.data() + h.off[r] : nullptr;
+    *bytes = h.bytes[r];
+    return LW_OK;
+}
+
+extern "C" void lw_bundle_free(lw_bundle *b) { delete b; }
+
+extern "C" lw_status lw_twin_build(const uint8_t *codes, int bits, int64_t rows, int64_t cols,
+                                   const uint16_t *d, const uint16_t *m, uint8_t *twin, uint32_t *dm)
+{
+    if (!codes || !d || !m || !twin || !dm) return lw_fail(LW_E_ARG, "null argument");
+    if (bits != 4) return lw_fail(LW_E_ARG, "twin supports 4-bit codes");
+    if (rows <= 0 || cols <= 0 || cols % 256) return lw_fail(LW_E_SHAPE, "cols must be a multiple of 256");
+    std::atomic<int> bad(0);
+    parallel_for(rows, [&](int64_t r) {
+        const uint8_t *q = codes + r * cols;
+        uint8_t *o = twin + r * (cols / 2);
+        for (int64_t c = 0; c < cols; c += 2) {
+            if ((q[c] | q[c + 1]) > 15) bad = 1;
+            o[c / 2] = (uint8_t)((q[c] & 15) | (q[c + 1] << 4));
+        }
+        for (int64_t s = 0; s < cols / 256; s++)
+            dm[r * (cols / 256) + s] = (uint32_t)d[r * (cols / 256) + s] | ((uint32_t)m[r * (cols / 256) + s] << 16);
+    });
+    if (bad) return lw_fail(LW_E_ARG, "code >= 16");
+    return LW_OK;
+}

@@ -1,0 +1,84 @@
+/*
+ * lw_internal.h -- bundle image layout shared by the host builder and the
+ * device runtime of liblw (not part of the public ABI).
+ *
+ * An image is one little-endian byte array: a 512-byte header followed by the
+ * regions of lw_region, each starting on a 256-byte boundary, so that one
+ * device buffer holds a whole matrix and every region is aligned for wide
+ * loads.
+ */
+#ifndef LW_INTERNAL_H
+#define LW_INTERNAL_H
+
+#include <stdint.h>
+#include "lw.h"
+
+#define LW_MAGIC 0x3142574Cu       /* "LWB1" */
+#define LW_VERSION 1u
+#define LW_MAXLEN 11               /* "LazyWeights", 2 . Code them: 11-bit codes */
+#define LW_TILE_ROWS 64            /* a 64x256 tile is 32 lanes of two rows */
+#define LW_TILE_COLS 256
+#define LW_LANES 32
+#define LW_ALIGN 256
+#define LW_HEADER_BYTES 512
+#define LW_BATCH_MAX 16
+#define LW_CB_PER_WG 4             /* column blocks one workgroup covers (one per wave) */
+#define LW_RB_PER_WG 2             /* row bands one workgroup covers (two half-waves) */
+
+typedef struct {
+    uint32_t magic;
+    uint32_t version;
+    int32_t kind;
+    int32_t bits;
+    int64_t rows;
+    int64_t cols;
+    int64_t n_tiles;
+    int32_t n_rb;
+    int32_t n_cb;
+    int32_t spl;                   /* symbols per lane */
+    int32_t n_sym;
+    int32_t min_len;
+    int32_t max_len;
+    int32_t max_words;
+    int32_t n_pal;
+    int64_t n_verbatim;
+    int32_t work_groups;           /* split-column groups the workspace is sized for */
+    int32_t reserved0;
+    uint64_t coded_bytes;
+    uint64_t twin_bytes;
+    uint64_t off[LW_REG_COUNT];
+    uint64_t bytes[LW_REG_COUNT];
+} lw_image_header;
+
+/* LW_REG_TABLE: the canonical decoder table of the matrix. */
+typedef struct {
+    uint16_t count[12];
+    uint16_t first[12];
+    uint16_t limit[12];            /* (first + count) << (11 - L): 11-bit peek bound */
+    uint16_t offset[12];
+    uint16_t sym_sorted[256];
+} lw_table;
+
+/* LW_REG_GPUTAB: tables derived from lw_table for the kernels.
+ * With r = number of lengths L in [min_len, max_len) whose limit is <= the
+ * peek, the code length is min_len + r. */
+typedef struct {
+    uint32_t limlj[16];            /* limit[min_len + i] << 21, i < max_len - min_len; else ~0 */
+    uint32_t len[16];              /* code length for comparison count r */
+    int32_t base[16];              /* offset[len] - first[len] for comparison count r */
+    uint32_t payload[256];         /* per canonical index: Q4 half2(q_even, q_odd); Q6 half2(q, 0);
+                                      bf16: exponent << 7 (low bf16 of a pair) */
+    uint32_t payload_hi[256];      /* Q6 half2(0, q); bf16 exponent << 23 (high bf16 of a pair) */
+    uint32_t symval[256];          /* the symbol itself (decode-only) */
+} lw_gputab;
+
+static inline uint64_t lw_align_up(uint64_t v) { return (v + LW_ALIGN - 1) & ~(uint64_t)(LW_ALIGN - 1); }
+
+/* workspace layout: partial sums [work_groups][LW_BATCH_MAX][rows] f32, then
+ * one u32 arrival counter per workgroup row (rows / (64 * LW_RB_PER_WG), rounded up) */
+static inline uint64_t lw_work_partial_bytes(int32_t groups, int64_t rows)
+{
+    return (uint64_t)groups * LW_BATCH_MAX * (uint64_t)rows * 4u;
+}
+
+#endif

@@ -1,0 +1,149 @@
+// runtime.hip -- device side of the liblw C ABI: upload of a bundle image
+// into caller-owned device memory, and the enqueue-only entry points that
+// pick and launch the gfx950 kernels.  The library never allocates device
+// memory; PyTorch (or any caller) owns buffers and streams.
+#include <cstring>
+#include <memory>
+#include <string>
+
+#include "kernels.h"
+
+lw_status lw_fail(lw_status s, const std::string &msg);   // bundle.cpp
+
+struct lw_dev_bundle {
+    lw_image_header h;
+    lw_gputab tab;
+    uint8_t *base;
+};
+
+static lw_status hip_fail(hipError_t e, const char *what)
+{
+    return lw_fail(LW_E_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+template <class T>
+static T *dev_region(const lw_dev_bundle *db, int r)
+{
+    return db->h.bytes[r] ? reinterpret_cast<T *>(db->base + db->h.off[r]) : nullptr;
+}
+
+extern "C" lw_status lw_bundle_image(const lw_bundle *b, const void **image, size_t *bytes);
+extern "C" lw_status lw_bundle_validate(const lw_bundle *b);
+
+extern "C" lw_status lw_bundle_upload(const lw_bundle *b, void *dev_buf, size_t dev_bytes, void *stream,
+                                      lw_dev_bundle **out)
+{
+    if (!out) return lw_fail(LW_E_ARG, "out is null");
+    *out = nullptr;
+    if (!b || !dev_buf) return lw_fail(LW_E_ARG, "null bundle or device buffer");
+    lw_status st = lw_bundle_validate(b);
+    if (st) return st;
+    const void *img = nullptr;
+    size_t bytes = 0;
+    lw_bundle_image(b, &img, &bytes);
+    if (dev_bytes < bytes) return lw_fail(LW_E_ARG, "device buffer smaller than the bundle image");
+    if (reinterpret_cast<uintptr_t>(dev_buf) % LW_ALIGN) return lw_fail(LW_E_ARG, "device buffer not 256-byte aligned");
+    hipError_t e = hipMemcpyAsync(dev_buf, img, bytes, hipMemcpyHostToDevice, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    std::unique_ptr<lw_dev_bundle> db(new lw_dev_bundle);
+    std::memcpy(&db->h, img, sizeof(db->h));
+    std::memcpy(&db->tab, static_cast<const uint8_t *>(img) + db->h.off[LW_REG_GPUTAB], sizeof(db->tab));
+    db->base = static_cast<uint8_t *>(dev_buf);
+    *out = db.release();
+    return LW_OK;
+}
+
+extern "C" void lw_dev_bundle_free(lw_dev_bundle *db) { delete db; }
+
+static KArgs make_args(const lw_dev_bundle *db)
+{
+    KArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.words = dev_region<uint32_t>(db, LW_REG_WORDS);
+    a.tile_off = dev_region<uint32_t>(db, LW_REG_TILE_OFF);
+    a.dm = dev_region<uint32_t>(db, LW_REG_DM);
+    a.tab = dev_region<lw_gputab>(db, LW_REG_GPUTAB);
+    a.sm = dev_region<uint32_t>(db, LW_REG_SM);
+    a.vb_bits = dev_region<uint32_t>(db, LW_REG_VB_BITS);
+    a.vb_start = dev_region<uint32_t>(db, LW_REG_VB_START);
+    a.verbatim = dev_region<uint16_t>(db, LW_REG_VERBATIM);
+    uint8_t *work = dev_region<uint8_t>(db, LW_REG_WORK);
+    a.part = reinterpret_cast<float *>(work);
+    a.count = work ? reinterpret_cast<uint32_t *>(work + lw_work_partial_bytes(db->h.work_groups, db->h.rows)) : nullptr;
+    a.rows = db->h.rows;
+    a.cols = db->h.cols;
+    a.n_rb = db->h.n_rb;
+    a.n_cb = db->h.n_cb;
+    a.groups = db->h.work_groups;
+    a.max_words = db->h.max_words;
+    a.min_len = db->h.min_len;
+    for (int i = 0; i < 10; i++) a.lim[i] = db->tab.limlj[i];
+    return a;
+}
+
+static int ncmp_of(const lw_dev_bundle *db) { return db->h.max_len - db->h.min_len; }
+
+extern "C" lw_status lw_gemv(const lw_dev_bundle *db, const void *x, float *y, int batch, void *stream)
+{
+    if (!db || !x || !y) return lw_fail(LW_E_ARG, "null argument");
+    if (batch < 1 || batch > LW_BATCH_MAX) return lw_fail(LW_E_ARG, "batch must be in 1..16");
+    if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 16)
+        return lw_fail(LW_E_ARG, "x and y must be 16-byte aligned");
+    KArgs a = make_args(db);
+    a.x = static_cast<const uint16_t *>(x);
+    a.y = y;
+    a.batch = batch;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (db->h.kind == LW_BF16_EXP) {
+        a.pal0 = db->tab.payload[0] >> 7;
+        e = lw_launch_gemv_bf16(a, ncmp_of(db), batch, s);
+    } else if (batch < 8) {
+        e = lw_launch_gemv_q(a, db->h.kind, ncmp_of(db), batch, s);
+    } else {
+        e = lw_launch_gemv_mfma(a, db->h.kind, ncmp_of(db), batch, s);
+    }
+    if (e == hipErrorNotSupported) return lw_fail(LW_E_UNSUPPORTED, "no kernel for this kind and batch");
+    if (e != hipSuccess) return hip_fail(e, "gemv launch");
+    return LW_OK;
+}
+
+extern "C" lw_status lw_decode_only(const lw_dev_bundle *db, void *out, size_t out_bytes, uint32_t *lane_bits,
+                                    void *stream)
+{
+    if (!db || !out) return lw_fail(LW_E_ARG, "null argument");
+    const uint64_t need = db->h.kind == LW_Q4_PAIR ? (uint64_t)db->h.rows * db->h.cols / 2
+                          : db->h.kind == LW_Q6_SINGLE ? (uint64_t)db->h.rows * db->h.cols
+                                                       : (uint64_t)db->h.rows * db->h.cols * 2;
+    if (out_bytes < need) return lw_fail(LW_E_ARG, "output buffer too small");
+    if (reinterpret_cast<uintptr_t>(out) % 16) return lw_fail(LW_E_ARG, "output must be 16-byte aligned");
+    KArgs a = make_args(db);
+    a.out = out;
+    a.lane_bits = lane_bits;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (db->h.kind == LW_BF16_EXP) {
+        a.pal0 = db->tab.payload[0] >> 7;
+        e = lw_launch_decode_bf16(a, ncmp_of(db), s);
+    } else {
+        e = lw_launch_decode_q(a, db->h.kind, ncmp_of(db), s);
+    }
+    if (e == hipErrorNotSupported) return lw_fail(LW_E_UNSUPPORTED, "no decode kernel for this kind");
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return LW_OK;
+}
+
+extern "C" lw_status lw_twin_gemv(const void *twin, const uint32_t *dm, int bits, int64_t rows, int64_t cols,
+                                  const void *x, float *y, int batch, void *stream)
+{
+    if (!twin || !dm || !x || !y) return lw_fail(LW_E_ARG, "null argument");
+    if (bits != 4) return lw_fail(LW_E_ARG, "twin supports 4-bit codes");
+    if (rows <= 0 || cols <= 0 || cols % 256) return lw_fail(LW_E_SHAPE, "cols must be a multiple of 256");
+    if (batch < 1 || batch > LW_BATCH_MAX) return lw_fail(LW_E_ARG, "batch must be in 1..16");
+    if (reinterpret_cast<uintptr_t>(twin) % 16 || reinterpret_cast<uintptr_t>(x) % 16)
+        return lw_fail(LW_E_ARG, "twin and x must be 16-byte aligned");
+    hipError_t e = lw_launch_twin(static_cast<const uint8_t *>(twin), dm, rows, cols,
+                                  static_cast<const uint16_t *>(x), y, batch, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "twin launch");
+    return LW_OK;
+}

@@ -1,0 +1,245 @@
+"""Python binding of liblw (include/lw.h): argument marshalling only.
+
+Every function has the name of the C entry point it calls.  Host arrays are
+numpy; device memory and streams come from PyTorch (a uint8 CUDA tensor for a
+bundle image, fp16/bf16/fp32 CUDA tensors for x and y, the current stream).
+All compute runs in the HIP kernels of liblw; if the library is missing the
+import of this module fails.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblw.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "lw.h")
+
+LW_OK, LW_E_ARG, LW_E_SHAPE, LW_E_TABLE, LW_E_FORMAT, LW_E_NOMEM, LW_E_DEVICE, LW_E_UNSUPPORTED = range(8)
+LW_Q4_PAIR, LW_Q6_SINGLE, LW_BF16_EXP = 1, 2, 3
+(LW_REG_TABLE, LW_REG_GPUTAB, LW_REG_TILE_OFF, LW_REG_WORDS, LW_REG_DM, LW_REG_PALETTE, LW_REG_SM,
+ LW_REG_VB_BITS, LW_REG_VB_START, LW_REG_VERBATIM, LW_REG_WORK, LW_REG_COUNT) = range(12)
+
+
+class LwError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"lw status {status}: {msg}")
+        self.status = status
+
+
+class lw_bundle_info(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("bits", C.c_int32), ("rows", C.c_int64), ("cols", C.c_int64),
+                ("n_tiles", C.c_int64), ("n_rb", C.c_int32), ("n_cb", C.c_int32),
+                ("symbols_per_lane", C.c_int32), ("n_symbols", C.c_int32), ("min_len", C.c_int32),
+                ("max_len", C.c_int32), ("max_words", C.c_int32), ("n_palette", C.c_int32),
+                ("n_verbatim", C.c_int64), ("count_per_len", C.c_uint16 * 12),
+                ("region_offset", C.c_uint64 * LW_REG_COUNT), ("region_bytes", C.c_uint64 * LW_REG_COUNT),
+                ("image_bytes", C.c_uint64), ("coded_bytes", C.c_uint64), ("twin_bytes", C.c_uint64)]
+
+
+def _load():
+    # Device memory and streams come from PyTorch, so liblw must run on the
+    # same HIP runtime instance as torch: importing torch first maps torch's
+    # libamdhip64, which then satisfies liblw's dependency by its soname.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m decode_gemv_amd.build`")
+    L = C.CDLL(LIB_PATH)
+    P, i64, i32, st = C.c_void_p, C.c_int64, C.c_int, C.c_int
+    sig = {
+        "lw_bundle_build_q": (st, [i32, i64, i64, P, P, P, C.POINTER(P)]),
+        "lw_bundle_build_bf16": (st, [i64, i64, P, C.POINTER(P)]),
+        "lw_bundle_load": (st, [P, C.c_size_t, C.POINTER(P)]),
+        "lw_bundle_validate": (st, [P]),
+        "lw_bundle_get_info": (st, [P, C.POINTER(lw_bundle_info)]),
+        "lw_bundle_image": (st, [P, C.POINTER(P), C.POINTER(C.c_size_t)]),
+        "lw_bundle_region": (st, [P, i32, C.POINTER(P), C.POINTER(C.c_size_t)]),
+        "lw_bundle_free": (None, [P]),
+        "lw_twin_build": (st, [P, i32, i64, i64, P, P, P, P]),
+        "lw_bundle_upload": (st, [P, P, C.c_size_t, P, C.POINTER(P)]),
+        "lw_dev_bundle_free": (None, [P]),
+        "lw_gemv": (st, [P, P, P, i32, P]),
+        "lw_decode_only": (st, [P, P, C.c_size_t, P, P]),
+        "lw_twin_gemv": (st, [P, P, i32, i64, i64, P, P, i32, P]),
+        "lw_status_str": (C.c_char_p, [st]),
+        "lw_last_error": (C.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+_L = _load()
+
+
+def lib():
+    return _L
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/lw.h declares."""
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(lw_[a-z0-9_]+)\s*\(", txt)))
+
+
+def _check(status: int):
+    if status != LW_OK:
+        raise LwError(status, (_L.lw_last_error() or b"").decode())
+
+
+def _np(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(C.c_void_p)
+
+
+# ---------------------------------------------------------------- host bundles
+
+class Bundle:
+    """Owner of a host lw_bundle pointer."""
+
+    def __init__(self, ptr: int):
+        self.ptr = C.c_void_p(ptr)
+
+    def __del__(self):
+        if getattr(self, "ptr", None) and self.ptr.value:
+            _L.lw_bundle_free(self.ptr)
+            self.ptr = None
+
+
+def lw_bundle_build_q(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray) -> Bundle:
+    rows, cols = codes.shape
+    codes, pc = _np(codes, np.uint8)
+    d, pd = _np(d, np.uint16)
+    m, pm = _np(m, np.uint16)
+    out = C.c_void_p()
+    _check(_L.lw_bundle_build_q(kind, rows, cols, pc, pd, pm, C.byref(out)))
+    return Bundle(out.value)
+
+
+def lw_bundle_build_bf16(w: np.ndarray) -> Bundle:
+    rows, cols = w.shape
+    w, pw = _np(w, np.uint16)
+    out = C.c_void_p()
+    _check(_L.lw_bundle_build_bf16(rows, cols, pw, C.byref(out)))
+    return Bundle(out.value)
+
+
+def lw_bundle_load(image: np.ndarray) -> Bundle:
+    image, p = _np(image, np.uint8)
+    out = C.c_void_p()
+    _check(_L.lw_bundle_load(p, image.nbytes, C.byref(out)))
+    return Bundle(out.value)
+
+
+def lw_bundle_validate(b: Bundle) -> None:
+    _check(_L.lw_bundle_validate(b.ptr))
+
+
+def lw_bundle_get_info(b: Bundle) -> dict:
+    info = lw_bundle_info()
+    _check(_L.lw_bundle_get_info(b.ptr, C.byref(info)))
+    d = {k: getattr(info, k) for k, _ in lw_bundle_info._fields_}
+    for k in ("count_per_len", "region_offset", "region_bytes"):
+        d[k] = list(d[k])
+    return d
+
+
+def lw_bundle_image(b: Bundle) -> np.ndarray:
+    p, n = C.c_void_p(), C.c_size_t()
+    _check(_L.lw_bundle_image(b.ptr, C.byref(p), C.byref(n)))
+    return np.ctypeslib.as_array((C.c_uint8 * n.value).from_address(p.value)).copy()
+
+
+def lw_bundle_region(b: Bundle, region: int, dtype=np.uint8) -> np.ndarray:
+    p, n = C.c_void_p(), C.c_size_t()
+    _check(_L.lw_bundle_region(b.ptr, region, C.byref(p), C.byref(n)))
+    if not n.value:
+        return np.zeros(0, dtype=dtype)
+    raw = np.ctypeslib.as_array((C.c_uint8 * n.value).from_address(p.value)).copy()
+    return raw.view(dtype)
+
+
+def lw_twin_build(codes: np.ndarray, bits: int, d: np.ndarray, m: np.ndarray):
+    rows, cols = codes.shape
+    codes, pc = _np(codes, np.uint8)
+    d, pd = _np(d, np.uint16)
+    m, pm = _np(m, np.uint16)
+    twin = np.zeros((rows, cols // 2), np.uint8)
+    dm = np.zeros((rows, cols // 256), np.uint32)
+    _check(_L.lw_twin_build(pc, bits, rows, cols, pd, pm, twin.ctypes.data_as(C.c_void_p),
+                            dm.ctypes.data_as(C.c_void_p)))
+    return twin, dm
+
+
+def lw_status_str(s: int) -> str:
+    return _L.lw_status_str(s).decode()
+
+
+def lw_last_error() -> str:
+    return (_L.lw_last_error() or b"").decode()
+
+
+# ---------------------------------------------------------------- device side
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dptr(t, what):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+        raise LwError(LW_E_ARG, f"{what} must be a contiguous device tensor")
+    return C.c_void_p(t.data_ptr())
+
+
+class DevBundle:
+    """Host-side descriptor of an uploaded bundle; keeps its buffer alive."""
+
+    def __init__(self, ptr: int, buf, info: dict):
+        self.ptr = C.c_void_p(ptr)
+        self.buf = buf
+        self.info = info
+
+    def __del__(self):
+        if getattr(self, "ptr", None) and self.ptr.value:
+            _L.lw_dev_bundle_free(self.ptr)
+            self.ptr = None
+
+
+def lw_bundle_upload(b: Bundle, dev_buf, stream=None) -> DevBundle:
+    out = C.c_void_p()
+    _check(_L.lw_bundle_upload(b.ptr, _dptr(dev_buf, "dev_buf"), dev_buf.numel() * dev_buf.element_size(),
+                               _stream(stream), C.byref(out)))
+    return DevBundle(out.value, dev_buf, lw_bundle_get_info(b))
+
+
+def lw_gemv(db: DevBundle, x, y, batch: int, stream=None) -> None:
+    _check(_L.lw_gemv(db.ptr, _dptr(x, "x"), _dptr(y, "y"), batch, _stream(stream)))
+
+
+def lw_decode_only(db: DevBundle, out, lane_bits=None, stream=None) -> None:
+    lb = _dptr(lane_bits, "lane_bits") if lane_bits is not None else None
+    _check(_L.lw_decode_only(db.ptr, _dptr(out, "out"), out.numel() * out.element_size(), lb, _stream(stream)))
+
+
+def lw_twin_gemv(twin, dm, bits: int, rows: int, cols: int, x, y, batch: int, stream=None) -> None:
+    _check(_L.lw_twin_gemv(_dptr(twin, "twin"), _dptr(dm, "dm"), bits, rows, cols, _dptr(x, "x"), _dptr(y, "y"),
+                           batch, _stream(stream)))
+
+
+# ---------------------------------------------------------------- conveniences
+
+def upload(b: Bundle, device="cuda"):
+    """Allocate a device buffer of the image size with torch and upload into it."""
+    import torch
+    info = lw_bundle_get_info(b)
+    buf = torch.empty(int(info["image_bytes"]), dtype=torch.uint8, device=device)
+    return lw_bundle_upload(b, buf)

@@ -1,0 +1,198 @@
+/*
+ * lw.h -- C ABI of the MI355X (gfx950) library for matrix-vector products
+ * over losslessly entropy-coded LLM weights.
+ *
+ * The method: "LazyWeights: Decode-on-Demand Edge LLMs", section "2 . Code
+ * them" (one length-limited Huffman table with 11-bit codes per matrix;
+ * 64x256 tiles of 32 lanes of two rows; lanes' 32-bit words interleaved;
+ * 4-bit codes coded in pairs; scales and minimums kept raw), section
+ * "3 . Decode on demand" and Fig. 3 (a lane compares an 11-bit peek against
+ * per-length limits, adds the length's offset to index the symbol table and
+ * shifts by the length; per-tile lane offsets let any tile start on its own),
+ * and the runtime paragraph under Fig. 3 (software decode fused into GEMV; a
+ * decode-free fixed-width "twin").  The bf16 variant follows "Unweight:
+ * Compressing LLM Weights for Faster Inference", sections "Understanding BF16
+ * weight structure" and "The exponent's exploitable redundancy" (only the
+ * exponent byte is Huffman coded, over the matrix's top-16 palette; a 64-weight
+ * row segment with an exponent outside the palette is stored verbatim; sign and
+ * mantissa stay raw).  Dequantisation w = d*q - m per 256-weight super-block is
+ * the grouped-storage rule of "Software-Defined Bandwidth Expansion", IV-A.
+ *
+ * Conventions for every entry point:
+ *  - Every function returns lw_status; nothing throws across the ABI.  On an
+ *    error lw_last_error() returns a thread-local detail string.
+ *  - Host pointers are plain host memory; "device" pointers are HIP device
+ *    addresses on the current device (PyTorch allocates them).  The library
+ *    never allocates device memory and never frees caller memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  GPU
+ *    entry points only enqueue work; errors found while enqueueing are
+ *    returned, faults inside kernels surface at the caller's next sync.
+ *  - All multi-byte values are little-endian; fp16 and bf16 values are passed
+ *    as their 16-bit patterns.
+ */
+#ifndef LW_H
+#define LW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LW_OK = 0,
+    LW_E_ARG = 1,          /* null pointer, out-of-range value, buffer too small, misalignment */
+    LW_E_SHAPE = 2,        /* rows not a multiple of 64 or cols not a multiple of 256 */
+    LW_E_TABLE = 3,        /* code table invalid: a length above 11 or a Kraft violation */
+    LW_E_FORMAT = 4,       /* bundle image corrupt or inconsistent */
+    LW_E_NOMEM = 5,        /* host allocation failed */
+    LW_E_DEVICE = 6,       /* a HIP call failed */
+    LW_E_UNSUPPORTED = 7   /* valid request that this build does not implement */
+} lw_status;
+
+typedef enum {
+    LW_Q4_PAIR = 1,        /* 4-bit codes, coded in pairs: 256-symbol alphabet, 256 symbols per lane */
+    LW_Q6_SINGLE = 2,      /* 6-bit codes, coded singly: 64-symbol alphabet, 512 symbols per lane */
+    LW_BF16_EXP = 3        /* bf16 weights, exponent palette index coded singly: 16 symbols, 512 per lane */
+} lw_kind;
+
+typedef struct lw_bundle lw_bundle;          /* host bundle: opaque, owned by the library */
+typedef struct lw_dev_bundle lw_dev_bundle;  /* host-side descriptor of an uploaded bundle */
+
+/* Region identifiers for lw_bundle_region (the image layout of a bundle). */
+typedef enum {
+    LW_REG_TABLE = 0,      /* canonical table: u16 count[12], first[12], limit[12], offset[12], sym_sorted[256] */
+    LW_REG_GPUTAB = 1,     /* tables derived for the kernels (not part of the coded format) */
+    LW_REG_TILE_OFF = 2,   /* u32 [n_tiles+1] word offset of each tile block */
+    LW_REG_WORDS = 3,      /* u32 interleaved lane words; tile t's word j of lane l at tile_off[t] + 32j + l */
+    LW_REG_DM = 4,         /* u32 [n_tiles][64] = d | m << 16 (fp16 bits), Q4/Q6 only */
+    LW_REG_PALETTE = 5,    /* u8 [16] exponents, index 0 the most frequent (bf16 only) */
+    LW_REG_SM = 6,         /* u32 [n_tiles][4096] sign+mantissa bytes, lane-interleaved (bf16 only) */
+    LW_REG_VB_BITS = 7,    /* u32 [n_tiles][8], bit 4i+s marks segment s of tile row i verbatim (bf16) */
+    LW_REG_VB_START = 8,   /* u32 [n_tiles+1] verbatim segments before each tile (bf16) */
+    LW_REG_VERBATIM = 9,   /* u16 [n_verbatim][64] raw bf16 segments (bf16) */
+    LW_REG_WORK = 10,      /* device workspace of the split-column reduction (zero in the image) */
+    LW_REG_COUNT = 11
+} lw_region;
+
+typedef struct {
+    int32_t kind;              /* lw_kind */
+    int32_t bits;              /* 4, 6 or 16 */
+    int64_t rows, cols;
+    int64_t n_tiles;           /* (rows/64) * (cols/256), row-band-major */
+    int32_t n_rb, n_cb;        /* row bands (rows/64) and column blocks (cols/256) */
+    int32_t symbols_per_lane;  /* 256 (Q4) or 512 (Q6, BF16) */
+    int32_t n_symbols;         /* symbols with a code */
+    int32_t min_len, max_len;  /* shortest and longest code length used */
+    int32_t max_words;         /* longest lane of any tile, in 32-bit words */
+    int32_t n_palette;         /* bf16: distinct exponents in the palette */
+    int64_t n_verbatim;        /* bf16: verbatim 64-weight segments */
+    uint16_t count_per_len[12];/* index L = 1..11 */
+    uint64_t region_offset[LW_REG_COUNT]; /* byte offset of each region inside the image */
+    uint64_t region_bytes[LW_REG_COUNT];  /* byte size of each region (0 if absent) */
+    uint64_t image_bytes;      /* size of the device image = bytes lw_bundle_upload copies/needs */
+    uint64_t coded_bytes;      /* bytes a fused GEMV must read for the weights: words + tile_off +
+                                  table + dm (Q4/Q6) or + sm + vb_bits + vb_start + verbatim +
+                                  palette (bf16); excludes x, y and the workspace */
+    uint64_t twin_bytes;       /* the fixed-width equivalent: rows*cols*bits/8 + rows*cols/256*4
+                                  (bf16: rows*cols*2, the dense matrix) */
+} lw_bundle_info;
+
+/* ---------------------------------------------------------------- host side */
+
+/* Build a bundle from quantised codes ("2 . Code them").
+ *   kind  : LW_Q4_PAIR or LW_Q6_SINGLE
+ *   codes : host [rows][cols] row-major, one code per byte (< 16 or < 64)
+ *   d, m  : host fp16 bits [rows][cols/256]: scale and minimum of each
+ *           256-weight super-block; the weight is w = d*q - m
+ * The inputs are copied; no caller pointer is retained.  *out receives a
+ * library-owned bundle to free with lw_bundle_free.
+ * Errors: LW_E_ARG (null, bad kind, a code out of range), LW_E_SHAPE,
+ * LW_E_NOMEM. */
+lw_status lw_bundle_build_q(int kind, int64_t rows, int64_t cols, const uint8_t *codes,
+                            const uint16_t *d, const uint16_t *m, lw_bundle **out);
+
+/* Build a bf16 exponent-coded bundle ("Unweight", exponent palette and
+ * verbatim rows).  w: host bf16 bits [rows][cols].  Errors as above. */
+lw_status lw_bundle_build_bf16(int64_t rows, int64_t cols, const uint16_t *w, lw_bundle **out);
+
+/* Re-create a bundle from an image (as returned by lw_bundle_image); the image
+ * is copied and validated.  Errors: LW_E_ARG, LW_E_FORMAT, LW_E_TABLE. */
+lw_status lw_bundle_load(const void *image, size_t bytes, lw_bundle **out);
+
+/* Check every invariant of a bundle: header, region bounds, code table (Kraft
+ * sum, lengths <= 11, limits), tile offsets and the longest lane.
+ * Errors: LW_E_FORMAT, LW_E_TABLE. */
+lw_status lw_bundle_validate(const lw_bundle *b);
+
+lw_status lw_bundle_get_info(const lw_bundle *b, lw_bundle_info *info);
+
+/* Pointer to the bundle's image (valid until lw_bundle_free) and its size. */
+lw_status lw_bundle_image(const lw_bundle *b, const void **image, size_t *bytes);
+
+/* Pointer to one region of the image and its size in bytes. */
+lw_status lw_bundle_region(const lw_bundle *b, int region, const void **ptr, size_t *bytes);
+
+void lw_bundle_free(lw_bundle *b);
+
+/* Fixed-width "twin" of a quantised matrix (the decode-free stand-in of the
+ * runtime paragraph under "LazyWeights" Fig. 3; grouped packing of "Software-
+ * Defined Bandwidth Expansion" IV-A):
+ *   bits = 4: packed [rows][cols/2] bytes, low nibble = even column.
+ * dm_out receives [rows][cols/256] u32 = d | m << 16.
+ * Errors: LW_E_ARG (null, bits other than 4, code >= 16), LW_E_SHAPE. */
+lw_status lw_twin_build(const uint8_t *codes, int bits, int64_t rows, int64_t cols,
+                        const uint16_t *d, const uint16_t *m, uint8_t *twin_out, uint32_t *dm_out);
+
+/* ---------------------------------------------------------------- device side */
+
+/* Copy a bundle image into caller-owned device memory dev_buf (at least
+ * info.image_bytes bytes, 256-byte aligned) on `stream`, and zero its
+ * workspace.  *out receives a host-side descriptor (free with
+ * lw_dev_bundle_free; dev_buf must outlive it).  The host bundle may be freed
+ * once the stream has passed the copy.
+ * Errors: LW_E_ARG (null, buffer too small or misaligned), LW_E_DEVICE. */
+lw_status lw_bundle_upload(const lw_bundle *b, void *dev_buf, size_t dev_bytes, void *stream,
+                           lw_dev_bundle **out);
+
+void lw_dev_bundle_free(lw_dev_bundle *db);
+
+/* y = W x for an uploaded bundle, decoding the weights on chip (fused decode +
+ * dequantise + dot product; HBM moves only coded bytes).
+ *   x : device [batch][cols], fp16 (Q4/Q6) or bf16 (BF16) bits, 16-byte aligned
+ *   y : device [batch][rows] fp32, overwritten, 16-byte aligned
+ *   1 <= batch <= 16; batch >= 8 uses the matrix-core (MFMA) kernel.
+ * The split-column reduction uses the bundle's workspace: calls on one
+ * uploaded bundle must not overlap in time (use one stream per bundle).
+ * Summation order is fixed, so results are deterministic.
+ * Errors: LW_E_ARG, LW_E_UNSUPPORTED, LW_E_DEVICE. */
+lw_status lw_gemv(const lw_dev_bundle *db, const void *x, float *y, int batch, void *stream);
+
+/* Decode only: restore the fixed-width codes ("3 . Decode on demand": the unit
+ * restores the packed codes).
+ *   Q4  : out [rows][cols/2] bytes, low nibble = even column (the twin layout)
+ *   Q6  : out [rows][cols] bytes, one code each
+ *   BF16: out [rows][cols] u16, the reconstructed bf16 weights
+ *   lane_bits: optional device u32 [n_tiles*32] receiving each lane's consumed
+ *              bit count (NULL to skip)
+ * Errors: LW_E_ARG (null, out_bytes too small), LW_E_DEVICE. */
+lw_status lw_decode_only(const lw_dev_bundle *db, void *out, size_t out_bytes, uint32_t *lane_bits,
+                         void *stream);
+
+/* GEMV over the fixed-width twin (ablation and latency bar).
+ *   twin : device packed codes as produced by lw_twin_build
+ *   dm   : device [rows][cols/256] u32
+ *   x    : device fp16 [batch][cols]; y: device fp32 [batch][rows], overwritten
+ * Errors: LW_E_ARG, LW_E_SHAPE, LW_E_DEVICE. */
+lw_status lw_twin_gemv(const void *twin, const uint32_t *dm, int bits, int64_t rows, int64_t cols,
+                       const void *x, float *y, int batch, void *stream);
+
+const char *lw_status_str(lw_status s);
+const char *lw_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LW_H */

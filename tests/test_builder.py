@@ -1,0 +1,169 @@
+"""CPU tests of the product's host side: the C ABI loads and exports what
+include/lw.h declares, the bundle builder produces exactly the oracle's
+format, and validation rejects corrupt images.  No GPU call is made."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import decode_gemv_amd as dg
+import oracle as O
+import synth
+
+
+def test_library_exports_every_declared_symbol():
+    names = dg.header_functions()
+    assert len(names) >= 16
+    lib = ctypes.CDLL(dg.lw.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _table_from_region(b):
+    t = dg.lw_bundle_region(b, dg.LW_REG_TABLE, np.uint16)
+    return dict(count=t[0:12], first=t[12:24], limit=t[24:36], offset=t[36:48], sym_sorted=t[48:])
+
+
+def _compare_q(kind, codes, d, m):
+    ob = O.build_bundle_q(kind, codes, d, m)
+    pb = dg.lw_bundle_build_q(kind, codes, d, m)
+    dg.lw_bundle_validate(pb)
+    info = dg.lw_bundle_get_info(pb)
+    tab = _table_from_region(pb)
+    for k in ("count", "first", "limit", "offset"):
+        assert np.array_equal(tab[k], ob["table"][k]), k
+    n = ob["table"]["n_sym"]
+    assert info["n_symbols"] == n
+    assert np.array_equal(tab["sym_sorted"][:n], ob["table"]["sym_sorted"])
+    assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_TILE_OFF, np.uint32), ob["tile_off"])
+    assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_WORDS, np.uint32), ob["words"])
+    assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_DM, np.uint32), ob["dm"])
+    W = np.diff(ob["tile_off"].astype(np.int64)) // 32
+    assert info["max_words"] == W.max()
+    assert info["coded_bytes"] == ob["words"].nbytes + ob["tile_off"].nbytes + ob["dm"].nbytes + 608
+    return pb, ob, info
+
+
+@pytest.mark.parametrize("kind,rows,cols,law,seed", [
+    (dg.LW_Q4_PAIR, 64, 256, "normal", 1), (dg.LW_Q4_PAIR, 192, 1024, "normal", 2),
+    (dg.LW_Q4_PAIR, 128, 768, "laplace", 3), (dg.LW_Q6_SINGLE, 128, 512, "normal", 4),
+    (dg.LW_Q4_PAIR, 64, 512, "uniform", 5), (dg.LW_Q4_PAIR, 64, 256, "const", 6),
+    (dg.LW_Q6_SINGLE, 64, 256, "uniform", 7), (dg.LW_Q6_SINGLE, 64, 256, "const", 8)])
+def test_builder_matches_oracle_bytes(kind, rows, cols, law, seed):
+    qmax = 15 if kind == dg.LW_Q4_PAIR else 63
+    codes, d, m, _ = synth.gen_q_custom(rows, cols, seed, qmax=qmax, law=law,
+                                        mu=7.5 if qmax == 15 else 31.5, scale=1.8 if qmax == 15 else 5.0)
+    _compare_q(kind, codes, d, m)
+
+
+def test_builder_matches_oracle_config_shapes():
+    for cfg in (1, 2, 3, 5):
+        mat = synth.CONFIGS[cfg][0]
+        kind = dg.LW_Q4_PAIR if mat.kind == "q4" else dg.LW_Q6_SINGLE
+        codes, d, m, _ = synth.gen_q(mat, rows=min(mat.rows, 256), cols=min(mat.cols, 4096))
+        _compare_q(kind, codes, d, m)
+
+
+@pytest.mark.parametrize("frac,seed", [(0.0, 11), (0.002, 12), (0.02, 13)])
+def test_builder_matches_oracle_bf16(frac, seed):
+    w, _ = synth.gen_bf16_custom(128, 512, seed, outlier_frac=frac)
+    ob = O.build_bundle_bf16(w)
+    pb = dg.lw_bundle_build_bf16(w)
+    dg.lw_bundle_validate(pb)
+    info = dg.lw_bundle_get_info(pb)
+    tab = _table_from_region(pb)
+    for k in ("count", "first", "limit", "offset"):
+        assert np.array_equal(tab[k], ob["table"][k]), k
+    assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_PALETTE, np.uint8), ob["palette"])
+    assert info["n_palette"] == ob["n_pal"] and info["n_verbatim"] == ob["n_verbatim"]
+    for reg, key in ((dg.LW_REG_TILE_OFF, "tile_off"), (dg.LW_REG_WORDS, "words"), (dg.LW_REG_SM, "sm"),
+                     (dg.LW_REG_VB_BITS, "vb_bits"), (dg.LW_REG_VB_START, "vb_start")):
+        assert np.array_equal(dg.lw_bundle_region(pb, reg, np.uint32), ob[key]), key
+    assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_VERBATIM, np.uint16), ob["verbatim"])
+
+
+def test_bf16_config_shape_sample():
+    w, _ = synth.gen_bf16(synth.CONFIGS[4][0], rows=256, cols=4096)
+    ob = O.build_bundle_bf16(w)
+    pb = dg.lw_bundle_build_bf16(w)
+    assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_WORDS, np.uint32), ob["words"])
+    assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_VERBATIM, np.uint16), ob["verbatim"])
+
+
+def test_twin_layout():
+    codes, d, m, _ = synth.gen_q_custom(64, 512, 21)
+    twin, dm = dg.lw_twin_build(codes, 4, d, m)
+    assert np.array_equal(twin & 15, codes[:, 0::2]) and np.array_equal(twin >> 4, codes[:, 1::2])
+    assert np.array_equal(dm & 0xFFFF, d) and np.array_equal(dm >> 16, m)
+
+
+# ------------------------------------------------------------------ errors
+
+def test_argument_errors():
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_bundle_build_q(dg.LW_Q4_PAIR, np.zeros((65, 256), np.uint8), np.zeros((65, 1), np.uint16),
+                             np.zeros((65, 1), np.uint16))
+    assert e.value.status == dg.LW_E_SHAPE
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_bundle_build_q(dg.LW_Q4_PAIR, np.full((64, 256), 16, np.uint8), np.zeros((64, 1), np.uint16),
+                             np.zeros((64, 1), np.uint16))
+    assert e.value.status == dg.LW_E_ARG
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_bundle_build_q(7, np.zeros((64, 256), np.uint8), np.zeros((64, 1), np.uint16),
+                             np.zeros((64, 1), np.uint16))
+    assert e.value.status == dg.LW_E_ARG
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_bundle_build_bf16(np.zeros((64, 100), np.uint16))
+    assert e.value.status == dg.LW_E_SHAPE
+    assert dg.lw_status_str(dg.LW_E_TABLE) == "invalid code table"
+
+
+def _image(seed=31, kind=dg.LW_Q4_PAIR):
+    codes, d, m, _ = synth.gen_q_custom(128, 1024, seed)
+    b = dg.lw_bundle_build_q(kind, codes, d, m)
+    return b, dg.lw_bundle_image(b), dg.lw_bundle_get_info(b)
+
+
+def test_load_round_trip():
+    b, img, info = _image()
+    b2 = dg.lw_bundle_load(img)
+    assert np.array_equal(dg.lw_bundle_image(b2), img)
+
+
+@pytest.mark.parametrize("what", ["magic", "truncate", "len12", "kraft", "tile_off", "tile_off_end",
+                                  "shape", "region"])
+def test_corrupt_images_rejected(what):
+    b, img, info = _image()
+    img = img.copy()
+    off = info["region_offset"]
+    expect = dg.LW_E_FORMAT
+    if what == "magic":
+        img[0] ^= 0xFF
+    elif what == "truncate":
+        img = img[: len(img) // 2]
+    elif what == "len12":
+        # move a symbol from length 11 to a (nonexistent) 12th length slot is not
+        # representable; corrupt count[11] instead so the Kraft sum breaks
+        t = img[off[dg.LW_REG_TABLE]:].view(np.uint16)
+        t[11] += 1
+        expect = dg.LW_E_TABLE
+    elif what == "kraft":
+        t = img[off[dg.LW_REG_TABLE]:].view(np.uint16)
+        t[24 + 5] ^= 0x40          # a limit[] entry no longer consistent
+        expect = dg.LW_E_TABLE
+    elif what == "tile_off":
+        to = img[off[dg.LW_REG_TILE_OFF]:].view(np.uint32)
+        to[3] += 1
+    elif what == "tile_off_end":
+        to = img[off[dg.LW_REG_TILE_OFF]:].view(np.uint32)
+        to[info["n_tiles"]] += 32
+    elif what == "shape":
+        img[16:24] = np.frombuffer(np.int64(100).tobytes(), np.uint8)   # rows = 100
+    elif what == "region":
+        hdr = img[:512].view(np.uint64)
+        # the header's region offset array starts at byte 104; push the words region past the end
+        assert hdr[104 // 8 + dg.LW_REG_WORDS] == off[dg.LW_REG_WORDS]
+        hdr[104 // 8 + dg.LW_REG_WORDS] = len(img) + 4096
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_bundle_load(img)
+    assert e.value.status == expect, (what, e.value)

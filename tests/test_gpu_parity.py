@@ -1,0 +1,203 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Decoded codes and bf16 weights must be bit-exact; GEMV outputs must agree with
+the oracle's fp64 GEMV within max relative error 1e-3, where the relative
+error of an output is |y - y_ref| / max(|y_ref|, 0.01 * rms(y_ref)) (the floor
+keeps rows whose exact value is near zero from dividing by ~0; fp32
+accumulation over <= 28672 terms is far inside this bound).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as T
+    assert T.cuda.is_available(), "GPU tests need a GPU"
+    return T
+
+
+@pytest.fixture(scope="module")
+def dg():
+    import decode_gemv_amd as D
+    return D
+
+
+def rel_err(y, ref):
+    ref = np.asarray(ref, np.float64)
+    floor = 0.01 * np.sqrt(np.mean(ref ** 2))
+    return float(np.max(np.abs(np.asarray(y, np.float64) - ref) / np.maximum(np.abs(ref), floor)))
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _upload(dg, torch, b):
+    return dg.upload(b)
+
+
+def _run_gemv(dg, torch, db, x_bits, batch, rows):
+    x = torch.from_numpy(np.ascontiguousarray(x_bits[:batch]).view(np.int16)).cuda()
+    y = torch.full((batch, rows), float("nan"), dtype=torch.float32, device="cuda")
+    dg.lw_gemv(db, x, y, batch)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _decode_q(dg, torch, db, kind, rows, cols, n_tiles):
+    nbytes = rows * cols // 2 if kind == dg.LW_Q4_PAIR else rows * cols
+    out = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    lb = torch.zeros(n_tiles * 32, dtype=torch.int32, device="cuda")
+    dg.lw_decode_only(db, out, lane_bits=lb)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    if kind == dg.LW_Q4_PAIR:
+        o = o.reshape(rows, cols // 2)
+        q = np.empty((rows, cols), np.uint8)
+        q[:, 0::2] = o & 15
+        q[:, 1::2] = o >> 4
+    else:
+        q = o.reshape(rows, cols)
+    return q, lb.cpu().numpy().view(np.uint32)
+
+
+SMALL_Q = [
+    # kind, rows, cols, law, seed  (edge shapes: one tile, odd row bands,
+    # column blocks not a multiple of four, several column groups)
+    ("q4", 64, 256, "normal", 101), ("q4", 192, 768, "normal", 102), ("q4", 256, 1024, "normal", 103),
+    ("q4", 128, 1280, "laplace", 104), ("q4", 320, 2304, "normal", 105), ("q4", 64, 4096, "normal", 106),
+    ("q4", 128, 512, "uniform", 107), ("q4", 64, 512, "const", 108),
+    ("q6", 64, 256, "normal", 111), ("q6", 192, 1280, "normal", 112), ("q6", 128, 2048, "uniform", 113),
+    ("q6", 64, 768, "const", 114),
+]
+
+
+def _gen_small(kind, rows, cols, law, seed):
+    if kind == "q4":
+        return synth.gen_q_custom(rows, cols, seed, qmax=15, law=law, mu=7.5, scale=1.8)
+    return synth.gen_q_custom(rows, cols, seed, qmax=63, law=law, mu=31.5, scale=5.0)
+
+
+@pytest.mark.parametrize("case", SMALL_Q, ids=lambda c: "-".join(map(str, c)))
+def test_decode_only_bit_exact_small(torch, dg, case):
+    kind_s, rows, cols, law, seed = case
+    say("decode", case)
+    kind = dg.LW_Q4_PAIR if kind_s == "q4" else dg.LW_Q6_SINGLE
+    codes, d, m, x = _gen_small(*case)
+    b = dg.lw_bundle_build_q(kind, codes, d, m)
+    info = dg.lw_bundle_get_info(b)
+    db = _upload(dg, torch, b)
+    q, bits = _decode_q(dg, torch, db, kind, rows, cols, info["n_tiles"])
+    assert np.array_equal(q, codes)
+    ob = O.build_bundle_q(kind, codes, d, m)
+    _, obits = O.decode_bundle_q(ob)
+    assert np.array_equal(bits, obits)
+
+
+@pytest.mark.parametrize("case", SMALL_Q, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 7])
+def test_gemv_small(torch, dg, case, batch):
+    kind_s, rows, cols, law, seed = case
+    say("gemv", case, batch)
+    kind = dg.LW_Q4_PAIR if kind_s == "q4" else dg.LW_Q6_SINGLE
+    codes, d, m, x = _gen_small(*case)
+    b = dg.lw_bundle_build_q(kind, codes, d, m)
+    db = _upload(dg, torch, b)
+    y = _run_gemv(dg, torch, db, x, batch, rows)
+    ref = O.gemv_q(codes, d, m, x, batch)
+    assert rel_err(y, ref) <= TOL
+    # deterministic: a second call gives identical bits
+    y2 = _run_gemv(dg, torch, db, x, batch, rows)
+    assert np.array_equal(y, y2)
+
+
+def test_gemv_all_eights_is_zero(torch, dg):
+    codes = np.full((128, 1024), 8, np.uint8)
+    _, d, m, x = synth.gen_q_custom(128, 1024, 120)
+    db = _upload(dg, torch, dg.lw_bundle_build_q(dg.LW_Q4_PAIR, codes, d, m))
+    y = _run_gemv(dg, torch, db, x, 2, 128)
+    assert np.all(np.abs(y) < 1e-6)
+
+
+def test_twin_small(torch, dg):
+    for rows, cols, seed in ((64, 256, 130), (192, 1024, 131), (128, 4096, 132), (64, 14336, 133)):
+        codes, d, m, x = synth.gen_q_custom(rows, cols, seed)
+        twin, dm = dg.lw_twin_build(codes, 4, d, m)
+        tw = torch.from_numpy(twin).cuda()
+        dmt = torch.from_numpy(dm.view(np.int32)).cuda()
+        for batch in (1, 4, 16):
+            say("twin", rows, cols, batch)
+            xt = torch.from_numpy(np.ascontiguousarray(x[:batch]).view(np.int16)).cuda()
+            y = torch.full((batch, rows), float("nan"), device="cuda")
+            dg.lw_twin_gemv(tw, dmt, 4, rows, cols, xt, y, batch)
+            torch.cuda.synchronize()
+            assert rel_err(y.cpu().numpy(), O.gemv_q(codes, d, m, x, batch)) <= TOL
+
+
+def test_argument_errors_device(torch, dg):
+    codes, d, m, x = synth.gen_q_custom(64, 256, 140)
+    b = dg.lw_bundle_build_q(dg.LW_Q4_PAIR, codes, d, m)
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_bundle_upload(b, small)
+    assert e.value.status == dg.LW_E_ARG
+    db = _upload(dg, torch, b)
+    xt = torch.zeros((1, 256), dtype=torch.int16, device="cuda")
+    y = torch.zeros((1, 64), device="cuda")
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_gemv(db, xt, y, 17)
+    assert e.value.status == dg.LW_E_ARG
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_decode_only(db, torch.zeros(16, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == dg.LW_E_ARG
+
+
+# ------------------------------------------------------------------ full sizes
+
+def _sample_rows(rows, n, seed):
+    rng = np.random.default_rng(seed)
+    r = np.unique(np.concatenate([[0, rows - 1], rng.choice(rows, n, replace=False)]))
+    return r
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_full_size_q4(torch, dg, cfg):
+    mat = synth.CONFIGS[cfg][0]
+    say("full", mat.name)
+    codes, d, m, x = synth.gen_q(mat)
+    b = dg.lw_bundle_build_q(dg.LW_Q4_PAIR, codes, d, m)
+    info = dg.lw_bundle_get_info(b)
+    db = _upload(dg, torch, b)
+    q, bits = _decode_q(dg, torch, db, dg.LW_Q4_PAIR, mat.rows, mat.cols, info["n_tiles"])
+    assert np.array_equal(q, codes)
+    del q
+    rows = _sample_rows(mat.rows, 96, cfg)
+    for batch in (b_ for b_ in synth.BATCHES[cfg] if b_ < 8):
+        say("full gemv", mat.name, batch)
+        y = _run_gemv(dg, torch, db, x, batch, mat.rows)
+        ref = O.gemv_q(codes, d, m, x, batch, rows=rows)
+        assert rel_err(y[:, rows], ref) <= TOL
+        assert np.all(np.isfinite(y))
+
+
+def test_full_size_q6_one_matrix(torch, dg):
+    mat = synth.CONFIGS[5][2]        # down 8192 x 28672: the widest split
+    say("full", mat.name)
+    codes, d, m, x = synth.gen_q(mat)
+    b = dg.lw_bundle_build_q(dg.LW_Q6_SINGLE, codes, d, m)
+    info = dg.lw_bundle_get_info(b)
+    db = _upload(dg, torch, b)
+    q, bits = _decode_q(dg, torch, db, dg.LW_Q6_SINGLE, mat.rows, mat.cols, info["n_tiles"])
+    assert np.array_equal(q, codes)
+    del q
+    rows = _sample_rows(mat.rows, 48, 5)
+    y = _run_gemv(dg, torch, db, x, 1, mat.rows)
+    assert rel_err(y[:, rows], O.gemv_q(codes, d, m, x, 1, rows=rows)) <= TOL
