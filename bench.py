@@ -1,0 +1,179 @@
+"""Benchmark of the fused decode + dequantise + GEMV over a Huffman-coded matrix.
+
+Workload: the Llama-3.1-8B MLP up/gate shape, 14336 x 4096, 4-bit codes
+q = clamp(rint(N(7.5, 1.8)), 0, 15) coded in pairs (one length-limited
+canonical Huffman table per matrix, 64x256 tiles of 32 lanes), fp16 d/m per
+256-weight super-block, fp16 x, batch 1 (synthetic inputs, synth.py).
+
+One step = one lw_gemv call (stage, lane decode, dequantise, dot, reduce).
+Each step reads a different copy of the bundle so that the 256 MB Infinity
+Cache cannot serve the weights: the timed bytes come from HBM.  Time is taken
+with HIP events on the stream the kernels run on (torch's current stream).
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+
+Prints one JSON line.  Extra flags: --config {1,2,3,4,5} (default 2),
+--batch, --no-cpu (skip the oracle CPU baseline), --copy-calib (also run a
+plain device copy of known size, for counter calibration).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", type=int, default=2)
+    p.add_argument("--batch", type=int, default=1)
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-extras", action="store_true")
+    p.add_argument("--copy-calib", action="store_true")
+    return p.parse_args()
+
+
+def copies_for(nbytes: int) -> int:
+    """Bundle copies needed so that one pass over them exceeds twice the MALL."""
+    return int(max(2, min(64, -(-2 * MALL_BYTES // max(nbytes, 1)))))
+
+
+def time_loop(torch, fn, n_copies, steps, warmup):
+    for i in range(warmup):
+        fn(i % n_copies)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for i in range(steps):
+        fn(i % n_copies)
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps       # ms per step
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for {a.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import decode_gemv_amd as dg
+    import synth
+
+    mats = synth.CONFIGS[a.config]
+    mat = mats[0]
+    kind = {"q4": dg.LW_Q4_PAIR, "q6": dg.LW_Q6_SINGLE, "bf16": dg.LW_BF16_EXP}[mat.kind]
+    t0 = time.time()
+    if kind == dg.LW_BF16_EXP:
+        w, xb = synth.gen_bf16(mat)
+        b = dg.lw_bundle_build_bf16(w)
+        codes = d = m = None
+    else:
+        codes, d, m, xb = synth.gen_q(mat)
+        b = dg.lw_bundle_build_q(kind, codes, d, m)
+    info = dg.lw_bundle_get_info(b)
+    build_s = time.time() - t0
+
+    img = torch.from_numpy(dg.lw_bundle_image(b)).cuda()
+    n_copies = copies_for(int(info["image_bytes"]))
+    dbs = []
+    for _ in range(n_copies):
+        buf = torch.empty_like(img)
+        dbs.append(dg.lw_bundle_upload(b, buf))
+    torch.cuda.synchronize()
+    batch = a.batch
+    x = torch.from_numpy(np.ascontiguousarray(xb[:batch]).view(np.int16)).cuda()
+    y = torch.empty((batch, mat.rows), dtype=torch.float32, device="cuda")
+
+    ms = time_loop(torch, lambda i: dg.lw_gemv(dbs[i], x, y, batch), n_copies, a.steps, a.warmup)
+    us = ms * 1e3
+    coded = int(info["coded_bytes"])
+    algo_bytes = coded + 2 * batch * mat.cols + 4 * batch * mat.rows
+    achieved = algo_bytes / (us * 1e-6) / 1e9
+    result = {
+        "metric": "fused decode+GEMV us/matrix; coded-byte HBM GB/s and % of MI355X HBM peak",
+        "value": round(coded / (us * 1e-6) / 1e9, 2),
+        "unit": "GB/s (coded bytes)",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16 x, fp32 accumulate" if kind != dg.LW_BF16_EXP else "bf16 x, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": f"{mat.name}: {mat.rows}x{mat.cols} {mat.kind} coded, batch {batch}",
+                   "rows": mat.rows, "cols": mat.cols, "batch": batch, "bundle_copies": n_copies},
+        "us_per_matrix": round(us, 3),
+        "pct_hbm_peak_coded": round(100 * coded / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+        "coded_bytes": coded,
+        "bits_per_weight": round(8 * coded / (mat.rows * mat.cols), 4),
+        "equiv_uncompressed_GBs": round(int(info["twin_bytes"]) / (us * 1e-6) / 1e9, 2),
+        "B_eff_GBs": round(2 * mat.rows * mat.cols / (us * 1e-6) / 1e9, 2),
+        "symbols_per_s": (mat.rows * mat.cols // (2 if kind == dg.LW_Q4_PAIR else 1)) / (us * 1e-6),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": algo_bytes},
+    }
+
+    if not a.no_extras and kind == dg.LW_Q4_PAIR:
+        # fixed-width twin on the same codes and scales (latency bar)
+        twin, dmw = dg.lw_twin_build(codes, 4, d, m)
+        tw0 = torch.from_numpy(twin).cuda()
+        dm0 = torch.from_numpy(dmw.view(np.int32)).cuda()
+        tn = copies_for(twin.nbytes)
+        tws = [tw0.clone() for _ in range(tn)]
+        yt = torch.empty_like(y)
+        tms = time_loop(torch, lambda i: dg.lw_twin_gemv(tws[i], dm0, 4, mat.rows, mat.cols, x, yt, batch),
+                        tn, a.steps, a.warmup)
+        tbytes = twin.nbytes + dmw.nbytes
+        result["twin"] = {"us_per_matrix": round(tms * 1e3, 3), "bytes": tbytes,
+                          "GBs": round(tbytes / (tms * 1e-3) / 1e9, 2),
+                          "fused_over_twin_time": round(us / (tms * 1e3), 3)}
+        del tws
+        # decode only (restores the packed codes to HBM)
+        out = torch.empty(mat.rows * mat.cols // 2, dtype=torch.uint8, device="cuda")
+        dms = time_loop(torch, lambda i: dg.lw_decode_only(dbs[i], out), n_copies, max(a.steps // 4, 10),
+                        a.warmup)
+        result["decode_only"] = {"us_per_matrix": round(dms * 1e3, 3),
+                                 "symbols_per_s": (mat.rows * mat.cols // 2) / (dms * 1e-3)}
+    if a.copy_calib:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calib_bytes"] = src.numel()
+
+    if not a.no_cpu and kind != dg.LW_BF16_EXP:
+        import oracle as O
+        # the oracle as it stands, one thread: limit-method decode of every
+        # tile and the fp64 GEMV, on the whole matrix
+        ob = O.build_bundle_q(O.KIND[mat.kind], codes, d, m)
+        times = []
+        for _ in range(2):
+            t = time.time()
+            q, _ = O.decode_bundle_q(ob)
+            O.gemv_q(q, d, m, xb, batch)
+            times.append(time.time() - t)
+        tc = min(times)
+        result["cpu_baseline"] = {"value": round(coded / tc / 1e9, 4), "unit": "GB/s (coded bytes)",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": f"whole {mat.rows}x{mat.cols} matrix, limit-method decode + fp64 GEMV, "
+                                            f"best of 2 runs: {tc * 1e6:.0f} us/matrix"}
+    result["build_s"] = round(build_s, 2)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,33 +13,32 @@
 //
 // Dequantisation w = d*q - m per 256-weight super-block (one tile row) is
 // applied after the dot product: y = d * sum(q x) - m * sum(x).
-#include "kernels.h"
+#include <type_traits>
+
 #include "lane_decode.hpp"
 
 namespace {
 
 constexpr int WAVES = 4;
 
-LW_DEV int slots_of(int max_words) { return max_words + 2; }
-
 struct LdsLayout {
-    size_t tab, x, tiles, total;
+    uint32_t x, tiles, flag, total;
 };
 
 __host__ __device__ inline LdsLayout lds_layout(int batch, int max_words, bool decode_only)
 {
     LdsLayout L;
-    L.tab = 0;
-    L.x = (sizeof(LdsTab) + 255) & ~(size_t)255;
-    size_t xbytes = decode_only ? 0 : (size_t)WAVES * batch * 128 * 4;
+    L.x = LW_TAB_BYTES;
+    const uint32_t xbytes = decode_only ? 0u : (uint32_t)(WAVES * batch * 128 * 4);
     L.tiles = L.x + xbytes;
-    size_t tiles = (size_t)WAVES * 2 * (max_words + 2) * 128;
-    size_t red = (size_t)WAVES * batch * 128 * 4;
-    L.total = L.tiles + (tiles > red ? tiles : red);
+    const uint32_t tiles = (uint32_t)(WAVES * 2 * (max_words + 3) * 128);
+    const uint32_t red = (uint32_t)(WAVES * batch * 128 * 4);
+    L.flag = L.tiles + (tiles > red ? tiles : red);
+    L.total = L.flag + 16;
     return L;
 }
 
-// Shared prologue: tables, this wave's two tiles, and the lane's identity.
+// Identity of a lane within the grid.
 struct LaneCtx {
     int wave, lane, half, l, g, rbp, cb, rb, t;
     bool wave_active, lane_active;
@@ -56,7 +55,7 @@ LW_DEV LaneCtx lane_ctx(const KArgs &a)
     c.rbp = blockIdx.y;
     c.cb = c.g * WAVES + c.wave;
     c.wave_active = c.cb < a.n_cb;
-    int rb = c.rbp * 2 + c.half;
+    const int rb = c.rbp * 2 + c.half;
     c.lane_active = c.wave_active && rb < a.n_rb;
     // a missing second row band decodes the first one again; its results are dropped
     c.rb = rb < a.n_rb ? rb : rb - 1;
@@ -64,19 +63,63 @@ LW_DEV LaneCtx lane_ctx(const KArgs &a)
     return c;
 }
 
-template <int KIND, int NCMP, int BATCH>
+// Sum the per-wave partials of the workgroup's 128 rows (red[wave][b][row])
+// and either write y (one column group) or take part in the split-column
+// reduction.  The partials travel through the bundle's workspace as
+// device-scope atomic exchanges, which are performed at the coherence point
+// of all XCDs without an L2 writeback; each workgroup then bumps its row's
+// arrival counter, and the last one to arrive reads the partials back with
+// device-scope atomic loads and adds them in group order (deterministic),
+// then re-arms the counter for the next call.
+template <int BATCH>
+LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g, int rbp, int waves,
+                           uint32_t *last_flag)
+{
+    for (int i = threadIdx.x; i < BATCH * 128; i += blockDim.x) {
+        const int b = i >> 7, row = i & 127;
+        float v = 0.f;
+        for (int w = 0; w < waves; w++) v += red[(w * BATCH + b) * 128 + row];
+        if (row0 + row < a.rows) {
+            if (a.groups == 1) a.y[(size_t)b * a.rows + row0 + row] = v;
+            else
+                (void)__hip_atomic_exchange(&a.part[((size_t)g * LW_BATCH_MAX + b) * a.rows + row0 + row], v,
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (a.groups == 1) return;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's exchanges are performed
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&a.count[rbp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *last_flag = (old == (uint32_t)a.groups - 1u) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!*last_flag) return;
+    for (int i = threadIdx.x; i < BATCH * 128; i += blockDim.x) {
+        const int b = i >> 7, row = i & 127;
+        if (row0 + row >= a.rows) continue;
+        float v = 0.f;
+        for (int gg = 0; gg < a.groups; gg++)
+            v += __hip_atomic_load(&a.part[((size_t)gg * LW_BATCH_MAX + b) * a.rows + row0 + row], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        a.y[(size_t)b * a.rows + row0 + row] = v;
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(&a.count[rbp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int KIND, int N8, int N16, int BATCH>
 __global__ __launch_bounds__(256) void k_gemv_q(KArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int SPL = KIND == LW_Q4_PAIR ? 256 : 512;
     const LdsLayout L = lds_layout(BATCH, a.max_words, false);
-    LdsTab &tab = *reinterpret_cast<LdsTab *>(lds + L.tab);
     const LaneCtx c = lane_ctx(a);
-    const int S = slots_of(a.max_words);
+    const int S = a.max_words + 3;
     uint32_t *xs = reinterpret_cast<uint32_t *>(lds + L.x) + c.wave * BATCH * 128;
+    const uint32_t xs_addr = (uint32_t)(size_t)xs;
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + (c.wave * 2 + c.half) * S * 32;
 
-    lw_stage_tab(tab, a.tab, false);
+    lw_stage_tab(lds, a.tab, a.min_len, a.max_len, false);
     float sx[BATCH];
     if (c.wave_active) {
         const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
@@ -85,7 +128,7 @@ __global__ __launch_bounds__(256) void k_gemv_q(KArgs a)
 #pragma unroll
         for (int b = 0; b < BATCH; b++) {
             const uint32_t *xb = xg + (size_t)b * (a.cols / 2) + (size_t)c.cb * 128;
-            uint32_t v0 = xb[c.lane], v1 = xb[c.lane + 64];
+            const uint32_t v0 = xb[c.lane], v1 = xb[c.lane + 64];
             xs[b * 128 + c.lane] = v0;
             xs[b * 128 + c.lane + 64] = v1;
             sx[b] = lw_wave_sum(lw_half_lo(v0) + lw_half_hi(v0) + lw_half_lo(v1) + lw_half_hi(v1));
@@ -100,24 +143,60 @@ __global__ __launch_bounds__(256) void k_gemv_q(KArgs a)
         for (int b = 0; b < BATCH; b++) acc[p][b] = 0.f;
 
     if (c.wave_active) {
-        const uint32_t *lw = slots + c.l;
-        uint32_t u = 31;
+        LaneDec d;
+        const bool ok = lw_lane_init(d, lds, slots, c.l, a);
+        constexpr int NG = SPL / 4;           // groups of four symbols per lane
+        constexpr int HALF = NG / 2;          // groups per tile row
+        if (ok) {
+            // activations of one group: Q4 four pairs, Q6 two pairs (four columns) per batch row
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            struct XA {
+                u32x4 v[BATCH];
+            };
+            auto fetch = [&](int g) {
+                XA r;
 #pragma unroll
-        for (int p = 0; p < 2; p++) {
-#pragma unroll 4
-            for (int k = 0; k < SPL / 2; k++) {
-                const uint32_t idx = lw_decode_step<NCMP>(lw, u, a.lim, tab);
-                if constexpr (KIND == LW_Q4_PAIR) {
-                    const uint32_t pay = tab.pay[idx];
-#pragma unroll
-                    for (int b = 0; b < BATCH; b++) acc[p][b] = lw_dot2(pay, xs[b * 128 + k], acc[p][b]);
-                } else {
-                    const uint32_t pay = (k & 1) ? tab.pay_hi[idx] : tab.pay[idx];
-#pragma unroll
-                    for (int b = 0; b < BATCH; b++) acc[p][b] = lw_dot2(pay, xs[b * 128 + (k >> 1)], acc[p][b]);
+                for (int b = 0; b < BATCH; b++) {
+                    if constexpr (KIND == LW_Q4_PAIR) {
+                        const uint32_t ad = xs_addr + (uint32_t)(b * 512 + 16 * g);
+                        r.v[b] = *(__attribute__((address_space(3))) const u32x4 *)(size_t)ad;
+                    } else {
+                        const uint32_t ad = xs_addr + (uint32_t)(b * 512 + 8 * g);
+                        const u32x2 t = *(__attribute__((address_space(3))) const u32x2 *)(size_t)ad;
+                        r.v[b] = u32x4{t.x, t.y, 0u, 0u};
+                    }
                 }
-            }
+                return r;
+            };
+            // one call per tile row (p): the accumulator row is a compile-time index
+            auto run_row = [&](auto pc) {
+                constexpr int p = decltype(pc)::value;
+                auto use = [&](int, int j, uint32_t pay, const XA &x) {
+#pragma unroll
+                    for (int b = 0; b < BATCH; b++) {
+                        uint32_t xp;
+                        if constexpr (KIND == LW_Q4_PAIR)
+                            xp = j == 0 ? x.v[b].x : j == 1 ? x.v[b].y : j == 2 ? x.v[b].z : x.v[b].w;
+                        else
+                            xp = j < 2 ? x.v[b].x : x.v[b].y;
+                        acc[p][b] = lw_dot2(pay, xp, acc[p][b]);
+                    }
+                };
+                if constexpr (KIND == LW_Q4_PAIR)
+                    lw_decode_pipelined<N8, N16, HALF, XA>(d, a, [](int) { return 0u; }, fetch, use);
+                else
+                    lw_decode_pipelined<N8, N16, HALF, XA>(
+                        d, a, [](int j) { return (j & 1) ? (LW_TPAY_HI - LW_TPAY) : 0u; }, fetch, use);
+            };
+            run_row(std::integral_constant<int, 0>{});
+            run_row(std::integral_constant<int, 1>{});
         }
+        if (!ok)                           // unusable LDS base: poison the output
+#pragma unroll
+            for (int p = 0; p < 2; p++)
+#pragma unroll
+                for (int b = 0; b < BATCH; b++) acc[p][b] = __builtin_nanf("");
     }
 
     // dequantise: y_row = d * sum(q x) - m * sum(x) for this tile row
@@ -127,9 +206,9 @@ __global__ __launch_bounds__(256) void k_gemv_q(KArgs a)
 #pragma unroll
         for (int p = 0; p < 2; p++) {
             const uint32_t w = p ? dm.y : dm.x;
-            const float d = lw_half_lo(w), m = lw_half_hi(w);
+            const float dd = lw_half_lo(w), mm = lw_half_hi(w);
 #pragma unroll
-            for (int b = 0; b < BATCH; b++) val[p][b] = d * acc[p][b] - m * sx[b];
+            for (int b = 0; b < BATCH; b++) val[p][b] = dd * acc[p][b] - mm * sx[b];
         }
     }
     __syncthreads();                      // tiles no longer read: reuse for the reduction
@@ -139,156 +218,123 @@ __global__ __launch_bounds__(256) void k_gemv_q(KArgs a)
     for (int p = 0; p < 2; p++)
 #pragma unroll
         for (int b = 0; b < BATCH; b++)
-            red[(c.wave * BATCH + b) * 128 + c.half * 64 + 2 * c.l + p] =
-                (c.wave_active && c.lane_active) ? val[p][b] : 0.f;
+            red[(c.wave * BATCH + b) * 128 + c.half * 64 + 2 * c.l + p] = c.lane_active ? val[p][b] : 0.f;
     __syncthreads();
 
     const int64_t row0 = (int64_t)c.rbp * 128;
-    __shared__ uint32_t last_flag;
-    for (int i = threadIdx.x; i < BATCH * 128; i += blockDim.x) {
-        const int b = i >> 7, row = i & 127;
-        float v = 0.f;
-#pragma unroll
-        for (int w = 0; w < WAVES; w++) v += red[(w * BATCH + b) * 128 + row];
-        if (row0 + row < a.rows) {
-            if (a.groups == 1) a.y[(size_t)b * a.rows + row0 + row] = v;
-            else a.part[((size_t)c.g * LW_BATCH_MAX + b) * a.rows + row0 + row] = v;
-        }
-    }
-    if (a.groups == 1) return;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t old = atomicAdd(&a.count[c.rbp], 1u);
-        last_flag = (old == (uint32_t)a.groups - 1u) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (!last_flag) return;
-    __threadfence();
-    for (int i = threadIdx.x; i < BATCH * 128; i += blockDim.x) {
-        const int b = i >> 7, row = i & 127;
-        if (row0 + row >= a.rows) continue;
-        float v = 0.f;
-        for (int g = 0; g < a.groups; g++)
-            v += __builtin_nontemporal_load(&a.part[((size_t)g * LW_BATCH_MAX + b) * a.rows + row0 + row]);
-        a.y[(size_t)b * a.rows + row0 + row] = v;
-    }
-    if (threadIdx.x == 0) a.count[c.rbp] = 0u;
+    uint32_t *last_flag = reinterpret_cast<uint32_t *>(lds + L.flag);
+    lw_finish_rows<BATCH>(a, red, row0, c.g, c.rbp, WAVES, last_flag);
 }
 
+
 // Decode only: restore the fixed-width codes (Q4 packed nibbles, Q6 bytes).
-template <int KIND, int NCMP>
+template <int KIND, int N8, int N16>
 __global__ __launch_bounds__(256) void k_decode_q(KArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int SPL = KIND == LW_Q4_PAIR ? 256 : 512;
     const LdsLayout L = lds_layout(1, a.max_words, true);
-    LdsTab &tab = *reinterpret_cast<LdsTab *>(lds + L.tab);
     const LaneCtx c = lane_ctx(a);
-    const int S = slots_of(a.max_words);
+    const int S = a.max_words + 3;
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + (c.wave * 2 + c.half) * S * 32;
-    lw_stage_tab(tab, a.tab, true);
+    lw_stage_tab(lds, a.tab, a.min_len, a.max_len, true);
     if (c.wave_active) {
         const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
         lw_stage_tile(slots, a.words, w0, (w1 - w0) >> 5, c.l);
     }
     __syncthreads();
     if (!c.wave_active) return;
-    const uint32_t *lw = slots + c.l;
-    uint32_t u = 31;
+    LaneDec d;
+    if (!lw_lane_init(d, lds, slots, c.l, a)) return;
     uint32_t *out = reinterpret_cast<uint32_t *>(a.out);
     const int64_t row_bytes = KIND == LW_Q4_PAIR ? a.cols / 2 : a.cols;
-#pragma unroll
-    for (int p = 0; p < 2; p++) {
-        const int64_t row = (int64_t)c.rb * 64 + 2 * c.l + p;
-        uint32_t *orow = out + (row * row_bytes + (int64_t)c.cb * (SPL / 2)) / 4;
-        uint32_t pk = 0;
-#pragma unroll 4
-        for (int k = 0; k < SPL / 2; k++) {
-            const uint32_t idx = lw_decode_step<NCMP>(lw, u, a.lim, tab);
-            pk |= tab.pay_hi[idx] << (8 * (k & 3));
-            if ((k & 3) == 3) {
-                if (c.lane_active) orow[k >> 2] = pk;
-                pk = 0;
-            }
-        }
-    }
-    if (a.lane_bits && c.lane_active) a.lane_bits[(size_t)c.t * 32 + c.l] = u - 31;
+    constexpr int NG = SPL / 4;
+    constexpr int HALF = NG / 2;
+    uint32_t *orow0 = out + (((int64_t)c.rb * 64 + 2 * c.l) * row_bytes + (int64_t)c.cb * (SPL / 2)) / 4;
+    uint32_t *orow1 = orow0 + row_bytes / 4;
+    struct NoAux {};
+    uint32_t pk = 0;
+    auto run_row = [&](uint32_t *orow) {
+        lw_decode_pipelined<N8, N16, HALF, NoAux>(
+            d, a, [](int) { return LW_TPAY_HI - LW_TPAY; }, [](int) { return NoAux{}; },
+            [&](int g, int j, uint32_t sym, const NoAux &) {
+                pk |= sym << (8 * j);
+                if (j == 3) {
+                    if (c.lane_active) orow[g] = pk;
+                    pk = 0;
+                }
+            });
+    };
+    run_row(orow0);
+    run_row(orow1);
+    if (a.lane_bits && c.lane_active) a.lane_bits[(size_t)c.t * 32 + c.l] = d.u - 31;
 }
 
-template <int KIND, int NCMP, int BATCH>
+template <int KIND, int N8, int N16, int BATCH>
 hipError_t launch_gemv_q(const KArgs &a, hipStream_t s)
 {
     const LdsLayout L = lds_layout(BATCH, a.max_words, false);
     dim3 grid((unsigned)a.groups, (unsigned)((a.n_rb + 1) / 2));
-    auto kern = k_gemv_q<KIND, NCMP, BATCH>;
+    auto kern = k_gemv_q<KIND, N8, N16, BATCH>;
     hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, dim3(256), L.total, s, a);
     return hipGetLastError();
 }
 
-template <int KIND, int NCMP>
+template <int KIND, int N8, int N16>
 hipError_t launch_decode_q(const KArgs &a, hipStream_t s)
 {
     const LdsLayout L = lds_layout(1, a.max_words, true);
     dim3 grid((unsigned)a.groups, (unsigned)((a.n_rb + 1) / 2));
-    auto kern = k_decode_q<KIND, NCMP>;
+    auto kern = k_decode_q<KIND, N8, N16>;
     hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, dim3(256), L.total, s, a);
     return hipGetLastError();
 }
 
-template <int KIND, int NCMP>
+template <int KIND, int N8, int N16>
 hipError_t gemv_batch(const KArgs &a, int batch, hipStream_t s)
 {
     switch (batch) {
-    case 1: return launch_gemv_q<KIND, NCMP, 1>(a, s);
-    case 2: return launch_gemv_q<KIND, NCMP, 2>(a, s);
-    case 3: return launch_gemv_q<KIND, NCMP, 3>(a, s);
-    case 4: return launch_gemv_q<KIND, NCMP, 4>(a, s);
-    case 5: return launch_gemv_q<KIND, NCMP, 5>(a, s);
-    case 6: return launch_gemv_q<KIND, NCMP, 6>(a, s);
-    case 7: return launch_gemv_q<KIND, NCMP, 7>(a, s);
+    case 1: return launch_gemv_q<KIND, N8, N16, 1>(a, s);
+    case 2: return launch_gemv_q<KIND, N8, N16, 2>(a, s);
+    case 3: return launch_gemv_q<KIND, N8, N16, 3>(a, s);
+    case 4: return launch_gemv_q<KIND, N8, N16, 4>(a, s);
+    case 5: return launch_gemv_q<KIND, N8, N16, 5>(a, s);
+    case 6: return launch_gemv_q<KIND, N8, N16, 6>(a, s);
+    case 7: return launch_gemv_q<KIND, N8, N16, 7>(a, s);
     }
     return hipErrorInvalidValue;
 }
 
 template <int KIND>
-hipError_t gemv_ncmp(const KArgs &a, int ncmp, int batch, hipStream_t s)
+hipError_t gemv_plan(const KArgs &a, SadPlan p, int batch, hipStream_t s)
 {
-    switch (ncmp) {
-    case 0: return gemv_batch<KIND, 0>(a, batch, s);
-    case 1: return gemv_batch<KIND, 1>(a, batch, s);
-    case 2: return gemv_batch<KIND, 2>(a, batch, s);
-    case 3: return gemv_batch<KIND, 3>(a, batch, s);
-    case 4: return gemv_batch<KIND, 4>(a, batch, s);
-    case 5: return gemv_batch<KIND, 5>(a, batch, s);
-    case 6: return gemv_batch<KIND, 6>(a, batch, s);
-    case 7: return gemv_batch<KIND, 7>(a, batch, s);
-    case 8: return gemv_batch<KIND, 8>(a, batch, s);
-    case 9: return gemv_batch<KIND, 9>(a, batch, s);
-    case 10: return gemv_batch<KIND, 10>(a, batch, s);
+    const int code = p.n8ops * 2 + p.n16ops;
+    switch (code) {
+    case 0: return gemv_batch<KIND, 0, 0>(a, batch, s);
+    case 1: return gemv_batch<KIND, 0, 1>(a, batch, s);
+    case 2: return gemv_batch<KIND, 1, 0>(a, batch, s);
+    case 3: return gemv_batch<KIND, 1, 1>(a, batch, s);
+    case 4: return gemv_batch<KIND, 2, 0>(a, batch, s);
+    case 5: return gemv_batch<KIND, 2, 1>(a, batch, s);
     }
     return hipErrorInvalidValue;
 }
 
 template <int KIND>
-hipError_t decode_ncmp(const KArgs &a, int ncmp, hipStream_t s)
+hipError_t decode_plan(const KArgs &a, SadPlan p, hipStream_t s)
 {
-    switch (ncmp) {
-    case 0: return launch_decode_q<KIND, 0>(a, s);
-    case 1: return launch_decode_q<KIND, 1>(a, s);
-    case 2: return launch_decode_q<KIND, 2>(a, s);
-    case 3: return launch_decode_q<KIND, 3>(a, s);
-    case 4: return launch_decode_q<KIND, 4>(a, s);
-    case 5: return launch_decode_q<KIND, 5>(a, s);
-    case 6: return launch_decode_q<KIND, 6>(a, s);
-    case 7: return launch_decode_q<KIND, 7>(a, s);
-    case 8: return launch_decode_q<KIND, 8>(a, s);
-    case 9: return launch_decode_q<KIND, 9>(a, s);
-    case 10: return launch_decode_q<KIND, 10>(a, s);
+    const int code = p.n8ops * 2 + p.n16ops;
+    switch (code) {
+    case 0: return launch_decode_q<KIND, 0, 0>(a, s);
+    case 1: return launch_decode_q<KIND, 0, 1>(a, s);
+    case 2: return launch_decode_q<KIND, 1, 0>(a, s);
+    case 3: return launch_decode_q<KIND, 1, 1>(a, s);
+    case 4: return launch_decode_q<KIND, 2, 0>(a, s);
+    case 5: return launch_decode_q<KIND, 2, 1>(a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -301,16 +347,16 @@ size_t lw_lds_bytes(int kind, int batch, int max_words, bool decode_only)
     return lds_layout(batch, max_words, decode_only).total;
 }
 
-hipError_t lw_launch_gemv_q(const KArgs &a, int kind, int ncmp, int batch, hipStream_t s)
+hipError_t lw_launch_gemv_q(const KArgs &a, int kind, SadPlan p, int batch, hipStream_t s)
 {
-    if (kind == LW_Q4_PAIR) return gemv_ncmp<LW_Q4_PAIR>(a, ncmp, batch, s);
-    if (kind == LW_Q6_SINGLE) return gemv_ncmp<LW_Q6_SINGLE>(a, ncmp, batch, s);
+    if (kind == LW_Q4_PAIR) return gemv_plan<LW_Q4_PAIR>(a, p, batch, s);
+    if (kind == LW_Q6_SINGLE) return gemv_plan<LW_Q6_SINGLE>(a, p, batch, s);
     return hipErrorInvalidValue;
 }
 
-hipError_t lw_launch_decode_q(const KArgs &a, int kind, int ncmp, hipStream_t s)
+hipError_t lw_launch_decode_q(const KArgs &a, int kind, SadPlan p, hipStream_t s)
 {
-    if (kind == LW_Q4_PAIR) return decode_ncmp<LW_Q4_PAIR>(a, ncmp, s);
-    if (kind == LW_Q6_SINGLE) return decode_ncmp<LW_Q6_SINGLE>(a, ncmp, s);
+    if (kind == LW_Q4_PAIR) return decode_plan<LW_Q4_PAIR>(a, p, s);
+    if (kind == LW_Q6_SINGLE) return decode_plan<LW_Q6_SINGLE>(a, p, s);
     return hipErrorInvalidValue;
 }

@@ -26,19 +26,30 @@ struct KArgs {
     void *out;                   // decode-only output
     uint32_t *lane_bits;         // decode-only optional per-lane bit counts
     int64_t rows, cols;
-    int32_t n_rb, n_cb, groups, batch, max_words, min_len;
+    int32_t n_rb, n_cb, groups, batch, max_words, min_len, max_len;
     uint32_t pal0;               // bf16: exponent of palette index 0
-    uint32_t lim[10];            // left-justified limits for lengths min_len .. max_len-1
+    // Limit comparison by sums of absolute differences (see lane_decode.hpp):
+    // byte lanes compare the top 8 peek bits with limit/8 (lengths <= 8),
+    // 16-bit lanes the top 16 window bits with limit*32 (lengths 9, 10).
+    uint32_t c8[2], c8m1[2];     // limit/8 and limit/8 - 1 per byte, 0 in unused bytes
+    uint32_t c16, c16m1;         // limit*32 and limit*32 - 1 per half, 0 in unused halves
+    uint32_t sad_k;              // accumulator offset: PBASE - 2*min_len - (number of comparisons)
 };
+
+// SAD comparison layout of a bundle: byte-lane ops (0..2) and 16-bit ops (0..1)
+struct SadPlan {
+    int n8ops, n16ops;
+};
+SadPlan lw_sad_plan(const lw_table &t, int min_len, int max_len, KArgs &a);
 
 // LDS bytes a fused/decode kernel needs per workgroup
 size_t lw_lds_bytes(int kind, int batch, int max_words, bool decode_only);
 
-hipError_t lw_launch_gemv_q(const KArgs &a, int kind, int ncmp, int batch, hipStream_t s);
-hipError_t lw_launch_decode_q(const KArgs &a, int kind, int ncmp, hipStream_t s);
-hipError_t lw_launch_gemv_mfma(const KArgs &a, int kind, int ncmp, int batch, hipStream_t s);
-hipError_t lw_launch_gemv_bf16(const KArgs &a, int ncmp, int batch, hipStream_t s);
-hipError_t lw_launch_decode_bf16(const KArgs &a, int ncmp, hipStream_t s);
+hipError_t lw_launch_gemv_q(const KArgs &a, int kind, SadPlan p, int batch, hipStream_t s);
+hipError_t lw_launch_decode_q(const KArgs &a, int kind, SadPlan p, hipStream_t s);
+hipError_t lw_launch_gemv_mfma(const KArgs &a, int kind, SadPlan p, int batch, hipStream_t s);
+hipError_t lw_launch_gemv_bf16(const KArgs &a, SadPlan p, int batch, hipStream_t s);
+hipError_t lw_launch_decode_bf16(const KArgs &a, SadPlan p, hipStream_t s);
 hipError_t lw_launch_twin(const uint8_t *twin, const uint32_t *dm, int64_t rows, int64_t cols,
                           const uint16_t *x, float *y, int batch, hipStream_t s);
 hipError_t lw_launch_fill_zero(void *p, size_t bytes, hipStream_t s);

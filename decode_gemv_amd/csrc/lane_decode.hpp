@@ -5,56 +5,44 @@
 // adds the code length's offset to index the symbol table, and shifts its
 // buffer by the length.  Here one lane of a wavefront is one lane stream.
 //
-// Layout: a tile's interleaved words are staged in LDS as `slots` rows of 32
-// dwords, slot j+1 holding word row j (slot 0 is a pad row before the stream,
-// the last slot a pad row after it).  A lane keeps u = bitpos + 31, so the two
-// words that hold bits [bitpos, bitpos+32) are slots u>>5 and (u>>5)+1, and
-// the left-justified 32-bit window is their concatenation shifted left by
-// bitpos mod 32 (v_alignbit with shift ~u mod 32).  Comparing the window with
-// limit << 21 is the 11-bit peek comparison; the count r of limits passed
-// gives the length min_len + r.  Bits past a lane's last code are don't-care
-// (prefix property), and the slots bound every read of a valid stream.
+// Words.  A tile's interleaved words are staged in LDS as rows of 32 dwords
+// ("slots"): slot j+1 holds word row j, slot 0 and the last two slots are
+// pads.  A lane keeps u = bitpos + 31; the three words starting at slot u>>5
+// hold bits [bitpos, bitpos + 64) and two v_alignbit by ~u give a 64-bit
+// left-justified register window (hi, lo).  One window serves four symbols:
+// after three codes of at most 11 bits, 31 bits of it are still valid, more
+// than the 11-bit peek needs.  So the LDS read sits on the lane's serial
+// chain once per four symbols.
+//
+// Length.  For sorted limits c_i and an integer peek p,
+//     |p - (c_i - 1)| - |p - c_i| = 2 [p >= c_i] - 1,
+// so two sums of absolute differences count the limits the peek has passed:
+// v_sad_u8 handles four limits per instruction on the top 8 peek bits (exact
+// for lengths <= 8, whose limits are multiples of 8), v_sad_u16 two limits
+// on the top 16 window bits (lengths 9 and 10).  With the accumulator chosen
+// as K = PBASE - 2*min_len - n, the difference of the two sums is
+//     A = PBASE - 2*len,
+// which is at once the LDS address of the 16-bit entry of that length (the
+// symbol-table base offset[len] - first[len], pre-scaled) and, shifted right
+// by one, a shift amount s = PBASE/2 - len whose low five bits are 32 - len:
+//     code = hi >> s,  window <<= len  ==  alignbit(hi, lo, s), alignbit(lo, 0, s).
+// Bits past a lane's last code are don't-care (prefix property); the slots
+// bound every read of a valid stream.
 #ifndef LW_LANE_DECODE_HPP
 #define LW_LANE_DECODE_HPP
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 #define LW_DEV __device__ __forceinline__
 
-// Tables staged in LDS at the start of every decoding workgroup.
-struct LdsTab {
-    uint32_t pay[256];       // payload per canonical index
-    uint32_t pay_hi[256];    // second payload (Q6 odd column / bf16 high half / symbol value)
-    uint32_t len[16];        // code length per comparison count
-    int32_t base[16];        // offset[len] - first[len] per comparison count
-};
-
-template <int NCMP>
-LW_DEV uint32_t lw_count_limits(uint32_t win, const uint32_t *lim)
-{
-    uint32_t r = 0;
-#pragma unroll
-    for (int i = 0; i < NCMP; i++) r += (win >= lim[i]) ? 1u : 0u;
-    return r;
-}
-
-// Decode one symbol of the lane whose slot-0 word is lane_words[0] (stride
-// 32 dwords between slots).  Returns the canonical index; advances u.
-template <int NCMP>
-LW_DEV uint32_t lw_decode_step(const uint32_t *lane_words, uint32_t &u, const uint32_t *lim,
-                               const LdsTab &tab)
-{
-    const uint32_t slot = u >> 5;
-    const uint32_t a = lane_words[slot * 32];
-    const uint32_t b = lane_words[slot * 32 + 32];
-    const uint32_t win = __builtin_amdgcn_alignbit(a, b, ~u);
-    const uint32_t r = lw_count_limits<NCMP>(win, lim);
-    const uint32_t len = tab.len[r];
-    const int32_t base = tab.base[r];
-    u += len;
-    return (uint32_t)((int32_t)(win >> (32u - len)) + base);
-}
+// LDS layout common to all decoding kernels (byte offsets)
+#define LW_PBASE 1024u       // length entries at PBASE - 2*len, len = 1..11
+#define LW_TPAY 1024u        // payload per canonical index, u32[256]
+#define LW_TPAY_HI 2048u     // second payload, u32[256]
+#define LW_TAB_BYTES 3072u
 
 LW_DEV uint32_t lw_wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
@@ -76,27 +64,230 @@ LW_DEV float lw_wave_sum(float v)
     return v;
 }
 
-// Stage the tables of a bundle into LDS (all threads of the block).
-LW_DEV void lw_stage_tab(LdsTab &t, const lw_gputab *g, bool symval_as_hi)
+// LDS accessed by byte address (the kernels allocate only dynamic LDS, so
+// the dynamic area starts at the workgroup's LDS address lb, normally 0;
+// lb is folded into the table entries and the SAD offset so that the hot
+// loop adds no base).
+typedef __attribute__((address_space(3))) const int16_t lw_lds_i16;
+typedef __attribute__((address_space(3))) const uint32_t lw_lds_u32;
+
+LW_DEV uint32_t lw_ld32(uint32_t addr) { return *(lw_lds_u32 *)(size_t)addr; }
+LW_DEV int32_t lw_ld16s(uint32_t addr) { return *(lw_lds_i16 *)(size_t)addr; }
+
+// Stage the decoder tables into LDS (all threads of the block): the
+// per-length entries (LDS address of the symbol-table base offset[len] -
+// first[len], scaled by 4) and the two payload tables.  `symval_second`
+// selects what fills the second table: the kind's high payload, or the
+// symbol value.
+LW_DEV void lw_stage_tab(uint8_t *lds, const lw_gputab *g, int min_len, int max_len, bool symval_second)
 {
+    const uint32_t lb = (uint32_t)(size_t)lds;
+    uint32_t *pay = reinterpret_cast<uint32_t *>(lds + LW_TPAY);
+    uint32_t *pay2 = reinterpret_cast<uint32_t *>(lds + LW_TPAY_HI);
     for (int i = threadIdx.x; i < 256; i += blockDim.x) {
-        t.pay[i] = g->payload[i];
-        t.pay_hi[i] = symval_as_hi ? g->symval[i] : g->payload_hi[i];
+        pay[i] = g->payload[i];
+        pay2[i] = symval_second ? g->symval[i] : g->payload_hi[i];
     }
-    for (int i = threadIdx.x; i < 16; i += blockDim.x) {
-        t.len[i] = g->len[i];
-        t.base[i] = g->base[i];
+    if ((int)threadIdx.x <= max_len - min_len) {
+        const int r = threadIdx.x;
+        const int len = min_len + r;
+        int16_t *ent = reinterpret_cast<int16_t *>(lds + LW_PBASE - 2 * len);
+        *ent = (int16_t)((int32_t)lb + (int32_t)LW_TPAY + 4 * g->base[r]);
     }
 }
 
-// Copy one tile block (W word rows) into LDS slots 1..W, by the 32 lanes l of
-// a half-wave; 16 bytes per lane per step.
+// Copy one tile block (nrows word rows) into LDS slots 1..nrows, by the 32
+// lanes l of a half-wave.  All global loads of a batch of up to 16 x 16 bytes
+// per lane are issued before the first LDS store, so a wave keeps its whole
+// tile in flight instead of one 16-byte load per round trip.
 LW_DEV void lw_stage_tile(uint32_t *slots, const uint32_t *words, uint32_t w0, uint32_t nrows, int l)
 {
     const uint4 *src = reinterpret_cast<const uint4 *>(words + w0);
     uint4 *dst = reinterpret_cast<uint4 *>(slots + 32);
     const uint32_t n = nrows * 8u;
-    for (uint32_t i = (uint32_t)l; i < n; i += 32u) dst[i] = src[i];
+    // indices past the block are clamped to its last vector: the extra lanes
+    // reload and rewrite that same vector, so no load or store is predicated
+    for (uint32_t b0 = 0; b0 < n; b0 += 32u * 16u) {
+        uint4 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const uint32_t idx = min(b0 + (uint32_t)l + 32u * i, n - 1u);
+            v[i] = src[idx];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const uint32_t idx = min(b0 + (uint32_t)l + 32u * i, n - 1u);
+            dst[idx] = v[i];
+        }
+    }
+}
+
+// One lane's decoder state.
+struct LaneDec {
+    uint32_t slot0;              // LDS byte address of this lane's word in slot 0
+    uint32_t u;                  // bit position + 31
+    uint32_t hi, lo;             // 64-bit window
+    uint32_t k;                  // SAD offset including the LDS base
+};
+
+LW_DEV void lw_window(LaneDec &d)
+{
+    const uint32_t p = d.slot0 + ((d.u >> 5) << 7);
+    const uint32_t a = lw_ld32(p), b = lw_ld32(p + 128), c = lw_ld32(p + 256);
+    d.hi = __builtin_amdgcn_alignbit(a, b, ~d.u);
+    d.lo = __builtin_amdgcn_alignbit(b, c, ~d.u);
+}
+
+// Count the limits the window's peek has passed; returns A = lb + PBASE - 2*len.
+template <int N8, int N16>
+LW_DEV uint32_t lw_sad_count(uint32_t hi, uint32_t k, const KArgs &a)
+{
+    const uint32_t p8 = __builtin_amdgcn_perm(hi, hi, 0x03030303u);
+    const uint32_t p16 = __builtin_amdgcn_perm(hi, hi, 0x03020302u);
+    uint32_t s1 = 0, s2 = k;
+    if constexpr (N16 > 0) {
+        s1 = __builtin_amdgcn_sad_u16(p16, a.c16m1, s1);
+        s2 = __builtin_amdgcn_sad_u16(p16, a.c16, s2);
+    }
+    if constexpr (N8 > 1) {
+        s1 = __builtin_amdgcn_sad_u8(p8, a.c8m1[1], s1);
+        s2 = __builtin_amdgcn_sad_u8(p8, a.c8[1], s2);
+    }
+    if constexpr (N8 > 0) {
+        s1 = __builtin_amdgcn_sad_u8(p8, a.c8m1[0], s1);
+        s2 = __builtin_amdgcn_sad_u8(p8, a.c8[0], s2);
+    }
+    return s2 - s1;
+}
+
+// Decode one symbol from the window: returns the LDS byte address of its
+// entry in the first payload table (add LW_TPAY_HI - LW_TPAY for the second);
+// sets s (low five bits = 32 - len).
+template <int N8, int N16>
+LW_DEV uint32_t lw_symbol(const LaneDec &d, const KArgs &a, uint32_t &s)
+{
+    const uint32_t A = lw_sad_count<N8, N16>(d.hi, d.k, a);
+    const int32_t base = lw_ld16s(A);
+    s = A >> 1;
+    const uint32_t code = d.hi >> (s & 31u);
+    return (uint32_t)((int32_t)(code << 2) + base);
+}
+
+LW_DEV void lw_advance(LaneDec &d, uint32_t s)
+{
+    d.hi = __builtin_amdgcn_alignbit(d.hi, d.lo, s);
+    d.lo = __builtin_amdgcn_alignbit(d.lo, 0u, s);
+}
+
+// Software-pipelined decode of NG (even) groups of four symbols of one lane
+// stream.  LDS reads complete in issue order, so the loop keeps only the next
+// window read on the serial chain: in step g it decodes group g (VALU only),
+// issues the window read of group g+1, the payload reads (and fetch(g-1),
+// the caller's other LDS operands) of group g-1 and the length-entry reads
+// of group g, and hands group g-2 to use(group, j, payload, aux).  Pipeline
+// registers are double-buffered by group parity and the loop is unrolled by
+// two, so every buffer index is a compile-time constant (no register moves).
+// pay_off(j) selects the payload table.  Scheduling barriers keep the issue
+// order; the extra window read after the last group stays inside the staged
+// slots.
+template <int N8, int N16, int NG, class Aux, class PayOff, class Fetch, class Use>
+LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetch fetch, Use use)
+{
+    static_assert(NG % 2 == 0 && NG >= 4, "groups must be even");
+    uint32_t wa, wb, wc;
+    uint32_t code[2][4], A[2][4], base[2][4], pay[2][4];
+    Aux aux[2];
+    auto issue_window = [&]() {
+        const uint32_t p = d.slot0 + ((d.u >> 5) << 7);
+        wa = lw_ld32(p);
+        wb = lw_ld32(p + 128);
+        wc = lw_ld32(p + 256);
+    };
+    auto decode_group = [&](int q) {
+        const uint32_t sh = ~d.u;
+        d.hi = __builtin_amdgcn_alignbit(wa, wb, sh);
+        d.lo = __builtin_amdgcn_alignbit(wb, wc, sh);
+        uint32_t ssum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint32_t Aj = lw_sad_count<N8, N16>(d.hi, d.k, a);
+            const uint32_t s = Aj >> 1;
+            A[q][j] = Aj;
+            code[q][j] = d.hi >> (s & 31u);
+            if (j < 3) lw_advance(d, s);
+            ssum += s;
+        }
+        d.u += 4u * (LW_PBASE / 2) - ssum;
+    };
+    auto issue_payloads = [&](int q, int g) {
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            pay[q][j] = lw_ld32((uint32_t)((int32_t)(code[q][j] << 2) + (int32_t)base[q][j]) + pay_off(j));
+        aux[q] = fetch(g);
+    };
+    auto issue_params = [&](int q) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) base[q][j] = (uint32_t)lw_ld16s(A[q][j]);
+    };
+    auto use_group = [&](int q, int g) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) use(g, j, pay[q][j], aux[q]);
+    };
+#define LW_FENCE() __builtin_amdgcn_sched_barrier(0)
+    issue_window();
+    LW_FENCE();
+    decode_group(0);           // group 0
+    LW_FENCE();
+    issue_window();
+    LW_FENCE();
+    issue_params(0);
+    LW_FENCE();
+    decode_group(1);           // group 1
+    LW_FENCE();
+    issue_window();
+    LW_FENCE();
+    issue_payloads(0, 0);
+    LW_FENCE();
+    issue_params(1);
+    LW_FENCE();
+    for (int g = 2; g < NG; g += 2) {
+        decode_group(0);       // group g (even)
+        LW_FENCE();
+        issue_window();        // group g+1
+        LW_FENCE();
+        issue_payloads(1, g - 1);
+        LW_FENCE();
+        use_group(0, g - 2);
+        LW_FENCE();
+        issue_params(0);
+        LW_FENCE();
+        decode_group(1);       // group g+1 (odd)
+        LW_FENCE();
+        issue_window();        // group g+2 (past the end at the last step: in bounds)
+        LW_FENCE();
+        issue_payloads(0, g);
+        LW_FENCE();
+        use_group(1, g - 1);
+        LW_FENCE();
+        issue_params(1);
+        LW_FENCE();
+    }
+    issue_payloads(1, NG - 1);
+    use_group(0, NG - 2);
+    use_group(1, NG - 1);
+#undef LW_FENCE
+}
+
+// Set up a lane's decoder on its staged tile.  Returns false (the kernel must
+// then produce nothing) if the LDS base is not 64-byte aligned, which the
+// shift-amount identity s = A >> 1 needs.
+LW_DEV bool lw_lane_init(LaneDec &d, uint8_t *lds, const uint32_t *slots, int l, const KArgs &a)
+{
+    const uint32_t lb = (uint32_t)(size_t)lds;
+    d.slot0 = (uint32_t)(size_t)(slots + l);
+    d.u = 31;
+    d.k = a.sad_k + lb;
+    return (lb & 63u) == 0;
 }
 
 #endif

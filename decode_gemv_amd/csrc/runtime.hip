@@ -6,12 +6,13 @@
 #include <memory>
 #include <string>
 
-#include "kernels.h"
+#include "lane_decode.hpp"
 
 lw_status lw_fail(lw_status s, const std::string &msg);   // bundle.cpp
 
 struct lw_dev_bundle {
     lw_image_header h;
+    lw_table table;
     lw_gputab tab;
     uint8_t *base;
 };
@@ -48,6 +49,7 @@ extern "C" lw_status lw_bundle_upload(const lw_bundle *b, void *dev_buf, size_t 
     std::unique_ptr<lw_dev_bundle> db(new lw_dev_bundle);
     std::memcpy(&db->h, img, sizeof(db->h));
     std::memcpy(&db->tab, static_cast<const uint8_t *>(img) + db->h.off[LW_REG_GPUTAB], sizeof(db->tab));
+    std::memcpy(&db->table, static_cast<const uint8_t *>(img) + db->h.off[LW_REG_TABLE], sizeof(db->table));
     db->base = static_cast<uint8_t *>(dev_buf);
     *out = db.release();
     return LW_OK;
@@ -77,11 +79,44 @@ static KArgs make_args(const lw_dev_bundle *db)
     a.groups = db->h.work_groups;
     a.max_words = db->h.max_words;
     a.min_len = db->h.min_len;
-    for (int i = 0; i < 10; i++) a.lim[i] = db->tab.limlj[i];
+    a.max_len = db->h.max_len;
     return a;
 }
 
-static int ncmp_of(const lw_dev_bundle *db) { return db->h.max_len - db->h.min_len; }
+// Limit comparisons of lengths min_len .. max_len-1, packed for the SAD
+// counting of lane_decode.hpp: lengths <= 8 in byte lanes (top 8 peek bits
+// against limit/8), lengths 9 and 10 in 16-bit lanes (top 16 window bits
+// against limit*32).  Unused lanes compare 0 with 0 and contribute nothing.
+SadPlan lw_sad_plan(const lw_table &t, int min_len, int max_len, KArgs &a)
+{
+    int l8[8], l16[2], n8 = 0, n16 = 0;
+    for (int L = min_len; L < max_len; L++) {
+        if (L <= 8) l8[n8++] = L;
+        else l16[n16++] = L;
+    }
+    a.c8[0] = a.c8[1] = a.c8m1[0] = a.c8m1[1] = 0;
+    a.c16 = a.c16m1 = 0;
+    for (int i = 0; i < n8; i++) {
+        const uint32_t c = (uint32_t)t.limit[l8[i]] >> 3;
+        a.c8[i / 4] |= c << (8 * (i % 4));
+        a.c8m1[i / 4] |= (c - 1) << (8 * (i % 4));
+    }
+    for (int i = 0; i < n16; i++) {
+        const uint32_t c = (uint32_t)t.limit[l16[i]] << 5;
+        a.c16 |= c << (16 * i);
+        a.c16m1 |= (c - 1) << (16 * i);
+    }
+    a.sad_k = LW_PBASE - 2u * (uint32_t)min_len - (uint32_t)(max_len - min_len);
+    SadPlan p;
+    p.n8ops = (n8 + 3) / 4;
+    p.n16ops = n16 > 0 ? 1 : 0;
+    return p;
+}
+
+static SadPlan plan_of(const lw_dev_bundle *db, KArgs &a)
+{
+    return lw_sad_plan(db->table, db->h.min_len, db->h.max_len, a);
+}
 
 extern "C" lw_status lw_gemv(const lw_dev_bundle *db, const void *x, float *y, int batch, void *stream)
 {
@@ -97,11 +132,11 @@ extern "C" lw_status lw_gemv(const lw_dev_bundle *db, const void *x, float *y, i
     hipError_t e;
     if (db->h.kind == LW_BF16_EXP) {
         a.pal0 = db->tab.payload[0] >> 7;
-        e = lw_launch_gemv_bf16(a, ncmp_of(db), batch, s);
+        e = lw_launch_gemv_bf16(a, plan_of(db, a), batch, s);
     } else if (batch < 8) {
-        e = lw_launch_gemv_q(a, db->h.kind, ncmp_of(db), batch, s);
+        e = lw_launch_gemv_q(a, db->h.kind, plan_of(db, a), batch, s);
     } else {
-        e = lw_launch_gemv_mfma(a, db->h.kind, ncmp_of(db), batch, s);
+        e = lw_launch_gemv_mfma(a, db->h.kind, plan_of(db, a), batch, s);
     }
     if (e == hipErrorNotSupported) return lw_fail(LW_E_UNSUPPORTED, "no kernel for this kind and batch");
     if (e != hipSuccess) return hip_fail(e, "gemv launch");
@@ -124,9 +159,9 @@ extern "C" lw_status lw_decode_only(const lw_dev_bundle *db, void *out, size_t o
     hipError_t e;
     if (db->h.kind == LW_BF16_EXP) {
         a.pal0 = db->tab.payload[0] >> 7;
-        e = lw_launch_decode_bf16(a, ncmp_of(db), s);
+        e = lw_launch_decode_bf16(a, plan_of(db, a), s);
     } else {
-        e = lw_launch_decode_q(a, db->h.kind, ncmp_of(db), s);
+        e = lw_launch_decode_q(a, db->h.kind, plan_of(db, a), s);
     }
     if (e == hipErrorNotSupported) return lw_fail(LW_E_UNSUPPORTED, "no decode kernel for this kind");
     if (e != hipSuccess) return hip_fail(e, "decode launch");
