@@ -63,50 +63,6 @@ LW_DEV LaneCtx lane_ctx(const KArgs &a)
     return c;
 }
 
-// Sum the per-wave partials of the workgroup's 128 rows (red[wave][b][row])
-// and either write y (one column group) or take part in the split-column
-// reduction.  The partials travel through the bundle's workspace as
-// device-scope atomic exchanges, which are performed at the coherence point
-// of all XCDs without an L2 writeback; each workgroup then bumps its row's
-// arrival counter, and the last one to arrive reads the partials back with
-// device-scope atomic loads and adds them in group order (deterministic),
-// then re-arms the counter for the next call.
-template <int BATCH>
-LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g, int rbp, int waves,
-                           uint32_t *last_flag)
-{
-    for (int i = threadIdx.x; i < BATCH * 128; i += blockDim.x) {
-        const int b = i >> 7, row = i & 127;
-        float v = 0.f;
-        for (int w = 0; w < waves; w++) v += red[(w * BATCH + b) * 128 + row];
-        if (row0 + row < a.rows) {
-            if (a.groups == 1) a.y[(size_t)b * a.rows + row0 + row] = v;
-            else
-                (void)__hip_atomic_exchange(&a.part[((size_t)g * LW_BATCH_MAX + b) * a.rows + row0 + row], v,
-                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-    if (a.groups == 1) return;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's exchanges are performed
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&a.count[rbp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *last_flag = (old == (uint32_t)a.groups - 1u) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (!*last_flag) return;
-    for (int i = threadIdx.x; i < BATCH * 128; i += blockDim.x) {
-        const int b = i >> 7, row = i & 127;
-        if (row0 + row >= a.rows) continue;
-        float v = 0.f;
-        for (int gg = 0; gg < a.groups; gg++)
-            v += __hip_atomic_load(&a.part[((size_t)gg * LW_BATCH_MAX + b) * a.rows + row0 + row], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        a.y[(size_t)b * a.rows + row0 + row] = v;
-    }
-    if (threadIdx.x == 0) __hip_atomic_store(&a.count[rbp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 template <int KIND, int N8, int N16, int BATCH>
 __global__ __launch_bounds__(256) void k_gemv_q(KArgs a)
 {

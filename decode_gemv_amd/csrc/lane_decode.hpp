@@ -190,7 +190,7 @@ LW_DEV void lw_advance(LaneDec &d, uint32_t s)
 // pay_off(j) selects the payload table.  Scheduling barriers keep the issue
 // order; the extra window read after the last group stays inside the staged
 // slots.
-template <int N8, int N16, int NG, class Aux, class PayOff, class Fetch, class Use>
+template <int N8, int N16, int NG, class Aux, bool UNROLL_ALL = false, class PayOff, class Fetch, class Use>
 LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetch fetch, Use use)
 {
     static_assert(NG % 2 == 0 && NG >= 4, "groups must be even");
@@ -250,6 +250,7 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
     LW_FENCE();
     issue_params(1);
     LW_FENCE();
+#pragma unroll(UNROLL_ALL ? NG : 1)
     for (int g = 2; g < NG; g += 2) {
         decode_group(0);       // group g (even)
         LW_FENCE();
@@ -288,6 +289,50 @@ LW_DEV bool lw_lane_init(LaneDec &d, uint8_t *lds, const uint32_t *slots, int l,
     d.u = 31;
     d.k = a.sad_k + lb;
     return (lb & 63u) == 0;
+}
+
+// Sum the per-wave partials of the workgroup's 128 rows (red[wave][b][row])
+// and either write y (one column group) or take part in the split-column
+// reduction.  The partials travel through the bundle's workspace as
+// device-scope atomic exchanges, which are performed at the coherence point
+// of all XCDs without an L2 writeback; each workgroup then bumps its row's
+// arrival counter, and the last one to arrive reads the partials back with
+// device-scope atomic loads and adds them in group order (deterministic),
+// then re-arms the counter for the next call.
+template <int BATCH>
+LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g, int rbp, int waves,
+                           uint32_t *last_flag)
+{
+    for (int i = threadIdx.x; i < BATCH * 128; i += blockDim.x) {
+        const int b = i >> 7, row = i & 127;
+        float v = 0.f;
+        for (int w = 0; w < waves; w++) v += red[(w * BATCH + b) * 128 + row];
+        if (row0 + row < a.rows) {
+            if (a.groups == 1) a.y[(size_t)b * a.rows + row0 + row] = v;
+            else
+                (void)__hip_atomic_exchange(&a.part[((size_t)g * LW_BATCH_MAX + b) * a.rows + row0 + row], v,
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (a.groups == 1) return;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's exchanges are performed
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&a.count[rbp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *last_flag = (old == (uint32_t)a.groups - 1u) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!*last_flag) return;
+    for (int i = threadIdx.x; i < BATCH * 128; i += blockDim.x) {
+        const int b = i >> 7, row = i & 127;
+        if (row0 + row >= a.rows) continue;
+        float v = 0.f;
+        for (int gg = 0; gg < a.groups; gg++)
+            v += __hip_atomic_load(&a.part[((size_t)gg * LW_BATCH_MAX + b) * a.rows + row0 + row], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        a.y[(size_t)b * a.rows + row0 + row] = v;
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(&a.count[rbp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 #endif

@@ -2,5 +2,3 @@
 #include "kernels.h"
 
 hipError_t lw_launch_gemv_mfma(const KArgs &, int, SadPlan, int, hipStream_t) { return hipErrorNotSupported; }
-hipError_t lw_launch_gemv_bf16(const KArgs &, SadPlan, int, hipStream_t) { return hipErrorNotSupported; }
-hipError_t lw_launch_decode_bf16(const KArgs &, SadPlan, hipStream_t) { return hipErrorNotSupported; }

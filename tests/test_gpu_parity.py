@@ -201,3 +201,59 @@ def test_full_size_q6_one_matrix(torch, dg):
     rows = _sample_rows(mat.rows, 48, 5)
     y = _run_gemv(dg, torch, db, x, 1, mat.rows)
     assert rel_err(y[:, rows], O.gemv_q(codes, d, m, x, 1, rows=rows)) <= TOL
+
+
+# ------------------------------------------------------------------ bf16 exponent coding
+
+def _decode_bf16(dg, torch, db, rows, cols, n_tiles):
+    out = torch.zeros(rows * cols, dtype=torch.int16, device="cuda")
+    lb = torch.zeros(n_tiles * 32, dtype=torch.int32, device="cuda")
+    dg.lw_decode_only(db, out, lane_bits=lb)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint16).reshape(rows, cols), lb.cpu().numpy().view(np.uint32)
+
+
+SMALL_BF16 = [(64, 256, 0.0, 201), (192, 768, 0.001, 202), (128, 1280, 0.02, 203), (320, 2304, 0.002, 204),
+              (64, 4096, 0.0, 205)]
+
+
+@pytest.mark.parametrize("case", SMALL_BF16, ids=lambda c: "-".join(map(str, c)))
+def test_bf16_decode_bit_exact_small(torch, dg, case):
+    rows, cols, frac, seed = case
+    say("bf16 decode", case)
+    w, x = synth.gen_bf16_custom(rows, cols, seed, outlier_frac=frac)
+    b = dg.lw_bundle_build_bf16(w)
+    info = dg.lw_bundle_get_info(b)
+    if frac > 0:
+        assert info["n_verbatim"] > 0
+    db = _upload(dg, torch, b)
+    w2, bits = _decode_bf16(dg, torch, db, rows, cols, info["n_tiles"])
+    assert np.array_equal(w2, w)
+    _, obits = O.decode_bundle_bf16(O.build_bundle_bf16(w))
+    assert np.array_equal(bits, obits)
+
+
+@pytest.mark.parametrize("case", SMALL_BF16, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("batch", [1, 3, 7])
+def test_bf16_gemv_small(torch, dg, case, batch):
+    rows, cols, frac, seed = case
+    say("bf16 gemv", case, batch)
+    w, x = synth.gen_bf16_custom(rows, cols, seed, outlier_frac=frac)
+    db = _upload(dg, torch, dg.lw_bundle_build_bf16(w))
+    y = _run_gemv(dg, torch, db, x, batch, rows)
+    assert rel_err(y, O.gemv_bf16(w, x, batch)) <= TOL
+
+
+def test_full_size_bf16(torch, dg):
+    mat = synth.CONFIGS[4][0]
+    say("full", mat.name)
+    w, x = synth.gen_bf16(mat)
+    b = dg.lw_bundle_build_bf16(w)
+    info = dg.lw_bundle_get_info(b)
+    db = _upload(dg, torch, b)
+    w2, _ = _decode_bf16(dg, torch, db, mat.rows, mat.cols, info["n_tiles"])
+    assert np.array_equal(w2, w)
+    del w2
+    rows = _sample_rows(mat.rows, 64, 4)
+    y = _run_gemv(dg, torch, db, x, 1, mat.rows)
+    assert rel_err(y[:, rows], O.gemv_bf16(w, x, 1, rows=rows)) <= TOL
