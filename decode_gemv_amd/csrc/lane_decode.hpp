@@ -305,6 +305,7 @@ LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g
 {
     for (int i = threadIdx.x; i < BATCH * 128; i += blockDim.x) {
         const int b = i >> 7, row = i & 127;
+        if (b >= a.batch) break;
         float v = 0.f;
         for (int w = 0; w < waves; w++) v += red[(w * BATCH + b) * 128 + row];
         if (row0 + row < a.rows) {
@@ -325,6 +326,7 @@ LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g
     if (!*last_flag) return;
     for (int i = threadIdx.x; i < BATCH * 128; i += blockDim.x) {
         const int b = i >> 7, row = i & 127;
+        if (b >= a.batch) break;
         if (row0 + row >= a.rows) continue;
         float v = 0.f;
         for (int gg = 0; gg < a.groups; gg++)

@@ -1,0 +1,328 @@
+// mfma.hip -- fused decode + GEMM for batch 8..16 on the matrix cores of
+// gfx950 ("LazyWeights" bundle, decoded as in lane_decode.hpp; the matrix
+// product fed from on-chip memory follows the reconstructive matmul idea of
+// "Unweight", section "How reconstructive matmul works").
+//
+// At batch >= 8 the product is a real dense contraction (64 rows x 32
+// columns x 16 batch per step), so the decoded weights go through a small
+// LDS staging tile into v_mfma_f32_16x16x16{f16,bf16}:
+//   - each lane decodes its tile row (rows of the two row bands = the 64
+//     lanes of the wavefront) 32 columns at a time and writes them as
+//     16-bit values to stage[lane][0..31] (row stride 80 bytes: conflict-
+//     free 16-byte writes and 8-byte fragment reads);
+//   - every 32 columns, 2 k-steps x 4 row blocks of 16x16x16 MFMA
+//     accumulate D[row][batch] += W[row][k] * X[k][batch], with the X
+//     fragments (x[batch][k], zero for batch >= the call's batch) loaded
+//     from global memory one chunk ahead;
+//   - dequantisation uses y = d * (W q x) - m * sum(x) per tile row.
+// MFMA 16x16x16 lane layout: A lane i = A[i%16][4(i/16)..+3], B lane i =
+// B[4(i/16)..+3][i%16], D lane i = D[4(i/16)+j][i%16], j = 0..3.
+#include <type_traits>
+
+#include "lane_decode.hpp"
+
+namespace {
+
+constexpr int WAVES = 4;
+constexpr int NB = 16;                     // batch columns of the MFMA tile
+constexpr int STAGE_STRIDE = 80;           // bytes per staged row (32 x 2 bytes + 16 pad)
+constexpr int STAGE_BYTES = 64 * STAGE_STRIDE;
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct LdsLayout {
+    uint32_t tiles, stage, flag, total;
+};
+
+__host__ __device__ inline LdsLayout lds_layout(int max_words)
+{
+    LdsLayout L;
+    L.stage = LW_TAB_BYTES;
+    L.tiles = L.stage + WAVES * STAGE_BYTES;
+    const uint32_t tiles = (uint32_t)(WAVES * 2 * (max_words + 3) * 128);
+    const uint32_t red = (uint32_t)(WAVES * NB * 128 * 4);
+    L.flag = L.tiles + (tiles > red ? tiles : red);
+    L.total = L.flag + 16;
+    return L;
+}
+
+struct LaneCtx {
+    int wave, lane, half, l, g, rbp, cb, rb, t;
+    bool wave_active, lane_active;
+};
+
+LW_DEV LaneCtx lane_ctx(const KArgs &a)
+{
+    LaneCtx c;
+    c.wave = (int)lw_wave_id();
+    c.lane = threadIdx.x & 63;
+    c.half = c.lane >> 5;
+    c.l = c.lane & 31;
+    c.g = blockIdx.x;
+    c.rbp = blockIdx.y;
+    c.cb = c.g * WAVES + c.wave;
+    c.wave_active = c.cb < a.n_cb;
+    const int rb = c.rbp * 2 + c.half;
+    c.lane_active = c.wave_active && rb < a.n_rb;
+    c.rb = rb < a.n_rb ? rb : rb - 1;
+    c.t = c.rb * a.n_cb + (c.wave_active ? c.cb : 0);
+    return c;
+}
+
+// Ordinal, in the verbatim store, of segment `bit` (4*row + segment) of tile t.
+LW_DEV uint32_t lw_verbatim_ordinal(const KArgs &a, int64_t t, int bit)
+{
+    const uint32_t *vb = a.vb_bits + (size_t)t * 8;
+    uint32_t n = a.vb_start[t];
+    for (int w = 0; w < bit / 32; w++) n += __builtin_popcount(vb[w]);
+    return n + __builtin_popcount(vb[bit / 32] & ((1u << (bit % 32)) - 1u));
+}
+
+LW_DEV void lw_st32(uint32_t addr, uint32_t v) { *(__attribute__((address_space(3))) uint32_t *)(size_t)addr = v; }
+LW_DEV u32x2 lw_ld64(uint32_t addr) { return *(__attribute__((address_space(3))) const u32x2 *)(size_t)addr; }
+
+template <int KIND>
+LW_DEV f4 mfma(u32x2 a, u32x2 b, f4 acc)
+{
+    if constexpr (KIND == LW_BF16_EXP)
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b), acc, 0,
+                                                          0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4, a), __builtin_bit_cast(h4, b), acc, 0, 0, 0);
+}
+
+template <int KIND, int N8, int N16>
+__global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr int GPC = KIND == LW_Q4_PAIR ? 4 : 8;      // groups of four symbols per 32-column chunk
+    constexpr int NG = KIND == LW_Q4_PAIR ? 32 : 64;     // groups per tile row
+    const LdsLayout L = lds_layout(a.max_words);
+    const LaneCtx c = lane_ctx(a);
+    const int S = a.max_words + 3;
+    uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + (c.wave * 2 + c.half) * S * 32;
+    const uint32_t stage = (uint32_t)(size_t)(lds + L.stage + c.wave * STAGE_BYTES);
+    const uint32_t my_row = stage + (uint32_t)(c.lane * STAGE_STRIDE);
+    // MFMA fragment coordinates of this lane
+    const int fr = c.lane & 15, fk = c.lane >> 4;
+
+    lw_stage_tab(lds, a.tab, a.min_len, a.max_len, false);
+    if (c.wave_active) {
+        const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
+        lw_stage_tile(slots, a.words, w0, (w1 - w0) >> 5, c.l);
+    }
+    __syncthreads();
+
+    // x fragments: lane holds x[b = fr][col0 + 16 kk + 4 fk .. +3] for kk = 0, 1
+    const bool xb_ok = fr < a.batch;
+    const uint16_t *xrow = a.x + (size_t)(xb_ok ? fr : 0) * a.cols + (size_t)(c.wave_active ? c.cb : 0) * 256 + 4 * fk;
+    auto load_x = [&](int chunk, u32x2 (&dst)[2]) {
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++) {
+            const u32x2 v = *reinterpret_cast<const u32x2 *>(xrow + 32 * chunk + 16 * kk);
+            dst[kk] = xb_ok ? v : u32x2{0u, 0u};
+        }
+    };
+
+    f4 acc[2][4];
+#pragma unroll
+    for (int p = 0; p < 2; p++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) acc[p][r] = f4{0.f, 0.f, 0.f, 0.f};
+    float sx = 0.f;                          // sum of x[fr][k] over this lane's k subset
+
+    if (c.wave_active) {
+        LaneDec d;
+        const bool ok = lw_lane_init(d, lds, slots, c.l, a);
+        if (ok) {
+            auto run_row = [&](auto pc) {
+                constexpr int p = decltype(pc)::value;
+                u32x2 xcur[2];
+                load_x(0, xcur);
+                uint32_t pend = 0;
+                auto mfma_step = [&](int chunk) {
+#pragma unroll
+                    for (int kk = 0; kk < 2; kk++) {
+                        if (p == 0) {
+                            const f4 xf = {lw_half_lo(xcur[kk].x), lw_half_hi(xcur[kk].x), lw_half_lo(xcur[kk].y),
+                                           lw_half_hi(xcur[kk].y)};
+                            if constexpr (KIND == LW_BF16_EXP)
+                                sx += __builtin_bit_cast(float, xcur[kk].x << 16) +
+                                      __builtin_bit_cast(float, xcur[kk].x & 0xFFFF0000u) +
+                                      __builtin_bit_cast(float, xcur[kk].y << 16) +
+                                      __builtin_bit_cast(float, xcur[kk].y & 0xFFFF0000u);
+                            else
+                                sx += xf.x + xf.y + xf.z + xf.w;
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; r++) {
+                            const u32x2 af = lw_ld64(stage + (uint32_t)((16 * r + fr) * STAGE_STRIDE + 32 * kk + 8 * fk));
+                            acc[p][r] = mfma<KIND>(af, xcur[kk], acc[p][r]);
+                        }
+                    }
+                    // x of the next chunk, used one chunk of decoding later
+                    load_x(chunk + 1 < 8 ? chunk + 1 : chunk, xcur);
+                };
+                auto put = [&](int g, int j, uint32_t pay, uint32_t smw) {
+                    // 16-bit weights of this symbol into the staged row
+                    if constexpr (KIND == LW_Q4_PAIR) {
+                        lw_st32(my_row + (uint32_t)(((g % GPC) * 4 + j) * 4), pay);
+                    } else {
+                        if (j & 1) {
+                            uint32_t w2;
+                            if constexpr (KIND == LW_BF16_EXP) {
+                                const uint32_t spread = __builtin_amdgcn_perm(smw, smw, j == 1 ? 0x01010000u : 0x03030202u);
+                                w2 = (spread & 0x807F807Fu) | pend | pay;
+                            } else {
+                                w2 = pend | pay;
+                            }
+                            lw_st32(my_row + (uint32_t)(((g % GPC) * 2 + (j >> 1)) * 4), w2);
+                        } else {
+                            pend = pay;
+                        }
+                    }
+                    if (j == 3 && (g % GPC) == GPC - 1) mfma_step(g / GPC);
+                };
+                auto pay_off = [](int j) { return (KIND != LW_Q4_PAIR && (j & 1)) ? (LW_TPAY_HI - LW_TPAY) : 0u; };
+                if constexpr (KIND == LW_BF16_EXP) {
+                    // sign+mantissa words stream in 16-group chunks, as in the VALU kernel
+                    const uint32_t *smrow = a.sm + (size_t)c.t * 4096 + (size_t)p * 64 * 32 + c.l;
+                    struct XA {
+                        uint32_t sm;
+                    };
+                    uint32_t ring[2][16];
+                    auto run_chunk = [&](int ch, const uint32_t (&cur)[16]) {
+                        lw_decode_pipelined<N8, N16, 16, XA, true>(
+                            d, a, pay_off, [&](int g) { return XA{cur[g]}; },
+                            [&](int g, int j, uint32_t pay, const XA &x) { put(16 * ch + g, j, pay, x.sm); });
+                    };
+#pragma unroll
+                    for (int i = 0; i < 16; i++) ring[0][i] = smrow[i * 32];
+#pragma unroll
+                    for (int ch = 0; ch < 4; ch += 2) {
+#pragma unroll
+                        for (int i = 0; i < 16; i++) ring[1][i] = smrow[((ch + 1) * 16 + i) * 32];
+                        run_chunk(ch, ring[0]);
+                        if (ch + 2 < 4)
+#pragma unroll
+                            for (int i = 0; i < 16; i++) ring[0][i] = smrow[((ch + 2) * 16 + i) * 32];
+                        run_chunk(ch + 1, ring[1]);
+                    }
+                } else {
+                    struct NoAux {};
+                    lw_decode_pipelined<N8, N16, NG, NoAux>(
+                        d, a, pay_off, [](int) { return NoAux{}; },
+                        [&](int g, int j, uint32_t pay, const NoAux &) { put(g, j, pay, 0u); });
+                }
+            };
+            run_row(std::integral_constant<int, 0>{});
+            run_row(std::integral_constant<int, 1>{});
+        } else {
+#pragma unroll
+            for (int p = 0; p < 2; p++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) acc[p][r] = f4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                                           __builtin_nanf("")};
+        }
+    }
+    // sum of x over the tile's 256 columns for batch column fr
+    sx += __shfl_xor(sx, 16, 64);
+    sx += __shfl_xor(sx, 32, 64);
+
+    __syncthreads();                      // tiles no longer read: reuse for the reduction
+    float *red = reinterpret_cast<float *>(lds + L.tiles);
+    // D lane layout: row R = 16 r + 4 fk + jj of the 64 staged rows (= wavefront
+    // lane R: half R/32, lane R%32), batch column fr
+#pragma unroll
+    for (int p = 0; p < 2; p++)
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+                const int R = 16 * r + 4 * fk + jj;
+                const int h = R >> 5, l = R & 31;
+                const int rb = c.rbp * 2 + h;
+                float v = 0.f;
+                if (c.wave_active && rb < a.n_rb) {
+                    if constexpr (KIND == LW_BF16_EXP) {
+                        v = acc[p][r][jj];           // bf16 bundles carry no scales
+                    } else {
+                        const uint32_t w = a.dm[((size_t)rb * a.n_cb + c.cb) * 64 + 2 * l + p];
+                        v = lw_half_lo(w) * acc[p][r][jj] - lw_half_hi(w) * sx;
+                    }
+                }
+                red[(c.wave * NB + fr) * 128 + h * 64 + 2 * l + p] = v;
+            }
+    __syncthreads();
+    if constexpr (KIND == LW_BF16_EXP) {
+        // verbatim segments (rare): the lane owning each row replaces the
+        // placeholder weights' contribution by the stored values', per batch
+        const uint32_t bits =
+            c.lane_active ? (a.vb_bits[(size_t)c.t * 8 + c.l / 4] >> (8 * (c.l % 4))) & 0xFFu : 0u;
+        if (bits) {
+            const uint16_t *xcol = a.x + (size_t)c.cb * 256;
+            for (int q = 0; q < 8; q++) {
+                if (!((bits >> q) & 1u)) continue;
+                const int p = q >> 2, seg = q & 3;
+                const uint32_t ord = lw_verbatim_ordinal(a, c.t, 8 * c.l + q);
+                const uint16_t *vv = a.verbatim + (size_t)ord * 64;
+                const uint32_t *smw = a.sm + (size_t)c.t * 4096 + (size_t)p * 64 * 32 + c.l;
+                for (int b = 0; b < a.batch; b++) {
+                    float sacc = 0.f;
+                    for (int k = 0; k < 64; k++) {
+                        const int col = 64 * seg + k;
+                        const uint32_t smb = (smw[(col / 4) * 32] >> (8 * (col % 4))) & 0xFFu;
+                        const uint32_t ph = ((smb & 0x80u) << 8) | (a.pal0 << 7) | (smb & 0x7Fu);
+                        const float wdiff = __builtin_bit_cast(float, (uint32_t)vv[k] << 16) -
+                                            __builtin_bit_cast(float, ph << 16);
+                        sacc += wdiff * __builtin_bit_cast(float, (uint32_t)xcol[(size_t)b * a.cols + col] << 16);
+                    }
+                    red[(c.wave * NB + b) * 128 + c.half * 64 + 2 * c.l + p] += sacc;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    uint32_t *last_flag = reinterpret_cast<uint32_t *>(lds + L.flag);
+    lw_finish_rows<NB>(a, red, (int64_t)c.rbp * 128, c.g, c.rbp, WAVES, last_flag);
+}
+
+template <int KIND, int N8, int N16>
+hipError_t launch(const KArgs &a, hipStream_t s)
+{
+    const LdsLayout L = lds_layout(a.max_words);
+    dim3 grid((unsigned)a.groups, (unsigned)((a.n_rb + 1) / 2));
+    auto kern = k_gemv_mfma<KIND, N8, N16>;
+    hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, grid, dim3(256), L.total, s, a);
+    return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t by_plan(const KArgs &a, SadPlan p, hipStream_t s)
+{
+    switch (p.n8ops * 2 + p.n16ops) {
+    case 0: return launch<KIND, 0, 0>(a, s);
+    case 1: return launch<KIND, 0, 1>(a, s);
+    case 2: return launch<KIND, 1, 0>(a, s);
+    case 3: return launch<KIND, 1, 1>(a, s);
+    case 4: return launch<KIND, 2, 0>(a, s);
+    case 5: return launch<KIND, 2, 1>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t lw_launch_gemv_mfma(const KArgs &a, int kind, SadPlan p, int batch, hipStream_t s)
+{
+    if (batch < 1 || batch > NB) return hipErrorInvalidValue;
+    if (kind == LW_Q4_PAIR) return by_plan<LW_Q4_PAIR>(a, p, s);
+    if (kind == LW_Q6_SINGLE) return by_plan<LW_Q6_SINGLE>(a, p, s);
+    if (kind == LW_BF16_EXP) return by_plan<LW_BF16_EXP>(a, p, s);
+    return hipErrorInvalidValue;
+}

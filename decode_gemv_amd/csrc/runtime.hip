@@ -130,14 +130,13 @@ extern "C" lw_status lw_gemv(const lw_dev_bundle *db, const void *x, float *y, i
     a.batch = batch;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    if (db->h.kind == LW_BF16_EXP) {
-        a.pal0 = db->tab.payload[0] >> 7;
-        e = lw_launch_gemv_bf16(a, plan_of(db, a), batch, s);
-    } else if (batch < 8) {
-        e = lw_launch_gemv_q(a, db->h.kind, plan_of(db, a), batch, s);
-    } else {
+    a.pal0 = db->h.kind == LW_BF16_EXP ? db->tab.payload[0] >> 7 : 0u;
+    if (batch >= 8)                        // a real dense contraction: matrix cores
         e = lw_launch_gemv_mfma(a, db->h.kind, plan_of(db, a), batch, s);
-    }
+    else if (db->h.kind == LW_BF16_EXP)
+        e = lw_launch_gemv_bf16(a, plan_of(db, a), batch, s);
+    else
+        e = lw_launch_gemv_q(a, db->h.kind, plan_of(db, a), batch, s);
     if (e == hipErrorNotSupported) return lw_fail(LW_E_UNSUPPORTED, "no kernel for this kind and batch");
     if (e != hipSuccess) return hip_fail(e, "gemv launch");
     return LW_OK;

@@ -257,3 +257,44 @@ def test_full_size_bf16(torch, dg):
     rows = _sample_rows(mat.rows, 64, 4)
     y = _run_gemv(dg, torch, db, x, 1, mat.rows)
     assert rel_err(y[:, rows], O.gemv_bf16(w, x, 1, rows=rows)) <= TOL
+
+
+# ------------------------------------------------------------------ batch >= 8: matrix cores
+
+MFMA_CASES = [("q4", 64, 256, "normal", 301), ("q4", 192, 1280, "laplace", 302), ("q4", 320, 2304, "normal", 303),
+              ("q6", 128, 768, "normal", 304), ("q6", 64, 2048, "uniform", 305)]
+
+
+@pytest.mark.parametrize("case", MFMA_CASES, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("batch", [8, 11, 16])
+def test_gemv_mfma_small(torch, dg, case, batch):
+    kind_s, rows, cols, law, seed = case
+    say("mfma", case, batch)
+    kind = dg.LW_Q4_PAIR if kind_s == "q4" else dg.LW_Q6_SINGLE
+    codes, d, m, x = _gen_small(*case)
+    db = _upload(dg, torch, dg.lw_bundle_build_q(kind, codes, d, m))
+    y = _run_gemv(dg, torch, db, x, batch, rows)
+    assert rel_err(y, O.gemv_q(codes, d, m, x, batch)) <= TOL
+    assert np.array_equal(y, _run_gemv(dg, torch, db, x, batch, rows))
+
+
+@pytest.mark.parametrize("case", SMALL_BF16[:4], ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("batch", [8, 16])
+def test_bf16_gemv_mfma_small(torch, dg, case, batch):
+    rows, cols, frac, seed = case
+    say("bf16 mfma", case, batch)
+    w, x = synth.gen_bf16_custom(rows, cols, seed, outlier_frac=frac)
+    db = _upload(dg, torch, dg.lw_bundle_build_bf16(w))
+    y = _run_gemv(dg, torch, db, x, batch, rows)
+    assert rel_err(y, O.gemv_bf16(w, x, batch)) <= TOL
+
+
+def test_full_size_down_batch16(torch, dg):
+    mat = synth.CONFIGS[3][0]
+    say("full mfma", mat.name)
+    codes, d, m, x = synth.gen_q(mat)
+    db = _upload(dg, torch, dg.lw_bundle_build_q(dg.LW_Q4_PAIR, codes, d, m))
+    rows = _sample_rows(mat.rows, 48, 33)
+    y = _run_gemv(dg, torch, db, x, 16, mat.rows)
+    assert np.all(np.isfinite(y))
+    assert rel_err(y[:, rows], O.gemv_q(codes, d, m, x, 16, rows=rows)) <= TOL
