@@ -74,35 +74,52 @@ def main():
     import synth
 
     mats = synth.CONFIGS[a.config]
-    mat = mats[0]
-    kind = {"q4": dg.LW_Q4_PAIR, "q6": dg.LW_Q6_SINGLE, "bf16": dg.LW_BF16_EXP}[mat.kind]
+    kinds = {"q4": dg.LW_Q4_PAIR, "q6": dg.LW_Q6_SINGLE, "bf16": dg.LW_BF16_EXP}
     t0 = time.time()
-    if kind == dg.LW_BF16_EXP:
-        w, xb = synth.gen_bf16(mat)
-        b = dg.lw_bundle_build_bf16(w)
-        codes = d = m = None
-    else:
-        codes, d, m, xb = synth.gen_q(mat)
-        b = dg.lw_bundle_build_q(kind, codes, d, m)
-    info = dg.lw_bundle_get_info(b)
+    inputs, bundles = [], []
+    for mat in mats:                      # one matrix, or the three of a 70B MLP pass
+        if mat.kind == "bf16":
+            w, xb = synth.gen_bf16(mat)
+            bundles.append(dg.lw_bundle_build_bf16(w))
+            inputs.append((None, None, None, xb))
+            del w
+        else:
+            codes, d, m, xb = synth.gen_q(mat)
+            bundles.append(dg.lw_bundle_build_q(kinds[mat.kind], codes, d, m))
+            inputs.append((codes, d, m, xb))
+    infos = [dg.lw_bundle_get_info(b) for b in bundles]
     build_s = time.time() - t0
+    mat = mats[0]
+    kind = kinds[mat.kind]
+    codes, d, m, xb = inputs[0]
 
-    img = torch.from_numpy(dg.lw_bundle_image(b)).cuda()
-    n_copies = copies_for(int(info["image_bytes"]))
-    dbs = []
+    total_image = sum(int(i["image_bytes"]) for i in infos)
+    n_copies = copies_for(total_image)
+    dbs = []                              # dbs[copy][matrix]
     for _ in range(n_copies):
-        buf = torch.empty_like(img)
-        dbs.append(dg.lw_bundle_upload(b, buf))
+        row = []
+        for b, info in zip(bundles, infos):
+            buf = torch.empty(int(info["image_bytes"]), dtype=torch.uint8, device="cuda")
+            row.append(dg.lw_bundle_upload(b, buf))
+        dbs.append(row)
     torch.cuda.synchronize()
     batch = a.batch
-    x = torch.from_numpy(np.ascontiguousarray(xb[:batch]).view(np.int16)).cuda()
-    y = torch.empty((batch, mat.rows), dtype=torch.float32, device="cuda")
+    xs = [torch.from_numpy(np.ascontiguousarray(inp[3][:batch]).view(np.int16)).cuda() for inp in inputs]
+    ys = [torch.empty((batch, mm.rows), dtype=torch.float32, device="cuda") for mm in mats]
 
-    ms = time_loop(torch, lambda i: dg.lw_gemv(dbs[i], x, y, batch), n_copies, a.steps, a.warmup)
+    def step(i):
+        for j in range(len(mats)):
+            dg.lw_gemv(dbs[i][j], xs[j], ys[j], batch)
+
+    ms = time_loop(torch, step, n_copies, a.steps, a.warmup)
     us = ms * 1e3
-    coded = int(info["coded_bytes"])
-    algo_bytes = coded + 2 * batch * mat.cols + 4 * batch * mat.rows
+    coded = sum(int(i["coded_bytes"]) for i in infos)
+    twin_bytes = sum(int(i["twin_bytes"]) for i in infos)
+    weights = sum(mm.rows * mm.cols for mm in mats)
+    algo_bytes = coded + sum(2 * batch * mm.cols + 4 * batch * mm.rows for mm in mats)
     achieved = algo_bytes / (us * 1e-6) / 1e9
+    shape = " + ".join(f"{mm.rows}x{mm.cols}" for mm in mats)
+    symbols = sum(mm.rows * mm.cols // (2 if mm.kind == "q4" else 1) for mm in mats)
     result = {
         "metric": "fused decode+GEMV us/matrix; coded-byte HBM GB/s and % of MI355X HBM peak",
         "value": round(coded / (us * 1e-6) / 1e9, 2),
@@ -112,29 +129,30 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp16 x, fp32 accumulate" if kind != dg.LW_BF16_EXP else "bf16 x, fp32 accumulate",
         "data": "synthetic",
-        "config": {"workload": f"{mat.name}: {mat.rows}x{mat.cols} {mat.kind} coded, batch {batch}",
-                   "rows": mat.rows, "cols": mat.cols, "batch": batch, "bundle_copies": n_copies},
-        "us_per_matrix": round(us, 3),
+        "config": {"workload": f"{' + '.join(mm.name for mm in mats)}: {shape} {mat.kind} coded, batch {batch}",
+                   "matrices": len(mats), "batch": batch, "bundle_copies": n_copies},
+        "us_per_matrix": round(us / len(mats), 3),
+        "us_per_step": round(us, 3),
         "pct_hbm_peak_coded": round(100 * coded / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
         "coded_bytes": coded,
-        "bits_per_weight": round(8 * coded / (mat.rows * mat.cols), 4),
-        "equiv_uncompressed_GBs": round(int(info["twin_bytes"]) / (us * 1e-6) / 1e9, 2),
-        "B_eff_GBs": round(2 * mat.rows * mat.cols / (us * 1e-6) / 1e9, 2),
-        "symbols_per_s": (mat.rows * mat.cols // (2 if kind == dg.LW_Q4_PAIR else 1)) / (us * 1e-6),
+        "bits_per_weight": round(8 * coded / weights, 4),
+        "equiv_uncompressed_GBs": round(twin_bytes / (us * 1e-6) / 1e9, 2),
+        "B_eff_GBs": round(2 * weights / (us * 1e-6) / 1e9, 2),
+        "symbols_per_s": symbols / (us * 1e-6),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "algorithmic_bytes_per_launch": algo_bytes},
+                     "algorithmic_bytes_per_launch": algo_bytes // len(mats)},
     }
 
-    if not a.no_extras and kind == dg.LW_Q4_PAIR:
+    if not a.no_extras and kind == dg.LW_Q4_PAIR and len(mats) == 1:
         # fixed-width twin on the same codes and scales (latency bar)
         twin, dmw = dg.lw_twin_build(codes, 4, d, m)
         tw0 = torch.from_numpy(twin).cuda()
         dm0 = torch.from_numpy(dmw.view(np.int32)).cuda()
         tn = copies_for(twin.nbytes)
         tws = [tw0.clone() for _ in range(tn)]
-        yt = torch.empty_like(y)
-        tms = time_loop(torch, lambda i: dg.lw_twin_gemv(tws[i], dm0, 4, mat.rows, mat.cols, x, yt, batch),
+        yt = torch.empty_like(ys[0])
+        tms = time_loop(torch, lambda i: dg.lw_twin_gemv(tws[i], dm0, 4, mat.rows, mat.cols, xs[0], yt, batch),
                         tn, a.steps, a.warmup)
         tbytes = twin.nbytes + dmw.nbytes
         result["twin"] = {"us_per_matrix": round(tms * 1e3, 3), "bytes": tbytes,
@@ -143,7 +161,7 @@ def main():
         del tws
         # decode only (restores the packed codes to HBM)
         out = torch.empty(mat.rows * mat.cols // 2, dtype=torch.uint8, device="cuda")
-        dms = time_loop(torch, lambda i: dg.lw_decode_only(dbs[i], out), n_copies, max(a.steps // 4, 10),
+        dms = time_loop(torch, lambda i: dg.lw_decode_only(dbs[i][0], out), n_copies, max(a.steps // 4, 10),
                         a.warmup)
         result["decode_only"] = {"us_per_matrix": round(dms * 1e3, 3),
                                  "symbols_per_s": (mat.rows * mat.cols // 2) / (dms * 1e-3)}
@@ -155,7 +173,7 @@ def main():
         torch.cuda.synchronize()
         result["copy_calib_bytes"] = src.numel()
 
-    if not a.no_cpu and kind != dg.LW_BF16_EXP:
+    if not a.no_cpu and kind != dg.LW_BF16_EXP and len(mats) == 1:
         import oracle as O
         # the oracle as it stands, one thread: limit-method decode of every
         # tile and the fp64 GEMV, on the whole matrix
