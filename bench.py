@@ -12,13 +12,17 @@ with HIP events on the stream the kernels run on (torch's current stream).
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20]
 
-Prints one JSON line.  Extra flags: --config {1,2,3,4,5} (default 2),
+Prints one JSON line.  Extra flags: --workload NAME (default
+q4_up_14336x4096; the others are q4_256x1024, q4_down_4096x14336,
+bf16_up_14336x4096 and q6_mlp_70b),
 --batch, --no-cpu (skip the oracle CPU baseline), --copy-calib (also run a
 plain device copy of known size, for counter calibration).
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +32,38 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MALL_BYTES = 256 << 20
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def sources_digest() -> str:
+    """Digest of the HIP sources and the ABI header: a recorded traffic figure
+    is only reported while the kernels it was measured on are unchanged."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "decode_gemv_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "lw.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, batch: int, digest: str):
+    """HBM bytes per launch of the dominant kernel from the counter runs
+    recorded in profiles/hbm_traffic.txt (FETCH_SIZE and WRITE_SIZE, each
+    scaled by its copy-kernel calibration factor), or None when no record
+    matches this workload, batch and source digest."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            f = line.split()
+            if not f or f[0].startswith("#"):
+                continue
+            if f[0] == workload and int(f[1]) == batch and f[3] == digest:
+                return int(f[2])
+    return None
 
 
 def parse():
@@ -35,7 +71,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", type=int, default=2)
+    p.add_argument("--workload", default="q4_up_14336x4096")
     p.add_argument("--batch", type=int, default=1)
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-extras", action="store_true")
@@ -73,7 +109,7 @@ def main():
     import decode_gemv_amd as dg
     import synth
 
-    mats = synth.CONFIGS[a.config]
+    mats = synth.WORKLOADS[a.workload]
     kinds = {"q4": dg.LW_Q4_PAIR, "q6": dg.LW_Q6_SINGLE, "bf16": dg.LW_BF16_EXP}
     t0 = time.time()
     inputs, bundles = [], []
@@ -111,6 +147,7 @@ def main():
         for j in range(len(mats)):
             dg.lw_gemv(dbs[i][j], xs[j], ys[j], batch)
 
+    digest = sources_digest()
     ms = time_loop(torch, step, n_copies, a.steps, a.warmup)
     us = ms * 1e3
     coded = sum(int(i["coded_bytes"]) for i in infos)
@@ -140,7 +177,8 @@ def main():
         "B_eff_GBs": round(2 * weights / (us * 1e-6) / 1e9, 2),
         "symbols_per_s": symbols / (us * 1e-6),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(a.workload, batch, digest),
                      "algorithmic_bytes_per_launch": algo_bytes // len(mats)},
     }
 
@@ -189,6 +227,7 @@ def main():
                                   "cores": 1, "kind": "oracle",
                                   "sample": f"whole {mat.rows}x{mat.cols} matrix, limit-method decode + fp64 GEMV, "
                                             f"best of 2 runs: {tc * 1e6:.0f} us/matrix"}
+    result["kernel_sources_digest"] = digest
     result["build_s"] = round(build_s, 2)
     print(json.dumps(result), flush=True)
 

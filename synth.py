@@ -8,19 +8,21 @@ Workloads (shapes of Llama-3.1-8B and Llama-70B MLP matrices, the matrices the
 Unweight write-up compresses, "Understanding BF16 weight structure"; code
 histograms stand in for the concentrated GPTQ codes of LazyWeights, Fig. 2):
 
-  1  256x1024, 4-bit codes q = clamp(rint(N(7.5, 1.8)), 0, 15)
-  2  14336x4096 (up/gate), same code law
-  3  4096x14336 (down), q = clamp(rint(Laplace(7.5, b=1.2)), 0, 15)
-  4  14336x4096 bf16 weights W = bf16(N(0, 0.02)), bf16 activations
-  5  70B MLP: gate 28672x8192 (j=0), up 28672x8192 (j=1), down 8192x28672
-     (j=2), 6-bit codes q = clamp(rint(N(31.5, 5)), 0, 63)
+  q4_256x1024          256x1024, 4-bit codes q = clamp(rint(N(7.5, 1.8)), 0, 15)
+  q4_up_14336x4096     14336x4096 (up/gate), same code law
+  q4_down_4096x14336   4096x14336 (down), q = clamp(rint(Laplace(7.5, b=1.2)), 0, 15)
+  bf16_up_14336x4096   14336x4096 bf16 weights W = bf16(N(0, 0.02)), bf16 activations
+  q6_mlp_70b           gate 28672x8192, up 28672x8192, down 8192x28672, 6-bit
+                       codes q = clamp(rint(N(31.5, 5)), 0, 63), run back to back
 
-For the quantised configs each 256-weight super-block (256 consecutive weights
-of one row) carries fp16 d ~ U(0.005, 0.02) and m = 8 d (exact in fp16);
-activations are fp16 N(0, 1), drawn as 16 rows so that batch b uses the first b.
+For the quantised workloads each 256-weight super-block (256 consecutive
+weights of one row) carries fp16 d ~ U(0.005, 0.02) and m = 8 d (exact in
+fp16); activations are fp16 N(0, 1), drawn as 16 rows so that batch b uses the
+first b.
 
-Seeds: config i, matrix j draws from SeedSequence(1000*i + j).spawn(3), the
-three children feeding (codes or W), (scales), (x) in that order.
+Seeds: each matrix has a seed s (1000, 2000, 3000, 4000 and 5000..5002 in the
+order above) and draws from SeedSequence(s).spawn(3), the three children
+feeding (codes or W), (scales), (x) in that order.
 """
 from __future__ import annotations
 
@@ -33,8 +35,7 @@ XROWS = 16           # activation rows drawn per matrix (max batch)
 
 @dataclasses.dataclass(frozen=True)
 class Matrix:
-    cfg: int
-    j: int
+    seed: int
     name: str
     kind: str        # "q4", "q6" or "bf16"
     rows: int
@@ -44,21 +45,26 @@ class Matrix:
     scale: float
 
 
-CONFIGS = {
-    1: [Matrix(1, 0, "c1_256x1024_q4", "q4", 256, 1024, "normal", 7.5, 1.8)],
-    2: [Matrix(2, 0, "c2_up_14336x4096_q4", "q4", 14336, 4096, "normal", 7.5, 1.8)],
-    3: [Matrix(3, 0, "c3_down_4096x14336_q4", "q4", 4096, 14336, "laplace", 7.5, 1.2)],
-    4: [Matrix(4, 0, "c4_up_14336x4096_bf16", "bf16", 14336, 4096, "bf16normal", 0.0, 0.02)],
-    5: [Matrix(5, 0, "c5_gate_28672x8192_q6", "q6", 28672, 8192, "normal", 31.5, 5.0),
-        Matrix(5, 1, "c5_up_28672x8192_q6", "q6", 28672, 8192, "normal", 31.5, 5.0),
-        Matrix(5, 2, "c5_down_8192x28672_q6", "q6", 8192, 28672, "normal", 31.5, 5.0)],
+WORKLOADS = {
+    "q4_256x1024": [Matrix(1000, "q4_256x1024", "q4", 256, 1024, "normal", 7.5, 1.8)],
+    "q4_up_14336x4096": [Matrix(2000, "q4_up_14336x4096", "q4", 14336, 4096, "normal", 7.5, 1.8)],
+    "q4_down_4096x14336": [Matrix(3000, "q4_down_4096x14336", "q4", 4096, 14336, "laplace", 7.5, 1.2)],
+    "bf16_up_14336x4096": [Matrix(4000, "bf16_up_14336x4096", "bf16", 14336, 4096, "bf16normal", 0.0, 0.02)],
+    "q6_mlp_70b": [Matrix(5000, "q6_gate_28672x8192", "q6", 28672, 8192, "normal", 31.5, 5.0),
+                   Matrix(5001, "q6_up_28672x8192", "q6", 28672, 8192, "normal", 31.5, 5.0),
+                   Matrix(5002, "q6_down_8192x28672", "q6", 8192, 28672, "normal", 31.5, 5.0)],
 }
 
-BATCHES = {1: (1,), 2: (1,), 3: (1, 4, 16), 4: (1,), 5: (1,)}
+# batch sizes each workload is checked at
+BATCHES = {"q4_256x1024": (1,), "q4_up_14336x4096": (1,), "q4_down_4096x14336": (1, 4, 16),
+           "bf16_up_14336x4096": (1,), "q6_mlp_70b": (1,)}
+
+SMALL = "q4_256x1024"
+DEFAULT = "q4_up_14336x4096"
 
 
-def _rngs(cfg: int, j: int):
-    return [np.random.default_rng(s) for s in np.random.SeedSequence(1000 * cfg + j).spawn(3)]
+def _rngs(seed: int):
+    return [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(3)]
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -101,7 +107,7 @@ def gen_q(mat: Matrix, rows: int | None = None, cols: int | None = None):
     C = mat.cols if cols is None else cols
     assert C % SUPER == 0
     qmax = 15 if mat.kind == "q4" else 63
-    rc, rs, rx = _rngs(mat.cfg, mat.j)
+    rc, rs, rx = _rngs(mat.seed)
     codes = _codes(rc, mat.law, mat.mu, mat.scale, R, C, qmax)
     d = rs.uniform(0.005, 0.02, size=(R, C // SUPER)).astype(np.float16)
     m = (d.astype(np.float32) * 8).astype(np.float16)   # exact: power-of-two scale
@@ -113,7 +119,7 @@ def gen_bf16(mat: Matrix, rows: int | None = None, cols: int | None = None):
     """BF16 matrix: (W bf16-bits [R][C], x bf16-bits [16][C])."""
     R = mat.rows if rows is None else rows
     C = mat.cols if cols is None else cols
-    rw, _, rx = _rngs(mat.cfg, mat.j)
+    rw, _, rx = _rngs(mat.seed)
     n = R * C
     w = np.empty(n, dtype=np.uint16)
     chunk = 1 << 24

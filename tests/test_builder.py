@@ -56,9 +56,9 @@ def test_builder_matches_oracle_bytes(kind, rows, cols, law, seed):
     _compare_q(kind, codes, d, m)
 
 
-def test_builder_matches_oracle_config_shapes():
-    for cfg in (1, 2, 3, 5):
-        mat = synth.CONFIGS[cfg][0]
+def test_builder_matches_oracle_workload_shapes():
+    for wl in ("q4_256x1024", "q4_up_14336x4096", "q4_down_4096x14336", "q6_mlp_70b"):
+        mat = synth.WORKLOADS[wl][0]
         kind = dg.LW_Q4_PAIR if mat.kind == "q4" else dg.LW_Q6_SINGLE
         codes, d, m, _ = synth.gen_q(mat, rows=min(mat.rows, 256), cols=min(mat.cols, 4096))
         _compare_q(kind, codes, d, m)
@@ -82,8 +82,8 @@ def test_builder_matches_oracle_bf16(frac, seed):
     assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_VERBATIM, np.uint16), ob["verbatim"])
 
 
-def test_bf16_config_shape_sample():
-    w, _ = synth.gen_bf16(synth.CONFIGS[4][0], rows=256, cols=4096)
+def test_bf16_workload_shape_sample():
+    w, _ = synth.gen_bf16(synth.WORKLOADS["bf16_up_14336x4096"][0], rows=256, cols=4096)
     ob = O.build_bundle_bf16(w)
     pb = dg.lw_bundle_build_bf16(w)
     assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_WORDS, np.uint32), ob["words"])

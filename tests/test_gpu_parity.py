@@ -168,9 +168,9 @@ def _sample_rows(rows, n, seed):
     return r
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3])
-def test_full_size_q4(torch, dg, cfg):
-    mat = synth.CONFIGS[cfg][0]
+@pytest.mark.parametrize("wl", ["q4_256x1024", "q4_up_14336x4096", "q4_down_4096x14336"])
+def test_full_size_q4(torch, dg, wl):
+    mat = synth.WORKLOADS[wl][0]
     say("full", mat.name)
     codes, d, m, x = synth.gen_q(mat)
     b = dg.lw_bundle_build_q(dg.LW_Q4_PAIR, codes, d, m)
@@ -179,8 +179,8 @@ def test_full_size_q4(torch, dg, cfg):
     q, bits = _decode_q(dg, torch, db, dg.LW_Q4_PAIR, mat.rows, mat.cols, info["n_tiles"])
     assert np.array_equal(q, codes)
     del q
-    rows = _sample_rows(mat.rows, 96, cfg)
-    for batch in (b_ for b_ in synth.BATCHES[cfg] if b_ < 8):
+    rows = _sample_rows(mat.rows, 96, mat.seed)
+    for batch in (b_ for b_ in synth.BATCHES[wl] if b_ < 8):
         say("full gemv", mat.name, batch)
         y = _run_gemv(dg, torch, db, x, batch, mat.rows)
         ref = O.gemv_q(codes, d, m, x, batch, rows=rows)
@@ -189,7 +189,7 @@ def test_full_size_q4(torch, dg, cfg):
 
 
 def test_full_size_q6_one_matrix(torch, dg):
-    mat = synth.CONFIGS[5][2]        # down 8192 x 28672: the widest split
+    mat = synth.WORKLOADS["q6_mlp_70b"][2]        # down 8192 x 28672: the widest split
     say("full", mat.name)
     codes, d, m, x = synth.gen_q(mat)
     b = dg.lw_bundle_build_q(dg.LW_Q6_SINGLE, codes, d, m)
@@ -245,7 +245,7 @@ def test_bf16_gemv_small(torch, dg, case, batch):
 
 
 def test_full_size_bf16(torch, dg):
-    mat = synth.CONFIGS[4][0]
+    mat = synth.WORKLOADS["bf16_up_14336x4096"][0]
     say("full", mat.name)
     w, x = synth.gen_bf16(mat)
     b = dg.lw_bundle_build_bf16(w)
@@ -290,7 +290,7 @@ def test_bf16_gemv_mfma_small(torch, dg, case, batch):
 
 
 def test_full_size_down_batch16(torch, dg):
-    mat = synth.CONFIGS[3][0]
+    mat = synth.WORKLOADS["q4_down_4096x14336"][0]
     say("full mfma", mat.name)
     codes, d, m, x = synth.gen_q(mat)
     db = _upload(dg, torch, dg.lw_bundle_build_q(dg.LW_Q4_PAIR, codes, d, m))

@@ -249,9 +249,9 @@ def test_round_trip_every_tile_and_bitwise(kind, rows, cols, law, seed):
     assert np.array_equal(b["table"]["lens"][syms].astype(np.int64).sum(1), bits.astype(np.int64))
 
 
-def test_round_trip_reduced_configs():
-    for cfg, kind in ((2, O.Q4), (3, O.Q4), (5, O.Q6)):
-        mat = synth.CONFIGS[cfg][0]
+def test_round_trip_reduced_workloads():
+    for wl, kind in (("q4_up_14336x4096", O.Q4), ("q4_down_4096x14336", O.Q4), ("q6_mlp_70b", O.Q6)):
+        mat = synth.WORKLOADS[wl][0]
         codes, d, m, _ = synth.gen_q(mat, rows=256, cols=2048)
         b = O.build_bundle_q(kind, codes, d, m)
         q, _ = O.decode_bundle_q(b)
@@ -347,7 +347,7 @@ def test_bf16_bit_exact_and_verbatim(frac, seed):
 def test_bf16_exponent_statistics():
     # "Unweight": the top-16 exponents cover over 99% of a layer's weights and
     # the exponent distribution needs about 2.6 bits
-    mat = synth.CONFIGS[4][0]
+    mat = synth.WORKLOADS["bf16_up_14336x4096"][0]
     w, _ = synth.gen_bf16(mat, rows=512, cols=4096)
     e = ((w >> 7) & 0xFF).ravel()
     cnt = np.bincount(e, minlength=256).astype(np.float64)
