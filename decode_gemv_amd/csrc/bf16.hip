@@ -298,7 +298,7 @@ hipError_t launch_gemv(const KArgs &a, hipStream_t s)
     const LdsLayout L = lds_layout(BATCH, a.max_words, false);
     dim3 grid((unsigned)a.groups, (unsigned)((a.n_rb + 1) / 2));
     auto kern = k_gemv_bf16<N8, N16, BATCH>;
-    hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
+    hipError_t e = lw_allow_lds<k_gemv_bf16<N8, N16, BATCH>>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, dim3(256), L.total, s, a);
     return hipGetLastError();
@@ -310,7 +310,7 @@ hipError_t launch_decode(const KArgs &a, hipStream_t s)
     const LdsLayout L = lds_layout(1, a.max_words, true);
     dim3 grid((unsigned)a.groups, (unsigned)((a.n_rb + 1) / 2));
     auto kern = k_decode_bf16<N8, N16>;
-    hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
+    hipError_t e = lw_allow_lds<k_decode_bf16<N8, N16>>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, dim3(256), L.total, s, a);
     return hipGetLastError();

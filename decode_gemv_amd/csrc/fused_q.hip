@@ -77,8 +77,10 @@ __global__ __launch_bounds__(256) void k_gemv_q(KArgs a)
 
     lw_stage_tab(lds, a.tab, a.min_len, a.max_len, false);
     float sx[BATCH];
+    uint2 dm = make_uint2(0u, 0u);       // (d, m) of this lane's two tile rows, fetched with the tile
     if (c.wave_active) {
         const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
+        dm = *reinterpret_cast<const uint2 *>(a.dm + (size_t)c.t * 64 + 2 * c.l);
         lw_stage_tile(slots, a.words, w0, (w1 - w0) >> 5, c.l);
         const uint32_t *xg = reinterpret_cast<const uint32_t *>(a.x);
 #pragma unroll
@@ -158,7 +160,6 @@ __global__ __launch_bounds__(256) void k_gemv_q(KArgs a)
     // dequantise: y_row = d * sum(q x) - m * sum(x) for this tile row
     float val[2][BATCH];
     if (c.wave_active) {
-        const uint2 dm = *reinterpret_cast<const uint2 *>(a.dm + (size_t)c.t * 64 + 2 * c.l);
 #pragma unroll
         for (int p = 0; p < 2; p++) {
             const uint32_t w = p ? dm.y : dm.x;
@@ -232,7 +233,7 @@ hipError_t launch_gemv_q(const KArgs &a, hipStream_t s)
     const LdsLayout L = lds_layout(BATCH, a.max_words, false);
     dim3 grid((unsigned)a.groups, (unsigned)((a.n_rb + 1) / 2));
     auto kern = k_gemv_q<KIND, N8, N16, BATCH>;
-    hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
+    hipError_t e = lw_allow_lds<k_gemv_q<KIND, N8, N16, BATCH>>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, dim3(256), L.total, s, a);
     return hipGetLastError();
@@ -244,7 +245,7 @@ hipError_t launch_decode_q(const KArgs &a, hipStream_t s)
     const LdsLayout L = lds_layout(1, a.max_words, true);
     dim3 grid((unsigned)a.groups, (unsigned)((a.n_rb + 1) / 2));
     auto kern = k_decode_q<KIND, N8, N16>;
-    hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
+    hipError_t e = lw_allow_lds<k_decode_q<KIND, N8, N16>>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, dim3(256), L.total, s, a);
     return hipGetLastError();

@@ -34,9 +34,35 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 #define LW_DEV __device__ __forceinline__
+
+// Host: allow kernel KERN the device's largest dynamic LDS allocation, once
+// per device.  The limit is a permission, not an allocation (a launch still
+// reserves only what it asks for), so raising it to the maximum once keeps
+// the runtime call off the launch path and can never be lowered by a
+// concurrent caller.
+template <auto KERN>
+inline hipError_t lw_allow_lds()
+{
+    constexpr int MAXDEV = 64;
+    static std::once_flag once[MAXDEV];
+    static hipError_t result[MAXDEV];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAXDEV) return hipErrorInvalidDevice;
+    std::call_once(once[dev], [dev]() {
+        int bytes = 0;
+        result[dev] = hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+        if (result[dev] == hipSuccess)
+            result[dev] = hipFuncSetAttribute((const void *)KERN, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    });
+    return result[dev];
+}
 
 // LDS layout common to all decoding kernels (byte offsets)
 #define LW_PBASE 1024u       // length entries at PBASE - 2*len, len = 1..11

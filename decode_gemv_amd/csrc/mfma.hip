@@ -296,7 +296,7 @@ hipError_t launch(const KArgs &a, hipStream_t s)
     const LdsLayout L = lds_layout(a.max_words);
     dim3 grid((unsigned)a.groups, (unsigned)((a.n_rb + 1) / 2));
     auto kern = k_gemv_mfma<KIND, N8, N16>;
-    hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
+    hipError_t e = lw_allow_lds<k_gemv_mfma<KIND, N8, N16>>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, dim3(256), L.total, s, a);
     return hipGetLastError();
