@@ -187,6 +187,7 @@ struct LaneWriter {
     uint64_t acc = 0;   // pending bits, right-aligned
     int nacc = 0;
     int64_t word = 0;
+    uint64_t bits() const { return 32u * (uint64_t)word + (uint64_t)nacc; }
     void put(uint32_t code, int len)
     {
         acc = (acc << len) | code;
@@ -230,6 +231,7 @@ static lw_image_header plan_image(int kind, const Shape &sh, int64_t n_words, in
     bytes[LW_REG_GPUTAB] = sizeof(lw_gputab);
     bytes[LW_REG_TILE_OFF] = 4u * (uint64_t)(sh.n_tiles + 1);
     bytes[LW_REG_WORDS] = 4u * (uint64_t)n_words;
+    bytes[LW_REG_SPLIT] = 2u * LW_LANES * (uint64_t)sh.n_tiles;
     if (kind == LW_BF16_EXP) {
         bytes[LW_REG_PALETTE] = 16;
         bytes[LW_REG_SM] = 4u * 4096u * (uint64_t)sh.n_tiles;
@@ -248,7 +250,7 @@ static lw_image_header plan_image(int kind, const Shape &sh, int64_t n_words, in
         h.bytes[r] = bytes[r];
         pos = lw_align_up(pos + bytes[r]);
     }
-    h.coded_bytes = bytes[LW_REG_WORDS] + bytes[LW_REG_TILE_OFF] + bytes[LW_REG_TABLE] +
+    h.coded_bytes = bytes[LW_REG_WORDS] + bytes[LW_REG_TILE_OFF] + bytes[LW_REG_SPLIT] + bytes[LW_REG_TABLE] +
                     bytes[LW_REG_DM] + bytes[LW_REG_SM] + bytes[LW_REG_VB_BITS] +
                     bytes[LW_REG_VB_START] + bytes[LW_REG_VERBATIM] + bytes[LW_REG_PALETTE];
     h.twin_bytes = kind == LW_BF16_EXP
@@ -339,11 +341,13 @@ static void encode_tiles(const Shape &sh, int spl, const uint8_t *lens, const ui
         return;
     }
     uint32_t *words = region<uint32_t>(*img, *h, LW_REG_WORDS);
+    uint16_t *split = region<uint16_t>(*img, *h, LW_REG_SPLIT);
     parallel_for(sh.n_tiles, [&](int64_t t) {
         uint32_t *blk = words + tile_off[t];
         for (int l = 0; l < LW_LANES; l++) {
             LaneWriter w{blk, l};
             for (int k = 0; k < spl; k++) {
+                if (k == spl / 2) split[t * LW_LANES + l] = (uint16_t)w.bits();
                 int s = sym(t, l, k);
                 w.put(codes[s], lens[s]);
             }
@@ -617,12 +621,13 @@ static lw_status validate_image(const uint8_t *img, size_t bytes)
     }
     bool need[LW_REG_COUNT] = {true, true, true, true, h.kind != LW_BF16_EXP, h.kind == LW_BF16_EXP,
                                h.kind == LW_BF16_EXP, h.kind == LW_BF16_EXP, h.kind == LW_BF16_EXP,
-                               false, false};
+                               false, true, false};
     for (int r = 0; r < LW_REG_COUNT; r++)
         if (need[r] && !h.bytes[r]) return lw_fail(LW_E_FORMAT, "missing region " + std::to_string(r));
     if (h.bytes[LW_REG_TABLE] != sizeof(lw_table) || h.bytes[LW_REG_GPUTAB] != sizeof(lw_gputab))
         return lw_fail(LW_E_FORMAT, "table region size");
     if (h.bytes[LW_REG_TILE_OFF] != 4u * (uint64_t)(h.n_tiles + 1)) return lw_fail(LW_E_FORMAT, "tile_off size");
+    if (h.bytes[LW_REG_SPLIT] != 2u * LW_LANES * (uint64_t)h.n_tiles) return lw_fail(LW_E_FORMAT, "split size");
     if (h.kind != LW_BF16_EXP && h.bytes[LW_REG_DM] != 256u * (uint64_t)h.n_tiles)
         return lw_fail(LW_E_FORMAT, "dm size");
     if (h.kind == LW_BF16_EXP &&
@@ -672,6 +677,14 @@ static lw_status validate_image(const uint8_t *img, size_t bytes)
         wmax = std::max<int32_t>(wmax, (int32_t)((to[i + 1] - to[i]) / 32));
     }
     if ((uint64_t)to[h.n_tiles] * 4u != h.bytes[LW_REG_WORDS]) return lw_fail(LW_E_FORMAT, "words size");
+    // a lane's second tile row starts inside its stream, after at least one bit per symbol of the first
+    const uint16_t *sp = reinterpret_cast<const uint16_t *>(img + h.off[LW_REG_SPLIT]);
+    for (int64_t i = 0; i < h.n_tiles; i++)
+        for (int l = 0; l < LW_LANES; l++) {
+            const uint32_t v = sp[i * LW_LANES + l];
+            if (v < (uint32_t)h.spl / 2 || v > 32u * ((to[i + 1] - to[i]) / 32u) || v > (uint32_t)(h.spl / 2) * LW_MAXLEN)
+                return lw_fail(LW_E_FORMAT, "split outside the lane stream");
+        }
     if (wmax != h.max_words) return lw_fail(LW_E_FORMAT, "max_words mismatch");
     // a lane can hold at most symbols_per_lane codes of 11 bits
     if ((int64_t)wmax * 32 > (int64_t)h.spl * LW_MAXLEN + 31) return lw_fail(LW_E_FORMAT, "tile longer than possible");

@@ -14,7 +14,7 @@
 #include "lw.h"
 
 #define LW_MAGIC 0x3142574Cu       /* "LWB1" */
-#define LW_VERSION 1u
+#define LW_VERSION 2u
 #define LW_MAXLEN 11               /* "LazyWeights", 2 . Code them: 11-bit codes */
 #define LW_TILE_ROWS 64            /* a 64x256 tile is 32 lanes of two rows */
 #define LW_TILE_COLS 256

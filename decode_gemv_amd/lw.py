@@ -21,7 +21,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "lw.h")
 LW_OK, LW_E_ARG, LW_E_SHAPE, LW_E_TABLE, LW_E_FORMAT, LW_E_NOMEM, LW_E_DEVICE, LW_E_UNSUPPORTED = range(8)
 LW_Q4_PAIR, LW_Q6_SINGLE, LW_BF16_EXP = 1, 2, 3
 (LW_REG_TABLE, LW_REG_GPUTAB, LW_REG_TILE_OFF, LW_REG_WORDS, LW_REG_DM, LW_REG_PALETTE, LW_REG_SM,
- LW_REG_VB_BITS, LW_REG_VB_START, LW_REG_VERBATIM, LW_REG_WORK, LW_REG_COUNT) = range(12)
+ LW_REG_VB_BITS, LW_REG_VB_START, LW_REG_VERBATIM, LW_REG_SPLIT, LW_REG_WORK, LW_REG_COUNT) = range(13)
 
 
 class LwError(RuntimeError):

@@ -72,8 +72,10 @@ typedef enum {
     LW_REG_VB_BITS = 7,    /* u32 [n_tiles][8], bit 4i+s marks segment s of tile row i verbatim (bf16) */
     LW_REG_VB_START = 8,   /* u32 [n_tiles+1] verbatim segments before each tile (bf16) */
     LW_REG_VERBATIM = 9,   /* u16 [n_verbatim][64] raw bf16 segments (bf16) */
-    LW_REG_WORK = 10,      /* device workspace of the split-column reduction (zero in the image) */
-    LW_REG_COUNT = 11
+    LW_REG_SPLIT = 10,     /* u16 [n_tiles][32]: bits of lane l's first tile row (row 2l); its second
+                              row (2l+1) starts at that bit of the lane stream */
+    LW_REG_WORK = 11,      /* device workspace of the split-column reduction (zero in the image) */
+    LW_REG_COUNT = 12
 } lw_region;
 
 typedef struct {

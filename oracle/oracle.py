@@ -215,6 +215,14 @@ def bf16_to_double(b: int) -> float:
 
 # ---------------------------------------------------------------- bundles
 
+def row_split(syms: np.ndarray, spl: int, lens: np.ndarray) -> np.ndarray:
+    """Per tile and lane, the number of bits of the lane's first tile row
+    (its first spl/2 symbols): the bit of the lane stream where its second
+    row starts.  u16 [n_tiles * 32]."""
+    s = np.asarray(syms).reshape(-1, 32, spl)[:, :, :spl // 2]
+    return np.asarray(lens, dtype=np.int64)[s].sum(axis=2).astype(np.uint16).ravel()
+
+
 def build_bundle_q(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray) -> dict:
     """Quantised bundle: per-matrix table, tile offsets, interleaved words, dm."""
     R, Cc = codes.shape
@@ -227,7 +235,8 @@ def build_bundle_q(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray) -
     tab = canonical(lens)
     tile_off, words, lane_bits = encode_tiles(syms, spl, lens, tab["codes"])
     return dict(kind=kind, rows=R, cols=Cc, spl=spl, counts=counts, table=tab,
-                tile_off=tile_off, words=words, lane_bits=lane_bits, dm=pack_dm(d, m))
+                tile_off=tile_off, words=words, lane_bits=lane_bits, dm=pack_dm(d, m),
+                split=row_split(syms, spl, lens))
 
 
 def decode_bundle_q(b: dict, bitwise: bool = False):
@@ -237,6 +246,17 @@ def decode_bundle_q(b: dict, bitwise: bool = False):
     else:
         syms, bits = decode_limit(b["table"], b["tile_off"], b["words"], b["spl"])
     return unsymbolise_q(b["kind"], b["rows"], b["cols"], syms), bits
+
+
+def symbolise_bf16(w: np.ndarray, palette: np.ndarray, n_pal: int, vb_bits: np.ndarray) -> np.ndarray:
+    """Lane symbol streams of a bf16 matrix: palette indices, placeholder 0
+    inside verbatim segments; u16 [n_tiles * 32 * 512]."""
+    R, Cc = w.shape
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    syms = np.zeros((R // 64) * (Cc // 256) * 32 * 512, dtype=np.uint16)
+    lib().or_bf16_symbolise(R, Cc, _p(w), _p(np.ascontiguousarray(palette)), n_pal,
+                            _p(np.ascontiguousarray(vb_bits)), _p(syms))
+    return syms
 
 
 def build_bundle_bf16(w: np.ndarray) -> dict:
@@ -253,8 +273,7 @@ def build_bundle_bf16(w: np.ndarray) -> dict:
     nv = L.or_bf16_verbatim(R, Cc, _p(w), _p(palette), n_pal, _p(vb_bits), _p(vb_start), None)
     verbatim = np.zeros(max(nv, 1) * 64, dtype=np.uint16)
     L.or_bf16_verbatim(R, Cc, _p(w), _p(palette), n_pal, _p(vb_bits), _p(vb_start), _p(verbatim))
-    syms = np.zeros(nt * 32 * 512, dtype=np.uint16)
-    L.or_bf16_symbolise(R, Cc, _p(w), _p(palette), n_pal, _p(vb_bits), _p(syms))
+    syms = symbolise_bf16(w, palette, n_pal, vb_bits)
     counts = histogram(syms, 16)
     lens = package_merge(counts)
     tab = canonical(lens)
@@ -263,7 +282,8 @@ def build_bundle_bf16(w: np.ndarray) -> dict:
     L.or_bf16_pack_sm(R, Cc, _p(w), _p(sm))
     return dict(kind=BF16, rows=R, cols=Cc, spl=512, counts=counts, table=tab, palette=palette,
                 n_pal=n_pal, vb_bits=vb_bits, vb_start=vb_start, verbatim=verbatim[:nv * 64],
-                n_verbatim=nv, tile_off=tile_off, words=words, lane_bits=lane_bits, sm=sm)
+                n_verbatim=nv, tile_off=tile_off, words=words, lane_bits=lane_bits, sm=sm,
+                split=row_split(syms, 512, lens))
 
 
 def decode_bundle_bf16(b: dict, bitwise: bool = False):

@@ -38,9 +38,11 @@ def _compare_q(kind, codes, d, m):
     assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_TILE_OFF, np.uint32), ob["tile_off"])
     assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_WORDS, np.uint32), ob["words"])
     assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_DM, np.uint32), ob["dm"])
+    assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_SPLIT, np.uint16), ob["split"])
     W = np.diff(ob["tile_off"].astype(np.int64)) // 32
     assert info["max_words"] == W.max()
-    assert info["coded_bytes"] == ob["words"].nbytes + ob["tile_off"].nbytes + ob["dm"].nbytes + 608
+    assert info["coded_bytes"] == (ob["words"].nbytes + ob["tile_off"].nbytes + ob["dm"].nbytes +
+                                   ob["split"].nbytes + 608)
     return pb, ob, info
 
 
@@ -80,6 +82,7 @@ def test_builder_matches_oracle_bf16(frac, seed):
                      (dg.LW_REG_VB_BITS, "vb_bits"), (dg.LW_REG_VB_START, "vb_start")):
         assert np.array_equal(dg.lw_bundle_region(pb, reg, np.uint32), ob[key]), key
     assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_VERBATIM, np.uint16), ob["verbatim"])
+    assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_SPLIT, np.uint16), ob["split"])
 
 
 def test_bf16_workload_shape_sample():
@@ -131,7 +134,7 @@ def test_load_round_trip():
 
 
 @pytest.mark.parametrize("what", ["magic", "truncate", "len12", "kraft", "tile_off", "tile_off_end",
-                                  "shape", "region"])
+                                  "shape", "region", "split"])
 def test_corrupt_images_rejected(what):
     b, img, info = _image()
     img = img.copy()
@@ -164,6 +167,9 @@ def test_corrupt_images_rejected(what):
         # the header's region offset array starts at byte 104; push the words region past the end
         assert hdr[104 // 8 + dg.LW_REG_WORDS] == off[dg.LW_REG_WORDS]
         hdr[104 // 8 + dg.LW_REG_WORDS] = len(img) + 4096
+    elif what == "split":
+        sp = img[off[dg.LW_REG_SPLIT]:].view(np.uint16)
+        sp[5] = 0xFFFF                # second row starting past the lane's words
     with pytest.raises(dg.LwError) as e:
         dg.lw_bundle_load(img)
     assert e.value.status == expect, (what, e.value)

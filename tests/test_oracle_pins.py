@@ -364,3 +364,60 @@ def test_rejects_bad_shapes():
     codes = np.zeros((65, 256), np.uint8)
     with pytest.raises(ValueError):
         O.build_bundle_q(O.Q4, codes, np.zeros((65, 1), np.uint16), np.zeros((65, 1), np.uint16))
+
+
+def _lane_bits(words, tile_off, t, l):
+    """Bit string of lane l of tile t (MSB-first words at tile_off[t] + 32 j + l)."""
+    w0, w1 = int(tile_off[t]), int(tile_off[t + 1])
+    out = []
+    for j in range((w1 - w0) // 32):
+        v = int(words[w0 + 32 * j + l])
+        out.extend((v >> (31 - i)) & 1 for i in range(32))
+    return out
+
+
+def _bitwise_from(bits, start, n, code_map):
+    """Decode n symbols bit by bit from position start; returns (symbols, end)."""
+    pos, syms = start, []
+    for _ in range(n):
+        code, ln = 0, 0
+        while True:
+            code = (code << 1) | bits[pos]
+            pos += 1
+            ln += 1
+            assert ln <= 11
+            if (ln, code) in code_map:
+                syms.append(code_map[(ln, code)])
+                break
+    return syms, pos
+
+
+@pytest.mark.parametrize("case", ["q4", "q6", "bf16"])
+def test_row_split_marks_second_row(case):
+    # the split of lane l is where its second tile row starts: decoding the
+    # first half from bit 0 ends there, and decoding from there yields the
+    # second row's symbols (checked with a bit-at-a-time decoder)
+    if case == "bf16":
+        w, _ = synth.gen_bf16_custom(64, 512, 77, outlier_frac=0.01)
+        b = O.build_bundle_bf16(w)
+        spl = 512
+        syms = O.symbolise_bf16(w, b["palette"], b["n_pal"], b["vb_bits"])
+    else:
+        kind = O.Q4 if case == "q4" else O.Q6
+        codes, d, m, _ = synth.gen_q_custom(64, 512, 78, qmax=15 if case == "q4" else 63,
+                                            mu=7.5 if case == "q4" else 31.5, scale=1.8 if case == "q4" else 5.0)
+        b = O.build_bundle_q(kind, codes, d, m)
+        spl = b["spl"]
+        syms = O.symbolise_q(kind, codes)
+    syms = syms.reshape(-1, 32, spl)
+    lens, cw = b["table"]["lens"], b["table"]["codes"]
+    code_map = {(int(lens[s]), int(cw[s])): s for s in range(len(lens)) if lens[s] > 0}
+    split = b["split"].reshape(-1, 32)
+    for t in range(syms.shape[0]):
+        for l in (0, 5, 17, 31):
+            bits = _lane_bits(b["words"], b["tile_off"], t, l)
+            first, end = _bitwise_from(bits, 0, spl // 2, code_map)
+            assert end == split[t, l]
+            assert first == list(syms[t, l, :spl // 2])
+            second, _ = _bitwise_from(bits, int(split[t, l]), spl // 2, code_map)
+            assert second == list(syms[t, l, spl // 2:])
