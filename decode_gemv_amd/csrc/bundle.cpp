@@ -241,9 +241,10 @@ static lw_image_header plan_image(int kind, const Shape &sh, int64_t n_words, in
     } else {
         bytes[LW_REG_DM] = 4u * 64u * (uint64_t)sh.n_tiles;
     }
-    int64_t n_rows_wg = (sh.n_rb + LW_RB_PER_WG - 1) / LW_RB_PER_WG;
+    // one arrival counter per row band (kernels that combine two row bands per
+    // workgroup use the first half of them), plus slack
     bytes[LW_REG_WORK] = h.work_groups > 1
-        ? lw_work_partial_bytes(h.work_groups, sh.rows) + 4u * (uint64_t)(n_rows_wg + 64) : 0;
+        ? lw_work_partial_bytes(h.work_groups, sh.rows) + 4u * (uint64_t)(sh.n_rb + 64) : 0;
     uint64_t pos = LW_HEADER_BYTES;
     for (int r = 0; r < LW_REG_COUNT; r++) {
         h.off[r] = bytes[r] ? pos : 0;
@@ -702,8 +703,7 @@ static lw_status validate_image(const uint8_t *img, size_t bytes)
     }
     int32_t groups = (int32_t)((h.n_cb + LW_CB_PER_WG - 1) / LW_CB_PER_WG);
     if (h.work_groups != groups) return lw_fail(LW_E_FORMAT, "workspace groups");
-    int64_t n_rows_wg = (h.n_rb + LW_RB_PER_WG - 1) / LW_RB_PER_WG;
-    if (groups > 1 && h.bytes[LW_REG_WORK] < lw_work_partial_bytes(groups, h.rows) + 4u * (uint64_t)n_rows_wg)
+    if (groups > 1 && h.bytes[LW_REG_WORK] < lw_work_partial_bytes(groups, h.rows) + 4u * (uint64_t)h.n_rb)
         return lw_fail(LW_E_FORMAT, "workspace too small");
     return LW_OK;
 }

@@ -13,6 +13,7 @@
 struct KArgs {
     const uint32_t *words;       // interleaved lane words
     const uint32_t *tile_off;    // [n_tiles+1]
+    const uint16_t *split;       // [n_tiles][32] first bit of each lane's second tile row
     const uint32_t *dm;          // [n_tiles][64] d | m << 16 (Q4/Q6)
     const lw_gputab *tab;        // derived tables
     const uint32_t *sm;          // bf16 sign+mantissa words

@@ -148,6 +148,115 @@ LW_DEV void lw_stage_tile(uint32_t *slots, const uint32_t *words, uint32_t w0, u
     }
 }
 
+// Split-phase staging.  A kernel's prologue first issues every global load
+// it needs (tile offsets first, since the tile words depend on them; then the
+// decoder table, scales and activations; then the tile words) and only then
+// writes LDS, through address-space-3 pointers so that no store can be taken
+// to alias a later load.  The prologue then costs the tile-offset and tile-word
+// round trips instead of one round trip per kind of data.
+typedef __attribute__((address_space(3))) uint32_t lw_lds_w32;
+typedef __attribute__((address_space(3))) int16_t lw_lds_w16;
+typedef uint32_t lw_u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) lw_u32x4 lw_lds_w128;
+
+struct LwTabRegs {
+    uint32_t pay, pay2;
+    int32_t ent;
+};
+
+// thread tid (< 256) fetches payload entry tid of both tables and length
+// entry tid % 16 (only the first max_len - min_len + 1 are stored)
+LW_DEV LwTabRegs lw_tab_fetch(const lw_gputab *g, int min_len, int max_len, bool symval_second)
+{
+    LwTabRegs r;
+    const int tid = threadIdx.x;
+    r.pay = g->payload[tid & 255];
+    r.pay2 = symval_second ? g->symval[tid & 255] : g->payload_hi[tid & 255];
+    r.ent = g->base[tid & 15];          // unconditional: a divergent load would be waited on at once
+    return r;
+}
+
+LW_DEV void lw_tab_put(uint8_t *lds, const LwTabRegs &r, int min_len, int max_len)
+{
+    const uint32_t lb = (uint32_t)(size_t)lds;
+    const int tid = threadIdx.x;
+    if (tid < 256) {
+        *(lw_lds_w32 *)(size_t)(lb + LW_TPAY + 4u * tid) = r.pay;
+        *(lw_lds_w32 *)(size_t)(lb + LW_TPAY_HI + 4u * tid) = r.pay2;
+    }
+    if (tid <= max_len - min_len) {
+        const int len = min_len + tid;
+        *(lw_lds_w16 *)(size_t)(lb + LW_PBASE - 2u * len) = (int16_t)((int32_t)lb + (int32_t)LW_TPAY + 4 * r.ent);
+    }
+}
+
+// The first 64 word rows of a tile block (16 x 16 bytes per lane of a
+// half-wave); rows beyond 64 are staged by lw_tile_put.  Indices past the
+// block are clamped to its last vector (no predicated loads or stores).
+struct LwTileRegs {
+    lw_u32x4 v[16];
+};
+
+LW_DEV void lw_tile_fetch(const uint32_t *words, uint32_t w0, uint32_t nrows, int l, LwTileRegs &r)
+{
+    const lw_u32x4 *src = reinterpret_cast<const lw_u32x4 *>(words + w0);
+    const uint32_t n = nrows * 8u;
+#pragma unroll
+    for (int i = 0; i < 16; i++) r.v[i] = src[min((uint32_t)l + 32u * i, n - 1u)];
+}
+
+LW_DEV void lw_tile_put(uint32_t *slots, const uint32_t *words, uint32_t w0, uint32_t nrows, int l,
+                        const LwTileRegs &r)
+{
+    const uint32_t base = (uint32_t)(size_t)(slots + 32);      // slot 1
+    const uint32_t n = nrows * 8u;
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+        *(lw_lds_w128 *)(size_t)(base + 16u * min((uint32_t)l + 32u * i, n - 1u)) = r.v[i];
+    const lw_u32x4 *src = reinterpret_cast<const lw_u32x4 *>(words + w0);
+    for (uint32_t b0 = 512u; b0 < n; b0 += 512u) {            // long lanes: more batches
+        lw_u32x4 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) v[i] = src[min(b0 + (uint32_t)l + 32u * i, n - 1u)];
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+            *(lw_lds_w128 *)(size_t)(base + 16u * min(b0 + (uint32_t)l + 32u * i, n - 1u)) = v[i];
+    }
+}
+
+// The same for a whole wavefront staging one tile: 8 x 16 bytes per lane
+// per batch of 64 word rows.
+struct LwTileRegs64 {
+    lw_u32x4 v[8];
+};
+
+LW_DEV void lw_tile_fetch64(const uint32_t *words, uint32_t w0, uint32_t nrows, int lane, LwTileRegs64 &r)
+{
+    const lw_u32x4 *src = reinterpret_cast<const lw_u32x4 *>(words + w0);
+    const uint32_t n = nrows * 8u;
+#pragma unroll
+    for (int i = 0; i < 8; i++) r.v[i] = src[min((uint32_t)lane + 64u * i, n - 1u)];
+}
+
+LW_DEV void lw_tile_put64(uint32_t *slots, const uint32_t *words, uint32_t w0, uint32_t nrows, int lane,
+                          const LwTileRegs64 &r)
+{
+    const uint32_t base = (uint32_t)(size_t)(slots + 32);      // slot 1
+    const uint32_t n = nrows * 8u;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        *(lw_lds_w128 *)(size_t)(base + 16u * min((uint32_t)lane + 64u * i, n - 1u)) = r.v[i];
+    const lw_u32x4 *src = reinterpret_cast<const lw_u32x4 *>(words + w0);
+    for (uint32_t b0 = 512u; b0 < n; b0 += 512u) {            // long lanes: more batches
+        lw_u32x4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[i] = src[min(b0 + (uint32_t)lane + 64u * i, n - 1u)];
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            *(lw_lds_w128 *)(size_t)(base + 16u * min(b0 + (uint32_t)lane + 64u * i, n - 1u)) = v[i];
+    }
+}
+
 // One lane's decoder state.
 struct LaneDec {
     uint32_t slot0;              // LDS byte address of this lane's word in slot 0
@@ -305,6 +414,128 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
 #undef LW_FENCE
 }
 
+// Two-stream version: a lane decodes its two tile rows as independent
+// chains -- stream 0 from the start of the lane (row 2l), stream 1 from the
+// split bit (row 2l+1) -- so each lane has two serial decode chains to
+// interleave instead of one.  Both rows cover the same columns at every
+// step, so group g of both streams shares the caller's fetch(g) (its
+// activations); use(g, j, pay0, pay1, aux) receives both rows' payloads.
+// Pipeline as lw_decode_pipelined, per stream.
+template <int N8, int N16, int NG, class Aux, bool UNROLL_ALL = false, class PayOff, class Fetch, class Use>
+LW_DEV void lw_decode2(LaneDec (&d)[2], const KArgs &a, PayOff pay_off, Fetch fetch, Use use)
+{
+    static_assert(NG % 2 == 0 && NG >= 4, "groups must be even");
+    uint32_t wa[2], wb[2], wc[2];
+    uint32_t code[2][2][4], A[2][2][4], base[2][2][4], pay[2][2][4];   // [parity][stream][symbol]
+    Aux aux[2];
+    auto issue_window = [&](int s) {
+        const uint32_t p = d[s].slot0 + ((d[s].u >> 5) << 7);
+        wa[s] = lw_ld32(p);
+        wb[s] = lw_ld32(p + 128);
+        wc[s] = lw_ld32(p + 256);
+    };
+    auto decode_group = [&](int q, int s) {
+        const uint32_t sh = ~d[s].u;
+        d[s].hi = __builtin_amdgcn_alignbit(wa[s], wb[s], sh);
+        d[s].lo = __builtin_amdgcn_alignbit(wb[s], wc[s], sh);
+        uint32_t ssum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint32_t Aj = lw_sad_count<N8, N16>(d[s].hi, d[s].k, a);
+            const uint32_t sj = Aj >> 1;
+            A[q][s][j] = Aj;
+            code[q][s][j] = d[s].hi >> (sj & 31u);
+            if (j < 3) lw_advance(d[s], sj);
+            ssum += sj;
+        }
+        d[s].u += 4u * (LW_PBASE / 2) - ssum;
+    };
+    auto issue_payloads = [&](int q, int g) {
+#pragma unroll
+        for (int s = 0; s < 2; s++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                pay[q][s][j] =
+                    lw_ld32((uint32_t)((int32_t)(code[q][s][j] << 2) + (int32_t)base[q][s][j]) + pay_off(j));
+        aux[q] = fetch(g);
+    };
+    auto issue_params = [&](int q) {
+#pragma unroll
+        for (int s = 0; s < 2; s++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) base[q][s][j] = (uint32_t)lw_ld16s(A[q][s][j]);
+    };
+    auto use_group = [&](int q, int g) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) use(g, j, pay[q][0][j], pay[q][1][j], aux[q]);
+    };
+#define LW_FENCE() __builtin_amdgcn_sched_barrier(0)
+    issue_window(0);
+    issue_window(1);
+    LW_FENCE();
+    decode_group(0, 0);
+    decode_group(0, 1);
+    LW_FENCE();
+    issue_window(0);
+    issue_window(1);
+    LW_FENCE();
+    issue_params(0);
+    LW_FENCE();
+    decode_group(1, 0);
+    decode_group(1, 1);
+    LW_FENCE();
+    issue_window(0);
+    issue_window(1);
+    LW_FENCE();
+    issue_payloads(0, 0);
+    LW_FENCE();
+    issue_params(1);
+    LW_FENCE();
+#pragma unroll(UNROLL_ALL ? NG : 1)
+    for (int g = 2; g < NG; g += 2) {
+        decode_group(0, 0);    // group g (even)
+        decode_group(0, 1);
+        LW_FENCE();
+        issue_window(0);       // group g+1
+        issue_window(1);
+        LW_FENCE();
+        issue_payloads(1, g - 1);
+        LW_FENCE();
+        use_group(0, g - 2);
+        LW_FENCE();
+        issue_params(0);
+        LW_FENCE();
+        decode_group(1, 0);    // group g+1 (odd)
+        decode_group(1, 1);
+        LW_FENCE();
+        issue_window(0);       // group g+2 (past the end at the last step: in bounds)
+        issue_window(1);
+        LW_FENCE();
+        issue_payloads(0, g);
+        LW_FENCE();
+        use_group(1, g - 1);
+        LW_FENCE();
+        issue_params(1);
+        LW_FENCE();
+    }
+    issue_payloads(1, NG - 1);
+    use_group(0, NG - 2);
+    use_group(1, NG - 1);
+#undef LW_FENCE
+}
+
+// Set up both streams of a lane: stream 1 starts at the lane's split bit.
+LW_DEV bool lw_lane_init2(LaneDec (&d)[2], uint8_t *lds, const uint32_t *slots, int l, uint32_t split,
+                          const KArgs &a)
+{
+    const uint32_t lb = (uint32_t)(size_t)lds;
+    d[0].slot0 = d[1].slot0 = (uint32_t)(size_t)(slots + l);
+    d[0].u = 31;
+    d[1].u = 31 + split;
+    d[0].k = d[1].k = a.sad_k + lb;
+    return (lb & 63u) == 0;
+}
+
 // Set up a lane's decoder on its staged tile.  Returns false (the kernel must
 // then produce nothing) if the LDS base is not 64-byte aligned, which the
 // shift-amount identity s = A >> 1 needs.
@@ -317,23 +548,23 @@ LW_DEV bool lw_lane_init(LaneDec &d, uint8_t *lds, const uint32_t *slots, int l,
     return (lb & 63u) == 0;
 }
 
-// Sum the per-wave partials of the workgroup's 128 rows (red[wave][b][row])
+// Sum the per-wave partials of the workgroup's ROWS rows (red[wave][b][row])
 // and either write y (one column group) or take part in the split-column
 // reduction.  The partials travel through the bundle's workspace as
 // device-scope atomic exchanges, which are performed at the coherence point
-// of all XCDs without an L2 writeback; each workgroup then bumps its row's
-// arrival counter, and the last one to arrive reads the partials back with
-// device-scope atomic loads and adds them in group order (deterministic),
-// then re-arms the counter for the next call.
-template <int BATCH>
-LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g, int rbp, int waves,
+// of all XCDs without an L2 writeback; each workgroup then bumps the arrival
+// counter of its rows (index ctr), and the last one to arrive reads the
+// partials back with device-scope atomic loads and adds them in group order
+// (deterministic), then re-arms the counter for the next call.
+template <int BATCH, int ROWS = 128>
+LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g, int ctr, int waves,
                            uint32_t *last_flag)
 {
-    for (int i = threadIdx.x; i < BATCH * 128; i += blockDim.x) {
-        const int b = i >> 7, row = i & 127;
+    for (int i = threadIdx.x; i < BATCH * ROWS; i += blockDim.x) {
+        const int b = i / ROWS, row = i % ROWS;
         if (b >= a.batch) break;
         float v = 0.f;
-        for (int w = 0; w < waves; w++) v += red[(w * BATCH + b) * 128 + row];
+        for (int w = 0; w < waves; w++) v += red[(w * BATCH + b) * ROWS + row];
         if (row0 + row < a.rows) {
             if (a.groups == 1) a.y[(size_t)b * a.rows + row0 + row] = v;
             else
@@ -345,13 +576,13 @@ LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's exchanges are performed
     __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&a.count[rbp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t old = __hip_atomic_fetch_add(&a.count[ctr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *last_flag = (old == (uint32_t)a.groups - 1u) ? 1u : 0u;
     }
     __syncthreads();
     if (!*last_flag) return;
-    for (int i = threadIdx.x; i < BATCH * 128; i += blockDim.x) {
-        const int b = i >> 7, row = i & 127;
+    for (int i = threadIdx.x; i < BATCH * ROWS; i += blockDim.x) {
+        const int b = i / ROWS, row = i % ROWS;
         if (b >= a.batch) break;
         if (row0 + row >= a.rows) continue;
         float v = 0.f;
@@ -360,7 +591,7 @@ LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g
                                    __HIP_MEMORY_SCOPE_AGENT);
         a.y[(size_t)b * a.rows + row0 + row] = v;
     }
-    if (threadIdx.x == 0) __hip_atomic_store(&a.count[rbp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_store(&a.count[ctr], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 #endif

@@ -75,7 +75,7 @@ typedef struct {
 static inline uint64_t lw_align_up(uint64_t v) { return (v + LW_ALIGN - 1) & ~(uint64_t)(LW_ALIGN - 1); }
 
 /* workspace layout: partial sums [work_groups][LW_BATCH_MAX][rows] f32, then
- * one u32 arrival counter per workgroup row (rows / (64 * LW_RB_PER_WG), rounded up) */
+ * one u32 arrival counter per row band (rows / 64) */
 static inline uint64_t lw_work_partial_bytes(int32_t groups, int64_t rows)
 {
     return (uint64_t)groups * LW_BATCH_MAX * (uint64_t)rows * 4u;

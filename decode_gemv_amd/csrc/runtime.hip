@@ -63,6 +63,7 @@ static KArgs make_args(const lw_dev_bundle *db)
     std::memset(&a, 0, sizeof(a));
     a.words = dev_region<uint32_t>(db, LW_REG_WORDS);
     a.tile_off = dev_region<uint32_t>(db, LW_REG_TILE_OFF);
+    a.split = dev_region<uint16_t>(db, LW_REG_SPLIT);
     a.dm = dev_region<uint32_t>(db, LW_REG_DM);
     a.tab = dev_region<lw_gputab>(db, LW_REG_GPUTAB);
     a.sm = dev_region<uint32_t>(db, LW_REG_SM);
