@@ -73,44 +73,38 @@ __global__ __launch_bounds__(256) void k_gemv_q(KArgs a)
     const uint32_t xs_addr = (uint32_t)(size_t)(lds + L.x) + 4u * (uint32_t)(c.wave * BATCH * 128);
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
 
-    // issue: tile offsets, decoder table, scales, split, activations, tile words
-    uint32_t w0 = 0, w1 = 0;
-    if (c.active) {
-        w0 = a.tile_off[c.t];
-        w1 = a.tile_off[c.t + 1];
-    }
+    // Issue every global load first (unconditionally: an inactive wavefront
+    // reads tile 0 and drops it), tile offsets first since the tile words
+    // depend on them.  Only the decoder table is shared by the workgroup, so
+    // the barrier waits for the table stores alone; each wavefront then
+    // stores its own tile and activations and starts decoding as soon as its
+    // own data is in (a wavefront's LDS operations complete in order).
+    const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
     const LwTabRegs tr = lw_tab_fetch(a.tab, a.min_len, a.max_len, false);
-    uint32_t dm = 0, split = 0;           // (d, m) of this lane's tile row; second-row start
+    const uint32_t dm = a.dm[(size_t)c.t * 64 + 2 * c.l + c.half];   // (d, m) of this lane's tile row
+    const uint32_t split = a.split[(size_t)c.t * 32 + c.l];          // second-row start
     uint32_t xv[BATCH][2];
-    const uint32_t *xg = reinterpret_cast<const uint32_t *>(a.x);
+    const uint32_t *xg = reinterpret_cast<const uint32_t *>(a.x) + (size_t)(c.active ? c.cb : 0) * 128;
+#pragma unroll
+    for (int b = 0; b < BATCH; b++) {
+        xv[b][0] = xg[(size_t)b * (a.cols / 2) + c.lane];
+        xv[b][1] = xg[(size_t)b * (a.cols / 2) + c.lane + 64];
+    }
     LwTileRegs64 tile;
-    if (c.active) {
-        dm = a.dm[(size_t)c.t * 64 + 2 * c.l + c.half];
-        split = a.split[(size_t)c.t * 32 + c.l];
-#pragma unroll
-        for (int b = 0; b < BATCH; b++) {
-            const uint32_t *xb = xg + (size_t)b * (a.cols / 2) + (size_t)c.cb * 128;
-            xv[b][0] = xb[c.lane];
-            xv[b][1] = xb[c.lane + 64];
-        }
-        lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    }
-    // store
+    lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     lw_tab_put(lds, tr, a.min_len, a.max_len);
-    float sx[BATCH];
-    if (c.active) {
+    __syncthreads();                      // the decoder table is complete
 #pragma unroll
-        for (int b = 0; b < BATCH; b++) {
-            *(lw_lds_w32 *)(size_t)(xs_addr + 4u * (b * 128 + c.lane)) = xv[b][0];
-            *(lw_lds_w32 *)(size_t)(xs_addr + 4u * (b * 128 + c.lane + 64)) = xv[b][1];
-        }
-        lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-#pragma unroll
-        for (int b = 0; b < BATCH; b++)
-            sx[b] = lw_wave_sum(lw_half_lo(xv[b][0]) + lw_half_hi(xv[b][0]) + lw_half_lo(xv[b][1]) +
-                                lw_half_hi(xv[b][1]));
+    for (int b = 0; b < BATCH; b++) {
+        *(lw_lds_w32 *)(size_t)(xs_addr + 4u * (b * 128 + c.lane)) = xv[b][0];
+        *(lw_lds_w32 *)(size_t)(xs_addr + 4u * (b * 128 + c.lane + 64)) = xv[b][1];
     }
-    __syncthreads();
+    lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
+    float sx[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; b++)
+        sx[b] = lw_wave_sum(lw_half_lo(xv[b][0]) + lw_half_hi(xv[b][0]) + lw_half_lo(xv[b][1]) +
+                            lw_half_hi(xv[b][1]));
 
     float acc[BATCH];
 #pragma unroll
@@ -192,22 +186,15 @@ __global__ __launch_bounds__(256) void k_decode_q(KArgs a)
     const int S = a.max_words + 3;
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
     // issue, then store (as in k_gemv_q)
-    uint32_t w0 = 0, w1 = 0;
-    if (c.active) {
-        w0 = a.tile_off[c.t];
-        w1 = a.tile_off[c.t + 1];
-    }
+    const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
     const LwTabRegs tr = lw_tab_fetch(a.tab, a.min_len, a.max_len, true);
-    uint32_t split = 0;
+    const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
     LwTileRegs64 tile;
-    if (c.active) {
-        split = a.split[(size_t)c.t * 32 + c.l];
-        lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    }
+    lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     lw_tab_put(lds, tr, a.min_len, a.max_len);
-    if (c.active) lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     __syncthreads();
     if (!c.active) return;
+    lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     LaneDec d;
     if (!lw_lane_init(d, lds, slots, c.l, a)) return;
     d.u += c.half ? split : 0u;

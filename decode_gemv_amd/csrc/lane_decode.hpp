@@ -165,29 +165,27 @@ struct LwTabRegs {
 };
 
 // thread tid (< 256) fetches payload entry tid of both tables and length
-// entry tid % 16 (only the first max_len - min_len + 1 are stored)
+// entry min(tid, max_len - min_len).  Loads and stores are unconditional: a
+// load the compiler sinks into a divergent branch is waited on together
+// with every load issued before it.
 LW_DEV LwTabRegs lw_tab_fetch(const lw_gputab *g, int min_len, int max_len, bool symval_second)
 {
     LwTabRegs r;
     const int tid = threadIdx.x;
     r.pay = g->payload[tid & 255];
     r.pay2 = symval_second ? g->symval[tid & 255] : g->payload_hi[tid & 255];
-    r.ent = g->base[tid & 15];          // unconditional: a divergent load would be waited on at once
+    r.ent = g->base[min(tid, max_len - min_len)];   // threads past the last entry repeat it
     return r;
 }
 
 LW_DEV void lw_tab_put(uint8_t *lds, const LwTabRegs &r, int min_len, int max_len)
 {
     const uint32_t lb = (uint32_t)(size_t)lds;
-    const int tid = threadIdx.x;
-    if (tid < 256) {
-        *(lw_lds_w32 *)(size_t)(lb + LW_TPAY + 4u * tid) = r.pay;
-        *(lw_lds_w32 *)(size_t)(lb + LW_TPAY_HI + 4u * tid) = r.pay2;
-    }
-    if (tid <= max_len - min_len) {
-        const int len = min_len + tid;
-        *(lw_lds_w16 *)(size_t)(lb + LW_PBASE - 2u * len) = (int16_t)((int32_t)lb + (int32_t)LW_TPAY + 4 * r.ent);
-    }
+    const int tid = threadIdx.x;          // workgroups have 256 threads: one entry each, unconditionally
+    *(lw_lds_w32 *)(size_t)(lb + LW_TPAY + 4u * (tid & 255)) = r.pay;
+    *(lw_lds_w32 *)(size_t)(lb + LW_TPAY_HI + 4u * (tid & 255)) = r.pay2;
+    const int len = min_len + min(tid, max_len - min_len);   // repeated stores write the same value
+    *(lw_lds_w16 *)(size_t)(lb + LW_PBASE - 2u * len) = (int16_t)((int32_t)lb + (int32_t)LW_TPAY + 4 * r.ent);
 }
 
 // The first 64 word rows of a tile block (16 x 16 bytes per lane of a
