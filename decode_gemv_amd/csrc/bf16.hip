@@ -3,8 +3,10 @@
 // LLM Weights for Faster Inference", sections "Understanding BF16 weight
 // structure" and "The exponent's exploitable redundancy"), gfx950.
 //
-// A lane decodes palette indices with the same per-lane decoder as the
-// quantised kernels (512 single symbols: tile rows 2l then 2l+1).  Payload
+// Palette indices are decoded with the same per-lane decoder and work split
+// as the quantised kernels: one wavefront per tile, lane l + 32*half decodes
+// the 256 single symbols of tile row 2l + half (the second row from the
+// lane's split bit).  Payload
 // tables hold the palette exponent pre-shifted to the low (<< 7) and high
 // (<< 23) bf16 of a pair.  The raw sign+mantissa bytes of a lane come as one
 // 32-bit word per four columns, coalesced across the lanes; every lane uses
@@ -34,16 +36,18 @@ __host__ __device__ inline LdsLayout lds_layout(int batch, int max_words, bool d
     L.x = LW_TAB_BYTES;
     const uint32_t xbytes = decode_only ? 0u : (uint32_t)(WAVES * batch * 128 * 4);
     L.tiles = L.x + xbytes;
-    const uint32_t tiles = (uint32_t)(WAVES * 2 * (max_words + 3) * 128);
-    const uint32_t red = (uint32_t)(WAVES * batch * 128 * 4);
+    const uint32_t tiles = (uint32_t)(WAVES * (max_words + 3) * 128);
+    const uint32_t red = (uint32_t)(WAVES * batch * 64 * 4);
     L.flag = L.tiles + (tiles > red ? tiles : red);
     L.total = L.flag + 16;
     return L;
 }
 
+// Identity of a lane: one wavefront per tile, lane l + 32*half decodes tile
+// row 2l + half (the second row from the lane's split bit).
 struct LaneCtx {
-    int wave, lane, half, l, g, rbp, cb, rb, t;
-    bool wave_active, lane_active;
+    int wave, lane, half, l, g, cb, rb, t;
+    bool active;
 };
 
 LW_DEV LaneCtx lane_ctx(const KArgs &a)
@@ -54,13 +58,10 @@ LW_DEV LaneCtx lane_ctx(const KArgs &a)
     c.half = c.lane >> 5;
     c.l = c.lane & 31;
     c.g = blockIdx.x;
-    c.rbp = blockIdx.y;
+    c.rb = blockIdx.y;
     c.cb = c.g * WAVES + c.wave;
-    c.wave_active = c.cb < a.n_cb;
-    const int rb = c.rbp * 2 + c.half;
-    c.lane_active = c.wave_active && rb < a.n_rb;
-    c.rb = rb < a.n_rb ? rb : rb - 1;
-    c.t = c.rb * a.n_cb + (c.wave_active ? c.cb : 0);
+    c.active = c.cb < a.n_cb;
+    c.t = c.rb * a.n_cb + (c.active ? c.cb : 0);
     return c;
 }
 
@@ -108,121 +109,115 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(KArgs a)
     const LdsLayout L = lds_layout(BATCH, a.max_words, false);
     const LaneCtx c = lane_ctx(a);
     const int S = a.max_words + 3;
-    uint32_t *xs = reinterpret_cast<uint32_t *>(lds + L.x) + c.wave * BATCH * 128;
-    const uint32_t xs_addr = (uint32_t)(size_t)xs;
-    uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + (c.wave * 2 + c.half) * S * 32;
+    const uint32_t xs_addr = (uint32_t)(size_t)(lds + L.x) + 4u * (uint32_t)(c.wave * BATCH * 128);
+    uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
+    // the lane's sign+mantissa row: word g holds columns 4g..4g+3
+    const uint32_t *smrow = a.sm + (size_t)c.t * 4096 + (size_t)c.half * 64 * 32 + c.l;
 
-    lw_stage_tab(lds, a.tab, a.min_len, a.max_len, false);
-    if (c.wave_active) {
-        const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-        lw_stage_tile(slots, a.words, w0, (w1 - w0) >> 5, c.l);
-        const uint32_t *xg = reinterpret_cast<const uint32_t *>(a.x);
+    // issue every load, tile offsets first; table barrier; own tile and x (as in fused_q.hip)
+    const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
+    const LwTabRegs tr = lw_tab_fetch(a.tab, a.min_len, a.max_len, false);
+    const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
+    uint32_t xv[BATCH][2];
+    const uint32_t *xg = reinterpret_cast<const uint32_t *>(a.x) + (size_t)(c.active ? c.cb : 0) * 128;
 #pragma unroll
-        for (int b = 0; b < BATCH; b++) {
-            const uint32_t *xb = xg + (size_t)b * (a.cols / 2) + (size_t)c.cb * 128;
-            xs[b * 128 + c.lane] = xb[c.lane];
-            xs[b * 128 + c.lane + 64] = xb[c.lane + 64];
-        }
+    for (int b = 0; b < BATCH; b++) {
+        xv[b][0] = xg[(size_t)b * (a.cols / 2) + c.lane];
+        xv[b][1] = xg[(size_t)b * (a.cols / 2) + c.lane + 64];
     }
-    __syncthreads();
-
-    float acc[2][BATCH];
+    uint32_t ring[2][CHUNK];
+    lw_load_sm(ring[0], smrow, 0);
+    LwTileRegs64 tile;
+    lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
+    lw_tab_put(lds, tr, a.min_len, a.max_len);
+    __syncthreads();                      // the decoder table is complete
 #pragma unroll
-    for (int p = 0; p < 2; p++)
-#pragma unroll
-        for (int b = 0; b < BATCH; b++) acc[p][b] = 0.f;
+    for (int b = 0; b < BATCH; b++) {
+        *(lw_lds_w32 *)(size_t)(xs_addr + 4u * (b * 128 + c.lane)) = xv[b][0];
+        *(lw_lds_w32 *)(size_t)(xs_addr + 4u * (b * 128 + c.lane + 64)) = xv[b][1];
+    }
+    lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
 
-    if (c.wave_active) {
+    float acc[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; b++) acc[b] = 0.f;
+
+    if (c.active) {
         LaneDec d;
         const bool ok = lw_lane_init(d, lds, slots, c.l, a);
+        d.u += c.half ? split : 0u;       // the second tile row starts at the split bit
         if (ok) {
             struct XA {
                 u32x2 v[BATCH];
                 uint32_t sm;
             };
-            auto run_row = [&](auto pc) {
-                constexpr int p = decltype(pc)::value;
-                const uint32_t *smrow = a.sm + (size_t)c.t * 4096 + (size_t)p * 64 * 32 + c.l;
-                uint32_t ring[2][CHUNK];
-                uint32_t pend = 0;
-                auto run_chunk = [&](int ch, const uint32_t (&cur)[CHUNK]) {
-                    auto fetch = [&](int g) {
-                        XA r;
+            uint32_t pend = 0;
+            auto run_chunk = [&](int ch, const uint32_t (&cur)[CHUNK]) {
+                auto fetch = [&](int g) {
+                    XA r;
 #pragma unroll
-                        for (int b = 0; b < BATCH; b++) {
-                            const uint32_t ad = xs_addr + (uint32_t)(b * 512 + 8 * (ch * CHUNK + g));
-                            r.v[b] = *(__attribute__((address_space(3))) const u32x2 *)(size_t)ad;
-                        }
-                        r.sm = cur[g];
-                        return r;
-                    };
-                    auto use = [&](int, int j, uint32_t pay, const XA &x) {
-                        if (j & 1) {
-                            const uint32_t w2 = (j == 1) ? lw_pair<0>(x.sm, pend, pay) : lw_pair<2>(x.sm, pend, pay);
-#pragma unroll
-                            for (int b = 0; b < BATCH; b++)
-                                acc[p][b] = lw_dot2_bf16(w2, j == 1 ? x.v[b].x : x.v[b].y, acc[p][b]);
-                        } else {
-                            pend = pay;
-                        }
-                    };
-                    lw_decode_pipelined<N8, N16, CHUNK, XA, true>(
-                        d, a, [](int j) { return (j & 1) ? (LW_TPAY_HI - LW_TPAY) : 0u; }, fetch, use);
+                    for (int b = 0; b < BATCH; b++) {
+                        const uint32_t ad = xs_addr + (uint32_t)(b * 512 + 8 * (ch * CHUNK + g));
+                        r.v[b] = *(__attribute__((address_space(3))) const u32x2 *)(size_t)ad;
+                    }
+                    r.sm = cur[g];
+                    return r;
                 };
-                lw_load_sm(ring[0], smrow, 0);
+                auto use = [&](int, int j, uint32_t pay, const XA &x) {
+                    if (j & 1) {
+                        const uint32_t w2 = (j == 1) ? lw_pair<0>(x.sm, pend, pay) : lw_pair<2>(x.sm, pend, pay);
 #pragma unroll
-                for (int ch = 0; ch < 64 / CHUNK; ch += 2) {
-                    lw_load_sm(ring[1], smrow, ch + 1);
-                    run_chunk(ch, ring[0]);
-                    if (ch + 2 < 64 / CHUNK) lw_load_sm(ring[0], smrow, ch + 2);
-                    run_chunk(ch + 1, ring[1]);
-                }
+                        for (int b = 0; b < BATCH; b++)
+                            acc[b] = lw_dot2_bf16(w2, j == 1 ? x.v[b].x : x.v[b].y, acc[b]);
+                    } else {
+                        pend = pay;
+                    }
+                };
+                lw_decode_pipelined<N8, N16, CHUNK, XA, true>(
+                    d, a, [](int j) { return (j & 1) ? (LW_TPAY_HI - LW_TPAY) : 0u; }, fetch, use);
             };
-            run_row(std::integral_constant<int, 0>{});
-            run_row(std::integral_constant<int, 1>{});
+#pragma unroll
+            for (int ch = 0; ch < 64 / CHUNK; ch += 2) {
+                lw_load_sm(ring[1], smrow, ch + 1);
+                run_chunk(ch, ring[0]);
+                if (ch + 2 < 64 / CHUNK) lw_load_sm(ring[0], smrow, ch + 2);
+                run_chunk(ch + 1, ring[1]);
+            }
 
-            // verbatim segments of this lane's two rows (rare): replace the
+            // verbatim segments of this lane's row (rare): replace the
             // placeholder weights' contribution by the stored values'
-            const uint32_t bits = (a.vb_bits[(size_t)c.t * 8 + c.l / 4] >> (8 * (c.l % 4))) & 0xFFu;
+            const uint32_t bits = (a.vb_bits[(size_t)c.t * 8 + c.l / 4] >> (8 * (c.l % 4) + 4 * c.half)) & 0xFu;
             if (bits) {
                 const uint16_t *xrow = a.x + (size_t)c.cb * 256;
-                for (int q = 0; q < 8; q++) {
-                    if (!((bits >> q) & 1u)) continue;
-                    const int p = q >> 2, seg = q & 3;
-                    const uint32_t ord = lw_verbatim_ordinal(a, c.t, 8 * c.l + q);
+                for (int seg = 0; seg < 4; seg++) {
+                    if (!((bits >> seg) & 1u)) continue;
+                    const uint32_t ord = lw_verbatim_ordinal(a, c.t, 8 * c.l + 4 * c.half + seg);
                     const uint16_t *v = a.verbatim + (size_t)ord * 64;
-                    const uint32_t *smw = a.sm + (size_t)c.t * 4096 + (size_t)p * 64 * 32 + c.l;
                     for (int b = 0; b < BATCH; b++) {
-                        float s = 0.f;
+                        float sacc = 0.f;
                         for (int k = 0; k < 64; k++) {
                             const int col = 64 * seg + k;
-                            const uint32_t smb = (smw[(col / 4) * 32] >> (8 * (col % 4))) & 0xFFu;
+                            const uint32_t smb = (smrow[(col / 4) * 32] >> (8 * (col % 4))) & 0xFFu;
                             const uint32_t ph = ((smb & 0x80u) << 8) | (a.pal0 << 7) | (smb & 0x7Fu);
                             const float wdiff = lw_bf16_to_f32(v[k]) - lw_bf16_to_f32(ph);
-                            s += wdiff * lw_bf16_to_f32(xrow[(size_t)b * a.cols + col]);
+                            sacc += wdiff * lw_bf16_to_f32(xrow[(size_t)b * a.cols + col]);
                         }
-                        if (p) acc[1][b] += s;
-                        else acc[0][b] += s;
+                        acc[b] += sacc;
                     }
                 }
             }
         } else {
 #pragma unroll
-            for (int p = 0; p < 2; p++)
-#pragma unroll
-                for (int b = 0; b < BATCH; b++) acc[p][b] = __builtin_nanf("");
+            for (int b = 0; b < BATCH; b++) acc[b] = __builtin_nanf("");
         }
     }
     __syncthreads();                      // tiles no longer read: reuse for the reduction
     float *red = reinterpret_cast<float *>(lds + L.tiles);
 #pragma unroll
-    for (int p = 0; p < 2; p++)
-#pragma unroll
-        for (int b = 0; b < BATCH; b++)
-            red[(c.wave * BATCH + b) * 128 + c.half * 64 + 2 * c.l + p] = c.lane_active ? acc[p][b] : 0.f;
+    for (int b = 0; b < BATCH; b++) red[(c.wave * BATCH + b) * 64 + 2 * c.l + c.half] = c.active ? acc[b] : 0.f;
     __syncthreads();
     uint32_t *last_flag = reinterpret_cast<uint32_t *>(lds + L.flag);
-    lw_finish_rows<BATCH>(a, red, (int64_t)c.rbp * 128, c.g, c.rbp, WAVES, last_flag);
+    lw_finish_rows<BATCH, 64>(a, red, (int64_t)c.rb * 64, c.g, c.rb, WAVES, last_flag);
 }
 
 // Decode only: rebuild the bf16 matrix [rows][cols].
@@ -233,59 +228,58 @@ __global__ __launch_bounds__(256) void k_decode_bf16(KArgs a)
     const LdsLayout L = lds_layout(1, a.max_words, true);
     const LaneCtx c = lane_ctx(a);
     const int S = a.max_words + 3;
-    uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + (c.wave * 2 + c.half) * S * 32;
-    lw_stage_tab(lds, a.tab, a.min_len, a.max_len, false);
-    if (c.wave_active) {
-        const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-        lw_stage_tile(slots, a.words, w0, (w1 - w0) >> 5, c.l);
-    }
+    uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
+    const uint32_t *smrow = a.sm + (size_t)c.t * 4096 + (size_t)c.half * 64 * 32 + c.l;
+    const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
+    const LwTabRegs tr = lw_tab_fetch(a.tab, a.min_len, a.max_len, false);
+    const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
+    uint32_t ring[2][CHUNK];
+    lw_load_sm(ring[0], smrow, 0);
+    LwTileRegs64 tile;
+    lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
+    lw_tab_put(lds, tr, a.min_len, a.max_len);
     __syncthreads();
-    if (!c.wave_active) return;
+    if (!c.active) return;
+    lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     LaneDec d;
     if (!lw_lane_init(d, lds, slots, c.l, a)) return;
-    uint32_t *out = reinterpret_cast<uint32_t *>(a.out);
+    d.u += c.half ? split : 0u;
+    uint32_t *orow = reinterpret_cast<uint32_t *>(a.out) +
+                     (((int64_t)c.rb * 64 + 2 * c.l + c.half) * a.cols + (int64_t)c.cb * 256) / 2;
     struct XA {
         uint32_t sm;
     };
-    auto run_row = [&](int p) {
-        const uint32_t *smrow = a.sm + (size_t)c.t * 4096 + (size_t)p * 64 * 32 + c.l;
-        uint32_t *orow = out + (((int64_t)c.rb * 64 + 2 * c.l + p) * a.cols + (int64_t)c.cb * 256) / 2;
-        uint32_t ring[2][CHUNK];
-        uint32_t pend = 0;
-        auto run_chunk = [&](int ch, const uint32_t (&cur)[CHUNK]) {
-            lw_decode_pipelined<N8, N16, CHUNK, XA, true>(
-                d, a, [](int j) { return (j & 1) ? (LW_TPAY_HI - LW_TPAY) : 0u; },
-                [&](int g) { return XA{cur[g]}; },
-                [&](int g, int j, uint32_t pay, const XA &x) {
-                    if (j & 1) {
-                        const uint32_t w2 = (j == 1) ? lw_pair<0>(x.sm, pend, pay) : lw_pair<2>(x.sm, pend, pay);
-                        if (c.lane_active) orow[2 * (ch * CHUNK + g) + (j >> 1)] = w2;
-                    } else {
-                        pend = pay;
-                    }
-                });
-        };
-        lw_load_sm(ring[0], smrow, 0);
-#pragma unroll
-        for (int ch = 0; ch < 64 / CHUNK; ch += 2) {
-            lw_load_sm(ring[1], smrow, ch + 1);
-            run_chunk(ch, ring[0]);
-            if (ch + 2 < 64 / CHUNK) lw_load_sm(ring[0], smrow, ch + 2);
-            run_chunk(ch + 1, ring[1]);
-        }
+    uint32_t pend = 0;
+    auto run_chunk = [&](int ch, const uint32_t (&cur)[CHUNK]) {
+        lw_decode_pipelined<N8, N16, CHUNK, XA, true>(
+            d, a, [](int j) { return (j & 1) ? (LW_TPAY_HI - LW_TPAY) : 0u; },
+            [&](int g) { return XA{cur[g]}; },
+            [&](int g, int j, uint32_t pay, const XA &x) {
+                if (j & 1) {
+                    const uint32_t w2 = (j == 1) ? lw_pair<0>(x.sm, pend, pay) : lw_pair<2>(x.sm, pend, pay);
+                    orow[2 * (ch * CHUNK + g) + (j >> 1)] = w2;
+                } else {
+                    pend = pay;
+                }
+            });
     };
-    run_row(0);
-    run_row(1);
-    if (a.lane_bits && c.lane_active) a.lane_bits[(size_t)c.t * 32 + c.l] = d.u - 31;
+#pragma unroll
+    for (int ch = 0; ch < 64 / CHUNK; ch += 2) {
+        lw_load_sm(ring[1], smrow, ch + 1);
+        run_chunk(ch, ring[0]);
+        if (ch + 2 < 64 / CHUNK) lw_load_sm(ring[0], smrow, ch + 2);
+        run_chunk(ch + 1, ring[1]);
+    }
+    // the lane of the second row ends where the whole lane stream ends
+    if (a.lane_bits && c.half) a.lane_bits[(size_t)c.t * 32 + c.l] = d.u - 31;
     // verbatim segments overwrite the placeholder weights (rare)
-    const uint32_t bits = (a.vb_bits[(size_t)c.t * 8 + c.l / 4] >> (8 * (c.l % 4))) & 0xFFu;
-    if (bits && c.lane_active) {
+    const uint32_t bits = (a.vb_bits[(size_t)c.t * 8 + c.l / 4] >> (8 * (c.l % 4) + 4 * c.half)) & 0xFu;
+    if (bits) {
         uint16_t *o16 = reinterpret_cast<uint16_t *>(a.out);
-        for (int q = 0; q < 8; q++) {
-            if (!((bits >> q) & 1u)) continue;
-            const int p = q >> 2, seg = q & 3;
-            const uint32_t ord = lw_verbatim_ordinal(a, c.t, 8 * c.l + q);
-            const int64_t row = (int64_t)c.rb * 64 + 2 * c.l + p;
+        const int64_t row = (int64_t)c.rb * 64 + 2 * c.l + c.half;
+        for (int seg = 0; seg < 4; seg++) {
+            if (!((bits >> seg) & 1u)) continue;
+            const uint32_t ord = lw_verbatim_ordinal(a, c.t, 8 * c.l + 4 * c.half + seg);
             for (int k = 0; k < 64; k++)
                 o16[row * a.cols + (int64_t)c.cb * 256 + 64 * seg + k] = a.verbatim[(size_t)ord * 64 + k];
         }
@@ -296,7 +290,7 @@ template <int N8, int N16, int BATCH>
 hipError_t launch_gemv(const KArgs &a, hipStream_t s)
 {
     const LdsLayout L = lds_layout(BATCH, a.max_words, false);
-    dim3 grid((unsigned)a.groups, (unsigned)((a.n_rb + 1) / 2));
+    dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
     auto kern = k_gemv_bf16<N8, N16, BATCH>;
     hipError_t e = lw_allow_lds<k_gemv_bf16<N8, N16, BATCH>>();
     if (e != hipSuccess) return e;
@@ -308,7 +302,7 @@ template <int N8, int N16>
 hipError_t launch_decode(const KArgs &a, hipStream_t s)
 {
     const LdsLayout L = lds_layout(1, a.max_words, true);
-    dim3 grid((unsigned)a.groups, (unsigned)((a.n_rb + 1) / 2));
+    dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
     auto kern = k_decode_bf16<N8, N16>;
     hipError_t e = lw_allow_lds<k_decode_bf16<N8, N16>>();
     if (e != hipSuccess) return e;

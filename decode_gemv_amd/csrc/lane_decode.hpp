@@ -100,54 +100,6 @@ typedef __attribute__((address_space(3))) const uint32_t lw_lds_u32;
 LW_DEV uint32_t lw_ld32(uint32_t addr) { return *(lw_lds_u32 *)(size_t)addr; }
 LW_DEV int32_t lw_ld16s(uint32_t addr) { return *(lw_lds_i16 *)(size_t)addr; }
 
-// Stage the decoder tables into LDS (all threads of the block): the
-// per-length entries (LDS address of the symbol-table base offset[len] -
-// first[len], scaled by 4) and the two payload tables.  `symval_second`
-// selects what fills the second table: the kind's high payload, or the
-// symbol value.
-LW_DEV void lw_stage_tab(uint8_t *lds, const lw_gputab *g, int min_len, int max_len, bool symval_second)
-{
-    const uint32_t lb = (uint32_t)(size_t)lds;
-    uint32_t *pay = reinterpret_cast<uint32_t *>(lds + LW_TPAY);
-    uint32_t *pay2 = reinterpret_cast<uint32_t *>(lds + LW_TPAY_HI);
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) {
-        pay[i] = g->payload[i];
-        pay2[i] = symval_second ? g->symval[i] : g->payload_hi[i];
-    }
-    if ((int)threadIdx.x <= max_len - min_len) {
-        const int r = threadIdx.x;
-        const int len = min_len + r;
-        int16_t *ent = reinterpret_cast<int16_t *>(lds + LW_PBASE - 2 * len);
-        *ent = (int16_t)((int32_t)lb + (int32_t)LW_TPAY + 4 * g->base[r]);
-    }
-}
-
-// Copy one tile block (nrows word rows) into LDS slots 1..nrows, by the 32
-// lanes l of a half-wave.  All global loads of a batch of up to 16 x 16 bytes
-// per lane are issued before the first LDS store, so a wave keeps its whole
-// tile in flight instead of one 16-byte load per round trip.
-LW_DEV void lw_stage_tile(uint32_t *slots, const uint32_t *words, uint32_t w0, uint32_t nrows, int l)
-{
-    const uint4 *src = reinterpret_cast<const uint4 *>(words + w0);
-    uint4 *dst = reinterpret_cast<uint4 *>(slots + 32);
-    const uint32_t n = nrows * 8u;
-    // indices past the block are clamped to its last vector: the extra lanes
-    // reload and rewrite that same vector, so no load or store is predicated
-    for (uint32_t b0 = 0; b0 < n; b0 += 32u * 16u) {
-        uint4 v[16];
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const uint32_t idx = min(b0 + (uint32_t)l + 32u * i, n - 1u);
-            v[i] = src[idx];
-        }
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const uint32_t idx = min(b0 + (uint32_t)l + 32u * i, n - 1u);
-            dst[idx] = v[i];
-        }
-    }
-}
-
 // Split-phase staging.  A kernel's prologue first issues every global load
 // it needs (tile offsets first, since the tile words depend on them; then the
 // decoder table, scales and activations; then the tile words) and only then
@@ -188,42 +140,10 @@ LW_DEV void lw_tab_put(uint8_t *lds, const LwTabRegs &r, int min_len, int max_le
     *(lw_lds_w16 *)(size_t)(lb + LW_PBASE - 2u * len) = (int16_t)((int32_t)lb + (int32_t)LW_TPAY + 4 * r.ent);
 }
 
-// The first 64 word rows of a tile block (16 x 16 bytes per lane of a
-// half-wave); rows beyond 64 are staged by lw_tile_put.  Indices past the
-// block are clamped to its last vector (no predicated loads or stores).
-struct LwTileRegs {
-    lw_u32x4 v[16];
-};
-
-LW_DEV void lw_tile_fetch(const uint32_t *words, uint32_t w0, uint32_t nrows, int l, LwTileRegs &r)
-{
-    const lw_u32x4 *src = reinterpret_cast<const lw_u32x4 *>(words + w0);
-    const uint32_t n = nrows * 8u;
-#pragma unroll
-    for (int i = 0; i < 16; i++) r.v[i] = src[min((uint32_t)l + 32u * i, n - 1u)];
-}
-
-LW_DEV void lw_tile_put(uint32_t *slots, const uint32_t *words, uint32_t w0, uint32_t nrows, int l,
-                        const LwTileRegs &r)
-{
-    const uint32_t base = (uint32_t)(size_t)(slots + 32);      // slot 1
-    const uint32_t n = nrows * 8u;
-#pragma unroll
-    for (int i = 0; i < 16; i++)
-        *(lw_lds_w128 *)(size_t)(base + 16u * min((uint32_t)l + 32u * i, n - 1u)) = r.v[i];
-    const lw_u32x4 *src = reinterpret_cast<const lw_u32x4 *>(words + w0);
-    for (uint32_t b0 = 512u; b0 < n; b0 += 512u) {            // long lanes: more batches
-        lw_u32x4 v[16];
-#pragma unroll
-        for (int i = 0; i < 16; i++) v[i] = src[min(b0 + (uint32_t)l + 32u * i, n - 1u)];
-#pragma unroll
-        for (int i = 0; i < 16; i++)
-            *(lw_lds_w128 *)(size_t)(base + 16u * min(b0 + (uint32_t)l + 32u * i, n - 1u)) = v[i];
-    }
-}
-
-// The same for a whole wavefront staging one tile: 8 x 16 bytes per lane
-// per batch of 64 word rows.
+// A wavefront stages one tile: lw_tile_fetch64 loads the first 64 word rows
+// of the tile block (8 x 16 bytes per lane), lw_tile_put64 stores them into
+// slots 1.. and stages any further rows in batches of 64.  Indices past the
+// block are clamped to its last vector, so no load or store is predicated.
 struct LwTileRegs64 {
     lw_u32x4 v[8];
 };
@@ -262,14 +182,6 @@ struct LaneDec {
     uint32_t hi, lo;             // 64-bit window
     uint32_t k;                  // SAD offset including the LDS base
 };
-
-LW_DEV void lw_window(LaneDec &d)
-{
-    const uint32_t p = d.slot0 + ((d.u >> 5) << 7);
-    const uint32_t a = lw_ld32(p), b = lw_ld32(p + 128), c = lw_ld32(p + 256);
-    d.hi = __builtin_amdgcn_alignbit(a, b, ~d.u);
-    d.lo = __builtin_amdgcn_alignbit(b, c, ~d.u);
-}
 
 // Count the limits the window's peek has passed; returns A = lb + PBASE - 2*len.
 template <int N8, int N16>
@@ -410,128 +322,6 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
     use_group(0, NG - 2);
     use_group(1, NG - 1);
 #undef LW_FENCE
-}
-
-// Two-stream version: a lane decodes its two tile rows as independent
-// chains -- stream 0 from the start of the lane (row 2l), stream 1 from the
-// split bit (row 2l+1) -- so each lane has two serial decode chains to
-// interleave instead of one.  Both rows cover the same columns at every
-// step, so group g of both streams shares the caller's fetch(g) (its
-// activations); use(g, j, pay0, pay1, aux) receives both rows' payloads.
-// Pipeline as lw_decode_pipelined, per stream.
-template <int N8, int N16, int NG, class Aux, bool UNROLL_ALL = false, class PayOff, class Fetch, class Use>
-LW_DEV void lw_decode2(LaneDec (&d)[2], const KArgs &a, PayOff pay_off, Fetch fetch, Use use)
-{
-    static_assert(NG % 2 == 0 && NG >= 4, "groups must be even");
-    uint32_t wa[2], wb[2], wc[2];
-    uint32_t code[2][2][4], A[2][2][4], base[2][2][4], pay[2][2][4];   // [parity][stream][symbol]
-    Aux aux[2];
-    auto issue_window = [&](int s) {
-        const uint32_t p = d[s].slot0 + ((d[s].u >> 5) << 7);
-        wa[s] = lw_ld32(p);
-        wb[s] = lw_ld32(p + 128);
-        wc[s] = lw_ld32(p + 256);
-    };
-    auto decode_group = [&](int q, int s) {
-        const uint32_t sh = ~d[s].u;
-        d[s].hi = __builtin_amdgcn_alignbit(wa[s], wb[s], sh);
-        d[s].lo = __builtin_amdgcn_alignbit(wb[s], wc[s], sh);
-        uint32_t ssum = 0;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const uint32_t Aj = lw_sad_count<N8, N16>(d[s].hi, d[s].k, a);
-            const uint32_t sj = Aj >> 1;
-            A[q][s][j] = Aj;
-            code[q][s][j] = d[s].hi >> (sj & 31u);
-            if (j < 3) lw_advance(d[s], sj);
-            ssum += sj;
-        }
-        d[s].u += 4u * (LW_PBASE / 2) - ssum;
-    };
-    auto issue_payloads = [&](int q, int g) {
-#pragma unroll
-        for (int s = 0; s < 2; s++)
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-                pay[q][s][j] =
-                    lw_ld32((uint32_t)((int32_t)(code[q][s][j] << 2) + (int32_t)base[q][s][j]) + pay_off(j));
-        aux[q] = fetch(g);
-    };
-    auto issue_params = [&](int q) {
-#pragma unroll
-        for (int s = 0; s < 2; s++)
-#pragma unroll
-            for (int j = 0; j < 4; j++) base[q][s][j] = (uint32_t)lw_ld16s(A[q][s][j]);
-    };
-    auto use_group = [&](int q, int g) {
-#pragma unroll
-        for (int j = 0; j < 4; j++) use(g, j, pay[q][0][j], pay[q][1][j], aux[q]);
-    };
-#define LW_FENCE() __builtin_amdgcn_sched_barrier(0)
-    issue_window(0);
-    issue_window(1);
-    LW_FENCE();
-    decode_group(0, 0);
-    decode_group(0, 1);
-    LW_FENCE();
-    issue_window(0);
-    issue_window(1);
-    LW_FENCE();
-    issue_params(0);
-    LW_FENCE();
-    decode_group(1, 0);
-    decode_group(1, 1);
-    LW_FENCE();
-    issue_window(0);
-    issue_window(1);
-    LW_FENCE();
-    issue_payloads(0, 0);
-    LW_FENCE();
-    issue_params(1);
-    LW_FENCE();
-#pragma unroll(UNROLL_ALL ? NG : 1)
-    for (int g = 2; g < NG; g += 2) {
-        decode_group(0, 0);    // group g (even)
-        decode_group(0, 1);
-        LW_FENCE();
-        issue_window(0);       // group g+1
-        issue_window(1);
-        LW_FENCE();
-        issue_payloads(1, g - 1);
-        LW_FENCE();
-        use_group(0, g - 2);
-        LW_FENCE();
-        issue_params(0);
-        LW_FENCE();
-        decode_group(1, 0);    // group g+1 (odd)
-        decode_group(1, 1);
-        LW_FENCE();
-        issue_window(0);       // group g+2 (past the end at the last step: in bounds)
-        issue_window(1);
-        LW_FENCE();
-        issue_payloads(0, g);
-        LW_FENCE();
-        use_group(1, g - 1);
-        LW_FENCE();
-        issue_params(1);
-        LW_FENCE();
-    }
-    issue_payloads(1, NG - 1);
-    use_group(0, NG - 2);
-    use_group(1, NG - 1);
-#undef LW_FENCE
-}
-
-// Set up both streams of a lane: stream 1 starts at the lane's split bit.
-LW_DEV bool lw_lane_init2(LaneDec (&d)[2], uint8_t *lds, const uint32_t *slots, int l, uint32_t split,
-                          const KArgs &a)
-{
-    const uint32_t lb = (uint32_t)(size_t)lds;
-    d[0].slot0 = d[1].slot0 = (uint32_t)(size_t)(slots + l);
-    d[0].u = 31;
-    d[1].u = 31 + split;
-    d[0].k = d[1].k = a.sad_k + lb;
-    return (lb & 63u) == 0;
 }
 
 // Set up a lane's decoder on its staged tile.  Returns false (the kernel must

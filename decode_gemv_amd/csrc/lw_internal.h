@@ -23,7 +23,6 @@
 #define LW_HEADER_BYTES 512
 #define LW_BATCH_MAX 16
 #define LW_CB_PER_WG 4             /* column blocks one workgroup covers (one per wave) */
-#define LW_RB_PER_WG 2             /* row bands one workgroup covers (two half-waves) */
 
 typedef struct {
     uint32_t magic;

@@ -6,10 +6,10 @@
 // At batch >= 8 the product is a real dense contraction (64 rows x 32
 // columns x 16 batch per step), so the decoded weights go through a small
 // LDS staging tile into v_mfma_f32_16x16x16{f16,bf16}:
-//   - each lane decodes its tile row (rows of the two row bands = the 64
-//     lanes of the wavefront) 32 columns at a time and writes them as
-//     16-bit values to stage[lane][0..31] (row stride 80 bytes: conflict-
-//     free 16-byte writes and 8-byte fragment reads);
+//   - one wavefront per tile: lane l + 32*half decodes tile row 2l + half
+//     (the second row from the lane's split bit) 32 columns at a time and
+//     writes them as 16-bit values to stage[lane][0..31] (row stride 80
+//     bytes: conflict-free 16-byte writes and 8-byte fragment reads);
 //   - every 32 columns, 2 k-steps x 4 row blocks of 16x16x16 MFMA
 //     accumulate D[row][batch] += W[row][k] * X[k][batch], with the X
 //     fragments (x[batch][k], zero for batch >= the call's batch) loaded
@@ -42,16 +42,19 @@ __host__ __device__ inline LdsLayout lds_layout(int max_words)
     LdsLayout L;
     L.stage = LW_TAB_BYTES;
     L.tiles = L.stage + WAVES * STAGE_BYTES;
-    const uint32_t tiles = (uint32_t)(WAVES * 2 * (max_words + 3) * 128);
-    const uint32_t red = (uint32_t)(WAVES * NB * 128 * 4);
+    const uint32_t tiles = (uint32_t)(WAVES * (max_words + 3) * 128);
+    const uint32_t red = (uint32_t)(WAVES * NB * 64 * 4);
     L.flag = L.tiles + (tiles > red ? tiles : red);
     L.total = L.flag + 16;
     return L;
 }
 
+// Identity of a lane: one wavefront per tile, lane l + 32*half decodes tile
+// row 2l + half (the second row from the lane's split bit); the lane's index
+// is also its row of the staged 64 x 32 weight block.
 struct LaneCtx {
-    int wave, lane, half, l, g, rbp, cb, rb, t;
-    bool wave_active, lane_active;
+    int wave, lane, half, l, g, cb, rb, t;
+    bool active;
 };
 
 LW_DEV LaneCtx lane_ctx(const KArgs &a)
@@ -62,13 +65,10 @@ LW_DEV LaneCtx lane_ctx(const KArgs &a)
     c.half = c.lane >> 5;
     c.l = c.lane & 31;
     c.g = blockIdx.x;
-    c.rbp = blockIdx.y;
+    c.rb = blockIdx.y;
     c.cb = c.g * WAVES + c.wave;
-    c.wave_active = c.cb < a.n_cb;
-    const int rb = c.rbp * 2 + c.half;
-    c.lane_active = c.wave_active && rb < a.n_rb;
-    c.rb = rb < a.n_rb ? rb : rb - 1;
-    c.t = c.rb * a.n_cb + (c.wave_active ? c.cb : 0);
+    c.active = c.cb < a.n_cb;
+    c.t = c.rb * a.n_cb + (c.active ? c.cb : 0);
     return c;
 }
 
@@ -103,22 +103,25 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
     const LdsLayout L = lds_layout(a.max_words);
     const LaneCtx c = lane_ctx(a);
     const int S = a.max_words + 3;
-    uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + (c.wave * 2 + c.half) * S * 32;
+    uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
     const uint32_t stage = (uint32_t)(size_t)(lds + L.stage + c.wave * STAGE_BYTES);
     const uint32_t my_row = stage + (uint32_t)(c.lane * STAGE_STRIDE);
     // MFMA fragment coordinates of this lane
     const int fr = c.lane & 15, fk = c.lane >> 4;
 
-    lw_stage_tab(lds, a.tab, a.min_len, a.max_len, false);
-    if (c.wave_active) {
-        const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-        lw_stage_tile(slots, a.words, w0, (w1 - w0) >> 5, c.l);
-    }
-    __syncthreads();
+    // issue every load, tile offsets first; table barrier; own tile (as in fused_q.hip)
+    const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
+    const LwTabRegs tr = lw_tab_fetch(a.tab, a.min_len, a.max_len, false);
+    const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
+    LwTileRegs64 tile;
+    lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
+    lw_tab_put(lds, tr, a.min_len, a.max_len);
+    __syncthreads();                      // the decoder table is complete
+    lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
 
     // x fragments: lane holds x[b = fr][col0 + 16 kk + 4 fk .. +3] for kk = 0, 1
     const bool xb_ok = fr < a.batch;
-    const uint16_t *xrow = a.x + (size_t)(xb_ok ? fr : 0) * a.cols + (size_t)(c.wave_active ? c.cb : 0) * 256 + 4 * fk;
+    const uint16_t *xrow = a.x + (size_t)(xb_ok ? fr : 0) * a.cols + (size_t)(c.active ? c.cb : 0) * 256 + 4 * fk;
     auto load_x = [&](int chunk, u32x2 (&dst)[2]) {
 #pragma unroll
         for (int kk = 0; kk < 2; kk++) {
@@ -127,105 +130,94 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
         }
     };
 
-    f4 acc[2][4];
+    f4 acc[4];
 #pragma unroll
-    for (int p = 0; p < 2; p++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) acc[p][r] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < 4; r++) acc[r] = f4{0.f, 0.f, 0.f, 0.f};
     float sx = 0.f;                          // sum of x[fr][k] over this lane's k subset
 
-    if (c.wave_active) {
+    if (c.active) {
         LaneDec d;
         const bool ok = lw_lane_init(d, lds, slots, c.l, a);
+        d.u += c.half ? split : 0u;       // the second tile row starts at the split bit
         if (ok) {
-            auto run_row = [&](auto pc) {
-                constexpr int p = decltype(pc)::value;
-                u32x2 xcur[2];
-                load_x(0, xcur);
-                uint32_t pend = 0;
-                auto mfma_step = [&](int chunk) {
+            u32x2 xcur[2];
+            load_x(0, xcur);
+            uint32_t pend = 0;
+            auto mfma_step = [&](int chunk) {
 #pragma unroll
-                    for (int kk = 0; kk < 2; kk++) {
-                        if (p == 0) {
-                            const f4 xf = {lw_half_lo(xcur[kk].x), lw_half_hi(xcur[kk].x), lw_half_lo(xcur[kk].y),
-                                           lw_half_hi(xcur[kk].y)};
-                            if constexpr (KIND == LW_BF16_EXP)
-                                sx += __builtin_bit_cast(float, xcur[kk].x << 16) +
-                                      __builtin_bit_cast(float, xcur[kk].x & 0xFFFF0000u) +
-                                      __builtin_bit_cast(float, xcur[kk].y << 16) +
-                                      __builtin_bit_cast(float, xcur[kk].y & 0xFFFF0000u);
-                            else
-                                sx += xf.x + xf.y + xf.z + xf.w;
-                        }
+                for (int kk = 0; kk < 2; kk++) {
+                    if constexpr (KIND == LW_BF16_EXP)
+                        sx += __builtin_bit_cast(float, xcur[kk].x << 16) +
+                              __builtin_bit_cast(float, xcur[kk].x & 0xFFFF0000u) +
+                              __builtin_bit_cast(float, xcur[kk].y << 16) +
+                              __builtin_bit_cast(float, xcur[kk].y & 0xFFFF0000u);
+                    else
+                        sx += lw_half_lo(xcur[kk].x) + lw_half_hi(xcur[kk].x) + lw_half_lo(xcur[kk].y) +
+                              lw_half_hi(xcur[kk].y);
 #pragma unroll
-                        for (int r = 0; r < 4; r++) {
-                            const u32x2 af = lw_ld64(stage + (uint32_t)((16 * r + fr) * STAGE_STRIDE + 32 * kk + 8 * fk));
-                            acc[p][r] = mfma<KIND>(af, xcur[kk], acc[p][r]);
-                        }
+                    for (int r = 0; r < 4; r++) {
+                        const u32x2 af = lw_ld64(stage + (uint32_t)((16 * r + fr) * STAGE_STRIDE + 32 * kk + 8 * fk));
+                        acc[r] = mfma<KIND>(af, xcur[kk], acc[r]);
                     }
-                    // x of the next chunk, used one chunk of decoding later
-                    load_x(chunk + 1 < 8 ? chunk + 1 : chunk, xcur);
-                };
-                auto put = [&](int g, int j, uint32_t pay, uint32_t smw) {
-                    // 16-bit weights of this symbol into the staged row
-                    if constexpr (KIND == LW_Q4_PAIR) {
-                        lw_st32(my_row + (uint32_t)(((g % GPC) * 4 + j) * 4), pay);
-                    } else {
-                        if (j & 1) {
-                            uint32_t w2;
-                            if constexpr (KIND == LW_BF16_EXP) {
-                                const uint32_t spread = __builtin_amdgcn_perm(smw, smw, j == 1 ? 0x01010000u : 0x03030202u);
-                                w2 = (spread & 0x807F807Fu) | pend | pay;
-                            } else {
-                                w2 = pend | pay;
-                            }
-                            lw_st32(my_row + (uint32_t)(((g % GPC) * 2 + (j >> 1)) * 4), w2);
-                        } else {
-                            pend = pay;
-                        }
-                    }
-                    if (j == 3 && (g % GPC) == GPC - 1) mfma_step(g / GPC);
-                };
-                auto pay_off = [](int j) { return (KIND != LW_Q4_PAIR && (j & 1)) ? (LW_TPAY_HI - LW_TPAY) : 0u; };
-                if constexpr (KIND == LW_BF16_EXP) {
-                    // sign+mantissa words stream in 16-group chunks, as in the VALU kernel
-                    const uint32_t *smrow = a.sm + (size_t)c.t * 4096 + (size_t)p * 64 * 32 + c.l;
-                    struct XA {
-                        uint32_t sm;
-                    };
-                    uint32_t ring[2][16];
-                    auto run_chunk = [&](int ch, const uint32_t (&cur)[16]) {
-                        lw_decode_pipelined<N8, N16, 16, XA, true>(
-                            d, a, pay_off, [&](int g) { return XA{cur[g]}; },
-                            [&](int g, int j, uint32_t pay, const XA &x) { put(16 * ch + g, j, pay, x.sm); });
-                    };
-#pragma unroll
-                    for (int i = 0; i < 16; i++) ring[0][i] = smrow[i * 32];
-#pragma unroll
-                    for (int ch = 0; ch < 4; ch += 2) {
-#pragma unroll
-                        for (int i = 0; i < 16; i++) ring[1][i] = smrow[((ch + 1) * 16 + i) * 32];
-                        run_chunk(ch, ring[0]);
-                        if (ch + 2 < 4)
-#pragma unroll
-                            for (int i = 0; i < 16; i++) ring[0][i] = smrow[((ch + 2) * 16 + i) * 32];
-                        run_chunk(ch + 1, ring[1]);
-                    }
-                } else {
-                    struct NoAux {};
-                    lw_decode_pipelined<N8, N16, NG, NoAux>(
-                        d, a, pay_off, [](int) { return NoAux{}; },
-                        [&](int g, int j, uint32_t pay, const NoAux &) { put(g, j, pay, 0u); });
                 }
+                // x of the next chunk, used one chunk of decoding later
+                load_x(chunk + 1 < 8 ? chunk + 1 : chunk, xcur);
             };
-            run_row(std::integral_constant<int, 0>{});
-            run_row(std::integral_constant<int, 1>{});
+            auto put = [&](int g, int j, uint32_t pay, uint32_t smw) {
+                // 16-bit weights of this symbol into the staged row
+                if constexpr (KIND == LW_Q4_PAIR) {
+                    lw_st32(my_row + (uint32_t)(((g % GPC) * 4 + j) * 4), pay);
+                } else {
+                    if (j & 1) {
+                        uint32_t w2;
+                        if constexpr (KIND == LW_BF16_EXP) {
+                            const uint32_t spread = __builtin_amdgcn_perm(smw, smw, j == 1 ? 0x01010000u : 0x03030202u);
+                            w2 = (spread & 0x807F807Fu) | pend | pay;
+                        } else {
+                            w2 = pend | pay;
+                        }
+                        lw_st32(my_row + (uint32_t)(((g % GPC) * 2 + (j >> 1)) * 4), w2);
+                    } else {
+                        pend = pay;
+                    }
+                }
+                if (j == 3 && (g % GPC) == GPC - 1) mfma_step(g / GPC);
+            };
+            auto pay_off = [](int j) { return (KIND != LW_Q4_PAIR && (j & 1)) ? (LW_TPAY_HI - LW_TPAY) : 0u; };
+            if constexpr (KIND == LW_BF16_EXP) {
+                // sign+mantissa words stream in 16-group chunks, as in the VALU kernel
+                const uint32_t *smrow = a.sm + (size_t)c.t * 4096 + (size_t)c.half * 64 * 32 + c.l;
+                struct XA {
+                    uint32_t sm;
+                };
+                uint32_t ring[2][16];
+                auto run_chunk = [&](int ch, const uint32_t (&cur)[16]) {
+                    lw_decode_pipelined<N8, N16, 16, XA, true>(
+                        d, a, pay_off, [&](int g) { return XA{cur[g]}; },
+                        [&](int g, int j, uint32_t pay, const XA &x) { put(16 * ch + g, j, pay, x.sm); });
+                };
+#pragma unroll
+                for (int i = 0; i < 16; i++) ring[0][i] = smrow[i * 32];
+#pragma unroll
+                for (int ch = 0; ch < 4; ch += 2) {
+#pragma unroll
+                    for (int i = 0; i < 16; i++) ring[1][i] = smrow[((ch + 1) * 16 + i) * 32];
+                    run_chunk(ch, ring[0]);
+                    if (ch + 2 < 4)
+#pragma unroll
+                        for (int i = 0; i < 16; i++) ring[0][i] = smrow[((ch + 2) * 16 + i) * 32];
+                    run_chunk(ch + 1, ring[1]);
+                }
+            } else {
+                struct NoAux {};
+                lw_decode_pipelined<N8, N16, NG, NoAux>(
+                    d, a, pay_off, [](int) { return NoAux{}; },
+                    [&](int g, int j, uint32_t pay, const NoAux &) { put(g, j, pay, 0u); });
+            }
         } else {
 #pragma unroll
-            for (int p = 0; p < 2; p++)
-#pragma unroll
-                for (int r = 0; r < 4; r++) acc[p][r] = f4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
-                                                           __builtin_nanf("")};
+            for (int r = 0; r < 4; r++)
+                acc[r] = f4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
         }
     }
     // sum of x over the tile's 256 columns for batch column fr
@@ -234,42 +226,38 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
 
     __syncthreads();                      // tiles no longer read: reuse for the reduction
     float *red = reinterpret_cast<float *>(lds + L.tiles);
-    // D lane layout: row R = 16 r + 4 fk + jj of the 64 staged rows (= wavefront
-    // lane R: half R/32, lane R%32), batch column fr
+    // D lane layout: staged row R = 16 r + 4 fk + jj (= wavefront lane R, which
+    // decoded tile row 2 (R % 32) + R / 32), batch column fr
 #pragma unroll
-    for (int p = 0; p < 2; p++)
+    for (int r = 0; r < 4; r++)
 #pragma unroll
-        for (int r = 0; r < 4; r++)
-#pragma unroll
-            for (int jj = 0; jj < 4; jj++) {
-                const int R = 16 * r + 4 * fk + jj;
-                const int h = R >> 5, l = R & 31;
-                const int rb = c.rbp * 2 + h;
-                float v = 0.f;
-                if (c.wave_active && rb < a.n_rb) {
-                    if constexpr (KIND == LW_BF16_EXP) {
-                        v = acc[p][r][jj];           // bf16 bundles carry no scales
-                    } else {
-                        const uint32_t w = a.dm[((size_t)rb * a.n_cb + c.cb) * 64 + 2 * l + p];
-                        v = lw_half_lo(w) * acc[p][r][jj] - lw_half_hi(w) * sx;
-                    }
+        for (int jj = 0; jj < 4; jj++) {
+            const int R = 16 * r + 4 * fk + jj;
+            const int trow = 2 * (R & 31) + (R >> 5);
+            float v = 0.f;
+            if (c.active) {
+                if constexpr (KIND == LW_BF16_EXP) {
+                    v = acc[r][jj];              // bf16 bundles carry no scales
+                } else {
+                    const uint32_t w = a.dm[(size_t)c.t * 64 + trow];
+                    v = lw_half_lo(w) * acc[r][jj] - lw_half_hi(w) * sx;
                 }
-                red[(c.wave * NB + fr) * 128 + h * 64 + 2 * l + p] = v;
             }
+            red[(c.wave * NB + fr) * 64 + trow] = v;
+        }
     __syncthreads();
     if constexpr (KIND == LW_BF16_EXP) {
         // verbatim segments (rare): the lane owning each row replaces the
         // placeholder weights' contribution by the stored values', per batch
         const uint32_t bits =
-            c.lane_active ? (a.vb_bits[(size_t)c.t * 8 + c.l / 4] >> (8 * (c.l % 4))) & 0xFFu : 0u;
+            c.active ? (a.vb_bits[(size_t)c.t * 8 + c.l / 4] >> (8 * (c.l % 4) + 4 * c.half)) & 0xFu : 0u;
         if (bits) {
             const uint16_t *xcol = a.x + (size_t)c.cb * 256;
-            for (int q = 0; q < 8; q++) {
-                if (!((bits >> q) & 1u)) continue;
-                const int p = q >> 2, seg = q & 3;
-                const uint32_t ord = lw_verbatim_ordinal(a, c.t, 8 * c.l + q);
+            const uint32_t *smw = a.sm + (size_t)c.t * 4096 + (size_t)c.half * 64 * 32 + c.l;
+            for (int seg = 0; seg < 4; seg++) {
+                if (!((bits >> seg) & 1u)) continue;
+                const uint32_t ord = lw_verbatim_ordinal(a, c.t, 8 * c.l + 4 * c.half + seg);
                 const uint16_t *vv = a.verbatim + (size_t)ord * 64;
-                const uint32_t *smw = a.sm + (size_t)c.t * 4096 + (size_t)p * 64 * 32 + c.l;
                 for (int b = 0; b < a.batch; b++) {
                     float sacc = 0.f;
                     for (int k = 0; k < 64; k++) {
@@ -280,21 +268,21 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
                                             __builtin_bit_cast(float, ph << 16);
                         sacc += wdiff * __builtin_bit_cast(float, (uint32_t)xcol[(size_t)b * a.cols + col] << 16);
                     }
-                    red[(c.wave * NB + b) * 128 + c.half * 64 + 2 * c.l + p] += sacc;
+                    red[(c.wave * NB + b) * 64 + 2 * c.l + c.half] += sacc;
                 }
             }
         }
         __syncthreads();
     }
     uint32_t *last_flag = reinterpret_cast<uint32_t *>(lds + L.flag);
-    lw_finish_rows<NB>(a, red, (int64_t)c.rbp * 128, c.g, c.rbp, WAVES, last_flag);
+    lw_finish_rows<NB, 64>(a, red, (int64_t)c.rb * 64, c.g, c.rb, WAVES, last_flag);
 }
 
 template <int KIND, int N8, int N16>
 hipError_t launch(const KArgs &a, hipStream_t s)
 {
     const LdsLayout L = lds_layout(a.max_words);
-    dim3 grid((unsigned)a.groups, (unsigned)((a.n_rb + 1) / 2));
+    dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
     auto kern = k_gemv_mfma<KIND, N8, N16>;
     hipError_t e = lw_allow_lds<k_gemv_mfma<KIND, N8, N16>>();
     if (e != hipSuccess) return e;
