@@ -179,8 +179,8 @@ LW_DEV void lw_tile_put64(uint32_t *slots, const uint32_t *words, uint32_t w0, u
 struct LaneDec {
     uint32_t slot0;              // LDS byte address of this lane's word in slot 0
     uint32_t u;                  // bit position + 31
-    uint32_t hi, lo;             // 64-bit window
     uint32_t k;                  // SAD offset including the LDS base
+    uint32_t ubias;              // 4 * (lb/2 + PBASE/2): what four shifts s add beyond the code lengths
 };
 
 // Count the limits the window's peek has passed; returns A = lb + PBASE - 2*len.
@@ -205,25 +205,6 @@ LW_DEV uint32_t lw_sad_count(uint32_t hi, uint32_t k, const KArgs &a)
     return s2 - s1;
 }
 
-// Decode one symbol from the window: returns the LDS byte address of its
-// entry in the first payload table (add LW_TPAY_HI - LW_TPAY for the second);
-// sets s (low five bits = 32 - len).
-template <int N8, int N16>
-LW_DEV uint32_t lw_symbol(const LaneDec &d, const KArgs &a, uint32_t &s)
-{
-    const uint32_t A = lw_sad_count<N8, N16>(d.hi, d.k, a);
-    const int32_t base = lw_ld16s(A);
-    s = A >> 1;
-    const uint32_t code = d.hi >> (s & 31u);
-    return (uint32_t)((int32_t)(code << 2) + base);
-}
-
-LW_DEV void lw_advance(LaneDec &d, uint32_t s)
-{
-    d.hi = __builtin_amdgcn_alignbit(d.hi, d.lo, s);
-    d.lo = __builtin_amdgcn_alignbit(d.lo, 0u, s);
-}
-
 // Software-pipelined decode of NG (even) groups of four symbols of one lane
 // stream.  LDS reads complete in issue order, so the loop keeps only the next
 // window read on the serial chain: in step g it decodes group g (VALU only),
@@ -243,26 +224,31 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
     uint32_t code[2][4], A[2][4], base[2][4], pay[2][4];
     Aux aux[2];
     auto issue_window = [&]() {
-        const uint32_t p = d.slot0 + ((d.u >> 5) << 7);
+        const uint32_t p = d.slot0 + ((d.u & ~31u) << 2);     // slot u >> 5, 128 bytes per slot
         wa = lw_ld32(p);
         wb = lw_ld32(p + 128);
         wc = lw_ld32(p + 256);
     };
+    // One group: align a 64-bit window at the group's first bit, then peek
+    // each symbol at its offset o within it (at most 33 bits in, so the
+    // 11-bit peek stays inside the window) with one 64-bit shift.  s_j is
+    // bias - len_j with bias = lb/2 + 512 a multiple of 64, so o = -sum(s)
+    // equals the offset modulo 64, which is all the shift reads.
     auto decode_group = [&](int q) {
         const uint32_t sh = ~d.u;
-        d.hi = __builtin_amdgcn_alignbit(wa, wb, sh);
-        d.lo = __builtin_amdgcn_alignbit(wb, wc, sh);
-        uint32_t ssum = 0;
+        const uint64_t win = ((uint64_t)__builtin_amdgcn_alignbit(wa, wb, sh) << 32) |
+                             (uint64_t)__builtin_amdgcn_alignbit(wb, wc, sh);
+        uint32_t o = 0;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const uint32_t Aj = lw_sad_count<N8, N16>(d.hi, d.k, a);
+            const uint32_t peek = j == 0 ? (uint32_t)(win >> 32) : (uint32_t)((win << (o & 63u)) >> 32);
+            const uint32_t Aj = lw_sad_count<N8, N16>(peek, d.k, a);
             const uint32_t s = Aj >> 1;
             A[q][j] = Aj;
-            code[q][j] = d.hi >> (s & 31u);
-            if (j < 3) lw_advance(d, s);
-            ssum += s;
+            code[q][j] = peek >> (s & 31u);
+            o -= s;
         }
-        d.u += 4u * (LW_PBASE / 2) - ssum;
+        d.u += o + d.ubias;               // u + sum(len)
     };
     auto issue_payloads = [&](int q, int g) {
 #pragma unroll
@@ -325,15 +311,17 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
 }
 
 // Set up a lane's decoder on its staged tile.  Returns false (the kernel must
-// then produce nothing) if the LDS base is not 64-byte aligned, which the
-// shift-amount identity s = A >> 1 needs.
+// then produce nothing) if the LDS base is not 128-byte aligned: the shift
+// amounts s = A >> 1 then carry a bias lb/2 + PBASE/2 that is a multiple of
+// 64, which both the 32-bit shifts and the 64-bit window offset need.
 LW_DEV bool lw_lane_init(LaneDec &d, uint8_t *lds, const uint32_t *slots, int l, const KArgs &a)
 {
     const uint32_t lb = (uint32_t)(size_t)lds;
     d.slot0 = (uint32_t)(size_t)(slots + l);
     d.u = 31;
     d.k = a.sad_k + lb;
-    return (lb & 63u) == 0;
+    d.ubias = 4u * (lb / 2u + LW_PBASE / 2u);
+    return (lb & 127u) == 0;
 }
 
 // Sum the per-wave partials of the workgroup's ROWS rows (red[wave][b][row])
