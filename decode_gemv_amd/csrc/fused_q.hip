@@ -22,20 +22,20 @@
 
 namespace {
 
-constexpr int WAVES = 4;
+constexpr int WAVES = 4;                 // wavefronts per workgroup (one column block each), by default
 
 struct LdsLayout {
     uint32_t x, tiles, flag, total;
 };
 
-__host__ __device__ inline LdsLayout lds_layout(int batch, int max_words, bool decode_only)
+__host__ __device__ inline LdsLayout lds_layout(int batch, int max_words, bool decode_only, int waves = WAVES)
 {
     LdsLayout L;
     L.x = LW_TAB_BYTES;
-    const uint32_t xbytes = decode_only ? 0u : (uint32_t)(WAVES * batch * 128 * 4);
+    const uint32_t xbytes = decode_only ? 0u : (uint32_t)(waves * batch * 128 * 4);
     L.tiles = L.x + xbytes;
-    const uint32_t tiles = (uint32_t)(WAVES * (max_words + 3) * 128);
-    const uint32_t red = (uint32_t)(WAVES * batch * 64 * 4);
+    const uint32_t tiles = (uint32_t)(waves * (max_words + 3) * 128);
+    const uint32_t red = (uint32_t)(waves * batch * 64 * 4);
     L.flag = L.tiles + (tiles > red ? tiles : red);
     L.total = L.flag + 16;
     return L;
@@ -47,7 +47,7 @@ struct LaneCtx {
     bool active;
 };
 
-LW_DEV LaneCtx lane_ctx(const KArgs &a)
+LW_DEV LaneCtx lane_ctx(const KArgs &a, int waves = WAVES)
 {
     LaneCtx c;
     c.wave = (int)lw_wave_id();
@@ -56,19 +56,22 @@ LW_DEV LaneCtx lane_ctx(const KArgs &a)
     c.l = c.lane & 31;                    // lane stream of the tile
     c.g = blockIdx.x;
     c.rb = blockIdx.y;
-    c.cb = c.g * WAVES + c.wave;
+    c.cb = c.g * waves + c.wave;
     c.active = c.cb < a.n_cb;
     c.t = c.rb * a.n_cb + (c.active ? c.cb : 0);
     return c;
 }
 
-template <int KIND, int N8, int N16, int BATCH>
-__global__ __launch_bounds__(256) void k_gemv_q(KArgs a)
+// WPG wavefronts per workgroup cover WPG consecutive column blocks of one row
+// band; with WPG >= K/256 a workgroup holds whole rows and the reduction
+// stays in LDS.
+template <int KIND, int N8, int N16, int BATCH, int WPG>
+__global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int SPL = KIND == LW_Q4_PAIR ? 256 : 512;
-    const LdsLayout L = lds_layout(BATCH, a.max_words, false);
-    const LaneCtx c = lane_ctx(a);
+    const LdsLayout L = lds_layout(BATCH, a.max_words, false, WPG);
+    const LaneCtx c = lane_ctx(a, WPG);
     const int S = a.max_words + 3;
     const uint32_t xs_addr = (uint32_t)(size_t)(lds + L.x) + 4u * (uint32_t)(c.wave * BATCH * 128);
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(256) void k_gemv_q(KArgs a)
     __syncthreads();
 
     uint32_t *last_flag = reinterpret_cast<uint32_t *>(lds + L.flag);
-    lw_finish_rows<BATCH, 64>(a, red, (int64_t)c.rb * 64, c.g, c.rb, WAVES, last_flag);
+    lw_finish_rows<BATCH, 64>(a, red, (int64_t)c.rb * 64, c.g, c.rb, WPG, last_flag);
 }
 
 
@@ -217,16 +220,31 @@ __global__ __launch_bounds__(256) void k_decode_q(KArgs a)
     if (a.lane_bits && c.half) a.lane_bits[(size_t)c.t * 32 + c.l] = d.u - 31;
 }
 
+template <int KIND, int N8, int N16, int BATCH, int WPG>
+hipError_t launch_gemv_wpg(const KArgs &a0, hipStream_t s)
+{
+    KArgs a = a0;
+    a.groups = (a.n_cb + WPG - 1) / WPG;  // column groups combined through the workspace (none if 1)
+    const LdsLayout L = lds_layout(BATCH, a.max_words, false, WPG);
+    dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
+    auto kern = k_gemv_q<KIND, N8, N16, BATCH, WPG>;
+    hipError_t e = lw_allow_lds<k_gemv_q<KIND, N8, N16, BATCH, WPG>>();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, grid, dim3(64 * WPG), L.total, s, a);
+    return hipGetLastError();
+}
+
+// Whole rows per workgroup (16 wavefronts, no cross-workgroup reduction) when
+// a row band has 13..16 column blocks and the tiles fit in LDS; else four.
 template <int KIND, int N8, int N16, int BATCH>
 hipError_t launch_gemv_q(const KArgs &a, hipStream_t s)
 {
-    const LdsLayout L = lds_layout(BATCH, a.max_words, false);
-    dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
-    auto kern = k_gemv_q<KIND, N8, N16, BATCH>;
-    hipError_t e = lw_allow_lds<k_gemv_q<KIND, N8, N16, BATCH>>();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, grid, dim3(256), L.total, s, a);
-    return hipGetLastError();
+    if constexpr (BATCH <= 4) {
+        if (a.n_cb > 12 && a.n_cb <= 16 &&
+            lds_layout(BATCH, a.max_words, false, 16).total <= (uint32_t)lw_device_lds_bytes())
+            return launch_gemv_wpg<KIND, N8, N16, BATCH, 16>(a, s);
+    }
+    return launch_gemv_wpg<KIND, N8, N16, BATCH, WAVES>(a, s);
 }
 
 template <int KIND, int N8, int N16>
@@ -287,12 +305,6 @@ hipError_t decode_plan(const KArgs &a, SadPlan p, hipStream_t s)
 }
 
 }  // namespace
-
-size_t lw_lds_bytes(int kind, int batch, int max_words, bool decode_only)
-{
-    (void)kind;
-    return lds_layout(batch, max_words, decode_only).total;
-}
 
 hipError_t lw_launch_gemv_q(const KArgs &a, int kind, SadPlan p, int batch, hipStream_t s)
 {

@@ -44,7 +44,6 @@ struct SadPlan {
 SadPlan lw_sad_plan(const lw_table &t, int min_len, int max_len, KArgs &a);
 
 // LDS bytes a fused/decode kernel needs per workgroup
-size_t lw_lds_bytes(int kind, int batch, int max_words, bool decode_only);
 
 hipError_t lw_launch_gemv_q(const KArgs &a, int kind, SadPlan p, int batch, hipStream_t s);
 hipError_t lw_launch_decode_q(const KArgs &a, int kind, SadPlan p, hipStream_t s);

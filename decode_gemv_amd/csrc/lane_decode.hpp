@@ -40,6 +40,22 @@
 
 #define LW_DEV __device__ __forceinline__
 
+// Host: the current device's largest LDS allocation per workgroup (cached
+// per device; 0 if the query fails).
+inline int lw_device_lds_bytes()
+{
+    constexpr int MAXDEV = 64;
+    static std::once_flag once[MAXDEV];
+    static int bytes[MAXDEV];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAXDEV) return 0;
+    std::call_once(once[dev], [dev]() {
+        if (hipDeviceGetAttribute(&bytes[dev], hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            bytes[dev] = 0;
+    });
+    return bytes[dev];
+}
+
 // Host: allow kernel KERN the device's largest dynamic LDS allocation, once
 // per device.  The limit is a permission, not an allocation (a launch still
 // reserves only what it asks for), so raising it to the maximum once keeps
