@@ -244,24 +244,28 @@ __global__ __launch_bounds__(256) void k_decode_bf16(KArgs a)
     LaneDec d;
     if (!lw_lane_init(d, lds, slots, c.l, a)) return;
     d.u += c.half ? split : 0u;
-    uint32_t *orow = reinterpret_cast<uint32_t *>(a.out) +
-                     (((int64_t)c.rb * 64 + 2 * c.l + c.half) * a.cols + (int64_t)c.cb * 256) / 2;
+    // the lane's restored row segment: each chunk of 16 groups (64 weights,
+    // 128 bytes) is collected in registers and written as 16-byte stores
+    uint4 *orow = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.out) +
+                                            ((int64_t)c.rb * 64 + 2 * c.l + c.half) * a.cols + (int64_t)c.cb * 256);
     struct XA {
         uint32_t sm;
     };
     uint32_t pend = 0;
     auto run_chunk = [&](int ch, const uint32_t (&cur)[CHUNK]) {
+        uint32_t buf[2 * CHUNK];
         lw_decode_pipelined<N8, N16, CHUNK, XA, true>(
             d, a, [](int j) { return (j & 1) ? (LW_TPAY_HI - LW_TPAY) : 0u; },
             [&](int g) { return XA{cur[g]}; },
             [&](int g, int j, uint32_t pay, const XA &x) {
-                if (j & 1) {
-                    const uint32_t w2 = (j == 1) ? lw_pair<0>(x.sm, pend, pay) : lw_pair<2>(x.sm, pend, pay);
-                    orow[2 * (ch * CHUNK + g) + (j >> 1)] = w2;
-                } else {
+                if (j & 1)
+                    buf[2 * g + (j >> 1)] = (j == 1) ? lw_pair<0>(x.sm, pend, pay) : lw_pair<2>(x.sm, pend, pay);
+                else
                     pend = pay;
-                }
             });
+#pragma unroll
+        for (int i = 0; i < CHUNK / 2; i++)
+            orow[ch * (CHUNK / 2) + i] = make_uint4(buf[4 * i], buf[4 * i + 1], buf[4 * i + 2], buf[4 * i + 3]);
     };
 #pragma unroll
     for (int ch = 0; ch < 64 / CHUNK; ch += 2) {

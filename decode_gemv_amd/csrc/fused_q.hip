@@ -201,21 +201,34 @@ __global__ __launch_bounds__(256) void k_decode_q(KArgs a)
     LaneDec d;
     if (!lw_lane_init(d, lds, slots, c.l, a)) return;
     d.u += c.half ? split : 0u;
-    uint32_t *out = reinterpret_cast<uint32_t *>(a.out);
     const int64_t row_bytes = KIND == LW_Q4_PAIR ? a.cols / 2 : a.cols;
     constexpr int NG = SPL / 8;           // groups of four symbols per tile row
-    uint32_t *orow = out + (((int64_t)c.rb * 64 + 2 * c.l + c.half) * row_bytes + (int64_t)c.cb * (SPL / 2)) / 4;
+    // The lane's restored row segment (4 bytes per group) is collected in
+    // registers, 32 groups at a time (the loop is unrolled, so every index
+    // is a compile-time constant), and written as 16-byte stores that cover
+    // whole 128-byte lines.
+    constexpr int PART = 32;
+    uint4 *orow = reinterpret_cast<uint4 *>(static_cast<uint8_t *>(a.out) +
+                                            ((int64_t)c.rb * 64 + 2 * c.l + c.half) * row_bytes +
+                                            (int64_t)c.cb * (SPL / 2));
     struct NoAux {};
-    uint32_t pk = 0;
-    lw_decode_pipelined<N8, N16, NG, NoAux>(
-        d, a, [](int) { return LW_TPAY_HI - LW_TPAY; }, [](int) { return NoAux{}; },
-        [&](int g, int j, uint32_t sym, const NoAux &) {
-            pk |= sym << (8 * j);
-            if (j == 3) {
-                orow[g] = pk;
-                pk = 0;
-            }
-        });
+#pragma unroll
+    for (int part = 0; part < NG / PART; part++) {
+        uint32_t buf[PART];
+        uint32_t pk = 0;
+        lw_decode_pipelined<N8, N16, PART, NoAux, true>(
+            d, a, [](int) { return LW_TPAY_HI - LW_TPAY; }, [](int) { return NoAux{}; },
+            [&](int g, int j, uint32_t sym, const NoAux &) {
+                pk |= sym << (8 * j);
+                if (j == 3) {
+                    buf[g] = pk;
+                    pk = 0;
+                }
+            });
+#pragma unroll
+        for (int i = 0; i < PART / 4; i++)
+            orow[part * (PART / 4) + i] = make_uint4(buf[4 * i], buf[4 * i + 1], buf[4 * i + 2], buf[4 * i + 3]);
+    }
     // the lane of the second row ends where the whole lane stream ends
     if (a.lane_bits && c.half) a.lane_bits[(size_t)c.t * 32 + c.l] = d.u - 31;
 }
