@@ -50,6 +50,7 @@ hipError_t lw_launch_decode_q(const KArgs &a, int kind, SadPlan p, hipStream_t s
 hipError_t lw_launch_gemv_mfma(const KArgs &a, int kind, SadPlan p, int batch, hipStream_t s);
 hipError_t lw_launch_gemv_bf16(const KArgs &a, SadPlan p, int batch, hipStream_t s);
 hipError_t lw_launch_decode_bf16(const KArgs &a, SadPlan p, hipStream_t s);
+hipError_t lw_launch_swiglu(const float *g, const float *u, uint16_t *h, int64_t n, hipStream_t s);
 hipError_t lw_launch_twin(const uint8_t *twin, const uint32_t *dm, int64_t rows, int64_t cols,
                           const uint16_t *x, float *y, int batch, hipStream_t s);
 hipError_t lw_launch_fill_zero(void *p, size_t bytes, hipStream_t s);

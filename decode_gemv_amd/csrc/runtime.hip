@@ -182,3 +182,13 @@ extern "C" lw_status lw_twin_gemv(const void *twin, const uint32_t *dm, int bits
     if (e != hipSuccess) return hip_fail(e, "twin launch");
     return LW_OK;
 }
+
+extern "C" lw_status lw_swiglu(const float *gate, const float *up, uint16_t *h, int64_t n, void *stream)
+{
+    if (n < 0) return lw_fail(LW_E_ARG, "negative length");
+    if (n == 0) return LW_OK;                  // nothing read or written: pointers may be null
+    if (!gate || !up || !h) return lw_fail(LW_E_ARG, "null argument");
+    hipError_t e = lw_launch_swiglu(gate, up, h, n, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "swiglu launch");
+    return LW_OK;
+}

@@ -64,6 +64,7 @@ def _load():
         "lw_gemv": (st, [P, P, P, i32, P]),
         "lw_decode_only": (st, [P, P, C.c_size_t, P, P]),
         "lw_twin_gemv": (st, [P, P, i32, i64, i64, P, P, i32, P]),
+        "lw_swiglu": (st, [P, P, P, i64, P]),
         "lw_status_str": (C.c_char_p, [st]),
         "lw_last_error": (C.c_char_p, []),
     }
@@ -233,6 +234,14 @@ def lw_decode_only(db: DevBundle, out, lane_bits=None, stream=None) -> None:
 def lw_twin_gemv(twin, dm, bits: int, rows: int, cols: int, x, y, batch: int, stream=None) -> None:
     _check(_L.lw_twin_gemv(_dptr(twin, "twin"), _dptr(dm, "dm"), bits, rows, cols, _dptr(x, "x"), _dptr(y, "y"),
                            batch, _stream(stream)))
+
+
+def lw_swiglu(gate, up, h, stream=None) -> None:
+    """h = fp16(silu(gate) * up) elementwise; gate, up fp32 and h fp16 (int16 bits) device tensors of equal size."""
+    n = gate.numel()
+    if up.numel() != n or h.numel() != n:
+        raise LwError(LW_E_ARG, "gate, up and h must have the same number of elements")
+    _check(_L.lw_swiglu(_dptr(gate, "gate"), _dptr(up, "up"), _dptr(h, "h"), n, _stream(stream)))
 
 
 # ---------------------------------------------------------------- conveniences

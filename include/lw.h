@@ -190,6 +190,21 @@ lw_status lw_decode_only(const lw_dev_bundle *db, void *out, size_t out_bytes, u
 lw_status lw_twin_gemv(const void *twin, const uint32_t *dm, int bits, int64_t rows, int64_t cols,
                        const void *x, float *y, int batch, void *stream);
 
+/* SwiGLU activation between the coded gate/up projections and the coded down
+ * projection of an MLP ("Unweight", section "Overlapping Work Across
+ * Transformer Layers": the down projection consumes gate, activation and up;
+ * section "Measured Results": SwiGLU architectures).
+ *   gate, up : device fp32 [n], e.g. the [batch][rows] outputs of lw_gemv on
+ *              the gate and up bundles
+ *   h        : device fp16 [n], overwritten with
+ *              h = fp16_rne(silu(gate) * up),  silu(z) = z / (1 + e^-z),
+ *              evaluated in fp32; the x of lw_gemv on the down bundle
+ *   n        : element count (0 does nothing and accepts null pointers)
+ * Enqueue-only on `stream`; any alignment (16-byte aligned buffers and n a
+ * multiple of 4 take the vector path).
+ * Errors: LW_E_ARG (n < 0, or a null pointer with n > 0), LW_E_DEVICE. */
+lw_status lw_swiglu(const float *gate, const float *up, uint16_t *h, int64_t n, void *stream);
+
 const char *lw_status_str(lw_status s);
 const char *lw_last_error(void);
 

@@ -18,8 +18,7 @@
  *   [SDB] "Software-Defined Bandwidth Expansion ..." -- section IV-A/IV-C
  *         (grouped storage w = d*q - m, dense dequantise-then-multiply check).
  *
- * Readings of points the pages leave open are stated at each function; the
- * same list is kept in the repository's design notes.
+ * Readings of points the pages leave open are stated at each function.
  *
  * Parity pins: every function here is pinned by the CPU tests (Kraft
  * equality, brute-force optimal lengths, dyadic closed form, textbook heap
@@ -416,6 +415,42 @@ double or_half_to_double(uint16_t h)
     else if (e == 31) v = m ? NAN : INFINITY;
     else v = ldexp((double)(1024 + m), e - 25);
     return s ? -v : v;
+}
+
+/* double -> fp16 bits, round to nearest with ties to even (IEEE 754
+ * binary16), the rounding the activations between the MLP projections get.
+ * Worked from the binary expansion: a = f * 2^e, f in [0.5, 1), keeps an
+ * 11-bit significand; below 2^-14 the grid is multiples of 2^-24; from
+ * 65520 (halfway to 2^16) on the result is infinity. */
+uint16_t or_double_to_half(double v)
+{
+    const uint16_t s = signbit(v) ? 0x8000u : 0u;
+    const double a = fabs(v);
+    if (isnan(v)) return 0x7E00u;
+    if (a >= 65520.0) return (uint16_t)(s | 0x7C00u);
+    if (a < ldexp(1.0, -14)) {
+        const double q = nearbyint(ldexp(a, 24));     /* exact scaling, then ties to even */
+        return (uint16_t)(s | (uint16_t)q);           /* q == 1024 is the smallest normal */
+    }
+    int e;
+    const double f = frexp(a, &e);
+    double q = nearbyint(ldexp(f, 11));                /* significand in [1024, 2048] */
+    if (q == 2048.0) {
+        q = 1024.0;
+        e += 1;
+    }
+    const int E = e - 1 + 15;
+    if (E >= 31) return (uint16_t)(s | 0x7C00u);
+    return (uint16_t)(s | (uint16_t)(E << 10) | (uint16_t)((int)q - 1024));
+}
+
+/* SwiGLU activation of an MLP ([UW] "Overlapping Work Across Transformer
+ * Layers": the down projection consumes gate, activation and up; "Measured
+ * Results": SwiGLU architectures): h = fp16(silu(g) * u) with
+ * silu(z) = z / (1 + e^-z), in double, rounded once. */
+void or_swiglu(int64_t n, const double *g, const double *u, uint16_t *h)
+{
+    for (int64_t i = 0; i < n; i++) h[i] = or_double_to_half(g[i] / (1.0 + exp(-g[i])) * u[i]);
 }
 
 /* Exact bf16 -> double. */

@@ -57,6 +57,8 @@ def lib():
             "or_decode_limit": (i32, [i64, i32, P, P, P, P, P, P, P, P, P]),
             "or_decode_bitwise": (i32, [i64, i32, P, P, i32, P, P, P]),
             "or_half_to_double": (C.c_double, [C.c_uint16]),
+            "or_double_to_half": (C.c_uint16, [C.c_double]),
+            "or_swiglu": (None, [i64, P, P, P]),
             "or_bf16_to_double": (C.c_double, [C.c_uint16]),
             "or_pack_dm": (None, [i64, i64, P, P, P]),
             "or_gemv_q": (None, [i64, i64, P, P, P, P, i32, P, i64, P]),
@@ -179,6 +181,29 @@ def pack_dm(d: np.ndarray, m: np.ndarray) -> np.ndarray:
     lib().or_pack_dm(R, ncb * 256, _p(np.ascontiguousarray(d, np.uint16)),
                      _p(np.ascontiguousarray(m, np.uint16)), _p(dm))
     return dm
+
+
+def double_to_half(v: float) -> int:
+    return lib().or_double_to_half(v)
+
+
+def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """fp16 bits of silu(g) * u, elementwise, from fp64 g and u."""
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    h = np.zeros(g.shape, dtype=np.uint16)
+    lib().or_swiglu(g.size, _p(g), _p(u), _p(h))
+    return h
+
+
+def mlp_pass_q(gate, up, down, x, batch: int) -> np.ndarray:
+    """One SwiGLU MLP pass over quantised matrices, all in fp64: gate, up and
+    down are (codes, d, m) with down's columns = gate's rows; the gate and up
+    outputs meet in swiglu (rounded to fp16 once), which is down's input.
+    Returns y [batch][down rows]."""
+    g = gemv_q(*gate, x, batch)
+    u = gemv_q(*up, x, batch)
+    return gemv_q(*down, swiglu(g, u), batch)
 
 
 def gemv_q(codes, d, m, x, batch: int, rows=None) -> np.ndarray:

@@ -121,6 +121,14 @@ def test_argument_errors():
     assert dg.lw_status_str(dg.LW_E_TABLE) == "invalid code table"
 
 
+def test_swiglu_argument_rules():
+    # host-side checks only: each of these returns before any HIP call
+    from decode_gemv_amd import lw
+    assert lw._L.lw_swiglu(None, None, None, 0, None) == dg.LW_OK          # empty: nothing touched
+    assert lw._L.lw_swiglu(None, None, None, -1, None) == dg.LW_E_ARG
+    assert lw._L.lw_swiglu(None, None, None, 5, None) == dg.LW_E_ARG
+
+
 def _image(seed=31, kind=dg.LW_Q4_PAIR):
     codes, d, m, _ = synth.gen_q_custom(128, 1024, seed)
     b = dg.lw_bundle_build_q(kind, codes, d, m)

@@ -421,3 +421,60 @@ def test_row_split_marks_second_row(case):
             assert first == list(syms[t, l, :spl // 2])
             second, _ = _bitwise_from(bits, int(split[t, l]), spl // 2, code_map)
             assert second == list(syms[t, l, spl // 2:])
+
+
+def test_double_to_half_matches_numpy_rounding():
+    # or_double_to_half against numpy's correctly rounded float64 -> float16
+    # conversion: every fp16 value, every midpoint between neighbours (ties
+    # go to even), random values over the normal, subnormal and overflow
+    # ranges, signed zeros and infinities
+    allh = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    vals = allh.view(np.float16).astype(np.float64)
+    vals = vals[np.isfinite(vals)]
+    srt = np.unique(vals)
+    mids = (srt[:-1] + srt[1:]) / 2
+    rng = np.random.default_rng(5)
+    rnd = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 6, 20000),
+                          rng.uniform(65000, 70000, 200), -rng.uniform(65000, 70000, 200),
+                          [0.0, -0.0, np.inf, -np.inf, 65504.0, 65519.99, 65520.0, 2.0 ** -24, 2.0 ** -25,
+                           3 * 2.0 ** -26, 2.0 ** -14 - 2.0 ** -26]])
+    for v in np.concatenate([vals, mids, rnd]):
+        want = int(np.float64(v).astype(np.float16).view(np.uint16))
+        assert O.double_to_half(float(v)) == want, (v, hex(want))
+
+
+def test_swiglu_matches_expit():
+    # h = fp16(silu(g) u), silu(z) = z * sigmoid(z) with scipy's logistic
+    from scipy.special import expit
+    rng = np.random.default_rng(6)
+    g = np.concatenate([rng.standard_normal(5000) * 3, [0.0, 30.0, -30.0, 1e-6, -1e-6]])
+    u = np.concatenate([rng.standard_normal(5000) * 3, [2.0, 1.5, 7.0, 1.0, 1.0]])
+    want = (g * expit(g) * u).astype(np.float16).view(np.uint16)
+    assert np.array_equal(O.swiglu(g, u), want)
+    assert O.swiglu(np.array([0.0]), np.array([5.0]))[0] == 0           # silu(0) = 0
+
+
+@pytest.mark.parametrize("kind", ["q4", "q6"])
+def test_mlp_pass_vs_dense(kind):
+    # the oracle's MLP pass against dense fp64 matrices materialised as d*q - m
+    from scipy.special import expit
+    qmax = 15 if kind == "q4" else 63
+    mu, sc = (7.5, 1.8) if kind == "q4" else (31.5, 5.0)
+    R, C = 512, 256                       # gate, up: R x C; down: C x R
+    gate = synth.gen_q_custom(R, C, 81, qmax=qmax, mu=mu, scale=sc)
+    up = synth.gen_q_custom(R, C, 82, qmax=qmax, mu=mu, scale=sc)
+    down = synth.gen_q_custom(C, R, 83, qmax=qmax, mu=mu, scale=sc)
+    x = gate[3]
+
+    def dense(codes, d, m):
+        df = np.repeat(d.view(np.float16).astype(np.float64), 256, axis=1)
+        mf = np.repeat(m.view(np.float16).astype(np.float64), 256, axis=1)
+        return df * codes - mf
+
+    xf = x[:2].view(np.float16).astype(np.float64)
+    g = xf @ dense(*gate[:3]).T
+    u = xf @ dense(*up[:3]).T
+    h = (g * expit(g) * u).astype(np.float16).astype(np.float64)
+    want = h @ dense(*down[:3]).T
+    got = O.mlp_pass_q(gate[:3], up[:3], down[:3], x, 2)
+    assert np.allclose(got, want, rtol=1e-9, atol=1e-9 * np.abs(want).max())
