@@ -106,10 +106,11 @@ class Bundle:
 
     def __init__(self, ptr: int):
         self.ptr = C.c_void_p(ptr)
+        self._free = _L.lw_bundle_free      # held here: module globals may be gone at interpreter exit
 
     def __del__(self):
         if getattr(self, "ptr", None) and self.ptr.value:
-            _L.lw_bundle_free(self.ptr)
+            self._free(self.ptr)
             self.ptr = None
 
 
@@ -208,10 +209,11 @@ class DevBundle:
         self.ptr = C.c_void_p(ptr)
         self.buf = buf
         self.info = info
+        self._free = _L.lw_dev_bundle_free  # held here: module globals may be gone at interpreter exit
 
     def __del__(self):
         if getattr(self, "ptr", None) and self.ptr.value:
-            _L.lw_dev_bundle_free(self.ptr)
+            self._free(self.ptr)
             self.ptr = None
 
 
