@@ -15,8 +15,9 @@
  *   [UW]  "Unweight: Compressing LLM Weights for Faster Inference" -- sections
  *         "Understanding BF16 weight structure" and "The exponent's exploitable
  *         redundancy" (exponent palette, 64-weight verbatim rows).
- *   [SDB] "Software-Defined Bandwidth Expansion ..." -- section IV-A/IV-C
- *         (grouped storage w = d*q - m, dense dequantise-then-multiply check).
+ *   [SDB] "Software-Defined Bandwidth Expansion ..." -- sections IV-A/IV-C
+ *         (grouped storage w = d*q - m, dense dequantise-then-multiply check;
+ *         IV-B tile-transposed layout and IV-C tile skipping and its ledger).
  *
  * Readings of points the pages leave open are stated at each function.
  *
@@ -684,4 +685,82 @@ void or_bf16_reconstruct(int64_t rows, int64_t cols, const uint16_t *syms, const
                 }
             }
         }
+}
+
+/* ------------------------------------------------------------------------
+ * Tile-skipping fixed-width GEMV ([SDB] IV-A storage, IV-B layout, IV-C
+ * kernel and traffic ledger).
+ *
+ * Storage: b-bit codes (b in {2, 4, 8}), floor(32/b) = 32/b per 32-bit word,
+ * the weight at position i of a word in bits b*i .. b*i+b-1 (low bits first:
+ * the reading of "packed into 32-bit words" used here).  Groups of 256
+ * columns carry an fp16 scale d and zero m, w = d*q - m (the super-block of
+ * the coded path, so all paths share the same d, m).
+ * Layout: words[t][j][r] with t the tile of B_N = 64 consecutive rows, j the
+ * word column (0 .. WPR-1, WPR = cols / (32/b)) and r the row within the
+ * tile; scales dm[t][g][r] = d | m << 16 for the 256-column group g.
+ */
+#define OR_SKIP_BN 64
+
+void or_skip_pack(int64_t rows, int64_t cols, int bits, const uint8_t *q, const uint16_t *d,
+                  const uint16_t *m, uint32_t *words, uint32_t *dm)
+{
+    int64_t per = 32 / bits, wpr = cols / per, ng = cols / OR_TILE_COLS;
+    for (int64_t r = 0; r < rows; r++) {
+        int64_t t = r / OR_SKIP_BN, rr = r % OR_SKIP_BN;
+        for (int64_t j = 0; j < wpr; j++) {
+            uint32_t w = 0;
+            for (int64_t i = 0; i < per; i++)
+                w |= (uint32_t)q[r * cols + j * per + i] << (bits * i);
+            words[(t * wpr + j) * OR_SKIP_BN + rr] = w;
+        }
+        for (int64_t g = 0; g < ng; g++)
+            dm[(t * ng + g) * OR_SKIP_BN + rr] = (uint32_t)d[r * ng + g] | ((uint32_t)m[r * ng + g] << 16);
+    }
+}
+
+/* y[b][r] in double for the rows of every tile in the list, read back from
+ * the packed words and scales; rows of other tiles are not written.  A list
+ * entry outside 0 .. n_tiles-1 names no tile and is skipped (a repeated entry
+ * writes the same values again). */
+void or_skip_gemv(int64_t rows, int64_t cols, int bits, const uint32_t *words, const uint32_t *dm,
+                  const int32_t *tiles, int64_t n_list, const uint16_t *x, int batch, double *y)
+{
+    int64_t per = 32 / bits, wpr = cols / per, ng = cols / OR_TILE_COLS, nt = rows / OR_SKIP_BN;
+    uint32_t mask = (1u << bits) - 1u;
+    for (int64_t k = 0; k < n_list; k++) {
+        int64_t t = tiles[k];
+        if (t < 0 || t >= nt) continue;
+        for (int b = 0; b < batch; b++)
+            for (int64_t rr = 0; rr < OR_SKIP_BN; rr++) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < wpr; j++) {
+                    uint32_t w = words[(t * wpr + j) * OR_SKIP_BN + rr];
+                    for (int64_t i = 0; i < per; i++) {
+                        int64_t c = j * per + i;
+                        uint32_t sc = dm[(t * ng + c / OR_TILE_COLS) * OR_SKIP_BN + rr];
+                        double q = (double)((w >> (bits * i)) & mask);
+                        double wt = or_half_to_double((uint16_t)(sc & 0xFFFF)) * q -
+                                    or_half_to_double((uint16_t)(sc >> 16));
+                        acc += wt * or_half_to_double(x[(int64_t)b * cols + c]);
+                    }
+                }
+                y[(int64_t)b * rows + t * OR_SKIP_BN + rr] = acc;
+            }
+    }
+}
+
+/* Traffic ledger of one call with n_active listed tiles ([SDB] IV-C: the
+ * words touched are exactly n_active * WPR * B_N).  out[0] words, out[1]
+ * word bytes, out[2] scale bytes, out[3] activation bytes, out[4] output
+ * bytes, out[5] their sum. */
+void or_skip_ledger(int64_t cols, int bits, int64_t n_active, int batch, uint64_t out[6])
+{
+    uint64_t wpr = (uint64_t)(cols / (32 / bits));
+    out[0] = (uint64_t)n_active * wpr * OR_SKIP_BN;
+    out[1] = 4 * out[0];
+    out[2] = (uint64_t)n_active * (uint64_t)(cols / OR_TILE_COLS) * OR_SKIP_BN * 4;
+    out[3] = (uint64_t)batch * (uint64_t)cols * 2;
+    out[4] = (uint64_t)batch * (uint64_t)n_active * OR_SKIP_BN * 4;
+    out[5] = out[1] + out[2] + out[3] + out[4];
 }

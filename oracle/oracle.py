@@ -68,6 +68,9 @@ def lib():
             "or_bf16_symbolise": (None, [i64, i64, P, P, i32, P, P]),
             "or_bf16_pack_sm": (None, [i64, i64, P, P]),
             "or_bf16_reconstruct": (None, [i64, i64, P, P, P, P, P, P, P]),
+            "or_skip_pack": (None, [i64, i64, i32, P, P, P, P, P]),
+            "or_skip_gemv": (None, [i64, i64, i32, P, P, P, i64, P, i32, P]),
+            "or_skip_ledger": (None, [i64, i32, i64, i32, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -322,3 +325,39 @@ def decode_bundle_bf16(b: dict, bitwise: bool = False):
     lib().or_bf16_reconstruct(R, Cc, _p(syms), _p(b["sm"]), _p(b["palette"]), _p(b["vb_bits"]),
                               _p(b["vb_start"]), _p(verb), _p(out))
     return out, bits
+
+
+# ---------------------------------------------------------------- tile-skipping twin
+SKIP_BN = 64
+
+
+def skip_pack(codes: np.ndarray, bits: int, d: np.ndarray, m: np.ndarray):
+    """Tile-transposed fixed-width words [tiles][WPR][64] and scales
+    [tiles][cols/256][64] ("Software-Defined Bandwidth Expansion" IV-A, IV-B)."""
+    R, Cc = codes.shape
+    wpr = Cc // (32 // bits)
+    words = np.zeros((R // SKIP_BN) * wpr * SKIP_BN, dtype=np.uint32)
+    dm = np.zeros((R // SKIP_BN) * (Cc // 256) * SKIP_BN, dtype=np.uint32)
+    lib().or_skip_pack(R, Cc, bits, _p(np.ascontiguousarray(codes, np.uint8)),
+                       _p(np.ascontiguousarray(d, np.uint16)), _p(np.ascontiguousarray(m, np.uint16)),
+                       _p(words), _p(dm))
+    return words, dm
+
+
+def skip_gemv(words, dm, bits: int, rows: int, cols: int, tiles, x, batch: int, y=None) -> np.ndarray:
+    """fp64 y [batch][rows]: rows of listed tiles computed from the packed
+    words, every other row left as it was in y (NaN when y is not given)."""
+    tl = np.ascontiguousarray(tiles, dtype=np.int32)
+    x = np.ascontiguousarray(x[:batch], dtype=np.uint16)
+    if y is None:
+        y = np.full((batch, rows), np.nan)
+    lib().or_skip_gemv(rows, cols, bits, _p(words), _p(dm), _p(tl) if tl.size else None, tl.size, _p(x),
+                       batch, _p(y))
+    return y
+
+
+def skip_ledger(cols: int, bits: int, n_active: int, batch: int) -> dict:
+    out = np.zeros(6, dtype=np.uint64)
+    lib().or_skip_ledger(cols, bits, n_active, batch, _p(out))
+    return dict(zip(("words", "word_bytes", "scale_bytes", "x_bytes", "y_bytes", "total_bytes"),
+                    (int(v) for v in out)))

@@ -161,3 +161,23 @@ def gen_bf16_custom(rows: int, cols: int, seed: int, sigma: float = 0.02,
     w = f32_to_bf16_bits(z).reshape(rows, cols)
     x = f32_to_bf16_bits(rx.standard_normal((XROWS, cols)).astype(np.float32))
     return w, x
+
+
+def gen_fixed(rows: int, cols: int, bits: int, seed: int):
+    """b-bit codes for the fixed-width paths: q = clamp(rint(N((2^b - 1)/2,
+    2^b / 8.9)), 0, 2^b - 1) (the 4-bit law N(7.5, 1.8) scaled to b bits),
+    fp16 d ~ U(0.005, 0.02) per 256 columns, m = 2^(b-1) d, fp16 x ~ N(0, 1)."""
+    top = (1 << bits) - 1
+    rc, rs, rx = [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(3)]
+    codes = _codes(rc, "normal", top / 2.0, (1 << bits) / 8.9, rows, cols, top)
+    d = rs.uniform(0.005, 0.02, size=(rows, cols // SUPER)).astype(np.float16)
+    m = (d.astype(np.float32) * (1 << (bits - 1))).astype(np.float16)
+    x = rx.standard_normal((XROWS, cols)).astype(np.float16)
+    return codes, d.view(np.uint16), m.view(np.uint16), x.view(np.uint16)
+
+
+def active_tiles(n_tiles: int, n_active: int, seed: int) -> np.ndarray:
+    """A seeded set of n_active distinct tile indices in increasing order (the
+    synthetic stand-in for a sparsity predictor's launch list)."""
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(n_tiles, size=n_active, replace=False)).astype(np.int32)

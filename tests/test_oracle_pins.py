@@ -478,3 +478,95 @@ def test_mlp_pass_vs_dense(kind):
     want = h @ dense(*down[:3]).T
     got = O.mlp_pass_q(gate[:3], up[:3], down[:3], x, 2)
     assert np.allclose(got, want, rtol=1e-9, atol=1e-9 * np.abs(want).max())
+
+
+# ------------------------------------------------- tile-skipping fixed-width twin
+
+def _skip_golden():
+    rows = []
+    with open(os.path.join(os.path.dirname(__file__), "golden", "skip_layout.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def test_skip_layout_golden():
+    """Words and scales of the tile-transposed layout against the hand-worked
+    values of tests/golden/skip_layout.txt ("Software-Defined Bandwidth
+    Expansion" IV-A, IV-B)."""
+    R, Cc = 128, 256
+    rr, cc = np.meshgrid(np.arange(R), np.arange(Cc), indexing="ij")
+    d = np.arange(R, dtype=np.uint16).reshape(R, 1)
+    m = (1000 + np.arange(R)).astype(np.uint16).reshape(R, 1)
+    packed = {}
+    for bits in (2, 4, 8):
+        packed[bits] = O.skip_pack(((rr + cc) % (1 << bits)).astype(np.uint8), bits, d, m)
+    n = 0
+    for f in _skip_golden():
+        if f[0] == "dm":
+            r, want = int(f[1]), int(f[2], 16)
+            assert packed[4][1][((r // 64) * 1 + 0) * 64 + r % 64] == want
+        else:
+            bits, r, j, want = int(f[0]), int(f[1]), int(f[2]), int(f[3], 16)
+            wpr = Cc // (32 // bits)
+            got = packed[bits][0][((r // 64) * wpr + j) * 64 + r % 64]
+            assert got == want, (bits, r, j, hex(int(got)), hex(want))
+        n += 1
+    assert n == 13
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_skip_gemv_all_tiles_is_dense(bits):
+    """With every tile listed the packed GEMV is the dense dequantise-then-
+    multiply product over the original codes (IV-C's validation)."""
+    codes, d, m, x = synth.gen_fixed(192, 768, bits, 40 + bits)
+    words, dm = O.skip_pack(codes, bits, d, m)
+    y = O.skip_gemv(words, dm, bits, 192, 768, np.arange(3), x, 2)
+    ref = O.gemv_q(codes, d, m, x, 2)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_skip_gemv_skips_and_touches_only_listed_tiles():
+    """Rows of unlisted tiles are not written; repeated entries give the same
+    rows and out-of-range entries name no tile; words outside the listed
+    tiles do not enter the result, and the listed tiles hold exactly
+    n_active * WPR * B_N words (the IV-C ledger)."""
+    bits, R, Cc = 4, 64 * 8, 512
+    codes, d, m, x = synth.gen_fixed(R, Cc, bits, 77)
+    words, dm = O.skip_pack(codes, bits, d, m)
+    tiles = np.array([5, 1, 6, 1, -1, 8, 1000], dtype=np.int32)      # 3 distinct valid tiles + junk
+    active = [1, 5, 6]
+    y = O.skip_gemv(words, dm, bits, R, Cc, tiles, x, 1)
+    ref = O.gemv_q(codes, d, m, x, 1)
+    for t in range(R // 64):
+        sl = slice(64 * t, 64 * t + 64)
+        if t in active:
+            np.testing.assert_allclose(y[0, sl], ref[0, sl], rtol=1e-12, atol=1e-12)
+        else:
+            assert np.all(np.isnan(y[0, sl]))
+    wpr = Cc // (32 // bits)
+    poisoned = np.full_like(words, 0xFFFFFFFF)
+    kept = 0
+    for t in active:
+        sl = slice(t * wpr * 64, (t + 1) * wpr * 64)
+        poisoned[sl] = words[sl]
+        kept += sl.stop - sl.start
+    y2 = O.skip_gemv(poisoned, dm, bits, R, Cc, np.array(active, np.int32), x, 1)
+    np.testing.assert_array_equal(np.nan_to_num(y2, nan=7.0), np.nan_to_num(y, nan=7.0))
+    assert kept == O.skip_ledger(Cc, bits, len(active), 1)["words"] == len(active) * wpr * 64
+
+
+def test_skip_ledger_page_configuration():
+    """The representative configuration of IV-C (N = 1024, K = 4096, b = 2,
+    B_N = 64, 6 of 16 tiles active): words touched n_active * WPR * B_N with
+    WPR = K / 16 = 256, i.e. 98304 words; against a dense fp16 pass of the
+    whole matrix (8 MiB) the weight words alone are 1/64 of the bytes at full
+    activity (16 bits per weight -> 2) times 6/16."""
+    L = O.skip_ledger(4096, 2, 6, 1)
+    assert L["words"] == 6 * 256 * 64 == 98304
+    assert L["word_bytes"] == 4 * 98304
+    dense = 1024 * 4096 * 2
+    assert dense / (4 * 16 * 256 * 64) == 8.0          # packing alone, all 16 tiles
+    assert L["scale_bytes"] == 6 * 16 * 64 * 4
+    assert L["total_bytes"] == L["word_bytes"] + L["scale_bytes"] + 4096 * 2 + 6 * 64 * 4
