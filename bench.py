@@ -179,6 +179,41 @@ def cpu_baseline(mat, codes, d, m, xb, batch, coded):
             "one_thread_value": round(coded / t1 / 1e9, 4)}
 
 
+def skip_legs(torch, dg, synth, mat, codes, d, m, x, batch, a):
+    """Tile-skipping fixed-width GEMV (lw_skip_gemv): the same 4-bit codes and
+    scales in the tile-transposed layout with every tile listed and with a
+    seeded 40 % launch list, and the representative configuration of the
+    skipping kernel's page (1024 x 4096, 2-bit codes, 6 of 16 tiles).  Bytes
+    are the traffic ledger: listed tiles' words and scales + x + listed y rows."""
+    out = {}
+
+    def leg(words, dm, bits, rows, cols, tiles, xx, name):
+        n_act = len(set(int(t) for t in tiles))
+        wpr = cols * bits // 32
+        ledger = n_act * (wpr * 64 * 4 + (cols // 256) * 64 * 4) + 2 * batch * cols + 4 * batch * 64 * n_act
+        per_copy = words.nbytes + dm.nbytes
+        n = max(2, -(-2 * MALL_BYTES // per_copy))
+        wd = [torch.from_numpy(words.view(np.int32)).cuda() for _ in range(n)]
+        dd = [torch.from_numpy(dm.view(np.int32)).cuda() for _ in range(n)]
+        td = torch.from_numpy(np.ascontiguousarray(tiles, np.int32)).cuda()
+        yy = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
+        f = lambda i: dg.lw_skip_gemv(wd[i], dd[i], bits, rows, cols, td, xx, yy, batch)
+        ms = time_graph(torch, f, n, a.steps, a.warmup) or time_loop(torch, f, n, a.steps, a.warmup)
+        out[name] = {"us": round(ms * 1e3, 3), "active_tiles": n_act, "tiles": rows // 64,
+                     "ledger_bytes": ledger, "GBs": round(ledger / (ms * 1e-3) / 1e9, 2)}
+        del wd, dd
+
+    words, dm = dg.lw_skip_pack(codes, 4, d, m)
+    nt = mat.rows // 64
+    leg(words, dm, 4, mat.rows, mat.cols, np.arange(nt, dtype=np.int32), x, "all_tiles")
+    leg(words, dm, 4, mat.rows, mat.cols, synth.active_tiles(nt, int(round(0.4 * nt)), 41), x, "active_40pct")
+    pc, pd, pm, px = synth.gen_fixed(1024, 4096, 2, 40)
+    pw, pdm = dg.lw_skip_pack(pc, 2, pd, pm)
+    pxd = torch.from_numpy(np.ascontiguousarray(px[:batch]).view(np.int16)).cuda()
+    leg(pw, pdm, 2, 1024, 4096, synth.active_tiles(16, 6, 41), pxd, "page_1024x4096_b2_6of16")
+    return out
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -288,6 +323,8 @@ def main():
         dms = time_graph(torch, dec_step, n_copies, nd, a.warmup) or time_loop(torch, dec_step, n_copies, nd, a.warmup)
         result["decode_only"] = {"us_per_matrix": round(dms * 1e3, 3),
                                  "symbols_per_s": (mat.rows * mat.cols // 2) / (dms * 1e-3)}
+    if not a.no_extras and kind == dg.LW_Q4_PAIR and len(mats) == 1 and batch <= 4:
+        result["skip_twin"] = skip_legs(torch, dg, synth, mat, codes, d, m, xs[0], batch, a)
     if not a.no_extras and len(mats) == 3 and mats[2].cols == mats[0].rows:
         # the whole MLP pass, chained: gate and up on x, SwiGLU to fp16 h,
         # down on h (each graph step depends on the one before it)

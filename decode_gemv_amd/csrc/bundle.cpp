@@ -808,3 +808,39 @@ extern "C" lw_status lw_twin_build(const uint8_t *codes, int bits, int64_t rows,
     if (bad) return lw_fail(LW_E_ARG, "code >= 16");
     return LW_OK;
 }
+
+/* Tile-transposed fixed-width packing ("Software-Defined Bandwidth
+ * Expansion", IV-A storage and IV-B layout): 32/bits codes per 32-bit word,
+ * the code of the lowest column in the lowest bits; word (t, j, r) holds
+ * columns [j*32/bits, (j+1)*32/bits) of row 64t + r and sits at index
+ * (t*WPR + j)*64 + r, WPR = cols*bits/32; scales at (t*(cols/256) + g)*64 + r. */
+extern "C" lw_status lw_skip_pack(const uint8_t *codes, int bits, int64_t rows, int64_t cols,
+                                  const uint16_t *d, const uint16_t *m, uint32_t *words, uint32_t *dm)
+{
+    if (!codes || !d || !m || !words || !dm) return lw_fail(LW_E_ARG, "null argument");
+    if (bits != 2 && bits != 4 && bits != 8) return lw_fail(LW_E_ARG, "bits must be 2, 4 or 8");
+    if (rows <= 0 || cols <= 0 || rows % 64 || cols % 256)
+        return lw_fail(LW_E_SHAPE, "rows must be a multiple of 64 and cols of 256");
+    const int per = 32 / bits;
+    const int64_t wpr = cols / per, ng = cols / 256;
+    const unsigned top = (1u << bits) - 1u;
+    std::atomic<int> bad(0);
+    parallel_for(rows, [&](int64_t r) {
+        const uint8_t *q = codes + r * cols;
+        const int64_t t = r >> 6, rr = r & 63;
+        uint32_t *wt = words + t * wpr * 64 + rr;
+        for (int64_t j = 0; j < wpr; j++) {
+            uint32_t w = 0;
+            for (int i = per - 1; i >= 0; i--) {
+                const uint8_t c = q[j * per + i];
+                if (c > top) bad = 1;
+                w = (w << bits) | (c & top);
+            }
+            wt[j * 64] = w;
+        }
+        uint32_t *dt = dm + t * ng * 64 + rr;
+        for (int64_t g = 0; g < ng; g++) dt[g * 64] = (uint32_t)d[r * ng + g] | ((uint32_t)m[r * ng + g] << 16);
+    });
+    if (bad) return lw_fail(LW_E_ARG, "code does not fit in the bit width");
+    return LW_OK;
+}

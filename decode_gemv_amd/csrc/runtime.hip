@@ -192,3 +192,28 @@ extern "C" lw_status lw_swiglu(const float *gate, const float *up, uint16_t *h, 
     if (e != hipSuccess) return hip_fail(e, "swiglu launch");
     return LW_OK;
 }
+
+extern "C" lw_status lw_skip_gemv(const uint32_t *words, const uint32_t *dm, int bits, int64_t rows, int64_t cols,
+                                  const int32_t *tiles, int64_t n_list, const void *x, float *y, int batch,
+                                  void *stream)
+{
+    if (n_list < 0) return lw_fail(LW_E_ARG, "negative list length");
+    if (n_list > 0x7FFFFFFF) return lw_fail(LW_E_ARG, "list longer than the grid allows");
+    if (bits != 2 && bits != 4 && bits != 8) return lw_fail(LW_E_ARG, "bits must be 2, 4 or 8");
+    if (rows <= 0 || cols <= 0 || rows % 64 || cols % 256)
+        return lw_fail(LW_E_SHAPE, "rows must be a multiple of 64 and cols of 256");
+    if (rows / 64 > 0x7FFFFFFF) return lw_fail(LW_E_SHAPE, "too many tiles");
+    if (batch < 1 || batch > 4) return lw_fail(LW_E_ARG, "batch must be in 1..4");
+    if (n_list == 0) return LW_OK;             // an empty launch list moves nothing and writes nothing
+    if (!words || !dm || !tiles || !x || !y) return lw_fail(LW_E_ARG, "null argument");
+    if (reinterpret_cast<uintptr_t>(words) % 16 || reinterpret_cast<uintptr_t>(dm) % 16 ||
+        reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 4 ||
+        reinterpret_cast<uintptr_t>(tiles) % 4)
+        return lw_fail(LW_E_ARG, "words, dm and x must be 16-byte aligned, y and tiles 4-byte aligned");
+    hipError_t e = lw_launch_skip(words, dm, bits, rows, cols, tiles, n_list, static_cast<const uint16_t *>(x), y,
+                                  batch, (hipStream_t)stream);
+    if (e == hipErrorNotSupported)
+        return lw_fail(LW_E_UNSUPPORTED, "staged activations (2 * cols * batch bytes) exceed the LDS");
+    if (e != hipSuccess) return hip_fail(e, "skip launch");
+    return LW_OK;
+}

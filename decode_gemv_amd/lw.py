@@ -65,6 +65,8 @@ def _load():
         "lw_decode_only": (st, [P, P, C.c_size_t, P, P]),
         "lw_twin_gemv": (st, [P, P, i32, i64, i64, P, P, i32, P]),
         "lw_swiglu": (st, [P, P, P, i64, P]),
+        "lw_skip_pack": (st, [P, i32, i64, i64, P, P, P, P]),
+        "lw_skip_gemv": (st, [P, P, i32, i64, i64, P, i64, P, P, i32, P]),
         "lw_status_str": (C.c_char_p, [st]),
         "lw_last_error": (C.c_char_p, []),
     }
@@ -179,6 +181,19 @@ def lw_twin_build(codes: np.ndarray, bits: int, d: np.ndarray, m: np.ndarray):
     return twin, dm
 
 
+def lw_skip_pack(codes: np.ndarray, bits: int, d: np.ndarray, m: np.ndarray):
+    """Tile-transposed words [(rows/64) * WPR * 64] and scales [(rows/64) * (cols/256) * 64]."""
+    rows, cols = codes.shape
+    codes, pc = _np(codes, np.uint8)
+    d, pd = _np(d, np.uint16)
+    m, pm = _np(m, np.uint16)
+    words = np.zeros(rows * cols * bits // 32, np.uint32)
+    dm = np.zeros(rows * (cols // 256), np.uint32)
+    _check(_L.lw_skip_pack(pc, bits, rows, cols, pd, pm, words.ctypes.data_as(C.c_void_p),
+                           dm.ctypes.data_as(C.c_void_p)))
+    return words, dm
+
+
 def lw_status_str(s: int) -> str:
     return _L.lw_status_str(s).decode()
 
@@ -236,6 +251,17 @@ def lw_decode_only(db: DevBundle, out, lane_bits=None, stream=None) -> None:
 def lw_twin_gemv(twin, dm, bits: int, rows: int, cols: int, x, y, batch: int, stream=None) -> None:
     _check(_L.lw_twin_gemv(_dptr(twin, "twin"), _dptr(dm, "dm"), bits, rows, cols, _dptr(x, "x"), _dptr(y, "y"),
                            batch, _stream(stream)))
+
+
+def lw_skip_gemv(words, dm, bits: int, rows: int, cols: int, tiles, x, y, batch: int, stream=None) -> None:
+    """y rows of the listed tiles (device int32 tensor) = W x; other rows untouched."""
+    n = tiles.numel()
+    tp = _dptr(tiles, "tiles") if n else None
+    wp = _dptr(words, "words") if n else None
+    dp = _dptr(dm, "dm") if n else None
+    xp = _dptr(x, "x") if n else None
+    yp = _dptr(y, "y") if n else None
+    _check(_L.lw_skip_gemv(wp, dp, bits, rows, cols, tp, n, xp, yp, batch, _stream(stream)))
 
 
 def lw_swiglu(gate, up, h, stream=None) -> None:

@@ -190,6 +190,42 @@ lw_status lw_decode_only(const lw_dev_bundle *db, void *out, size_t out_bytes, u
 lw_status lw_twin_gemv(const void *twin, const uint32_t *dm, int bits, int64_t rows, int64_t cols,
                        const void *x, float *y, int batch, void *stream);
 
+/* Tile-transposed fixed-width packing for lw_skip_gemv ("Software-Defined
+ * Bandwidth Expansion", IV-A storage: floor(32/b) b-bit codes per 32-bit word,
+ * b in {2, 4, 8}, the lowest column in the lowest bits, so b = 3 and other
+ * widths that waste word bits are not admitted; IV-B layout: words stored
+ * neuron-contiguous, then tile-transposed to [n_tiles][WPR][B_N] with
+ * B_N = 64 rows per tile and WPR = cols / (32/b) word columns).
+ *   codes : host [rows][cols], one code per byte, each < 2^bits
+ *   d, m  : host fp16 bits [rows][cols/256], w = d*q - m per 256 columns
+ *   words : host out, rows*cols*bits/32 u32: word (t, j, r) at (t*WPR + j)*64 + r
+ *   dm    : host out, rows*cols/256 u32 = d | m << 16 at (t*(cols/256) + g)*64 + r
+ * Errors: LW_E_ARG (null, bits not 2/4/8, a code too wide), LW_E_SHAPE
+ * (rows not a multiple of 64 or cols of 256). */
+lw_status lw_skip_pack(const uint8_t *codes, int bits, int64_t rows, int64_t cols, const uint16_t *d,
+                       const uint16_t *m, uint32_t *words, uint32_t *dm);
+
+/* Tile-skipping fixed-width GEMV over a launch list ("Software-Defined
+ * Bandwidth Expansion", IV-C: one program per active tile loads the packed
+ * words, unpacks them in registers, applies scale and zero and accumulates
+ * the product with x in one pass; an inactive tile is absent from the launch
+ * grid, so it moves no weight bytes: n_active * WPR * 64 words are read).
+ *   words, dm : device, as produced by lw_skip_pack (16-byte aligned)
+ *   tiles     : device int32 [n_list], the launch list: tile t covers rows
+ *               64t .. 64t+63; an entry outside 0 .. rows/64 - 1 names no
+ *               tile and is skipped; a repeated entry writes the same rows
+ *               again with the same values
+ *   x         : device fp16 [batch][cols], 16-byte aligned
+ *   y         : device fp32 [batch][rows]; only the rows of listed tiles are
+ *               written, every other row keeps its contents
+ *   1 <= batch <= 4 (four rows and four batch rows of partial sums stay in
+ *   registers per thread); n_list = 0 enqueues nothing (pointers may then be null)
+ * Each workgroup stages x in LDS: 2 * cols * batch bytes must fit in the
+ * device's LDS per workgroup (LW_E_UNSUPPORTED otherwise).
+ * Errors: LW_E_ARG, LW_E_SHAPE, LW_E_UNSUPPORTED, LW_E_DEVICE. */
+lw_status lw_skip_gemv(const uint32_t *words, const uint32_t *dm, int bits, int64_t rows, int64_t cols,
+                       const int32_t *tiles, int64_t n_list, const void *x, float *y, int batch, void *stream);
+
 /* SwiGLU activation between the coded gate/up projections and the coded down
  * projection of an MLP ("Unweight", section "Overlapping Work Across
  * Transformer Layers": the down projection consumes gate, activation and up;

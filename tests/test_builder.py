@@ -181,3 +181,35 @@ def test_corrupt_images_rejected(what):
     with pytest.raises(dg.LwError) as e:
         dg.lw_bundle_load(img)
     assert e.value.status == expect, (what, e.value)
+
+
+# ------------------------------------------------------------------ tile-skipping fixed-width twin
+
+@pytest.mark.parametrize("bits,rows,cols,seed", [(2, 128, 512, 61), (4, 192, 768, 62), (8, 64, 1280, 63),
+                                                 (4, 320, 2304, 64)])
+def test_skip_pack_matches_oracle_bytes(bits, rows, cols, seed):
+    """The product packer and the oracle write the same tile-transposed words and scales."""
+    codes, d, m, _ = synth.gen_fixed(rows, cols, bits, seed)
+    w, dm = dg.lw_skip_pack(codes, bits, d, m)
+    ow, odm = O.skip_pack(codes, bits, d, m)
+    assert np.array_equal(w, ow) and np.array_equal(dm, odm)
+
+
+def test_skip_argument_rules():
+    from decode_gemv_amd import lw
+    codes, d, m, _ = synth.gen_fixed(64, 256, 4, 65)
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_skip_pack(codes, 3, d, m)
+    assert e.value.status == dg.LW_E_ARG
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_skip_pack(np.full((64, 256), 4, np.uint8), 2, d, m)       # 4 does not fit in 2 bits
+    assert e.value.status == dg.LW_E_ARG
+    # host-side checks of lw_skip_gemv: each returns before any HIP call
+    f = lw._L.lw_skip_gemv
+    assert f(None, None, 4, 64, 256, None, 0, None, None, 1, None) == dg.LW_OK       # empty list
+    assert f(None, None, 4, 64, 256, None, -1, None, None, 1, None) == dg.LW_E_ARG
+    assert f(None, None, 3, 64, 256, None, 1, None, None, 1, None) == dg.LW_E_ARG
+    assert f(None, None, 4, 65, 256, None, 1, None, None, 1, None) == dg.LW_E_SHAPE
+    assert f(None, None, 4, 64, 200, None, 1, None, None, 1, None) == dg.LW_E_SHAPE
+    assert f(None, None, 4, 64, 256, None, 1, None, None, 5, None) == dg.LW_E_ARG
+    assert f(None, None, 4, 64, 256, None, 1, None, None, 1, None) == dg.LW_E_ARG     # null pointers
