@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(KArgs a)
 
     // issue every load, tile offsets first; table barrier; own tile and x (as in fused_q.hip)
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-    const LwTabRegs tr = lw_tab_fetch(a.tab, a.min_len, a.max_len, false);
+    const LwTabRegs tr = lw_tab_fetch<lw_compact<N16>()>(a, false);
     const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
     uint32_t xv[BATCH][2];
     const uint32_t *xg = reinterpret_cast<const uint32_t *>(a.x) + (size_t)(c.active ? c.cb : 0) * 128;
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(KArgs a)
     lw_load_sm(ring[0], smrow, 0);
     LwTileRegs64 tile;
     lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    lw_tab_put(lds, tr, a.min_len, a.max_len);
+    lw_tab_put<lw_compact<N16>()>(lds, tr, a);
     __syncthreads();                      // the decoder table is complete
 #pragma unroll
     for (int b = 0; b < BATCH; b++) {
@@ -231,13 +231,13 @@ __global__ __launch_bounds__(256) void k_decode_bf16(KArgs a)
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
     const uint32_t *smrow = a.sm + (size_t)c.t * 4096 + (size_t)c.half * 64 * 32 + c.l;
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-    const LwTabRegs tr = lw_tab_fetch(a.tab, a.min_len, a.max_len, false);
+    const LwTabRegs tr = lw_tab_fetch<lw_compact<N16>()>(a, false);
     const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
     uint32_t ring[2][CHUNK];
     lw_load_sm(ring[0], smrow, 0);
     LwTileRegs64 tile;
     lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    lw_tab_put(lds, tr, a.min_len, a.max_len);
+    lw_tab_put<lw_compact<N16>()>(lds, tr, a);
     __syncthreads();
     if (!c.active) return;
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
@@ -333,6 +333,7 @@ hipError_t gemv_batch(const KArgs &a, int batch, hipStream_t s)
 
 hipError_t lw_launch_gemv_bf16(const KArgs &a, SadPlan p, int batch, hipStream_t s)
 {
+    if (p.compact) return gemv_batch<1, LW_N16_COMPACT>(a, batch, s);
     switch (p.n8ops * 2 + p.n16ops) {
     case 0: return gemv_batch<0, 0>(a, batch, s);
     case 1: return gemv_batch<0, 1>(a, batch, s);
@@ -346,6 +347,7 @@ hipError_t lw_launch_gemv_bf16(const KArgs &a, SadPlan p, int batch, hipStream_t
 
 hipError_t lw_launch_decode_bf16(const KArgs &a, SadPlan p, hipStream_t s)
 {
+    if (p.compact) return launch_decode<1, LW_N16_COMPACT>(a, s);
     switch (p.n8ops * 2 + p.n16ops) {
     case 0: return launch_decode<0, 0>(a, s);
     case 1: return launch_decode<0, 1>(a, s);

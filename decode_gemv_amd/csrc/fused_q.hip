@@ -83,7 +83,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
     // stores its own tile and activations and starts decoding as soon as its
     // own data is in (a wavefront's LDS operations complete in order).
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-    const LwTabRegs tr = lw_tab_fetch(a.tab, a.min_len, a.max_len, false);
+    const LwTabRegs tr = lw_tab_fetch<lw_compact<N16>()>(a, false);
     const uint32_t dm = a.dm[(size_t)c.t * 64 + 2 * c.l + c.half];   // (d, m) of this lane's tile row
     const uint32_t split = a.split[(size_t)c.t * 32 + c.l];          // second-row start
     uint32_t xv[BATCH][2];
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
     }
     LwTileRegs64 tile;
     lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    lw_tab_put(lds, tr, a.min_len, a.max_len);
+    lw_tab_put<lw_compact<N16>()>(lds, tr, a);
     __syncthreads();                      // the decoder table is complete
 #pragma unroll
     for (int b = 0; b < BATCH; b++) {
@@ -190,11 +190,11 @@ __global__ __launch_bounds__(256) void k_decode_q(KArgs a)
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
     // issue, then store (as in k_gemv_q)
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-    const LwTabRegs tr = lw_tab_fetch(a.tab, a.min_len, a.max_len, true);
+    const LwTabRegs tr = lw_tab_fetch<lw_compact<N16>()>(a, true);
     const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
     LwTileRegs64 tile;
     lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    lw_tab_put(lds, tr, a.min_len, a.max_len);
+    lw_tab_put<lw_compact<N16>()>(lds, tr, a);
     __syncthreads();
     if (!c.active) return;
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
@@ -290,6 +290,7 @@ hipError_t gemv_batch(const KArgs &a, int batch, hipStream_t s)
 template <int KIND>
 hipError_t gemv_plan(const KArgs &a, SadPlan p, int batch, hipStream_t s)
 {
+    if (p.compact) return gemv_batch<KIND, 1, LW_N16_COMPACT>(a, batch, s);
     const int code = p.n8ops * 2 + p.n16ops;
     switch (code) {
     case 0: return gemv_batch<KIND, 0, 0>(a, batch, s);
@@ -305,6 +306,7 @@ hipError_t gemv_plan(const KArgs &a, SadPlan p, int batch, hipStream_t s)
 template <int KIND>
 hipError_t decode_plan(const KArgs &a, SadPlan p, hipStream_t s)
 {
+    if (p.compact) return launch_decode_q<KIND, 1, LW_N16_COMPACT>(a, s);
     const int code = p.n8ops * 2 + p.n16ops;
     switch (code) {
     case 0: return launch_decode_q<KIND, 0, 0>(a, s);

@@ -35,12 +35,22 @@ struct KArgs {
     uint32_t c8[2], c8m1[2];     // limit/8 and limit/8 - 1 per byte, 0 in unused bytes
     uint32_t c16, c16m1;         // limit*32 and limit*32 - 1 per half, 0 in unused halves
     uint32_t sad_k;              // accumulator offset: PBASE - 2*min_len - (number of comparisons)
+    // Compact tables (at most four code lengths, the three shorter <= 8): the
+    // comparison count r indexes the used lengths; lut_hi:lut_lo hold
+    // 64 - length(r) at byte 6 - 2r, cbase[r] = offset - first of length(r)
+    uint32_t lut_lo, lut_hi;
+    int32_t cbase[4];
+    int32_t ncmp;                // comparisons (used lengths - 1)
 };
 
-// SAD comparison layout of a bundle: byte-lane ops (0..2) and 16-bit ops (0..1)
+// SAD comparison layout of a bundle: byte-lane ops (0..2) and 16-bit ops
+// (0..1); compact tables use one byte-lane op and the count-indexed tables
+// (kernels instantiate them with N16 == LW_N16_COMPACT)
 struct SadPlan {
     int n8ops, n16ops;
+    bool compact;
 };
+#define LW_N16_COMPACT 2
 SadPlan lw_sad_plan(const lw_table &t, int min_len, int max_len, KArgs &a);
 
 // LDS bytes a fused/decode kernel needs per workgroup

@@ -28,6 +28,15 @@
 //     code = hi >> s,  window <<= len  ==  alignbit(hi, lo, s), alignbit(lo, 0, s).
 // Bits past a lane's last code are don't-care (prefix property); the slots
 // bound every read of a valid stream.
+//
+// Compact tables (at most four code lengths, the three shorter <= 8: what
+// the builder makes).  One v_sad_u8 pair compares the top 8 peek bits with
+// the three limits, and the accumulator makes A = CBASE - 2r for r limits
+// passed: the LDS address of the base entry of the r-th used length, whose
+// low byte 6 - 2r also selects, through v_perm_b32, the byte 64 - length(r)
+// of a four-entry table held in two SGPRs -- the shift s, whose low five
+// bits are 32 - len and low six bits 64 - len.  The perm's upper bytes are
+// don't-care, so the consumed bits of a group are taken modulo 64.
 #ifndef LW_LANE_DECODE_HPP
 #define LW_LANE_DECODE_HPP
 
@@ -85,6 +94,7 @@ inline hipError_t lw_allow_lds()
 #define LW_TPAY 1024u        // payload per canonical index, u32[256]
 #define LW_TPAY_HI 2048u     // second payload, u32[256]
 #define LW_TAB_BYTES 3072u
+#define LW_CBASE 774u        // compact tables: base entry of count r at CBASE - 2r (low byte 6 - 2r)
 
 LW_DEV uint32_t lw_wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
@@ -132,28 +142,44 @@ struct LwTabRegs {
     int32_t ent;
 };
 
+// N16 value of the kernels' compact-table instantiations
+template <int N16>
+constexpr bool lw_compact() { return N16 == LW_N16_COMPACT; }
+
 // thread tid (< 256) fetches payload entry tid of both tables and length
-// entry min(tid, max_len - min_len).  Loads and stores are unconditional: a
-// load the compiler sinks into a divergent branch is waited on together
-// with every load issued before it.
-LW_DEV LwTabRegs lw_tab_fetch(const lw_gputab *g, int min_len, int max_len, bool symval_second)
+// entry min(tid, max_len - min_len) (compact tables: the base of count
+// min(tid, ncmp), from the kernel arguments).  Loads and stores are
+// unconditional: a load the compiler sinks into a divergent branch is
+// waited on together with every load issued before it.
+template <bool CMP>
+LW_DEV LwTabRegs lw_tab_fetch(const KArgs &a, bool symval_second)
 {
     LwTabRegs r;
     const int tid = threadIdx.x;
+    const lw_gputab *g = a.tab;
     r.pay = g->payload[tid & 255];
     r.pay2 = symval_second ? g->symval[tid & 255] : g->payload_hi[tid & 255];
-    r.ent = g->base[min(tid, max_len - min_len)];   // threads past the last entry repeat it
+    if constexpr (CMP) {
+        const int i = min(tid, a.ncmp);
+        r.ent = i == 0 ? a.cbase[0] : i == 1 ? a.cbase[1] : i == 2 ? a.cbase[2] : a.cbase[3];
+    } else {
+        r.ent = g->base[min(tid, a.max_len - a.min_len)];   // threads past the last entry repeat it
+    }
     return r;
 }
 
-LW_DEV void lw_tab_put(uint8_t *lds, const LwTabRegs &r, int min_len, int max_len)
+template <bool CMP>
+LW_DEV void lw_tab_put(uint8_t *lds, const LwTabRegs &r, const KArgs &a)
 {
     const uint32_t lb = (uint32_t)(size_t)lds;
     const int tid = threadIdx.x;          // workgroups have 256 threads: one entry each, unconditionally
     *(lw_lds_w32 *)(size_t)(lb + LW_TPAY + 4u * (tid & 255)) = r.pay;
     *(lw_lds_w32 *)(size_t)(lb + LW_TPAY_HI + 4u * (tid & 255)) = r.pay2;
-    const int len = min_len + min(tid, max_len - min_len);   // repeated stores write the same value
-    *(lw_lds_w16 *)(size_t)(lb + LW_PBASE - 2u * len) = (int16_t)((int32_t)lb + (int32_t)LW_TPAY + 4 * r.ent);
+    const int16_t v = (int16_t)((int32_t)lb + (int32_t)LW_TPAY + 4 * r.ent);   // repeated stores write the same value
+    if constexpr (CMP)
+        *(lw_lds_w16 *)(size_t)(lb + LW_CBASE - 2u * (uint32_t)min(tid, a.ncmp)) = v;
+    else
+        *(lw_lds_w16 *)(size_t)(lb + LW_PBASE - 2u * (uint32_t)(a.min_len + min(tid, a.max_len - a.min_len))) = v;
 }
 
 // A wavefront stages one tile: lw_tile_fetch64 loads the first 64 word rows
@@ -204,9 +230,9 @@ template <int N8, int N16>
 LW_DEV uint32_t lw_sad_count(uint32_t hi, uint32_t k, const KArgs &a)
 {
     const uint32_t p8 = __builtin_amdgcn_perm(hi, hi, 0x03030303u);
-    const uint32_t p16 = __builtin_amdgcn_perm(hi, hi, 0x03020302u);
     uint32_t s1 = 0, s2 = k;
-    if constexpr (N16 > 0) {
+    if constexpr (N16 == 1) {
+        const uint32_t p16 = __builtin_amdgcn_perm(hi, hi, 0x03020302u);
         s1 = __builtin_amdgcn_sad_u16(p16, a.c16m1, s1);
         s2 = __builtin_amdgcn_sad_u16(p16, a.c16, s2);
     }
@@ -236,6 +262,7 @@ template <int N8, int N16, int NG, class Aux, bool UNROLL_ALL = false, class Pay
 LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetch fetch, Use use)
 {
     static_assert(NG % 2 == 0 && NG >= 4, "groups must be even");
+    constexpr bool CMP = lw_compact<N16>();
     uint32_t wa, wb, wc;
     uint32_t code[2][4], A[2][4], base[2][4], pay[2][4];
     Aux aux[2];
@@ -259,12 +286,15 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
         for (int j = 0; j < 4; j++) {
             const uint32_t peek = j == 0 ? (uint32_t)(win >> 32) : (uint32_t)((win << (o & 63u)) >> 32);
             const uint32_t Aj = lw_sad_count<N8, N16>(peek, d.k, a);
-            const uint32_t s = Aj >> 1;
+            const uint32_t s = CMP ? __builtin_amdgcn_perm(a.lut_hi, a.lut_lo, Aj) : Aj >> 1;
             A[q][j] = Aj;
             code[q][j] = peek >> (s & 31u);
             o -= s;
         }
-        d.u += o + d.ubias;               // u + sum(len)
+        if constexpr (CMP)
+            d.u += o & 63u;               // sum(len) < 64; the perm's upper bytes are don't-care
+        else
+            d.u += o + d.ubias;           // u + sum(len)
     };
     auto issue_payloads = [&](int q, int g) {
 #pragma unroll
@@ -327,9 +357,10 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
 }
 
 // Set up a lane's decoder on its staged tile.  Returns false (the kernel must
-// then produce nothing) if the LDS base is not 128-byte aligned: the shift
+// then produce nothing) if the LDS base is not 256-byte aligned: the shift
 // amounts s = A >> 1 then carry a bias lb/2 + PBASE/2 that is a multiple of
-// 64, which both the 32-bit shifts and the 64-bit window offset need.
+// 64, which both the 32-bit shifts and the 64-bit window offset need, and
+// the low byte of a compact table's A is the byte-table selector.
 LW_DEV bool lw_lane_init(LaneDec &d, uint8_t *lds, const uint32_t *slots, int l, const KArgs &a)
 {
     const uint32_t lb = (uint32_t)(size_t)lds;
@@ -337,7 +368,7 @@ LW_DEV bool lw_lane_init(LaneDec &d, uint8_t *lds, const uint32_t *slots, int l,
     d.u = 31;
     d.k = a.sad_k + lb;
     d.ubias = 4u * (lb / 2u + LW_PBASE / 2u);
-    return (lb & 127u) == 0;
+    return (lb & 255u) == 0;
 }
 
 // Sum the per-wave partials of the workgroup's ROWS rows (red[wave][b][row])

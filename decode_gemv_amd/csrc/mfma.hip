@@ -111,11 +111,11 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
 
     // issue every load, tile offsets first; table barrier; own tile (as in fused_q.hip)
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-    const LwTabRegs tr = lw_tab_fetch(a.tab, a.min_len, a.max_len, false);
+    const LwTabRegs tr = lw_tab_fetch<lw_compact<N16>()>(a, false);
     const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
     LwTileRegs64 tile;
     lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    lw_tab_put(lds, tr, a.min_len, a.max_len);
+    lw_tab_put<lw_compact<N16>()>(lds, tr, a);
     __syncthreads();                      // the decoder table is complete
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
 
@@ -293,6 +293,7 @@ hipError_t launch(const KArgs &a, hipStream_t s)
 template <int KIND>
 hipError_t by_plan(const KArgs &a, SadPlan p, hipStream_t s)
 {
+    if (p.compact) return launch<KIND, 1, LW_N16_COMPACT>(a, s);
     switch (p.n8ops * 2 + p.n16ops) {
     case 0: return launch<KIND, 0, 0>(a, s);
     case 1: return launch<KIND, 0, 1>(a, s);

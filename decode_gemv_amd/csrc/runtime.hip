@@ -84,19 +84,51 @@ static KArgs make_args(const lw_dev_bundle *db)
     return a;
 }
 
-// Limit comparisons of lengths min_len .. max_len-1, packed for the SAD
-// counting of lane_decode.hpp: lengths <= 8 in byte lanes (top 8 peek bits
-// against limit/8), lengths 9 and 10 in 16-bit lanes (top 16 window bits
-// against limit*32).  Unused lanes compare 0 with 0 and contribute nothing.
+// Limit comparisons packed for the SAD counting of lane_decode.hpp.
+// Compact tables (at most four used lengths, the three shorter <= 8, as the
+// builder makes them): the limits of the used lengths but the longest, in
+// byte lanes (top 8 peek bits against limit/8), the count indexing the used
+// lengths.  Other tables: every length min_len .. max_len-1, lengths <= 8 in
+// byte lanes, 9 and 10 in 16-bit lanes (top 16 window bits against
+// limit*32), the count giving the length as min_len + count.  Unused lanes
+// compare 0 with 0 and contribute nothing.
 SadPlan lw_sad_plan(const lw_table &t, int min_len, int max_len, KArgs &a)
 {
+    SadPlan p;
+    a.c8[0] = a.c8[1] = a.c8m1[0] = a.c8m1[1] = 0;
+    a.c16 = a.c16m1 = 0;
+    a.lut_lo = a.lut_hi = 0;
+    a.cbase[0] = a.cbase[1] = a.cbase[2] = a.cbase[3] = 0;
+    a.ncmp = 0;
+    int used[LW_MAXLEN + 1], nu = 0;
+    for (int L = 1; L <= LW_MAXLEN; L++)
+        if (t.count[L]) used[nu++] = L;
+    if (nu >= 1 && nu <= 4 && (nu == 1 || used[nu - 2] <= 8)) {
+        uint64_t lut = 0;
+        for (int r = 0; r < nu; r++) {
+            const int L = used[r];
+            lut |= (uint64_t)(64 - L) << (8 * (6 - 2 * r));
+            a.cbase[r] = (int32_t)t.offset[L] - (int32_t)t.first[L];
+            if (r < nu - 1) {
+                const uint32_t c = (uint32_t)t.limit[L] >> 3;
+                a.c8[0] |= c << (8 * r);
+                a.c8m1[0] |= (c - 1) << (8 * r);
+            }
+        }
+        a.lut_lo = (uint32_t)lut;
+        a.lut_hi = (uint32_t)(lut >> 32);
+        a.ncmp = nu - 1;
+        a.sad_k = LW_CBASE - (uint32_t)(nu - 1);
+        p.n8ops = 1;
+        p.n16ops = 0;
+        p.compact = true;
+        return p;
+    }
     int l8[8], l16[2], n8 = 0, n16 = 0;
     for (int L = min_len; L < max_len; L++) {
         if (L <= 8) l8[n8++] = L;
         else l16[n16++] = L;
     }
-    a.c8[0] = a.c8[1] = a.c8m1[0] = a.c8m1[1] = 0;
-    a.c16 = a.c16m1 = 0;
     for (int i = 0; i < n8; i++) {
         const uint32_t c = (uint32_t)t.limit[l8[i]] >> 3;
         a.c8[i / 4] |= c << (8 * (i % 4));
@@ -108,9 +140,9 @@ SadPlan lw_sad_plan(const lw_table &t, int min_len, int max_len, KArgs &a)
         a.c16m1 |= (c - 1) << (16 * i);
     }
     a.sad_k = LW_PBASE - 2u * (uint32_t)min_len - (uint32_t)(max_len - min_len);
-    SadPlan p;
     p.n8ops = (n8 + 3) / 4;
     p.n16ops = n16 > 0 ? 1 : 0;
+    p.compact = false;
     return p;
 }
 
@@ -198,7 +230,7 @@ extern "C" lw_status lw_skip_gemv(const uint32_t *words, const uint32_t *dm, int
                                   void *stream)
 {
     if (n_list < 0) return lw_fail(LW_E_ARG, "negative list length");
-    if (n_list > 0x7FFFFFFF) return lw_fail(LW_E_ARG, "list longer than the grid allows");
+    if (n_list > 0x3FFFFFFF) return lw_fail(LW_E_ARG, "list longer than the grid allows");
     if (bits != 2 && bits != 4 && bits != 8) return lw_fail(LW_E_ARG, "bits must be 2, 4 or 8");
     if (rows <= 0 || cols <= 0 || rows % 64 || cols % 256)
         return lw_fail(LW_E_SHAPE, "rows must be a multiple of 64 and cols of 256");

@@ -6,13 +6,13 @@
 // scale and zero, and the product with x in one pass, and a skipped tile is
 // absent from the grid, so it moves no weight bytes).
 //
-// Work split.  One workgroup per list entry, 16 * JT threads.  Thread
-// (rq, jl) = (tid % 16, tid / 16) owns rows 4rq .. 4rq+3 of the tile and the
-// chunks jl, jl + JT, ... of eight consecutive word columns; for a fixed word
-// column the 64 rows' words are contiguous, so one 16-byte load per lane
-// brings four rows' words and the 16 lanes of a row quad cover 256
-// contiguous bytes.  A chunk's columns lie inside one 256-column group, so
-// one 16-byte load of scales serves it.
+// Work split.  Each list entry gets two workgroups, one per 32-row half of
+// its tile, of 8 * JT threads.  Thread (rq, jl) = (tid % 8, tid / 8) owns
+// rows 4rq .. 4rq+3 of the half and the chunks jl, jl + JT, ... of eight
+// consecutive word columns; for a fixed word column the half's 32 words are
+// contiguous, so one 16-byte load per lane brings four rows' words and the 8
+// lanes of a word column read one whole 128-byte line.  A chunk's columns
+// lie inside one 256-column group, so one 16-byte load of scales serves it.
 //
 // Activations.  Each workgroup stages x in LDS once, already arranged as the
 // half2 pairs the unpack produces (below), and the sum of x over each chunk
@@ -37,6 +37,9 @@ struct SkipGeom {
     static constexpr int PER = 32 / BITS;            // codes per word
     static constexpr int CC = SK_CW * PER;           // columns per chunk
     static constexpr int XU = PER / 2;               // x pairs per word
+    // dwords per chunk of staged pairs: the chunk's 8 words plus 4 of padding,
+    // so the 8 chunks a wavefront reads at once start 4 banks apart
+    static constexpr int XCS = SK_CW * XU + 4;
 };
 
 struct SkipArgs {
@@ -49,6 +52,8 @@ struct SkipArgs {
     int32_t n_tiles, n_jc, jt;
 };
 
+constexpr int SK_RW = 32;      // rows per workgroup (half a tile)
+
 struct SkipLds {
     uint32_t xs, sxs, total;
 };
@@ -58,8 +63,8 @@ struct SkipLds {
 __host__ __device__ inline SkipLds skip_lds(int batch, int64_t cols, int n_jc, int jt)
 {
     SkipLds L;
-    const uint32_t xbytes = (uint32_t)(batch * cols * 2);
-    const uint32_t red = (uint32_t)((jt / 4) * batch * SK_BN * 4);
+    const uint32_t xbytes = (uint32_t)(batch * cols * 2 + batch * n_jc * 16);
+    const uint32_t red = (uint32_t)((jt / 8) * batch * SK_RW * 4);
     L.xs = 0;
     L.sxs = xbytes > red ? xbytes : red;
     L.total = L.sxs + (uint32_t)(batch * n_jc * 4);
@@ -117,15 +122,17 @@ struct Chunk {
     lw_u32x4 dm;             // (d, m) of the four rows for the chunk's group
 };
 
-LW_DEV void load_chunk(const SkipArgs &a, int t, int jc, int rq, int cc, Chunk &c)
+// r0: the first of the lane's four rows within the tile
+LW_DEV void load_chunk(const SkipArgs &a, int t, int jc, int r0, int cc, Chunk &c)
 {
     const int64_t wpr = (int64_t)a.n_jc * SK_CW;
-    const lw_u32x4 *src = reinterpret_cast<const lw_u32x4 *>(a.words + ((int64_t)t * wpr + (int64_t)jc * SK_CW) * SK_BN) + rq;
+    const lw_u32x4 *src =
+        reinterpret_cast<const lw_u32x4 *>(a.words + ((int64_t)t * wpr + (int64_t)jc * SK_CW) * SK_BN + r0);
 #pragma unroll
     for (int i = 0; i < SK_CW; i++) c.w[i] = src[i * (SK_BN / 4)];
     const int64_t ng = a.cols / 256;
     const int64_t g = (int64_t)jc * cc / 256;
-    c.dm = reinterpret_cast<const lw_u32x4 *>(a.dm + ((int64_t)t * ng + g) * SK_BN)[rq];
+    c.dm = *reinterpret_cast<const lw_u32x4 *>(a.dm + ((int64_t)t * ng + g) * SK_BN + r0);
 }
 
 template <int BITS, int BATCH>
@@ -133,10 +140,12 @@ __global__ __launch_bounds__(1024) void k_skip(SkipArgs a)
 {
     using G = SkipGeom<BITS>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int t = a.tiles[blockIdx.x];
+    const int t = a.tiles[blockIdx.x >> 1];
     if (t < 0 || t >= a.n_tiles) return;                 // names no tile: the whole workgroup leaves
+    const int half = blockIdx.x & 1;
     const int tid = threadIdx.x, nt = blockDim.x;
-    const int rq = tid & 15, jl = tid >> 4;
+    const int rq = tid & 7, jl = tid >> 3;
+    const int r0 = half * SK_RW + 4 * rq;                // the lane's first row within the tile
     const int n_jc = a.n_jc, JT = a.jt;
     const int n_it = (n_jc + JT - 1) / JT;
     const SkipLds L = skip_lds(BATCH, a.cols, n_jc, JT);
@@ -144,27 +153,38 @@ __global__ __launch_bounds__(1024) void k_skip(SkipArgs a)
 
     // the first chunk's words and scales are in flight while x is staged
     Chunk c;
-    load_chunk(a, t, min(jl, n_jc - 1), rq, G::CC, c);
+    load_chunk(a, t, min(jl, n_jc - 1), r0, G::CC, c);
 
-    // stage x: item (b, jc) arranges the chunk's 8 words of activations and sums them
+    // stage x: item (b, j) arranges word column j's activations of batch row
+    // b; the 8 items of a chunk sit in 8 aligned consecutive lanes, which sum
+    // the chunk's activations by shuffles (the item count is a multiple of 8)
     const int wpc = a.n_jc * SK_CW;                      // word columns of the matrix
-    for (int item = tid; item < BATCH * n_jc; item += nt) {
-        const int b = item / n_jc, jc = item % n_jc;
-        const uint32_t *xg = reinterpret_cast<const uint32_t *>(a.x + (int64_t)b * a.cols + (int64_t)jc * G::CC);
+    for (int item = tid; item < BATCH * wpc; item += nt) {
+        const int b = item / wpc, j = item % wpc;
+        const uint32_t *xg = reinterpret_cast<const uint32_t *>(a.x + (int64_t)b * a.cols) + (int64_t)j * G::XU;
+        uint32_t X[G::XU], P[G::XU];
+        if constexpr (G::XU == 2) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(xg);
+            X[0] = v.x; X[1] = v.y;
+        } else {
+#pragma unroll
+            for (int k = 0; k < G::XU; k += 4) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(xg + k);
+                X[k] = v.x; X[k + 1] = v.y; X[k + 2] = v.z; X[k + 3] = v.w;
+            }
+        }
         float s = 0.f;
 #pragma unroll
-        for (int i = 0; i < SK_CW; i++) {
-            uint32_t X[G::XU], P[G::XU];
+        for (int k = 0; k < G::XU; k++) s = lw_dot2(X[k], 0x3C003C00u, s);          // times half2(1, 1)
+        arrange_pairs<BITS>(X, P);
+        const uint32_t ad = lb + L.xs + 4u * (uint32_t)((b * n_jc + j / SK_CW) * G::XCS + (j % SK_CW) * G::XU);
 #pragma unroll
-            for (int k = 0; k < G::XU; k++) X[k] = xg[i * G::XU + k];
-#pragma unroll
-            for (int k = 0; k < G::XU; k++) s = lw_dot2(X[k], 0x3C003C00u, s);     // times half2(1, 1)
-            arrange_pairs<BITS>(X, P);
-            const uint32_t ad = lb + L.xs + 4u * (uint32_t)(((b * wpc) + jc * SK_CW + i) * G::XU);
-#pragma unroll
-            for (int k = 0; k < G::XU; k++) *(lw_lds_w32 *)(size_t)(ad + 4u * k) = P[k];
-        }
-        *(lw_lds_w32 *)(size_t)(lb + L.sxs + 4u * (uint32_t)(b * n_jc + jc)) = __builtin_bit_cast(uint32_t, s);
+        for (int k = 0; k < G::XU; k++) *(lw_lds_w32 *)(size_t)(ad + 4u * k) = P[k];
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        s += __shfl_xor(s, 4, 64);
+        if ((j & 7) == 0)
+            *(lw_lds_w32 *)(size_t)(lb + L.sxs + 4u * (uint32_t)(b * n_jc + j / SK_CW)) = __builtin_bit_cast(uint32_t, s);
     }
     __syncthreads();
 
@@ -185,7 +205,7 @@ __global__ __launch_bounds__(1024) void k_skip(SkipArgs a)
 #pragma unroll
             for (int b = 0; b < BATCH; b++) {
                 uint32_t xp[G::XU];
-                const uint32_t ad = lb + L.xs + 4u * (uint32_t)(((b * wpc) + jc * SK_CW + i) * G::XU);
+                const uint32_t ad = lb + L.xs + 4u * (uint32_t)((b * n_jc + jc) * G::XCS + i * G::XU);
                 if constexpr (G::XU == 8) {
                     const lw_u32x4 u = *(__attribute__((address_space(3))) const lw_u32x4 *)(size_t)ad;
                     const lw_u32x4 v = *(__attribute__((address_space(3))) const lw_u32x4 *)(size_t)(ad + 16);
@@ -222,16 +242,17 @@ __global__ __launch_bounds__(1024) void k_skip(SkipArgs a)
     // the other workgroups' waves on the compute unit cover the reload latency
     for (int it = 0; it < n_it; it++) {
         const int jc = jl + it * JT;
-        if (it > 0) load_chunk(a, t, min(jc, n_jc - 1), rq, G::CC, c);
+        if (it > 0) load_chunk(a, t, min(jc, n_jc - 1), r0, G::CC, c);
         if (jc < n_jc) compute(jc);
     }
 
-    // rows: sum over the wave's four chunk lanes, then over the waves in LDS
+    // rows: sum over the wave's eight chunk lanes, then over the waves in LDS
 #pragma unroll
     for (int r = 0; r < 4; r++)
 #pragma unroll
         for (int b = 0; b < BATCH; b++) {
             float v = acc[r][b];
+            v += __shfl_xor(v, 8, 64);
             v += __shfl_xor(v, 16, 64);
             v += __shfl_xor(v, 32, 64);
             acc[r][b] = v;
@@ -239,19 +260,19 @@ __global__ __launch_bounds__(1024) void k_skip(SkipArgs a)
     __syncthreads();                                      // x no longer read: its space holds the partials
     const int wave = tid >> 6, lane = tid & 63;
     float *red = reinterpret_cast<float *>(lds + L.xs);
-    if (lane < 16) {
+    if (lane < 8) {
 #pragma unroll
         for (int r = 0; r < 4; r++)
 #pragma unroll
-            for (int b = 0; b < BATCH; b++) red[(wave * BATCH + b) * SK_BN + 4 * rq + r] = acc[r][b];
+            for (int b = 0; b < BATCH; b++) red[(wave * BATCH + b) * SK_RW + 4 * rq + r] = acc[r][b];
     }
     __syncthreads();
     const int waves = nt >> 6;
-    for (int i = tid; i < BATCH * SK_BN; i += nt) {
-        const int b = i / SK_BN, row = i % SK_BN;
+    for (int i = tid; i < BATCH * SK_RW; i += nt) {
+        const int b = i / SK_RW, row = i % SK_RW;
         float v = 0.f;
-        for (int w = 0; w < waves; w++) v += red[(w * BATCH + b) * SK_BN + row];
-        a.y[(int64_t)b * a.rows + (int64_t)t * SK_BN + row] = v;
+        for (int w = 0; w < waves; w++) v += red[(w * BATCH + b) * SK_RW + row];
+        a.y[(int64_t)b * a.rows + (int64_t)t * SK_BN + half * SK_RW + row] = v;
     }
 }
 
@@ -262,7 +283,7 @@ hipError_t launch_skip(const SkipArgs &a, int64_t n_list, hipStream_t s)
     if (L.total > (uint32_t)lw_device_lds_bytes()) return hipErrorNotSupported;
     hipError_t e = lw_allow_lds<k_skip<BITS, BATCH>>();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_skip<BITS, BATCH>), dim3((unsigned)n_list), dim3(16 * a.jt), L.total, s, a);
+    hipLaunchKernelGGL((k_skip<BITS, BATCH>), dim3((unsigned)(2 * n_list)), dim3(8 * a.jt), L.total, s, a);
     return hipGetLastError();
 }
 
@@ -295,7 +316,7 @@ hipError_t lw_launch_skip(const uint32_t *words, const uint32_t *dm, int bits, i
     a.n_tiles = (int32_t)(rows / SK_BN);
     const int cc = SK_CW * (32 / bits);
     a.n_jc = (int32_t)(cols / cc);
-    const int jt = a.n_jc < 64 ? ((a.n_jc + 3) / 4) * 4 : 64;   // chunk lanes: whole wavefronts, at most 16 waves
+    const int jt = a.n_jc < 128 ? ((a.n_jc + 7) / 8) * 8 : 128;   // chunk lanes: whole wavefronts, at most 16 waves
     a.jt = jt;
     switch (bits) {
     case 2: return skip_batch<2>(a, n_list, batch, s);

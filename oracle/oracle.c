@@ -222,6 +222,82 @@ int or_package_merge(int n_alpha, const uint64_t *counts, int L, uint8_t *lens)
 }
 
 /* ------------------------------------------------------------------ */
+/* Code lengths of the bundles: the compact code.                        */
+/* ------------------------------------------------------------------ */
+/* Reading: the pages fix the 11-bit limit and one table per matrix, not how
+ * the lengths are chosen.  The bundles use the cheapest prefix code (least
+ * total bits sum count * length) among those with lengths <= 11 and at most
+ * four distinct lengths, of which the three shorter are <= 8 (so a decoder
+ * needs three comparisons of the top 8 peek bits).  Search and ties:
+ *   - rank the used symbols by (count descending, symbol ascending);
+ *   - for every length set a < b < c <= 8, c < d <= 11, in ascending
+ *     lexicographic order, and every split of the ranks into n1 at length
+ *     a, n2 at b (n1, n2 ascending), give length c to as many of the
+ *     remaining ranks as the Kraft sum (<= 1) allows and d to the rest;
+ *   - keep the first split whose total is strictly below every earlier one.
+ * Giving c to more ranks never costs bits, so the search is exhaustive over
+ * the allowed codes.  A single used symbol gets length 1.  Returns 0, or -1
+ * if more than 256 symbols are used (no such code exists). */
+int or_compact_lengths(int n_alpha, const uint64_t *counts, uint8_t *lens)
+{
+    int n = 0;
+    or_leaf *rank = (or_leaf *)malloc(sizeof(or_leaf) * (size_t)(n_alpha > 0 ? n_alpha : 1));
+    for (int s = 0; s < n_alpha; s++) {
+        lens[s] = 0;
+        if (counts[s] > 0) { rank[n].c = counts[s]; rank[n].s = s; n++; }
+    }
+    if (n == 0) { free(rank); return 0; }
+    if (n == 1) { lens[rank[0].s] = 1; free(rank); return 0; }
+    if (n > 256) { free(rank); return -1; }
+    /* insertion sort: count descending, symbol ascending */
+    for (int i = 1; i < n; i++) {
+        or_leaf v = rank[i];
+        int j = i - 1;
+        while (j >= 0 && (rank[j].c < v.c || (rank[j].c == v.c && rank[j].s > v.s))) { rank[j + 1] = rank[j]; j--; }
+        rank[j + 1] = v;
+    }
+    /* total count of ranks [0, k) */
+    uint64_t *head = (uint64_t *)calloc((size_t)n + 1, sizeof(uint64_t));
+    for (int i = 0; i < n; i++) head[i + 1] = head[i] + rank[i].c;
+    const int64_t full = 2048;                 /* Kraft sum 1 in units of 2^-11 */
+    uint64_t best = UINT64_MAX;
+    int best_len[4] = {0, 0, 0, 0}, best_end[3] = {0, 0, 0};
+    for (int a = 1; a <= 8; a++)
+      for (int b = a + 1; b <= 8; b++)
+        for (int c = b + 1; c <= 8; c++)
+          for (int d = c + 1; d <= 11; d++) {
+            int64_t wa = full >> a, wb = full >> b, wc = full >> c, wd = full >> d;
+            for (int n1 = 0; n1 <= n; n1++) {
+              if (n1 * wa > full) break;
+              for (int n2 = 0; n1 + n2 <= n; n2++) {
+                int64_t used = n1 * wa + n2 * wb;
+                if (used > full) break;
+                int64_t left = n - n1 - n2;
+                int64_t spare = full - used - left * wd;       /* Kraft room once the rest takes d */
+                if (spare < 0) continue;
+                int64_t n3 = spare / (wc - wd);
+                if (n3 > left) n3 = left;
+                int e1 = n1, e2 = n1 + n2, e3 = n1 + n2 + (int)n3;
+                uint64_t bits = (uint64_t)a * head[e1] + (uint64_t)b * (head[e2] - head[e1]) +
+                                (uint64_t)c * (head[e3] - head[e2]) + (uint64_t)d * (head[n] - head[e3]);
+                if (bits < best) {
+                  best = bits;
+                  best_len[0] = a; best_len[1] = b; best_len[2] = c; best_len[3] = d;
+                  best_end[0] = e1; best_end[1] = e2; best_end[2] = e3;
+                }
+              }
+            }
+          }
+    for (int i = 0; i < n; i++) {
+        int g = i < best_end[0] ? 0 : (i < best_end[1] ? 1 : (i < best_end[2] ? 2 : 3));
+        lens[rank[i].s] = (uint8_t)best_len[g];
+    }
+    free(head);
+    free(rank);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Canonical code and the decoder's per-length arrays.                  */
 /* ------------------------------------------------------------------ */
 /* Reading: canonical assignment in the manner of RFC 1951 section 3.2.2:

@@ -52,6 +52,7 @@ def lib():
             "or_unsymbolise_q": (None, [i32, i64, i64, P, P]),
             "or_histogram": (None, [P, i64, i32, P]),
             "or_package_merge": (i32, [i32, P, i32, P]),
+            "or_compact_lengths": (i32, [i32, P, P]),
             "or_canonical": (i32, [i32, P, P, P, P, P, P, P]),
             "or_encode_tiles": (i64, [i64, i32, P, P, P, P, P, P]),
             "or_decode_limit": (i32, [i64, i32, P, P, P, P, P, P, P, P, P]),
@@ -123,6 +124,16 @@ def package_merge(counts, limit: int = MAXLEN) -> np.ndarray:
     rc = lib().or_package_merge(counts.size, _p(counts), limit, _p(lens))
     if rc != 0:
         raise ValueError("alphabet does not fit the length limit")
+    return lens
+
+
+def compact_lengths(counts) -> np.ndarray:
+    """Lengths of the bundles' code: the cheapest prefix code with lengths
+    <= 11 using at most four distinct lengths, the three shorter <= 8."""
+    counts = np.ascontiguousarray(counts, dtype=np.uint64)
+    lens = np.zeros(counts.size, dtype=np.uint8)
+    if lib().or_compact_lengths(counts.size, _p(counts), _p(lens)) != 0:
+        raise ValueError("more than 256 symbols")
     return lens
 
 
@@ -259,7 +270,7 @@ def build_bundle_q(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray) -
     spl = symbols_per_lane(kind)
     syms = symbolise_q(kind, codes)
     counts = histogram(syms, alphabet(kind))
-    lens = package_merge(counts)
+    lens = compact_lengths(counts)
     tab = canonical(lens)
     tile_off, words, lane_bits = encode_tiles(syms, spl, lens, tab["codes"])
     return dict(kind=kind, rows=R, cols=Cc, spl=spl, counts=counts, table=tab,
@@ -303,7 +314,7 @@ def build_bundle_bf16(w: np.ndarray) -> dict:
     L.or_bf16_verbatim(R, Cc, _p(w), _p(palette), n_pal, _p(vb_bits), _p(vb_start), _p(verbatim))
     syms = symbolise_bf16(w, palette, n_pal, vb_bits)
     counts = histogram(syms, 16)
-    lens = package_merge(counts)
+    lens = compact_lengths(counts)
     tab = canonical(lens)
     tile_off, words, lane_bits = encode_tiles(syms, 512, lens, tab["codes"])
     sm = np.zeros(nt * 4096, dtype=np.uint32)

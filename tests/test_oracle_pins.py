@@ -570,3 +570,102 @@ def test_skip_ledger_page_configuration():
     assert dense / (4 * 16 * 256 * 64) == 8.0          # packing alone, all 16 tiles
     assert L["scale_bytes"] == 6 * 16 * 64 * 4
     assert L["total_bytes"] == L["word_bytes"] + L["scale_bytes"] + 4096 * 2 + 6 * 64 * 4
+
+
+# ------------------------------------------------- compact code (the bundles' lengths)
+
+def _compact_ok(lens):
+    used = sorted(set(int(x) for x in lens if x))
+    return len(used) <= 4 and max(used) <= 11 and all(L <= 8 for L in used[:-1]) and kraft_sum(lens) <= 2048
+
+
+def _golden_rows(prefix):
+    out = {}
+    with open(os.path.join(GOLDEN, "canonical_small.txt")) as f:
+        for line in f:
+            if line.startswith(prefix):
+                k, *v = line.split()
+                out[k] = [int(x) for x in v]
+    return out
+
+
+def test_compact_golden_hand_worked():
+    """The hand-worked compact codes of tests/golden/canonical_small.txt: a
+    tie between two codes, a histogram whose optimum needs five lengths, and
+    a tie that the search order decides."""
+    g = _golden_rows("compact")
+    for ck, lk in (("compact_counts", "compact_lens"), ("compact6_counts", "compact6_lens"),
+                   ("compact7_counts", "compact7_lens")):
+        lens = O.compact_lengths(np.array(g[ck], np.uint64))
+        assert lens.tolist() == g[lk], (ck, lens.tolist())
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_compact_is_cheapest_allowed_code_exhaustive(seed):
+    """Exhaustive search over EVERY length vector (1..11 per symbol, 2..5
+    symbols) with at most four distinct lengths, the three shorter <= 8, and
+    Kraft sum <= 1: its least total equals the oracle's."""
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(2, 6))
+    counts = rng.integers(1, 60, size=n).astype(np.uint64)
+    if seed % 4 == 0:
+        counts = np.array([1 << int(k) for k in rng.integers(0, 12, size=n)], np.uint64)   # skewed
+    lens = O.compact_lengths(counts)
+    assert _compact_ok(lens)
+    got = int((lens.astype(np.int64) * counts.astype(np.int64)).sum())
+    best = None
+    for v in itertools.product(range(1, 12), repeat=n):
+        if not _compact_ok(v):
+            continue
+        c = int(sum(int(a) * int(b) for a, b in zip(v, counts)))
+        best = c if best is None or c < best else best
+    assert got == best
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_compact_versus_package_merge(seed):
+    """Never cheaper than the optimal 11-bit-limited code (package-merge);
+    exactly as cheap when that code already uses at most four lengths with
+    the three shorter <= 8; every rank no longer than a rarer one."""
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(2, 257))
+    counts = rng.integers(0, 1000, size=256).astype(np.uint64)
+    counts[rng.permutation(256)[n:]] = 0
+    if counts.sum() == 0:
+        counts[0] = 5
+    lens = O.compact_lengths(counts)
+    pm = O.package_merge(counts)
+    cost = lambda L: int((L.astype(np.int64) * counts.astype(np.int64)).sum())
+    assert _compact_ok(lens)
+    assert cost(lens) >= cost(pm)
+    if _compact_ok(pm):
+        assert cost(lens) == cost(pm)
+    nz = np.nonzero(counts)[0]
+    order = sorted(nz, key=lambda s: (-int(counts[s]), s))
+    assert all(lens[order[i]] <= lens[order[i + 1]] for i in range(len(order) - 1))
+
+
+def test_compact_degenerate_alphabets():
+    assert O.compact_lengths(np.array([0, 7, 0], np.uint64)).tolist() == [0, 1, 0]
+    assert O.compact_lengths(np.array([3, 9], np.uint64)).tolist() == [1, 1]
+    assert set(O.compact_lengths(np.ones(256, np.uint64)).tolist()) == {8}
+    assert set(O.compact_lengths(np.ones(16, np.uint64)).tolist()) == {4}
+
+
+def test_compact_bits_on_workload_distribution():
+    """4-bit pair symbols of q = clamp(rint(N(7.5, 1.8)), 0, 15), with counts
+    proportional to the exact discretised distribution: 5.9419 bits per pair
+    for the optimal 11-bit-limited code and 5.9775 for the compact one with
+    lengths 5, 6, 8 and 11 (both figures from a separate dynamic program over
+    length sets and splits, not from either implementation here)."""
+    from math import erf, sqrt
+    cdf = lambda t: 0.5 * (1.0 + erf((t - 7.5) / (1.8 * sqrt(2.0))))
+    p = np.array([(1.0 if q == 15 else cdf(q + 0.5)) - (0.0 if q == 0 else cdf(q - 0.5)) for q in range(16)])
+    pair = np.outer(p, p).ravel()                      # symbol = q_even | q_odd << 4
+    counts = np.maximum(np.rint(pair * 1e12), 1).astype(np.uint64)
+    w = counts.astype(np.float64) / counts.sum()
+    lens = O.compact_lengths(counts)
+    pm = O.package_merge(counts)
+    assert abs(float((lens * w).sum()) - 5.9775) < 5e-4
+    assert abs(float((pm * w).sum()) - 5.9419) < 5e-4
+    assert sorted(set(lens.tolist())) == [5, 6, 8, 11]
