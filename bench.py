@@ -179,6 +179,24 @@ def cpu_baseline(mat, codes, d, m, xb, batch, coded):
             "one_thread_value": round(coded / t1 / 1e9, 4)}
 
 
+def read_probe(torch, dg, nbytes, a):
+    """HBM bandwidth of a plain read-only kernel (lw_read_probe), cold: at the
+    workload's coded size (a different buffer each step, as for the decoding
+    kernels) and over 2 GiB."""
+    out = {}
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for name, size in (("coded_size", (nbytes + 15) // 16 * 16), ("2GiB", 2 << 30)):
+        n = copies_for(size)
+        bufs = [torch.zeros(size, dtype=torch.uint8, device="cuda") for _ in range(n)]
+        f = lambda i: dg.lw_read_probe(bufs[i], sink)
+        steps = a.steps if size < (256 << 20) else max(5, a.steps // 20)
+        ms = time_graph(torch, f, n, steps, min(a.warmup, steps)) or time_loop(torch, f, n, steps, a.warmup)
+        out[name] = {"bytes": size, "us": round(ms * 1e3, 3), "GBs": round(size / (ms * 1e-3) / 1e9, 1),
+                     "frac_of_peak": round(size / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del bufs
+    return out
+
+
 def skip_legs(torch, dg, synth, mat, codes, d, m, x, batch, a):
     """Tile-skipping fixed-width GEMV (lw_skip_gemv): the same 4-bit codes and
     scales in the tile-transposed layout with every tile listed and with a
@@ -342,6 +360,8 @@ def main():
         result["mlp_pass"] = {"us_per_pass": round(pms * 1e3, 3),
                               "coded_GBs": round(coded / (pms * 1e-3) / 1e9, 2),
                               "over_three_independent_gemvs": round(pms / ms, 4)}
+    if not a.no_extras:
+        result["attainable_read"] = read_probe(torch, dg, coded, a)
     if a.copy_calib:
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

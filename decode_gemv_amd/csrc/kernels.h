@@ -64,6 +64,7 @@ hipError_t lw_launch_swiglu(const float *g, const float *u, uint16_t *h, int64_t
 hipError_t lw_launch_twin(const uint8_t *twin, const uint32_t *dm, int64_t rows, int64_t cols,
                           const uint16_t *x, float *y, int batch, hipStream_t s);
 hipError_t lw_launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+hipError_t lw_launch_read_probe(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
 hipError_t lw_launch_skip(const uint32_t *words, const uint32_t *dm, int bits, int64_t rows, int64_t cols,
                           const int32_t *tiles, int64_t n_list, const uint16_t *x, float *y, int batch,
                           hipStream_t s);

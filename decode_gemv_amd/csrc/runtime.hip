@@ -249,3 +249,14 @@ extern "C" lw_status lw_skip_gemv(const uint32_t *words, const uint32_t *dm, int
     if (e != hipSuccess) return hip_fail(e, "skip launch");
     return LW_OK;
 }
+
+extern "C" lw_status lw_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream)
+{
+    if (!src || !sink) return lw_fail(LW_E_ARG, "null argument");
+    if (bytes < 16 || bytes % 16) return lw_fail(LW_E_ARG, "bytes must be a positive multiple of 16");
+    if (reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(sink) % 4)
+        return lw_fail(LW_E_ARG, "src must be 16-byte aligned and sink 4-byte aligned");
+    hipError_t e = lw_launch_read_probe(src, (int64_t)bytes, sink, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "read probe launch");
+    return LW_OK;
+}

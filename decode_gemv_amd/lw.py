@@ -67,6 +67,7 @@ def _load():
         "lw_swiglu": (st, [P, P, P, i64, P]),
         "lw_skip_pack": (st, [P, i32, i64, i64, P, P, P, P]),
         "lw_skip_gemv": (st, [P, P, i32, i64, i64, P, i64, P, P, i32, P]),
+        "lw_read_probe": (st, [P, C.c_size_t, P, P]),
         "lw_status_str": (C.c_char_p, [st]),
         "lw_last_error": (C.c_char_p, []),
     }
@@ -262,6 +263,12 @@ def lw_skip_gemv(words, dm, bits: int, rows: int, cols: int, tiles, x, y, batch:
     xp = _dptr(x, "x") if n else None
     yp = _dptr(y, "y") if n else None
     _check(_L.lw_skip_gemv(wp, dp, bits, rows, cols, tp, n, xp, yp, batch, _stream(stream)))
+
+
+def lw_read_probe(src, sink, stream=None) -> None:
+    """Read every byte of the device tensor src once (measurement only)."""
+    _check(_L.lw_read_probe(_dptr(src, "src"), src.numel() * src.element_size(), _dptr(sink, "sink"),
+                            _stream(stream)))
 
 
 def lw_swiglu(gate, up, h, stream=None) -> None:

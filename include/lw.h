@@ -241,6 +241,20 @@ lw_status lw_skip_gemv(const uint32_t *words, const uint32_t *dm, int bits, int6
  * Errors: LW_E_ARG (n < 0, or a null pointer with n > 0), LW_E_DEVICE. */
 lw_status lw_swiglu(const float *gate, const float *up, uint16_t *h, int64_t n, void *stream);
 
+/* ---------------------------------------------------------------- measurement */
+
+/* Read-only streaming probe: reads `bytes` from device memory `src` with
+ * fully coalesced 16-byte loads (512 threads per workgroup, eight loads per
+ * thread, all issued before use) and writes nothing except, to keep the loads
+ * live, sink[0] when the XOR of a thread's words equals 0x9E3779B9.  Timed
+ * beside the decoding kernels, it gives the HBM bandwidth a kernel that only
+ * reads attains at a given size (context for their fraction of peak; not part
+ * of the decode path).
+ *   src : device, 16-byte aligned; bytes: a positive multiple of 16
+ *   sink: device u32, 4-byte aligned
+ * Errors: LW_E_ARG, LW_E_DEVICE. */
+lw_status lw_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
 const char *lw_status_str(lw_status s);
 const char *lw_last_error(void);
 

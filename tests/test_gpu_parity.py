@@ -300,3 +300,15 @@ def test_full_size_down_batch16(torch, dg):
     y = _run_gemv(dg, torch, db, x, 16, mat.rows)
     assert np.all(np.isfinite(y))
     assert rel_err(y[:, rows], O.gemv_q(codes, d, m, x, 16, rows=rows)) <= TOL
+
+
+def test_read_probe_reads_and_writes_nothing(torch, dg):
+    """The measurement probe leaves its sink untouched for data whose words
+    do not fold to its marker, and rejects a size that is not a multiple of 16."""
+    src = torch.arange(1 << 20, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    dg.lw_read_probe(src, sink)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0
+    with pytest.raises(dg.LwError):
+        dg.lw_read_probe(torch.zeros(10, dtype=torch.uint8, device="cuda"), sink)
