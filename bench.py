@@ -179,6 +179,29 @@ def cpu_baseline(mat, codes, d, m, xb, batch, coded):
             "one_thread_value": round(coded / t1 / 1e9, 4)}
 
 
+def pipeline_legs(torch, dg, mat, db, a):
+    """"Unweight"'s pipelines on the bf16 matrix: lw_autotune times the fused
+    kernels (batch <= 16) and full decode + library GEMM at each batch and
+    keeps the faster per batch bucket (one resident copy of the bundle, as an
+    autotuner on the target would see it)."""
+    batches = [1, 4, 16, 64, 256, 1024]
+    rng = np.random.default_rng(5)
+    import synth
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((max(batches), mat.cols), dtype=np.float32))
+    x = torch.from_numpy(xb.view(np.int16)).cuda()
+    y = torch.empty((max(batches), mat.rows), dtype=torch.float32, device="cuda")
+    wbuf = torch.empty(mat.rows * mat.cols, dtype=torch.int16, device="cuda")
+    us = dg.lw_autotune(db, batches, x, y, wbuf, reps=10)
+    names = {dg.LW_PIPE_FUSED: "fused", dg.LW_PIPE_FULL_DECODE: "full_decode"}
+    out = {}
+    for i, b in enumerate(batches):
+        row = {names[p]: (round(float(us[i, p]), 2) if us[i, p] > 0 else None) for p in names}
+        row["chosen"] = names[dg.lw_pipeline_get(db, b)]
+        out[f"batch_{b}"] = row
+    del wbuf
+    return out
+
+
 def read_probe(torch, dg, nbytes, a):
     """HBM bandwidth of a plain read-only kernel (lw_read_probe), cold: at the
     workload's coded size (a different buffer each step, as for the decoding
@@ -360,6 +383,8 @@ def main():
         result["mlp_pass"] = {"us_per_pass": round(pms * 1e3, 3),
                               "coded_GBs": round(coded / (pms * 1e-3) / 1e9, 2),
                               "over_three_independent_gemvs": round(pms / ms, 4)}
+    if not a.no_extras and kind == dg.LW_BF16_EXP and len(mats) == 1:
+        result["pipelines"] = pipeline_legs(torch, dg, mat, dbs[0][0], a)
     if not a.no_extras:
         result["attainable_read"] = read_probe(torch, dg, coded, a)
     if a.copy_calib:

@@ -72,7 +72,7 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
             if verbose and err.strip():
                 print(err)
     tmp = LIB + ".tmp"
-    run([hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp, *objs])
+    run([hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp, *objs, "-L/opt/rocm/lib", "-lrocblas"])
     os.replace(tmp, LIB)
     return LIB
 

@@ -21,7 +21,8 @@
 #define LW_LANES 32
 #define LW_ALIGN 256
 #define LW_HEADER_BYTES 512
-#define LW_BATCH_MAX 16
+#define LW_BATCH_MAX 16             /* largest batch of the fused kernels */
+#define LW_GEMM_BATCH_MAX 65536     /* largest batch of lw_gemm */
 #define LW_CB_PER_WG 4             /* column blocks one workgroup covers (one per wave) */
 
 typedef struct {

@@ -3,18 +3,26 @@
 // pick and launch the gfx950 kernels.  The library never allocates device
 // memory; PyTorch (or any caller) owns buffers and streams.
 #include <cstring>
+#include <map>
 #include <memory>
 #include <string>
+
+#include <rocblas/rocblas.h>
 
 #include "lane_decode.hpp"
 
 lw_status lw_fail(lw_status s, const std::string &msg);   // bundle.cpp
+
+// Pipeline of each batch bucket: bucket k holds batches (2^(k-1), 2^k]
+// (bucket 0: batch 1), up to LW_GEMM_BATCH_MAX.
+#define LW_NBUCKET 17
 
 struct lw_dev_bundle {
     lw_image_header h;
     lw_table table;
     lw_gputab tab;
     uint8_t *base;
+    int8_t pipe[LW_NBUCKET];
 };
 
 static lw_status hip_fail(hipError_t e, const char *what)
@@ -51,6 +59,8 @@ extern "C" lw_status lw_bundle_upload(const lw_bundle *b, void *dev_buf, size_t 
     std::memcpy(&db->tab, static_cast<const uint8_t *>(img) + db->h.off[LW_REG_GPUTAB], sizeof(db->tab));
     std::memcpy(&db->table, static_cast<const uint8_t *>(img) + db->h.off[LW_REG_TABLE], sizeof(db->table));
     db->base = static_cast<uint8_t *>(dev_buf);
+    for (int k = 0; k < LW_NBUCKET; k++)      // default: the fused kernels where they exist
+        db->pipe[k] = (k <= 4 || db->h.kind != LW_BF16_EXP) ? LW_PIPE_FUSED : LW_PIPE_FULL_DECODE;
     *out = db.release();
     return LW_OK;
 }
@@ -259,4 +269,161 @@ extern "C" lw_status lw_read_probe(const void *src, size_t bytes, uint32_t *sink
     hipError_t e = lw_launch_read_probe(src, (int64_t)bytes, sink, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "read probe launch");
     return LW_OK;
+}
+
+// ------------------------------------------------------------------ pipelines
+// "Unweight", section "Four approaches to using compressed weights": full
+// decode reconstructs the bf16 weights into memory and hands them to a
+// library GEMM; the fused path never materialises them.  Which one is faster
+// depends on the batch and the matrix, so a per-bundle table, filled by
+// measurement (lw_autotune), picks the pipeline of each batch bucket.
+
+static int batch_bucket(int batch)
+{
+    int k = 0;
+    while ((1 << k) < batch) k++;
+    return k;
+}
+
+// one rocBLAS handle per thread and device (rocBLAS handles are not safe to
+// share between threads; each keeps rocBLAS's own workspace)
+static lw_status blas_handle(rocblas_handle *out)
+{
+    thread_local std::map<int, rocblas_handle> handles;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    auto it = handles.find(dev);
+    if (it == handles.end()) {
+        rocblas_handle h = nullptr;
+        if (rocblas_create_handle(&h) != rocblas_status_success)
+            return lw_fail(LW_E_DEVICE, "rocblas_create_handle failed");
+        it = handles.emplace(dev, h).first;
+    }
+    *out = it->second;
+    return LW_OK;
+}
+
+static bool valid_pipeline(const lw_dev_bundle *db, int pipeline, int batch)
+{
+    if (pipeline == LW_PIPE_FUSED) return batch <= LW_BATCH_MAX;
+    if (pipeline == LW_PIPE_FULL_DECODE) return db->h.kind == LW_BF16_EXP;
+    return false;
+}
+
+extern "C" lw_status lw_gemm_full_decode(const lw_dev_bundle *db, void *wbuf, size_t wbuf_bytes, const void *x,
+                                         float *y, int batch, void *stream)
+{
+    if (!db || !wbuf || !x || !y) return lw_fail(LW_E_ARG, "null argument");
+    if (db->h.kind != LW_BF16_EXP)
+        return lw_fail(LW_E_UNSUPPORTED, "full decode is for bf16 bundles (their decoded weights are exact)");
+    if (batch < 1 || batch > LW_GEMM_BATCH_MAX) return lw_fail(LW_E_ARG, "batch must be in 1..65536");
+    const uint64_t need = (uint64_t)db->h.rows * db->h.cols * 2;
+    if (wbuf_bytes < need) return lw_fail(LW_E_ARG, "weight buffer smaller than rows * cols * 2 bytes");
+    if (reinterpret_cast<uintptr_t>(wbuf) % 16 || reinterpret_cast<uintptr_t>(x) % 16 ||
+        reinterpret_cast<uintptr_t>(y) % 16)
+        return lw_fail(LW_E_ARG, "wbuf, x and y must be 16-byte aligned");
+    if (db->h.rows > 0x7FFFFFFF || db->h.cols > 0x7FFFFFFF) return lw_fail(LW_E_SHAPE, "matrix too large for the GEMM");
+    lw_status st = lw_decode_only(db, wbuf, wbuf_bytes, nullptr, stream);
+    if (st) return st;
+    rocblas_handle h;
+    if ((st = blas_handle(&h))) return st;
+    if (rocblas_set_stream(h, (hipStream_t)stream) != rocblas_status_success)
+        return lw_fail(LW_E_DEVICE, "rocblas_set_stream failed");
+    // column-major view: Y^T (rows x batch) = W (rows x cols) X^T (cols x batch),
+    // with W row-major = A^T of a cols x rows column-major A
+    const float alpha = 1.0f, beta = 0.0f;
+    const rocblas_int m = (rocblas_int)db->h.rows, n = batch, k = (rocblas_int)db->h.cols;
+    rocblas_status bs = rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none, m, n, k, &alpha,
+                                        wbuf, rocblas_datatype_bf16_r, k, x, rocblas_datatype_bf16_r, k, &beta, y,
+                                        rocblas_datatype_f32_r, m, y, rocblas_datatype_f32_r, m,
+                                        rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+    if (bs != rocblas_status_success)
+        return lw_fail(LW_E_DEVICE, std::string("rocblas_gemm_ex: ") + rocblas_status_to_string(bs));
+    return LW_OK;
+}
+
+extern "C" lw_status lw_pipeline_set(lw_dev_bundle *db, int batch_lo, int batch_hi, int pipeline)
+{
+    if (!db) return lw_fail(LW_E_ARG, "null bundle");
+    if (batch_lo < 1 || batch_hi < batch_lo || batch_hi > LW_GEMM_BATCH_MAX)
+        return lw_fail(LW_E_ARG, "batch range must lie in 1..65536");
+    for (int k = batch_bucket(batch_lo); k <= batch_bucket(batch_hi); k++)
+        if (!valid_pipeline(db, pipeline, 1 << k))
+            return lw_fail(LW_E_UNSUPPORTED, "pipeline not available for this bundle and batch");
+    for (int k = batch_bucket(batch_lo); k <= batch_bucket(batch_hi); k++) db->pipe[k] = (int8_t)pipeline;
+    return LW_OK;
+}
+
+extern "C" lw_status lw_pipeline_get(const lw_dev_bundle *db, int batch, int *pipeline)
+{
+    if (!db || !pipeline) return lw_fail(LW_E_ARG, "null argument");
+    if (batch < 1 || batch > LW_GEMM_BATCH_MAX) return lw_fail(LW_E_ARG, "batch must be in 1..65536");
+    *pipeline = db->pipe[batch_bucket(batch)];
+    return LW_OK;
+}
+
+extern "C" lw_status lw_gemm(const lw_dev_bundle *db, const void *x, float *y, int batch, void *wbuf,
+                             size_t wbuf_bytes, void *stream)
+{
+    if (!db) return lw_fail(LW_E_ARG, "null bundle");
+    if (batch < 1 || batch > LW_GEMM_BATCH_MAX) return lw_fail(LW_E_ARG, "batch must be in 1..65536");
+    const int p = db->pipe[batch_bucket(batch)];
+    if (p == LW_PIPE_FUSED) {
+        if (batch > LW_BATCH_MAX) return lw_fail(LW_E_UNSUPPORTED, "no pipeline for this batch");
+        return lw_gemv(db, x, y, batch, stream);
+    }
+    return lw_gemm_full_decode(db, wbuf, wbuf_bytes, x, y, batch, stream);
+}
+
+extern "C" lw_status lw_autotune(lw_dev_bundle *db, const int *batches, int n, void *wbuf, size_t wbuf_bytes,
+                                 const void *x, float *y, int reps, void *stream, float *us_out)
+{
+    if (!db || !batches || n < 1 || reps < 1 || !x || !y) return lw_fail(LW_E_ARG, "bad argument");
+    hipStream_t s = (hipStream_t)stream;
+    hipEvent_t e0, e1;
+    hipError_t he = hipEventCreate(&e0);
+    if (he != hipSuccess) return hip_fail(he, "hipEventCreate");
+    he = hipEventCreate(&e1);
+    if (he != hipSuccess) {
+        hipEventDestroy(e0);
+        return hip_fail(he, "hipEventCreate");
+    }
+    lw_status st = LW_OK;
+    for (int i = 0; i < n && !st; i++) {
+        const int batch = batches[i];
+        if (batch < 1 || batch > LW_GEMM_BATCH_MAX) {
+            st = lw_fail(LW_E_ARG, "batch must be in 1..65536");
+            break;
+        }
+        float best = -1.0f;
+        int best_p = -1;
+        for (int p = 0; p < LW_PIPE_COUNT && !st; p++) {
+            if (us_out) us_out[i * LW_PIPE_COUNT + p] = -1.0f;
+            if (!valid_pipeline(db, p, batch) || (p == LW_PIPE_FULL_DECODE && !wbuf)) continue;
+            auto run = [&]() {
+                return p == LW_PIPE_FUSED ? lw_gemv(db, x, y, batch, stream)
+                                          : lw_gemm_full_decode(db, wbuf, wbuf_bytes, x, y, batch, stream);
+            };
+            if ((st = run())) break;                       // warm-up (and first-use set-up)
+            hipEventRecord(e0, s);
+            for (int r = 0; r < reps && !st; r++) st = run();
+            hipEventRecord(e1, s);
+            if (st) break;
+            he = hipEventSynchronize(e1);
+            float ms = 0.f;
+            if (he == hipSuccess) he = hipEventElapsedTime(&ms, e0, e1);
+            if (he != hipSuccess) {
+                st = hip_fail(he, "timing");
+                break;
+            }
+            const float us = 1000.0f * ms / (float)reps;
+            if (us_out) us_out[i * LW_PIPE_COUNT + p] = us;
+            if (best < 0 || us < best) best = us, best_p = p;
+        }
+        if (!st && best_p >= 0) db->pipe[batch_bucket(batch)] = (int8_t)best_p;
+    }
+    hipEventDestroy(e0);
+    hipEventDestroy(e1);
+    return st;
 }

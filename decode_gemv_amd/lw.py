@@ -20,6 +20,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "lw.h")
 
 LW_OK, LW_E_ARG, LW_E_SHAPE, LW_E_TABLE, LW_E_FORMAT, LW_E_NOMEM, LW_E_DEVICE, LW_E_UNSUPPORTED = range(8)
 LW_Q4_PAIR, LW_Q6_SINGLE, LW_BF16_EXP = 1, 2, 3
+LW_PIPE_FUSED, LW_PIPE_FULL_DECODE, LW_PIPE_COUNT = 0, 1, 2
 (LW_REG_TABLE, LW_REG_GPUTAB, LW_REG_TILE_OFF, LW_REG_WORDS, LW_REG_DM, LW_REG_PALETTE, LW_REG_SM,
  LW_REG_VB_BITS, LW_REG_VB_START, LW_REG_VERBATIM, LW_REG_SPLIT, LW_REG_WORK, LW_REG_COUNT) = range(13)
 
@@ -68,6 +69,11 @@ def _load():
         "lw_skip_pack": (st, [P, i32, i64, i64, P, P, P, P]),
         "lw_skip_gemv": (st, [P, P, i32, i64, i64, P, i64, P, P, i32, P]),
         "lw_read_probe": (st, [P, C.c_size_t, P, P]),
+        "lw_gemm_full_decode": (st, [P, P, C.c_size_t, P, P, i32, P]),
+        "lw_pipeline_set": (st, [P, i32, i32, i32]),
+        "lw_pipeline_get": (st, [P, i32, C.POINTER(C.c_int)]),
+        "lw_gemm": (st, [P, P, P, i32, P, C.c_size_t, P]),
+        "lw_autotune": (st, [P, P, i32, P, C.c_size_t, P, P, i32, P, P]),
         "lw_status_str": (C.c_char_p, [st]),
         "lw_last_error": (C.c_char_p, []),
     }
@@ -263,6 +269,40 @@ def lw_skip_gemv(words, dm, bits: int, rows: int, cols: int, tiles, x, y, batch:
     xp = _dptr(x, "x") if n else None
     yp = _dptr(y, "y") if n else None
     _check(_L.lw_skip_gemv(wp, dp, bits, rows, cols, tp, n, xp, yp, batch, _stream(stream)))
+
+
+def _wbuf(wbuf):
+    return (_dptr(wbuf, "wbuf"), wbuf.numel() * wbuf.element_size()) if wbuf is not None else (None, 0)
+
+
+def lw_gemm_full_decode(db: DevBundle, wbuf, x, y, batch: int, stream=None) -> None:
+    wp, wn = _wbuf(wbuf)
+    _check(_L.lw_gemm_full_decode(db.ptr, wp, wn, _dptr(x, "x"), _dptr(y, "y"), batch, _stream(stream)))
+
+
+def lw_pipeline_set(db: DevBundle, batch_lo: int, batch_hi: int, pipeline: int) -> None:
+    _check(_L.lw_pipeline_set(db.ptr, batch_lo, batch_hi, pipeline))
+
+
+def lw_pipeline_get(db: DevBundle, batch: int) -> int:
+    p = C.c_int()
+    _check(_L.lw_pipeline_get(db.ptr, batch, C.byref(p)))
+    return p.value
+
+
+def lw_gemm(db: DevBundle, x, y, batch: int, wbuf=None, stream=None) -> None:
+    wp, wn = _wbuf(wbuf)
+    _check(_L.lw_gemm(db.ptr, _dptr(x, "x"), _dptr(y, "y"), batch, wp, wn, _stream(stream)))
+
+
+def lw_autotune(db: DevBundle, batches, x, y, wbuf=None, reps: int = 10, stream=None) -> np.ndarray:
+    """Time the pipelines at each batch, set the bundle's table; returns us [n][LW_PIPE_COUNT] (-1: n/a)."""
+    b = np.ascontiguousarray(batches, dtype=np.int32)
+    us = np.zeros((b.size, LW_PIPE_COUNT), dtype=np.float32)
+    wp, wn = _wbuf(wbuf)
+    _check(_L.lw_autotune(db.ptr, b.ctypes.data_as(C.c_void_p), b.size, wp, wn, _dptr(x, "x"), _dptr(y, "y"), reps,
+                          _stream(stream), us.ctypes.data_as(C.c_void_p)))
+    return us
 
 
 def lw_read_probe(src, sink, stream=None) -> None:

@@ -57,6 +57,14 @@ typedef enum {
     LW_BF16_EXP = 3        /* bf16 weights, exponent palette index coded singly: 16 symbols, 512 per lane */
 } lw_kind;
 
+/* Execution pipelines of lw_gemm ("Unweight", "Four approaches to using
+ * compressed weights"). */
+typedef enum {
+    LW_PIPE_FUSED = 0,         /* decode on chip inside the GEMV (lw_gemv); batch 1..16 */
+    LW_PIPE_FULL_DECODE = 1,   /* decode the weights into memory, then a library GEMM (bf16 bundles) */
+    LW_PIPE_COUNT = 2
+} lw_pipeline;
+
 typedef struct lw_bundle lw_bundle;          /* host bundle: opaque, owned by the library */
 typedef struct lw_dev_bundle lw_dev_bundle;  /* host-side descriptor of an uploaded bundle */
 
@@ -240,6 +248,50 @@ lw_status lw_skip_gemv(const uint32_t *words, const uint32_t *dm, int bits, int6
  * multiple of 4 take the vector path).
  * Errors: LW_E_ARG (n < 0, or a null pointer with n > 0), LW_E_DEVICE. */
 lw_status lw_swiglu(const float *gate, const float *up, uint16_t *h, int64_t n, void *stream);
+
+/* ---------------------------------------------------------------- pipelines */
+/* "Unweight", sections "Four approaches to using compressed weights" and
+ * "Why no single pipeline wins": full decode reconstructs the original bf16
+ * weights and hands them to a library GEMM (most bytes written, the plainest
+ * GEMM); the fused kernels never write the weights.  Which wins depends on
+ * the batch and the matrix, so a table per uploaded bundle (filled by
+ * measurement, lw_autotune) picks the pipeline of each batch bucket
+ * (2^(k-1), 2^k].  Default: fused wherever it exists (batch <= 16), else
+ * full decode. */
+
+/* y = W x through full decode: lw_decode_only into wbuf (bf16 [rows][cols],
+ * exact), then rocBLAS gemm_ex (bf16 x bf16, fp32 accumulate and output).
+ *   wbuf : device, >= rows*cols*2 bytes, 16-byte aligned, caller-owned
+ *   x    : device bf16 [batch][cols]; y: device fp32 [batch][rows]
+ *   1 <= batch <= 65536; bf16 bundles only (LW_E_UNSUPPORTED otherwise:
+ *   decoded 4- or 6-bit weights would be rounded)
+ * The library GEMM keeps one rocBLAS handle per thread and device (with
+ * rocBLAS's own workspace), created on first use: the one place where device
+ * memory is allocated on the library's behalf.
+ * Errors: LW_E_ARG, LW_E_UNSUPPORTED, LW_E_SHAPE, LW_E_DEVICE. */
+lw_status lw_gemm_full_decode(const lw_dev_bundle *db, void *wbuf, size_t wbuf_bytes, const void *x, float *y,
+                              int batch, void *stream);
+
+/* Set the pipeline (lw_pipeline) of the buckets holding batch_lo..batch_hi.
+ * Errors: LW_E_ARG, LW_E_UNSUPPORTED (the pipeline does not serve that batch
+ * or bundle kind). */
+lw_status lw_pipeline_set(lw_dev_bundle *db, int batch_lo, int batch_hi, int pipeline);
+lw_status lw_pipeline_get(const lw_dev_bundle *db, int batch, int *pipeline);
+
+/* y = W x through the pipeline the bundle's table names for this batch.
+ * wbuf/wbuf_bytes serve full decode (may be NULL/0 while the table picks the
+ * fused pipeline).  Errors: as lw_gemv and lw_gemm_full_decode. */
+lw_status lw_gemm(const lw_dev_bundle *db, const void *x, float *y, int batch, void *wbuf, size_t wbuf_bytes,
+                  void *stream);
+
+/* Measure every available pipeline at each of the n batch sizes (one warm-up
+ * call, then `reps` timed calls between HIP events on `stream`, synchronised
+ * here) and set each batch's bucket to the fastest.  x and y must hold the
+ * largest batch.  us_out (optional, host float [n][LW_PIPE_COUNT]) receives
+ * the microseconds per call, -1 where a pipeline does not apply.  wbuf = NULL
+ * leaves full decode out.  Errors: LW_E_ARG and those of the pipelines. */
+lw_status lw_autotune(lw_dev_bundle *db, const int *batches, int n, void *wbuf, size_t wbuf_bytes, const void *x,
+                      float *y, int reps, void *stream, float *us_out);
 
 /* ---------------------------------------------------------------- measurement */
 
