@@ -92,16 +92,6 @@ LW_DEV void lw_load_sm(uint32_t (&dst)[CHUNK], const uint32_t *smrow, int chunk)
     for (int i = 0; i < CHUNK; i++) dst[i] = smrow[(chunk * CHUNK + i) * 32];
 }
 
-// Ordinal, in the verbatim store, of segment `bit` (4*row + segment) of tile t.
-LW_DEV uint32_t lw_verbatim_ordinal(const KArgs &a, int64_t t, int bit)
-{
-    const uint32_t *vb = a.vb_bits + (size_t)t * 8;
-    uint32_t n = a.vb_start[t];
-    for (int w = 0; w < bit / 32; w++) n += __builtin_popcount(vb[w]);
-    const uint32_t below = vb[bit / 32] & ((1u << (bit % 32)) - 1u);
-    return n + __builtin_popcount(below);
-}
-
 template <int N8, int N16, int BATCH>
 __global__ __launch_bounds__(256) void k_gemv_bf16(KArgs a)
 {
@@ -184,28 +174,18 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(KArgs a)
                 run_chunk(ch + 1, ring[1]);
             }
 
-            // verbatim segments of this lane's row (rare): replace the
-            // placeholder weights' contribution by the stored values'
-            const uint32_t bits = (a.vb_bits[(size_t)c.t * 8 + c.l / 4] >> (8 * (c.l % 4) + 4 * c.half)) & 0xFu;
-            if (bits) {
-                const uint16_t *xrow = a.x + (size_t)c.cb * 256;
-                for (int seg = 0; seg < 4; seg++) {
-                    if (!((bits >> seg) & 1u)) continue;
-                    const uint32_t ord = lw_verbatim_ordinal(a, c.t, 8 * c.l + 4 * c.half + seg);
-                    const uint16_t *v = a.verbatim + (size_t)ord * 64;
-                    for (int b = 0; b < BATCH; b++) {
-                        float sacc = 0.f;
-                        for (int k = 0; k < 64; k++) {
-                            const int col = 64 * seg + k;
-                            const uint32_t smb = (smrow[(col / 4) * 32] >> (8 * (col % 4))) & 0xFFu;
-                            const uint32_t ph = ((smb & 0x80u) << 8) | (a.pal0 << 7) | (smb & 0x7Fu);
-                            const float wdiff = lw_bf16_to_f32(v[k]) - lw_bf16_to_f32(ph);
-                            sacc += wdiff * lw_bf16_to_f32(xrow[(size_t)b * a.cols + col]);
-                        }
-                        acc[b] += sacc;
-                    }
+            // verbatim segments (rare): replace the placeholder weights'
+            // contribution by the stored values', all lanes on one segment
+            const uint16_t *xcol = a.x + (size_t)c.cb * 256;
+            lw_verbatim_visit(a, c.t, c.lane, [&](int row, int col, uint32_t vv, uint32_t ph) {
+                const float wdiff = lw_bf16_to_f32(vv) - lw_bf16_to_f32(ph);
+                const int owner = (row >> 1) + 32 * (row & 1);
+#pragma unroll
+                for (int b = 0; b < BATCH; b++) {
+                    const float sb = lw_wave_sum(wdiff * lw_bf16_to_f32(xcol[(size_t)b * a.cols + col]));
+                    if (c.lane == owner) acc[b] += sb;
                 }
-            }
+            });
         } else {
 #pragma unroll
             for (int b = 0; b < BATCH; b++) acc[b] = __builtin_nanf("");
@@ -276,18 +256,13 @@ __global__ __launch_bounds__(256) void k_decode_bf16(KArgs a)
     }
     // the lane of the second row ends where the whole lane stream ends
     if (a.lane_bits && c.half) a.lane_bits[(size_t)c.t * 32 + c.l] = d.u - 31;
-    // verbatim segments overwrite the placeholder weights (rare)
-    const uint32_t bits = (a.vb_bits[(size_t)c.t * 8 + c.l / 4] >> (8 * (c.l % 4) + 4 * c.half)) & 0xFu;
-    if (bits) {
-        uint16_t *o16 = reinterpret_cast<uint16_t *>(a.out);
-        const int64_t row = (int64_t)c.rb * 64 + 2 * c.l + c.half;
-        for (int seg = 0; seg < 4; seg++) {
-            if (!((bits >> seg) & 1u)) continue;
-            const uint32_t ord = lw_verbatim_ordinal(a, c.t, 8 * c.l + 4 * c.half + seg);
-            for (int k = 0; k < 64; k++)
-                o16[row * a.cols + (int64_t)c.cb * 256 + 64 * seg + k] = a.verbatim[(size_t)ord * 64 + k];
-        }
-    }
+    // verbatim segments overwrite the placeholder weights (rare): after this
+    // wavefront's row stores, all lanes write one segment
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    uint16_t *o16 = reinterpret_cast<uint16_t *>(a.out);
+    lw_verbatim_visit(a, c.t, c.lane, [&](int row, int col, uint32_t vv, uint32_t) {
+        o16[((int64_t)c.rb * 64 + row) * a.cols + (int64_t)c.cb * 256 + col] = (uint16_t)vv;
+    });
 }
 
 template <int N8, int N16, int BATCH>

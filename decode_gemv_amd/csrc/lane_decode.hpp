@@ -217,6 +217,36 @@ LW_DEV void lw_tile_put64(uint32_t *slots, const uint32_t *words, uint32_t w0, u
     }
 }
 
+// Visit every verbatim segment of bf16 tile t ("Unweight": a 64-weight row
+// segment holding an exponent outside the palette is stored whole), the 64
+// lanes of the wavefront together: for tile row `row` and segment `seg`,
+// lane k gets column col = 64*seg + k, the stored bf16 weight vv and the
+// placeholder weight ph the stream decoded there (palette index 0 joined
+// with the column's sign and mantissa).  Segments are visited in bitmap
+// order (bit 4*row + seg), which is their order in the verbatim store, so
+// the store index is a running count from vb_start[t].  The loop is
+// wave-uniform; at N(0, 0.02) weights a tile holds about one such segment.
+template <class F>
+LW_DEV void lw_verbatim_visit(const KArgs &a, int64_t t, int lane, F f)
+{
+    const uint32_t words = a.vb_bits[(size_t)t * 8 + (lane & 7)];    // lanes 0..7: the tile's 256-bit map
+    uint32_t ord = a.vb_start[t];
+    for (int w = 0; w < 8; w++) {
+        uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)words, w);
+        while (bits) {
+            const int bit = 32 * w + __builtin_ctz(bits);
+            bits &= bits - 1u;
+            const int row = bit >> 2, seg = bit & 3, col = 64 * seg + lane;
+            const uint32_t vv = a.verbatim[(size_t)ord * 64 + lane];
+            ord++;
+            const uint32_t smw = a.sm[(size_t)t * 4096 + (size_t)(row & 1) * 64 * 32 + (size_t)(col / 4) * 32 + (row >> 1)];
+            const uint32_t smb = (smw >> (8 * (col % 4))) & 0xFFu;
+            const uint32_t ph = ((smb & 0x80u) << 8) | (a.pal0 << 7) | (smb & 0x7Fu);
+            f(row, col, vv, ph);
+        }
+    }
+}
+
 // One lane's decoder state.
 struct LaneDec {
     uint32_t slot0;              // LDS byte address of this lane's word in slot 0

@@ -72,15 +72,6 @@ LW_DEV LaneCtx lane_ctx(const KArgs &a)
     return c;
 }
 
-// Ordinal, in the verbatim store, of segment `bit` (4*row + segment) of tile t.
-LW_DEV uint32_t lw_verbatim_ordinal(const KArgs &a, int64_t t, int bit)
-{
-    const uint32_t *vb = a.vb_bits + (size_t)t * 8;
-    uint32_t n = a.vb_start[t];
-    for (int w = 0; w < bit / 32; w++) n += __builtin_popcount(vb[w]);
-    return n + __builtin_popcount(vb[bit / 32] & ((1u << (bit % 32)) - 1u));
-}
-
 LW_DEV void lw_st32(uint32_t addr, uint32_t v) { *(__attribute__((address_space(3))) uint32_t *)(size_t)addr = v; }
 LW_DEV u32x2 lw_ld64(uint32_t addr) { return *(__attribute__((address_space(3))) const u32x2 *)(size_t)addr; }
 
@@ -247,30 +238,19 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
         }
     __syncthreads();
     if constexpr (KIND == LW_BF16_EXP) {
-        // verbatim segments (rare): the lane owning each row replaces the
-        // placeholder weights' contribution by the stored values', per batch
-        const uint32_t bits =
-            c.active ? (a.vb_bits[(size_t)c.t * 8 + c.l / 4] >> (8 * (c.l % 4) + 4 * c.half)) & 0xFu : 0u;
-        if (bits) {
+        // verbatim segments (rare): replace the placeholder weights'
+        // contribution by the stored values', all lanes on one segment; lane
+        // 0 adds each batch column's sum to this wavefront's partial rows
+        if (c.active) {
             const uint16_t *xcol = a.x + (size_t)c.cb * 256;
-            const uint32_t *smw = a.sm + (size_t)c.t * 4096 + (size_t)c.half * 64 * 32 + c.l;
-            for (int seg = 0; seg < 4; seg++) {
-                if (!((bits >> seg) & 1u)) continue;
-                const uint32_t ord = lw_verbatim_ordinal(a, c.t, 8 * c.l + 4 * c.half + seg);
-                const uint16_t *vv = a.verbatim + (size_t)ord * 64;
+            lw_verbatim_visit(a, c.t, c.lane, [&](int row, int col, uint32_t vv, uint32_t ph) {
+                const float wdiff = __builtin_bit_cast(float, vv << 16) - __builtin_bit_cast(float, ph << 16);
                 for (int b = 0; b < a.batch; b++) {
-                    float sacc = 0.f;
-                    for (int k = 0; k < 64; k++) {
-                        const int col = 64 * seg + k;
-                        const uint32_t smb = (smw[(col / 4) * 32] >> (8 * (col % 4))) & 0xFFu;
-                        const uint32_t ph = ((smb & 0x80u) << 8) | (a.pal0 << 7) | (smb & 0x7Fu);
-                        const float wdiff = __builtin_bit_cast(float, (uint32_t)vv[k] << 16) -
-                                            __builtin_bit_cast(float, ph << 16);
-                        sacc += wdiff * __builtin_bit_cast(float, (uint32_t)xcol[(size_t)b * a.cols + col] << 16);
-                    }
-                    red[(c.wave * NB + b) * 64 + 2 * c.l + c.half] += sacc;
+                    const float sb = lw_wave_sum(
+                        wdiff * __builtin_bit_cast(float, (uint32_t)xcol[(size_t)b * a.cols + col] << 16));
+                    if (c.lane == 0) red[(c.wave * NB + b) * 64 + row] += sb;
                 }
-            }
+            });
         }
         __syncthreads();
     }
