@@ -5,8 +5,8 @@
 // A bundle is a flat image (lw_internal.h) holding, for one matrix:
 //   - one length-limited (<= 11 bit) canonical Huffman table,
 //   - the lane words of every 64x256 tile: 32 lanes, each carrying two
-//     adjacent rows as one MSB-first stream of 32-bit words, the lanes' words
-//     interleaved (word j of lane l at 32j + l) and zero-padded to the tile's
+//     adjacent rows as its own MSB-first bit stream cut into 32-bit words,
+//     the lanes' words interleaved (word j of lane l at 32j + l) and zero-padded to the tile's
 //     longest lane, plus a word offset per tile,
 //   - the raw per-super-block scales (Q4/Q6), or the raw sign+mantissa bytes,
 //     exponent palette and verbatim segments (bf16),

@@ -1,9 +1,9 @@
 // lane_decode.hpp -- the per-lane Huffman decoder shared by the gfx950 kernels.
 //
-// "LazyWeights", section "3 . Decode on demand" and Fig. 3(b): each lane
-// compares an 11-bit peek against per-length limits (no 2048-entry table),
-// adds the code length's offset to index the symbol table, and shifts its
-// buffer by the length.  Here one lane of a wavefront is one lane stream.
+// "LazyWeights", section "3 . Decode on demand" and Fig. 3(b): a lane finds
+// a code's length from the next 11 bits of its stream by comparison with one
+// bound per length (rather than a 2048-entry lookup), reads the symbol at that
+// length's base position plus the code's rank, and advances by the length.  Here one lane of a wavefront is one lane stream.
 //
 // Words.  A tile's interleaved words are staged in LDS as rows of 32 dwords
 // ("slots"): slot j+1 holds word row j, slot 0 and the last two slots are

@@ -6,9 +6,10 @@
  * them" (one length-limited Huffman table with 11-bit codes per matrix;
  * 64x256 tiles of 32 lanes of two rows; lanes' 32-bit words interleaved;
  * 4-bit codes coded in pairs; scales and minimums kept raw), section
- * "3 . Decode on demand" and Fig. 3 (a lane compares an 11-bit peek against
- * per-length limits, adds the length's offset to index the symbol table and
- * shifts by the length; per-tile lane offsets let any tile start on its own),
+ * "3 . Decode on demand" and Fig. 3 (a code's length comes from comparing the
+ * next 11 stream bits with per-length bounds, its symbol from that length's
+ * base position in the symbol list; each tile has its own offsets and so
+ * decodes independently),
  * and the runtime paragraph under Fig. 3 (software decode fused into GEMV; a
  * decode-free fixed-width "twin").  The bf16 variant follows "Unweight:
  * Compressing LLM Weights for Faster Inference", sections "Understanding BF16
@@ -251,8 +252,8 @@ lw_status lw_swiglu(const float *gate, const float *up, uint16_t *h, int64_t n, 
 
 /* ---------------------------------------------------------------- pipelines */
 /* "Unweight", sections "Four approaches to using compressed weights" and
- * "Why no single pipeline wins": full decode reconstructs the original bf16
- * weights and hands them to a library GEMM (most bytes written, the plainest
+ * "Why no single pipeline wins": full decode rebuilds every bf16 weight in
+ * memory and then runs a library GEMM on it (most bytes written, the plainest
  * GEMM); the fused kernels never write the weights.  Which wins depends on
  * the batch and the matrix, so a table per uploaded bundle (filled by
  * measurement, lw_autotune) picks the pipeline of each batch bucket

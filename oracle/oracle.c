@@ -32,8 +32,9 @@
 #include <string.h>
 #include <math.h>
 
-#define OR_MAXLEN 11          /* [LW] "length-limited Huffman table (11-bit codes)" */
-#define OR_TILE_ROWS 64       /* [LW] "A 64x256 tile is 32 lanes of two rows"      */
+#define OR_MAXLEN 11          /* [LW] section 2: no code is longer than 11 bits     */
+#define OR_TILE_ROWS 64       /* [LW] section 2: tiles of 64 rows by 256 columns,   */
+                              /* each lane holding two of the rows                 */
 #define OR_TILE_COLS 256
 #define OR_LANES 32
 
@@ -44,7 +45,8 @@ enum { OR_Q4 = 1, OR_Q6 = 2, OR_BF16 = 3 };
 /* ------------------------------------------------------------------ */
 
 /* Symbols one lane carries: two rows of 256 codes.  4-bit codes are coded
- * in pairs ([LW] "4-bit codes are coded in pairs"), so 256 pair symbols;
+ * in pairs (two adjacent 4-bit codes form one symbol, [LW] section 2), so
+ * 256 pair symbols;
  * 6-bit codes and bf16 exponent indices are coded singly, so 512. */
 int or_symbols_per_lane(int kind) { return kind == OR_Q4 ? 256 : 512; }
 
@@ -109,8 +111,8 @@ void or_unsymbolise_q(int kind, int64_t rows, int64_t cols, const uint16_t *syms
         }
 }
 
-/* One table per matrix ([LW] "Each matrix gets one length-limited Huffman
- * table"): the histogram is taken over all symbols of the matrix. */
+/* One code table serves a whole matrix ([LW] section 2), so the histogram
+ * is taken over all symbols of the matrix. */
 void or_histogram(const uint16_t *syms, int64_t n, int n_alpha, uint64_t *counts)
 {
     for (int s = 0; s < n_alpha; s++) counts[s] = 0;
@@ -308,9 +310,9 @@ int or_compact_lengths(int n_alpha, const uint64_t *counts, uint8_t *lens)
  *   limit[L]  = (first[L] + count[L]) << (11 - L), the 11-bit peek bound
  *   offset[L] = number of symbols with a shorter code
  * and sym_sorted lists the symbols by (length, symbol).  [LW] section
- * "3 . Decode on demand" and the Fig. 3 caption: a lane compares an 11-bit
- * peek against per-length limits, then adds the code length's offset to index
- * the symbol table.  Entries at index 0 of the per-length arrays are unused. */
+ * "3 . Decode on demand" and the Fig. 3 caption: the decoder finds a code's
+ * length by comparing the next 11 stream bits with one bound per length, and
+ * finds the symbol at that length's base position plus the code's rank.  Entries at index 0 of the per-length arrays are unused. */
 int or_canonical(int n_alpha, const uint8_t *lens, uint16_t *codes,
                  uint16_t *count, uint16_t *first, uint16_t *limit, uint16_t *offset,
                  uint16_t *sym_sorted)
@@ -348,13 +350,14 @@ int or_canonical(int n_alpha, const uint8_t *lens, uint16_t *codes,
 /* ------------------------------------------------------------------ */
 /* Lane streams and the interleave.                                     */
 /* ------------------------------------------------------------------ */
-/* Reading ([LW] Fig. 3a and its caption): each lane is one Huffman stream of
- * 32-bit words; codes are packed MSB-first (bit 31 of a lane's word 0 is its
- * first bit) and the last word is zero-filled.  The 32 lanes' words are
- * interleaved so that one aligned read fetches the next word of every lane:
+/* Reading ([LW] Fig. 3a and its caption): a lane's codes form a single bit
+ * stream cut into 32-bit words; codes are packed MSB-first (bit 31 of a
+ * lane's word 0 is its first bit) and the last word is zero-filled.  The
+ * words of the 32 lanes alternate so that the j-th words of all lanes sit
+ * side by side and one aligned access reads them together:
  * word j of lane l sits at block[32*j + l], every lane being padded with zero
  * words to the tile's longest lane W_t.  tile_off[t] is the word offset of
- * tile t's block ("per-tile lane offsets let any tile start on its own"),
+ * tile t's block (an offset per tile, so each tile decodes independently),
  * tile_off[n_tiles] the total.  lane_bits receives each lane's bit count.
  *
  * With words == NULL only tile_off and lane_bits are filled (sizing pass).
@@ -541,7 +544,8 @@ double or_bf16_to_double(uint16_t b)
     return s ? -v : v;
 }
 
-/* Reading of "Scales and minimums stay as llama.cpp stores them" under the
+/* Reading of the rule that scales and minimums are kept in llama.cpp's raw
+ * form ([LW] section 2), under the
  * synthetic workloads: one fp16 (d, m) per 256-weight super-block, a
  * super-block being one tile row.  dm[t][i] = d | m << 16 for tile row i. */
 void or_pack_dm(int64_t rows, int64_t cols, const uint16_t *d, const uint16_t *m, uint32_t *dm)
@@ -609,8 +613,8 @@ uint16_t or_bf16_join(uint8_t sm, uint8_t e)
     return (uint16_t)(((uint16_t)(sm >> 7) << 15) | ((uint16_t)e << 7) | (sm & 0x7F));
 }
 
-/* Palette: the matrix's 16 most frequent exponents ([UW]: "the top 16
- * exponents cover over 99% of all weights"), ordered by (count descending,
+/* Palette: the matrix's 16 most frequent exponents ([UW]: in trained bf16
+ * weights they account for more than 99 % of the values), ordered by (count descending,
  * exponent ascending) so index 0 is the most frequent.  Returns the number
  * of distinct exponents placed (<= 16); unused entries are 0. */
 int or_bf16_palette(int64_t n, const uint16_t *w, uint8_t *palette)
@@ -634,8 +638,8 @@ int or_bf16_palette(int64_t n, const uint16_t *w, uint8_t *palette)
     return k;
 }
 
-/* Verbatim segments ([UW]: if any weight in a row of 64 has an exponent
- * outside the palette, the entire row of 64 is stored verbatim).  Reading:
+/* Verbatim segments ([UW]: a 64-weight row whose exponents are not all in
+ * the palette is kept uncompressed as a whole).  Reading:
  * segments are 64-aligned runs along a matrix row, four per tile row.
  * vb_bits[t][8] bit (4*i + s) marks segment s of tile row i; vb_start[t] is
  * the number of verbatim segments in tiles before t; `verbatim` receives the
@@ -839,4 +843,178 @@ void or_skip_ledger(int64_t cols, int bits, int64_t n_active, int batch, uint64_
     out[3] = (uint64_t)batch * (uint64_t)cols * 2;
     out[4] = (uint64_t)batch * (uint64_t)n_active * OR_SKIP_BN * 4;
     out[5] = out[1] + out[2] + out[3] + out[4];
+}
+
+/* ------------------------------------------------------------------------
+ * rANS lane coder (decode-cost ablation).  [LW] section "Decoder hardware",
+ * paragraph on Huffman against rANS: at equal rate an rANS decoder is never
+ * smaller in bits and needs more area.  The pages give no rANS format; the
+ * readings here:
+ *   - one frequency table per matrix, scaled to M = 2^11 = 2048 (so the
+ *     rarest symbol costs at most 11 bits, the Huffman code-length limit);
+ *   - one stream per tile row (64 per tile), the row's symbols in column
+ *     order (4-bit codes in pairs, low nibble the even column; 6-bit codes
+ *     singly);
+ *   - 32-bit state x in [L, 2^16 L) with L = 2^16, renormalised 16 bits at a
+ *     time; a stream is its final encoder state followed by its 16-bit
+ *     chunks in decoding order;
+ *   - a tile block is the 64 head states (word r for row r), then the chunks
+ *     as 16-bit units, chunk k of row r at unit 64*k + r (little-endian: unit
+ *     h is the low half of the block's word 64 + h/2 when h is even), every
+ *     stream zero-padded to the tile's chunk count K_t, rounded up to even
+ *     so a block is 64 + 32*K_t words.
+ * ------------------------------------------------------------------------ */
+#define OR_RANS_PB 11
+#define OR_RANS_M (1u << OR_RANS_PB)
+#define OR_RANS_L (1u << 16)
+
+/* Frequencies f[s] summing to M: f = 0 for an absent symbol, else
+ * max(1, round-half-up(count * M / total)); then, while the sum exceeds M,
+ * take 1 from the largest f above 1 (ties: the smallest symbol), and while
+ * it falls short, give 1 to the largest f (ties: the smallest symbol).
+ * cum[s] = sum of f over the symbols below s.  Returns the number of used
+ * symbols, or -1 if the sum cannot be fixed (more than M used symbols). */
+int or_rans_freqs(int n_alpha, const uint64_t *counts, uint16_t *f, uint16_t *cum)
+{
+    uint64_t total = 0;
+    int used = 0;
+    for (int s = 0; s < n_alpha; s++) { total += counts[s]; if (counts[s]) used++; }
+    int64_t sum = 0;
+    for (int s = 0; s < n_alpha; s++) {
+        if (!counts[s]) { f[s] = 0; continue; }
+        uint64_t v = (2u * counts[s] * OR_RANS_M + total) / (2u * total);
+        f[s] = (uint16_t)(v < 1 ? 1 : v);
+        sum += f[s];
+    }
+    while (sum != (int64_t)OR_RANS_M && used > 0) {
+        int pick = -1;
+        for (int s = 0; s < n_alpha; s++) {
+            if (!f[s] || (sum > (int64_t)OR_RANS_M && f[s] <= 1)) continue;
+            if (pick < 0 || f[s] > f[pick]) pick = s;
+        }
+        if (pick < 0) return -1;
+        if (sum > (int64_t)OR_RANS_M) { f[pick]--; sum--; }
+        else { f[pick]++; sum++; }
+    }
+    uint32_t c = 0;
+    for (int s = 0; s < n_alpha; s++) { cum[s] = (uint16_t)c; c += f[s]; }
+    return used;
+}
+
+/* Symbols of the 64 row streams of every tile: stream (t, r) holds tile row
+ * r, spr symbols (128 pairs or 256 singles), at syms[(t*64 + r)*spr + i]. */
+void or_rans_symbolise(int kind, int64_t rows, int64_t cols, const uint8_t *q, uint16_t *syms)
+{
+    int64_t ncb = cols / OR_TILE_COLS, nt = (rows / OR_TILE_ROWS) * ncb;
+    int spr = kind == OR_Q4 ? 128 : 256;
+    for (int64_t t = 0; t < nt; t++)
+        for (int r = 0; r < 64; r++) {
+            const uint8_t *row = q + ((t / ncb) * 64 + r) * cols + (t % ncb) * OR_TILE_COLS;
+            uint16_t *o = syms + (t * 64 + r) * spr;
+            for (int i = 0; i < spr; i++)
+                o[i] = kind == OR_Q4 ? (uint16_t)(row[2 * i] | (row[2 * i + 1] << 4)) : row[i];
+        }
+}
+
+/* Encode one stream of n symbols: *state receives the final encoder state,
+ * chunks[0 .. returned count) the 16-bit chunks in decoding order (at most
+ * one per symbol, so chunks holds n entries).  Encoding runs from the last
+ * symbol to the first; before each symbol the state is brought below
+ * 2^21 f[s] by emitting its low 16 bits, which keeps the coded state below
+ * 2^32. */
+int or_rans_encode_stream(const uint16_t *s, int n, const uint16_t *f, const uint16_t *cum,
+                          uint32_t *state, uint16_t *chunks)
+{
+    uint32_t x = OR_RANS_L;
+    int k = 0;                                     /* chunks emitted, in encoding order */
+    for (int i = n - 1; i >= 0; i--) {
+        uint32_t fs = f[s[i]];
+        uint64_t xmax = ((uint64_t)(OR_RANS_L >> OR_RANS_PB) << 16) * fs;
+        while ((uint64_t)x >= xmax) { chunks[k++] = (uint16_t)(x & 0xFFFF); x >>= 16; }
+        x = (x / fs) * OR_RANS_M + (x % fs) + cum[s[i]];
+    }
+    *state = x;
+    for (int a = 0, b = k - 1; a < b; a++, b--) {  /* decoding order = reverse of emission */
+        uint16_t tmp = chunks[a]; chunks[a] = chunks[b]; chunks[b] = tmp;
+    }
+    return k;
+}
+
+/* Encode all tiles: tile_off[nt+1] (word offsets) and, unless words is NULL
+ * (sizing pass), the blocks.  Returns the total word count. */
+int64_t or_rans_encode_tiles(int64_t nt, int spr, const uint16_t *syms, const uint16_t *f, const uint16_t *cum,
+                             uint32_t *tile_off, uint32_t *words)
+{
+    uint16_t *ch = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)spr * 64);
+    int nk[64];
+    uint32_t st[64];
+    int64_t pos = 0;
+    for (int64_t t = 0; t < nt; t++) {
+        tile_off[t] = (uint32_t)pos;
+        int kmax = 0;
+        for (int r = 0; r < 64; r++) {
+            nk[r] = or_rans_encode_stream(syms + (t * 64 + r) * spr, spr, f, cum, &st[r], ch + (size_t)r * spr);
+            if (nk[r] > kmax) kmax = nk[r];
+        }
+        int kt = (kmax + 1) & ~1;
+        if (words) {
+            uint32_t *blk = words + pos;
+            for (int64_t i = 0; i < 64 + 32 * (int64_t)kt; i++) blk[i] = 0;
+            for (int r = 0; r < 64; r++) {
+                blk[r] = st[r];
+                for (int k = 0; k < nk[r]; k++) {
+                    int64_t h = 64 * (int64_t)k + r;            /* 16-bit unit in the chunk area */
+                    blk[64 + h / 2] |= (uint32_t)ch[(size_t)r * spr + k] << (16 * (h & 1));
+                }
+            }
+        }
+        pos += 64 + 32 * (int64_t)kt;
+    }
+    tile_off[nt] = (uint32_t)pos;
+    free(ch);
+    return pos;
+}
+
+/* Decode one stream of n symbols from its head state and its chunks, chunk
+ * k at chunks[stride * k] (nchunks of them).  A symbol's slot range is found
+ * by a plain search over the cumulative frequencies.  The stream must end in
+ * state L having read only its own chunks.  Returns 0, or -1 otherwise. */
+int or_rans_decode_stream(uint32_t state, const uint16_t *chunks, int64_t stride, int64_t nchunks, int n,
+                          int n_alpha, const uint16_t *f, const uint16_t *cum, uint16_t *out)
+{
+    uint32_t x = state;
+    int64_t k = 0;
+    for (int i = 0; i < n; i++) {
+        uint32_t slot = x & (OR_RANS_M - 1);
+        int s = -1;
+        for (int c = 0; c < n_alpha; c++)
+            if (f[c] && cum[c] <= slot && slot < (uint32_t)cum[c] + f[c]) { s = c; break; }
+        if (s < 0) return -1;
+        out[i] = (uint16_t)s;
+        x = f[s] * (x >> OR_RANS_PB) + slot - cum[s];
+        while (x < OR_RANS_L) {
+            if (k >= nchunks) return -1;
+            x = (x << 16) | chunks[stride * k];
+            k++;
+        }
+    }
+    return x == OR_RANS_L ? 0 : -1;
+}
+
+/* Decode all tiles back to symbols.  Returns 0, or -1 if any stream fails.
+ * The chunk area is read through a 16-bit view of the little-endian words. */
+int or_rans_decode_tiles(int64_t nt, int spr, int n_alpha, const uint16_t *f, const uint16_t *cum,
+                         const uint32_t *tile_off, const uint32_t *words, uint16_t *syms)
+{
+    for (int64_t t = 0; t < nt; t++) {
+        const uint32_t *blk = words + tile_off[t];
+        int64_t nw = (int64_t)tile_off[t + 1] - tile_off[t];
+        if (nw < 64 || (nw - 64) % 32) return -1;
+        int64_t kt = (nw - 64) / 32;
+        const uint16_t *area = (const uint16_t *)(blk + 64);
+        for (int r = 0; r < 64; r++)
+            if (or_rans_decode_stream(blk[r], area + r, 64, kt, spr, n_alpha, f, cum, syms + (t * 64 + r) * spr))
+                return -1;
+    }
+    return 0;
 }

@@ -44,7 +44,7 @@ def lib():
         build()
         L = C.CDLL(LIB)
         P = C.c_void_p
-        i64, i32 = C.c_int64, C.c_int
+        i64, i32, u32 = C.c_int64, C.c_int, C.c_uint32
         sig = {
             "or_symbols_per_lane": (i32, [i32]),
             "or_alphabet": (i32, [i32]),
@@ -53,6 +53,12 @@ def lib():
             "or_histogram": (None, [P, i64, i32, P]),
             "or_package_merge": (i32, [i32, P, i32, P]),
             "or_compact_lengths": (i32, [i32, P, P]),
+            "or_rans_freqs": (i32, [i32, P, P, P]),
+            "or_rans_symbolise": (None, [i32, i64, i64, P, P]),
+            "or_rans_encode_tiles": (i64, [i64, i32, P, P, P, P, P]),
+            "or_rans_decode_tiles": (i32, [i64, i32, i32, P, P, P, P, P]),
+            "or_rans_encode_stream": (i32, [P, i32, P, P, P, P]),
+            "or_rans_decode_stream": (i32, [u32, P, i64, i64, i32, i32, P, P, P]),
             "or_canonical": (i32, [i32, P, P, P, P, P, P, P]),
             "or_encode_tiles": (i64, [i64, i32, P, P, P, P, P, P]),
             "or_decode_limit": (i32, [i64, i32, P, P, P, P, P, P, P, P, P]),
@@ -372,3 +378,93 @@ def skip_ledger(cols: int, bits: int, n_active: int, batch: int) -> dict:
     lib().or_skip_ledger(cols, bits, n_active, batch, _p(out))
     return dict(zip(("words", "word_bytes", "scale_bytes", "x_bytes", "y_bytes", "total_bytes"),
                     (int(v) for v in out)))
+
+
+# ---------------------------------------------------------------- rANS lane coder (ablation)
+RANS_M = 2048
+RANS_L = 1 << 16
+
+
+def rans_freqs(counts) -> tuple:
+    counts = np.ascontiguousarray(counts, dtype=np.uint64)
+    f = np.zeros(counts.size, dtype=np.uint16)
+    cum = np.zeros(counts.size, dtype=np.uint16)
+    if lib().or_rans_freqs(counts.size, _p(counts), _p(f), _p(cum)) < 0:
+        raise ValueError("frequencies do not fit")
+    return f, cum
+
+
+def rans_symbolise(kind: int, codes: np.ndarray) -> np.ndarray:
+    R, Cc = codes.shape
+    spr = 128 if kind == Q4 else 256
+    syms = np.empty((R // 64) * (Cc // 256) * 64 * spr, dtype=np.uint16)
+    lib().or_rans_symbolise(kind, R, Cc, _p(np.ascontiguousarray(codes, np.uint8)), _p(syms))
+    return syms
+
+
+def rans_encode_stream(syms, f, cum) -> tuple:
+    """One stream: (final encoder state, 16-bit chunks in decoding order)."""
+    syms = np.ascontiguousarray(syms, np.uint16)
+    f = np.ascontiguousarray(f, np.uint16)
+    cum = np.ascontiguousarray(cum, np.uint16)
+    st = np.zeros(1, np.uint32)
+    ch = np.zeros(max(syms.size, 1), np.uint16)
+    k = lib().or_rans_encode_stream(_p(syms), syms.size, _p(f), _p(cum), _p(st), _p(ch))
+    return int(st[0]), ch[:k].copy()
+
+
+def rans_decode_stream(state, chunks, n, f, cum) -> np.ndarray:
+    """n symbols of one stream (consecutive chunks), or ValueError."""
+    chunks = np.ascontiguousarray(chunks, np.uint16)
+    if chunks.size == 0:
+        chunks = np.zeros(1, np.uint16)
+        nch = 0
+    else:
+        nch = chunks.size
+    f = np.ascontiguousarray(f, np.uint16)
+    cum = np.ascontiguousarray(cum, np.uint16)
+    out = np.zeros(max(n, 1), np.uint16)
+    if lib().or_rans_decode_stream(state, _p(chunks), 1, nch, n, f.size, _p(f), _p(cum), _p(out)) != 0:
+        raise ValueError("rANS stream does not decode to its final state")
+    return out[:n]
+
+
+def build_rans_q(kind: int, codes: np.ndarray) -> dict:
+    """rANS bundle content: frequencies, cumulative frequencies, tile offsets, words."""
+    R, Cc = codes.shape
+    spr = 128 if kind == Q4 else 256
+    nt = (R // 64) * (Cc // 256)
+    syms = rans_symbolise(kind, codes)
+    counts = histogram(syms, alphabet(kind))
+    f, cum = rans_freqs(counts)
+    tile_off = np.zeros(nt + 1, dtype=np.uint32)
+    n = lib().or_rans_encode_tiles(nt, spr, _p(syms), _p(f), _p(cum), _p(tile_off), None)
+    words = np.zeros(max(n, 1), dtype=np.uint32)
+    lib().or_rans_encode_tiles(nt, spr, _p(syms), _p(f), _p(cum), _p(tile_off), _p(words))
+    return dict(kind=kind, rows=R, cols=Cc, spr=spr, counts=counts, f=f, cum=cum, tile_off=tile_off,
+                words=words[:n], syms=syms)
+
+
+def decode_rans(b: dict) -> np.ndarray:
+    """Symbols of every stream, or ValueError for a stream that does not end in state L."""
+    nt = b["tile_off"].size - 1
+    syms = np.zeros(nt * 64 * b["spr"], dtype=np.uint16)
+    w = b["words"] if b["words"].size else np.zeros(1, np.uint32)
+    rc = lib().or_rans_decode_tiles(nt, b["spr"], b["f"].size, _p(b["f"]), _p(b["cum"]), _p(b["tile_off"]), _p(w),
+                                    _p(syms))
+    if rc != 0:
+        raise ValueError("rANS stream does not decode to its final state")
+    return syms
+
+
+def rans_unsymbolise(kind: int, rows: int, cols: int, syms: np.ndarray) -> np.ndarray:
+    """Codes [rows][cols] from the row streams (numpy; inverse of or_rans_symbolise)."""
+    spr = 128 if kind == Q4 else 256
+    s = np.asarray(syms).reshape(rows // 64, cols // 256, 64, spr)
+    if kind == Q4:
+        q = np.empty((rows // 64, cols // 256, 64, 256), dtype=np.uint8)
+        q[..., 0::2] = s & 15
+        q[..., 1::2] = s >> 4
+    else:
+        q = s.astype(np.uint8)
+    return q.transpose(0, 2, 1, 3).reshape(rows, cols)

@@ -134,8 +134,8 @@ def test_skip_zero_weights_and_unit_vector(torch, dg):
 @pytest.mark.parametrize("shape", [("page", 1024, 4096, 2, 6), ("up", 14336, 4096, 4, None),
                                    ("up40", 14336, 4096, 4, 0.4)])
 def test_skip_full_size(torch, dg, shape):
-    """The page's representative configuration (N=1024, K=4096, b=2, 6 of 16
-    tiles active) and the 14336x4096 4-bit matrix, all tiles and a 40 % list;
+    """The page's worked configuration (1024 rows, K=4096, 2-bit codes, 6 of
+    the 16 tiles active) and the 14336x4096 4-bit matrix, all tiles and a 40 % list;
     sampled listed rows against the oracle."""
     name, rows, cols, bits, act = shape
     say("skip full", name)

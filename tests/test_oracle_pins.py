@@ -345,8 +345,8 @@ def test_bf16_bit_exact_and_verbatim(frac, seed):
 
 
 def test_bf16_exponent_statistics():
-    # "Unweight": the top-16 exponents cover over 99% of a layer's weights and
-    # the exponent distribution needs about 2.6 bits
+    # "Unweight": more than 99 % of a layer's weights use one of its 16
+    # commonest exponents, whose distribution carries about 2.6 bits
     mat = synth.WORKLOADS["bf16_up_14336x4096"][0]
     w, _ = synth.gen_bf16(mat, rows=512, cols=4096)
     e = ((w >> 7) & 0xFF).ravel()
@@ -558,8 +558,8 @@ def test_skip_gemv_skips_and_touches_only_listed_tiles():
 
 
 def test_skip_ledger_page_configuration():
-    """The representative configuration of IV-C (N = 1024, K = 4096, b = 2,
-    B_N = 64, 6 of 16 tiles active): words touched n_active * WPR * B_N with
+    """IV-C's worked configuration (1024 output rows, K = 4096, 2-bit codes,
+    64-row tiles, 6 tiles of the 16 active): words touched n_active * WPR * B_N with
     WPR = K / 16 = 256, i.e. 98304 words; against a dense fp16 pass of the
     whole matrix (8 MiB) the weight words alone are 1/64 of the bytes at full
     activity (16 bits per weight -> 2) times 6/16."""
