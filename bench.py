@@ -255,6 +255,32 @@ def skip_legs(torch, dg, synth, mat, codes, d, m, x, batch, a):
     return out
 
 
+def rans_leg(torch, dg, kind, codes, a, huffman_us=None):
+    """Decode-only over the rANS twin of the same codes (lw_rans_decode), the
+    decoder ablation: time, coded bytes (words + offsets + table) and the
+    ratio to the Huffman decode-only kernel on the same matrix."""
+    rows, cols = codes.shape
+    r = dg.lw_rans_build(kind, codes)
+    coded = r["words"].nbytes + r["tile_off"].nbytes + 2 * r["freq"].nbytes
+    n = copies_for(r["words"].nbytes)
+    wd = [torch.from_numpy(r["words"].view(np.int32)).cuda() for _ in range(n)]
+    to = torch.from_numpy(r["tile_off"].view(np.int32)).cuda()
+    lut = torch.from_numpy(r["lut"].view(np.int32)).cuda()
+    out = torch.empty(rows * cols // (2 if kind == dg.LW_Q4_PAIR else 1), dtype=torch.uint8, device="cuda")
+    f = lambda i: dg.lw_rans_decode(kind, rows, cols, lut, to, wd[i], r["max_tile_words"], out)
+    nd = max(a.steps // 4, 10)
+    ms = time_graph(torch, f, n, nd, a.warmup) or time_loop(torch, f, n, nd, a.warmup)
+    sym = rows * cols // (2 if kind == dg.LW_Q4_PAIR else 1)
+    res = {"us_per_matrix": round(ms * 1e3, 3), "coded_bytes": coded,
+           "bits_per_weight": round(8 * coded / (rows * cols), 4),
+           "coded_GBs": round(coded / (ms * 1e-3) / 1e9, 2), "symbols_per_s": sym / (ms * 1e-3),
+           "max_tile_words": r["max_tile_words"]}
+    if huffman_us:
+        res["over_huffman_decode_time"] = round(ms * 1e3 / huffman_us, 3)
+    del wd
+    return res
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -364,6 +390,17 @@ def main():
         dms = time_graph(torch, dec_step, n_copies, nd, a.warmup) or time_loop(torch, dec_step, n_copies, nd, a.warmup)
         result["decode_only"] = {"us_per_matrix": round(dms * 1e3, 3),
                                  "symbols_per_s": (mat.rows * mat.cols // 2) / (dms * 1e-3)}
+        result["rans_decode_only"] = rans_leg(torch, dg, kind, codes, a, dms * 1e3)
+    if not a.no_extras and kind == dg.LW_Q6_SINGLE:
+        # decoder ablation on the first 6-bit matrix: Huffman and rANS decode-only
+        out = torch.empty(mat.rows * mat.cols, dtype=torch.uint8, device="cuda")
+        dec_step = lambda i: dg.lw_decode_only(dbs[i][0], out)
+        nd = max(a.steps // 4, 10)
+        dms = time_graph(torch, dec_step, n_copies, nd, a.warmup) or time_loop(torch, dec_step, n_copies, nd, a.warmup)
+        result["decode_only"] = {"matrix": mat.name, "us_per_matrix": round(dms * 1e3, 3),
+                                 "symbols_per_s": (mat.rows * mat.cols) / (dms * 1e-3)}
+        del out
+        result["rans_decode_only"] = rans_leg(torch, dg, kind, codes, a, dms * 1e3)
     if not a.no_extras and kind == dg.LW_Q4_PAIR and len(mats) == 1 and batch <= 4:
         result["skip_twin"] = skip_legs(torch, dg, synth, mat, codes, d, m, xs[0], batch, a)
     if not a.no_extras and len(mats) == 3 and mats[2].cols == mats[0].rows:

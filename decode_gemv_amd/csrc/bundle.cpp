@@ -840,3 +840,157 @@ extern "C" lw_status lw_skip_pack(const uint8_t *codes, int bits, int64_t rows, 
     if (bad) return lw_fail(LW_E_ARG, "code does not fit in the bit width");
     return LW_OK;
 }
+
+/* ------------------------------------------------------------------ rANS twin
+ * The rANS lane coder of the decode-cost ablation ("LazyWeights", section
+ * "Decoder hardware": Huffman against rANS).  Format: frequencies scaled to
+ * 2^11 (absent symbols 0, present ones at least 1, each its rounded share,
+ * then the largest entries nudged by one until the sum is exact), one stream
+ * per tile row with 32-bit state in [2^16, 2^32) and 16-bit renormalisation,
+ * a tile block = 64 head states then the chunks in 16-bit units, chunk k of
+ * row r at unit 64k + r, zero-padded to an even per-tile chunk count. */
+namespace {
+
+constexpr uint32_t RANS_PB = 11, RANS_M = 1u << RANS_PB, RANS_L = 1u << 16;
+
+bool rans_quantise(const std::vector<uint64_t> &hist, std::vector<uint32_t> &f)
+{
+    const size_t n = hist.size();
+    uint64_t total = 0;
+    for (uint64_t c : hist) total += c;
+    f.assign(n, 0);
+    if (!total) return false;
+    int64_t sum = 0;
+    for (size_t s = 0; s < n; s++) {
+        if (!hist[s]) continue;
+        // round(hist * M / total), halves up, never below 1
+        const uint64_t num = hist[s] * RANS_M, q = num / total, rem = num % total;
+        f[s] = std::max<uint64_t>(1, q + (2 * rem >= total ? 1 : 0));
+        sum += f[s];
+    }
+    while (sum != (int64_t)RANS_M) {
+        const bool over = sum > (int64_t)RANS_M;
+        size_t best = n;
+        for (size_t s = 0; s < n; s++) {
+            const uint32_t v = f[s];
+            if (v == 0 || (over && v == 1)) continue;
+            if (best == n || v > f[best]) best = s;                 // strict: the smaller symbol keeps a tie
+        }
+        if (best == n) return false;
+        if (over) { f[best]--; sum--; }
+        else { f[best]++; sum++; }
+    }
+    return true;
+}
+
+// Encode one row stream; chunks come out in emission order and are reversed
+// by the caller's placement.  Returns the chunk count.
+int rans_encode_row(const uint16_t *sym, int n, const uint32_t *f, const uint32_t *cum, uint32_t &state,
+                    uint16_t *chunks)
+{
+    uint32_t x = RANS_L;
+    int k = 0;
+    for (int i = n - 1; i >= 0; i--) {
+        const uint32_t fs = f[sym[i]];
+        const uint64_t bound = (uint64_t)fs << (32 - RANS_PB);    // 2^21 f: the coded state stays < 2^32
+        while (x >= bound) {
+            chunks[k++] = (uint16_t)x;
+            x >>= 16;
+        }
+        const uint32_t q = x / fs;
+        x = (q << RANS_PB) + (x - q * fs) + cum[sym[i]];
+    }
+    state = x;
+    return k;
+}
+
+}  // namespace
+
+extern "C" lw_status lw_rans_build(int kind, int64_t rows, int64_t cols, const uint8_t *codes, uint16_t *freq,
+                                   uint32_t *lut, uint32_t *tile_off, uint32_t *words, int64_t words_cap,
+                                   int64_t *n_words, int32_t *max_tile_words)
+{
+    if (!codes || !freq || !lut || !tile_off || !n_words || !max_tile_words) return lw_fail(LW_E_ARG, "null argument");
+    if (kind != LW_Q4_PAIR && kind != LW_Q6_SINGLE) return lw_fail(LW_E_ARG, "kind must be LW_Q4_PAIR or LW_Q6_SINGLE");
+    if (rows <= 0 || cols <= 0 || rows % 64 || cols % 256)
+        return lw_fail(LW_E_SHAPE, "rows must be a multiple of 64 and cols of 256");
+    const bool q4 = kind == LW_Q4_PAIR;
+    const int spr = q4 ? 128 : 256, n_alpha = q4 ? 256 : 64;
+    const int64_t ncb = cols / 256, nt = (rows / 64) * ncb;
+    if (nt > 0x7FFFFFFF) return lw_fail(LW_E_SHAPE, "too many tiles");
+    const unsigned top = q4 ? 15u : 63u;
+
+    // symbols: stream (t, r) = row r of tile t, pairs of columns (2i, 2i+1) or single codes
+    std::vector<uint16_t> syms;
+    try { syms.resize((size_t)nt * 64 * spr); } catch (...) { return lw_fail(LW_E_NOMEM, "symbol buffer"); }
+    std::atomic<int> bad(0);
+    parallel_for(rows, [&](int64_t r) {
+        const uint8_t *q = codes + r * cols;
+        for (int64_t cb = 0; cb < ncb; cb++) {
+            uint16_t *o = syms.data() + (((r >> 6) * ncb + cb) * 64 + (r & 63)) * spr;
+            const uint8_t *c = q + cb * 256;
+            for (int i = 0; i < spr; i++) {
+                const unsigned lo = q4 ? c[2 * i] : c[i], hi = q4 ? c[2 * i + 1] : 0u;
+                if (lo > top || hi > top) bad = 1;
+                o[i] = (uint16_t)(q4 ? (lo | hi << 4) : lo);
+            }
+        }
+    });
+    if (bad) return lw_fail(LW_E_ARG, "code out of range");
+
+    std::vector<uint64_t> hist(n_alpha, 0);
+    for (uint16_t s : syms) hist[s]++;
+    std::vector<uint32_t> f;
+    if (!rans_quantise(hist, f)) return lw_fail(LW_E_TABLE, "frequencies cannot be scaled to 2^11");
+    std::vector<uint32_t> cum(n_alpha + 1, 0);
+    for (int s = 0; s < n_alpha; s++) cum[s + 1] = cum[s] + f[s];
+    for (int s = 0; s < n_alpha; s++) freq[s] = (uint16_t)f[s];
+    for (int s = 0; s < n_alpha; s++)
+        for (uint32_t slot = cum[s]; slot < cum[s + 1]; slot++) {
+            lut[2 * slot] = f[s] | (uint32_t)s << 24;
+            lut[2 * slot + 1] = slot - cum[s];
+        }
+
+    // pass 1: chunk count of every tile (even), then offsets
+    std::vector<int32_t> kt((size_t)nt);
+    parallel_for(nt, [&](int64_t t) {
+        std::vector<uint16_t> ch(spr);
+        int kmax = 0;
+        for (int r = 0; r < 64; r++) {
+            uint32_t st;
+            kmax = std::max(kmax, rans_encode_row(syms.data() + (t * 64 + r) * spr, spr, f.data(), cum.data(), st,
+                                                  ch.data()));
+        }
+        kt[t] = kmax + (kmax & 1);
+    });
+    int64_t pos = 0;
+    int32_t tmax = 0;
+    for (int64_t t = 0; t < nt; t++) {
+        if (pos > 0xFFFFFFFFll) return lw_fail(LW_E_SHAPE, "word offsets exceed 32 bits");
+        tile_off[t] = (uint32_t)pos;
+        pos += 64 + 32 * (int64_t)kt[t];
+        tmax = std::max<int32_t>(tmax, 64 + 32 * kt[t]);
+    }
+    if (pos > 0xFFFFFFFFll) return lw_fail(LW_E_SHAPE, "word offsets exceed 32 bits");
+    tile_off[nt] = (uint32_t)pos;
+    *n_words = pos;
+    *max_tile_words = tmax;
+    if (!words) return LW_OK;
+    if (words_cap < pos) return lw_fail(LW_E_ARG, "words buffer too small");
+
+    // pass 2: the blocks
+    parallel_for(nt, [&](int64_t t) {
+        std::vector<uint16_t> ch(spr);
+        uint32_t *blk = words + tile_off[t];
+        std::memset(blk, 0, sizeof(uint32_t) * (size_t)(64 + 32 * (int64_t)kt[t]));
+        uint16_t *area = reinterpret_cast<uint16_t *>(blk + 64);   // little-endian 16-bit view
+        for (int r = 0; r < 64; r++) {
+            uint32_t st;
+            const int k = rans_encode_row(syms.data() + (t * 64 + r) * spr, spr, f.data(), cum.data(), st,
+                                          ch.data());
+            blk[r] = st;
+            for (int j = 0; j < k; j++) area[64 * j + r] = ch[k - 1 - j];   // the decoder reads the last emitted first
+        }
+    });
+    return LW_OK;
+}

@@ -65,6 +65,9 @@ hipError_t lw_launch_twin(const uint8_t *twin, const uint32_t *dm, int64_t rows,
                           const uint16_t *x, float *y, int batch, hipStream_t s);
 hipError_t lw_launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t lw_launch_read_probe(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
+hipError_t lw_launch_rans_decode(int spr, const uint32_t *lut, const uint32_t *tile_off, const uint32_t *words,
+                                 uint8_t *out, uint32_t *final_state, int64_t nt, int ncb, int64_t out_stride,
+                                 int max_tile_words, hipStream_t s);
 hipError_t lw_launch_skip(const uint32_t *words, const uint32_t *dm, int bits, int64_t rows, int64_t cols,
                           const int32_t *tiles, int64_t n_list, const uint16_t *x, float *y, int batch,
                           hipStream_t s);

@@ -69,6 +69,8 @@ def _load():
         "lw_skip_pack": (st, [P, i32, i64, i64, P, P, P, P]),
         "lw_skip_gemv": (st, [P, P, i32, i64, i64, P, i64, P, P, i32, P]),
         "lw_read_probe": (st, [P, C.c_size_t, P, P]),
+        "lw_rans_build": (st, [i32, i64, i64, P, P, P, P, P, i64, C.POINTER(C.c_int64), C.POINTER(C.c_int32)]),
+        "lw_rans_decode": (st, [i32, i64, i64, P, P, P, C.c_int32, P, C.c_size_t, P, P]),
         "lw_gemm_full_decode": (st, [P, P, C.c_size_t, P, P, i32, P]),
         "lw_pipeline_set": (st, [P, i32, i32, i32]),
         "lw_pipeline_get": (st, [P, i32, C.POINTER(C.c_int)]),
@@ -201,6 +203,24 @@ def lw_skip_pack(codes: np.ndarray, bits: int, d: np.ndarray, m: np.ndarray):
     return words, dm
 
 
+def lw_rans_build(kind: int, codes: np.ndarray) -> dict:
+    """rANS twin: dict(freq, lut, tile_off, words, max_tile_words) as numpy arrays / int."""
+    rows, cols = codes.shape
+    codes, pc = _np(codes, np.uint8)
+    n_alpha = 256 if kind == LW_Q4_PAIR else 64
+    freq = np.zeros(n_alpha, np.uint16)
+    lut = np.zeros(4096, np.uint32)
+    tile_off = np.zeros((rows // 64) * (cols // 256) + 1, np.uint32)
+    nw, mt = C.c_int64(), C.c_int32()
+    vp = lambda a: a.ctypes.data_as(C.c_void_p)
+    _check(_L.lw_rans_build(kind, rows, cols, pc, vp(freq), vp(lut), vp(tile_off), None, 0, C.byref(nw), C.byref(mt)))
+    words = np.zeros(max(nw.value, 4), np.uint32)
+    _check(_L.lw_rans_build(kind, rows, cols, pc, vp(freq), vp(lut), vp(tile_off), vp(words), words.size, C.byref(nw),
+                            C.byref(mt)))
+    return dict(kind=kind, rows=rows, cols=cols, freq=freq, lut=lut, tile_off=tile_off, words=words[:nw.value],
+                max_tile_words=mt.value)
+
+
 def lw_status_str(s: int) -> str:
     return _L.lw_status_str(s).decode()
 
@@ -269,6 +289,15 @@ def lw_skip_gemv(words, dm, bits: int, rows: int, cols: int, tiles, x, y, batch:
     xp = _dptr(x, "x") if n else None
     yp = _dptr(y, "y") if n else None
     _check(_L.lw_skip_gemv(wp, dp, bits, rows, cols, tp, n, xp, yp, batch, _stream(stream)))
+
+
+def lw_rans_decode(kind: int, rows: int, cols: int, lut, tile_off, words, max_tile_words: int, out,
+                   final_state=None, stream=None) -> None:
+    """Decode the rANS twin (device tensors) into out (device uint8 tensor, the lw_decode_only layout)."""
+    fp = _dptr(final_state, "final_state") if final_state is not None else None
+    _check(_L.lw_rans_decode(kind, rows, cols, _dptr(lut, "lut"), _dptr(tile_off, "tile_off"), _dptr(words, "words"),
+                             max_tile_words, _dptr(out, "out"), out.numel() * out.element_size(), fp,
+                             _stream(stream)))
 
 
 def _wbuf(wbuf):

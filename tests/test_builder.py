@@ -213,3 +213,61 @@ def test_skip_argument_rules():
     assert f(None, None, 4, 64, 200, None, 1, None, None, 1, None) == dg.LW_E_SHAPE
     assert f(None, None, 4, 64, 256, None, 1, None, None, 5, None) == dg.LW_E_ARG
     assert f(None, None, 4, 64, 256, None, 1, None, None, 1, None) == dg.LW_E_ARG     # null pointers
+
+
+@pytest.mark.parametrize("kind,law,rows,cols,seed", [
+    (dg.LW_Q4_PAIR, "normal", 192, 768, 81), (dg.LW_Q4_PAIR, "uniform", 64, 512, 82),
+    (dg.LW_Q4_PAIR, "const", 128, 256, 83), (dg.LW_Q6_SINGLE, "normal", 128, 1280, 84),
+    (dg.LW_Q4_PAIR, "laplace", 320, 2304, 85)])
+def test_rans_build_matches_oracle(kind, law, rows, cols, seed):
+    """The product's rANS builder writes the oracle's frequencies, offsets and
+    words bit for bit, and its kernel table maps every slot to the oracle's
+    symbol, frequency and slot - cum."""
+    qmax, mu, sc = (15, 7.5, 1.8) if kind == dg.LW_Q4_PAIR else (63, 31.5, 5.0)
+    if law == "laplace":
+        sc = 1.2
+    codes, _, _, _ = synth.gen_q_custom(rows, cols, seed, qmax=qmax, law=law, mu=mu, scale=sc)
+    p = dg.lw_rans_build(kind, codes)
+    o = O.build_rans_q(O.Q4 if kind == dg.LW_Q4_PAIR else O.Q6, codes)
+    assert np.array_equal(p["freq"], o["f"])
+    assert np.array_equal(p["tile_off"], o["tile_off"])
+    assert np.array_equal(p["words"], o["words"])
+    blocks = np.diff(o["tile_off"].astype(np.int64))
+    assert p["max_tile_words"] == int(blocks.max())
+    lut = p["lut"].reshape(2048, 2)
+    slot = np.arange(2048)
+    sym = np.searchsorted(o["cum"].astype(np.int64), slot, side="right") - 1
+    # the search lands on the last symbol with cum <= slot, which has f > 0
+    assert np.all(o["f"][sym] > 0)
+    assert np.array_equal(lut[:, 0] & 0xFFF, o["f"][sym])
+    assert np.array_equal(lut[:, 0] >> 24, sym)
+    assert np.array_equal(lut[:, 1], slot - o["cum"][sym])
+    assert not np.any(lut[:, 0] & 0x00FFF000)
+
+
+def test_rans_argument_rules():
+    from decode_gemv_amd import lw
+    codes = np.zeros((64, 256), np.uint8)
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_rans_build(dg.LW_BF16_EXP, codes)
+    assert e.value.status == dg.LW_E_ARG
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_rans_build(dg.LW_Q4_PAIR, np.full((64, 256), 16, np.uint8))
+    assert e.value.status == dg.LW_E_ARG
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_rans_build(dg.LW_Q4_PAIR, np.zeros((64, 200), np.uint8))
+    assert e.value.status == dg.LW_E_SHAPE
+    # words_cap below the size the sizing pass reports
+    f16, lut, to = np.zeros(256, np.uint16), np.zeros(4096, np.uint32), np.zeros(2, np.uint32)
+    nw, mt = ctypes.c_int64(), ctypes.c_int32()
+    vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    small = np.zeros(8, np.uint32)
+    assert lw._L.lw_rans_build(1, 64, 256, vp(codes), vp(f16), vp(lut), vp(to), vp(small), 8, ctypes.byref(nw),
+                               ctypes.byref(mt)) == dg.LW_E_ARG
+    # host-side checks of lw_rans_decode: each returns before any HIP call
+    f = lw._L.lw_rans_decode
+    assert f(3, 64, 256, None, None, None, 64, None, 0, None, None) == dg.LW_E_ARG         # kind
+    assert f(1, 64, 200, None, None, None, 64, None, 0, None, None) == dg.LW_E_SHAPE
+    assert f(1, 64, 256, None, None, None, 80, None, 0, None, None) == dg.LW_E_ARG         # not 64 + 32k
+    assert f(1, 64, 256, None, None, None, 64 + 32 * 129, None, 0, None, None) == dg.LW_E_ARG
+    assert f(1, 64, 256, None, None, None, 64, None, 0, None, None) == dg.LW_E_ARG         # null pointers
