@@ -181,18 +181,27 @@ def cpu_baseline(mat, codes, d, m, xb, batch, coded):
 
 def pipeline_legs(torch, dg, mat, db, a):
     """"Unweight"'s pipelines on the bf16 matrix: lw_autotune times the fused
-    kernels (batch <= 16) and full decode + library GEMM at each batch and
-    keeps the faster per batch bucket (one resident copy of the bundle, as an
-    autotuner on the target would see it)."""
+    kernels (batch <= 16), full decode + library GEMM, the exponent-only and
+    the palette transcode each + the reconstructive GEMM, and the
+    reconstructive GEMM over a palette form transcoded once (direct palette),
+    the reconstructive pipelines in every variant, at each batch, and keeps
+    the fastest per batch bucket (one resident copy of the bundle, as an
+    autotuner on the target would see it).  The direct palette's form is
+    attached to that copy for the leg and not used by the timed steps."""
     batches = [1, 4, 16, 64, 256, 1024]
     rng = np.random.default_rng(5)
     import synth
     xb = synth.f32_to_bf16_bits(rng.standard_normal((max(batches), mat.cols), dtype=np.float32))
     x = torch.from_numpy(xb.view(np.int16)).cuda()
     y = torch.empty((max(batches), mat.rows), dtype=torch.float32, device="cuda")
-    wbuf = torch.empty(mat.rows * mat.cols, dtype=torch.int16, device="cuda")
+    scratch = max(dg.lw_pipeline_scratch_bytes(db, p) for p in range(dg.LW_PIPE_COUNT))
+    wbuf = torch.empty(scratch, dtype=torch.uint8, device="cuda")
+    pbuf = torch.empty(dg.lw_pipeline_scratch_bytes(db, dg.LW_PIPE_DIRECT_PALETTE), dtype=torch.uint8,
+                       device="cuda")
+    dg.lw_bundle_attach_palette(db, pbuf)
     us = dg.lw_autotune(db, batches, x, y, wbuf, reps=10)
-    names = {dg.LW_PIPE_FUSED: "fused", dg.LW_PIPE_FULL_DECODE: "full_decode"}
+    names = {dg.LW_PIPE_FUSED: "fused", dg.LW_PIPE_FULL_DECODE: "full_decode", dg.LW_PIPE_EXPONENT: "exponent",
+             dg.LW_PIPE_PALETTE: "palette", dg.LW_PIPE_DIRECT_PALETTE: "direct_palette"}
     out = {}
     for i, b in enumerate(batches):
         row = {names[p]: (round(float(us[i, p]), 2) if us[i, p] > 0 else None) for p in names}

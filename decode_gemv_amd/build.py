@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblw.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["runtime.hip", "fused_q.hip", "bf16.hip", "mfma.hip", "twin.hip", "mlp.hip", "skip.hip", "probe.hip", "rans.hip"]
+HIP_SOURCES = ["runtime.hip", "fused_q.hip", "bf16.hip", "mfma.hip", "twin.hip", "mlp.hip", "skip.hip", "probe.hip", "rans.hip", "recon.hip"]
 CXX_SOURCES = ["bundle.cpp"]
 
 

@@ -265,6 +265,94 @@ __global__ __launch_bounds__(256) void k_decode_bf16(KArgs a)
     });
 }
 
+// Transcode for the reconstructive GEMM ("Unweight", "Four approaches to
+// using compressed weights": the runtime palette transcode and the
+// exponent-only decode).  The lane decoder runs as in k_decode_bf16 but
+// writes, instead of weights, either the 4-bit palette index of every weight
+// (EXP = false; eight columns to a 32-bit word, the lowest column in the low
+// nibble) or its exponent byte (EXP = true; four columns to a word), in a
+// tile-major layout whose word (t, g, r) holds columns of group g of tile row
+// r at t * G * 64 + g * 64 + r (G = 32 or 64 groups per tile), so that the 64
+// lanes' stores of one group are one coalesced 256-byte row.  Verbatim
+// segments keep the placeholder index 0 (or its exponent); vrank[t][s][r]
+// receives the index of segment s of tile row r in the verbatim store, or -1.
+template <int N8, int N16, bool EXP>
+__global__ __launch_bounds__(256) void k_transcode_bf16(KArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const LdsLayout L = lds_layout(1, a.max_words, true);
+    const LaneCtx c = lane_ctx(a);
+    const int S = a.max_words + 3;
+    uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
+    const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
+    const LwTabRegs tr = lw_tab_fetch<lw_compact<N16>()>(a, !EXP);   // second table: the palette index itself
+    const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
+    LwTileRegs64 tile;
+    lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
+    lw_tab_put<lw_compact<N16>()>(lds, tr, a);
+    __syncthreads();
+    if (!c.active) return;
+    lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
+    LaneDec d;
+    if (!lw_lane_init(d, lds, slots, c.l, a)) return;
+    d.u += c.half ? split : 0u;
+    const int r = 2 * c.l + c.half;                                   // tile row
+    uint32_t *o = static_cast<uint32_t *>(a.out) + (size_t)c.t * (EXP ? 64 : 32) * 64 + r;
+    struct NoAux {};
+    uint32_t acc = 0;
+    lw_decode_pipelined<N8, N16, 64, NoAux, false>(
+        d, a, [](int) { return EXP ? 0u : (LW_TPAY_HI - LW_TPAY); }, [](int) { return NoAux{}; },
+        [&](int g, int j, uint32_t pay, const NoAux &) {
+            if constexpr (EXP) {
+                acc |= (pay >> 7) << (8 * j);                         // payload: exponent << 7
+                if (j == 3) {
+                    o[g * 64] = acc;
+                    acc = 0;
+                }
+            } else {
+                acc |= pay << (4 * (4 * (g & 1) + j));                 // payload: palette index
+                if (j == 3 && (g & 1)) {
+                    o[(g >> 1) * 64] = acc;
+                    acc = 0;
+                }
+            }
+        });
+    // verbatim ranks of the tile, one row per lane (the walk is wave-uniform)
+    const uint32_t mw = a.vb_bits[(size_t)c.t * 8 + (c.lane & 7)];
+    uint32_t ord = a.vb_start[c.t];
+    int32_t v[4] = {-1, -1, -1, -1};
+    for (int w = 0; w < 8; w++) {
+        uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)mw, w);
+        while (bits) {
+            const int bit = 32 * w + __builtin_ctz(bits);
+            bits &= bits - 1u;
+            const int row = bit >> 2, seg = bit & 3;
+#pragma unroll
+            for (int q = 0; q < 4; q++) v[q] = (c.lane == row && seg == q) ? (int32_t)ord : v[q];
+            ord++;
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; q++) a.vrank[(size_t)c.t * 256 + q * 64 + c.lane] = v[q];
+}
+
+template <int N8, int N16, bool EXP>
+hipError_t launch_transcode(const KArgs &a, hipStream_t s)
+{
+    const LdsLayout L = lds_layout(1, a.max_words, true);
+    dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
+    hipError_t e = lw_allow_lds<k_transcode_bf16<N8, N16, EXP>>();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_transcode_bf16<N8, N16, EXP>), grid, dim3(256), L.total, s, a);
+    return hipGetLastError();
+}
+
+template <int N8, int N16>
+hipError_t transcode_mode(const KArgs &a, bool exponents, hipStream_t s)
+{
+    return exponents ? launch_transcode<N8, N16, true>(a, s) : launch_transcode<N8, N16, false>(a, s);
+}
+
 template <int N8, int N16, int BATCH>
 hipError_t launch_gemv(const KArgs &a, hipStream_t s)
 {
@@ -330,6 +418,20 @@ hipError_t lw_launch_decode_bf16(const KArgs &a, SadPlan p, hipStream_t s)
     case 3: return launch_decode<1, 1>(a, s);
     case 4: return launch_decode<2, 0>(a, s);
     case 5: return launch_decode<2, 1>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t lw_launch_transcode_bf16(const KArgs &a, SadPlan p, bool exponents, hipStream_t s)
+{
+    if (p.compact) return transcode_mode<1, LW_N16_COMPACT>(a, exponents, s);
+    switch (p.n8ops * 2 + p.n16ops) {
+    case 0: return transcode_mode<0, 0>(a, exponents, s);
+    case 1: return transcode_mode<0, 1>(a, exponents, s);
+    case 2: return transcode_mode<1, 0>(a, exponents, s);
+    case 3: return transcode_mode<1, 1>(a, exponents, s);
+    case 4: return transcode_mode<2, 0>(a, exponents, s);
+    case 5: return transcode_mode<2, 1>(a, exponents, s);
     }
     return hipErrorInvalidValue;
 }

@@ -26,6 +26,7 @@ struct KArgs {
     uint32_t *count;             // workspace arrival counters
     void *out;                   // decode-only output
     uint32_t *lane_bits;         // decode-only optional per-lane bit counts
+    int32_t *vrank;              // bf16 transcode: verbatim store index of each (tile, segment, row), or -1
     int64_t rows, cols;
     int32_t n_rb, n_cb, groups, batch, max_words, min_len, max_len;
     uint32_t pal0;               // bf16: exponent of palette index 0
@@ -60,11 +61,16 @@ hipError_t lw_launch_decode_q(const KArgs &a, int kind, SadPlan p, hipStream_t s
 hipError_t lw_launch_gemv_mfma(const KArgs &a, int kind, SadPlan p, int batch, hipStream_t s);
 hipError_t lw_launch_gemv_bf16(const KArgs &a, SadPlan p, int batch, hipStream_t s);
 hipError_t lw_launch_decode_bf16(const KArgs &a, SadPlan p, hipStream_t s);
+hipError_t lw_launch_transcode_bf16(const KArgs &a, SadPlan p, bool exponents, hipStream_t s);
 hipError_t lw_launch_swiglu(const float *g, const float *u, uint16_t *h, int64_t n, hipStream_t s);
 hipError_t lw_launch_twin(const uint8_t *twin, const uint32_t *dm, int64_t rows, int64_t cols,
                           const uint16_t *x, float *y, int batch, hipStream_t s);
 hipError_t lw_launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t lw_launch_read_probe(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
+hipError_t lw_launch_recon(bool exponents, const uint32_t *src, const uint32_t *sm, const int32_t *vrank,
+                           const uint32_t *vb_start, const uint16_t *verbatim, const uint8_t *palette,
+                           const uint16_t *x, float *y, int64_t rows, int64_t cols, int batch, int variant,
+                           float *part, int splits, hipStream_t s);
 hipError_t lw_launch_rans_decode(int spr, const uint32_t *lut, const uint32_t *tile_off, const uint32_t *words,
                                  uint8_t *out, uint32_t *final_state, int64_t nt, int ncb, int64_t out_stride,
                                  int max_tile_words, hipStream_t s);

@@ -3,6 +3,7 @@
 // pick and launch the gfx950 kernels.  The library never allocates device
 // memory; PyTorch (or any caller) owns buffers and streams.
 #include <cstring>
+#include <algorithm>
 #include <map>
 #include <memory>
 #include <string>
@@ -23,6 +24,11 @@ struct lw_dev_bundle {
     lw_gputab tab;
     uint8_t *base;
     int8_t pipe[LW_NBUCKET];
+    int8_t variant[LW_NBUCKET];      // reconstructive GEMM variant of each bucket (-1: by batch)
+    const uint32_t *pal_src;         // resident palette form (lw_bundle_attach_palette), or null
+    const int32_t *pal_vrank;
+    void *pal_part;                  // partial sums of the column split, in the attached buffer
+    uint8_t palette[16];             // bf16: the exponent palette (host copy, for kernel arguments)
 };
 
 static lw_status hip_fail(hipError_t e, const char *what)
@@ -59,8 +65,16 @@ extern "C" lw_status lw_bundle_upload(const lw_bundle *b, void *dev_buf, size_t 
     std::memcpy(&db->tab, static_cast<const uint8_t *>(img) + db->h.off[LW_REG_GPUTAB], sizeof(db->tab));
     std::memcpy(&db->table, static_cast<const uint8_t *>(img) + db->h.off[LW_REG_TABLE], sizeof(db->table));
     db->base = static_cast<uint8_t *>(dev_buf);
-    for (int k = 0; k < LW_NBUCKET; k++)      // default: the fused kernels where they exist
+    for (int k = 0; k < LW_NBUCKET; k++) {    // default: the fused kernels where they exist
         db->pipe[k] = (k <= 4 || db->h.kind != LW_BF16_EXP) ? LW_PIPE_FUSED : LW_PIPE_FULL_DECODE;
+        db->variant[k] = -1;
+    }
+    db->pal_src = nullptr;
+    db->pal_vrank = nullptr;
+    db->pal_part = nullptr;
+    std::memset(db->palette, 0, sizeof(db->palette));
+    if (db->h.bytes[LW_REG_PALETTE] >= 16)
+        std::memcpy(db->palette, static_cast<const uint8_t *>(img) + db->h.off[LW_REG_PALETTE], 16);
     *out = db.release();
     return LW_OK;
 }
@@ -333,8 +347,152 @@ static lw_status blas_handle(rocblas_handle *out)
 static bool valid_pipeline(const lw_dev_bundle *db, int pipeline, int batch)
 {
     if (pipeline == LW_PIPE_FUSED) return batch <= LW_BATCH_MAX;
-    if (pipeline == LW_PIPE_FULL_DECODE) return db->h.kind == LW_BF16_EXP;
+    if (pipeline == LW_PIPE_FULL_DECODE || pipeline == LW_PIPE_EXPONENT || pipeline == LW_PIPE_PALETTE)
+        return db->h.kind == LW_BF16_EXP;
+    if (pipeline == LW_PIPE_DIRECT_PALETTE) return db->h.kind == LW_BF16_EXP && db->pal_src;
     return false;
+}
+
+// ------------------------------------------------------------------ reconstructive GEMM
+// "Unweight", "Four approaches to using compressed weights" and "How
+// reconstructive matmul works": the exponent-only and palette pipelines
+// transcode the coded exponents into a compact form (exponent bytes, or
+// 4-bit palette indices) and a matrix-core GEMM rebuilds the bf16 weights
+// on chip from that form and the bundle's sign+mantissa bytes.
+
+static uint64_t form_bytes(const lw_dev_bundle *db, int form)
+{
+    return (uint64_t)db->h.rows * db->h.cols / (form == LW_FORM_PALETTE ? 2 : 1);
+}
+
+static uint64_t vrank_bytes(const lw_dev_bundle *db) { return (uint64_t)db->h.n_tiles * 256 * 4; }
+
+static uint64_t round256(uint64_t v) { return (v + 255) & ~(uint64_t)255; }
+
+extern "C" lw_status lw_bf16_transcode(const lw_dev_bundle *db, int form, void *out, size_t out_bytes, int32_t *vrank,
+                                       size_t vrank_size, void *stream)
+{
+    if (!db || !out || !vrank) return lw_fail(LW_E_ARG, "null argument");
+    if (db->h.kind != LW_BF16_EXP) return lw_fail(LW_E_UNSUPPORTED, "transcode is for bf16 bundles");
+    if (form != LW_FORM_PALETTE && form != LW_FORM_EXPONENT) return lw_fail(LW_E_ARG, "unknown form");
+    if (out_bytes < form_bytes(db, form) || vrank_size < vrank_bytes(db))
+        return lw_fail(LW_E_ARG, "output buffer too small");
+    if (reinterpret_cast<uintptr_t>(out) % 16 || reinterpret_cast<uintptr_t>(vrank) % 16)
+        return lw_fail(LW_E_ARG, "out and vrank must be 16-byte aligned");
+    KArgs a = make_args(db);
+    a.out = out;
+    a.vrank = vrank;
+    a.pal0 = db->tab.payload[0] >> 7;
+    hipError_t e = lw_launch_transcode_bf16(a, plan_of(db, a), form == LW_FORM_EXPONENT, (hipStream_t)stream);
+    if (e == hipErrorNotSupported) return lw_fail(LW_E_UNSUPPORTED, "no transcode kernel for this table");
+    if (e != hipSuccess) return hip_fail(e, "transcode launch");
+    return LW_OK;
+}
+
+// variant by batch when the caller leaves it open: the batch tile that holds
+// the batch, up to 64 with the rows split, beyond with the batch split
+static int recon_variant_for(int batch)
+{
+    return batch <= 16 ? 0 : batch <= 32 ? 1 : batch <= 64 ? 2 : batch <= 128 ? 3 : 4;
+}
+
+// batch columns of a workgroup in each variant
+static int recon_tile(int variant) { return variant < 3 ? 16 << variant : 64 * (2 << (variant - 3)); }
+
+// bytes of partial sums the pipelines keep room for: 8 splits of 64 batch columns
+static uint64_t part_bytes(const lw_dev_bundle *db) { return (uint64_t)8 * 64 * db->h.rows * 4; }
+
+extern "C" lw_status lw_recon_gemm(const lw_dev_bundle *db, int form, const void *src, const int32_t *vrank,
+                                   const void *x, float *y, int batch, int variant, void *work, size_t work_bytes,
+                                   void *stream)
+{
+    if (!db || !src || !vrank || !x || !y) return lw_fail(LW_E_ARG, "null argument");
+    if (db->h.kind != LW_BF16_EXP) return lw_fail(LW_E_UNSUPPORTED, "reconstructive GEMM is for bf16 bundles");
+    if (form != LW_FORM_PALETTE && form != LW_FORM_EXPONENT) return lw_fail(LW_E_ARG, "unknown form");
+    if (batch < 1 || batch > LW_GEMM_BATCH_MAX) return lw_fail(LW_E_ARG, "batch must be in 1..65536");
+    if (variant < -1 || variant >= LW_RECON_VARIANTS) return lw_fail(LW_E_ARG, "unknown variant");
+    if (reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(vrank) % 4 ||
+        reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 16)
+        return lw_fail(LW_E_ARG, "src, x and y must be 16-byte aligned, vrank 4-byte aligned");
+    if (variant < 0) variant = recon_variant_for(batch);
+    // split the column blocks when the grid would leave the chip short of
+    // wavefronts (about four per SIMD wanted) and the partial sums fit `work`
+    const int64_t waves = db->h.n_rb * 4 * (((int64_t)batch + recon_tile(variant) - 1) / recon_tile(variant));
+    int splits = (int)std::min<int64_t>({(int64_t)db->h.n_cb, 8, (4096 + waves - 1) / waves});
+    if (!work || reinterpret_cast<uintptr_t>(work) % 16) splits = 1;
+    while (splits > 1 && (uint64_t)splits * batch * db->h.rows * 4 > work_bytes) splits--;
+    hipError_t e = lw_launch_recon(form == LW_FORM_EXPONENT, static_cast<const uint32_t *>(src),
+                                   dev_region<uint32_t>(db, LW_REG_SM), vrank, dev_region<uint32_t>(db, LW_REG_VB_START),
+                                   dev_region<uint16_t>(db, LW_REG_VERBATIM),
+                                   db->palette, static_cast<const uint16_t *>(x), y, db->h.rows, db->h.cols, batch,
+                                   variant, static_cast<float *>(work), splits, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "reconstructive GEMM launch");
+    return LW_OK;
+}
+
+extern "C" lw_status lw_bundle_attach_palette(lw_dev_bundle *db, void *buf, size_t bytes, void *stream)
+{
+    if (!db || !buf) return lw_fail(LW_E_ARG, "null argument");
+    if (db->h.kind != LW_BF16_EXP) return lw_fail(LW_E_UNSUPPORTED, "the palette form is for bf16 bundles");
+    const uint64_t sb = round256(form_bytes(db, LW_FORM_PALETTE));
+    if (bytes < sb + round256(vrank_bytes(db)) + part_bytes(db))
+        return lw_fail(LW_E_ARG, "buffer smaller than lw_pipeline_scratch_bytes(db, LW_PIPE_DIRECT_PALETTE)");
+    if (reinterpret_cast<uintptr_t>(buf) % 256) return lw_fail(LW_E_ARG, "buffer must be 256-byte aligned");
+    uint8_t *b = static_cast<uint8_t *>(buf);
+    lw_status st = lw_bf16_transcode(db, LW_FORM_PALETTE, b, sb, reinterpret_cast<int32_t *>(b + sb),
+                                     vrank_bytes(db), stream);
+    if (st) return st;
+    db->pal_src = reinterpret_cast<const uint32_t *>(b);
+    db->pal_vrank = reinterpret_cast<const int32_t *>(b + sb);
+    db->pal_part = b + sb + round256(vrank_bytes(db));
+    return LW_OK;
+}
+
+extern "C" size_t lw_pipeline_scratch_bytes(const lw_dev_bundle *db, int pipeline)
+{
+    if (!db || db->h.kind != LW_BF16_EXP) return 0;
+    switch (pipeline) {
+    case LW_PIPE_FULL_DECODE: return (size_t)db->h.rows * db->h.cols * 2;
+    case LW_PIPE_EXPONENT:
+        return (size_t)(round256(form_bytes(db, LW_FORM_EXPONENT)) + round256(vrank_bytes(db)) + part_bytes(db));
+    case LW_PIPE_PALETTE:
+    case LW_PIPE_DIRECT_PALETTE:
+        return (size_t)(round256(form_bytes(db, LW_FORM_PALETTE)) + round256(vrank_bytes(db)) + part_bytes(db));
+    }
+    return 0;
+}
+
+// transcode into the caller's scratch, then the reconstructive GEMM
+static lw_status transcode_gemm(const lw_dev_bundle *db, int form, void *wbuf, size_t wbuf_bytes, const void *x,
+                                float *y, int batch, int variant, void *stream)
+{
+    if (!wbuf) return lw_fail(LW_E_ARG, "null scratch buffer");
+    const uint64_t sb = round256(form_bytes(db, form)), vb = round256(vrank_bytes(db));
+    if (wbuf_bytes < sb + vb) return lw_fail(LW_E_ARG, "scratch buffer too small for the pipeline");
+    if (reinterpret_cast<uintptr_t>(wbuf) % 256) return lw_fail(LW_E_ARG, "scratch buffer must be 256-byte aligned");
+    uint8_t *b = static_cast<uint8_t *>(wbuf);
+    int32_t *vr = reinterpret_cast<int32_t *>(b + sb);
+    lw_status st = lw_bf16_transcode(db, form, b, sb, vr, vrank_bytes(db), stream);
+    if (st) return st;
+    return lw_recon_gemm(db, form, b, vr, x, y, batch, variant, b + sb + vb, wbuf_bytes - sb - vb, stream);
+}
+
+static lw_status run_pipeline(const lw_dev_bundle *db, int p, int variant, const void *x, float *y, int batch,
+                              void *wbuf, size_t wbuf_bytes, void *stream)
+{
+    switch (p) {
+    case LW_PIPE_FUSED:
+        if (batch > LW_BATCH_MAX) return lw_fail(LW_E_UNSUPPORTED, "no pipeline for this batch");
+        return lw_gemv(db, x, y, batch, stream);
+    case LW_PIPE_FULL_DECODE: return lw_gemm_full_decode(db, wbuf, wbuf_bytes, x, y, batch, stream);
+    case LW_PIPE_EXPONENT: return transcode_gemm(db, LW_FORM_EXPONENT, wbuf, wbuf_bytes, x, y, batch, variant, stream);
+    case LW_PIPE_PALETTE: return transcode_gemm(db, LW_FORM_PALETTE, wbuf, wbuf_bytes, x, y, batch, variant, stream);
+    case LW_PIPE_DIRECT_PALETTE:
+        if (!db->pal_src) return lw_fail(LW_E_UNSUPPORTED, "no palette form attached");
+        return lw_recon_gemm(db, LW_FORM_PALETTE, db->pal_src, db->pal_vrank, x, y, batch, variant, db->pal_part,
+                             (size_t)part_bytes(db), stream);
+    }
+    return lw_fail(LW_E_ARG, "unknown pipeline");
 }
 
 extern "C" lw_status lw_gemm_full_decode(const lw_dev_bundle *db, void *wbuf, size_t wbuf_bytes, const void *x,
@@ -377,7 +535,10 @@ extern "C" lw_status lw_pipeline_set(lw_dev_bundle *db, int batch_lo, int batch_
     for (int k = batch_bucket(batch_lo); k <= batch_bucket(batch_hi); k++)
         if (!valid_pipeline(db, pipeline, 1 << k))
             return lw_fail(LW_E_UNSUPPORTED, "pipeline not available for this bundle and batch");
-    for (int k = batch_bucket(batch_lo); k <= batch_bucket(batch_hi); k++) db->pipe[k] = (int8_t)pipeline;
+    for (int k = batch_bucket(batch_lo); k <= batch_bucket(batch_hi); k++) {
+        db->pipe[k] = (int8_t)pipeline;
+        db->variant[k] = -1;
+    }
     return LW_OK;
 }
 
@@ -394,12 +555,8 @@ extern "C" lw_status lw_gemm(const lw_dev_bundle *db, const void *x, float *y, i
 {
     if (!db) return lw_fail(LW_E_ARG, "null bundle");
     if (batch < 1 || batch > LW_GEMM_BATCH_MAX) return lw_fail(LW_E_ARG, "batch must be in 1..65536");
-    const int p = db->pipe[batch_bucket(batch)];
-    if (p == LW_PIPE_FUSED) {
-        if (batch > LW_BATCH_MAX) return lw_fail(LW_E_UNSUPPORTED, "no pipeline for this batch");
-        return lw_gemv(db, x, y, batch, stream);
-    }
-    return lw_gemm_full_decode(db, wbuf, wbuf_bytes, x, y, batch, stream);
+    const int k = batch_bucket(batch);
+    return run_pipeline(db, db->pipe[k], db->variant[k], x, y, batch, wbuf, wbuf_bytes, stream);
 }
 
 extern "C" lw_status lw_autotune(lw_dev_bundle *db, const int *batches, int n, void *wbuf, size_t wbuf_bytes,
@@ -423,31 +580,39 @@ extern "C" lw_status lw_autotune(lw_dev_bundle *db, const int *batches, int n, v
             break;
         }
         float best = -1.0f;
-        int best_p = -1;
+        int best_p = -1, best_v = -1;
         for (int p = 0; p < LW_PIPE_COUNT && !st; p++) {
             if (us_out) us_out[i * LW_PIPE_COUNT + p] = -1.0f;
-            if (!valid_pipeline(db, p, batch) || (p == LW_PIPE_FULL_DECODE && !wbuf)) continue;
-            auto run = [&]() {
-                return p == LW_PIPE_FUSED ? lw_gemv(db, x, y, batch, stream)
-                                          : lw_gemm_full_decode(db, wbuf, wbuf_bytes, x, y, batch, stream);
-            };
-            if ((st = run())) break;                       // warm-up (and first-use set-up)
-            hipEventRecord(e0, s);
-            for (int r = 0; r < reps && !st; r++) st = run();
-            hipEventRecord(e1, s);
-            if (st) break;
-            he = hipEventSynchronize(e1);
-            float ms = 0.f;
-            if (he == hipSuccess) he = hipEventElapsedTime(&ms, e0, e1);
-            if (he != hipSuccess) {
-                st = hip_fail(he, "timing");
-                break;
+            if (!valid_pipeline(db, p, batch)) continue;
+            if (p != LW_PIPE_FUSED && p != LW_PIPE_DIRECT_PALETTE &&
+                (!wbuf || wbuf_bytes < lw_pipeline_scratch_bytes(db, p)))
+                continue;                                  // no room for this pipeline's scratch
+            // the reconstructive GEMM pipelines are timed in every variant
+            const bool recon = p == LW_PIPE_EXPONENT || p == LW_PIPE_PALETTE || p == LW_PIPE_DIRECT_PALETTE;
+            for (int v = recon ? 0 : -1; v < (recon ? LW_RECON_VARIANTS : 0) && !st; v++) {
+                auto run = [&]() { return run_pipeline(db, p, v, x, y, batch, wbuf, wbuf_bytes, stream); };
+                if ((st = run())) break;                   // warm-up (and first-use set-up)
+                hipEventRecord(e0, s);
+                for (int r = 0; r < reps && !st; r++) st = run();
+                hipEventRecord(e1, s);
+                if (st) break;
+                he = hipEventSynchronize(e1);
+                float ms = 0.f;
+                if (he == hipSuccess) he = hipEventElapsedTime(&ms, e0, e1);
+                if (he != hipSuccess) {
+                    st = hip_fail(he, "timing");
+                    break;
+                }
+                const float us = 1000.0f * ms / (float)reps;
+                if (us_out && (us_out[i * LW_PIPE_COUNT + p] < 0 || us < us_out[i * LW_PIPE_COUNT + p]))
+                    us_out[i * LW_PIPE_COUNT + p] = us;
+                if (best < 0 || us < best) best = us, best_p = p, best_v = v;
             }
-            const float us = 1000.0f * ms / (float)reps;
-            if (us_out) us_out[i * LW_PIPE_COUNT + p] = us;
-            if (best < 0 || us < best) best = us, best_p = p;
         }
-        if (!st && best_p >= 0) db->pipe[batch_bucket(batch)] = (int8_t)best_p;
+        if (!st && best_p >= 0) {
+            db->pipe[batch_bucket(batch)] = (int8_t)best_p;
+            db->variant[batch_bucket(batch)] = (int8_t)best_v;
+        }
     }
     hipEventDestroy(e0);
     hipEventDestroy(e1);

@@ -20,7 +20,9 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "lw.h")
 
 LW_OK, LW_E_ARG, LW_E_SHAPE, LW_E_TABLE, LW_E_FORMAT, LW_E_NOMEM, LW_E_DEVICE, LW_E_UNSUPPORTED = range(8)
 LW_Q4_PAIR, LW_Q6_SINGLE, LW_BF16_EXP = 1, 2, 3
-LW_PIPE_FUSED, LW_PIPE_FULL_DECODE, LW_PIPE_COUNT = 0, 1, 2
+LW_PIPE_FUSED, LW_PIPE_FULL_DECODE, LW_PIPE_EXPONENT, LW_PIPE_PALETTE, LW_PIPE_DIRECT_PALETTE, LW_PIPE_COUNT = range(6)
+LW_FORM_PALETTE, LW_FORM_EXPONENT = 0, 1
+LW_RECON_VARIANTS = 5
 (LW_REG_TABLE, LW_REG_GPUTAB, LW_REG_TILE_OFF, LW_REG_WORDS, LW_REG_DM, LW_REG_PALETTE, LW_REG_SM,
  LW_REG_VB_BITS, LW_REG_VB_START, LW_REG_VERBATIM, LW_REG_SPLIT, LW_REG_WORK, LW_REG_COUNT) = range(13)
 
@@ -69,6 +71,10 @@ def _load():
         "lw_skip_pack": (st, [P, i32, i64, i64, P, P, P, P]),
         "lw_skip_gemv": (st, [P, P, i32, i64, i64, P, i64, P, P, i32, P]),
         "lw_read_probe": (st, [P, C.c_size_t, P, P]),
+        "lw_bf16_transcode": (st, [P, i32, P, C.c_size_t, P, C.c_size_t, P]),
+        "lw_recon_gemm": (st, [P, i32, P, P, P, P, i32, i32, P, C.c_size_t, P]),
+        "lw_bundle_attach_palette": (st, [P, P, C.c_size_t, P]),
+        "lw_pipeline_scratch_bytes": (C.c_size_t, [P, i32]),
         "lw_rans_build": (st, [i32, i64, i64, P, P, P, P, P, i64, C.POINTER(C.c_int64), C.POINTER(C.c_int32)]),
         "lw_rans_decode": (st, [i32, i64, i64, P, P, P, C.c_int32, P, C.c_size_t, P, P]),
         "lw_gemm_full_decode": (st, [P, P, C.c_size_t, P, P, i32, P]),
@@ -322,6 +328,29 @@ def lw_pipeline_get(db: DevBundle, batch: int) -> int:
 def lw_gemm(db: DevBundle, x, y, batch: int, wbuf=None, stream=None) -> None:
     wp, wn = _wbuf(wbuf)
     _check(_L.lw_gemm(db.ptr, _dptr(x, "x"), _dptr(y, "y"), batch, wp, wn, _stream(stream)))
+
+
+def lw_bf16_transcode(db: DevBundle, form: int, out, vrank, stream=None) -> None:
+    """Transcode the coded exponents into the palette or exponent form (device tensors)."""
+    _check(_L.lw_bf16_transcode(db.ptr, form, _dptr(out, "out"), out.numel() * out.element_size(),
+                                _dptr(vrank, "vrank"), vrank.numel() * vrank.element_size(), _stream(stream)))
+
+
+def lw_recon_gemm(db: DevBundle, form: int, src, vrank, x, y, batch: int, variant: int = -1, work=None,
+                  stream=None) -> None:
+    wp, wn = _wbuf(work)
+    _check(_L.lw_recon_gemm(db.ptr, form, _dptr(src, "src"), _dptr(vrank, "vrank"), _dptr(x, "x"), _dptr(y, "y"),
+                            batch, variant, wp, wn, _stream(stream)))
+
+
+def lw_bundle_attach_palette(db: DevBundle, buf, stream=None) -> None:
+    """Transcode into buf once and keep it with the bundle (the buffer is held by db from here on)."""
+    _check(_L.lw_bundle_attach_palette(db.ptr, _dptr(buf, "buf"), buf.numel() * buf.element_size(), _stream(stream)))
+    db.palette_buf = buf
+
+
+def lw_pipeline_scratch_bytes(db: DevBundle, pipeline: int) -> int:
+    return int(_L.lw_pipeline_scratch_bytes(db.ptr, pipeline))
 
 
 def lw_autotune(db: DevBundle, batches, x, y, wbuf=None, reps: int = 10, stream=None) -> np.ndarray:

@@ -63,8 +63,23 @@ typedef enum {
 typedef enum {
     LW_PIPE_FUSED = 0,         /* decode on chip inside the GEMV (lw_gemv); batch 1..16 */
     LW_PIPE_FULL_DECODE = 1,   /* decode the weights into memory, then a library GEMM (bf16 bundles) */
-    LW_PIPE_COUNT = 2
+    LW_PIPE_EXPONENT = 2,      /* decode the exponent bytes only, then the reconstructive GEMM (bf16) */
+    LW_PIPE_PALETTE = 3,       /* transcode to 4-bit palette indices, then the reconstructive GEMM (bf16) */
+    LW_PIPE_DIRECT_PALETTE = 4,/* the reconstructive GEMM over a palette form transcoded once at load (bf16) */
+    LW_PIPE_COUNT = 5
 } lw_pipeline;
+
+/* Compact forms the reconstructive GEMM rebuilds bf16 weights from. */
+typedef enum {
+    LW_FORM_PALETTE = 0,       /* 4-bit palette index per weight */
+    LW_FORM_EXPONENT = 1       /* exponent byte per weight */
+} lw_form;
+
+/* Variants of the reconstructive GEMM: 0, 1, 2 = each wavefront of a
+ * workgroup multiplies 16 of its 64 rows with 16, 32 or 64 batch columns;
+ * 3, 4 = each multiplies all 64 rows (rebuilt once, shared through LDS) with
+ * a quarter of 128 or 256 batch columns. */
+enum { LW_RECON_VARIANTS = 5 };
 
 typedef struct lw_bundle lw_bundle;          /* host bundle: opaque, owned by the library */
 typedef struct lw_dev_bundle lw_dev_bundle;  /* host-side descriptor of an uploaded bundle */
@@ -319,24 +334,81 @@ lw_status lw_swiglu(const float *gate, const float *up, uint16_t *h, int64_t n, 
 lw_status lw_gemm_full_decode(const lw_dev_bundle *db, void *wbuf, size_t wbuf_bytes, const void *x, float *y,
                               int batch, void *stream);
 
+/* Transcode a bf16 bundle's coded exponents into a compact form for the
+ * reconstructive GEMM ("Unweight", "Four approaches to using compressed
+ * weights": the exponent-only decode and the runtime palette transcode,
+ * which write one byte or half a byte per weight where full decode writes
+ * two).  The bundle's lane decoder
+ * runs unchanged; the form is laid out tile-major, word (t, g, r) at
+ * t*G*64 + g*64 + r for tile t, column group g and tile row r:
+ *   LW_FORM_PALETTE : G = 32 groups of 8 columns, 8 indices a word, the
+ *                     lowest column in the low nibble; rows*cols/2 bytes
+ *   LW_FORM_EXPONENT: G = 64 groups of 4 columns, 4 exponent bytes a word,
+ *                     the lowest column in the low byte; rows*cols bytes
+ * Weights of a verbatim segment carry the placeholder (palette index 0).
+ *   vrank: device int32 [n_tiles][4][64]: entry (t, s, r) = the index in the
+ *          bundle's verbatim store of segment s of tile row r, or -1;
+ *          n_tiles*1024 bytes
+ * out and vrank 16-byte aligned.  Errors: LW_E_ARG, LW_E_UNSUPPORTED (not
+ * a bf16 bundle), LW_E_DEVICE. */
+lw_status lw_bf16_transcode(const lw_dev_bundle *db, int form, void *out, size_t out_bytes, int32_t *vrank,
+                            size_t vrank_bytes, void *stream);
+
+/* Reconstructive GEMM ("Unweight", "How reconstructive matmul works"):
+ * y = W x for batch columns of x, the bf16 weights rebuilt on chip from
+ * the form `src` (lw_bf16_transcode's layout), the bundle's sign+mantissa
+ * bytes and, where vrank names one, a verbatim segment's stored values, and
+ * fed to the matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
+ *   x: device bf16 [batch][cols]; y: device fp32 [batch][rows], overwritten
+ *   1 <= batch <= 65536; variant 0..LW_RECON_VARIANTS-1, or -1 for one
+ *   chosen by batch.  src, x, y 16-byte aligned, vrank 4-byte aligned.
+ *   work/work_bytes: optional device scratch (16-byte aligned) for partial
+ *   sums: when the grid would be short of wavefronts, the column blocks are
+ *   split up to 8 ways (as far as splits * batch * rows * 4 bytes fit) and
+ *   a second kernel adds the partials in split order.
+ * The sums run in a fixed order: results are deterministic.
+ * Errors: LW_E_ARG, LW_E_UNSUPPORTED, LW_E_DEVICE. */
+lw_status lw_recon_gemm(const lw_dev_bundle *db, int form, const void *src, const int32_t *vrank, const void *x,
+                        float *y, int batch, int variant, void *work, size_t work_bytes, void *stream);
+
+/* Transcode the bundle into the palette form once ("Unweight": the direct
+ * palette pipeline, whose weights are transcoded at load time) into `buf`
+ * (device, 256-byte aligned, at least lw_pipeline_scratch_bytes(db,
+ * LW_PIPE_DIRECT_PALETTE) bytes, caller-owned and kept alive while the
+ * bundle is used) and keep it with the bundle for LW_PIPE_DIRECT_PALETTE.
+ * Errors: LW_E_ARG, LW_E_UNSUPPORTED, LW_E_DEVICE. */
+lw_status lw_bundle_attach_palette(lw_dev_bundle *db, void *buf, size_t bytes, void *stream);
+
+/* Bytes of caller scratch (wbuf of lw_gemm and lw_autotune) a pipeline needs
+ * on this bundle (0 for the fused pipeline), or for LW_PIPE_DIRECT_PALETTE
+ * the size of lw_bundle_attach_palette's buffer. */
+size_t lw_pipeline_scratch_bytes(const lw_dev_bundle *db, int pipeline);
+
 /* Set the pipeline (lw_pipeline) of the buckets holding batch_lo..batch_hi.
  * Errors: LW_E_ARG, LW_E_UNSUPPORTED (the pipeline does not serve that batch
  * or bundle kind). */
 lw_status lw_pipeline_set(lw_dev_bundle *db, int batch_lo, int batch_hi, int pipeline);
 lw_status lw_pipeline_get(const lw_dev_bundle *db, int batch, int *pipeline);
 
-/* y = W x through the pipeline the bundle's table names for this batch.
- * wbuf/wbuf_bytes serve full decode (may be NULL/0 while the table picks the
- * fused pipeline).  Errors: as lw_gemv and lw_gemm_full_decode. */
+/* y = W x through the pipeline the bundle's table names for this batch (and,
+ * for the reconstructive pipelines, the variant the autotuner chose there).
+ * wbuf/wbuf_bytes is the caller's scratch for full decode, the exponent-only
+ * and the palette pipelines (lw_pipeline_scratch_bytes; 256-byte aligned
+ * for the latter two; may be NULL/0 while the table picks the fused or the
+ * direct palette pipeline).  Errors: as the pipelines'. */
 lw_status lw_gemm(const lw_dev_bundle *db, const void *x, float *y, int batch, void *wbuf, size_t wbuf_bytes,
                   void *stream);
 
 /* Measure every available pipeline at each of the n batch sizes (one warm-up
  * call, then `reps` timed calls between HIP events on `stream`, synchronised
- * here) and set each batch's bucket to the fastest.  x and y must hold the
- * largest batch.  us_out (optional, host float [n][LW_PIPE_COUNT]) receives
- * the microseconds per call, -1 where a pipeline does not apply.  wbuf = NULL
- * leaves full decode out.  Errors: LW_E_ARG and those of the pipelines. */
+ * here; the reconstructive pipelines in each variant) and set each batch's
+ * bucket to the fastest pipeline and variant ("Unweight", "Autotuning the
+ * configuration space").  x and y must hold the largest batch.  us_out
+ * (optional, host float [n][LW_PIPE_COUNT]) receives the microseconds per
+ * call (the best variant's), -1 where a pipeline does not apply.  A pipeline
+ * whose scratch does not fit wbuf is left out (wbuf = NULL: all of them but
+ * the fused and the direct palette pipelines).
+ * Errors: LW_E_ARG and those of the pipelines. */
 lw_status lw_autotune(lw_dev_bundle *db, const int *batches, int n, void *wbuf, size_t wbuf_bytes, const void *x,
                       float *y, int reps, void *stream, float *us_out);
 

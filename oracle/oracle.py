@@ -468,3 +468,62 @@ def rans_unsymbolise(kind: int, rows: int, cols: int, syms: np.ndarray) -> np.nd
     else:
         q = s.astype(np.uint8)
     return q.transpose(0, 2, 1, 3).reshape(rows, cols)
+
+
+# ---------------------------------------------------------------- bf16 compact forms (reconstructive GEMM)
+def transcode_forms(b: dict, w: np.ndarray) -> dict:
+    """The compact forms of a bf16 matrix that the reconstructive GEMM reads
+    ("Unweight", "Four approaches to using compressed weights"), from the
+    oracle's palette and verbatim map (numpy):
+      palette : u32 [t][32][64], 8 palette indices of columns 8g..8g+7 of tile
+                row r, the lowest column in the low nibble
+      exponent: u32 [t][64][64], 4 exponent bytes of columns 4g..4g+3
+      vrank   : i32 [t][4][64], the verbatim store index of segment s of tile
+                row r (tiles in order, then rows, then segments), or -1
+    Weights of a verbatim segment carry palette index 0 (the placeholder)."""
+    R, Cc = w.shape
+    nrb, ncb = R // 64, Cc // 256
+    pal = b["palette"][:b["n_pal"]]
+    idx_of = np.full(256, -1, dtype=np.int64)
+    idx_of[pal] = np.arange(pal.size)
+    idx = idx_of[(w.astype(np.int64) >> 7) & 0xFF]                       # [R][C]
+    bits = np.unpackbits(b["vb_bits"].view(np.uint8), bitorder="little").reshape(nrb, ncb, 64, 4)  # [rb][cb][i][s]
+    verb = bits.transpose(0, 2, 1, 3).reshape(R, Cc // 64).astype(bool)   # [row][64-column segment]
+    idx[np.repeat(verb, 64, axis=1)] = 0
+    if np.any(idx < 0):
+        raise ValueError("an exponent outside the palette lies outside every verbatim segment")
+    I = idx.reshape(nrb, 64, ncb, 32, 8)
+    palw = (I << (4 * np.arange(8))).sum(-1).astype(np.uint32)         # [rb][i][cb][g]
+    E = b["palette"][idx].astype(np.int64).reshape(nrb, 64, ncb, 64, 4)
+    expw = (E << (8 * np.arange(4))).sum(-1).astype(np.uint32)
+    # rank of each set bit of a tile's map, in map order, offset by the tile's start
+    flat = bits.reshape(nrb * ncb, 256)
+    rank = np.cumsum(flat, axis=1) - flat + b["vb_start"][:-1, None].astype(np.int64)
+    vr = np.where(flat == 1, rank, -1).reshape(nrb * ncb, 64, 4).transpose(0, 2, 1)   # [t][s][i]
+    return dict(palette=palw.transpose(0, 2, 3, 1).reshape(-1), exponent=expw.transpose(0, 2, 3, 1).reshape(-1),
+                vrank=vr.astype(np.int32).reshape(-1))
+
+
+def rebuild_from_form(b: dict, forms: dict, form: str, rows: int, cols: int) -> np.ndarray:
+    """bf16 weights [rows][cols] rebuilt from a compact form, the sign+mantissa
+    stream and the verbatim store (numpy; the check that a form is complete)."""
+    nrb, ncb = rows // 64, cols // 256
+    if form == "palette":
+        wv = forms["palette"].reshape(nrb, ncb, 32, 64).astype(np.int64)
+        nib = (wv[..., None] >> (4 * np.arange(8))) & 15                  # [rb][cb][g][i][j]
+        e = b["palette"][nib.transpose(0, 3, 1, 2, 4).reshape(rows, cols)].astype(np.int64)
+    else:
+        wv = forms["exponent"].reshape(nrb, ncb, 64, 64).astype(np.int64)
+        by = (wv[..., None] >> (8 * np.arange(4))) & 255
+        e = by.transpose(0, 3, 1, 2, 4).reshape(rows, cols)
+    smw = b["sm"].reshape(nrb, ncb, 2, 64, 32).astype(np.int64)           # [rb][cb][i&1][g4][i>>1]
+    smb = (smw[..., None] >> (8 * np.arange(4))) & 255                     # [..][g4][i>>1][j]
+    smb = smb.transpose(0, 4, 2, 1, 3, 5).reshape(nrb, 64, ncb, 256)      # [rb][i>>1][i&1][cb][g4 j]
+    sm = smb.reshape(rows, cols)
+    out = ((sm >> 7) << 15) | (e << 7) | (sm & 0x7F)
+    vr = forms["vrank"].reshape(nrb, ncb, 4, 64)
+    for rb, cb, s, i in zip(*np.nonzero(vr >= 0)):
+        v = int(vr[rb, cb, s, i])
+        r, c0 = 64 * rb + i, 256 * cb + 64 * s
+        out[r, c0:c0 + 64] = b["verbatim"][64 * v:64 * v + 64]
+    return out.astype(np.uint16)

@@ -271,3 +271,14 @@ def test_rans_argument_rules():
     assert f(1, 64, 256, None, None, None, 80, None, 0, None, None) == dg.LW_E_ARG         # not 64 + 32k
     assert f(1, 64, 256, None, None, None, 64 + 32 * 129, None, 0, None, None) == dg.LW_E_ARG
     assert f(1, 64, 256, None, None, None, 64, None, 0, None, None) == dg.LW_E_ARG         # null pointers
+
+
+def test_recon_argument_rules():
+    """Host-side checks of the transcode and reconstructive GEMM entry points
+    (each returns before any HIP call)."""
+    from decode_gemv_amd import lw
+    assert lw._L.lw_bf16_transcode(None, 0, None, 0, None, 0, None) == dg.LW_E_ARG
+    assert lw._L.lw_recon_gemm(None, 0, None, None, None, None, 1, -1, None, 0, None) == dg.LW_E_ARG
+    assert lw._L.lw_bundle_attach_palette(None, None, 0, None) == dg.LW_E_ARG
+    assert lw._L.lw_pipeline_scratch_bytes(None, dg.LW_PIPE_PALETTE) == 0
+    assert dg.LW_PIPE_COUNT == 5 and dg.LW_RECON_VARIANTS == 5
