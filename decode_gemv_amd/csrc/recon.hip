@@ -191,9 +191,8 @@ __global__ __launch_bounds__(256, 2) void k_recon(RArgs a)
 #pragma unroll
         for (int n = 0; n < NB; n++) acc[f][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // sources three steps ahead (ring of four); activations three steps ahead
-    // as well, or one when they take four or more registers sets a thread
-    constexpr int XD = XV >= 4 ? 2 : 4, XL = XD - 1;
+    // sources and activations requested three steps ahead (rings of four)
+    constexpr int XD = 4, XL = XD - 1;
     Src<EXP> sw[4];
     u32x4 xr[XD][XV];
     src_load(kbeg, sw[0]);
