@@ -402,13 +402,15 @@ static int recon_tile(int variant) { return variant < 3 ? 16 << variant : 64 * (
 // bytes of partial sums the pipelines keep room for: 8 splits of 64 batch columns
 static uint64_t part_bytes(const lw_dev_bundle *db) { return (uint64_t)8 * 64 * db->h.rows * 4; }
 
-extern "C" lw_status lw_recon_gemm(const lw_dev_bundle *db, int form, const void *src, const int32_t *vrank,
-                                   const void *x, float *y, int batch, int variant, void *work, size_t work_bytes,
-                                   void *stream)
+extern "C" lw_status lw_recon_gemm(const lw_dev_bundle *db, int form, const void *src, size_t src_bytes,
+                                   const int32_t *vrank, size_t vrank_size, const void *x, float *y, int batch,
+                                   int variant, void *work, size_t work_bytes, void *stream)
 {
     if (!db || !src || !vrank || !x || !y) return lw_fail(LW_E_ARG, "null argument");
     if (db->h.kind != LW_BF16_EXP) return lw_fail(LW_E_UNSUPPORTED, "reconstructive GEMM is for bf16 bundles");
     if (form != LW_FORM_PALETTE && form != LW_FORM_EXPONENT) return lw_fail(LW_E_ARG, "unknown form");
+    if (src_bytes < form_bytes(db, form) || vrank_size < vrank_bytes(db))
+        return lw_fail(LW_E_ARG, "form or rank buffer smaller than the bundle needs");
     if (batch < 1 || batch > LW_GEMM_BATCH_MAX) return lw_fail(LW_E_ARG, "batch must be in 1..65536");
     if (variant < -1 || variant >= LW_RECON_VARIANTS) return lw_fail(LW_E_ARG, "unknown variant");
     if (reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(vrank) % 4 ||
@@ -474,7 +476,8 @@ static lw_status transcode_gemm(const lw_dev_bundle *db, int form, void *wbuf, s
     int32_t *vr = reinterpret_cast<int32_t *>(b + sb);
     lw_status st = lw_bf16_transcode(db, form, b, sb, vr, vrank_bytes(db), stream);
     if (st) return st;
-    return lw_recon_gemm(db, form, b, vr, x, y, batch, variant, b + sb + vb, wbuf_bytes - sb - vb, stream);
+    return lw_recon_gemm(db, form, b, sb, vr, vrank_bytes(db), x, y, batch, variant, b + sb + vb, wbuf_bytes - sb - vb,
+                         stream);
 }
 
 static lw_status run_pipeline(const lw_dev_bundle *db, int p, int variant, const void *x, float *y, int batch,
@@ -489,8 +492,8 @@ static lw_status run_pipeline(const lw_dev_bundle *db, int p, int variant, const
     case LW_PIPE_PALETTE: return transcode_gemm(db, LW_FORM_PALETTE, wbuf, wbuf_bytes, x, y, batch, variant, stream);
     case LW_PIPE_DIRECT_PALETTE:
         if (!db->pal_src) return lw_fail(LW_E_UNSUPPORTED, "no palette form attached");
-        return lw_recon_gemm(db, LW_FORM_PALETTE, db->pal_src, db->pal_vrank, x, y, batch, variant, db->pal_part,
-                             (size_t)part_bytes(db), stream);
+        return lw_recon_gemm(db, LW_FORM_PALETTE, db->pal_src, form_bytes(db, LW_FORM_PALETTE), db->pal_vrank,
+                             vrank_bytes(db), x, y, batch, variant, db->pal_part, (size_t)part_bytes(db), stream);
     }
     return lw_fail(LW_E_ARG, "unknown pipeline");
 }
@@ -569,7 +572,7 @@ extern "C" lw_status lw_autotune(lw_dev_bundle *db, const int *batches, int n, v
     if (he != hipSuccess) return hip_fail(he, "hipEventCreate");
     he = hipEventCreate(&e1);
     if (he != hipSuccess) {
-        hipEventDestroy(e0);
+        (void)hipEventDestroy(e0);
         return hip_fail(he, "hipEventCreate");
     }
     lw_status st = LW_OK;
@@ -592,11 +595,11 @@ extern "C" lw_status lw_autotune(lw_dev_bundle *db, const int *batches, int n, v
             for (int v = recon ? 0 : -1; v < (recon ? LW_RECON_VARIANTS : 0) && !st; v++) {
                 auto run = [&]() { return run_pipeline(db, p, v, x, y, batch, wbuf, wbuf_bytes, stream); };
                 if ((st = run())) break;                   // warm-up (and first-use set-up)
-                hipEventRecord(e0, s);
-                for (int r = 0; r < reps && !st; r++) st = run();
-                hipEventRecord(e1, s);
+                he = hipEventRecord(e0, s);
+                for (int r = 0; r < reps && !st && he == hipSuccess; r++) st = run();
                 if (st) break;
-                he = hipEventSynchronize(e1);
+                if (he == hipSuccess) he = hipEventRecord(e1, s);
+                if (he == hipSuccess) he = hipEventSynchronize(e1);
                 float ms = 0.f;
                 if (he == hipSuccess) he = hipEventElapsedTime(&ms, e0, e1);
                 if (he != hipSuccess) {
@@ -614,7 +617,7 @@ extern "C" lw_status lw_autotune(lw_dev_bundle *db, const int *batches, int n, v
             db->variant[batch_bucket(batch)] = (int8_t)best_v;
         }
     }
-    hipEventDestroy(e0);
-    hipEventDestroy(e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
     return st;
 }

@@ -72,7 +72,7 @@ def _load():
         "lw_skip_gemv": (st, [P, P, i32, i64, i64, P, i64, P, P, i32, P]),
         "lw_read_probe": (st, [P, C.c_size_t, P, P]),
         "lw_bf16_transcode": (st, [P, i32, P, C.c_size_t, P, C.c_size_t, P]),
-        "lw_recon_gemm": (st, [P, i32, P, P, P, P, i32, i32, P, C.c_size_t, P]),
+        "lw_recon_gemm": (st, [P, i32, P, C.c_size_t, P, C.c_size_t, P, P, i32, i32, P, C.c_size_t, P]),
         "lw_bundle_attach_palette": (st, [P, P, C.c_size_t, P]),
         "lw_pipeline_scratch_bytes": (C.c_size_t, [P, i32]),
         "lw_rans_build": (st, [i32, i64, i64, P, P, P, P, P, i64, C.POINTER(C.c_int64), C.POINTER(C.c_int32)]),
@@ -339,8 +339,9 @@ def lw_bf16_transcode(db: DevBundle, form: int, out, vrank, stream=None) -> None
 def lw_recon_gemm(db: DevBundle, form: int, src, vrank, x, y, batch: int, variant: int = -1, work=None,
                   stream=None) -> None:
     wp, wn = _wbuf(work)
-    _check(_L.lw_recon_gemm(db.ptr, form, _dptr(src, "src"), _dptr(vrank, "vrank"), _dptr(x, "x"), _dptr(y, "y"),
-                            batch, variant, wp, wn, _stream(stream)))
+    _check(_L.lw_recon_gemm(db.ptr, form, _dptr(src, "src"), src.numel() * src.element_size(), _dptr(vrank, "vrank"),
+                            vrank.numel() * vrank.element_size(), _dptr(x, "x"), _dptr(y, "y"), batch, variant, wp, wn,
+                            _stream(stream)))
 
 
 def lw_bundle_attach_palette(db: DevBundle, buf, stream=None) -> None:

@@ -356,7 +356,8 @@ lw_status lw_bf16_transcode(const lw_dev_bundle *db, int form, void *out, size_t
 
 /* Reconstructive GEMM ("Unweight", "How reconstructive matmul works"):
  * y = W x for batch columns of x, the bf16 weights rebuilt on chip from
- * the form `src` (lw_bf16_transcode's layout), the bundle's sign+mantissa
+ * the form `src` (lw_bf16_transcode's layout; src_bytes and vrank_bytes at
+ * least the sizes lw_bf16_transcode needs), the bundle's sign+mantissa
  * bytes and, where vrank names one, a verbatim segment's stored values, and
  * fed to the matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
  *   x: device bf16 [batch][cols]; y: device fp32 [batch][rows], overwritten
@@ -368,8 +369,9 @@ lw_status lw_bf16_transcode(const lw_dev_bundle *db, int form, void *out, size_t
  *   a second kernel adds the partials in split order.
  * The sums run in a fixed order: results are deterministic.
  * Errors: LW_E_ARG, LW_E_UNSUPPORTED, LW_E_DEVICE. */
-lw_status lw_recon_gemm(const lw_dev_bundle *db, int form, const void *src, const int32_t *vrank, const void *x,
-                        float *y, int batch, int variant, void *work, size_t work_bytes, void *stream);
+lw_status lw_recon_gemm(const lw_dev_bundle *db, int form, const void *src, size_t src_bytes, const int32_t *vrank,
+                        size_t vrank_bytes, const void *x, float *y, int batch, int variant, void *work,
+                        size_t work_bytes, void *stream);
 
 /* Transcode the bundle into the palette form once ("Unweight": the direct
  * palette pipeline, whose weights are transcoded at load time) into `buf`

@@ -278,7 +278,7 @@ def test_recon_argument_rules():
     (each returns before any HIP call)."""
     from decode_gemv_amd import lw
     assert lw._L.lw_bf16_transcode(None, 0, None, 0, None, 0, None) == dg.LW_E_ARG
-    assert lw._L.lw_recon_gemm(None, 0, None, None, None, None, 1, -1, None, 0, None) == dg.LW_E_ARG
+    assert lw._L.lw_recon_gemm(None, 0, None, 0, None, 0, None, None, 1, -1, None, 0, None) == dg.LW_E_ARG
     assert lw._L.lw_bundle_attach_palette(None, None, 0, None) == dg.LW_E_ARG
     assert lw._L.lw_pipeline_scratch_bytes(None, dg.LW_PIPE_PALETTE) == 0
     assert dg.LW_PIPE_COUNT == 5 and dg.LW_RECON_VARIANTS == 5
