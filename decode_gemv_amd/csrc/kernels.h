@@ -68,9 +68,9 @@ hipError_t lw_launch_twin(const uint8_t *twin, const uint32_t *dm, int64_t rows,
 hipError_t lw_launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t lw_launch_read_probe(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
 hipError_t lw_launch_recon(bool exponents, const uint32_t *src, const uint32_t *sm, const int32_t *vrank,
-                           const uint32_t *vb_start, const uint16_t *verbatim, const uint8_t *palette,
-                           const uint16_t *x, float *y, int64_t rows, int64_t cols, int batch, int variant,
-                           float *part, int splits, hipStream_t s);
+                           const uint32_t *vb_start, const uint16_t *verbatim, int64_t n_verbatim,
+                           const uint8_t *palette, const uint16_t *x, float *y, int64_t rows, int64_t cols,
+                           int batch, int variant, float *part, int splits, hipStream_t s);
 hipError_t lw_launch_rans_decode(int spr, const uint32_t *lut, const uint32_t *tile_off, const uint32_t *words,
                                  uint8_t *out, uint32_t *final_state, int64_t nt, int ncb, int64_t out_stride,
                                  int max_tile_words, hipStream_t s);

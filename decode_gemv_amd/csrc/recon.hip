@@ -59,6 +59,7 @@ struct RArgs {
     const uint32_t *sm;         // bundle sign+mantissa words [t][2][64][32]
     const int32_t *vrank;       // [t][4][64] verbatim store index, or -1
     const uint32_t *vb_start;   // [n_tiles + 1] verbatim segments before each tile
+    int64_t n_verbatim;         // segments in the verbatim store
     const uint16_t *verbatim;   // [n][64] stored bf16 segments
     const uint16_t *x;          // [batch][cols] bf16
     float *y;                   // [batch][rows]
@@ -207,10 +208,11 @@ __global__ __launch_bounds__(256, 2) void k_recon(RArgs a)
         // rebuild this step's operand of the wavefront's 16 rows
         u32x4 w = lw_rebuild8<EXP>(sw[s4].s0, EXP ? sw[s4].s1 : 0u, sw[s4].lo, sw[s4].hi, a);
         const int32_t v = sw[s4].vr;
-        if (v >= 0) {                                                    // rare: a stored segment
+        if (v >= 0 && v < a.n_verbatim) {                                // rare: a stored segment
             const uint32_t cl = 32u * (k & 7) + 8u * q;
-            w = staged ? *reinterpret_cast<const u32x4 *>(&vs[v - (int32_t)v0][cl & 63u])
-                       : *reinterpret_cast<const u32x4 *>(a.verbatim + (int64_t)v * 64 + (cl & 63u));
+            w = staged && (uint32_t)v - v0 < v1 - v0
+                    ? *reinterpret_cast<const u32x4 *>(&vs[(uint32_t)v - v0][cl & 63u])
+                    : *reinterpret_cast<const u32x4 *>(a.verbatim + (int64_t)v * 64 + (cl & 63u));
         }
         if constexpr (MODE) as[k & 1][wave][lane] = w;
         x_store(k & 1, xr[s4 % XD]);
@@ -302,11 +304,12 @@ hipError_t launch_variant(const RArgs &a, int variant, hipStream_t s)
 // variant: 0..2 = the rows split between the wavefronts, 16, 32 or 64 batch
 // columns a workgroup; 3..4 = the batch split, 128 or 256 batch columns.
 hipError_t lw_launch_recon(bool exponents, const uint32_t *src, const uint32_t *sm, const int32_t *vrank,
-                           const uint32_t *vb_start, const uint16_t *verbatim, const uint8_t *palette,
-                           const uint16_t *x, float *y, int64_t rows, int64_t cols, int batch, int variant,
-                           float *part, int splits, hipStream_t s)
+                           const uint32_t *vb_start, const uint16_t *verbatim, int64_t n_verbatim,
+                           const uint8_t *palette, const uint16_t *x, float *y, int64_t rows, int64_t cols,
+                           int batch, int variant, float *part, int splits, hipStream_t s)
 {
     RArgs a;
+    a.n_verbatim = n_verbatim;
     a.part = part;
     a.splits = splits;
     a.src = src;

@@ -425,7 +425,7 @@ extern "C" lw_status lw_recon_gemm(const lw_dev_bundle *db, int form, const void
     while (splits > 1 && (uint64_t)splits * batch * db->h.rows * 4 > work_bytes) splits--;
     hipError_t e = lw_launch_recon(form == LW_FORM_EXPONENT, static_cast<const uint32_t *>(src),
                                    dev_region<uint32_t>(db, LW_REG_SM), vrank, dev_region<uint32_t>(db, LW_REG_VB_START),
-                                   dev_region<uint16_t>(db, LW_REG_VERBATIM),
+                                   dev_region<uint16_t>(db, LW_REG_VERBATIM), db->h.n_verbatim,
                                    db->palette, static_cast<const uint16_t *>(x), y, db->h.rows, db->h.cols, batch,
                                    variant, static_cast<float *>(work), splits, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "reconstructive GEMM launch");

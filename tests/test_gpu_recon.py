@@ -136,6 +136,23 @@ def test_recon_deterministic(torch, dg):
         assert np.array_equal(ys[0], ys[1])
 
 
+def test_recon_corrupt_ranks_stay_in_bounds(torch, dg):
+    """Rank tables with entries past the store (or naming another row band's
+    segments) must not send the kernel outside the store or the staged run:
+    entries past the store are ignored, others only change values."""
+    rows, cols = 192, 768
+    w, db = setup(dg, torch, rows, cols, 451, 0.002)
+    nv = dg.lw_bundle_get_info(dg.lw_bundle_build_bf16(w))["n_verbatim"]
+    x = dev(torch, big_x(cols, 20, 452))
+    src, vr = transcode(dg, torch, db, dg.LW_FORM_PALETTE, rows, cols)
+    bad = np.random.default_rng(453).integers(-5, nv + 10 ** 6, size=vr.numel(), dtype=np.int64).astype(np.int32)
+    for variant in (0, 3):
+        y = torch.empty((20, rows), device="cuda")
+        dg.lw_recon_gemm(db, dg.LW_FORM_PALETTE, src, dev(torch, bad), x, y, 20, variant)
+        torch.cuda.synchronize()
+        assert np.all(np.isfinite(y.cpu().numpy()))
+
+
 def test_pipelines_through_the_table(torch, dg):
     """lw_gemm runs the pipeline (and variant) the table names; the direct
     palette pipeline needs an attached palette form; every pipeline agrees
