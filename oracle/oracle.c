@@ -854,15 +854,17 @@ void or_skip_ledger(int64_t cols, int bits, int64_t n_active, int batch, uint64_
  *     rarest symbol costs at most 11 bits, the Huffman code-length limit);
  *   - one stream per tile row (64 per tile), the row's symbols in column
  *     order (4-bit codes in pairs, low nibble the even column; 6-bit codes
- *     singly);
+ *     singly), or, as an option, two per row (128 per tile), one per half
+ *     of the row's columns: stream h*64 + r holds half h of row r;
  *   - 32-bit state x in [L, 2^16 L) with L = 2^16, renormalised 16 bits at a
  *     time; a stream is its final encoder state followed by its 16-bit
  *     chunks in decoding order;
- *   - a tile block is the 64 head states (word r for row r), then the chunks
- *     as 16-bit units, chunk k of row r at unit 64*k + r (little-endian: unit
- *     h is the low half of the block's word 64 + h/2 when h is even), every
- *     stream zero-padded to the tile's chunk count K_t, rounded up to even
- *     so a block is 64 + 32*K_t words.
+ *   - a tile block of ns streams is the ns head states (word s for stream
+ *     s), then the chunks as 16-bit units, chunk k of stream s at unit
+ *     ns*k + s (little-endian: unit h is the low half of the block's word
+ *     ns + h/2 when h is even), every stream zero-padded to the tile's
+ *     chunk count K_t, rounded up to even, so a block is ns + ns*K_t/2
+ *     words.
  * ------------------------------------------------------------------------ */
 #define OR_RANS_PB 11
 #define OR_RANS_M (1u << OR_RANS_PB)
@@ -940,38 +942,44 @@ int or_rans_encode_stream(const uint16_t *s, int n, const uint16_t *f, const uin
     return k;
 }
 
-/* Encode all tiles: tile_off[nt+1] (word offsets) and, unless words is NULL
- * (sizing pass), the blocks.  Returns the total word count. */
-int64_t or_rans_encode_tiles(int64_t nt, int spr, const uint16_t *syms, const uint16_t *f, const uint16_t *cum,
-                             uint32_t *tile_off, uint32_t *words)
+/* Encode all tiles: ns streams of sps symbols per tile, stream (t, s) at
+ * syms[(t*ns + s)*sps]; tile_off[nt+1] (word offsets) and, unless words is
+ * NULL (sizing pass), the blocks: the ns head states (word s for stream s),
+ * then chunk k of stream s at 16-bit unit ns*k + s, zero-padded to the
+ * tile's chunk count rounded up to even.  Returns the total word count. */
+int64_t or_rans_encode_tiles(int64_t nt, int ns, int sps, const uint16_t *syms, const uint16_t *f,
+                             const uint16_t *cum, uint32_t *tile_off, uint32_t *words)
 {
-    uint16_t *ch = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)spr * 64);
-    int nk[64];
-    uint32_t st[64];
+    uint16_t *ch = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)sps * (size_t)ns);
+    int *nk = (int *)malloc(sizeof(int) * (size_t)ns);
+    uint32_t *st = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)ns);
     int64_t pos = 0;
     for (int64_t t = 0; t < nt; t++) {
         tile_off[t] = (uint32_t)pos;
         int kmax = 0;
-        for (int r = 0; r < 64; r++) {
-            nk[r] = or_rans_encode_stream(syms + (t * 64 + r) * spr, spr, f, cum, &st[r], ch + (size_t)r * spr);
+        for (int r = 0; r < ns; r++) {
+            nk[r] = or_rans_encode_stream(syms + (t * ns + r) * sps, sps, f, cum, &st[r], ch + (size_t)r * sps);
             if (nk[r] > kmax) kmax = nk[r];
         }
         int kt = (kmax + 1) & ~1;
+        int64_t nw = ns + (int64_t)ns * kt / 2;
         if (words) {
             uint32_t *blk = words + pos;
-            for (int64_t i = 0; i < 64 + 32 * (int64_t)kt; i++) blk[i] = 0;
-            for (int r = 0; r < 64; r++) {
+            for (int64_t i = 0; i < nw; i++) blk[i] = 0;
+            for (int r = 0; r < ns; r++) {
                 blk[r] = st[r];
                 for (int k = 0; k < nk[r]; k++) {
-                    int64_t h = 64 * (int64_t)k + r;            /* 16-bit unit in the chunk area */
-                    blk[64 + h / 2] |= (uint32_t)ch[(size_t)r * spr + k] << (16 * (h & 1));
+                    int64_t h = (int64_t)ns * k + r;            /* 16-bit unit in the chunk area */
+                    blk[ns + h / 2] |= (uint32_t)ch[(size_t)r * sps + k] << (16 * (h & 1));
                 }
             }
         }
-        pos += 64 + 32 * (int64_t)kt;
+        pos += nw;
     }
     tile_off[nt] = (uint32_t)pos;
     free(ch);
+    free(nk);
+    free(st);
     return pos;
 }
 
@@ -1001,19 +1009,20 @@ int or_rans_decode_stream(uint32_t state, const uint16_t *chunks, int64_t stride
     return x == OR_RANS_L ? 0 : -1;
 }
 
-/* Decode all tiles back to symbols.  Returns 0, or -1 if any stream fails.
- * The chunk area is read through a 16-bit view of the little-endian words. */
-int or_rans_decode_tiles(int64_t nt, int spr, int n_alpha, const uint16_t *f, const uint16_t *cum,
+/* Decode all tiles back to symbols (the layout of or_rans_encode_tiles).
+ * Returns 0, or -1 if any stream fails.  The chunk area is read through a
+ * 16-bit view of the little-endian words. */
+int or_rans_decode_tiles(int64_t nt, int ns, int sps, int n_alpha, const uint16_t *f, const uint16_t *cum,
                          const uint32_t *tile_off, const uint32_t *words, uint16_t *syms)
 {
     for (int64_t t = 0; t < nt; t++) {
         const uint32_t *blk = words + tile_off[t];
         int64_t nw = (int64_t)tile_off[t + 1] - tile_off[t];
-        if (nw < 64 || (nw - 64) % 32) return -1;
-        int64_t kt = (nw - 64) / 32;
-        const uint16_t *area = (const uint16_t *)(blk + 64);
-        for (int r = 0; r < 64; r++)
-            if (or_rans_decode_stream(blk[r], area + r, 64, kt, spr, n_alpha, f, cum, syms + (t * 64 + r) * spr))
+        if (nw < ns || (nw - ns) % (ns / 2)) return -1;
+        int64_t kt = (nw - ns) / (ns / 2);
+        const uint16_t *area = (const uint16_t *)(blk + ns);
+        for (int r = 0; r < ns; r++)
+            if (or_rans_decode_stream(blk[r], area + r, ns, kt, sps, n_alpha, f, cum, syms + (t * ns + r) * sps))
                 return -1;
     }
     return 0;

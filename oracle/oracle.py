@@ -55,8 +55,8 @@ def lib():
             "or_compact_lengths": (i32, [i32, P, P]),
             "or_rans_freqs": (i32, [i32, P, P, P]),
             "or_rans_symbolise": (None, [i32, i64, i64, P, P]),
-            "or_rans_encode_tiles": (i64, [i64, i32, P, P, P, P, P]),
-            "or_rans_decode_tiles": (i32, [i64, i32, i32, P, P, P, P, P]),
+            "or_rans_encode_tiles": (i64, [i64, i32, i32, P, P, P, P, P]),
+            "or_rans_decode_tiles": (i32, [i64, i32, i32, i32, P, P, P, P, P]),
             "or_rans_encode_stream": (i32, [P, i32, P, P, P, P]),
             "or_rans_decode_stream": (i32, [u32, P, i64, i64, i32, i32, P, P, P]),
             "or_canonical": (i32, [i32, P, P, P, P, P, P, P]),
@@ -429,38 +429,46 @@ def rans_decode_stream(state, chunks, n, f, cum) -> np.ndarray:
     return out[:n]
 
 
-def build_rans_q(kind: int, codes: np.ndarray) -> dict:
-    """rANS bundle content: frequencies, cumulative frequencies, tile offsets, words."""
+def build_rans_q(kind: int, codes: np.ndarray, halves: int = 1) -> dict:
+    """rANS bundle content: frequencies, cumulative frequencies, tile offsets,
+    words, and the streams' symbols [t][ns][sps] (ns = 64 * halves streams a
+    tile, sps symbols a stream; with two halves, stream h*64 + r is half h of
+    row r)."""
     R, Cc = codes.shape
     spr = 128 if kind == Q4 else 256
     nt = (R // 64) * (Cc // 256)
-    syms = rans_symbolise(kind, codes)
+    rows = rans_symbolise(kind, codes)                                   # [t][64][spr]
+    sps = spr // halves
+    syms = np.ascontiguousarray(rows.reshape(nt, 64, halves, sps).transpose(0, 2, 1, 3)).reshape(-1)
     counts = histogram(syms, alphabet(kind))
     f, cum = rans_freqs(counts)
+    ns = 64 * halves
     tile_off = np.zeros(nt + 1, dtype=np.uint32)
-    n = lib().or_rans_encode_tiles(nt, spr, _p(syms), _p(f), _p(cum), _p(tile_off), None)
+    n = lib().or_rans_encode_tiles(nt, ns, sps, _p(syms), _p(f), _p(cum), _p(tile_off), None)
     words = np.zeros(max(n, 1), dtype=np.uint32)
-    lib().or_rans_encode_tiles(nt, spr, _p(syms), _p(f), _p(cum), _p(tile_off), _p(words))
-    return dict(kind=kind, rows=R, cols=Cc, spr=spr, counts=counts, f=f, cum=cum, tile_off=tile_off,
-                words=words[:n], syms=syms)
+    lib().or_rans_encode_tiles(nt, ns, sps, _p(syms), _p(f), _p(cum), _p(tile_off), _p(words))
+    return dict(kind=kind, rows=R, cols=Cc, spr=spr, halves=halves, ns=ns, sps=sps, counts=counts, f=f, cum=cum,
+                tile_off=tile_off, words=words[:n], syms=syms)
 
 
 def decode_rans(b: dict) -> np.ndarray:
-    """Symbols of every stream, or ValueError for a stream that does not end in state L."""
+    """Symbols of every stream ([t][ns][sps]), or ValueError for a stream that does not end in state L."""
     nt = b["tile_off"].size - 1
-    syms = np.zeros(nt * 64 * b["spr"], dtype=np.uint16)
+    syms = np.zeros(nt * b["ns"] * b["sps"], dtype=np.uint16)
     w = b["words"] if b["words"].size else np.zeros(1, np.uint32)
-    rc = lib().or_rans_decode_tiles(nt, b["spr"], b["f"].size, _p(b["f"]), _p(b["cum"]), _p(b["tile_off"]), _p(w),
-                                    _p(syms))
+    rc = lib().or_rans_decode_tiles(nt, b["ns"], b["sps"], b["f"].size, _p(b["f"]), _p(b["cum"]), _p(b["tile_off"]),
+                                    _p(w), _p(syms))
     if rc != 0:
         raise ValueError("rANS stream does not decode to its final state")
     return syms
 
 
-def rans_unsymbolise(kind: int, rows: int, cols: int, syms: np.ndarray) -> np.ndarray:
-    """Codes [rows][cols] from the row streams (numpy; inverse of or_rans_symbolise)."""
+def rans_unsymbolise(kind: int, rows: int, cols: int, syms: np.ndarray, halves: int = 1) -> np.ndarray:
+    """Codes [rows][cols] from the stream symbols [t][ns][sps] (numpy; inverse of build_rans_q's layout)."""
     spr = 128 if kind == Q4 else 256
-    s = np.asarray(syms).reshape(rows // 64, cols // 256, 64, spr)
+    nt = (rows // 64) * (cols // 256)
+    s = np.asarray(syms).reshape(nt, halves, 64, spr // halves).transpose(0, 2, 1, 3)
+    s = s.reshape(rows // 64, cols // 256, 64, spr)
     if kind == Q4:
         q = np.empty((rows // 64, cols // 256, 64, 256), dtype=np.uint8)
         q[..., 0::2] = s & 15

@@ -113,32 +113,36 @@ def test_corrupt_stream_is_rejected():
         O.rans_decode_stream(st, ch[:-1], syms.size, f, cum)
 
 
-@pytest.mark.parametrize("kind,law", [(O.Q4, "normal"), (O.Q4, "uniform"), (O.Q4, "const"), (O.Q6, "normal")])
-def test_tiles_round_trip_and_layout(kind, law):
+@pytest.mark.parametrize("kind,law,halves", [(O.Q4, "normal", 1), (O.Q4, "uniform", 1), (O.Q4, "const", 1),
+                                             (O.Q6, "normal", 1), (O.Q4, "normal", 2), (O.Q6, "uniform", 2)])
+def test_tiles_round_trip_and_layout(kind, law, halves):
     rows, cols = 192, 768
     qmax, mu, sc = (15, 7.5, 1.8) if kind == O.Q4 else (63, 31.5, 5.0)
     codes, _, _, _ = synth.gen_q_custom(rows, cols, 70 + kind, qmax=qmax, law=law, mu=mu, scale=sc)
-    b = O.build_rans_q(kind, codes)
-    assert np.array_equal(O.rans_unsymbolise(kind, rows, cols, O.decode_rans(b)), codes)
-    # the symbols: pairs (low nibble = even column) or single codes, by row
-    spr = 128 if kind == O.Q4 else 256
-    s = b["syms"].reshape(rows // 64, cols // 256, 64, spr)
+    b = O.build_rans_q(kind, codes, halves)
+    assert np.array_equal(O.rans_unsymbolise(kind, rows, cols, O.decode_rans(b), halves), codes)
+    ns, sps = b["ns"], b["sps"]
+    assert ns == 64 * halves and sps * halves == (128 if kind == O.Q4 else 256)
+    # the symbols: pairs (low nibble = even column) or single codes, by row;
+    # stream h*64 + r of a tile holds half h of row r
+    s = b["syms"].reshape(rows // 64, cols // 256, halves, 64, sps)
     row = codes[64 + 5, 512:768]
     want = row[0::2] | (row[1::2] << 4) if kind == O.Q4 else row
-    assert np.array_equal(s[1, 2, 5], want)
+    for h in range(halves):
+        assert np.array_equal(s[1, 2, h, 5], want[h * sps:(h + 1) * sps])
     # the block of every tile, stream by stream, from the stream encoder
     words = b["words"]
     for t in range(b["tile_off"].size - 1):
         blk = words[b["tile_off"][t]:b["tile_off"][t + 1]]
-        streams = [O.rans_encode_stream(b["syms"][(t * 64 + r) * spr:(t * 64 + r + 1) * spr], b["f"], b["cum"])
-                   for r in range(64)]
+        streams = [O.rans_encode_stream(b["syms"][(t * ns + r) * sps:(t * ns + r + 1) * sps], b["f"], b["cum"])
+                   for r in range(ns)]
         kt = max(c.size for _, c in streams)
         kt += kt & 1
-        assert blk.size == 64 + 32 * kt
-        area = blk[64:].view(np.uint16)
+        assert blk.size == ns + ns * kt // 2
+        area = blk[ns:].view(np.uint16)
         for r, (st, ch) in enumerate(streams):
             assert blk[r] == st
-            col = area[r::64]
+            col = area[r::ns]
             assert np.array_equal(col[:ch.size], ch) and not col[ch.size:].any()
 
 
