@@ -264,19 +264,20 @@ def skip_legs(torch, dg, synth, mat, codes, d, m, x, batch, a):
     return out
 
 
-def rans_leg(torch, dg, kind, codes, a, huffman_us=None):
+def rans_leg(torch, dg, kind, codes, a, huffman_us=None, halves=1):
     """Decode-only over the rANS twin of the same codes (lw_rans_decode), the
     decoder ablation: time, coded bytes (words + offsets + table) and the
-    ratio to the Huffman decode-only kernel on the same matrix."""
+    ratio to the Huffman decode-only kernel on the same matrix; one stream a
+    tile row, or two (halves=2: two independent chains a lane)."""
     rows, cols = codes.shape
-    r = dg.lw_rans_build(kind, codes)
+    r = dg.lw_rans_build(kind, codes, halves)
     coded = r["words"].nbytes + r["tile_off"].nbytes + 2 * r["freq"].nbytes
     n = copies_for(r["words"].nbytes)
     wd = [torch.from_numpy(r["words"].view(np.int32)).cuda() for _ in range(n)]
     to = torch.from_numpy(r["tile_off"].view(np.int32)).cuda()
     lut = torch.from_numpy(r["lut"].view(np.int32)).cuda()
     out = torch.empty(rows * cols // (2 if kind == dg.LW_Q4_PAIR else 1), dtype=torch.uint8, device="cuda")
-    f = lambda i: dg.lw_rans_decode(kind, rows, cols, lut, to, wd[i], r["max_tile_words"], out)
+    f = lambda i: dg.lw_rans_decode(kind, rows, cols, lut, to, wd[i], r["max_tile_words"], out, halves=halves)
     nd = max(a.steps // 4, 10)
     ms = time_graph(torch, f, n, nd, a.warmup) or time_loop(torch, f, n, nd, a.warmup)
     sym = rows * cols // (2 if kind == dg.LW_Q4_PAIR else 1)
@@ -400,6 +401,7 @@ def main():
         result["decode_only"] = {"us_per_matrix": round(dms * 1e3, 3),
                                  "symbols_per_s": (mat.rows * mat.cols // 2) / (dms * 1e-3)}
         result["rans_decode_only"] = rans_leg(torch, dg, kind, codes, a, dms * 1e3)
+        result["rans2_decode_only"] = rans_leg(torch, dg, kind, codes, a, dms * 1e3, halves=2)
     if not a.no_extras and kind == dg.LW_Q6_SINGLE:
         # decoder ablation on the first 6-bit matrix: Huffman and rANS decode-only
         out = torch.empty(mat.rows * mat.cols, dtype=torch.uint8, device="cuda")
@@ -410,6 +412,7 @@ def main():
                                  "symbols_per_s": (mat.rows * mat.cols) / (dms * 1e-3)}
         del out
         result["rans_decode_only"] = rans_leg(torch, dg, kind, codes, a, dms * 1e3)
+        result["rans2_decode_only"] = rans_leg(torch, dg, kind, codes, a, dms * 1e3, halves=2)
     if not a.no_extras and kind == dg.LW_Q4_PAIR and len(mats) == 1 and batch <= 4:
         result["skip_twin"] = skip_legs(torch, dg, synth, mat, codes, d, m, xs[0], batch, a)
     if not a.no_extras and len(mats) == 3 and mats[2].cols == mats[0].rows:

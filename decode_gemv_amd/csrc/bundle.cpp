@@ -846,9 +846,10 @@ extern "C" lw_status lw_skip_pack(const uint8_t *codes, int bits, int64_t rows, 
  * "Decoder hardware": Huffman against rANS).  Format: frequencies scaled to
  * 2^11 (absent symbols 0, present ones at least 1, each its rounded share,
  * then the largest entries nudged by one until the sum is exact), one stream
- * per tile row with 32-bit state in [2^16, 2^32) and 16-bit renormalisation,
- * a tile block = 64 head states then the chunks in 16-bit units, chunk k of
- * row r at unit 64k + r, zero-padded to an even per-tile chunk count. */
+ * per tile row (or two, one per half of the row's columns: stream h*64 + r)
+ * with 32-bit state in [2^16, 2^32) and 16-bit renormalisation, a tile block
+ * = ns head states then the chunks in 16-bit units, chunk k of stream s at
+ * unit ns*k + s, zero-padded to an even per-tile chunk count. */
 namespace {
 
 constexpr uint32_t RANS_PB = 11, RANS_M = 1u << RANS_PB, RANS_L = 1u << 16;
@@ -883,7 +884,7 @@ bool rans_quantise(const std::vector<uint64_t> &hist, std::vector<uint32_t> &f)
     return true;
 }
 
-// Encode one row stream; chunks come out in emission order and are reversed
+// Encode one stream; chunks come out in emission order and are reversed
 // by the caller's placement.  Returns the chunk count.
 int rans_encode_row(const uint16_t *sym, int n, const uint32_t *f, const uint32_t *cum, uint32_t &state,
                     uint16_t *chunks)
@@ -906,16 +907,22 @@ int rans_encode_row(const uint16_t *sym, int n, const uint32_t *f, const uint32_
 
 }  // namespace
 
-extern "C" lw_status lw_rans_build(int kind, int64_t rows, int64_t cols, const uint8_t *codes, uint16_t *freq,
-                                   uint32_t *lut, uint32_t *tile_off, uint32_t *words, int64_t words_cap,
-                                   int64_t *n_words, int32_t *max_tile_words)
+extern "C" lw_status lw_rans_build(int kind, int64_t rows, int64_t cols, const uint8_t *codes, int halves,
+                                   uint16_t *freq, uint32_t *lut, uint32_t *tile_off, uint32_t *words,
+                                   int64_t words_cap, int64_t *n_words, int32_t *max_tile_words)
 {
     if (!codes || !freq || !lut || !tile_off || !n_words || !max_tile_words) return lw_fail(LW_E_ARG, "null argument");
     if (kind != LW_Q4_PAIR && kind != LW_Q6_SINGLE) return lw_fail(LW_E_ARG, "kind must be LW_Q4_PAIR or LW_Q6_SINGLE");
+    if (halves != 1 && halves != 2) return lw_fail(LW_E_ARG, "halves must be 1 or 2");
     if (rows <= 0 || cols <= 0 || rows % 64 || cols % 256)
         return lw_fail(LW_E_SHAPE, "rows must be a multiple of 64 and cols of 256");
     const bool q4 = kind == LW_Q4_PAIR;
     const int spr = q4 ? 128 : 256, n_alpha = q4 ? 256 : 64;
+    const int ns = 64 * halves, sps = spr / halves;          // streams a tile, symbols a stream
+    // stream s = h*64 + r of tile t: half h of row r's symbols
+    auto stream = [&](const std::vector<uint16_t> &sy, int64_t t, int st) {
+        return sy.data() + (t * 64 + (st & 63)) * spr + (st >> 6) * sps;
+    };
     const int64_t ncb = cols / 256, nt = (rows / 64) * ncb;
     if (nt > 0x7FFFFFFF) return lw_fail(LW_E_SHAPE, "too many tiles");
     const unsigned top = q4 ? 15u : 63u;
@@ -954,12 +961,11 @@ extern "C" lw_status lw_rans_build(int kind, int64_t rows, int64_t cols, const u
     // pass 1: chunk count of every tile (even), then offsets
     std::vector<int32_t> kt((size_t)nt);
     parallel_for(nt, [&](int64_t t) {
-        std::vector<uint16_t> ch(spr);
+        std::vector<uint16_t> ch(sps);
         int kmax = 0;
-        for (int r = 0; r < 64; r++) {
+        for (int r = 0; r < ns; r++) {
             uint32_t st;
-            kmax = std::max(kmax, rans_encode_row(syms.data() + (t * 64 + r) * spr, spr, f.data(), cum.data(), st,
-                                                  ch.data()));
+            kmax = std::max(kmax, rans_encode_row(stream(syms, t, r), sps, f.data(), cum.data(), st, ch.data()));
         }
         kt[t] = kmax + (kmax & 1);
     });
@@ -968,8 +974,8 @@ extern "C" lw_status lw_rans_build(int kind, int64_t rows, int64_t cols, const u
     for (int64_t t = 0; t < nt; t++) {
         if (pos > 0xFFFFFFFFll) return lw_fail(LW_E_SHAPE, "word offsets exceed 32 bits");
         tile_off[t] = (uint32_t)pos;
-        pos += 64 + 32 * (int64_t)kt[t];
-        tmax = std::max<int32_t>(tmax, 64 + 32 * kt[t]);
+        pos += ns + (int64_t)ns / 2 * kt[t];
+        tmax = std::max<int32_t>(tmax, ns + ns / 2 * kt[t]);
     }
     if (pos > 0xFFFFFFFFll) return lw_fail(LW_E_SHAPE, "word offsets exceed 32 bits");
     tile_off[nt] = (uint32_t)pos;
@@ -980,16 +986,15 @@ extern "C" lw_status lw_rans_build(int kind, int64_t rows, int64_t cols, const u
 
     // pass 2: the blocks
     parallel_for(nt, [&](int64_t t) {
-        std::vector<uint16_t> ch(spr);
+        std::vector<uint16_t> ch(sps);
         uint32_t *blk = words + tile_off[t];
-        std::memset(blk, 0, sizeof(uint32_t) * (size_t)(64 + 32 * (int64_t)kt[t]));
-        uint16_t *area = reinterpret_cast<uint16_t *>(blk + 64);   // little-endian 16-bit view
-        for (int r = 0; r < 64; r++) {
+        std::memset(blk, 0, sizeof(uint32_t) * (size_t)(ns + (int64_t)ns / 2 * kt[t]));
+        uint16_t *area = reinterpret_cast<uint16_t *>(blk + ns);   // little-endian 16-bit view
+        for (int r = 0; r < ns; r++) {
             uint32_t st;
-            const int k = rans_encode_row(syms.data() + (t * 64 + r) * spr, spr, f.data(), cum.data(), st,
-                                          ch.data());
+            const int k = rans_encode_row(stream(syms, t, r), sps, f.data(), cum.data(), st, ch.data());
             blk[r] = st;
-            for (int j = 0; j < k; j++) area[64 * j + r] = ch[k - 1 - j];   // the decoder reads the last emitted first
+            for (int j = 0; j < k; j++) area[(size_t)ns * j + r] = ch[k - 1 - j];   // the decoder reads the last emitted first
         }
     });
     return LW_OK;

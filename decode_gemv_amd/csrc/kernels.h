@@ -71,9 +71,9 @@ hipError_t lw_launch_recon(bool exponents, const uint32_t *src, const uint32_t *
                            const uint32_t *vb_start, const uint16_t *verbatim, int64_t n_verbatim,
                            const uint8_t *palette, const uint16_t *x, float *y, int64_t rows, int64_t cols,
                            int batch, int variant, float *part, int splits, hipStream_t s);
-hipError_t lw_launch_rans_decode(int spr, const uint32_t *lut, const uint32_t *tile_off, const uint32_t *words,
-                                 uint8_t *out, uint32_t *final_state, int64_t nt, int ncb, int64_t out_stride,
-                                 int max_tile_words, hipStream_t s);
+hipError_t lw_launch_rans_decode(int spr, int halves, const uint32_t *lut, const uint32_t *tile_off,
+                                 const uint32_t *words, uint8_t *out, uint32_t *final_state, int64_t nt, int ncb,
+                                 int64_t out_stride, int max_tile_words, hipStream_t s);
 hipError_t lw_launch_skip(const uint32_t *words, const uint32_t *dm, int bits, int64_t rows, int64_t cols,
                           const int32_t *tiles, int64_t n_list, const uint16_t *x, float *y, int batch,
                           hipStream_t s);

@@ -3,10 +3,13 @@
 // hardware", the comparison of Huffman and rANS decoders).
 //
 // Format (built by lw_rans_build): one frequency table per matrix scaled to
-// 2^11 slots; one stream per tile row, so a 64x256 tile is 64 streams and a
-// wavefront decodes a tile with one stream per lane; a tile block is the 64
-// head states followed by the 16-bit renormalisation chunks, chunk k of row r
-// at 16-bit unit 64k + r.
+// 2^11 slots; one stream per tile row, or two (one per half of the row's
+// columns), so a 64x256 tile is NS = 64 or 128 streams and a wavefront
+// decodes a tile with one row per lane; a tile block is the NS head states
+// followed by the 16-bit renormalisation chunks, chunk k of stream s at
+// 16-bit unit NS k + s.  With two streams a row, a lane's two chains are
+// independent and their steps interleave, hiding one chain's table latency
+// behind the other's.
 //
 // Per symbol a lane does
 //     (e, d) = lut[x mod 2^11]     e = f | symbol << 24, d = slot - cum
@@ -38,18 +41,22 @@ constexpr int LUT_SLOTS = 2048;
 constexpr int LUT_WORDS = 2 * LUT_SLOTS; // (e, d) pairs
 constexpr int GROUP = 16;                // symbols per output vector
 constexpr int CLAMP = 4;                 // symbols per clamp of the read position
-constexpr int SPARE_WORDS = 32 * (CLAMP + 1);
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-template <int SPR, int RW>
+// One tile per wavefront: H streams per row (H = 1: the whole row; H = 2:
+// one per half of its columns), lane l decoding row l's H streams, whose
+// steps are independent and interleaved.
+template <int SPR, int H, int RW>
 __global__ __launch_bounds__(64 * RW) void k_rans_decode(const u32x4 *__restrict__ lut_g,
                                                          const uint32_t *__restrict__ tile_off,
                                                          const uint32_t *__restrict__ words, uint8_t *__restrict__ out,
                                                          uint32_t *__restrict__ final_state, int64_t nt, int ncb,
                                                          int64_t out_stride, int region)
 {
+    constexpr int NS = 64 * H, SPS = SPR / H;            // streams a tile, symbols a stream
+    constexpr int SPARE = (NS / 2) * (CLAMP + 1);       // spare chunk rows, in words
     extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     u32x4 *lut4 = reinterpret_cast<u32x4 *>(lds);
@@ -62,60 +69,72 @@ __global__ __launch_bounds__(64 * RW) void k_rans_decode(const u32x4 *__restrict
     if (t < nt) {
         off = tile_off[t];
         const int64_t n = (int64_t)tile_off[t + 1] - off;
-        // a block is 64 states plus whole rows of 32 words, and must leave the spare area
-        if (n >= 64 && n <= region - SPARE_WORDS && ((n - 64) & 31) == 0) nw = (int)n;
+        // a block is NS states plus whole rows of NS/2 words, and must leave the spare area
+        if (n >= NS && n <= region - SPARE && ((n - NS) % (NS / 2)) == 0) nw = (int)n;
     }
     const u32x4 *src = reinterpret_cast<const u32x4 *>(words + off);
     for (int i = lane; i < nw / 4; i += 64) reinterpret_cast<u32x4 *>(blk)[i] = src[i];
     if (nw)
-        for (int i = lane; i < SPARE_WORDS; i += 64) blk[nw + i] = 0;
+        for (int i = lane; i < SPARE; i += 64) blk[nw + i] = 0;
     __syncthreads();
     if (!nw) return;
 
-    const uint32_t kt = (uint32_t)(nw - 64) >> 5;
+    const uint32_t kt = (uint32_t)(nw - NS) / (NS / 2);
     const u32x2 *lut = reinterpret_cast<const u32x2 *>(lds);
-    // byte address of this lane's chunk k: the block's chunk area + 128 k + 2 lane
-    const char *cbase = reinterpret_cast<const char *>(blk + 64) + 2 * lane;
-    uint32_t k = 0;
-    uint32_t x = blk[lane];
+    // byte address of stream s's chunk k: the block's chunk area + 2 (NS k + s)
+    const char *cbase = reinterpret_cast<const char *>(blk + NS);
+    uint32_t x[H], k[H];
+#pragma unroll
+    for (int h = 0; h < H; h++) {
+        x[h] = blk[64 * h + lane];
+        k[h] = 0;
+    }
     const int64_t row = (t / ncb) * 64 + lane;
-    u32x4 *dst = reinterpret_cast<u32x4 *>(out + row * out_stride + (t % ncb) * SPR);
-    for (int g = 0; g < SPR / GROUP; g++) {
-        uint32_t e[GROUP];
+    uint8_t *drow = out + row * out_stride + (t % ncb) * SPR;
+    for (int g = 0; g < SPS / GROUP; g++) {
+        uint32_t e[H][GROUP];
 #pragma unroll
         for (int j = 0; j < GROUP; j++) {
-            if (j % CLAMP == 0) k = min(k, kt);      // row kt is the first spare row
-            const u32x2 ed = lut[x & (LUT_SLOTS - 1)];
-            uint32_t c = *reinterpret_cast<const uint16_t *>(cbase + 128u * k);
-            asm volatile("" : "+v"(c));              // keep the chunk read unconditional (no branch per symbol)
-            x = (ed.x & 0xFFFFFFu) * (x >> 11) + ed.y;
-            const bool need = x < RANS_L;
-            x = need ? (x << 16) | c : x;
-            unsigned carry;
-            k = __builtin_addc(k, 0u, need ? 1u : 0u, &carry);
-            e[j] = ed.x;
-        }
-        uint32_t o[GROUP / 4];
 #pragma unroll
-        for (int q = 0; q < GROUP / 4; q++)
-            o[q] = __builtin_amdgcn_perm(e[4 * q + 1], e[4 * q], 0x0C0C0703u) |
-                   __builtin_amdgcn_perm(e[4 * q + 3], e[4 * q + 2], 0x07030C0Cu);
-        dst[g] = u32x4{o[0], o[1], o[2], o[3]};
+            for (int h = 0; h < H; h++) {
+                if (j % CLAMP == 0) k[h] = min(k[h], kt);   // row kt is the first spare row
+                const u32x2 ed = lut[x[h] & (LUT_SLOTS - 1)];
+                uint32_t c = *reinterpret_cast<const uint16_t *>(cbase + 2u * (NS * k[h] + 64 * h + lane));
+                asm volatile("" : "+v"(c));                 // keep the chunk read unconditional (no branch per symbol)
+                uint32_t xx = (ed.x & 0xFFFFFFu) * (x[h] >> 11) + ed.y;
+                const bool need = xx < RANS_L;
+                x[h] = need ? (xx << 16) | c : xx;
+                unsigned carry;
+                k[h] = __builtin_addc(k[h], 0u, need ? 1u : 0u, &carry);
+                e[h][j] = ed.x;
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < H; h++) {
+            uint32_t o[GROUP / 4];
+#pragma unroll
+            for (int q = 0; q < GROUP / 4; q++)
+                o[q] = __builtin_amdgcn_perm(e[h][4 * q + 1], e[h][4 * q], 0x0C0C0703u) |
+                       __builtin_amdgcn_perm(e[h][4 * q + 3], e[h][4 * q + 2], 0x07030C0Cu);
+            reinterpret_cast<u32x4 *>(drow + h * SPS)[g] = u32x4{o[0], o[1], o[2], o[3]};
+        }
     }
-    if (final_state) final_state[t * 64 + lane] = x;
+    if (final_state)
+#pragma unroll
+        for (int h = 0; h < H; h++) final_state[t * NS + 64 * h + lane] = x[h];
 }
 
 constexpr size_t lds_bytes(int rw, int region) { return sizeof(uint32_t) * ((size_t)LUT_WORDS + (size_t)rw * region); }
 
-template <int SPR, int RW>
+template <int SPR, int H, int RW>
 hipError_t launch_rw(const uint32_t *lut, const uint32_t *tile_off, const uint32_t *words, uint8_t *out,
                      uint32_t *final_state, int64_t nt, int ncb, int64_t out_stride, int region, hipStream_t s)
 {
-    hipError_t e = lw_allow_lds<k_rans_decode<SPR, RW>>();
+    hipError_t e = lw_allow_lds<k_rans_decode<SPR, H, RW>>();
     if (e != hipSuccess) return e;
     const int64_t grid = (nt + RW - 1) / RW;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_rans_decode<SPR, RW>), dim3((unsigned)grid), dim3(64 * RW), lds_bytes(RW, region), s,
+    hipLaunchKernelGGL((k_rans_decode<SPR, H, RW>), dim3((unsigned)grid), dim3(64 * RW), lds_bytes(RW, region), s,
                        reinterpret_cast<const u32x4 *>(lut), tile_off, words, out, final_state, nt, ncb, out_stride,
                        region);
     return hipGetLastError();
@@ -135,28 +154,32 @@ inline int pick_rw(int region, size_t cu_lds)
     return best;
 }
 
-template <int SPR>
+template <int SPR, int H>
 hipError_t launch(const uint32_t *lut, const uint32_t *tile_off, const uint32_t *words, uint8_t *out,
                   uint32_t *final_state, int64_t nt, int ncb, int64_t out_stride, int max_tile_words, hipStream_t s)
 {
-    const int region = max_tile_words + SPARE_WORDS;
+    const int region = max_tile_words + 32 * H * (CLAMP + 1);
     const int lds = lw_device_lds_bytes();
     const int rw = lds > 0 ? pick_rw(region, (size_t)lds) : 0;
-    if (rw == 4) return launch_rw<SPR, 4>(lut, tile_off, words, out, final_state, nt, ncb, out_stride, region, s);
-    if (rw == 6) return launch_rw<SPR, 6>(lut, tile_off, words, out, final_state, nt, ncb, out_stride, region, s);
-    if (rw == 8) return launch_rw<SPR, 8>(lut, tile_off, words, out, final_state, nt, ncb, out_stride, region, s);
+    if (rw == 4) return launch_rw<SPR, H, 4>(lut, tile_off, words, out, final_state, nt, ncb, out_stride, region, s);
+    if (rw == 6) return launch_rw<SPR, H, 6>(lut, tile_off, words, out, final_state, nt, ncb, out_stride, region, s);
+    if (rw == 8) return launch_rw<SPR, H, 8>(lut, tile_off, words, out, final_state, nt, ncb, out_stride, region, s);
     return hipErrorNotSupported;
 }
 
 }  // namespace
 
-hipError_t lw_launch_rans_decode(int spr, const uint32_t *lut, const uint32_t *tile_off, const uint32_t *words,
-                                 uint8_t *out, uint32_t *final_state, int64_t nt, int ncb, int64_t out_stride,
-                                 int max_tile_words, hipStream_t s)
+hipError_t lw_launch_rans_decode(int spr, int halves, const uint32_t *lut, const uint32_t *tile_off,
+                                 const uint32_t *words, uint8_t *out, uint32_t *final_state, int64_t nt, int ncb,
+                                 int64_t out_stride, int max_tile_words, hipStream_t s)
 {
-    if (spr == 128)
-        return launch<128>(lut, tile_off, words, out, final_state, nt, ncb, out_stride, max_tile_words, s);
-    if (spr == 256)
-        return launch<256>(lut, tile_off, words, out, final_state, nt, ncb, out_stride, max_tile_words, s);
+    if (spr == 128 && halves == 1)
+        return launch<128, 1>(lut, tile_off, words, out, final_state, nt, ncb, out_stride, max_tile_words, s);
+    if (spr == 256 && halves == 1)
+        return launch<256, 1>(lut, tile_off, words, out, final_state, nt, ncb, out_stride, max_tile_words, s);
+    if (spr == 128 && halves == 2)
+        return launch<128, 2>(lut, tile_off, words, out, final_state, nt, ncb, out_stride, max_tile_words, s);
+    if (spr == 256 && halves == 2)
+        return launch<256, 2>(lut, tile_off, words, out, final_state, nt, ncb, out_stride, max_tile_words, s);
     return hipErrorInvalidValue;
 }

@@ -274,18 +274,19 @@ extern "C" lw_status lw_skip_gemv(const uint32_t *words, const uint32_t *dm, int
     return LW_OK;
 }
 
-extern "C" lw_status lw_rans_decode(int kind, int64_t rows, int64_t cols, const uint32_t *lut, const uint32_t *tile_off,
-                                    const uint32_t *words, int32_t max_tile_words, void *out, size_t out_bytes,
-                                    uint32_t *final_state, void *stream)
+extern "C" lw_status lw_rans_decode(int kind, int64_t rows, int64_t cols, int halves, const uint32_t *lut,
+                                    const uint32_t *tile_off, const uint32_t *words, int32_t max_tile_words, void *out,
+                                    size_t out_bytes, uint32_t *final_state, void *stream)
 {
     if (kind != LW_Q4_PAIR && kind != LW_Q6_SINGLE) return lw_fail(LW_E_ARG, "kind must be LW_Q4_PAIR or LW_Q6_SINGLE");
     if (rows <= 0 || cols <= 0 || rows % 64 || cols % 256)
         return lw_fail(LW_E_SHAPE, "rows must be a multiple of 64 and cols of 256");
-    const int spr = kind == LW_Q4_PAIR ? 128 : 256;
+    if (halves != 1 && halves != 2) return lw_fail(LW_E_ARG, "halves must be 1 or 2");
+    const int spr = kind == LW_Q4_PAIR ? 128 : 256, ns = 64 * halves;
     const int64_t ncb = cols / 256, nt = (rows / 64) * ncb;
     if (ncb > 0x7FFFFFFF || nt > 0x7FFFFFFFll * 4) return lw_fail(LW_E_SHAPE, "too many tiles");
-    if (max_tile_words < 64 || max_tile_words > 64 + 32 * spr || (max_tile_words - 64) % 32)
-        return lw_fail(LW_E_ARG, "max_tile_words must be 64 + 32k with k <= symbols per row");
+    if (max_tile_words < ns || max_tile_words > ns + ns / 2 * (spr / halves) || (max_tile_words - ns) % (ns / 2))
+        return lw_fail(LW_E_ARG, "max_tile_words must be ns + (ns/2) k with k <= symbols per stream");
     if (!lut || !tile_off || !words || !out) return lw_fail(LW_E_ARG, "null argument");
     const int64_t stride = kind == LW_Q4_PAIR ? cols / 2 : cols;
     if (out_bytes < (size_t)(rows * stride)) return lw_fail(LW_E_ARG, "out_bytes too small");
@@ -293,8 +294,8 @@ extern "C" lw_status lw_rans_decode(int kind, int64_t rows, int64_t cols, const 
         reinterpret_cast<uintptr_t>(out) % 16 || reinterpret_cast<uintptr_t>(tile_off) % 4 ||
         reinterpret_cast<uintptr_t>(final_state) % 4)
         return lw_fail(LW_E_ARG, "lut, words and out must be 16-byte aligned, tile_off and final_state 4-byte");
-    hipError_t e = lw_launch_rans_decode(spr, lut, tile_off, words, static_cast<uint8_t *>(out), final_state, nt,
-                                         (int)ncb, stride, max_tile_words, (hipStream_t)stream);
+    hipError_t e = lw_launch_rans_decode(spr, halves, lut, tile_off, words, static_cast<uint8_t *>(out), final_state,
+                                         nt, (int)ncb, stride, max_tile_words, (hipStream_t)stream);
     if (e == hipErrorNotSupported) return lw_fail(LW_E_UNSUPPORTED, "tile blocks exceed the LDS");
     if (e != hipSuccess) return hip_fail(e, "rANS decode launch");
     return LW_OK;

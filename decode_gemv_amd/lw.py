@@ -75,8 +75,8 @@ def _load():
         "lw_recon_gemm": (st, [P, i32, P, C.c_size_t, P, C.c_size_t, P, P, i32, i32, P, C.c_size_t, P]),
         "lw_bundle_attach_palette": (st, [P, P, C.c_size_t, P]),
         "lw_pipeline_scratch_bytes": (C.c_size_t, [P, i32]),
-        "lw_rans_build": (st, [i32, i64, i64, P, P, P, P, P, i64, C.POINTER(C.c_int64), C.POINTER(C.c_int32)]),
-        "lw_rans_decode": (st, [i32, i64, i64, P, P, P, C.c_int32, P, C.c_size_t, P, P]),
+        "lw_rans_build": (st, [i32, i64, i64, P, i32, P, P, P, P, i64, C.POINTER(C.c_int64), C.POINTER(C.c_int32)]),
+        "lw_rans_decode": (st, [i32, i64, i64, i32, P, P, P, C.c_int32, P, C.c_size_t, P, P]),
         "lw_gemm_full_decode": (st, [P, P, C.c_size_t, P, P, i32, P]),
         "lw_pipeline_set": (st, [P, i32, i32, i32]),
         "lw_pipeline_get": (st, [P, i32, C.POINTER(C.c_int)]),
@@ -209,8 +209,9 @@ def lw_skip_pack(codes: np.ndarray, bits: int, d: np.ndarray, m: np.ndarray):
     return words, dm
 
 
-def lw_rans_build(kind: int, codes: np.ndarray) -> dict:
-    """rANS twin: dict(freq, lut, tile_off, words, max_tile_words) as numpy arrays / int."""
+def lw_rans_build(kind: int, codes: np.ndarray, halves: int = 1) -> dict:
+    """rANS twin (one stream per tile row, or two with halves=2): dict(freq, lut, tile_off, words,
+    max_tile_words, halves)."""
     rows, cols = codes.shape
     codes, pc = _np(codes, np.uint8)
     n_alpha = 256 if kind == LW_Q4_PAIR else 64
@@ -219,12 +220,13 @@ def lw_rans_build(kind: int, codes: np.ndarray) -> dict:
     tile_off = np.zeros((rows // 64) * (cols // 256) + 1, np.uint32)
     nw, mt = C.c_int64(), C.c_int32()
     vp = lambda a: a.ctypes.data_as(C.c_void_p)
-    _check(_L.lw_rans_build(kind, rows, cols, pc, vp(freq), vp(lut), vp(tile_off), None, 0, C.byref(nw), C.byref(mt)))
-    words = np.zeros(max(nw.value, 4), np.uint32)
-    _check(_L.lw_rans_build(kind, rows, cols, pc, vp(freq), vp(lut), vp(tile_off), vp(words), words.size, C.byref(nw),
+    _check(_L.lw_rans_build(kind, rows, cols, pc, halves, vp(freq), vp(lut), vp(tile_off), None, 0, C.byref(nw),
                             C.byref(mt)))
+    words = np.zeros(max(nw.value, 4), np.uint32)
+    _check(_L.lw_rans_build(kind, rows, cols, pc, halves, vp(freq), vp(lut), vp(tile_off), vp(words), words.size,
+                            C.byref(nw), C.byref(mt)))
     return dict(kind=kind, rows=rows, cols=cols, freq=freq, lut=lut, tile_off=tile_off, words=words[:nw.value],
-                max_tile_words=mt.value)
+                max_tile_words=mt.value, halves=halves)
 
 
 def lw_status_str(s: int) -> str:
@@ -298,12 +300,12 @@ def lw_skip_gemv(words, dm, bits: int, rows: int, cols: int, tiles, x, y, batch:
 
 
 def lw_rans_decode(kind: int, rows: int, cols: int, lut, tile_off, words, max_tile_words: int, out,
-                   final_state=None, stream=None) -> None:
+                   final_state=None, halves: int = 1, stream=None) -> None:
     """Decode the rANS twin (device tensors) into out (device uint8 tensor, the lw_decode_only layout)."""
     fp = _dptr(final_state, "final_state") if final_state is not None else None
-    _check(_L.lw_rans_decode(kind, rows, cols, _dptr(lut, "lut"), _dptr(tile_off, "tile_off"), _dptr(words, "words"),
-                             max_tile_words, _dptr(out, "out"), out.numel() * out.element_size(), fp,
-                             _stream(stream)))
+    _check(_L.lw_rans_decode(kind, rows, cols, halves, _dptr(lut, "lut"), _dptr(tile_off, "tile_off"),
+                             _dptr(words, "words"), max_tile_words, _dptr(out, "out"), out.numel() * out.element_size(),
+                             fp, _stream(stream)))
 
 
 def _wbuf(wbuf):

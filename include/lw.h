@@ -259,15 +259,18 @@ lw_status lw_skip_gemv(const uint32_t *words, const uint32_t *dm, int bits, int6
  *     present ones at least 1: each its share rounded half up, then the
  *     largest entries moved by one, ties to the smaller symbol, until the
  *     sum is exact);
- *   - one stream per tile row (64 per 64x256 tile), 128 pair symbols (Q4,
- *     low nibble the even column) or 256 single codes (Q6) in column order;
- *     32-bit state in [2^16, 2^32), renormalised 16 bits at a time;
- *   - tile t's block at word tile_off[t]: the 64 final encoder states (word
- *     r for row r), then the chunks in decoding order as 16-bit units, chunk
- *     k of row r at unit 64k + r (little-endian halves of the following
- *     words), zero-padded to the tile's chunk count rounded up to even; a
- *     block is 64 + 32k words.
+ *   - one stream per tile row (halves = 1: 64 per 64x256 tile) or two
+ *     (halves = 2: 128, stream h*64 + r holding half h of row r's columns):
+ *     128 pair symbols a row (Q4, low nibble the even column) or 256 single
+ *     codes (Q6) in column order; 32-bit state in [2^16, 2^32),
+ *     renormalised 16 bits at a time;
+ *   - tile t's block at word tile_off[t] with ns = 64*halves streams: the ns
+ *     final encoder states (word s for stream s), then the chunks in
+ *     decoding order as 16-bit units, chunk k of stream s at unit ns*k + s
+ *     (little-endian halves of the following words), zero-padded to the
+ *     tile's chunk count rounded up to even; a block is ns + (ns/2)k words.
  *   kind  : LW_Q4_PAIR or LW_Q6_SINGLE; codes: host [rows][cols], one code a byte
+ *   halves: 1 or 2
  *   freq  : host out u16 [256] (Q4) or [64] (Q6)
  *   lut   : host out u32 [4096], derived for the kernel: slot s -> the pair
  *           (f | symbol << 24, s - cum) at [2s], [2s + 1]
@@ -276,25 +279,27 @@ lw_status lw_skip_gemv(const uint32_t *words, const uint32_t *dm, int bits, int6
  *   n_words, max_tile_words: out, total words and the largest block
  * Errors: LW_E_ARG (null, bad kind, a code out of range, words_cap too
  * small), LW_E_SHAPE (shape, or offsets beyond 32 bits), LW_E_TABLE. */
-lw_status lw_rans_build(int kind, int64_t rows, int64_t cols, const uint8_t *codes, uint16_t *freq, uint32_t *lut,
-                        uint32_t *tile_off, uint32_t *words, int64_t words_cap, int64_t *n_words,
+lw_status lw_rans_build(int kind, int64_t rows, int64_t cols, const uint8_t *codes, int halves, uint16_t *freq,
+                        uint32_t *lut, uint32_t *tile_off, uint32_t *words, int64_t words_cap, int64_t *n_words,
                         int32_t *max_tile_words);
 
-/* Decode-only over the rANS twin (one wavefront per tile, one stream per
- * lane), writing the fixed-width codes as lw_decode_only does:
+/* Decode-only over the rANS twin (one wavefront per tile, one row per lane:
+ * its one stream, or its two interleaved), writing the fixed-width codes as
+ * lw_decode_only does:
  *   Q4: out [rows][cols/2] bytes, low nibble = even column; Q6: [rows][cols] bytes.
  *   lut, tile_off, words: device copies of lw_rans_build's outputs (lut,
- *   words and out 16-byte aligned); max_tile_words as lw_rans_build gave it.
- *   final_state: optional device u32 [n_tiles * 64] receiving each stream's
+ *   words and out 16-byte aligned); halves and max_tile_words as given to
+ *   and by lw_rans_build.
+ *   final_state: optional device u32 [n_tiles * 64 * halves] receiving each stream's
  *   state after its last symbol (2^16 for a well-formed stream), or NULL.
  * A block whose size does not fit max_tile_words is skipped (its output is
  * left as it was); a corrupt stream yields wrong codes and a final state
  * other than 2^16 but reads only its own block.
  * Errors: LW_E_ARG, LW_E_SHAPE, LW_E_UNSUPPORTED (blocks exceed the LDS),
  * LW_E_DEVICE. */
-lw_status lw_rans_decode(int kind, int64_t rows, int64_t cols, const uint32_t *lut, const uint32_t *tile_off,
-                         const uint32_t *words, int32_t max_tile_words, void *out, size_t out_bytes,
-                         uint32_t *final_state, void *stream);
+lw_status lw_rans_decode(int kind, int64_t rows, int64_t cols, int halves, const uint32_t *lut,
+                         const uint32_t *tile_off, const uint32_t *words, int32_t max_tile_words, void *out,
+                         size_t out_bytes, uint32_t *final_state, void *stream);
 
 /* SwiGLU activation between the coded gate/up projections and the coded down
  * projection of an MLP ("Unweight", section "Overlapping Work Across

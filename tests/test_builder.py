@@ -215,11 +215,12 @@ def test_skip_argument_rules():
     assert f(None, None, 4, 64, 256, None, 1, None, None, 1, None) == dg.LW_E_ARG     # null pointers
 
 
+@pytest.mark.parametrize("halves", [1, 2])
 @pytest.mark.parametrize("kind,law,rows,cols,seed", [
     (dg.LW_Q4_PAIR, "normal", 192, 768, 81), (dg.LW_Q4_PAIR, "uniform", 64, 512, 82),
     (dg.LW_Q4_PAIR, "const", 128, 256, 83), (dg.LW_Q6_SINGLE, "normal", 128, 1280, 84),
     (dg.LW_Q4_PAIR, "laplace", 320, 2304, 85)])
-def test_rans_build_matches_oracle(kind, law, rows, cols, seed):
+def test_rans_build_matches_oracle(kind, law, rows, cols, seed, halves):
     """The product's rANS builder writes the oracle's frequencies, offsets and
     words bit for bit, and its kernel table maps every slot to the oracle's
     symbol, frequency and slot - cum."""
@@ -227,8 +228,8 @@ def test_rans_build_matches_oracle(kind, law, rows, cols, seed):
     if law == "laplace":
         sc = 1.2
     codes, _, _, _ = synth.gen_q_custom(rows, cols, seed, qmax=qmax, law=law, mu=mu, scale=sc)
-    p = dg.lw_rans_build(kind, codes)
-    o = O.build_rans_q(O.Q4 if kind == dg.LW_Q4_PAIR else O.Q6, codes)
+    p = dg.lw_rans_build(kind, codes, halves)
+    o = O.build_rans_q(O.Q4 if kind == dg.LW_Q4_PAIR else O.Q6, codes, halves)
     assert np.array_equal(p["freq"], o["f"])
     assert np.array_equal(p["tile_off"], o["tile_off"])
     assert np.array_equal(p["words"], o["words"])
@@ -262,15 +263,19 @@ def test_rans_argument_rules():
     nw, mt = ctypes.c_int64(), ctypes.c_int32()
     vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)
     small = np.zeros(8, np.uint32)
-    assert lw._L.lw_rans_build(1, 64, 256, vp(codes), vp(f16), vp(lut), vp(to), vp(small), 8, ctypes.byref(nw),
+    assert lw._L.lw_rans_build(1, 64, 256, vp(codes), 1, vp(f16), vp(lut), vp(to), vp(small), 8, ctypes.byref(nw),
                                ctypes.byref(mt)) == dg.LW_E_ARG
+    assert lw._L.lw_rans_build(1, 64, 256, vp(codes), 3, vp(f16), vp(lut), vp(to), None, 0, ctypes.byref(nw),
+                               ctypes.byref(mt)) == dg.LW_E_ARG                                   # halves
     # host-side checks of lw_rans_decode: each returns before any HIP call
     f = lw._L.lw_rans_decode
-    assert f(3, 64, 256, None, None, None, 64, None, 0, None, None) == dg.LW_E_ARG         # kind
-    assert f(1, 64, 200, None, None, None, 64, None, 0, None, None) == dg.LW_E_SHAPE
-    assert f(1, 64, 256, None, None, None, 80, None, 0, None, None) == dg.LW_E_ARG         # not 64 + 32k
-    assert f(1, 64, 256, None, None, None, 64 + 32 * 129, None, 0, None, None) == dg.LW_E_ARG
-    assert f(1, 64, 256, None, None, None, 64, None, 0, None, None) == dg.LW_E_ARG         # null pointers
+    assert f(3, 64, 256, 1, None, None, None, 64, None, 0, None, None) == dg.LW_E_ARG         # kind
+    assert f(1, 64, 200, 1, None, None, None, 64, None, 0, None, None) == dg.LW_E_SHAPE
+    assert f(1, 64, 256, 3, None, None, None, 64, None, 0, None, None) == dg.LW_E_ARG         # halves
+    assert f(1, 64, 256, 1, None, None, None, 80, None, 0, None, None) == dg.LW_E_ARG         # not 64 + 32k
+    assert f(1, 64, 256, 1, None, None, None, 64 + 32 * 129, None, 0, None, None) == dg.LW_E_ARG
+    assert f(1, 64, 256, 2, None, None, None, 64, None, 0, None, None) == dg.LW_E_ARG         # below 128 states
+    assert f(1, 64, 256, 1, None, None, None, 64, None, 0, None, None) == dg.LW_E_ARG         # null pointers
 
 
 def test_recon_argument_rules():

@@ -38,16 +38,17 @@ def packed(kind_q4, codes):
     return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8) if kind_q4 else codes.astype(np.uint8)
 
 
-def run(dg, torch, kind, codes, r=None, max_tile_words=None, sentinel=0xA5):
+def run(dg, torch, kind, codes, r=None, max_tile_words=None, sentinel=0xA5, halves=1):
     rows, cols = codes.shape
-    r = r or dg.lw_rans_build(kind, codes)
+    r = r or dg.lw_rans_build(kind, codes, halves)
+    halves = r["halves"]
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).cuda()
     lut, to, w = dev(r["lut"]), dev(r["tile_off"]), dev(r["words"] if r["words"].size else np.zeros(4, np.uint32))
     ob = rows * cols // 2 if kind == dg.LW_Q4_PAIR else rows * cols
     out = torch.full((ob,), sentinel, dtype=torch.uint8, device="cuda")
     nt = (rows // 64) * (cols // 256)
-    fs = torch.zeros(nt * 64, dtype=torch.int32, device="cuda")
-    dg.lw_rans_decode(kind, rows, cols, lut, to, w, max_tile_words or r["max_tile_words"], out, fs)
+    fs = torch.zeros(nt * 64 * halves, dtype=torch.int32, device="cuda")
+    dg.lw_rans_decode(kind, rows, cols, lut, to, w, max_tile_words or r["max_tile_words"], out, fs, halves)
     torch.cuda.synchronize()
     return out.cpu().numpy().reshape(rows, -1), fs.cpu().numpy().view(np.uint32), r
 
@@ -64,18 +65,19 @@ CASES = [  # kind (1 = Q4, 2 = Q6), law, rows, cols, seed: one tile, ragged work
 ]
 
 
+@pytest.mark.parametrize("halves", [1, 2])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"k{c[0]}_{c[1]}_{c[2]}x{c[3]}")
-def test_rans_decode_restores_codes(torch, dg, case):
+def test_rans_decode_restores_codes(torch, dg, case, halves):
     kind, law, rows, cols, seed = case
-    say("rans decode", case)
+    say("rans decode", case, halves)
     qmax, mu, sc = qlaw(kind, dg)
     codes, _, _, _ = synth.gen_q_custom(rows, cols, seed, qmax=qmax, law=law, mu=mu,
                                         scale=1.2 if law == "laplace" else sc)
-    out, fs, r = run(dg, torch, kind, codes)
+    out, fs, r = run(dg, torch, kind, codes, halves=halves)
     assert np.array_equal(out, packed(kind == dg.LW_Q4_PAIR, codes))
     assert np.all(fs == 65536)
-    ob = O.build_rans_q(O.Q4 if kind == dg.LW_Q4_PAIR else O.Q6, codes)
-    assert np.array_equal(O.rans_unsymbolise(ob["kind"], rows, cols, O.decode_rans(ob)), codes)
+    ob = O.build_rans_q(O.Q4 if kind == dg.LW_Q4_PAIR else O.Q6, codes, halves)
+    assert np.array_equal(O.rans_unsymbolise(ob["kind"], rows, cols, O.decode_rans(ob), halves), codes)
 
 
 def test_rans_decode_twice_is_identical(torch, dg):
@@ -106,11 +108,12 @@ def test_rans_blocks_beyond_the_limit_are_skipped(torch, dg):
             assert np.all(out[blk] == 0xA5)
 
 
-def test_rans_corrupt_words_stay_in_bounds(torch, dg):
+@pytest.mark.parametrize("halves", [1, 2])
+def test_rans_corrupt_words_stay_in_bounds(torch, dg, halves):
     """Random words under valid offsets decode to garbage codes and final
     states other than 2^16, touching only the output."""
     codes, _, _, _ = synth.gen_q_custom(128, 512, 23)
-    r = dg.lw_rans_build(dg.LW_Q4_PAIR, codes)
+    r = dg.lw_rans_build(dg.LW_Q4_PAIR, codes, halves)
     r = dict(r)
     r["words"] = np.random.default_rng(24).integers(0, 2 ** 32, size=r["words"].size, dtype=np.uint64).astype(np.uint32)
     out, fs, _ = run(dg, torch, dg.LW_Q4_PAIR, codes, r=r)
@@ -118,14 +121,15 @@ def test_rans_corrupt_words_stay_in_bounds(torch, dg):
     assert np.mean(fs != 65536) > 0.9
 
 
+@pytest.mark.parametrize("halves", [1, 2])
 @pytest.mark.parametrize("name", ["q4_up_14336x4096", "q6_gate_28672x8192"])
-def test_rans_full_size(torch, dg, name):
+def test_rans_full_size(torch, dg, name, halves):
     """The 14336x4096 4-bit matrix and one 28672x8192 6-bit 70B matrix: every
     code restored and every stream ending in 2^16."""
     mat = next(m for ms in synth.WORKLOADS.values() for m in ms if m.name == name)
-    say("rans full", name)
+    say("rans full", name, halves)
     codes, _, _, _ = synth.gen_q(mat)
     kind = dg.LW_Q4_PAIR if mat.kind == "q4" else dg.LW_Q6_SINGLE
-    out, fs, _ = run(dg, torch, kind, codes)
+    out, fs, _ = run(dg, torch, kind, codes, halves=halves)
     assert np.array_equal(out, packed(kind == dg.LW_Q4_PAIR, codes))
     assert np.all(fs == 65536)
