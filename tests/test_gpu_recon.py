@@ -216,3 +216,33 @@ def test_recon_full_size(torch, dg, batch):
     torch.cuda.synchronize()
     rows = np.sort(np.random.default_rng(10).choice(mat.rows, 48, replace=False))
     assert rel_err(y.cpu().numpy()[:, rows], O.gemv_bf16(w, x, batch, rows=rows)) <= TOL
+
+
+def test_recon_argument_errors(torch, dg):
+    rows, cols = 64, 256
+    w, db = setup(dg, torch, rows, cols, 461, 0.0)
+    src, vr = transcode(dg, torch, db, dg.LW_FORM_PALETTE, rows, cols)
+    x = dev(torch, big_x(cols, 4, 462))
+    y = torch.empty((4, rows), device="cuda")
+    for kw, status in ((dict(variant=dg.LW_RECON_VARIANTS), dg.LW_E_ARG), (dict(variant=-2), dg.LW_E_ARG)):
+        with pytest.raises(dg.LwError) as e:
+            dg.lw_recon_gemm(db, dg.LW_FORM_PALETTE, src, vr, x, y, 4, **kw)
+        assert e.value.status == status
+    with pytest.raises(dg.LwError) as e:                 # the exponent form is twice the palette form's size
+        dg.lw_recon_gemm(db, dg.LW_FORM_EXPONENT, src, vr, x, y, 4)
+    assert e.value.status == dg.LW_E_ARG
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_recon_gemm(db, 7, src, vr, x, y, 4)
+    assert e.value.status == dg.LW_E_ARG
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_recon_gemm(db, dg.LW_FORM_PALETTE, src, vr, x, y, 0)
+    assert e.value.status == dg.LW_E_ARG
+    codes, d, m, _ = synth.gen_q_custom(64, 256, 463)
+    qdb = dg.upload(dg.lw_bundle_build_q(dg.LW_Q4_PAIR, codes, d, m))
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_bf16_transcode(qdb, dg.LW_FORM_PALETTE, src, vr)
+    assert e.value.status == dg.LW_E_UNSUPPORTED
+    with pytest.raises(dg.LwError) as e:                 # no palette form attached yet
+        dg.lw_pipeline_set(db, 1, 1, dg.LW_PIPE_DIRECT_PALETTE)
+    assert e.value.status == dg.LW_E_UNSUPPORTED
+    assert dg.lw_pipeline_scratch_bytes(qdb, dg.LW_PIPE_PALETTE) == 0
