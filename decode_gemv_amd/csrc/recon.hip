@@ -23,8 +23,8 @@
 // (large batches) each rebuilds its 16 rows into an LDS tile and multiplies
 // all 64 rows with its own quarter of the batch columns, so one rebuilt
 // operand feeds four times as many matrix instructions.  The activations of
-// a 32-column step are shared through an LDS double buffer (rows padded to
-// 80 bytes, so the 16 lanes of a B read hit 64 distinct banks).
+// a 32-column step are shared through an LDS double buffer (16-byte chunks
+// swizzled within a row, so stores and B reads are free of bank conflicts).
 //
 // Rebuilding eight weights (one A operand) from the palette form: the eight
 // indices give eight bytes T = ror8(exponent) by two byte permutes over the
@@ -52,7 +52,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int XSTRIDE = 80;                  // bytes per staged activation row (64 + 16 padding)
+constexpr int XSTRIDE = 64;                  // bytes per staged activation row (32 bf16)
+
+// 16-byte chunk q of staged row r sits at chunk q ^ ((r >> 2) & 3): the 16
+// lanes of a B read (rows r0 .. r0+15, one chunk) and the 16 lanes of a
+// store (rows r0 .. r0+3, all four chunks) then hit 16 distinct groups of
+// four banks
+__device__ __forceinline__ int xs_off(int r, int q) { return r * XSTRIDE + 16 * (q ^ ((r >> 2) & 3)); }
 
 struct RArgs {
     const uint32_t *src;        // palette: [t][32][64] u32 (8 indices); exponent: [t][64][64] u32 (4 bytes)
@@ -181,7 +187,7 @@ __global__ __launch_bounds__(256, 2) void k_recon(RArgs a)
 #pragma unroll
         for (int m = 0; m < XV; m++) {
             const int id = threadIdx.x + 256 * m;
-            if (id < BN * 4) *reinterpret_cast<u32x4 *>(&xs[buf][id >> 2][16 * (id & 3)]) = xr[m];
+            if (id < BN * 4) *reinterpret_cast<u32x4 *>(&xs[buf][0][0] + xs_off(id >> 2, id & 3)) = xr[m];
         }
     };
 
@@ -230,7 +236,7 @@ __global__ __launch_bounds__(256, 2) void k_recon(RArgs a)
         }
 #pragma unroll
         for (int n = 0; n < NB; n++) {
-            const u32x4 bv = *reinterpret_cast<const u32x4 *>(xb + (nb0 + 16 * n + j) * XSTRIDE + 16 * q);
+            const u32x4 bv = *reinterpret_cast<const u32x4 *>(xb + xs_off(nb0 + 16 * n + j, q));
             const bf16x8 b = __builtin_bit_cast(bf16x8, bv);
 #pragma unroll
             for (int f = 0; f < FB; f++) acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[f], b, acc[f][n], 0, 0, 0);
