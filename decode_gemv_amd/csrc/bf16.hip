@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(KArgs a)
     if (c.active) {
         LaneDec d;
         const bool ok = lw_lane_init(d, lds, slots, c.l, a);
-        d.u += c.half ? split : 0u;       // the second tile row starts at the split bit
+        d.advance(c.half ? split : 0u);       // the second tile row starts at the split bit
         if (ok) {
             struct XA {
                 u32x2 v[BATCH];
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) void k_decode_bf16(KArgs a)
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     LaneDec d;
     if (!lw_lane_init(d, lds, slots, c.l, a)) return;
-    d.u += c.half ? split : 0u;
+    d.advance(c.half ? split : 0u);
     // the lane's restored row segment: each chunk of 16 groups (64 weights,
     // 128 bytes) is collected in registers and written as 16-byte stores
     uint4 *orow = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.out) +
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256) void k_decode_bf16(KArgs a)
         run_chunk(ch + 1, ring[1]);
     }
     // the lane of the second row ends where the whole lane stream ends
-    if (a.lane_bits && c.half) a.lane_bits[(size_t)c.t * 32 + c.l] = d.u - 31;
+    if (a.lane_bits && c.half) a.lane_bits[(size_t)c.t * 32 + c.l] = d.bitpos();
     // verbatim segments overwrite the placeholder weights (rare): after this
     // wavefront's row stores, all lanes write one segment
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(256) void k_transcode_bf16(KArgs a)
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     LaneDec d;
     if (!lw_lane_init(d, lds, slots, c.l, a)) return;
-    d.u += c.half ? split : 0u;
+    d.advance(c.half ? split : 0u);
     const int r = 2 * c.l + c.half;                                   // tile row
     uint32_t *o = static_cast<uint32_t *>(a.out) + (size_t)c.t * (EXP ? 64 : 32) * 64 + r;
     struct NoAux {};

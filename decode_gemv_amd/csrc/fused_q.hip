@@ -116,7 +116,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
     if (c.active) {
         LaneDec d;
         const bool ok = lw_lane_init(d, lds, slots, c.l, a);
-        d.u += c.half ? split : 0u;       // the second tile row starts at the split bit
+        d.advance(c.half ? split : 0u);       // the second tile row starts at the split bit
         constexpr int NG = SPL / 8;       // groups of four symbols per tile row
         if (ok) {
             // activations of one group: Q4 four pairs, Q6 two pairs (four columns) per batch row
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
                 }
             };
             if constexpr (KIND == LW_Q4_PAIR)
-                lw_decode_pipelined<N8, N16, NG, XA>(d, a, [](int) { return 0u; }, fetch, use);
+                lw_decode_pipelined<N8, N16, NG, XA, true>(d, a, [](int) { return 0u; }, fetch, use);
             else
                 lw_decode_pipelined<N8, N16, NG, XA>(
                     d, a, [](int j) { return (j & 1) ? (LW_TPAY_HI - LW_TPAY) : 0u; }, fetch, use);
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256) void k_decode_q(KArgs a)
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     LaneDec d;
     if (!lw_lane_init(d, lds, slots, c.l, a)) return;
-    d.u += c.half ? split : 0u;
+    d.advance(c.half ? split : 0u);
     const int64_t row_bytes = KIND == LW_Q4_PAIR ? a.cols / 2 : a.cols;
     constexpr int NG = SPL / 8;           // groups of four symbols per tile row
     // The lane's restored row segment (4 bytes per group) is collected in
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(256) void k_decode_q(KArgs a)
             orow[part * (PART / 4) + i] = make_uint4(buf[4 * i], buf[4 * i + 1], buf[4 * i + 2], buf[4 * i + 3]);
     }
     // the lane of the second row ends where the whole lane stream ends
-    if (a.lane_bits && c.half) a.lane_bits[(size_t)c.t * 32 + c.l] = d.u - 31;
+    if (a.lane_bits && c.half) a.lane_bits[(size_t)c.t * 32 + c.l] = d.bitpos();
 }
 
 template <int KIND, int N8, int N16, int BATCH, int WPG>

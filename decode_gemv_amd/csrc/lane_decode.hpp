@@ -7,9 +7,11 @@
 //
 // Words.  A tile's interleaved words are staged in LDS as rows of 32 dwords
 // ("slots"): slot j+1 holds word row j, slot 0 and the last two slots are
-// pads.  A lane keeps u = bitpos + 31; the three words starting at slot u>>5
-// hold bits [bitpos, bitpos + 64) and two v_alignbit by ~u give a 64-bit
-// left-justified register window (hi, lo).  One window serves four symbols:
+// pads.  With u = bitpos + 31, the three words starting at slot u>>5 hold
+// bits [bitpos, bitpos + 64) and two v_alignbit by ~u give a 64-bit
+// left-justified register window (hi, lo).  A lane keeps un = ~u itself, so
+// the shift is the register and the slot address is one shift-or and one
+// subtraction: 128 (u >> 5) = -4 - ((un << 2) | 124).  One window serves four symbols:
 // after three codes of at most 11 bits, 31 bits of it are still valid, more
 // than the 11-bit peek needs.  So the LDS read sits on the lane's serial
 // chain once per four symbols.
@@ -31,12 +33,13 @@
 //
 // Compact tables (at most four code lengths, the three shorter <= 8: what
 // the builder makes).  One v_sad_u8 pair compares the top 8 peek bits with
-// the three limits, and the accumulator makes A = CBASE - 2r for r limits
-// passed: the LDS address of the base entry of the r-th used length, whose
-// low byte 6 - 2r also selects, through v_perm_b32, the byte 64 - length(r)
-// of a four-entry table held in two SGPRs -- the shift s, whose low five
-// bits are 32 - len and low six bits 64 - len.  The perm's upper bytes are
-// don't-care, so the consumed bits of a group are taken modulo 64.
+// the three limits, and the accumulator makes A = CSEL - 2r for r limits
+// passed.  A + 1 is the LDS address of the base entry of the r-th used
+// length, and A is at once a v_perm_b32 selector into an 8-byte table held
+// in two SGPRs: its low byte 7 - 2r picks the byte -length(r) mod 256, its
+// second byte (at least 13) makes 0xFF, and its two zero upper bytes pick
+// table byte 0, which holds 0xFF.  So the shift is s = -len exactly: its low
+// five bits are 32 - len, and the lengths of a group sum without a mask.
 #ifndef LW_LANE_DECODE_HPP
 #define LW_LANE_DECODE_HPP
 
@@ -93,8 +96,8 @@ inline hipError_t lw_allow_lds()
 #define LW_PBASE 1024u       // length entries at PBASE - 2*len, len = 1..11
 #define LW_TPAY 1024u        // payload per canonical index, u32[256]
 #define LW_TPAY_HI 2048u     // second payload, u32[256]
-#define LW_TAB_BYTES 3072u
-#define LW_CBASE 774u        // compact tables: base entry of count r at CBASE - 2r (low byte 6 - 2r)
+#define LW_CSEL 0xD07u      // compact tables: selector of count r CSEL - 2r, its base entry at CSEL + 1 - 2r
+#define LW_TAB_BYTES 3584u
 
 LW_DEV uint32_t lw_wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
@@ -177,7 +180,7 @@ LW_DEV void lw_tab_put(uint8_t *lds, const LwTabRegs &r, const KArgs &a)
     *(lw_lds_w32 *)(size_t)(lb + LW_TPAY_HI + 4u * (tid & 255)) = r.pay2;
     const int16_t v = (int16_t)((int32_t)lb + (int32_t)LW_TPAY + 4 * r.ent);   // repeated stores write the same value
     if constexpr (CMP)
-        *(lw_lds_w16 *)(size_t)(lb + LW_CBASE - 2u * (uint32_t)min(tid, a.ncmp)) = v;
+        *(lw_lds_w16 *)(size_t)(lb + LW_CSEL + 1u - 2u * (uint32_t)min(tid, a.ncmp)) = v;
     else
         *(lw_lds_w16 *)(size_t)(lb + LW_PBASE - 2u * (uint32_t)(a.min_len + min(tid, a.max_len - a.min_len))) = v;
 }
@@ -249,10 +252,12 @@ LW_DEV void lw_verbatim_visit(const KArgs &a, int64_t t, int lane, F f)
 
 // One lane's decoder state.
 struct LaneDec {
-    uint32_t slot0;              // LDS byte address of this lane's word in slot 0
-    uint32_t u;                  // bit position + 31
+    uint32_t wref;               // LDS byte address of this lane's word in slot 0, minus 4
+    uint32_t un;                 // ~(bit position + 31)
     uint32_t k;                  // SAD offset including the LDS base
     uint32_t ubias;              // 4 * (lb/2 + PBASE/2): what four shifts s add beyond the code lengths
+    LW_DEV void advance(uint32_t bits) { un -= bits; }
+    LW_DEV uint32_t bitpos() const { return ~un - 31u; }
 };
 
 // Count the limits the window's peek has passed; returns A = lb + PBASE - 2*len.
@@ -293,11 +298,16 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
 {
     static_assert(NG % 2 == 0 && NG >= 4, "groups must be even");
     constexpr bool CMP = lw_compact<N16>();
+    // Wave-uniform operands that a VOP3 instruction takes beside a scalar
+    // one (it may read a single scalar register) live in vector registers
+    // for the whole loop, so no copy is made per group.
+    uint32_t kv = d.k, lut_lo = a.lut_lo;
+    asm volatile("" : "+v"(kv), "+v"(lut_lo));
     uint32_t wa, wb, wc;
     uint32_t code[2][4], A[2][4], base[2][4], pay[2][4];
     Aux aux[2];
     auto issue_window = [&]() {
-        const uint32_t p = d.slot0 + ((d.u & ~31u) << 2);     // slot u >> 5, 128 bytes per slot
+        const uint32_t p = d.wref - ((d.un << 2) | 124u);    // slot u >> 5, 128 bytes per slot
         wa = lw_ld32(p);
         wb = lw_ld32(p + 128);
         wc = lw_ld32(p + 256);
@@ -305,26 +315,27 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
     // One group: align a 64-bit window at the group's first bit, then peek
     // each symbol at its offset o within it (at most 33 bits in, so the
     // 11-bit peek stays inside the window) with one 64-bit shift.  s_j is
-    // bias - len_j with bias = lb/2 + 512 a multiple of 64, so o = -sum(s)
-    // equals the offset modulo 64, which is all the shift reads.
+    // -len_j (compact tables) or bias - len_j with bias = lb/2 + 512 a
+    // multiple of 64, so o = -sum(s) equals the offset modulo 64, which is
+    // all the shift reads.
     auto decode_group = [&](int q) {
-        const uint32_t sh = ~d.u;
+        const uint32_t sh = d.un;
         const uint64_t win = ((uint64_t)__builtin_amdgcn_alignbit(wa, wb, sh) << 32) |
                              (uint64_t)__builtin_amdgcn_alignbit(wb, wc, sh);
         uint32_t o = 0;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             const uint32_t peek = j == 0 ? (uint32_t)(win >> 32) : (uint32_t)((win << (o & 63u)) >> 32);
-            const uint32_t Aj = lw_sad_count<N8, N16>(peek, d.k, a);
-            const uint32_t s = CMP ? __builtin_amdgcn_perm(a.lut_hi, a.lut_lo, Aj) : Aj >> 1;
+            const uint32_t Aj = lw_sad_count<N8, N16>(peek, kv, a);
+            const uint32_t s = CMP ? __builtin_amdgcn_perm(a.lut_hi, lut_lo, Aj) : Aj >> 1;
             A[q][j] = Aj;
             code[q][j] = peek >> (s & 31u);
             o -= s;
         }
         if constexpr (CMP)
-            d.u += o & 63u;               // sum(len) < 64; the perm's upper bytes are don't-care
+            d.un -= o;                    // o = sum(len) exactly
         else
-            d.u += o + d.ubias;           // u + sum(len)
+            d.un -= o + d.ubias;          // o + ubias = sum(len)
     };
     auto issue_payloads = [&](int q, int g) {
 #pragma unroll
@@ -334,7 +345,7 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
     };
     auto issue_params = [&](int q) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) base[q][j] = (uint32_t)lw_ld16s(A[q][j]);
+        for (int j = 0; j < 4; j++) base[q][j] = (uint32_t)lw_ld16s(A[q][j] + (CMP ? 1u : 0u));
     };
     auto use_group = [&](int q, int g) {
 #pragma unroll
@@ -387,18 +398,20 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
 }
 
 // Set up a lane's decoder on its staged tile.  Returns false (the kernel must
-// then produce nothing) if the LDS base is not 256-byte aligned: the shift
+// then produce nothing) unless the LDS base is 256-byte aligned (the shift
 // amounts s = A >> 1 then carry a bias lb/2 + PBASE/2 that is a multiple of
 // 64, which both the 32-bit shifts and the 64-bit window offset need, and
-// the low byte of a compact table's A is the byte-table selector.
+// the low byte of a compact table's A is its byte-table selector) and low
+// enough that the selector's second byte stays a 0xFF selector and its
+// upper bytes stay zero.
 LW_DEV bool lw_lane_init(LaneDec &d, uint8_t *lds, const uint32_t *slots, int l, const KArgs &a)
 {
     const uint32_t lb = (uint32_t)(size_t)lds;
-    d.slot0 = (uint32_t)(size_t)(slots + l);
-    d.u = 31;
+    d.wref = (uint32_t)(size_t)(slots + l) - 4u;
+    d.un = ~31u;
     d.k = a.sad_k + lb;
     d.ubias = 4u * (lb / 2u + LW_PBASE / 2u);
-    return (lb & 255u) == 0;
+    return (lb & 255u) == 0 && lb + LW_CSEL < 0xFF00u;
 }
 
 // Sum the per-wave partials of the workgroup's ROWS rows (red[wave][b][row])

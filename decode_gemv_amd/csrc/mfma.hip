@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
     if (c.active) {
         LaneDec d;
         const bool ok = lw_lane_init(d, lds, slots, c.l, a);
-        d.u += c.half ? split : 0u;       // the second tile row starts at the split bit
+        d.advance(c.half ? split : 0u);       // the second tile row starts at the split bit
         if (ok) {
             u32x2 xcur[2];
             load_x(0, xcur);

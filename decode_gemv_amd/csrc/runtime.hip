@@ -128,10 +128,10 @@ SadPlan lw_sad_plan(const lw_table &t, int min_len, int max_len, KArgs &a)
     for (int L = 1; L <= LW_MAXLEN; L++)
         if (t.count[L]) used[nu++] = L;
     if (nu >= 1 && nu <= 4 && (nu == 1 || used[nu - 2] <= 8)) {
-        uint64_t lut = 0;
+        uint64_t lut = 0x00FF00FF00FF00FFull;   // even bytes 0xFF: what the selector's zero upper bytes pick
         for (int r = 0; r < nu; r++) {
             const int L = used[r];
-            lut |= (uint64_t)(64 - L) << (8 * (6 - 2 * r));
+            lut |= (uint64_t)((256 - L) & 0xFF) << (8 * (7 - 2 * r));
             a.cbase[r] = (int32_t)t.offset[L] - (int32_t)t.first[L];
             if (r < nu - 1) {
                 const uint32_t c = (uint32_t)t.limit[L] >> 3;
@@ -142,7 +142,7 @@ SadPlan lw_sad_plan(const lw_table &t, int min_len, int max_len, KArgs &a)
         a.lut_lo = (uint32_t)lut;
         a.lut_hi = (uint32_t)(lut >> 32);
         a.ncmp = nu - 1;
-        a.sad_k = LW_CBASE - (uint32_t)(nu - 1);
+        a.sad_k = LW_CSEL - (uint32_t)(nu - 1);
         p.n8ops = 1;
         p.n16ops = 0;
         p.compact = true;
