@@ -103,11 +103,6 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
         *(lw_lds_w32 *)(size_t)(xs_addr + 4u * (b * 128 + c.lane + 64)) = xv[b][1];
     }
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    float sx[BATCH];
-#pragma unroll
-    for (int b = 0; b < BATCH; b++)
-        sx[b] = lw_wave_sum(lw_half_lo(xv[b][0]) + lw_half_hi(xv[b][0]) + lw_half_lo(xv[b][1]) +
-                            lw_half_hi(xv[b][1]));
 
     float acc[BATCH];
 #pragma unroll
@@ -162,7 +157,13 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
         }
     }
 
-    // dequantise: y_row = d * sum(q x) - m * sum(x) for this tile row
+    // dequantise: y_row = d * sum(q x) - m * sum(x) for this tile row (the
+    // column block's activation sum is taken here, off the decode's start)
+    float sx[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; b++)
+        sx[b] = lw_wave_sum(lw_half_lo(xv[b][0]) + lw_half_hi(xv[b][0]) + lw_half_lo(xv[b][1]) +
+                            lw_half_hi(xv[b][1]));
     float val[BATCH];
 #pragma unroll
     for (int b = 0; b < BATCH; b++) val[b] = c.active ? lw_half_lo(dm) * acc[b] - lw_half_hi(dm) * sx[b] : 0.f;

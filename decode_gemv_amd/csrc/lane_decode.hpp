@@ -111,12 +111,26 @@ LW_DEV float lw_dot2(uint32_t a, uint32_t b, float c)
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(lw_half2, a), __builtin_bit_cast(lw_half2, b), c, false);
 }
 
-// sum over the 64 lanes of a wavefront
+// v + v of the lane that DPP control CTRL names (all rows and banks)
+template <int CTRL>
+LW_DEV float lw_dpp_add(float v)
+{
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the 64 lanes of a wavefront (every lane active), the same value
+// in every lane: four DPP steps sum each row of 16 lanes (pairs, quads,
+// eights by the half-row mirror, rows by the row mirror), then the four row
+// sums are read from lanes 0, 16, 32 and 48.  No LDS round trip.
 LW_DEV float lw_wave_sum(float v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v = lw_dpp_add<0xB1>(v);              // quad_perm [1,0,3,2]
+    v = lw_dpp_add<0x4E>(v);              // quad_perm [2,3,0,1]
+    v = lw_dpp_add<0x141>(v);             // row_half_mirror
+    v = lw_dpp_add<0x140>(v);             // row_mirror
+    const int i = __builtin_bit_cast(int, v);
+    auto lane = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(i, l)); };
+    return (lane(0) + lane(16)) + (lane(32) + lane(48));
 }
 
 // LDS accessed by byte address (the kernels allocate only dynamic LDS, so
