@@ -149,7 +149,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
             if constexpr (KIND == LW_Q4_PAIR)
                 lw_decode_pipelined<N8, N16, NG, XA, true>(d, a, [](int) { return 0u; }, fetch, use);
             else
-                lw_decode_pipelined<N8, N16, NG, XA>(
+                lw_decode_pipelined<N8, N16, NG, XA, true>(
                     d, a, [](int j) { return (j & 1) ? (LW_TPAY_HI - LW_TPAY) : 0u; }, fetch, use);
         } else {                           // unusable LDS base: poison the output
 #pragma unroll
