@@ -326,30 +326,33 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
         wb = lw_ld32(p + 128);
         wc = lw_ld32(p + 256);
     };
-    // One group: align a 64-bit window at the group's first bit, then peek
-    // each symbol at its offset o within it (at most 33 bits in, so the
-    // 11-bit peek stays inside the window) with one 64-bit shift.  s_j is
-    // -len_j (compact tables) or bias - len_j with bias = lb/2 + 512 a
-    // multiple of 64, so o = -sum(s) equals the offset modulo 64, which is
-    // all the shift reads.
+    // One group: align a 64-bit window (hi, lo) at the group's first bit,
+    // then peek each symbol at its offset o within it.  s_j is -len_j
+    // (compact tables) or bias - len_j with bias = lb/2 + 512 a multiple of
+    // 64, so the running sum t of the s before symbol j is -o modulo 64.
+    // Symbols 1 and 2 sit at most 22 bits in: one alignbit by t (which reads
+    // t mod 32 = 32 - o) takes their peek.  Symbol 3 can sit 33 bits in,
+    // past one alignment, so it takes a 64-bit shift by -t.
     auto decode_group = [&](int q) {
         const uint32_t sh = d.un;
-        const uint64_t win = ((uint64_t)__builtin_amdgcn_alignbit(wa, wb, sh) << 32) |
-                             (uint64_t)__builtin_amdgcn_alignbit(wb, wc, sh);
-        uint32_t o = 0;
+        const uint32_t hi = __builtin_amdgcn_alignbit(wa, wb, sh), lo = __builtin_amdgcn_alignbit(wb, wc, sh);
+        uint32_t t = 0;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const uint32_t peek = j == 0 ? (uint32_t)(win >> 32) : (uint32_t)((win << (o & 63u)) >> 32);
+            uint32_t peek;
+            if (j == 0) peek = hi;
+            else if (j < 3) peek = __builtin_amdgcn_alignbit(hi, lo, t);
+            else peek = (uint32_t)((((uint64_t)hi << 32 | lo) << ((0u - t) & 63u)) >> 32);
             const uint32_t Aj = lw_sad_count<N8, N16>(peek, kv, a);
             const uint32_t s = CMP ? __builtin_amdgcn_perm(a.lut_hi, lut_lo, Aj) : Aj >> 1;
             A[q][j] = Aj;
             code[q][j] = peek >> (s & 31u);
-            o -= s;
+            t += s;
         }
         if constexpr (CMP)
-            d.un -= o;                    // o = sum(len) exactly
+            d.un += t;                    // t = -sum(len) exactly
         else
-            d.un -= o + d.ubias;          // o + ubias = sum(len)
+            d.un += t - d.ubias;          // t - ubias = -sum(len)
     };
     auto issue_payloads = [&](int q, int g) {
 #pragma unroll
