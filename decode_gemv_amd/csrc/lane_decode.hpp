@@ -269,6 +269,7 @@ struct LaneDec {
     uint32_t wref;               // LDS byte address of this lane's word in slot 0, minus 4
     uint32_t un;                 // ~(bit position + 31)
     uint32_t k;                  // SAD offset including the LDS base
+    uint32_t lut_lo;             // low word of the compact tables' shift bytes
     uint32_t ubias;              // 4 * (lb/2 + PBASE/2): what four shifts s add beyond the code lengths
     LW_DEV void advance(uint32_t bits) { un -= bits; }
     LW_DEV uint32_t bitpos() const { return ~un - 31u; }
@@ -312,11 +313,6 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
 {
     static_assert(NG % 2 == 0 && NG >= 4, "groups must be even");
     constexpr bool CMP = lw_compact<N16>();
-    // Wave-uniform operands that a VOP3 instruction takes beside a scalar
-    // one (it may read a single scalar register) live in vector registers
-    // for the whole loop, so no copy is made per group.
-    uint32_t kv = d.k, lut_lo = a.lut_lo;
-    asm volatile("" : "+v"(kv), "+v"(lut_lo));
     uint32_t wa, wb, wc;
     uint32_t code[2][4], A[2][4], base[2][4], pay[2][4];
     Aux aux[2];
@@ -343,8 +339,8 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
             if (j == 0) peek = hi;
             else if (j < 3) peek = __builtin_amdgcn_alignbit(hi, lo, t);
             else peek = (uint32_t)((((uint64_t)hi << 32 | lo) << ((0u - t) & 63u)) >> 32);
-            const uint32_t Aj = lw_sad_count<N8, N16>(peek, kv, a);
-            const uint32_t s = CMP ? __builtin_amdgcn_perm(a.lut_hi, lut_lo, Aj) : Aj >> 1;
+            const uint32_t Aj = lw_sad_count<N8, N16>(peek, d.k, a);
+            const uint32_t s = CMP ? __builtin_amdgcn_perm(a.lut_hi, d.lut_lo, Aj) : Aj >> 1;
             A[q][j] = Aj;
             code[q][j] = peek >> (s & 31u);
             t += s;
@@ -427,6 +423,11 @@ LW_DEV bool lw_lane_init(LaneDec &d, uint8_t *lds, const uint32_t *slots, int l,
     d.wref = (uint32_t)(size_t)(slots + l) - 4u;
     d.un = ~31u;
     d.k = a.sad_k + lb;
+    d.lut_lo = a.lut_lo;
+    // Wave-uniform operands that a VOP3 instruction takes beside a scalar
+    // one (it may read a single scalar register) are held in vector
+    // registers, set once here, so the decode loops make no copy per group.
+    asm volatile("" : "+v"(d.k), "+v"(d.lut_lo));
     d.ubias = 4u * (lb / 2u + LW_PBASE / 2u);
     return (lb & 255u) == 0 && lb + LW_CSEL < 0xFF00u;
 }
