@@ -38,7 +38,8 @@ struct KArgs {
     uint32_t sad_k;              // accumulator offset: PBASE - 2*min_len - (number of comparisons)
     // Compact tables (at most four code lengths, the three shorter <= 8): the
     // comparison count r indexes the used lengths; lut_hi:lut_lo hold
-    // 64 - length(r) at byte 6 - 2r, cbase[r] = offset - first of length(r)
+    // -length(r) mod 256 at byte 7 - 2r and 0xFF in the even bytes,
+    // cbase[r] = offset - first of length(r)
     uint32_t lut_lo, lut_hi;
     int32_t cbase[4];
     int32_t ncmp;                // comparisons (used lengths - 1)
