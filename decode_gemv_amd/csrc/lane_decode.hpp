@@ -469,10 +469,21 @@ LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g
         const int b = i / ROWS, row = i % ROWS;
         if (b >= a.batch) break;
         if (row0 + row >= a.rows) continue;
+        // eight groups' partials are requested together (clamped indices, so
+        // every load is unconditional) and then added in group order
+        const float *pp = &a.part[(size_t)b * a.rows + row0 + row];
+        const size_t gstride = (size_t)LW_BATCH_MAX * a.rows;
         float v = 0.f;
-        for (int gg = 0; gg < a.groups; gg++)
-            v += __hip_atomic_load(&a.part[((size_t)gg * LW_BATCH_MAX + b) * a.rows + row0 + row], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+        for (int g0 = 0; g0 < a.groups; g0 += 8) {
+            float t[8];
+#pragma unroll
+            for (int k = 0; k < 8; k++)
+                t[k] = __hip_atomic_load(pp + (size_t)min(g0 + k, a.groups - 1) * gstride, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int k = 0; k < 8; k++)
+                if (g0 + k < a.groups) v += t[k];
+        }
         a.y[(size_t)b * a.rows + row0 + row] = v;
     }
     if (threadIdx.x == 0) __hip_atomic_store(&a.count[ctr], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
