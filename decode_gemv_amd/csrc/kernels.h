@@ -43,6 +43,7 @@ struct KArgs {
     uint32_t lut_lo, lut_hi;
     int32_t cbase[4];
     int32_t ncmp;                // comparisons (used lengths - 1)
+    int32_t ramp;                // 1: the whole grid is resident at once (wavefronts lower their priority as they progress)
 };
 
 // SAD comparison layout of a bundle: byte-lane ops (0..2) and 16-bit ops

@@ -68,6 +68,21 @@ inline int lw_device_lds_bytes()
     return bytes[dev];
 }
 
+// Host: the current device's compute-unit count (cached per device; 0 if the
+// query fails).
+inline int lw_device_cu_count()
+{
+    constexpr int MAXDEV = 64;
+    static std::once_flag once[MAXDEV];
+    static int cus[MAXDEV];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAXDEV) return 0;
+    std::call_once(once[dev], [dev]() {
+        if (hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus[dev] = 0;
+    });
+    return cus[dev];
+}
+
 // Host: allow kernel KERN the device's largest dynamic LDS allocation, once
 // per device.  The limit is a permission, not an allocation (a launch still
 // reserves only what it asks for), so raising it to the maximum once keeps
