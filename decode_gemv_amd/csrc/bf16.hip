@@ -144,6 +144,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(KArgs a)
             uint32_t pend = 0;
             auto run_chunk = [&](int ch, const uint32_t (&cur)[CHUNK]) {
                 auto fetch = [&](int g) {
+                    lw_ramp<64>(a.ramp, ch * CHUNK + g);
                     XA r;
 #pragma unroll
                     for (int b = 0; b < BATCH; b++) {
@@ -354,8 +355,10 @@ hipError_t transcode_mode(const KArgs &a, bool exponents, hipStream_t s)
 }
 
 template <int N8, int N16, int BATCH>
-hipError_t launch_gemv(const KArgs &a, hipStream_t s)
+hipError_t launch_gemv(const KArgs &a0, hipStream_t s)
 {
+    KArgs a = a0;
+    a.ramp = lw_resident_ramp((int64_t)a.n_rb * a.n_cb);
     const LdsLayout L = lds_layout(BATCH, a.max_words, false);
     dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
     auto kern = k_gemv_bf16<N8, N16, BATCH>;

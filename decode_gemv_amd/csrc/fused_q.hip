@@ -65,16 +65,6 @@ LW_DEV LaneCtx lane_ctx(const KArgs &a, int waves = WAVES)
 // WPG wavefronts per workgroup cover WPG consecutive column blocks of one row
 // band; with WPG >= K/256 a workgroup holds whole rows and the reduction
 // stays in LDS.
-// s_setprio P when `on` (wave-uniform) is nonzero.  The test and the skip
-// sit inside one asm statement, so the unrolled decode loop around it stays
-// one basic block (a branch there splits its scheduling and register
-// allocation).
-template <int P>
-LW_DEV void lw_progress_priority(int on)
-{
-    asm volatile("s_cmp_eq_u32 %0, 0\n\ts_cbranch_scc1 1f\n\ts_setprio %1\n1:" ::"s"(on), "i"(P) : "scc");
-}
-
 template <int KIND, int N8, int N16, int BATCH, int WPG>
 __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
 {
@@ -137,15 +127,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
                 u32x4 v[BATCH];
             };
             auto fetch = [&](int g) {
-                // with the whole grid resident, issue priority falls with
-                // progress (3 at the start, 0 in the last quarter), so the
-                // wavefronts sharing a SIMD finish together instead of oldest
-                // first; with several generations of wavefronts it would hold
-                // back the ones about to free their slots
-                if (g == 0) lw_progress_priority<3>(a.ramp);
-                if (g == NG / 4) lw_progress_priority<2>(a.ramp);
-                if (g == NG / 2) lw_progress_priority<1>(a.ramp);
-                if (g == 3 * NG / 4) lw_progress_priority<0>(a.ramp);
+                lw_ramp<NG>(a.ramp, g);
                 XA r;
 #pragma unroll
                 for (int b = 0; b < BATCH; b++) {
@@ -243,7 +225,8 @@ __global__ __launch_bounds__(256) void k_decode_q(KArgs a)
         uint32_t buf[PART];
         uint32_t pk = 0;
         lw_decode_pipelined<N8, N16, PART, NoAux, true>(
-            d, a, [](int) { return LW_TPAY_HI - LW_TPAY; }, [](int) { return NoAux{}; },
+            d, a, [](int) { return LW_TPAY_HI - LW_TPAY; },
+            [](int) { return NoAux{}; },
             [&](int g, int j, uint32_t sym, const NoAux &) {
                 pk |= sym << (8 * j);
                 if (j == 3) {
@@ -264,8 +247,7 @@ hipError_t launch_gemv_wpg(const KArgs &a0, hipStream_t s)
 {
     KArgs a = a0;
     a.groups = (a.n_cb + WPG - 1) / WPG;  // column groups combined through the workspace (none if 1)
-    // one wavefront per tile: resident at once if at most four a SIMD
-    a.ramp = (int64_t)a.n_rb * a.n_cb <= 16 * (int64_t)lw_device_cu_count() ? 1 : 0;
+    a.ramp = lw_resident_ramp((int64_t)a.n_rb * a.n_cb);
     const LdsLayout L = lds_layout(BATCH, a.max_words, false, WPG);
     dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
     auto kern = k_gemv_q<KIND, N8, N16, BATCH, WPG>;

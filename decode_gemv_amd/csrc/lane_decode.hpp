@@ -83,6 +83,14 @@ inline int lw_device_cu_count()
     return cus[dev];
 }
 
+// Host: whether a grid of one wavefront per tile is resident at once (at
+// most four wavefronts a SIMD): 1 or 0, the kernels' `ramp` argument.
+inline int lw_resident_ramp(int64_t waves)
+{
+    const int cus = lw_device_cu_count();
+    return cus > 0 && waves <= 16 * (int64_t)cus ? 1 : 0;
+}
+
 // Host: allow kernel KERN the device's largest dynamic LDS allocation, once
 // per device.  The limit is a permission, not an allocation (a launch still
 // reserves only what it asks for), so raising it to the maximum once keeps
@@ -423,6 +431,34 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
     use_group(0, NG - 2);
     use_group(1, NG - 1);
 #undef LW_FENCE
+}
+
+// s_setprio P when `on` (wave-uniform) is nonzero.  The test and the skip
+// sit inside one asm statement, so an unrolled decode loop around it stays
+// one basic block (a branch there splits its scheduling and register
+// allocation).
+template <int P>
+LW_DEV void lw_progress_priority(int on)
+{
+    asm volatile("s_cmp_eq_u32 %0, 0\n\ts_cbranch_scc1 1f\n\ts_setprio %1\n1:" ::"s"(on), "i"(P) : "scc");
+}
+
+// Issue priority that falls with a wavefront's progress through its NG
+// groups (3 in the first quarter, 0 in the last), when `on`: with the whole
+// grid resident, the wavefronts sharing a SIMD then finish together instead
+// of oldest first (the hardware's order), which would leave the last-staged
+// one decoding alone at the end.  With several generations of wavefronts it
+// would hold back the ones about to free their slots, so the host passes 0.
+// Decode-only kernels keep the hardware's order: there the staggered ends
+// overlap each wavefront's output stores with the others' decoding.  g must
+// fold to a constant (fully unrolled loops).
+template <int NG>
+LW_DEV void lw_ramp(int on, int g)
+{
+    if (g == 0) lw_progress_priority<3>(on);
+    if (g == NG / 4) lw_progress_priority<2>(on);
+    if (g == NG / 2) lw_progress_priority<1>(on);
+    if (g == 3 * NG / 4) lw_progress_priority<0>(on);
 }
 
 // Set up a lane's decoder on its staged tile.  Returns false (the kernel must
