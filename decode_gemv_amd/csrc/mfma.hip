@@ -201,7 +201,7 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
                 }
             } else {
                 struct NoAux {};
-                lw_decode_pipelined<N8, N16, NG, NoAux>(
+                lw_decode_pipelined<N8, N16, NG, NoAux, true>(
                     d, a, pay_off, [](int) { return NoAux{}; },
                     [&](int g, int j, uint32_t pay, const NoAux &) { put(g, j, pay, 0u); });
             }
