@@ -8,11 +8,14 @@
 // starts).  So every lane runs one serial chain of 128 (Q4) or 256 (Q6)
 // symbols, there are twice as many wavefronts to hide each other's latency,
 // and all 64 lanes consume the same activation pair at each step (x is read
-// once per wavefront from LDS).  A workgroup of four wavefronts covers four
+// once per wavefront from LDS).  A workgroup of four wavefronts (sixteen,
+// whole rows, when a row band has 13 to 16 column blocks) covers that many
 // consecutive column blocks of one row band; workgroups of different column
 // groups are combined by a fixed-order reduction through the bundle's
 // workspace (the last workgroup to arrive sums the partials in group order),
-// so the result is deterministic.
+// so the result is deterministic.  When the whole grid is resident at once,
+// each wavefront lowers its issue priority as its decode progresses, so the
+// wavefronts sharing a SIMD finish together.
 //
 // Dequantisation w = d*q - m per 256-weight super-block (one tile row) is
 // applied after the dot product: y = d * sum(q x) - m * sum(x).
@@ -94,10 +97,11 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
         xv[b][1] = xg[(size_t)b * (a.cols / 2) + c.lane + 64];
     }
     // With 16 wavefronts a workgroup (whole rows, one workgroup a CU) the
-    // tile loads go out after the table barrier instead: the barrier then
-    // waits only for the small loads, not behind 16 tiles' worth of words,
-    // which measures about 5 % faster on a 16-block row band; with four
-    // wavefronts the order makes no difference.
+    // tile loads go out after the table barrier instead: issued before it,
+    // a wavefront whose loads the memory system holds back (the whole
+    // matrix is requested at once) reaches the barrier late and stalls all
+    // 16, about 5 % on a 16-block row band; with four wavefronts the order
+    // makes no difference.
     LwTileRegs64 tile;
     if constexpr (WPG != 16) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     lw_tab_put<lw_compact<N16>()>(lds, tr, a);
