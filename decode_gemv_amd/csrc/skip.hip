@@ -157,7 +157,7 @@ __global__ __launch_bounds__(1024) void k_skip(SkipArgs a)
 
     // stage x: item (b, j) arranges word column j's activations of batch row
     // b; the 8 items of a chunk sit in 8 aligned consecutive lanes, which sum
-    // the chunk's activations by shuffles (the item count is a multiple of 8)
+    // the chunk's activations by lane sums (the item count is a multiple of 8)
     const int wpc = a.n_jc * SK_CW;                      // word columns of the matrix
     for (int item = tid; item < BATCH * wpc; item += nt) {
         const int b = item / wpc, j = item % wpc;
@@ -180,9 +180,11 @@ __global__ __launch_bounds__(1024) void k_skip(SkipArgs a)
         const uint32_t ad = lb + L.xs + 4u * (uint32_t)((b * n_jc + j / SK_CW) * G::XCS + (j % SK_CW) * G::XU);
 #pragma unroll
         for (int k = 0; k < G::XU; k++) *(lw_lds_w32 *)(size_t)(ad + 4u * k) = P[k];
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
-        s += __shfl_xor(s, 4, 64);
+        // sum over the 8 lanes of the chunk (whole 8-lane groups are active):
+        // DPP pairs, quads and the half-row mirror, no LDS round trip
+        s = lw_dpp_add<0xB1>(s);
+        s = lw_dpp_add<0x4E>(s);
+        s = lw_dpp_add<0x141>(s);
         if ((j & 7) == 0)
             *(lw_lds_w32 *)(size_t)(lb + L.sxs + 4u * (uint32_t)(b * n_jc + j / SK_CW)) = __builtin_bit_cast(uint32_t, s);
     }
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(1024) void k_skip(SkipArgs a)
 #pragma unroll
         for (int b = 0; b < BATCH; b++) {
             float v = acc[r][b];
-            v += __shfl_xor(v, 8, 64);
+            v = lw_dpp_add<0x128>(v);                   // row_ror:8, lane i ^ 8 within its row
             v += __shfl_xor(v, 16, 64);
             v += __shfl_xor(v, 32, 64);
             acc[r][b] = v;
