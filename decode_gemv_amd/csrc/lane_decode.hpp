@@ -141,6 +141,13 @@ LW_DEV float lw_dpp_add(float v)
     return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
+// Sum over aligned groups of W lanes (W a power of two, at most 64, every
+// lane of a group active), the group's sum in each of its lanes: DPP steps
+// inside rows of 16 lanes (pairs, quads, eights by the half-row mirror,
+// sixteens by rotating the row by 8), LDS permutes across rows.
+template <int W>
+LW_DEV float lw_group_sum(float v);
+
 // Sum over the 64 lanes of a wavefront (every lane active), the same value
 // in every lane: four DPP steps sum each row of 16 lanes (pairs, quads,
 // eights by the half-row mirror, rows by the row mirror), then the four row
@@ -154,6 +161,19 @@ LW_DEV float lw_wave_sum(float v)
     const int i = __builtin_bit_cast(int, v);
     auto lane = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(i, l)); };
     return (lane(0) + lane(16)) + (lane(32) + lane(48));
+}
+
+template <int W>
+LW_DEV float lw_group_sum(float v)
+{
+    static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "group of 1 to 64 lanes, a power of two");
+    if constexpr (W >= 2) v = lw_dpp_add<0xB1>(v);    // quad_perm [1,0,3,2]
+    if constexpr (W >= 4) v = lw_dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]
+    if constexpr (W >= 8) v = lw_dpp_add<0x141>(v);   // row_half_mirror
+    if constexpr (W >= 16) v = lw_dpp_add<0x128>(v);  // row_ror:8
+    if constexpr (W >= 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (W >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
 }
 
 // LDS accessed by byte address (the kernels allocate only dynamic LDS, so

@@ -180,11 +180,7 @@ __global__ __launch_bounds__(1024) void k_skip(SkipArgs a)
         const uint32_t ad = lb + L.xs + 4u * (uint32_t)((b * n_jc + j / SK_CW) * G::XCS + (j % SK_CW) * G::XU);
 #pragma unroll
         for (int k = 0; k < G::XU; k++) *(lw_lds_w32 *)(size_t)(ad + 4u * k) = P[k];
-        // sum over the 8 lanes of the chunk (whole 8-lane groups are active):
-        // DPP pairs, quads and the half-row mirror, no LDS round trip
-        s = lw_dpp_add<0xB1>(s);
-        s = lw_dpp_add<0x4E>(s);
-        s = lw_dpp_add<0x141>(s);
+        s = lw_group_sum<8>(s);                          // whole 8-lane groups are active
         if ((j & 7) == 0)
             *(lw_lds_w32 *)(size_t)(lb + L.sxs + 4u * (uint32_t)(b * n_jc + j / SK_CW)) = __builtin_bit_cast(uint32_t, s);
     }
