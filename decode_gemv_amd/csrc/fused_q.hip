@@ -96,17 +96,17 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
         xv[b][0] = xg[(size_t)b * (a.cols / 2) + c.lane];
         xv[b][1] = xg[(size_t)b * (a.cols / 2) + c.lane + 64];
     }
-    // With 16 wavefronts a workgroup (whole rows, one workgroup a CU) the
-    // tile loads go out after the table barrier instead: issued before it,
-    // a wavefront whose loads the memory system holds back (the whole
-    // matrix is requested at once) reaches the barrier late and stalls all
-    // 16, about 5 % on a 16-block row band; with four wavefronts the order
-    // makes no difference.
+    // With 14 or 16 wavefronts a workgroup (one workgroup a CU) the tile
+    // loads go out after the table barrier instead: issued before it, a
+    // wavefront whose loads the memory system holds back (the whole matrix
+    // is requested at once) reaches the barrier late and stalls all of
+    // them, about 5 % on a 16-block row band; with four wavefronts the
+    // order makes no difference.
     LwTileRegs64 tile;
-    if constexpr (WPG != 16) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
+    if constexpr (WPG <= WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     lw_tab_put<lw_compact<N16>()>(lds, tr, a);
     __syncthreads();                      // the decoder table is complete
-    if constexpr (WPG == 16) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
+    if constexpr (WPG > WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
 #pragma unroll
     for (int b = 0; b < BATCH; b++) {
         *(lw_lds_w32 *)(size_t)(xs_addr + 4u * (b * 128 + c.lane)) = xv[b][0];
@@ -262,14 +262,23 @@ hipError_t launch_gemv_wpg(const KArgs &a0, hipStream_t s)
 }
 
 // Whole rows per workgroup (16 wavefronts, no cross-workgroup reduction) when
-// a row band has 13..16 column blocks and the tiles fit in LDS; else four.
+// a row band has 13..16 column blocks and the tiles fit in LDS; 14 wavefronts
+// (a few column groups, every wavefront active) when the column blocks are a
+// multiple of 14 (K = 14336 and 28672, compact tables) and the whole grid is
+// resident at once (with several generations, workgroups this large free
+// their CU only all together: 8 % slower on 8192x28672); else four.
 template <int KIND, int N8, int N16, int BATCH>
 hipError_t launch_gemv_q(const KArgs &a, hipStream_t s)
 {
     if constexpr (BATCH <= 4) {
-        if (a.n_cb > 12 && a.n_cb <= 16 &&
-            lds_layout(BATCH, a.max_words, false, 16).total <= (uint32_t)lw_device_lds_bytes())
+        const uint32_t lds = (uint32_t)lw_device_lds_bytes();
+        if (a.n_cb > 12 && a.n_cb <= 16 && lds_layout(BATCH, a.max_words, false, 16).total <= lds)
             return launch_gemv_wpg<KIND, N8, N16, BATCH, 16>(a, s);
+        if constexpr (lw_compact<N16>()) {
+            if (a.n_cb > 16 && a.n_cb % 14 == 0 && lw_resident_ramp((int64_t)a.n_rb * a.n_cb) &&
+                lds_layout(BATCH, a.max_words, false, 14).total <= lds)
+                return launch_gemv_wpg<KIND, N8, N16, BATCH, 14>(a, s);
+        }
     }
     return launch_gemv_wpg<KIND, N8, N16, BATCH, WAVES>(a, s);
 }

@@ -72,10 +72,12 @@ def _decode_q(dg, torch, db, kind, rows, cols, n_tiles):
 SMALL_Q = [
     # kind, rows, cols, law, seed  (edge shapes: one tile, odd row bands,
     # column blocks not a multiple of four, several column groups, whole-row
-    # workgroups with all and with some wavefronts active)
+    # workgroups with all and with some wavefronts active, 14-wavefront
+    # workgroups in two and three column groups)
     ("q4", 64, 256, "normal", 101), ("q4", 192, 768, "normal", 102), ("q4", 256, 1024, "normal", 103),
     ("q4", 128, 1280, "laplace", 104), ("q4", 320, 2304, "normal", 105), ("q4", 64, 4096, "normal", 106),
     ("q4", 192, 3584, "normal", 109), ("q6", 128, 3328, "normal", 115),
+    ("q4", 128, 7168, "normal", 116), ("q4", 64, 10752, "laplace", 117), ("q6", 64, 7168, "normal", 118),
     ("q4", 128, 512, "uniform", 107), ("q4", 64, 512, "const", 108),
     ("q6", 64, 256, "normal", 111), ("q6", 192, 1280, "normal", 112), ("q6", 128, 2048, "uniform", 113),
     ("q6", 64, 768, "const", 114),
