@@ -377,8 +377,27 @@ static lw_status finish_table(int n_alpha, const std::vector<uint64_t> &hist, ui
     return LW_OK;
 }
 
-extern "C" lw_status lw_bundle_build_q(int kind, int64_t rows, int64_t cols, const uint8_t *q,
-                                       const uint16_t *d, const uint16_t *m, lw_bundle **out)
+// Code lengths given by the caller: every symbol that occurs needs a length
+// of 1..11, an absent one may have 0, and the lengths must satisfy Kraft's
+// inequality (a prefix code exists).
+static lw_status user_table(int n_alpha, const std::vector<uint64_t> &hist, const uint8_t *user, uint8_t *lens,
+                            uint16_t *codes, lw_table &tab, int &n_sym)
+{
+    uint64_t kraft = 0;                              // in units of 2^-11
+    for (int s = 0; s < n_alpha; s++) {
+        lens[s] = user[s];
+        if (lens[s] > LW_MAXLEN || (hist[s] && lens[s] == 0))
+            return lw_fail(LW_E_TABLE, "a symbol that occurs needs a code length of 1..11");
+        if (lens[s]) kraft += 1ull << (LW_MAXLEN - lens[s]);
+    }
+    if (kraft > (1ull << LW_MAXLEN)) return lw_fail(LW_E_TABLE, "code lengths violate the Kraft inequality");
+    n_sym = canonical_table(n_alpha, lens, codes, &tab);
+    if (n_sym < 0) return lw_fail(LW_E_TABLE, "code length above 11");
+    return LW_OK;
+}
+
+static lw_status build_q(int kind, int64_t rows, int64_t cols, const uint8_t *q, const uint16_t *d,
+                         const uint16_t *m, const uint8_t *user_lens, lw_bundle **out)
 {
     if (!out) return lw_fail(LW_E_ARG, "out is null");
     *out = nullptr;
@@ -419,7 +438,9 @@ extern "C" lw_status lw_bundle_build_q(int kind, int64_t rows, int64_t cols, con
         uint16_t codes[256];
         lw_table tab;
         int n_sym = 0;
-        if ((st = finish_table(n_alpha, hist, lens, codes, tab, n_sym))) return st;
+        st = user_lens ? user_table(n_alpha, hist, user_lens, lens, codes, tab, n_sym)
+                       : finish_table(n_alpha, hist, lens, codes, tab, n_sym);
+        if (st) return st;
 
         auto sym = [&](int64_t t, int l, int k) -> int {
             int64_t rb = t / sh.n_cb, cb = t % sh.n_cb;
@@ -459,6 +480,23 @@ extern "C" lw_status lw_bundle_build_q(int kind, int64_t rows, int64_t cols, con
     } catch (const std::bad_alloc &) {
         return lw_fail(LW_E_NOMEM, "host allocation failed");
     }
+}
+
+extern "C" lw_status lw_bundle_build_q(int kind, int64_t rows, int64_t cols, const uint8_t *q,
+                                       const uint16_t *d, const uint16_t *m, lw_bundle **out)
+{
+    return build_q(kind, rows, cols, q, d, m, nullptr, out);
+}
+
+extern "C" lw_status lw_bundle_build_q_lens(int kind, int64_t rows, int64_t cols, const uint8_t *q,
+                                            const uint16_t *d, const uint16_t *m, const uint8_t *lens,
+                                            lw_bundle **out)
+{
+    if (!lens) {
+        if (out) *out = nullptr;
+        return lw_fail(LW_E_ARG, "lens is null");
+    }
+    return build_q(kind, rows, cols, q, d, m, lens, out);
 }
 
 extern "C" lw_status lw_bundle_build_bf16(int64_t rows, int64_t cols, const uint16_t *w, lw_bundle **out)

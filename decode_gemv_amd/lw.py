@@ -54,6 +54,7 @@ def _load():
     P, i64, i32, st = C.c_void_p, C.c_int64, C.c_int, C.c_int
     sig = {
         "lw_bundle_build_q": (st, [i32, i64, i64, P, P, P, C.POINTER(P)]),
+        "lw_bundle_build_q_lens": (st, [i32, i64, i64, P, P, P, P, C.POINTER(P)]),
         "lw_bundle_build_bf16": (st, [i64, i64, P, C.POINTER(P)]),
         "lw_bundle_load": (st, [P, C.c_size_t, C.POINTER(P)]),
         "lw_bundle_validate": (st, [P]),
@@ -138,6 +139,21 @@ def lw_bundle_build_q(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray
     m, pm = _np(m, np.uint16)
     out = C.c_void_p()
     _check(_L.lw_bundle_build_q(kind, rows, cols, pc, pd, pm, C.byref(out)))
+    return Bundle(out.value)
+
+
+def lw_bundle_build_q_lens(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray, lens: np.ndarray) -> Bundle:
+    rows, cols = codes.shape
+    codes, pc = _np(codes, np.uint8)
+    d, pd = _np(d, np.uint16)
+    m, pm = _np(m, np.uint16)
+    n = 256 if kind == LW_Q4_PAIR else 64
+    lens = np.ascontiguousarray(lens, dtype=np.uint8)
+    if lens.size != n:
+        raise ValueError(f"lens must hold {n} lengths")
+    lens, pl = _np(lens, np.uint8)
+    out = C.c_void_p()
+    _check(_L.lw_bundle_build_q_lens(kind, rows, cols, pc, pd, pm, pl, C.byref(out)))
     return Bundle(out.value)
 
 

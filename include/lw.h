@@ -139,6 +139,19 @@ typedef struct {
 lw_status lw_bundle_build_q(int kind, int64_t rows, int64_t cols, const uint8_t *codes,
                             const uint16_t *d, const uint16_t *m, lw_bundle **out);
 
+/* As lw_bundle_build_q, with the code lengths chosen by the caller instead of
+ * the library's compact code ("2 . Code them" fixes only the 11-bit limit and
+ * one table per matrix): any prefix code of at most 11 bits, for instance the
+ * optimal length-limited code.  A table with more than four lengths, or with a
+ * shorter length above 8, takes the decoders' general counting plan.
+ *   lens : host u8 [256] (Q4: one per pair symbol lo | hi << 4) or [64] (Q6),
+ *          the code length of each symbol; a symbol that occurs needs 1..11,
+ *          an absent one may have 0.  Copied, not retained.
+ * Errors: as lw_bundle_build_q, LW_E_ARG for a null lens, LW_E_TABLE for a
+ * missing or too long length or lengths that violate Kraft's inequality. */
+lw_status lw_bundle_build_q_lens(int kind, int64_t rows, int64_t cols, const uint8_t *codes,
+                                 const uint16_t *d, const uint16_t *m, const uint8_t *lens, lw_bundle **out);
+
 /* Build a bf16 exponent-coded bundle ("Unweight", exponent palette and
  * verbatim rows).  w: host bf16 bits [rows][cols].  Errors as above. */
 lw_status lw_bundle_build_bf16(int64_t rows, int64_t cols, const uint16_t *w, lw_bundle **out);

@@ -58,6 +58,49 @@ def test_builder_matches_oracle_bytes(kind, rows, cols, law, seed):
     _compare_q(kind, codes, d, m)
 
 
+@pytest.mark.parametrize("kind,law,seed", [(dg.LW_Q4_PAIR, "normal", 41), (dg.LW_Q4_PAIR, "laplace", 42),
+                                            (dg.LW_Q6_SINGLE, "normal", 43)])
+def test_builder_with_given_lengths_matches_oracle(kind, law, seed):
+    """Caller-chosen code lengths (here the optimal 11-bit-limited code by
+    package-merge, which uses more than four lengths: the decoders' general
+    plan) give the oracle's canonical table, tile offsets, words and splits."""
+    qmax = 15 if kind == dg.LW_Q4_PAIR else 63
+    codes, d, m, _ = synth.gen_q_custom(192, 1280, seed, qmax=qmax, law=law,
+                                        mu=7.5 if qmax == 15 else 31.5, scale=1.8 if qmax == 15 else 5.0)
+    ok = O.Q4 if kind == dg.LW_Q4_PAIR else O.Q6
+    syms = O.symbolise_q(ok, codes)
+    lens = O.package_merge(O.histogram(syms, O.alphabet(ok)))
+    assert len(set(lens[lens > 0].tolist())) > 4
+    tab = O.canonical(lens)
+    spl = O.symbols_per_lane(ok)
+    tile_off, words, _ = O.encode_tiles(syms, spl, lens, tab["codes"])
+    pb = dg.lw_bundle_build_q_lens(kind, codes, d, m, lens)
+    dg.lw_bundle_validate(pb)
+    t = _table_from_region(pb)
+    for k in ("count", "first", "limit", "offset"):
+        assert np.array_equal(t[k], tab[k]), k
+    assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_TILE_OFF, np.uint32), tile_off)
+    assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_WORDS, np.uint32), words)
+    assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_SPLIT, np.uint16), O.row_split(syms, spl, lens))
+
+
+def test_given_lengths_rejected():
+    codes, d, m, _ = synth.gen_q_custom(64, 256, 44)
+    syms = O.symbolise_q(O.Q4, codes)
+    lens = O.package_merge(O.histogram(syms, 256))
+    missing = lens.copy()
+    missing[np.flatnonzero(lens)[0]] = 0                  # a symbol that occurs without a length
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_bundle_build_q_lens(dg.LW_Q4_PAIR, codes, d, m, missing)
+    assert e.value.status == dg.LW_E_TABLE
+    with pytest.raises(dg.LwError) as e:                  # 256 codes of one bit: Kraft sum 128
+        dg.lw_bundle_build_q_lens(dg.LW_Q4_PAIR, codes, d, m, np.ones(256, np.uint8))
+    assert e.value.status == dg.LW_E_TABLE
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_bundle_build_q_lens(dg.LW_Q4_PAIR, codes, d, m, np.full(256, 12, np.uint8))
+    assert e.value.status == dg.LW_E_TABLE
+
+
 def test_builder_matches_oracle_workload_shapes():
     for wl in ("q4_256x1024", "q4_up_14336x4096", "q4_down_4096x14336", "q6_mlp_70b"):
         mat = synth.WORKLOADS[wl][0]

@@ -282,6 +282,34 @@ def test_gemv_mfma_small(torch, dg, case, batch):
     assert np.array_equal(y, _run_gemv(dg, torch, db, x, batch, rows))
 
 
+GENERAL_Q = [("q4", 192, 1280, "normal", 131), ("q4", 128, 4096, "laplace", 132), ("q6", 128, 1024, "normal", 133)]
+
+
+@pytest.mark.parametrize("case", GENERAL_Q, ids=lambda c: "-".join(map(str, c)))
+def test_general_plan_tables(torch, dg, case):
+    """Bundles built with the optimal 11-bit-limited code (package-merge, more
+    than four lengths) take the decoders' general counting plan: decode-only
+    restores every code, and the fused GEMV (VALU at batch 1 and 3, matrix
+    cores at 16; whole-row workgroups on the 4096-column case) matches the
+    oracle."""
+    kind_s, rows, cols, law, seed = case
+    say("general plan", case)
+    kind = dg.LW_Q4_PAIR if kind_s == "q4" else dg.LW_Q6_SINGLE
+    ok = O.Q4 if kind_s == "q4" else O.Q6
+    codes, d, m, x = _gen_small(*case)
+    syms = O.symbolise_q(ok, codes)
+    lens = O.package_merge(O.histogram(syms, O.alphabet(ok)))
+    assert len(set(lens[lens > 0].tolist())) > 4
+    b = dg.lw_bundle_build_q_lens(kind, codes, d, m, lens)
+    info = dg.lw_bundle_get_info(b)
+    db = _upload(dg, torch, b)
+    q, _ = _decode_q(dg, torch, db, kind, rows, cols, info["n_tiles"])
+    assert np.array_equal(q, codes)
+    for batch in (1, 3, 16):
+        y = _run_gemv(dg, torch, db, x, batch, rows)
+        assert rel_err(y, O.gemv_q(codes, d, m, x, batch)) <= TOL
+
+
 @pytest.mark.parametrize("case", SMALL_BF16[:4], ids=lambda c: "-".join(map(str, c)))
 @pytest.mark.parametrize("batch", [8, 16])
 def test_bf16_gemv_mfma_small(torch, dg, case, batch):
