@@ -83,12 +83,97 @@ static void parallel_for(int64_t n, F f)
     for (auto &x : th) x.join();
 }
 
-// Code lengths: the cheapest prefix code with lengths <= 11 that uses at
-// most four distinct lengths, the three shorter of them <= 8 ("compact").
-// A lane then finds a code's length with three comparisons of the top 8
-// peek bits against per-length limits, and the shift from a four-entry byte
-// table (lane_decode.hpp); against the optimal 11-bit-limited code this
-// costs +0.6 % bits on the 4-bit pair histogram of the workloads.
+// Code lengths of the format: the optimal prefix code whose lengths do not
+// exceed 11 bits ("2 . Code them": a length-limited Huffman table with
+// 11-bit codes), found by package-merge (Larmore and Hirschberg's
+// coin-collector method).  Each symbol with a nonzero count is a coin of
+// every denomination 2^-1 .. 2^-11; packages are formed level by level from
+// the smallest denominations up, and the cheapest 2n - 2 items of the last
+// level give every symbol's length as the number of items it appears in.
+// Ties are broken so that the result is reproducible: leaves ordered by
+// (count, symbol), a level's items paired in list order, and a leaf placed
+// before a package of equal weight.
+//
+// Here the items live in one arena: a leaf refers to its symbol, a package
+// to its two children, and a symbol's length is counted by walking the
+// chosen items down to their leaves.
+namespace {
+struct PmItem {
+    uint64_t w;
+    int32_t a, b;                  // leaf: a = symbol, b = -1; package: the two child items
+};
+}
+
+static bool package_merge_lengths(int n_alpha, const uint64_t *counts, uint8_t *lens)
+{
+    std::vector<int> leaves;
+    for (int s = 0; s < n_alpha; s++) {
+        lens[s] = 0;
+        if (counts[s]) leaves.push_back(s);
+    }
+    const int n = (int)leaves.size();
+    if (n == 0) return true;
+    if (n == 1) {
+        lens[leaves[0]] = 1;
+        return true;
+    }
+    if (n > (1 << LW_MAXLEN)) return false;
+    std::stable_sort(leaves.begin(), leaves.end(), [&](int x, int y) { return counts[x] < counts[y]; });
+    std::vector<PmItem> arena;
+    arena.reserve((size_t)n * (LW_MAXLEN + 1) * 2);
+    std::vector<int32_t> leaf_item(n);
+    for (int i = 0; i < n; i++) {
+        leaf_item[i] = (int32_t)arena.size();
+        arena.push_back(PmItem{counts[leaves[i]], leaves[i], -1});
+    }
+    std::vector<int32_t> level(leaf_item), next;
+    for (int depth = 1; depth < LW_MAXLEN; depth++) {
+        // packages of adjacent items of this level, in order
+        std::vector<int32_t> pk;
+        for (size_t k = 0; k + 1 < level.size(); k += 2) {
+            pk.push_back((int32_t)arena.size());
+            arena.push_back(PmItem{arena[level[k]].w + arena[level[k + 1]].w, level[k], level[k + 1]});
+        }
+        // the next level: the leaves and these packages by weight, a leaf first on ties
+        next.clear();
+        size_t i = 0, j = 0;
+        while (i < leaf_item.size() || j < pk.size()) {
+            const bool leaf = j == pk.size() || (i < leaf_item.size() && arena[leaf_item[i]].w <= arena[pk[j]].w);
+            next.push_back(leaf ? leaf_item[i++] : pk[j++]);
+        }
+        level.swap(next);
+    }
+    // walk the first 2n - 2 items down to their leaves
+    std::vector<int32_t> stack;
+    std::vector<uint32_t> depthcount(n_alpha, 0);
+    for (int k = 0; k < 2 * n - 2 && k < (int)level.size(); k++) {
+        stack.push_back(level[k]);
+        while (!stack.empty()) {
+            const PmItem it = arena[stack.back()];
+            stack.pop_back();
+            if (it.b < 0) {
+                depthcount[it.a]++;
+            } else {
+                stack.push_back(it.a);
+                stack.push_back(it.b);
+            }
+        }
+    }
+    for (int s = 0; s < n_alpha; s++) {
+        if (depthcount[s] > LW_MAXLEN) return false;
+        lens[s] = (uint8_t)depthcount[s];
+    }
+    return true;
+}
+
+// The compact code (an opt-in of lw_bundle_build_q_compact and
+// lw_bundle_build_bf16_compact, not the format's default): the cheapest
+// prefix code with lengths <= 11 that uses at most four distinct lengths, the
+// three shorter of them <= 8.  A lane then finds a code's length with one
+// pair of byte-sum comparisons of the top 8 peek bits and the shift from a
+// four-entry byte table (lane_decode.hpp).  Against the optimal code this
+// costs bits: +0.6 % on the 4-bit pair histogram of the up projection,
+// +2.2 % on the sharper histogram of the down projection.
 //
 // Symbols with a nonzero count are ranked by (count desc, symbol asc); a
 // length set a < b < c <= 8, c < d <= 11 takes the first n1 ranks at length
@@ -367,11 +452,12 @@ static lw_status check_shape(int64_t rows, int64_t cols, Shape &sh)
     return LW_OK;
 }
 
-static lw_status finish_table(int n_alpha, const std::vector<uint64_t> &hist, uint8_t *lens,
+static lw_status finish_table(int n_alpha, const std::vector<uint64_t> &hist, int code, uint8_t *lens,
                               uint16_t *codes, lw_table &tab, int &n_sym)
 {
-    if (!compact_lengths(n_alpha, hist.data(), lens))
-        return lw_fail(LW_E_TABLE, "alphabet does not fit the code");
+    const bool ok = code == LW_CODE_COMPACT ? compact_lengths(n_alpha, hist.data(), lens)
+                                            : package_merge_lengths(n_alpha, hist.data(), lens);
+    if (!ok) return lw_fail(LW_E_TABLE, "alphabet does not fit the code");
     n_sym = canonical_table(n_alpha, lens, codes, &tab);
     if (n_sym < 0) return lw_fail(LW_E_TABLE, "code length above 11");
     return LW_OK;
@@ -397,7 +483,7 @@ static lw_status user_table(int n_alpha, const std::vector<uint64_t> &hist, cons
 }
 
 static lw_status build_q(int kind, int64_t rows, int64_t cols, const uint8_t *q, const uint16_t *d,
-                         const uint16_t *m, const uint8_t *user_lens, lw_bundle **out)
+                         const uint16_t *m, const uint8_t *user_lens, int code, lw_bundle **out)
 {
     if (!out) return lw_fail(LW_E_ARG, "out is null");
     *out = nullptr;
@@ -439,7 +525,7 @@ static lw_status build_q(int kind, int64_t rows, int64_t cols, const uint8_t *q,
         lw_table tab;
         int n_sym = 0;
         st = user_lens ? user_table(n_alpha, hist, user_lens, lens, codes, tab, n_sym)
-                       : finish_table(n_alpha, hist, lens, codes, tab, n_sym);
+                       : finish_table(n_alpha, hist, code, lens, codes, tab, n_sym);
         if (st) return st;
 
         auto sym = [&](int64_t t, int l, int k) -> int {
@@ -456,6 +542,7 @@ static lw_status build_q(int kind, int64_t rows, int64_t cols, const uint8_t *q,
         lw_image_header h = plan_image(kind, sh, tile_off[sh.n_tiles], 0);
         h.n_sym = n_sym;
         h.max_words = max_words;
+        h.code = user_lens ? LW_CODE_LENS : code;
         std::unique_ptr<lw_bundle> b(new lw_bundle);
         uint64_t total = lw_align_up(h.off[LW_REG_WORK] + h.bytes[LW_REG_WORK]);
         for (int r = 0; r < LW_REG_COUNT; r++)
@@ -485,7 +572,13 @@ static lw_status build_q(int kind, int64_t rows, int64_t cols, const uint8_t *q,
 extern "C" lw_status lw_bundle_build_q(int kind, int64_t rows, int64_t cols, const uint8_t *q,
                                        const uint16_t *d, const uint16_t *m, lw_bundle **out)
 {
-    return build_q(kind, rows, cols, q, d, m, nullptr, out);
+    return build_q(kind, rows, cols, q, d, m, nullptr, LW_CODE_HUFFMAN, out);
+}
+
+extern "C" lw_status lw_bundle_build_q_compact(int kind, int64_t rows, int64_t cols, const uint8_t *q,
+                                               const uint16_t *d, const uint16_t *m, lw_bundle **out)
+{
+    return build_q(kind, rows, cols, q, d, m, nullptr, LW_CODE_COMPACT, out);
 }
 
 extern "C" lw_status lw_bundle_build_q_lens(int kind, int64_t rows, int64_t cols, const uint8_t *q,
@@ -496,10 +589,10 @@ extern "C" lw_status lw_bundle_build_q_lens(int kind, int64_t rows, int64_t cols
         if (out) *out = nullptr;
         return lw_fail(LW_E_ARG, "lens is null");
     }
-    return build_q(kind, rows, cols, q, d, m, lens, out);
+    return build_q(kind, rows, cols, q, d, m, lens, LW_CODE_LENS, out);
 }
 
-extern "C" lw_status lw_bundle_build_bf16(int64_t rows, int64_t cols, const uint16_t *w, lw_bundle **out)
+static lw_status build_bf16(int64_t rows, int64_t cols, const uint16_t *w, int code, lw_bundle **out)
 {
     if (!out) return lw_fail(LW_E_ARG, "out is null");
     *out = nullptr;
@@ -581,7 +674,7 @@ extern "C" lw_status lw_bundle_build_bf16(int64_t rows, int64_t cols, const uint
         uint16_t codes[16];
         lw_table tab;
         int n_sym = 0;
-        if ((st = finish_table(16, hist, lens, codes, tab, n_sym))) return st;
+        if ((st = finish_table(16, hist, code, lens, codes, tab, n_sym))) return st;
         std::vector<uint32_t> tile_off;
         int32_t max_words = 0;
         encode_tiles(sh, 512, lens, codes, sym, tile_off, max_words, nullptr, nullptr);
@@ -589,6 +682,7 @@ extern "C" lw_status lw_bundle_build_bf16(int64_t rows, int64_t cols, const uint
         h.n_sym = n_sym;
         h.max_words = max_words;
         h.n_pal = n_pal;
+        h.code = code;
         std::unique_ptr<lw_bundle> b(new lw_bundle);
         uint64_t total = 0;
         for (int r = 0; r < LW_REG_COUNT; r++)
@@ -635,6 +729,16 @@ extern "C" lw_status lw_bundle_build_bf16(int64_t rows, int64_t cols, const uint
     }
 }
 
+extern "C" lw_status lw_bundle_build_bf16(int64_t rows, int64_t cols, const uint16_t *w, lw_bundle **out)
+{
+    return build_bf16(rows, cols, w, LW_CODE_HUFFMAN, out);
+}
+
+extern "C" lw_status lw_bundle_build_bf16_compact(int64_t rows, int64_t cols, const uint16_t *w, lw_bundle **out)
+{
+    return build_bf16(rows, cols, w, LW_CODE_COMPACT, out);
+}
+
 // ----------------------------------------------------------------- validate
 static lw_status validate_image(const uint8_t *img, size_t bytes)
 {
@@ -647,6 +751,7 @@ static lw_status validate_image(const uint8_t *img, size_t bytes)
     if (h.n_rb != h.rows / 64 || h.n_cb != h.cols / 256 || h.n_tiles != (int64_t)h.n_rb * h.n_cb)
         return lw_fail(LW_E_FORMAT, "inconsistent tile counts");
     if (h.spl != (h.kind == LW_Q4_PAIR ? 256 : 512)) return lw_fail(LW_E_FORMAT, "bad symbols per lane");
+    if (h.code < LW_CODE_HUFFMAN || h.code > LW_CODE_LENS) return lw_fail(LW_E_FORMAT, "unknown code kind");
     uint64_t prev_end = LW_HEADER_BYTES;
     for (int r = 0; r < LW_REG_COUNT; r++) {
         if (!h.bytes[r]) continue;
@@ -798,6 +903,7 @@ extern "C" lw_status lw_bundle_get_info(const lw_bundle *b, lw_bundle_info *info
     info->image_bytes = b->image.size();
     info->coded_bytes = h.coded_bytes;
     info->twin_bytes = h.twin_bytes;
+    info->code = h.code;
     return LW_OK;
 }
 

@@ -43,7 +43,7 @@ typedef struct {
     int32_t n_pal;
     int64_t n_verbatim;
     int32_t work_groups;           /* split-column groups the workspace is sized for */
-    int32_t reserved0;
+    int32_t code;                  /* lw_code the lengths were chosen by */
     uint64_t coded_bytes;
     uint64_t twin_bytes;
     uint64_t off[LW_REG_COUNT];

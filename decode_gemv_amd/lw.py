@@ -22,6 +22,7 @@ LW_OK, LW_E_ARG, LW_E_SHAPE, LW_E_TABLE, LW_E_FORMAT, LW_E_NOMEM, LW_E_DEVICE, L
 LW_Q4_PAIR, LW_Q6_SINGLE, LW_BF16_EXP = 1, 2, 3
 LW_PIPE_FUSED, LW_PIPE_FULL_DECODE, LW_PIPE_EXPONENT, LW_PIPE_PALETTE, LW_PIPE_DIRECT_PALETTE, LW_PIPE_COUNT = range(6)
 LW_FORM_PALETTE, LW_FORM_EXPONENT = 0, 1
+LW_CODE_HUFFMAN, LW_CODE_COMPACT, LW_CODE_LENS = 0, 1, 2
 LW_RECON_VARIANTS = 5
 (LW_REG_TABLE, LW_REG_GPUTAB, LW_REG_TILE_OFF, LW_REG_WORDS, LW_REG_DM, LW_REG_PALETTE, LW_REG_SM,
  LW_REG_VB_BITS, LW_REG_VB_START, LW_REG_VERBATIM, LW_REG_SPLIT, LW_REG_WORK, LW_REG_COUNT) = range(13)
@@ -40,7 +41,8 @@ class lw_bundle_info(C.Structure):
                 ("max_len", C.c_int32), ("max_words", C.c_int32), ("n_palette", C.c_int32),
                 ("n_verbatim", C.c_int64), ("count_per_len", C.c_uint16 * 12),
                 ("region_offset", C.c_uint64 * LW_REG_COUNT), ("region_bytes", C.c_uint64 * LW_REG_COUNT),
-                ("image_bytes", C.c_uint64), ("coded_bytes", C.c_uint64), ("twin_bytes", C.c_uint64)]
+                ("image_bytes", C.c_uint64), ("coded_bytes", C.c_uint64), ("twin_bytes", C.c_uint64),
+                ("code", C.c_int32), ("reserved", C.c_int32)]
 
 
 def _load():
@@ -54,8 +56,10 @@ def _load():
     P, i64, i32, st = C.c_void_p, C.c_int64, C.c_int, C.c_int
     sig = {
         "lw_bundle_build_q": (st, [i32, i64, i64, P, P, P, C.POINTER(P)]),
+        "lw_bundle_build_q_compact": (st, [i32, i64, i64, P, P, P, C.POINTER(P)]),
         "lw_bundle_build_q_lens": (st, [i32, i64, i64, P, P, P, P, C.POINTER(P)]),
         "lw_bundle_build_bf16": (st, [i64, i64, P, C.POINTER(P)]),
+        "lw_bundle_build_bf16_compact": (st, [i64, i64, P, C.POINTER(P)]),
         "lw_bundle_load": (st, [P, C.c_size_t, C.POINTER(P)]),
         "lw_bundle_validate": (st, [P]),
         "lw_bundle_get_info": (st, [P, C.POINTER(lw_bundle_info)]),
@@ -142,15 +146,30 @@ def lw_bundle_build_q(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray
     return Bundle(out.value)
 
 
+def lw_bundle_build_q_compact(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray) -> Bundle:
+    rows, cols = codes.shape
+    codes, pc = _np(codes, np.uint8)
+    d, pd = _np(d, np.uint16)
+    m, pm = _np(m, np.uint16)
+    out = C.c_void_p()
+    _check(_L.lw_bundle_build_q_compact(kind, rows, cols, pc, pd, pm, C.byref(out)))
+    return Bundle(out.value)
+
+
 def lw_bundle_build_q_lens(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray, lens: np.ndarray) -> Bundle:
     rows, cols = codes.shape
     codes, pc = _np(codes, np.uint8)
     d, pd = _np(d, np.uint16)
     m, pm = _np(m, np.uint16)
     n = 256 if kind == LW_Q4_PAIR else 64
-    lens = np.ascontiguousarray(lens, dtype=np.uint8)
+    lens = np.asarray(lens)
+    # the C side takes one byte per length: refuse what a cast would wrap or truncate
+    if lens.dtype.kind not in "iu":
+        raise ValueError("lens must be an integer array")
     if lens.size != n:
         raise ValueError(f"lens must hold {n} lengths")
+    if lens.size and (lens.min() < 0 or lens.max() > 11):
+        raise ValueError("code lengths must lie in 0..11")
     lens, pl = _np(lens, np.uint8)
     out = C.c_void_p()
     _check(_L.lw_bundle_build_q_lens(kind, rows, cols, pc, pd, pm, pl, C.byref(out)))
@@ -162,6 +181,14 @@ def lw_bundle_build_bf16(w: np.ndarray) -> Bundle:
     w, pw = _np(w, np.uint16)
     out = C.c_void_p()
     _check(_L.lw_bundle_build_bf16(rows, cols, pw, C.byref(out)))
+    return Bundle(out.value)
+
+
+def lw_bundle_build_bf16_compact(w: np.ndarray) -> Bundle:
+    rows, cols = w.shape
+    w, pw = _np(w, np.uint16)
+    out = C.c_void_p()
+    _check(_L.lw_bundle_build_bf16_compact(rows, cols, pw, C.byref(out)))
     return Bundle(out.value)
 
 

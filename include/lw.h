@@ -58,6 +58,16 @@ typedef enum {
     LW_BF16_EXP = 3        /* bf16 weights, exponent palette index coded singly: 16 symbols, 512 per lane */
 } lw_kind;
 
+/* How a bundle's code lengths were chosen (lw_bundle_info.code). */
+typedef enum {
+    LW_CODE_HUFFMAN = 0,   /* the optimal prefix code with lengths <= 11 ("2 . Code them": a
+                              length-limited Huffman table with 11-bit codes), by package-merge */
+    LW_CODE_COMPACT = 1,   /* opt-in: the cheapest prefix code with lengths <= 11 that uses at most
+                              four lengths, the three shorter <= 8 (a smaller decoder comparison plan,
+                              a few tenths of a percent to two percent more bits) */
+    LW_CODE_LENS = 2       /* lengths given by the caller (lw_bundle_build_q_lens) */
+} lw_code;
+
 /* Execution pipelines of lw_gemm ("Unweight", "Four approaches to using
  * compressed weights"). */
 typedef enum {
@@ -123,11 +133,15 @@ typedef struct {
                                   palette (bf16); excludes x, y and the workspace */
     uint64_t twin_bytes;       /* the fixed-width equivalent: rows*cols*bits/8 + rows*cols/256*4
                                   (bf16: rows*cols*2, the dense matrix) */
+    int32_t code;              /* lw_code: how the code lengths were chosen */
+    int32_t reserved;
 } lw_bundle_info;
 
 /* ---------------------------------------------------------------- host side */
 
-/* Build a bundle from quantised codes ("2 . Code them").
+/* Build a bundle from quantised codes ("2 . Code them": one length-limited
+ * Huffman table per matrix, 11-bit codes; the lengths are the optimal prefix
+ * code of at most 11 bits for the matrix's symbol histogram, LW_CODE_HUFFMAN).
  *   kind  : LW_Q4_PAIR or LW_Q6_SINGLE
  *   codes : host [rows][cols] row-major, one code per byte (< 16 or < 64)
  *   d, m  : host fp16 bits [rows][cols/256]: scale and minimum of each
@@ -139,11 +153,17 @@ typedef struct {
 lw_status lw_bundle_build_q(int kind, int64_t rows, int64_t cols, const uint8_t *codes,
                             const uint16_t *d, const uint16_t *m, lw_bundle **out);
 
-/* As lw_bundle_build_q, with the code lengths chosen by the caller instead of
- * the library's compact code ("2 . Code them" fixes only the 11-bit limit and
- * one table per matrix): any prefix code of at most 11 bits, for instance the
- * optimal length-limited code.  A table with more than four lengths, or with a
- * shorter length above 8, takes the decoders' general counting plan.
+/* As lw_bundle_build_q with the compact code (LW_CODE_COMPACT) instead of the
+ * optimal one: an opt-in that trades a little size for a decoder with one
+ * pair of limit comparisons per symbol.  The bit cost is visible in
+ * lw_bundle_info.coded_bytes beside the default bundle's.
+ * Errors: as lw_bundle_build_q. */
+lw_status lw_bundle_build_q_compact(int kind, int64_t rows, int64_t cols, const uint8_t *codes,
+                                    const uint16_t *d, const uint16_t *m, lw_bundle **out);
+
+/* As lw_bundle_build_q, with the code lengths chosen by the caller (LW_CODE_LENS)
+ * instead of the library's ("2 . Code them" fixes the 11-bit limit and one
+ * table per matrix): any prefix code of at most 11 bits.
  *   lens : host u8 [256] (Q4: one per pair symbol lo | hi << 4) or [64] (Q6),
  *          the code length of each symbol; a symbol that occurs needs 1..11,
  *          an absent one may have 0.  Copied, not retained.
@@ -153,8 +173,13 @@ lw_status lw_bundle_build_q_lens(int kind, int64_t rows, int64_t cols, const uin
                                  const uint16_t *d, const uint16_t *m, const uint8_t *lens, lw_bundle **out);
 
 /* Build a bf16 exponent-coded bundle ("Unweight", exponent palette and
- * verbatim rows).  w: host bf16 bits [rows][cols].  Errors as above. */
+ * verbatim rows; the palette indices coded with the optimal prefix code of at
+ * most 11 bits, LW_CODE_HUFFMAN).  w: host bf16 bits [rows][cols].  Errors as
+ * above. */
 lw_status lw_bundle_build_bf16(int64_t rows, int64_t cols, const uint16_t *w, lw_bundle **out);
+
+/* As lw_bundle_build_bf16 with the compact code (LW_CODE_COMPACT). */
+lw_status lw_bundle_build_bf16_compact(int64_t rows, int64_t cols, const uint16_t *w, lw_bundle **out);
 
 /* Re-create a bundle from an image (as returned by lw_bundle_image); the image
  * is copied and validated.  Errors: LW_E_ARG, LW_E_FORMAT, LW_E_TABLE. */

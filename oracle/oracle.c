@@ -224,10 +224,12 @@ int or_package_merge(int n_alpha, const uint64_t *counts, int L, uint8_t *lens)
 }
 
 /* ------------------------------------------------------------------ */
-/* Code lengths of the bundles: the compact code.                        */
+/* Code lengths of the opt-in compact code.                              */
 /* ------------------------------------------------------------------ */
-/* Reading: the pages fix the 11-bit limit and one table per matrix, not how
- * the lengths are chosen.  The bundles use the cheapest prefix code (least
+/* The bundles' default lengths are package-merge's above.  The compact code
+ * is an option of the product (a smaller decoder comparison plan at a small
+ * cost in bits); the oracle builds it so the option can be checked too.  It
+ * is the cheapest prefix code (least
  * total bits sum count * length) among those with lengths <= 11 and at most
  * four distinct lengths, of which the three shorter are <= 8 (so a decoder
  * needs three comparisons of the top 8 peek bits).  Search and ties:

@@ -134,8 +134,8 @@ def package_merge(counts, limit: int = MAXLEN) -> np.ndarray:
 
 
 def compact_lengths(counts) -> np.ndarray:
-    """Lengths of the bundles' code: the cheapest prefix code with lengths
-    <= 11 using at most four distinct lengths, the three shorter <= 8."""
+    """Lengths of the opt-in compact code: the cheapest prefix code with
+    lengths <= 11 using at most four distinct lengths, the three shorter <= 8."""
     counts = np.ascontiguousarray(counts, dtype=np.uint64)
     lens = np.zeros(counts.size, dtype=np.uint8)
     if lib().or_compact_lengths(counts.size, _p(counts), _p(lens)) != 0:
@@ -268,7 +268,19 @@ def row_split(syms: np.ndarray, spl: int, lens: np.ndarray) -> np.ndarray:
     return np.asarray(lens, dtype=np.int64)[s].sum(axis=2).astype(np.uint16).ravel()
 
 
-def build_bundle_q(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray) -> dict:
+def code_lengths(counts, code: str = "huffman") -> np.ndarray:
+    """The bundle's code lengths: "huffman" (the default) is the optimal
+    prefix code with lengths <= 11, the length-limited Huffman table of
+    "LazyWeights", section "2 . Code them", found by package-merge;
+    "compact" is the opt-in code with at most four lengths."""
+    if code == "huffman":
+        return package_merge(counts)
+    if code == "compact":
+        return compact_lengths(counts)
+    raise ValueError(f"unknown code {code!r}")
+
+
+def build_bundle_q(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray, code: str = "huffman") -> dict:
     """Quantised bundle: per-matrix table, tile offsets, interleaved words, dm."""
     R, Cc = codes.shape
     if R % 64 or Cc % 256:
@@ -276,7 +288,7 @@ def build_bundle_q(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray) -
     spl = symbols_per_lane(kind)
     syms = symbolise_q(kind, codes)
     counts = histogram(syms, alphabet(kind))
-    lens = compact_lengths(counts)
+    lens = code_lengths(counts, code)
     tab = canonical(lens)
     tile_off, words, lane_bits = encode_tiles(syms, spl, lens, tab["codes"])
     return dict(kind=kind, rows=R, cols=Cc, spl=spl, counts=counts, table=tab,
@@ -304,7 +316,7 @@ def symbolise_bf16(w: np.ndarray, palette: np.ndarray, n_pal: int, vb_bits: np.n
     return syms
 
 
-def build_bundle_bf16(w: np.ndarray) -> dict:
+def build_bundle_bf16(w: np.ndarray, code: str = "huffman") -> dict:
     R, Cc = w.shape
     if R % 64 or Cc % 256:
         raise ValueError("shape must be a multiple of 64x256")
@@ -320,7 +332,7 @@ def build_bundle_bf16(w: np.ndarray) -> dict:
     L.or_bf16_verbatim(R, Cc, _p(w), _p(palette), n_pal, _p(vb_bits), _p(vb_start), _p(verbatim))
     syms = symbolise_bf16(w, palette, n_pal, vb_bits)
     counts = histogram(syms, 16)
-    lens = compact_lengths(counts)
+    lens = code_lengths(counts, code)
     tab = canonical(lens)
     tile_off, words, lane_bits = encode_tiles(syms, 512, lens, tab["codes"])
     sm = np.zeros(nt * 4096, dtype=np.uint32)

@@ -24,11 +24,13 @@ def _table_from_region(b):
     return dict(count=t[0:12], first=t[12:24], limit=t[24:36], offset=t[36:48], sym_sorted=t[48:])
 
 
-def _compare_q(kind, codes, d, m):
-    ob = O.build_bundle_q(kind, codes, d, m)
-    pb = dg.lw_bundle_build_q(kind, codes, d, m)
+def _compare_q(kind, codes, d, m, code="huffman"):
+    ob = O.build_bundle_q(kind, codes, d, m, code=code)
+    build = dg.lw_bundle_build_q if code == "huffman" else dg.lw_bundle_build_q_compact
+    pb = build(kind, codes, d, m)
     dg.lw_bundle_validate(pb)
     info = dg.lw_bundle_get_info(pb)
+    assert info["code"] == (dg.LW_CODE_HUFFMAN if code == "huffman" else dg.LW_CODE_COMPACT)
     tab = _table_from_region(pb)
     for k in ("count", "first", "limit", "offset"):
         assert np.array_equal(tab[k], ob["table"][k]), k
@@ -51,11 +53,12 @@ def _compare_q(kind, codes, d, m):
     (dg.LW_Q4_PAIR, 128, 768, "laplace", 3), (dg.LW_Q6_SINGLE, 128, 512, "normal", 4),
     (dg.LW_Q4_PAIR, 64, 512, "uniform", 5), (dg.LW_Q4_PAIR, 64, 256, "const", 6),
     (dg.LW_Q6_SINGLE, 64, 256, "uniform", 7), (dg.LW_Q6_SINGLE, 64, 256, "const", 8)])
-def test_builder_matches_oracle_bytes(kind, rows, cols, law, seed):
+@pytest.mark.parametrize("code", ["huffman", "compact"])
+def test_builder_matches_oracle_bytes(kind, rows, cols, law, seed, code):
     qmax = 15 if kind == dg.LW_Q4_PAIR else 63
     codes, d, m, _ = synth.gen_q_custom(rows, cols, seed, qmax=qmax, law=law,
                                         mu=7.5 if qmax == 15 else 31.5, scale=1.8 if qmax == 15 else 5.0)
-    _compare_q(kind, codes, d, m)
+    _compare_q(kind, codes, d, m, code)
 
 
 @pytest.mark.parametrize("kind,law,seed", [(dg.LW_Q4_PAIR, "normal", 41), (dg.LW_Q4_PAIR, "laplace", 42),
@@ -96,24 +99,55 @@ def test_given_lengths_rejected():
     with pytest.raises(dg.LwError) as e:                  # 256 codes of one bit: Kraft sum 128
         dg.lw_bundle_build_q_lens(dg.LW_Q4_PAIR, codes, d, m, np.ones(256, np.uint8))
     assert e.value.status == dg.LW_E_TABLE
-    with pytest.raises(dg.LwError) as e:
-        dg.lw_bundle_build_q_lens(dg.LW_Q4_PAIR, codes, d, m, np.full(256, 12, np.uint8))
-    assert e.value.status == dg.LW_E_TABLE
+    # a length above 11 is refused by the C side (called directly, as any C caller would) ...
+    c12 = np.ascontiguousarray(codes, np.uint8)
+    dd, mm = np.ascontiguousarray(d, np.uint16), np.ascontiguousarray(m, np.uint16)
+    l12 = np.full(256, 12, np.uint8)
+    out = ctypes.c_void_p()
+    st = dg.lw.lib().lw_bundle_build_q_lens(dg.LW_Q4_PAIR, 64, 256, c12.ctypes.data, dd.ctypes.data,
+                                            mm.ctypes.data, l12.ctypes.data, ctypes.byref(out))
+    assert st == dg.LW_E_TABLE and not out.value
+    # ... and by the binding before any byte cast could wrap it (267 would become 11)
+    for bad in (np.full(256, 12, np.int32), np.full(256, 267, np.int64), np.full(256, -1, np.int16),
+                np.full(256, 5.0)):
+        with pytest.raises(ValueError):
+            dg.lw_bundle_build_q_lens(dg.LW_Q4_PAIR, codes, d, m, bad)
 
 
-def test_builder_matches_oracle_workload_shapes():
+@pytest.mark.parametrize("code", ["huffman", "compact"])
+def test_builder_matches_oracle_workload_shapes(code):
     for wl in ("q4_256x1024", "q4_up_14336x4096", "q4_down_4096x14336", "q6_mlp_70b"):
         mat = synth.WORKLOADS[wl][0]
         kind = dg.LW_Q4_PAIR if mat.kind == "q4" else dg.LW_Q6_SINGLE
         codes, d, m, _ = synth.gen_q(mat, rows=min(mat.rows, 256), cols=min(mat.cols, 4096))
-        _compare_q(kind, codes, d, m)
+        _compare_q(kind, codes, d, m, code)
 
 
+def test_default_code_is_the_optimal_length_limited_code():
+    """The default bundle's table is package-merge's (the oracle's optimal
+    11-bit-limited code): its total bits equal the oracle's, the compact
+    option's are never fewer, and lengths 9 to 11 occur (the general
+    comparison plan of the decoders is the one the default format needs)."""
+    mat = synth.WORKLOADS["q4_up_14336x4096"][0]
+    codes, d, m, _ = synth.gen_q(mat, rows=256, cols=4096)
+    counts = O.histogram(O.symbolise_q(O.Q4, codes), 256)
+    pm = O.package_merge(counts).astype(np.int64)
+    huff = dg.lw_bundle_get_info(dg.lw_bundle_build_q(dg.LW_Q4_PAIR, codes, d, m))
+    comp = dg.lw_bundle_get_info(dg.lw_bundle_build_q_compact(dg.LW_Q4_PAIR, codes, d, m))
+    lens_h = np.repeat(np.arange(12), huff["count_per_len"])
+    assert lens_h.size == np.count_nonzero(counts)
+    assert sorted(lens_h.tolist()) == sorted(pm[counts > 0].tolist())
+    assert huff["max_len"] == 11 and huff["min_len"] == 5
+    assert comp["coded_bytes"] >= huff["coded_bytes"]
+    assert huff["code"] == dg.LW_CODE_HUFFMAN and comp["code"] == dg.LW_CODE_COMPACT
+
+
+@pytest.mark.parametrize("code", ["huffman", "compact"])
 @pytest.mark.parametrize("frac,seed", [(0.0, 11), (0.002, 12), (0.02, 13)])
-def test_builder_matches_oracle_bf16(frac, seed):
+def test_builder_matches_oracle_bf16(frac, seed, code):
     w, _ = synth.gen_bf16_custom(128, 512, seed, outlier_frac=frac)
-    ob = O.build_bundle_bf16(w)
-    pb = dg.lw_bundle_build_bf16(w)
+    ob = O.build_bundle_bf16(w, code=code)
+    pb = (dg.lw_bundle_build_bf16 if code == "huffman" else dg.lw_bundle_build_bf16_compact)(w)
     dg.lw_bundle_validate(pb)
     info = dg.lw_bundle_get_info(pb)
     tab = _table_from_region(pb)
