@@ -91,14 +91,58 @@ def parse():
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--copy-calib", action="store_true")
     p.add_argument("--copies", type=int, default=0,
-                   help="bundle copies cycled through (default: enough to exceed twice the MALL; "
-                        "1 measures with the bundle cache-resident)")
+                   help="bundle copies cycled through (default: enough that one pass over their coded "
+                        "bytes exceeds twice the MALL; 1 measures with the bundle cache-resident)")
+    p.add_argument("--code", choices=("huffman", "compact"), default="huffman",
+                   help="code lengths of the timed bundles: the optimal 11-bit-limited Huffman code "
+                        "(the format's default) or the opt-in compact code")
+    p.add_argument("--trace-stats", metavar="CSV",
+                   help="summarise a rocprofv3 kernel trace (kernel_trace.csv) per kernel -- calls, "
+                        "mean, median, p10, p90, min, max in us -- and exit")
     return p.parse_args()
 
 
 def copies_for(nbytes: int) -> int:
-    """Bundle copies needed so that one pass over them exceeds twice the MALL."""
-    return int(max(2, min(64, -(-2 * MALL_BYTES // max(nbytes, 1)))))
+    """Copies needed so that one pass over their `nbytes` each (the bytes a
+    step reads) exceeds twice the MALL."""
+    return int(max(2, min(96, -(-2 * MALL_BYTES // max(nbytes, 1)))))
+
+
+def trace_stats(path: str) -> list:
+    """Per-kernel duration statistics of a rocprofv3 --kernel-trace CSV
+    (columns Kernel_Name, Start_Timestamp, End_Timestamp in ns)."""
+    import csv
+    by = {}
+    with open(path) as fh:
+        for row in csv.DictReader(fh):
+            d = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+            by.setdefault(row["Kernel_Name"], []).append(d)
+    out = []
+    for name, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        a = np.array(v)
+        out.append({"kernel": name, "calls": a.size, "mean_us": round(float(a.mean()), 3),
+                    "median_us": round(float(np.median(a)), 3), "p10_us": round(float(np.percentile(a, 10)), 3),
+                    "p90_us": round(float(np.percentile(a, 90)), 3), "min_us": round(float(a.min()), 3),
+                    "max_us": round(float(a.max()), 3)})
+    return out
+
+
+def host_cpu():
+    """The host's CPU model and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return model, cores, os.cpu_count() or cores
 
 
 def time_loop(torch, fn, n_copies, steps, warmup):
@@ -147,8 +191,8 @@ def time_graph(torch, fn, n_copies, steps, warmup):
 def cpu_baseline(mat, codes, d, m, xb, batch, coded):
     """The oracle as it stands -- limit-method decode of every tile, then the
     fp64 GEMV -- on the whole matrix: once on one thread, then split by row
-    bands over the host's cores (the C routines release the GIL, and row bands
-    are independent, so the threaded result is the same y)."""
+    bands over every core this process may use (the C routines release the
+    GIL, and row bands are independent, so the threaded result is the same y)."""
     from concurrent.futures import ThreadPoolExecutor
     import oracle as O
     ob = O.build_bundle_q(O.KIND[mat.kind], codes, d, m)
@@ -162,7 +206,7 @@ def cpu_baseline(mat, codes, d, m, xb, batch, coded):
     t = time.time()
     y1 = band_range(0, nrb)
     t1 = time.time() - t
-    cores = max(1, min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "16")), 16))
+    model, cores, nproc = host_cpu()
     parts = 4 * cores
     cuts = [nrb * i // parts for i in range(parts + 1)]
     times = []
@@ -176,7 +220,7 @@ def cpu_baseline(mat, codes, d, m, xb, batch, coded):
     return {"value": round(coded / tc / 1e9, 4), "unit": "GB/s (coded bytes)", "cores": cores, "kind": "oracle",
             "sample": f"whole {mat.rows}x{mat.cols} matrix, limit-method decode + fp64 GEMV, row bands over "
                       f"{cores} threads, best of 3: {tc * 1e6:.0f} us/matrix; one thread: {t1 * 1e6:.0f} us/matrix",
-            "one_thread_value": round(coded / t1 / 1e9, 4)}
+            "one_thread_value": round(coded / t1 / 1e9, 4), "cpu_model": model, "nproc": nproc}
 
 
 def pipeline_legs(torch, dg, mat, db, a):
@@ -291,8 +335,37 @@ def rans_leg(torch, dg, kind, codes, a, huffman_us=None, halves=1):
     return res
 
 
+def timed_bundle_leg(torch, dg, build, mats, inputs, kinds, batch, a):
+    """The fused kernel on bundles built by `build` (one copy set rotated
+    like the main steps): us per matrix, coded bytes and bits per weight."""
+    bl = [build(kinds[mm.kind], inp[0], inp[1], inp[2]) for mm, inp in zip(mats, inputs)]
+    inf = [dg.lw_bundle_get_info(b) for b in bl]
+    coded = sum(int(i["coded_bytes"]) for i in inf)
+    n = copies_for(coded)
+    dbs = [[dg.lw_bundle_upload(b, torch.empty(int(i["image_bytes"]), dtype=torch.uint8, device="cuda"))
+            for b, i in zip(bl, inf)] for _ in range(n)]
+    xs = [torch.from_numpy(np.ascontiguousarray(inp[3][:batch]).view(np.int16)).cuda() for inp in inputs]
+    ys = [torch.empty((batch, mm.rows), dtype=torch.float32, device="cuda") for mm in mats]
+
+    def step(i):
+        for j in range(len(mats)):
+            dg.lw_gemv(dbs[i][j], xs[j], ys[j], batch)
+
+    ms = time_graph(torch, step, n, a.steps, a.warmup) or time_loop(torch, step, n, a.steps, a.warmup)
+    weights = sum(mm.rows * mm.cols for mm in mats)
+    res = {"us_per_matrix": round(ms * 1e3 / len(mats), 3), "coded_bytes": coded,
+           "bits_per_weight": round(8 * coded / weights, 4),
+           "coded_GBs": round(coded / (ms * 1e-3) / 1e9, 2)}
+    del dbs
+    return res
+
+
 def main():
     a = parse()
+    if a.trace_stats:
+        for row in trace_stats(a.trace_stats):
+            print(json.dumps(row))
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for {a.gpus}).",
               file=sys.stderr)
@@ -308,12 +381,13 @@ def main():
     for mat in mats:                      # one matrix, or the three of a 70B MLP pass
         if mat.kind == "bf16":
             w, xb = synth.gen_bf16(mat)
-            bundles.append(dg.lw_bundle_build_bf16(w))
+            bundles.append((dg.lw_bundle_build_bf16 if a.code == "huffman" else dg.lw_bundle_build_bf16_compact)(w))
             inputs.append((None, None, None, xb))
             del w
         else:
             codes, d, m, xb = synth.gen_q(mat)
-            bundles.append(dg.lw_bundle_build_q(kinds[mat.kind], codes, d, m))
+            build = dg.lw_bundle_build_q if a.code == "huffman" else dg.lw_bundle_build_q_compact
+            bundles.append(build(kinds[mat.kind], codes, d, m))
             inputs.append((codes, d, m, xb))
     infos = [dg.lw_bundle_get_info(b) for b in bundles]
     build_s = time.time() - t0
@@ -321,8 +395,8 @@ def main():
     kind = kinds[mat.kind]
     codes, d, m, xb = inputs[0]
 
-    total_image = sum(int(i["image_bytes"]) for i in infos)
-    n_copies = a.copies if a.copies > 0 else copies_for(total_image)
+    total_coded = sum(int(i["coded_bytes"]) for i in infos)
+    n_copies = a.copies if a.copies > 0 else copies_for(total_coded)
     dbs = []                              # dbs[copy][matrix]
     for _ in range(n_copies):
         row = []
@@ -361,7 +435,9 @@ def main():
         "dtype": "fp16 x, fp32 accumulate" if kind != dg.LW_BF16_EXP else "bf16 x, fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": f"{' + '.join(mm.name for mm in mats)}: {shape} {mat.kind} coded, batch {batch}",
-                   "matrices": len(mats), "batch": batch, "bundle_copies": n_copies},
+                   "matrices": len(mats), "batch": batch, "bundle_copies": n_copies,
+                   "code": "optimal 11-bit-limited Huffman" if a.code == "huffman" else "compact (opt-in)",
+                   "rotated_coded_bytes": n_copies * coded},
         "timing": "hip graph replay of the timed steps" if ms_graph is not None else "eager launches",
         "us_per_step_eager": round(ms_eager * 1e3, 3),
         "us_per_matrix": round(us / len(mats), 3),
@@ -415,6 +491,21 @@ def main():
         result["rans2_decode_only"] = rans_leg(torch, dg, kind, codes, a, dms * 1e3, halves=2)
     if not a.no_extras and kind == dg.LW_Q4_PAIR and len(mats) == 1 and batch <= 4:
         result["skip_twin"] = skip_legs(torch, dg, synth, mat, codes, d, m, xs[0], batch, a)
+    if not a.no_extras and kind != dg.LW_BF16_EXP:
+        # the other code of the same matrices, beside the timed one
+        other = "compact" if a.code == "huffman" else "huffman"
+        build = dg.lw_bundle_build_q_compact if other == "compact" else dg.lw_bundle_build_q
+        leg = timed_bundle_leg(torch, dg, build, mats, inputs, kinds, batch, a)
+        leg["over_timed_code_time"] = round(leg["us_per_matrix"] / (us / len(mats)), 3)
+        result[f"{other}_code"] = leg
+    if not a.no_extras and a.workload == "q4_down_4096x14336":
+        # the batches the down projection's workload names: 1, 4 and 16 (matrix cores)
+        by = {}
+        for b in (1, 4, 16):
+            leg = timed_bundle_leg(torch, dg, dg.lw_bundle_build_q if a.code == "huffman"
+                                   else dg.lw_bundle_build_q_compact, mats, inputs, kinds, b, a)
+            by[f"batch_{b}"] = {"us_per_matrix": leg["us_per_matrix"], "coded_GBs": leg["coded_GBs"]}
+        result["batches"] = by
     if not a.no_extras and len(mats) == 3 and mats[2].cols == mats[0].rows:
         # the whole MLP pass, chained: gate and up on x, SwiGLU to fp16 h,
         # down on h (each graph step depends on the one before it)

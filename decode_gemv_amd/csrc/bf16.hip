@@ -92,7 +92,7 @@ LW_DEV void lw_load_sm(uint32_t (&dst)[CHUNK], const uint32_t *smrow, int chunk)
     for (int i = 0; i < CHUNK; i++) dst[i] = smrow[(chunk * CHUNK + i) * 32];
 }
 
-template <int N8, int N16, int BATCH>
+template <int PLAN, int BATCH>
 __global__ __launch_bounds__(256) void k_gemv_bf16(KArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(KArgs a)
 
     // issue every load, tile offsets first; table barrier; own tile and x (as in fused_q.hip)
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-    const LwTabRegs tr = lw_tab_fetch<lw_compact<N16>()>(a, false);
+    const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, false);
     const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
     uint32_t xv[BATCH][2];
     const uint32_t *xg = reinterpret_cast<const uint32_t *>(a.x) + (size_t)(c.active ? c.cb : 0) * 128;
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(KArgs a)
     lw_load_sm(ring[0], smrow, 0);
     LwTileRegs64 tile;
     lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    lw_tab_put<lw_compact<N16>()>(lds, tr, a);
+    lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
     __syncthreads();                      // the decoder table is complete
 #pragma unroll
     for (int b = 0; b < BATCH; b++) {
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(KArgs a)
                         pend = pay;
                     }
                 };
-                lw_decode_pipelined<N8, N16, CHUNK, XA, true>(
+                lw_decode_pipelined<PLAN, CHUNK, XA, true>(
                     d, a, [](int j) { return (j & 1) ? (LW_TPAY_HI - LW_TPAY) : 0u; }, fetch, use);
             };
 #pragma unroll
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(KArgs a)
 }
 
 // Decode only: rebuild the bf16 matrix [rows][cols].
-template <int N8, int N16>
+template <int PLAN>
 __global__ __launch_bounds__(256) void k_decode_bf16(KArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -212,13 +212,13 @@ __global__ __launch_bounds__(256) void k_decode_bf16(KArgs a)
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
     const uint32_t *smrow = a.sm + (size_t)c.t * 4096 + (size_t)c.half * 64 * 32 + c.l;
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-    const LwTabRegs tr = lw_tab_fetch<lw_compact<N16>()>(a, false);
+    const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, false);
     const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
     uint32_t ring[2][CHUNK];
     lw_load_sm(ring[0], smrow, 0);
     LwTileRegs64 tile;
     lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    lw_tab_put<lw_compact<N16>()>(lds, tr, a);
+    lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
     __syncthreads();
     if (!c.active) return;
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256) void k_decode_bf16(KArgs a)
     uint32_t pend = 0;
     auto run_chunk = [&](int ch, const uint32_t (&cur)[CHUNK]) {
         uint32_t buf[2 * CHUNK];
-        lw_decode_pipelined<N8, N16, CHUNK, XA, true>(
+        lw_decode_pipelined<PLAN, CHUNK, XA, true>(
             d, a, [](int j) { return (j & 1) ? (LW_TPAY_HI - LW_TPAY) : 0u; },
             [&](int g) { return XA{cur[g]}; },
             [&](int g, int j, uint32_t pay, const XA &x) {
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(256) void k_decode_bf16(KArgs a)
 // lanes' stores of one group are one coalesced 256-byte row.  Verbatim
 // segments keep the placeholder index 0 (or its exponent); vrank[t][s][r]
 // receives the index of segment s of tile row r in the verbatim store, or -1.
-template <int N8, int N16, bool EXP>
+template <int PLAN, bool EXP>
 __global__ __launch_bounds__(256) void k_transcode_bf16(KArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -286,11 +286,11 @@ __global__ __launch_bounds__(256) void k_transcode_bf16(KArgs a)
     const int S = a.max_words + 3;
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-    const LwTabRegs tr = lw_tab_fetch<lw_compact<N16>()>(a, !EXP);   // second table: the palette index itself
+    const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, !EXP);   // second table: the palette index itself
     const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
     LwTileRegs64 tile;
     lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    lw_tab_put<lw_compact<N16>()>(lds, tr, a);
+    lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
     __syncthreads();
     if (!c.active) return;
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256) void k_transcode_bf16(KArgs a)
     uint32_t *o = static_cast<uint32_t *>(a.out) + (size_t)c.t * (EXP ? 64 : 32) * 64 + r;
     struct NoAux {};
     uint32_t acc = 0;
-    lw_decode_pipelined<N8, N16, 64, NoAux, false>(
+    lw_decode_pipelined<PLAN, 64, NoAux, false>(
         d, a, [](int) { return EXP ? 0u : (LW_TPAY_HI - LW_TPAY); }, [](int) { return NoAux{}; },
         [&](int g, int j, uint32_t pay, const NoAux &) {
             if constexpr (EXP) {
@@ -337,60 +337,60 @@ __global__ __launch_bounds__(256) void k_transcode_bf16(KArgs a)
     for (int q = 0; q < 4; q++) a.vrank[(size_t)c.t * 256 + q * 64 + c.lane] = v[q];
 }
 
-template <int N8, int N16, bool EXP>
+template <int PLAN, bool EXP>
 hipError_t launch_transcode(const KArgs &a, hipStream_t s)
 {
     const LdsLayout L = lds_layout(1, a.max_words, true);
     dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
-    hipError_t e = lw_allow_lds<k_transcode_bf16<N8, N16, EXP>>();
+    hipError_t e = lw_allow_lds<k_transcode_bf16<PLAN, EXP>>();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_transcode_bf16<N8, N16, EXP>), grid, dim3(256), L.total, s, a);
+    hipLaunchKernelGGL((k_transcode_bf16<PLAN, EXP>), grid, dim3(256), L.total, s, a);
     return hipGetLastError();
 }
 
-template <int N8, int N16>
+template <int PLAN>
 hipError_t transcode_mode(const KArgs &a, bool exponents, hipStream_t s)
 {
-    return exponents ? launch_transcode<N8, N16, true>(a, s) : launch_transcode<N8, N16, false>(a, s);
+    return exponents ? launch_transcode<PLAN, true>(a, s) : launch_transcode<PLAN, false>(a, s);
 }
 
-template <int N8, int N16, int BATCH>
+template <int PLAN, int BATCH>
 hipError_t launch_gemv(const KArgs &a0, hipStream_t s)
 {
     KArgs a = a0;
     a.ramp = lw_resident_ramp((int64_t)a.n_rb * a.n_cb);
     const LdsLayout L = lds_layout(BATCH, a.max_words, false);
     dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
-    auto kern = k_gemv_bf16<N8, N16, BATCH>;
-    hipError_t e = lw_allow_lds<k_gemv_bf16<N8, N16, BATCH>>();
+    auto kern = k_gemv_bf16<PLAN, BATCH>;
+    hipError_t e = lw_allow_lds<k_gemv_bf16<PLAN, BATCH>>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, dim3(256), L.total, s, a);
     return hipGetLastError();
 }
 
-template <int N8, int N16>
+template <int PLAN>
 hipError_t launch_decode(const KArgs &a, hipStream_t s)
 {
     const LdsLayout L = lds_layout(1, a.max_words, true);
     dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
-    auto kern = k_decode_bf16<N8, N16>;
-    hipError_t e = lw_allow_lds<k_decode_bf16<N8, N16>>();
+    auto kern = k_decode_bf16<PLAN>;
+    hipError_t e = lw_allow_lds<k_decode_bf16<PLAN>>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, dim3(256), L.total, s, a);
     return hipGetLastError();
 }
 
-template <int N8, int N16>
+template <int PLAN>
 hipError_t gemv_batch(const KArgs &a, int batch, hipStream_t s)
 {
     switch (batch) {
-    case 1: return launch_gemv<N8, N16, 1>(a, s);
-    case 2: return launch_gemv<N8, N16, 2>(a, s);
-    case 3: return launch_gemv<N8, N16, 3>(a, s);
-    case 4: return launch_gemv<N8, N16, 4>(a, s);
-    case 5: return launch_gemv<N8, N16, 5>(a, s);
-    case 6: return launch_gemv<N8, N16, 6>(a, s);
-    case 7: return launch_gemv<N8, N16, 7>(a, s);
+    case 1: return launch_gemv<PLAN, 1>(a, s);
+    case 2: return launch_gemv<PLAN, 2>(a, s);
+    case 3: return launch_gemv<PLAN, 3>(a, s);
+    case 4: return launch_gemv<PLAN, 4>(a, s);
+    case 5: return launch_gemv<PLAN, 5>(a, s);
+    case 6: return launch_gemv<PLAN, 6>(a, s);
+    case 7: return launch_gemv<PLAN, 7>(a, s);
     }
     return hipErrorNotSupported;
 }
@@ -399,42 +399,15 @@ hipError_t gemv_batch(const KArgs &a, int batch, hipStream_t s)
 
 hipError_t lw_launch_gemv_bf16(const KArgs &a, SadPlan p, int batch, hipStream_t s)
 {
-    if (p.compact) return gemv_batch<1, LW_N16_COMPACT>(a, batch, s);
-    switch (p.n8ops * 2 + p.n16ops) {
-    case 0: return gemv_batch<0, 0>(a, batch, s);
-    case 1: return gemv_batch<0, 1>(a, batch, s);
-    case 2: return gemv_batch<1, 0>(a, batch, s);
-    case 3: return gemv_batch<1, 1>(a, batch, s);
-    case 4: return gemv_batch<2, 0>(a, batch, s);
-    case 5: return gemv_batch<2, 1>(a, batch, s);
-    }
-    return hipErrorInvalidValue;
+    return lw_with_plan(p, [&](auto P) { return gemv_batch<decltype(P)::value>(a, batch, s); });
 }
 
 hipError_t lw_launch_decode_bf16(const KArgs &a, SadPlan p, hipStream_t s)
 {
-    if (p.compact) return launch_decode<1, LW_N16_COMPACT>(a, s);
-    switch (p.n8ops * 2 + p.n16ops) {
-    case 0: return launch_decode<0, 0>(a, s);
-    case 1: return launch_decode<0, 1>(a, s);
-    case 2: return launch_decode<1, 0>(a, s);
-    case 3: return launch_decode<1, 1>(a, s);
-    case 4: return launch_decode<2, 0>(a, s);
-    case 5: return launch_decode<2, 1>(a, s);
-    }
-    return hipErrorInvalidValue;
+    return lw_with_plan(p, [&](auto P) { return launch_decode<decltype(P)::value>(a, s); });
 }
 
 hipError_t lw_launch_transcode_bf16(const KArgs &a, SadPlan p, bool exponents, hipStream_t s)
 {
-    if (p.compact) return transcode_mode<1, LW_N16_COMPACT>(a, exponents, s);
-    switch (p.n8ops * 2 + p.n16ops) {
-    case 0: return transcode_mode<0, 0>(a, exponents, s);
-    case 1: return transcode_mode<0, 1>(a, exponents, s);
-    case 2: return transcode_mode<1, 0>(a, exponents, s);
-    case 3: return transcode_mode<1, 1>(a, exponents, s);
-    case 4: return transcode_mode<2, 0>(a, exponents, s);
-    case 5: return transcode_mode<2, 1>(a, exponents, s);
-    }
-    return hipErrorInvalidValue;
+    return lw_with_plan(p, [&](auto P) { return transcode_mode<decltype(P)::value>(a, exponents, s); });
 }

@@ -377,6 +377,7 @@ static void fill_gputab(int kind, const lw_table &t, const uint8_t *palette, lw_
         g->len[r] = (uint32_t)L;
         g->base[r] = (int32_t)t.offset[L] - (int32_t)t.first[L];
     }
+    lw_make_plan(t, lmin, lmax, g->plan);
     for (int i = 0; i < h.n_sym; i++) {
         uint32_t s = t.sym_sorted[i];
         g->symval[i] = s;
@@ -391,6 +392,145 @@ static void fill_gputab(int kind, const lw_table &t, const uint8_t *palette, lw_
             g->payload_hi[i] = e << 23;
         }
     }
+}
+
+// Limit comparisons packed for the SAD counting of lane_decode.hpp.
+// Compact tables (at most four used lengths, the three shorter <= 8): the
+// limits of the used lengths but the longest, in byte lanes (top 8 peek bits
+// against limit/8), the count indexing the used lengths.  Other tables
+// compare every length min_len .. max_len-1 (an absent length repeats the
+// previous limit), so the length is min_len + count:
+//   - up to eight limits whose residues mod 8 take at most two values besides
+//     0 go to two SAD byte pairs (residue plans): a limit c with c mod 8 = r
+//     compares floor((p + k)/8) with (c + k)/8, k = 8 - r, on a byte taken
+//     from the peek plus k << 21; the residue-0 limits compare the top byte;
+//   - anything else takes the general plan (lengths <= 8 in byte lanes, 9 and
+//     10 in 16-bit lanes against the top 16 window bits).
+// Unused lanes compare 0 with 0 and contribute nothing.
+void lw_make_plan(const lw_table &t, int min_len, int max_len, lw_plan &a)
+{
+    std::memset(&a, 0, sizeof(a));
+    a.c8[0] = a.c8[1] = a.c8m1[0] = a.c8m1[1] = 0;
+    a.c16 = a.c16m1 = 0;
+    a.xsel[0] = a.xsel[1] = 0x03030303u;
+    a.xk[0] = a.xk[1] = 0;
+    a.lut_lo = a.lut_hi = 0;
+    a.cbase[0] = a.cbase[1] = a.cbase[2] = a.cbase[3] = 0;
+    a.ncmp = 0;
+    int used[LW_MAXLEN + 1], nu = 0;
+    for (int L = 1; L <= LW_MAXLEN; L++)
+        if (t.count[L]) used[nu++] = L;
+    if (nu >= 1 && nu <= 4 && (nu == 1 || used[nu - 2] <= 8)) {
+        uint64_t lut = 0x00FF00FF00FF00FFull;   // even bytes 0xFF: what the selector's zero upper bytes pick
+        for (int r = 0; r < nu; r++) {
+            const int L = used[r];
+            lut |= (uint64_t)((256 - L) & 0xFF) << (8 * (7 - 2 * r));
+            a.cbase[r] = (int32_t)t.offset[L] - (int32_t)t.first[L];
+            if (r < nu - 1) {
+                const uint32_t c = (uint32_t)t.limit[L] >> 3;
+                a.c8[0] |= c << (8 * r);
+                a.c8m1[0] |= (c - 1) << (8 * r);
+            }
+        }
+        a.lut_lo = (uint32_t)lut;
+        a.lut_hi = (uint32_t)(lut >> 32);
+        a.ncmp = nu - 1;
+        a.sad_k = LW_PLAN_CSEL - (uint32_t)(nu - 1);
+        a.plan = LW_P_COMPACT;
+        return;
+    }
+    const int n = max_len - min_len;          // comparisons: lengths min_len .. max_len - 1
+    a.sad_k = LW_PLAN_PBASE - 2u * (uint32_t)min_len - (uint32_t)n;
+    // residue plans: per limit its residue mod 8 and its byte threshold
+    int thr[LW_MAXLEN + 1], zero[LW_MAXLEN + 1], rl[2][LW_MAXLEN + 1], nz = 0, nrl[2] = {0, 0}, rv[2] = {0, 0};
+    int nres = 0;
+    bool fits = n <= 8;
+    for (int i = 0; i < n && fits; i++) {
+        const uint32_t c = t.limit[min_len + i];
+        const int r = (int)(c & 7u);
+        thr[i] = (int)((c + (uint32_t)((8 - r) & 7)) >> 3);   // exact: c + k is a multiple of 8
+        if (thr[i] < 1 || thr[i] > 255) {
+            fits = false;
+            break;
+        }
+        if (!r) {
+            zero[nz++] = i;
+            continue;
+        }
+        int q = -1;
+        for (int j = 0; j < nres; j++)
+            if (rv[j] == r) q = j;
+        if (q < 0) {
+            if (nres == 2) {
+                fits = false;
+                break;
+            }
+            q = nres;
+            rv[nres++] = r;
+        }
+        rl[q][nrl[q]++] = i;
+    }
+    if (fits) {
+        // residue limits of pair j sit in its top bytes (3, 2, ..), read from
+        // the peek plus k_j; the residue-0 limits fill bytes 0.. of pair 0,
+        // then of pair 1, read from the top peek byte.  One residue: its
+        // limits split over both pairs, which share one register.
+        int pres[2] = {0, 0}, plist[2][LW_MAXLEN + 1], pn[2] = {0, 0};
+        if (nres == 1) {
+            pres[0] = pres[1] = rv[0];
+            for (int i = 0; i < nrl[0]; i++) {
+                const int j = i & 1;
+                plist[j][pn[j]++] = rl[0][i];
+            }
+        } else if (nres == 2) {
+            for (int j = 0; j < 2; j++) {
+                pres[j] = rv[j];
+                for (int i = 0; i < nrl[j]; i++) plist[j][pn[j]++] = rl[j][i];
+            }
+        }
+        const int extra = std::max(pn[0], pn[1]);
+        if (extra <= 4 && nz <= 2 * (4 - extra)) {
+            for (int j = 0; j < 2; j++)
+                for (int i = 0; i < pn[j]; i++) {
+                    const int b = 3 - i;
+                    a.c8[j] |= (uint32_t)thr[plist[j][i]] << (8 * b);
+                    a.c8m1[j] |= (uint32_t)(thr[plist[j][i]] - 1) << (8 * b);
+                }
+            for (int i = 0; i < nz; i++) {
+                const int j = i / (4 - extra), b = i % (4 - extra);
+                a.c8[j] |= (uint32_t)thr[zero[i]] << (8 * b);
+                a.c8m1[j] |= (uint32_t)(thr[zero[i]] - 1) << (8 * b);
+            }
+            for (int j = 0; j < 2; j++) {
+                const int k = (8 - pres[j]) & 7;
+                a.xk[j] = (uint32_t)k << 21;
+                uint32_t sel = 0;
+                for (int b = 0; b < 4; b++) sel |= (k && b >= 4 - extra ? 7u : 3u) << (8 * b);
+                a.xsel[j] = sel;
+            }
+            a.plan = nres == 0 ? LW_P_R2 : nres == 1 ? LW_P_R2K : LW_P_R2X2;
+            return;
+        }
+    }
+    a.xsel[0] = a.xsel[1] = 0x03030303u;
+    a.xk[0] = a.xk[1] = 0;
+    a.c8[0] = a.c8[1] = a.c8m1[0] = a.c8m1[1] = 0;
+    int l8[8], l16[2], n8 = 0, n16 = 0;
+    for (int L = min_len; L < max_len; L++) {
+        if (L <= 8) l8[n8++] = L;
+        else l16[n16++] = L;
+    }
+    for (int i = 0; i < n8; i++) {
+        const uint32_t c = (uint32_t)t.limit[l8[i]] >> 3;
+        a.c8[i / 4] |= c << (8 * (i % 4));
+        a.c8m1[i / 4] |= (c - 1) << (8 * (i % 4));
+    }
+    for (int i = 0; i < n16; i++) {
+        const uint32_t c = (uint32_t)t.limit[l16[i]] << 5;
+        a.c16 |= c << (16 * i);
+        a.c16m1 |= (c - 1) << (16 * i);
+    }
+    a.plan = LW_P_GEN;
 }
 
 // Encode every tile of a symbol source.  sym(t, l, k) gives symbol k of lane
@@ -808,6 +948,11 @@ static lw_status validate_image(const uint8_t *img, size_t bytes)
     }
     for (int L = lmin; L < lmax; L++)
         if (g->limlj[L - lmin] != ((uint32_t)t.limit[L] << 21)) return lw_fail(LW_E_FORMAT, "gpu limits mismatch");
+    {
+        lw_plan want;
+        lw_make_plan(t, lmin, lmax, want);
+        if (std::memcmp(&want, &g->plan, sizeof(want)) != 0) return lw_fail(LW_E_FORMAT, "comparison plan mismatch");
+    }
     // tile offsets: start at 0, grow by whole word rows, end at the word count
     const uint32_t *to = reinterpret_cast<const uint32_t *>(img + h.off[LW_REG_TILE_OFF]);
     if (to[0] != 0) return lw_fail(LW_E_FORMAT, "tile_off[0] != 0");

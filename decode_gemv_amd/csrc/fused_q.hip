@@ -68,7 +68,7 @@ LW_DEV LaneCtx lane_ctx(const KArgs &a, int waves = WAVES)
 // WPG wavefronts per workgroup cover WPG consecutive column blocks of one row
 // band; with WPG >= K/256 a workgroup holds whole rows and the reduction
 // stays in LDS.
-template <int KIND, int N8, int N16, int BATCH, int WPG>
+template <int KIND, int PLAN, int BATCH, int WPG>
 __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
     // stores its own tile and activations and starts decoding as soon as its
     // own data is in (a wavefront's LDS operations complete in order).
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-    const LwTabRegs tr = lw_tab_fetch<lw_compact<N16>()>(a, false);
+    const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, false);
     const uint32_t dm = a.dm[(size_t)c.t * 64 + 2 * c.l + c.half];   // (d, m) of this lane's tile row
     const uint32_t split = a.split[(size_t)c.t * 32 + c.l];          // second-row start
     uint32_t xv[BATCH][2];
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
     // order makes no difference.
     LwTileRegs64 tile;
     if constexpr (WPG <= WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    lw_tab_put<lw_compact<N16>()>(lds, tr, a);
+    lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
     __syncthreads();                      // the decoder table is complete
     if constexpr (WPG > WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
 #pragma unroll
@@ -158,9 +158,9 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
                 }
             };
             if constexpr (KIND == LW_Q4_PAIR)
-                lw_decode_pipelined<N8, N16, NG, XA, true>(d, a, [](int) { return 0u; }, fetch, use);
+                lw_decode_pipelined<PLAN, NG, XA, true>(d, a, [](int) { return 0u; }, fetch, use);
             else
-                lw_decode_pipelined<N8, N16, NG, XA, true>(
+                lw_decode_pipelined<PLAN, NG, XA, true>(
                     d, a, [](int j) { return (j & 1) ? (LW_TPAY_HI - LW_TPAY) : 0u; }, fetch, use);
         } else {                           // unusable LDS base: poison the output
 #pragma unroll
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
 
 
 // Decode only: restore the fixed-width codes (Q4 packed nibbles, Q6 bytes).
-template <int KIND, int N8, int N16>
+template <int KIND, int PLAN>
 __global__ __launch_bounds__(256) void k_decode_q(KArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -202,11 +202,11 @@ __global__ __launch_bounds__(256) void k_decode_q(KArgs a)
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
     // issue, then store (as in k_gemv_q)
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-    const LwTabRegs tr = lw_tab_fetch<lw_compact<N16>()>(a, true);
+    const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, true);
     const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
     LwTileRegs64 tile;
     lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    lw_tab_put<lw_compact<N16>()>(lds, tr, a);
+    lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
     __syncthreads();
     if (!c.active) return;
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void k_decode_q(KArgs a)
     for (int part = 0; part < NG / PART; part++) {
         uint32_t buf[PART];
         uint32_t pk = 0;
-        lw_decode_pipelined<N8, N16, PART, NoAux, true>(
+        lw_decode_pipelined<PLAN, PART, NoAux, true>(
             d, a, [](int) { return LW_TPAY_HI - LW_TPAY; },
             [](int) { return NoAux{}; },
             [&](int g, int j, uint32_t sym, const NoAux &) {
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(256) void k_decode_q(KArgs a)
     if (a.lane_bits && c.half) a.lane_bits[(size_t)c.t * 32 + c.l] = d.bitpos();
 }
 
-template <int KIND, int N8, int N16, int BATCH, int WPG>
+template <int KIND, int PLAN, int BATCH, int WPG>
 hipError_t launch_gemv_wpg(const KArgs &a0, hipStream_t s)
 {
     KArgs a = a0;
@@ -254,8 +254,8 @@ hipError_t launch_gemv_wpg(const KArgs &a0, hipStream_t s)
     a.ramp = lw_resident_ramp((int64_t)a.n_rb * a.n_cb);
     const LdsLayout L = lds_layout(BATCH, a.max_words, false, WPG);
     dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
-    auto kern = k_gemv_q<KIND, N8, N16, BATCH, WPG>;
-    hipError_t e = lw_allow_lds<k_gemv_q<KIND, N8, N16, BATCH, WPG>>();
+    auto kern = k_gemv_q<KIND, PLAN, BATCH, WPG>;
+    hipError_t e = lw_allow_lds<k_gemv_q<KIND, PLAN, BATCH, WPG>>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, dim3(64 * WPG), L.total, s, a);
     return hipGetLastError();
@@ -264,48 +264,48 @@ hipError_t launch_gemv_wpg(const KArgs &a0, hipStream_t s)
 // Whole rows per workgroup (16 wavefronts, no cross-workgroup reduction) when
 // a row band has 13..16 column blocks and the tiles fit in LDS; 14 wavefronts
 // (a few column groups, every wavefront active) when the column blocks are a
-// multiple of 14 (K = 14336 and 28672, compact tables) and the whole grid is
+// multiple of 14 (K = 14336 and 28672; plans of at most eight comparisons) and the whole grid is
 // resident at once (with several generations, workgroups this large free
 // their CU only all together: 8 % slower on 8192x28672); else four.
-template <int KIND, int N8, int N16, int BATCH>
+template <int KIND, int PLAN, int BATCH>
 hipError_t launch_gemv_q(const KArgs &a, hipStream_t s)
 {
     if constexpr (BATCH <= 4) {
         const uint32_t lds = (uint32_t)lw_device_lds_bytes();
         if (a.n_cb > 12 && a.n_cb <= 16 && lds_layout(BATCH, a.max_words, false, 16).total <= lds)
-            return launch_gemv_wpg<KIND, N8, N16, BATCH, 16>(a, s);
-        if constexpr (lw_compact<N16>()) {
+            return launch_gemv_wpg<KIND, PLAN, BATCH, 16>(a, s);
+        if constexpr (PLAN != LW_P_GEN) {
             if (a.n_cb > 16 && a.n_cb % 14 == 0 && lw_resident_ramp((int64_t)a.n_rb * a.n_cb) &&
                 lds_layout(BATCH, a.max_words, false, 14).total <= lds)
-                return launch_gemv_wpg<KIND, N8, N16, BATCH, 14>(a, s);
+                return launch_gemv_wpg<KIND, PLAN, BATCH, 14>(a, s);
         }
     }
-    return launch_gemv_wpg<KIND, N8, N16, BATCH, WAVES>(a, s);
+    return launch_gemv_wpg<KIND, PLAN, BATCH, WAVES>(a, s);
 }
 
-template <int KIND, int N8, int N16>
+template <int KIND, int PLAN>
 hipError_t launch_decode_q(const KArgs &a, hipStream_t s)
 {
     const LdsLayout L = lds_layout(1, a.max_words, true);
     dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
-    auto kern = k_decode_q<KIND, N8, N16>;
-    hipError_t e = lw_allow_lds<k_decode_q<KIND, N8, N16>>();
+    auto kern = k_decode_q<KIND, PLAN>;
+    hipError_t e = lw_allow_lds<k_decode_q<KIND, PLAN>>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, dim3(256), L.total, s, a);
     return hipGetLastError();
 }
 
-template <int KIND, int N8, int N16>
+template <int KIND, int PLAN>
 hipError_t gemv_batch(const KArgs &a, int batch, hipStream_t s)
 {
     switch (batch) {
-    case 1: return launch_gemv_q<KIND, N8, N16, 1>(a, s);
-    case 2: return launch_gemv_q<KIND, N8, N16, 2>(a, s);
-    case 3: return launch_gemv_q<KIND, N8, N16, 3>(a, s);
-    case 4: return launch_gemv_q<KIND, N8, N16, 4>(a, s);
-    case 5: return launch_gemv_q<KIND, N8, N16, 5>(a, s);
-    case 6: return launch_gemv_q<KIND, N8, N16, 6>(a, s);
-    case 7: return launch_gemv_q<KIND, N8, N16, 7>(a, s);
+    case 1: return launch_gemv_q<KIND, PLAN, 1>(a, s);
+    case 2: return launch_gemv_q<KIND, PLAN, 2>(a, s);
+    case 3: return launch_gemv_q<KIND, PLAN, 3>(a, s);
+    case 4: return launch_gemv_q<KIND, PLAN, 4>(a, s);
+    case 5: return launch_gemv_q<KIND, PLAN, 5>(a, s);
+    case 6: return launch_gemv_q<KIND, PLAN, 6>(a, s);
+    case 7: return launch_gemv_q<KIND, PLAN, 7>(a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -313,33 +313,13 @@ hipError_t gemv_batch(const KArgs &a, int batch, hipStream_t s)
 template <int KIND>
 hipError_t gemv_plan(const KArgs &a, SadPlan p, int batch, hipStream_t s)
 {
-    if (p.compact) return gemv_batch<KIND, 1, LW_N16_COMPACT>(a, batch, s);
-    const int code = p.n8ops * 2 + p.n16ops;
-    switch (code) {
-    case 0: return gemv_batch<KIND, 0, 0>(a, batch, s);
-    case 1: return gemv_batch<KIND, 0, 1>(a, batch, s);
-    case 2: return gemv_batch<KIND, 1, 0>(a, batch, s);
-    case 3: return gemv_batch<KIND, 1, 1>(a, batch, s);
-    case 4: return gemv_batch<KIND, 2, 0>(a, batch, s);
-    case 5: return gemv_batch<KIND, 2, 1>(a, batch, s);
-    }
-    return hipErrorInvalidValue;
+    return lw_with_plan(p, [&](auto P) { return gemv_batch<KIND, decltype(P)::value>(a, batch, s); });
 }
 
 template <int KIND>
 hipError_t decode_plan(const KArgs &a, SadPlan p, hipStream_t s)
 {
-    if (p.compact) return launch_decode_q<KIND, 1, LW_N16_COMPACT>(a, s);
-    const int code = p.n8ops * 2 + p.n16ops;
-    switch (code) {
-    case 0: return launch_decode_q<KIND, 0, 0>(a, s);
-    case 1: return launch_decode_q<KIND, 0, 1>(a, s);
-    case 2: return launch_decode_q<KIND, 1, 0>(a, s);
-    case 3: return launch_decode_q<KIND, 1, 1>(a, s);
-    case 4: return launch_decode_q<KIND, 2, 0>(a, s);
-    case 5: return launch_decode_q<KIND, 2, 1>(a, s);
-    }
-    return hipErrorInvalidValue;
+    return lw_with_plan(p, [&](auto P) { return launch_decode_q<KIND, decltype(P)::value>(a, s); });
 }
 
 }  // namespace

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "lw_internal.h"
 
 // Everything a kernel needs about one uploaded bundle and one call.  Passed
@@ -30,11 +32,16 @@ struct KArgs {
     int64_t rows, cols;
     int32_t n_rb, n_cb, groups, batch, max_words, min_len, max_len;
     uint32_t pal0;               // bf16: exponent of palette index 0
-    // Limit comparison by sums of absolute differences (see lane_decode.hpp):
-    // byte lanes compare the top 8 peek bits with limit/8 (lengths <= 8),
-    // 16-bit lanes the top 16 window bits with limit*32 (lengths 9, 10).
-    uint32_t c8[2], c8m1[2];     // limit/8 and limit/8 - 1 per byte, 0 in unused bytes
-    uint32_t c16, c16m1;         // limit*32 and limit*32 - 1 per half, 0 in unused halves
+    // Limit comparison by sums of absolute differences (see lane_decode.hpp).
+    // c8[j], c8m1[j]: the byte thresholds of SAD pair j (t and t - 1 per
+    // byte, equal in unused bytes).  Residue plans: byte i of the compared
+    // register X is the top peek byte (xsel byte 3) or the top byte of the
+    // peek plus xk[.] (saturating; xsel byte 7), so a limit that is not a
+    // multiple of 8 is compared exactly too.  General plan: c16, c16m1 hold
+    // limit*32 (and - 1) per half for lengths 9 and 10 on the top 16 bits.
+    uint32_t c8[2], c8m1[2];
+    uint32_t c16, c16m1;
+    uint32_t xsel[2], xk[2];
     uint32_t sad_k;              // accumulator offset: PBASE - 2*min_len - (number of comparisons)
     // Compact tables (at most four code lengths, the three shorter <= 8): the
     // comparison count r indexes the used lengths; lut_hi:lut_lo hold
@@ -46,15 +53,35 @@ struct KArgs {
     int32_t ramp;                // 1: the whole grid is resident at once (wavefronts lower their priority as they progress)
 };
 
-// SAD comparison layout of a bundle: byte-lane ops (0..2) and 16-bit ops
-// (0..1); compact tables use one byte-lane op and the count-indexed tables
-// (kernels instantiate them with N16 == LW_N16_COMPACT)
+// Comparison plans of the lane decoder (lane_decode.hpp, lw_count):
+//   LW_P_COMPACT  at most four used lengths, the three shorter <= 8: one SAD
+//                 pair on the replicated top peek byte, length from a byte table
+//   LW_P_R2       every limit a multiple of 8, at most 8 comparisons: two SAD
+//                 pairs on the replicated top peek byte, length min_len + count
+//   LW_P_R2K      as R2 with one more residue: some bytes come from the peek
+//                 plus a constant, so limits congruent to r mod 8 compare exactly
+//   LW_P_R2X2     two residues besides 0: each SAD pair has its own register
+//   LW_P_GEN      anything else (more than 8 comparisons): two byte pairs on
+//                 the top byte and one 16-bit pair on the top 16 bits
 struct SadPlan {
-    int n8ops, n16ops;
-    bool compact;
+    int plan;
 };
-#define LW_N16_COMPACT 2
-SadPlan lw_sad_plan(const lw_table &t, int min_len, int max_len, KArgs &a);
+// Copy a bundle's comparison plan into the kernel arguments.
+SadPlan lw_apply_plan(const lw_plan &p, KArgs &a);
+
+// Call f(std::integral_constant<int, PLAN>{}) for the plan's compile-time value.
+template <class F>
+inline hipError_t lw_with_plan(SadPlan p, F f)
+{
+    switch (p.plan) {
+    case LW_P_COMPACT: return f(std::integral_constant<int, LW_P_COMPACT>{});
+    case LW_P_R2: return f(std::integral_constant<int, LW_P_R2>{});
+    case LW_P_R2K: return f(std::integral_constant<int, LW_P_R2K>{});
+    case LW_P_R2X2: return f(std::integral_constant<int, LW_P_R2X2>{});
+    case LW_P_GEN: return f(std::integral_constant<int, LW_P_GEN>{});
+    }
+    return hipErrorInvalidValue;
+}
 
 // LDS bytes a fused/decode kernel needs per workgroup
 

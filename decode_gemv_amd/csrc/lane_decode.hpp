@@ -19,10 +19,19 @@
 // Length.  For sorted limits c_i and an integer peek p,
 //     |p - (c_i - 1)| - |p - c_i| = 2 [p >= c_i] - 1,
 // so two sums of absolute differences count the limits the peek has passed:
-// v_sad_u8 handles four limits per instruction on the top 8 peek bits (exact
-// for lengths <= 8, whose limits are multiples of 8), v_sad_u16 two limits
-// on the top 16 window bits (lengths 9 and 10).  With the accumulator chosen
-// as K = PBASE - 2*min_len - n, the difference of the two sums is
+// v_sad_u8 handles four limits per instruction on bytes, v_sad_u16 two on
+// 16-bit halves.  A limit of a length <= 8 is a multiple of 8, so it compares
+// exactly on the top 8 peek bits (floor(p / 8)).  A limit c of length 9 or 10
+// is a multiple of 4 or 2: with k = (8 - c) mod 8, p >= c exactly when
+// floor((p + k) / 8) >= (c + k) / 8, the top byte of the peek plus k << 21
+// (a saturating add: k never carries a valid comparison past 2047).  So one
+// v_perm_b32 gathers, per byte, the top byte of the peek or of the peek plus
+// k, and two v_sad_u8 pairs compare up to eight limits (the residue plans;
+// a table with two residues besides 0 gives each pair its own register).
+// Tables with more than eight comparisons take the general plan: byte pairs
+// on the top byte and one v_sad_u16 pair on the top 16 window bits.  With the
+// accumulator chosen as K = PBASE - 2*min_len - n, the difference of the two
+// sums is
 //     A = PBASE - 2*len,
 // which is at once the LDS address of the 16-bit entry of that length (the
 // symbol-table base offset[len] - first[len], pre-scaled) and, shifted right
@@ -116,10 +125,10 @@ inline hipError_t lw_allow_lds()
 }
 
 // LDS layout common to all decoding kernels (byte offsets)
-#define LW_PBASE 1024u       // length entries at PBASE - 2*len, len = 1..11
+#define LW_PBASE LW_PLAN_PBASE   // length entries at PBASE - 2*len, len = 1..11
 #define LW_TPAY 1024u        // payload per canonical index, u32[256]
 #define LW_TPAY_HI 2048u     // second payload, u32[256]
-#define LW_CSEL 0xD07u      // compact tables: selector of count r CSEL - 2r, its base entry at CSEL + 1 - 2r
+#define LW_CSEL LW_PLAN_CSEL     // compact tables: selector of count r CSEL - 2r, its base entry at CSEL + 1 - 2r
 #define LW_TAB_BYTES 3584u
 
 LW_DEV uint32_t lw_wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -202,9 +211,9 @@ struct LwTabRegs {
     int32_t ent;
 };
 
-// N16 value of the kernels' compact-table instantiations
-template <int N16>
-constexpr bool lw_compact() { return N16 == LW_N16_COMPACT; }
+// whether a plan indexes the compact tables (length from a byte table)
+template <int PLAN>
+constexpr bool lw_compact() { return PLAN == LW_P_COMPACT; }
 
 // thread tid (< 256) fetches payload entry tid of both tables and length
 // entry min(tid, max_len - min_len) (compact tables: the base of count
@@ -313,29 +322,55 @@ struct LaneDec {
     uint32_t un;                 // ~(bit position + 31)
     uint32_t k;                  // SAD offset including the LDS base
     uint32_t lut_lo;             // low word of the compact tables' shift bytes
+    uint32_t xk[2];              // residue plans: the constants added to the peek
     uint32_t ubias;              // 4 * (lb/2 + PBASE/2): what four shifts s add beyond the code lengths
     LW_DEV void advance(uint32_t bits) { un -= bits; }
     LW_DEV uint32_t bitpos() const { return ~un - 31u; }
 };
 
-// Count the limits the window's peek has passed; returns A = lb + PBASE - 2*len.
-template <int N8, int N16>
-LW_DEV uint32_t lw_sad_count(uint32_t hi, uint32_t k, const KArgs &a)
+// peek + k with unsigned saturation (one v_add_u32 with the clamp bit)
+LW_DEV uint32_t lw_add_sat(uint32_t v, uint32_t k)
 {
-    const uint32_t p8 = __builtin_amdgcn_perm(hi, hi, 0x03030303u);
+    uint32_t r;
+    asm("v_add_u32_e64 %0, %1, %2 clamp" : "=v"(r) : "v"(v), "v"(k));
+    return r;
+}
+
+// Count the limits the window's peek has passed; returns A = lb + PBASE - 2*len
+// (compact tables: A = lb + CSEL - 2r for r limits passed).  xk holds the
+// residue plans' additive constants in vector registers (see LaneDec).
+template <int PLAN>
+LW_DEV uint32_t lw_count(uint32_t hi, uint32_t k, const uint32_t (&xk)[2], const KArgs &a)
+{
     uint32_t s1 = 0, s2 = k;
-    if constexpr (N16 == 1) {
+    if constexpr (PLAN == LW_P_COMPACT) {
+        const uint32_t p8 = __builtin_amdgcn_perm(hi, hi, 0x03030303u);
+        s1 = __builtin_amdgcn_sad_u8(p8, a.c8m1[0], s1);
+        s2 = __builtin_amdgcn_sad_u8(p8, a.c8[0], s2);
+    } else if constexpr (PLAN == LW_P_GEN) {
+        const uint32_t p8 = __builtin_amdgcn_perm(hi, hi, 0x03030303u);
         const uint32_t p16 = __builtin_amdgcn_perm(hi, hi, 0x03020302u);
         s1 = __builtin_amdgcn_sad_u16(p16, a.c16m1, s1);
         s2 = __builtin_amdgcn_sad_u16(p16, a.c16, s2);
-    }
-    if constexpr (N8 > 1) {
         s1 = __builtin_amdgcn_sad_u8(p8, a.c8m1[1], s1);
         s2 = __builtin_amdgcn_sad_u8(p8, a.c8[1], s2);
-    }
-    if constexpr (N8 > 0) {
         s1 = __builtin_amdgcn_sad_u8(p8, a.c8m1[0], s1);
         s2 = __builtin_amdgcn_sad_u8(p8, a.c8[0], s2);
+    } else {
+        uint32_t x1, x2;
+        if constexpr (PLAN == LW_P_R2) {
+            x1 = __builtin_amdgcn_perm(hi, hi, 0x03030303u);
+        } else {
+            x1 = __builtin_amdgcn_perm(lw_add_sat(hi, xk[0]), hi, a.xsel[0]);
+        }
+        if constexpr (PLAN == LW_P_R2X2)
+            x2 = __builtin_amdgcn_perm(lw_add_sat(hi, xk[1]), hi, a.xsel[1]);
+        else
+            x2 = x1;
+        s1 = __builtin_amdgcn_sad_u8(x1, a.c8m1[0], s1);
+        s2 = __builtin_amdgcn_sad_u8(x1, a.c8[0], s2);
+        s1 = __builtin_amdgcn_sad_u8(x2, a.c8m1[1], s1);
+        s2 = __builtin_amdgcn_sad_u8(x2, a.c8[1], s2);
     }
     return s2 - s1;
 }
@@ -351,11 +386,11 @@ LW_DEV uint32_t lw_sad_count(uint32_t hi, uint32_t k, const KArgs &a)
 // pay_off(j) selects the payload table.  Scheduling barriers keep the issue
 // order; the extra window read after the last group stays inside the staged
 // slots.
-template <int N8, int N16, int NG, class Aux, bool UNROLL_ALL = false, class PayOff, class Fetch, class Use>
+template <int PLAN, int NG, class Aux, bool UNROLL_ALL = false, class PayOff, class Fetch, class Use>
 LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetch fetch, Use use)
 {
     static_assert(NG % 2 == 0 && NG >= 4, "groups must be even");
-    constexpr bool CMP = lw_compact<N16>();
+    constexpr bool CMP = lw_compact<PLAN>();
     uint32_t wa, wb, wc;
     uint32_t code[2][4], A[2][4], base[2][4], pay[2][4];
     Aux aux[2];
@@ -382,7 +417,7 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
             if (j == 0) peek = hi;
             else if (j < 3) peek = __builtin_amdgcn_alignbit(hi, lo, t);
             else peek = (uint32_t)((((uint64_t)hi << 32 | lo) << ((0u - t) & 63u)) >> 32);
-            const uint32_t Aj = lw_sad_count<N8, N16>(peek, d.k, a);
+            const uint32_t Aj = lw_count<PLAN>(peek, d.k, d.xk, a);
             const uint32_t s = CMP ? __builtin_amdgcn_perm(a.lut_hi, d.lut_lo, Aj) : Aj >> 1;
             A[q][j] = Aj;
             code[q][j] = peek >> (s & 31u);
@@ -495,10 +530,14 @@ LW_DEV bool lw_lane_init(LaneDec &d, uint8_t *lds, const uint32_t *slots, int l,
     d.un = ~31u;
     d.k = a.sad_k + lb;
     d.lut_lo = a.lut_lo;
+    d.xk[0] = a.xk[0];
+    d.xk[1] = a.xk[1];
     // Wave-uniform operands that a VOP3 instruction takes beside a scalar
     // one (it may read a single scalar register) are held in vector
-    // registers, set once here, so the decode loops make no copy per group.
-    asm volatile("" : "+v"(d.k), "+v"(d.lut_lo));
+    // registers, set once here, so the decode loops make no copy per group
+    // (a VALU instruction that reads a scalar register also issues at the
+    // slower rate on gfx950).
+    asm volatile("" : "+v"(d.k), "+v"(d.lut_lo), "+v"(d.xk[0]), "+v"(d.xk[1]));
     d.ubias = 4u * (lb / 2u + LW_PBASE / 2u);
     return (lb & 255u) == 0 && lb + LW_CSEL < 0xFF00u;
 }

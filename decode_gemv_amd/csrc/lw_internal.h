@@ -59,6 +59,25 @@ typedef struct {
     uint16_t sym_sorted[256];
 } lw_table;
 
+/* How a lane decoder compares its peek with the limits (derived from the
+ * table at build time, checked again on load).  plan is one of the kernels'
+ * comparison plans (kernels.h); c8/c8m1 hold the byte thresholds t and t - 1
+ * of the two SAD pairs, c16/c16m1 the 16-bit ones of the general plan, xsel
+ * and xk the byte gather and additive constant of the residue plans, sad_k
+ * the accumulator offset; lut_lo/lut_hi, cbase and ncmp the compact tables'
+ * shift bytes and bases. */
+typedef struct {
+    int32_t plan;
+    uint32_t sad_k;
+    uint32_t c8[2], c8m1[2];
+    uint32_t c16, c16m1;
+    uint32_t xsel[2], xk[2];
+    uint32_t lut_lo, lut_hi;
+    int32_t cbase[4];
+    int32_t ncmp;
+    int32_t reserved[3];
+} lw_plan;
+
 /* LW_REG_GPUTAB: tables derived from lw_table for the kernels.
  * With r = number of lengths L in [min_len, max_len) whose limit is <= the
  * peek, the code length is min_len + r. */
@@ -70,7 +89,19 @@ typedef struct {
                                       bf16: exponent << 7 (low bf16 of a pair) */
     uint32_t payload_hi[256];      /* Q6 half2(0, q); bf16 exponent << 23 (high bf16 of a pair) */
     uint32_t symval[256];          /* the symbol itself (decode-only) */
+    lw_plan plan;                  /* the decoders' comparison plan */
 } lw_gputab;
+
+/* LDS byte offsets the plans' accumulator offsets are relative to: the
+ * length entries sit at PBASE - 2*len, the compact tables' at CSEL + 1 - 2r. */
+#define LW_PLAN_PBASE 1024u
+#define LW_PLAN_CSEL 0xD07u
+
+/* Comparison plans (lane_decode.hpp): see kernels.h. */
+enum { LW_P_COMPACT = 0, LW_P_R2 = 1, LW_P_R2K = 2, LW_P_R2X2 = 3, LW_P_GEN = 4 };
+
+/* Derive the comparison plan of a canonical table (bundle.cpp). */
+void lw_make_plan(const lw_table &t, int min_len, int max_len, lw_plan &p);
 
 static inline uint64_t lw_align_up(uint64_t v) { return (v + LW_ALIGN - 1) & ~(uint64_t)(LW_ALIGN - 1); }
 

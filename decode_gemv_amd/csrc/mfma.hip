@@ -85,7 +85,7 @@ LW_DEV f4 mfma(u32x2 a, u32x2 b, f4 acc)
         return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4, a), __builtin_bit_cast(h4, b), acc, 0, 0, 0);
 }
 
-template <int KIND, int N8, int N16>
+template <int KIND, int PLAN>
 __global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -102,11 +102,11 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
 
     // issue every load, tile offsets first; table barrier; own tile (as in fused_q.hip)
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-    const LwTabRegs tr = lw_tab_fetch<lw_compact<N16>()>(a, false);
+    const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, false);
     const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
     LwTileRegs64 tile;
     lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    lw_tab_put<lw_compact<N16>()>(lds, tr, a);
+    lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
     __syncthreads();                      // the decoder table is complete
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
 
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
                 };
                 uint32_t ring[2][16];
                 auto run_chunk = [&](int ch, const uint32_t (&cur)[16]) {
-                    lw_decode_pipelined<N8, N16, 16, XA, true>(
+                    lw_decode_pipelined<PLAN, 16, XA, true>(
                         d, a, pay_off, [&](int g) { return XA{cur[g]}; },
                         [&](int g, int j, uint32_t pay, const XA &x) { put(16 * ch + g, j, pay, x.sm); });
                 };
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
                 }
             } else {
                 struct NoAux {};
-                lw_decode_pipelined<N8, N16, NG, NoAux, true>(
+                lw_decode_pipelined<PLAN, NG, NoAux, true>(
                     d, a, pay_off, [](int) { return NoAux{}; },
                     [&](int g, int j, uint32_t pay, const NoAux &) { put(g, j, pay, 0u); });
             }
@@ -258,13 +258,13 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
     lw_finish_rows<NB, 64>(a, red, (int64_t)c.rb * 64, c.g, c.rb, WAVES, last_flag);
 }
 
-template <int KIND, int N8, int N16>
+template <int KIND, int PLAN>
 hipError_t launch(const KArgs &a, hipStream_t s)
 {
     const LdsLayout L = lds_layout(a.max_words);
     dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
-    auto kern = k_gemv_mfma<KIND, N8, N16>;
-    hipError_t e = lw_allow_lds<k_gemv_mfma<KIND, N8, N16>>();
+    auto kern = k_gemv_mfma<KIND, PLAN>;
+    hipError_t e = lw_allow_lds<k_gemv_mfma<KIND, PLAN>>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, dim3(256), L.total, s, a);
     return hipGetLastError();
@@ -273,16 +273,7 @@ hipError_t launch(const KArgs &a, hipStream_t s)
 template <int KIND>
 hipError_t by_plan(const KArgs &a, SadPlan p, hipStream_t s)
 {
-    if (p.compact) return launch<KIND, 1, LW_N16_COMPACT>(a, s);
-    switch (p.n8ops * 2 + p.n16ops) {
-    case 0: return launch<KIND, 0, 0>(a, s);
-    case 1: return launch<KIND, 0, 1>(a, s);
-    case 2: return launch<KIND, 1, 0>(a, s);
-    case 3: return launch<KIND, 1, 1>(a, s);
-    case 4: return launch<KIND, 2, 0>(a, s);
-    case 5: return launch<KIND, 2, 1>(a, s);
-    }
-    return hipErrorInvalidValue;
+    return lw_with_plan(p, [&](auto P) { return launch<KIND, decltype(P)::value>(a, s); });
 }
 
 }  // namespace

@@ -108,71 +108,29 @@ static KArgs make_args(const lw_dev_bundle *db)
     return a;
 }
 
-// Limit comparisons packed for the SAD counting of lane_decode.hpp.
-// Compact tables (at most four used lengths, the three shorter <= 8, as the
-// builder makes them): the limits of the used lengths but the longest, in
-// byte lanes (top 8 peek bits against limit/8), the count indexing the used
-// lengths.  Other tables: every length min_len .. max_len-1, lengths <= 8 in
-// byte lanes, 9 and 10 in 16-bit lanes (top 16 window bits against
-// limit*32), the count giving the length as min_len + count.  Unused lanes
-// compare 0 with 0 and contribute nothing.
-SadPlan lw_sad_plan(const lw_table &t, int min_len, int max_len, KArgs &a)
+SadPlan lw_apply_plan(const lw_plan &p, KArgs &a)
 {
-    SadPlan p;
-    a.c8[0] = a.c8[1] = a.c8m1[0] = a.c8m1[1] = 0;
-    a.c16 = a.c16m1 = 0;
-    a.lut_lo = a.lut_hi = 0;
-    a.cbase[0] = a.cbase[1] = a.cbase[2] = a.cbase[3] = 0;
-    a.ncmp = 0;
-    int used[LW_MAXLEN + 1], nu = 0;
-    for (int L = 1; L <= LW_MAXLEN; L++)
-        if (t.count[L]) used[nu++] = L;
-    if (nu >= 1 && nu <= 4 && (nu == 1 || used[nu - 2] <= 8)) {
-        uint64_t lut = 0x00FF00FF00FF00FFull;   // even bytes 0xFF: what the selector's zero upper bytes pick
-        for (int r = 0; r < nu; r++) {
-            const int L = used[r];
-            lut |= (uint64_t)((256 - L) & 0xFF) << (8 * (7 - 2 * r));
-            a.cbase[r] = (int32_t)t.offset[L] - (int32_t)t.first[L];
-            if (r < nu - 1) {
-                const uint32_t c = (uint32_t)t.limit[L] >> 3;
-                a.c8[0] |= c << (8 * r);
-                a.c8m1[0] |= (c - 1) << (8 * r);
-            }
-        }
-        a.lut_lo = (uint32_t)lut;
-        a.lut_hi = (uint32_t)(lut >> 32);
-        a.ncmp = nu - 1;
-        a.sad_k = LW_CSEL - (uint32_t)(nu - 1);
-        p.n8ops = 1;
-        p.n16ops = 0;
-        p.compact = true;
-        return p;
+    a.sad_k = p.sad_k;
+    for (int j = 0; j < 2; j++) {
+        a.c8[j] = p.c8[j];
+        a.c8m1[j] = p.c8m1[j];
+        a.xsel[j] = p.xsel[j];
+        a.xk[j] = p.xk[j];
     }
-    int l8[8], l16[2], n8 = 0, n16 = 0;
-    for (int L = min_len; L < max_len; L++) {
-        if (L <= 8) l8[n8++] = L;
-        else l16[n16++] = L;
-    }
-    for (int i = 0; i < n8; i++) {
-        const uint32_t c = (uint32_t)t.limit[l8[i]] >> 3;
-        a.c8[i / 4] |= c << (8 * (i % 4));
-        a.c8m1[i / 4] |= (c - 1) << (8 * (i % 4));
-    }
-    for (int i = 0; i < n16; i++) {
-        const uint32_t c = (uint32_t)t.limit[l16[i]] << 5;
-        a.c16 |= c << (16 * i);
-        a.c16m1 |= (c - 1) << (16 * i);
-    }
-    a.sad_k = LW_PBASE - 2u * (uint32_t)min_len - (uint32_t)(max_len - min_len);
-    p.n8ops = (n8 + 3) / 4;
-    p.n16ops = n16 > 0 ? 1 : 0;
-    p.compact = false;
-    return p;
+    a.c16 = p.c16;
+    a.c16m1 = p.c16m1;
+    a.lut_lo = p.lut_lo;
+    a.lut_hi = p.lut_hi;
+    for (int r = 0; r < 4; r++) a.cbase[r] = p.cbase[r];
+    a.ncmp = p.ncmp;
+    SadPlan sp;
+    sp.plan = p.plan;
+    return sp;
 }
 
 static SadPlan plan_of(const lw_dev_bundle *db, KArgs &a)
 {
-    return lw_sad_plan(db->table, db->h.min_len, db->h.max_len, a);
+    return lw_apply_plan(db->tab.plan, a);
 }
 
 extern "C" lw_status lw_gemv(const lw_dev_bundle *db, const void *x, float *y, int batch, void *stream)
