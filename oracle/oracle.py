@@ -280,15 +280,17 @@ def code_lengths(counts, code: str = "huffman") -> np.ndarray:
     raise ValueError(f"unknown code {code!r}")
 
 
-def build_bundle_q(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray, code: str = "huffman") -> dict:
-    """Quantised bundle: per-matrix table, tile offsets, interleaved words, dm."""
+def build_bundle_q(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray, code: str = "huffman",
+                   lens=None) -> dict:
+    """Quantised bundle: per-matrix table, tile offsets, interleaved words, dm.
+    `lens` (one length per symbol), when given, replaces the chosen code's."""
     R, Cc = codes.shape
     if R % 64 or Cc % 256:
         raise ValueError("shape must be a multiple of 64x256")
     spl = symbols_per_lane(kind)
     syms = symbolise_q(kind, codes)
     counts = histogram(syms, alphabet(kind))
-    lens = code_lengths(counts, code)
+    lens = code_lengths(counts, code) if lens is None else np.ascontiguousarray(lens, dtype=np.uint8)
     tab = canonical(lens)
     tile_off, words, lane_bits = encode_tiles(syms, spl, lens, tab["codes"])
     return dict(kind=kind, rows=R, cols=Cc, spl=spl, counts=counts, table=tab,

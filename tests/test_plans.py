@@ -19,8 +19,8 @@ import numpy as np
 import pytest
 
 import decode_gemv_amd as dg
-import oracle as O
 import synth
+from support import codes_over, plan_of, random_complete_lengths
 
 PBASE, CSEL = 1024, 0xD07
 PLANS = {0: "compact", 1: "r2", 2: "r2k", 3: "r2x2", 4: "gen"}
@@ -68,17 +68,6 @@ def v_add_u32_clamp(a, b):
 
 
 # ------------------------------------------------------------ the stored plan
-
-def plan_of(bundle):
-    """The plan in the bundle's derived GPU tables (lw_gputab.plan)."""
-    g = dg.lw_bundle_region(bundle, dg.LW_REG_GPUTAB, np.uint32)
-    off = (16 * 3 + 256 * 3)                 # limlj, len, base, payload, payload_hi, symval
-    w = g[off:off + 24]
-    return dict(plan=int(w[0]), sad_k=int(w[1]), c8=[int(w[2]), int(w[3])], c8m1=[int(w[4]), int(w[5])],
-                c16=int(w[6]), c16m1=int(w[7]), xsel=[int(w[8]), int(w[9])], xk=[int(w[10]), int(w[11])],
-                lut_lo=int(w[12]), lut_hi=int(w[13]), cbase=[int(np.int32(v)) for v in w[14:18]],
-                ncmp=int(w[18]))
-
 
 def kernel_count(pl, hi):
     """A = s2 - s1 as the kernels compute it for peek registers hi."""
@@ -149,36 +138,6 @@ def check_bundle(bundle, rng, junk_draws=3):
     return pl["plan"]
 
 
-def random_complete_lengths(rng, n_alpha, n_sym, max_depth=11):
-    """Lengths of a random complete prefix code over n_sym of n_alpha symbols:
-    split random leaves of a binary tree (depth <= max_depth) until n_sym
-    leaves exist."""
-    leaves = [0]
-    while len(leaves) < n_sym:
-        cand = [i for i, dpt in enumerate(leaves) if dpt < max_depth]
-        i = cand[rng.integers(len(cand))]
-        dpt = leaves.pop(i)
-        leaves += [dpt + 1, dpt + 1]
-    syms = rng.permutation(n_alpha)[:n_sym]
-    lens = np.zeros(n_alpha, np.uint8)
-    lens[syms] = leaves
-    return lens, syms
-
-
-def codes_over(rng, kind, syms, rows=64, cols=256):
-    """A code matrix in which exactly the given symbols occur (pair symbols for Q4)."""
-    n = rows * cols // (2 if kind == dg.LW_Q4_PAIR else 1)
-    pick = np.concatenate([syms, rng.choice(syms, n - syms.size)])
-    rng.shuffle(pick)
-    if kind == dg.LW_Q4_PAIR:
-        q = np.empty(rows * cols, np.uint8)
-        q[0::2] = pick & 15
-        q[1::2] = pick >> 4
-    else:
-        q = pick.astype(np.uint8)
-    return q.reshape(rows, cols)
-
-
 def test_plans_of_workload_tables():
     rng = np.random.default_rng(7)
     seen = {}
@@ -208,7 +167,7 @@ def test_plans_of_random_complete_codes(seed):
         n_sym = int(rng.integers(2, n_alpha + 1))
         depth = int(rng.integers(max(1, int(np.ceil(np.log2(n_sym)))), 12))
         lens, syms = random_complete_lengths(rng, n_alpha, n_sym, depth)
-        codes = codes_over(rng, kind, syms)
+        codes = codes_over(rng, kind == dg.LW_Q4_PAIR, syms)
         d = np.zeros((64, 1), np.uint16)
         b = dg.lw_bundle_build_q_lens(kind, codes, d, d, lens)
         seen.add(PLANS[check_bundle(b, rng, junk_draws=2)])
@@ -225,7 +184,7 @@ def test_every_plan_is_reached():
         n_sym = int(rng.integers(2, 257))
         depth = int(rng.integers(max(1, int(np.ceil(np.log2(n_sym)))), 12))
         lens, syms = random_complete_lengths(rng, 256, n_sym, depth)
-        b = dg.lw_bundle_build_q_lens(kind, codes_over(rng, kind, syms), np.zeros((64, 1), np.uint16),
+        b = dg.lw_bundle_build_q_lens(kind, codes_over(rng, True, syms), np.zeros((64, 1), np.uint16),
                                       np.zeros((64, 1), np.uint16), lens)
         pl = plan_of(b)["plan"]
         if PLANS[pl] not in seen:
