@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <map>
 #include <memory>
+#include <mutex>
 #include <string>
 
 #include <rocblas/rocblas.h>
@@ -133,17 +134,22 @@ static SadPlan plan_of(const lw_dev_bundle *db, KArgs &a)
     return lw_apply_plan(db->tab.plan, a);
 }
 
-extern "C" lw_status lw_gemv(const lw_dev_bundle *db, const void *x, float *y, int batch, void *stream)
+static lw_status gemv_check(const lw_dev_bundle *db, const void *x, float *y, int batch)
 {
     if (!db || !x || !y) return lw_fail(LW_E_ARG, "null argument");
     if (batch < 1 || batch > LW_BATCH_MAX) return lw_fail(LW_E_ARG, "batch must be in 1..16");
     if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 16)
         return lw_fail(LW_E_ARG, "x and y must be 16-byte aligned");
-    KArgs a = make_args(db);
+    return LW_OK;
+}
+
+// Launch the GEMV kernel of a bundle's kind and the batch; a.part and
+// a.count name the split-column reduction's scratch.
+static lw_status gemv_launch(const lw_dev_bundle *db, KArgs &a, const void *x, float *y, int batch, hipStream_t s)
+{
     a.x = static_cast<const uint16_t *>(x);
     a.y = y;
     a.batch = batch;
-    hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     a.pal0 = db->h.kind == LW_BF16_EXP ? db->tab.payload[0] >> 7 : 0u;
     if (batch >= 8)                        // a real dense contraction: matrix cores
@@ -155,6 +161,86 @@ extern "C" lw_status lw_gemv(const lw_dev_bundle *db, const void *x, float *y, i
     if (e == hipErrorNotSupported) return lw_fail(LW_E_UNSUPPORTED, "no kernel for this kind and batch");
     if (e != hipSuccess) return hip_fail(e, "gemv launch");
     return LW_OK;
+}
+
+extern "C" lw_status lw_gemv(const lw_dev_bundle *db, const void *x, float *y, int batch, void *stream)
+{
+    lw_status st = gemv_check(db, x, y, batch);
+    if (st) return st;
+    KArgs a = make_args(db);
+    return gemv_launch(db, a, x, y, batch, (hipStream_t)stream);
+}
+
+// ------------------------------------------------ lw_gemv without a workspace
+// The split-column reduction's partial sums and arrival counters live in a
+// file-scope device array instead of the bundle's workspace region.  Each
+// device holds its own copy of the array; host code uses only the address
+// hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in there), looked up once per device.
+#define LW_NOALLOC_SCRATCH_BYTES (16u << 20)
+static __device__ __align__(256) uint8_t scratch[LW_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+__global__ __launch_bounds__(256) void k_zero_u32(uint32_t *p, uint32_t n)
+{
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+struct DeviceScratch {
+    std::once_flag once;
+    uint8_t *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+
+// The current device's scratch address (looked up on its first use there).
+hipError_t device_scratch(uint8_t **out)
+{
+    constexpr int MAXDEV = 64;
+    static DeviceScratch per_dev[MAXDEV];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAXDEV) return hipErrorInvalidDevice;
+    DeviceScratch &d = per_dev[dev];
+    std::call_once(d.once, [&d]() {
+        void *p = nullptr;
+        d.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        d.ptr = d.err == hipSuccess ? static_cast<uint8_t *>(p) : nullptr;
+    });
+    *out = d.ptr;
+    return d.ptr ? d.err : (d.err != hipSuccess ? d.err : hipErrorInvalidSymbol);
+}
+
+}  // namespace
+
+extern "C" lw_status lw_gemv_noalloc(const lw_dev_bundle *db, const void *x, float *y, int batch, void *stream)
+{
+    lw_status st = gemv_check(db, x, y, batch);
+    if (st) return st;
+    KArgs a = make_args(db);
+    hipStream_t s = (hipStream_t)stream;
+    const uint64_t need = db->h.bytes[LW_REG_WORK];   // partial sums + counters (0: no split reduction)
+    if (need > LW_NOALLOC_SCRATCH_BYTES)
+        return lw_fail(LW_E_UNSUPPORTED, "the split-column reduction of this bundle needs " + std::to_string(need) +
+                                             " bytes of scratch, more than the " +
+                                             std::to_string(LW_NOALLOC_SCRATCH_BYTES) +
+                                             " lw_gemv_noalloc holds; use lw_gemv");
+    if (need) {
+        uint8_t *sp = nullptr;
+        hipError_t e = device_scratch(&sp);
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        const uint64_t pbytes = lw_work_partial_bytes(db->h.work_groups, db->h.rows);
+        a.part = reinterpret_cast<float *>(sp);
+        a.count = reinterpret_cast<uint32_t *>(sp + pbytes);
+        // the arrival counters must start at zero: the array keeps the last call's contents
+        const uint32_t nctr = (uint32_t)((need - pbytes) / 4u);
+        hipLaunchKernelGGL(k_zero_u32, dim3((nctr + 255u) / 256u), dim3(256), 0, s, a.count, nctr);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "scratch counter clear");
+    }
+    return gemv_launch(db, a, x, y, batch, s);
 }
 
 extern "C" lw_status lw_decode_only(const lw_dev_bundle *db, void *out, size_t out_bytes, uint32_t *lane_bits,

@@ -70,6 +70,7 @@ def _load():
         "lw_bundle_upload": (st, [P, P, C.c_size_t, P, C.POINTER(P)]),
         "lw_dev_bundle_free": (None, [P]),
         "lw_gemv": (st, [P, P, P, i32, P]),
+        "lw_gemv_noalloc": (st, [P, P, P, i32, P]),
         "lw_decode_only": (st, [P, P, C.c_size_t, P, P]),
         "lw_twin_gemv": (st, [P, P, i32, i64, i64, P, P, i32, P]),
         "lw_swiglu": (st, [P, P, P, i64, P]),
@@ -319,6 +320,10 @@ def lw_bundle_upload(b: Bundle, dev_buf, stream=None) -> DevBundle:
 
 def lw_gemv(db: DevBundle, x, y, batch: int, stream=None) -> None:
     _check(_L.lw_gemv(db.ptr, _dptr(x, "x"), _dptr(y, "y"), batch, _stream(stream)))
+
+
+def lw_gemv_noalloc(db: DevBundle, x, y, batch: int, stream=None) -> None:
+    _check(_L.lw_gemv_noalloc(db.ptr, _dptr(x, "x"), _dptr(y, "y"), batch, _stream(stream)))
 
 
 def lw_decode_only(db: DevBundle, out, lane_bits=None, stream=None) -> None:

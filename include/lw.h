@@ -233,6 +233,20 @@ void lw_dev_bundle_free(lw_dev_bundle *db);
  * Errors: LW_E_ARG, LW_E_UNSUPPORTED, LW_E_DEVICE. */
 lw_status lw_gemv(const lw_dev_bundle *db, const void *x, float *y, int batch, void *stream);
 
+/* lw_gemv for callers that cannot allocate device memory or reserve a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same kernels and results as lw_gemv, with the
+ * split-column reduction's partial sums and arrival counters taken from a
+ * scratch array the library holds per device (16 MiB, held until the process
+ * ends) instead of the bundle's workspace region.  Nothing is allocated; the
+ * counters are cleared by a small kernel on `stream` before the GEMV.
+ * Calls that overlap in time on one device share that array and race: run
+ * them on one stream, or order them.  Arguments as lw_gemv.
+ * Errors: as lw_gemv; LW_E_UNSUPPORTED when the bundle's reduction needs more
+ * scratch than 16 MiB (groups * 16 * rows * 4 bytes of partial sums plus the
+ * counters; lw_bundle_info.region_bytes[LW_REG_WORK] gives it). */
+lw_status lw_gemv_noalloc(const lw_dev_bundle *db, const void *x, float *y, int batch, void *stream);
+
 /* Decode only: restore the fixed-width codes ("3 . Decode on demand": the unit
  * restores the packed codes).
  *   Q4  : out [rows][cols/2] bytes, low nibble = even column (the twin layout)
