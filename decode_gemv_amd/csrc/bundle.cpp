@@ -880,6 +880,29 @@ extern "C" lw_status lw_bundle_build_bf16_compact(int64_t rows, int64_t cols, co
 }
 
 // ----------------------------------------------------------------- validate
+const char *lw_region_name(int r)
+{
+    static const char *names[LW_REG_COUNT] = {"table", "gputab", "tile_off", "words", "dm", "palette",
+                                             "sm", "vb_bits", "vb_start", "verbatim", "split", "work"};
+    return r >= 0 && r < LW_REG_COUNT ? names[r] : "?";
+}
+
+uint32_t lw_regions_needed(const lw_image_header &h, int op)
+{
+    const bool bf16 = h.kind == LW_BF16_EXP;
+    uint32_t m = 1u << LW_REG_GPUTAB | 1u << LW_REG_TILE_OFF | 1u << LW_REG_WORDS | 1u << LW_REG_SPLIT;
+    if (op == LW_OP_ANY) m |= 1u << LW_REG_TABLE;
+    if (bf16) {
+        m |= 1u << LW_REG_SM | 1u << LW_REG_VB_BITS | 1u << LW_REG_VB_START;
+        if (op == LW_OP_ANY) m |= 1u << LW_REG_PALETTE;
+        if (h.n_verbatim > 0) m |= 1u << LW_REG_VERBATIM;
+    } else if (op != LW_OP_DECODE) {
+        m |= 1u << LW_REG_DM;                     // scales of the dequantisation
+    }
+    if (op != LW_OP_DECODE && h.work_groups > 1) m |= 1u << LW_REG_WORK;   // split-column reduction
+    return m;
+}
+
 static lw_status validate_image(const uint8_t *img, size_t bytes)
 {
     if (bytes < LW_HEADER_BYTES) return lw_fail(LW_E_FORMAT, "image shorter than its header");
@@ -899,11 +922,9 @@ static lw_status validate_image(const uint8_t *img, size_t bytes)
             return lw_fail(LW_E_FORMAT, "region out of bounds: " + std::to_string(r));
         prev_end = h.off[r] + h.bytes[r];
     }
-    bool need[LW_REG_COUNT] = {true, true, true, true, h.kind != LW_BF16_EXP, h.kind == LW_BF16_EXP,
-                               h.kind == LW_BF16_EXP, h.kind == LW_BF16_EXP, h.kind == LW_BF16_EXP,
-                               false, true, false};
+    const uint32_t need = lw_regions_needed(h, LW_OP_ANY);
     for (int r = 0; r < LW_REG_COUNT; r++)
-        if (need[r] && !h.bytes[r]) return lw_fail(LW_E_FORMAT, "missing region " + std::to_string(r));
+        if ((need >> r & 1u) && !h.bytes[r]) return lw_fail(LW_E_FORMAT, std::string("missing region ") + lw_region_name(r));
     if (h.bytes[LW_REG_TABLE] != sizeof(lw_table) || h.bytes[LW_REG_GPUTAB] != sizeof(lw_gputab))
         return lw_fail(LW_E_FORMAT, "table region size");
     if (h.bytes[LW_REG_TILE_OFF] != 4u * (uint64_t)(h.n_tiles + 1)) return lw_fail(LW_E_FORMAT, "tile_off size");

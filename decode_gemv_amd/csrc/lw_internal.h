@@ -100,6 +100,13 @@ typedef struct {
 /* Comparison plans (lane_decode.hpp): see kernels.h. */
 enum { LW_P_COMPACT = 0, LW_P_R2 = 1, LW_P_R2K = 2, LW_P_R2X2 = 3, LW_P_GEN = 4 };
 
+/* Regions each kind of kernel reads (bundle.cpp): a bit mask over lw_region.
+ * LW_OP_ANY is the union over every kernel of the kind (what a valid image
+ * must hold); the launch paths check their own op before enqueueing. */
+enum { LW_OP_GEMV = 0, LW_OP_DECODE = 1, LW_OP_ANY = 2 };
+uint32_t lw_regions_needed(const lw_image_header &h, int op);
+const char *lw_region_name(int r);
+
 /* Derive the comparison plan of a canonical table (bundle.cpp). */
 void lw_make_plan(const lw_table &t, int min_len, int max_len, lw_plan &p);
 

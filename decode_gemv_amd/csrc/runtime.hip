@@ -143,6 +143,18 @@ static lw_status gemv_check(const lw_dev_bundle *db, const void *x, float *y, in
     return LW_OK;
 }
 
+// Refuse a launch whose kernels would read a region the bundle does not
+// hold (an absent region has a null device pointer).
+static lw_status require_regions(const lw_dev_bundle *db, int op, const char *what, uint32_t supplied = 0)
+{
+    const uint32_t need = lw_regions_needed(db->h, op) & ~supplied;
+    for (int r = 0; r < LW_REG_COUNT; r++)
+        if ((need >> r & 1u) && !db->h.bytes[r])
+            return lw_fail(LW_E_FORMAT, std::string(what) + " reads region " + lw_region_name(r) +
+                                            ", which this bundle does not hold");
+    return LW_OK;
+}
+
 // Launch the GEMV kernel of a bundle's kind and the batch; a.part and
 // a.count name the split-column reduction's scratch.
 static lw_status gemv_launch(const lw_dev_bundle *db, KArgs &a, const void *x, float *y, int batch, hipStream_t s)
@@ -167,6 +179,7 @@ extern "C" lw_status lw_gemv(const lw_dev_bundle *db, const void *x, float *y, i
 {
     lw_status st = gemv_check(db, x, y, batch);
     if (st) return st;
+    if ((st = require_regions(db, LW_OP_GEMV, "lw_gemv"))) return st;
     KArgs a = make_args(db);
     return gemv_launch(db, a, x, y, batch, (hipStream_t)stream);
 }
@@ -219,6 +232,8 @@ extern "C" lw_status lw_gemv_noalloc(const lw_dev_bundle *db, const void *x, flo
 {
     lw_status st = gemv_check(db, x, y, batch);
     if (st) return st;
+    // the workspace comes from the scratch array, not from the bundle
+    if ((st = require_regions(db, LW_OP_GEMV, "lw_gemv_noalloc", 1u << LW_REG_WORK))) return st;
     KArgs a = make_args(db);
     hipStream_t s = (hipStream_t)stream;
     const uint64_t need = db->h.bytes[LW_REG_WORK];   // partial sums + counters (0: no split reduction)
@@ -252,6 +267,8 @@ extern "C" lw_status lw_decode_only(const lw_dev_bundle *db, void *out, size_t o
                                                        : (uint64_t)db->h.rows * db->h.cols * 2;
     if (out_bytes < need) return lw_fail(LW_E_ARG, "output buffer too small");
     if (reinterpret_cast<uintptr_t>(out) % 16) return lw_fail(LW_E_ARG, "output must be 16-byte aligned");
+    lw_status st = require_regions(db, LW_OP_DECODE, "lw_decode_only");
+    if (st) return st;
     KArgs a = make_args(db);
     a.out = out;
     a.lane_bits = lane_bits;
@@ -424,6 +441,8 @@ extern "C" lw_status lw_bf16_transcode(const lw_dev_bundle *db, int form, void *
         return lw_fail(LW_E_ARG, "output buffer too small");
     if (reinterpret_cast<uintptr_t>(out) % 16 || reinterpret_cast<uintptr_t>(vrank) % 16)
         return lw_fail(LW_E_ARG, "out and vrank must be 16-byte aligned");
+    lw_status st = require_regions(db, LW_OP_DECODE, "lw_bf16_transcode");
+    if (st) return st;
     KArgs a = make_args(db);
     a.out = out;
     a.vrank = vrank;

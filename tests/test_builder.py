@@ -260,6 +260,40 @@ def test_corrupt_images_rejected(what):
     assert e.value.status == expect, (what, e.value)
 
 
+REGION_NAMES = ["table", "gputab", "tile_off", "words", "dm", "palette", "sm", "vb_bits", "vb_start",
+                "verbatim", "split", "work"]
+
+
+@pytest.mark.parametrize("kind", ["q4", "bf16"])
+def test_missing_region_rejected(kind):
+    """An image without a region some kernel of its kind reads is refused
+    (LW_E_FORMAT, the region named) -- the same requirement table the launch
+    paths check before they enqueue anything, so a kernel never reads an
+    absent region through a null pointer."""
+    if kind == "q4":
+        codes, d, m, _ = synth.gen_q_custom(128, 1280, 71)          # five column blocks: a workspace
+        b = dg.lw_bundle_build_q(dg.LW_Q4_PAIR, codes, d, m)
+        needed = ["table", "gputab", "tile_off", "words", "dm", "split", "work"]
+    else:
+        w, _ = synth.gen_bf16_custom(128, 1280, 72, outlier_frac=0.02)
+        b = dg.lw_bundle_build_bf16(w)
+        needed = ["table", "gputab", "tile_off", "words", "palette", "sm", "vb_bits", "vb_start", "verbatim",
+                  "split", "work"]
+    info = dg.lw_bundle_get_info(b)
+    assert info["n_cb"] > 4 and (kind == "q4" or info["n_verbatim"] > 0)
+    base = dg.lw_bundle_image(b)
+    for name in needed:
+        r = REGION_NAMES.index(name)
+        img = base.copy()
+        hdr = img[:512].view(np.uint64)
+        hdr[104 // 8 + r] = 0                      # offset
+        hdr[200 // 8 + r] = 0                      # size
+        with pytest.raises(dg.LwError) as e:
+            dg.lw_bundle_load(img)
+        assert e.value.status == dg.LW_E_FORMAT, name
+        assert name in str(e.value), (name, str(e.value))
+
+
 # ------------------------------------------------------------------ tile-skipping fixed-width twin
 
 @pytest.mark.parametrize("bits,rows,cols,seed", [(2, 128, 512, 61), (4, 192, 768, 62), (8, 64, 1280, 63),
