@@ -542,15 +542,16 @@ LW_DEV bool lw_lane_init(LaneDec &d, uint8_t *lds, const uint32_t *slots, int l,
     return (lb & 255u) == 0 && lb + LW_CSEL < 0xFF00u;
 }
 
-// Sum the per-wave partials of the workgroup's ROWS rows (red[wave][b][row])
-// and either write y (one column group) or take part in the split-column
-// reduction.  The partials travel through the bundle's workspace as
-// device-scope atomic exchanges, which are performed at the coherence point
+// Sum the per-wave partials of the workgroup's ROWS rows (red[wave][b][row],
+// RS floats between consecutive (wave, b) runs) and either write y (one
+// column group) or take part in the split-column reduction.  The partials
+// travel through the bundle's workspace as device-scope atomic exchanges,
+// which are performed at the coherence point
 // of all XCDs without an L2 writeback; each workgroup then bumps the arrival
 // counter of its rows (index ctr), and the last one to arrive reads the
 // partials back with device-scope atomic loads and adds them in group order
 // (deterministic), then re-arms the counter for the next call.
-template <int BATCH, int ROWS = 128>
+template <int BATCH, int ROWS = 128, int RS = ROWS>
 LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g, int ctr, int waves,
                            uint32_t *last_flag)
 {
@@ -558,7 +559,7 @@ LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g
         const int b = i / ROWS, row = i % ROWS;
         if (b >= a.batch) break;
         float v = 0.f;
-        for (int w = 0; w < waves; w++) v += red[(w * BATCH + b) * ROWS + row];
+        for (int w = 0; w < waves; w++) v += red[(w * BATCH + b) * RS + row];
         if (row0 + row < a.rows) {
             if (a.groups == 1) a.y[(size_t)b * a.rows + row0 + row] = v;
             else

@@ -3,18 +3,28 @@
 // product fed from on-chip memory follows the reconstructive matmul idea of
 // "Unweight", section "How reconstructive matmul works").
 //
-// At batch >= 8 the product is a real dense contraction (64 rows x 32
+// At batch >= 8 the product is a real dense contraction (64 rows x 16
 // columns x 16 batch per step), so the decoded weights go through a small
 // LDS staging tile into v_mfma_f32_16x16x16{f16,bf16}:
 //   - one wavefront per tile: lane l + 32*half decodes tile row 2l + half
-//     (the second row from the lane's split bit) 32 columns at a time and
-//     writes them as 16-bit values to stage[lane][0..31] (row stride 80
-//     bytes: conflict-free 16-byte writes and 8-byte fragment reads);
-//   - every 32 columns, 2 k-steps x 4 row blocks of 16x16x16 MFMA
-//     accumulate D[row][batch] += W[row][k] * X[k][batch], with the X
-//     fragments (x[batch][k], zero for batch >= the call's batch) loaded
-//     from global memory one chunk ahead;
+//     (the second row from the lane's split bit) and writes each group of
+//     decoded weights as 8-byte stores (two for Q4) into its row of a 64 x 16
+//     staging block: 32-byte rows, the row's four 8-byte fragments (4
+//     columns each) permuted by fragment ^ ((row >> 2 ^ row >> 4) & 3), so
+//     that the stores (one fragment of 64 rows) and the fragment reads of the
+//     MFMA operands (16 rows x 4 fragments) each hit distinct banks;
+//   - every 16 columns, 4 row blocks of 16x16x16 MFMA accumulate
+//     D[row][batch] += W[row][k] * X[k][batch], with the X fragments
+//     (x[batch][k], zero for batch >= the call's batch) loaded from global
+//     memory one chunk ahead (loading all of them in the prologue measured
+//     slower); the activation sums of the dequantisation come from the same
+//     fragments by v_dot2 against (1, 1);
 //   - dequantisation uses y = d * (W q x) - m * sum(x) per tile row.
+// A workgroup is WPG wavefronts on WPG column blocks of one row band, as in
+// the VALU kernel: sixteen (whole rows) when a row band has 13 to 16 column
+// blocks, fourteen when the column blocks are a multiple of 14 and the whole
+// grid is resident at once, else four; the staging block is small enough that
+// a CU holds the whole grid of the 4096 x 14336 down projection at once.
 // MFMA 16x16x16 lane layout: A lane i = A[i%16][4(i/16)..+3], B lane i =
 // B[4(i/16)..+3][i%16], D lane i = D[4(i/16)+j][i%16], j = 0..3.
 #include <type_traits>
@@ -25,8 +35,17 @@ namespace {
 
 constexpr int WAVES = 4;
 constexpr int NB = 16;                     // batch columns of the MFMA tile
-constexpr int STAGE_STRIDE = 80;           // bytes per staged row (32 x 2 bytes + 16 pad)
+constexpr int CHUNK = 16;                  // columns staged per MFMA step
+constexpr int RED_RS = 65;                 // floats per (wavefront, batch) run of the partial sums: the 16
+                                           // lanes of one batch column store to distinct banks
+constexpr int STAGE_STRIDE = 32;           // bytes per staged row (16 x 2 bytes)
 constexpr int STAGE_BYTES = 64 * STAGE_STRIDE;
+
+// byte offset of 8-byte fragment f (columns 4f .. 4f+3) of staged row R
+__host__ __device__ constexpr uint32_t stage_frag(int R, int f)
+{
+    return (uint32_t)(R * STAGE_STRIDE + 8 * (f ^ (((R >> 2) ^ (R >> 4)) & 3)));
+}
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef short s4 __attribute__((ext_vector_type(4)));
@@ -37,13 +56,13 @@ struct LdsLayout {
     uint32_t tiles, stage, flag, total;
 };
 
-__host__ __device__ inline LdsLayout lds_layout(int max_words)
+__host__ __device__ inline LdsLayout lds_layout(int max_words, int waves)
 {
     LdsLayout L;
     L.stage = LW_TAB_BYTES;
-    L.tiles = L.stage + WAVES * STAGE_BYTES;
-    const uint32_t tiles = (uint32_t)(WAVES * (max_words + 3) * 128);
-    const uint32_t red = (uint32_t)(WAVES * NB * 64 * 4);
+    L.tiles = L.stage + waves * STAGE_BYTES;
+    const uint32_t tiles = (uint32_t)(waves * (max_words + 3) * 128);
+    const uint32_t red = (uint32_t)(waves * NB * RED_RS * 4);
     L.flag = L.tiles + (tiles > red ? tiles : red);
     L.total = L.flag + 16;
     return L;
@@ -51,13 +70,13 @@ __host__ __device__ inline LdsLayout lds_layout(int max_words)
 
 // Identity of a lane: one wavefront per tile, lane l + 32*half decodes tile
 // row 2l + half (the second row from the lane's split bit); the lane's index
-// is also its row of the staged 64 x 32 weight block.
+// is also its row of the staged 64 x 16 weight block.
 struct LaneCtx {
     int wave, lane, half, l, g, cb, rb, t;
     bool active;
 };
 
-LW_DEV LaneCtx lane_ctx(const KArgs &a)
+LW_DEV LaneCtx lane_ctx(const KArgs &a, int waves)
 {
     LaneCtx c;
     c.wave = (int)lw_wave_id();
@@ -66,13 +85,13 @@ LW_DEV LaneCtx lane_ctx(const KArgs &a)
     c.l = c.lane & 31;
     c.g = blockIdx.x;
     c.rb = blockIdx.y;
-    c.cb = c.g * WAVES + c.wave;
+    c.cb = c.g * waves + c.wave;
     c.active = c.cb < a.n_cb;
     c.t = c.rb * a.n_cb + (c.active ? c.cb : 0);
     return c;
 }
 
-LW_DEV void lw_st32(uint32_t addr, uint32_t v) { *(__attribute__((address_space(3))) uint32_t *)(size_t)addr = v; }
+LW_DEV void lw_st64(uint32_t addr, u32x2 v) { *(__attribute__((address_space(3))) u32x2 *)(size_t)addr = v; }
 LW_DEV u32x2 lw_ld64(uint32_t addr) { return *(__attribute__((address_space(3))) const u32x2 *)(size_t)addr; }
 
 template <int KIND>
@@ -85,40 +104,45 @@ LW_DEV f4 mfma(u32x2 a, u32x2 b, f4 acc)
         return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4, a), __builtin_bit_cast(h4, b), acc, 0, 0, 0);
 }
 
-template <int KIND, int PLAN>
-__global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
+template <int KIND, int PLAN, int WPG>
+__global__ __launch_bounds__(64 * WPG) void k_gemv_mfma(KArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    constexpr int GPC = KIND == LW_Q4_PAIR ? 4 : 8;      // groups of four symbols per 32-column chunk
+    constexpr int GPC = KIND == LW_Q4_PAIR ? 2 : 4;      // groups of four symbols per 16-column chunk
     constexpr int NG = KIND == LW_Q4_PAIR ? 32 : 64;     // groups per tile row
-    const LdsLayout L = lds_layout(a.max_words);
-    const LaneCtx c = lane_ctx(a);
+    constexpr int NCHUNK = 256 / CHUNK;
+    const LdsLayout L = lds_layout(a.max_words, WPG);
+    const LaneCtx c = lane_ctx(a, WPG);
     const int S = a.max_words + 3;
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
     const uint32_t stage = (uint32_t)(size_t)(lds + L.stage + c.wave * STAGE_BYTES);
-    const uint32_t my_row = stage + (uint32_t)(c.lane * STAGE_STRIDE);
     // MFMA fragment coordinates of this lane
     const int fr = c.lane & 15, fk = c.lane >> 4;
+    // this lane's stores (fragment f of row lane) and operand reads (fragment fk of row 16 r + fr)
+    uint32_t st_at[4], ld_at[4];
+#pragma unroll
+    for (int f = 0; f < 4; f++) {
+        st_at[f] = stage + stage_frag(c.lane, f);
+        ld_at[f] = stage + stage_frag(16 * f + fr, fk);
+    }
 
     // issue every load, tile offsets first; table barrier; own tile (as in fused_q.hip)
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
     const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, false);
     const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
     LwTileRegs64 tile;
-    lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
+    if constexpr (WPG <= WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
     __syncthreads();                      // the decoder table is complete
+    if constexpr (WPG > WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
 
-    // x fragments: lane holds x[b = fr][col0 + 16 kk + 4 fk .. +3] for kk = 0, 1
+    // x fragments: lane holds x[b = fr][col0 + 16 chunk + 4 fk .. +3], zero for b >= batch
     const bool xb_ok = fr < a.batch;
     const uint16_t *xrow = a.x + (size_t)(xb_ok ? fr : 0) * a.cols + (size_t)(c.active ? c.cb : 0) * 256 + 4 * fk;
-    auto load_x = [&](int chunk, u32x2 (&dst)[2]) {
-#pragma unroll
-        for (int kk = 0; kk < 2; kk++) {
-            const u32x2 v = *reinterpret_cast<const u32x2 *>(xrow + 32 * chunk + 16 * kk);
-            dst[kk] = xb_ok ? v : u32x2{0u, 0u};
-        }
+    auto load_x = [&](int chunk) -> u32x2 {
+        const u32x2 v = *reinterpret_cast<const u32x2 *>(xrow + CHUNK * chunk);
+        return xb_ok ? v : u32x2{0u, 0u};
     };
 
     f4 acc[4];
@@ -131,48 +155,59 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
         const bool ok = lw_lane_init(d, lds, slots, c.l, a);
         d.advance(c.half ? split : 0u);       // the second tile row starts at the split bit
         if (ok) {
-            u32x2 xcur[2];
-            load_x(0, xcur);
-            uint32_t pend = 0;
-            auto mfma_step = [&](int chunk) {
+            u32x2 xcur = load_x(0);
+            uint32_t gw[4];                   // the current group's 16-bit weights, two per word
+            // A chunk's weight fragments are requested when its last group is
+            // stored and multiplied one group later, so the LDS round trip
+            // overlaps decoding (the next group's store to the same staging
+            // row is issued after those reads, and a wavefront's LDS
+            // operations complete in order).
+            u32x2 af[4], xpend;
+            auto read_chunk = [&](int chunk) {
 #pragma unroll
-                for (int kk = 0; kk < 2; kk++) {
-                    if constexpr (KIND == LW_BF16_EXP)
-                        sx += __builtin_bit_cast(float, xcur[kk].x << 16) +
-                              __builtin_bit_cast(float, xcur[kk].x & 0xFFFF0000u) +
-                              __builtin_bit_cast(float, xcur[kk].y << 16) +
-                              __builtin_bit_cast(float, xcur[kk].y & 0xFFFF0000u);
-                    else
-                        sx += lw_half_lo(xcur[kk].x) + lw_half_hi(xcur[kk].x) + lw_half_lo(xcur[kk].y) +
-                              lw_half_hi(xcur[kk].y);
-#pragma unroll
-                    for (int r = 0; r < 4; r++) {
-                        const u32x2 af = lw_ld64(stage + (uint32_t)((16 * r + fr) * STAGE_STRIDE + 32 * kk + 8 * fk));
-                        acc[r] = mfma<KIND>(af, xcur[kk], acc[r]);
-                    }
-                }
+                for (int r = 0; r < 4; r++) af[r] = lw_ld64(ld_at[r]);
+                xpend = xcur;
                 // x of the next chunk, used one chunk of decoding later
-                load_x(chunk + 1 < 8 ? chunk + 1 : chunk, xcur);
+                xcur = load_x(chunk + 1 < NCHUNK ? chunk + 1 : chunk);
+            };
+            auto mfma_step = [&]() {
+                if constexpr (KIND == LW_BF16_EXP) {
+                    sx += __builtin_bit_cast(float, xpend.x << 16) + __builtin_bit_cast(float, xpend.x & 0xFFFF0000u) +
+                          __builtin_bit_cast(float, xpend.y << 16) + __builtin_bit_cast(float, xpend.y & 0xFFFF0000u);
+                } else {
+                    sx = lw_dot2(xpend.x, 0x3C003C00u, sx);     // (1, 1) in fp16
+                    sx = lw_dot2(xpend.y, 0x3C003C00u, sx);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; r++) acc[r] = mfma<KIND>(af[r], xpend, acc[r]);
             };
             auto put = [&](int g, int j, uint32_t pay, uint32_t smw) {
-                // 16-bit weights of this symbol into the staged row
+                if (j == 0) lw_ramp<NG>(a.ramp, g);
+                // 16-bit weights of this symbol into the group's words
                 if constexpr (KIND == LW_Q4_PAIR) {
-                    lw_st32(my_row + (uint32_t)(((g % GPC) * 4 + j) * 4), pay);
-                } else {
+                    gw[j] = pay;
+                } else if constexpr (KIND == LW_BF16_EXP) {
                     if (j & 1) {
-                        uint32_t w2;
-                        if constexpr (KIND == LW_BF16_EXP) {
-                            const uint32_t spread = __builtin_amdgcn_perm(smw, smw, j == 1 ? 0x01010000u : 0x03030202u);
-                            w2 = (spread & 0x807F807Fu) | pend | pay;
-                        } else {
-                            w2 = pend | pay;
-                        }
-                        lw_st32(my_row + (uint32_t)(((g % GPC) * 2 + (j >> 1)) * 4), w2);
+                        const uint32_t spread = __builtin_amdgcn_perm(smw, smw, j == 1 ? 0x01010000u : 0x03030202u);
+                        gw[j >> 1] = (spread & 0x807F807Fu) | gw[j >> 1] | pay;
                     } else {
-                        pend = pay;
+                        gw[j >> 1] = pay;
                     }
+                } else {
+                    if (j & 1) gw[j >> 1] |= pay;
+                    else gw[j >> 1] = pay;
                 }
-                if (j == 3 && (g % GPC) == GPC - 1) mfma_step(g / GPC);
+                if (j == 3) {
+                    // the group's fragments into the staged row (Q4: 8 columns, two fragments)
+                    if constexpr (KIND == LW_Q4_PAIR) {
+                        lw_st64(st_at[2 * (g % GPC)], u32x2{gw[0], gw[1]});
+                        lw_st64(st_at[2 * (g % GPC) + 1], u32x2{gw[2], gw[3]});
+                    } else {
+                        lw_st64(st_at[g % GPC], u32x2{gw[0], gw[1]});
+                    }
+                    if ((g % GPC) == 0 && g > 0) mfma_step();          // the previous chunk
+                    if ((g % GPC) == GPC - 1) read_chunk(g / GPC);
+                }
             };
             auto pay_off = [](int j) { return (KIND != LW_Q4_PAIR && (j & 1)) ? (LW_TPAY_HI - LW_TPAY) : 0u; };
             if constexpr (KIND == LW_BF16_EXP) {
@@ -205,6 +240,7 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
                     d, a, pay_off, [](int) { return NoAux{}; },
                     [&](int g, int j, uint32_t pay, const NoAux &) { put(g, j, pay, 0u); });
             }
+            mfma_step();                      // the last chunk
         } else {
 #pragma unroll
             for (int r = 0; r < 4; r++)
@@ -234,7 +270,7 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
                     v = lw_half_lo(w) * acc[r][jj] - lw_half_hi(w) * sx;
                 }
             }
-            red[(c.wave * NB + fr) * 64 + trow] = v;
+            red[(c.wave * NB + fr) * RED_RS + trow] = v;
         }
     __syncthreads();
     if constexpr (KIND == LW_BF16_EXP) {
@@ -248,26 +284,44 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(KArgs a)
                 for (int b = 0; b < a.batch; b++) {
                     const float sb = lw_wave_sum(
                         wdiff * __builtin_bit_cast(float, (uint32_t)xcol[(size_t)b * a.cols + col] << 16));
-                    if (c.lane == 0) red[(c.wave * NB + b) * 64 + row] += sb;
+                    if (c.lane == 0) red[(c.wave * NB + b) * RED_RS + row] += sb;
                 }
             });
         }
         __syncthreads();
     }
     uint32_t *last_flag = reinterpret_cast<uint32_t *>(lds + L.flag);
-    lw_finish_rows<NB, 64>(a, red, (int64_t)c.rb * 64, c.g, c.rb, WAVES, last_flag);
+    lw_finish_rows<NB, 64, RED_RS>(a, red, (int64_t)c.rb * 64, c.g, c.rb, WPG, last_flag);
 }
 
+template <int KIND, int PLAN, int WPG>
+hipError_t launch_wpg(const KArgs &a0, hipStream_t s)
+{
+    KArgs a = a0;
+    a.groups = (a.n_cb + WPG - 1) / WPG;  // column groups combined through the workspace (none if 1)
+    a.ramp = lw_resident_ramp((int64_t)a.n_rb * a.n_cb);
+    const LdsLayout L = lds_layout(a.max_words, WPG);
+    dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
+    auto kern = k_gemv_mfma<KIND, PLAN, WPG>;
+    hipError_t e = lw_allow_lds<k_gemv_mfma<KIND, PLAN, WPG>>();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, grid, dim3(64 * WPG), L.total, s, a);
+    return hipGetLastError();
+}
+
+// Workgroup shape as in the VALU kernel: whole rows (16 wavefronts) for 13..16
+// column blocks, 14 wavefronts when the column blocks are a multiple of 14 and
+// the whole grid is resident at once, when the staged tiles fit in LDS; else four.
 template <int KIND, int PLAN>
 hipError_t launch(const KArgs &a, hipStream_t s)
 {
-    const LdsLayout L = lds_layout(a.max_words);
-    dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
-    auto kern = k_gemv_mfma<KIND, PLAN>;
-    hipError_t e = lw_allow_lds<k_gemv_mfma<KIND, PLAN>>();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, grid, dim3(256), L.total, s, a);
-    return hipGetLastError();
+    const uint32_t lds = (uint32_t)lw_device_lds_bytes();
+    if (a.n_cb > 12 && a.n_cb <= 16 && lds_layout(a.max_words, 16).total <= lds)
+        return launch_wpg<KIND, PLAN, 16>(a, s);
+    if (a.n_cb > 16 && a.n_cb % 14 == 0 && lw_resident_ramp((int64_t)a.n_rb * a.n_cb) &&
+        lds_layout(a.max_words, 14).total <= lds)
+        return launch_wpg<KIND, PLAN, 14>(a, s);
+    return launch_wpg<KIND, PLAN, WAVES>(a, s);
 }
 
 template <int KIND>
