@@ -57,6 +57,33 @@ def mlp_pass_all(gate, up, down, x, batch: int):
     return g, u, h, gemv_q_all(*down, h, batch)
 
 
+def activation_spread(down, h_bits, h_ref_bits, chunk: int = 1024) -> np.ndarray:
+    """sum_j |w_ij| |h_j - h_ref_j| for every output i of the down matrix
+    (codes, d, m) and batch row: how far apart two fp16 activation vectors
+    can move its GEMV.  With w = d*q - m per 256-weight block (fp64)."""
+    codes, d, m = down
+    hd = np.abs(np.asarray(h_bits, np.uint16).view(np.float16).astype(np.float64) -
+                np.asarray(h_ref_bits, np.uint16).view(np.float16).astype(np.float64))
+    rows = codes.shape[0]
+    out = np.zeros((hd.shape[0], rows))
+    for r0 in range(0, rows, chunk):
+        q = codes[r0:r0 + chunk].astype(np.float64)
+        ds = np.repeat(np.asarray(d[r0:r0 + chunk], np.uint16).view(np.float16).astype(np.float64), 256, axis=1)
+        ms = np.repeat(np.asarray(m[r0:r0 + chunk], np.uint16).view(np.float16).astype(np.float64), 256, axis=1)
+        out[:, r0:r0 + chunk] = hd @ np.abs(ds * q - ms).T
+    return out
+
+
+def pass_within(y, yref, spread, tol: float) -> bool:
+    """|y - yref| <= tol * max(|yref|, 0.01 rms(yref)) + spread on every
+    output: the usual bar plus what the activations' fp16 rounding
+    differences carry through the down GEMV."""
+    ref = np.asarray(yref, np.float64)
+    floor = 0.01 * np.sqrt(np.mean(ref ** 2))
+    err = np.abs(np.asarray(y, np.float64) - ref)
+    return bool(np.all(err <= tol * np.maximum(np.abs(ref), floor) + spread * (1 + 1e-9)))
+
+
 def rel_err(y, ref) -> float:
     """max |y - ref| / max(|ref|, 0.01 rms(ref)) over all outputs."""
     ref = np.asarray(ref, np.float64)

@@ -222,8 +222,9 @@ def test_full_size_mlp_pass_70b(torch, dg):
     within one fp16 ulp of the oracle's SwiGLU of the GPU's own g and u (the
     fp32 sums are within 1e-3, but a gate output near zero carries a large
     relative error into silu, so h is compared on the same inputs), and y
-    matches both the oracle's down GEMV of that h and the oracle's whole fp64
-    pass."""
+    matches the oracle's down GEMV of that h, and the oracle's whole fp64
+    pass within 1e-3 plus the down GEMV of the two passes' activation
+    differences (sum_j |w_ij| |h_j - h_ref_j|)."""
     say("full mlp pass 70b")
     from support import mlp_pass_all
     mats = [_q6_matrix(i) for i in range(3)]
@@ -240,7 +241,7 @@ def test_full_size_mlp_pass_70b(torch, dg):
     dg.lw_swiglu(g, u, h)
     dg.lw_gemv(dbs[2], h, y, 1)
     torch.cuda.synchronize()
-    gref, uref, _, yref = mlp_pass_all(mats[0][:3], mats[1][:3], mats[2][:3], x, 1)
+    gref, uref, href_bits, yref = mlp_pass_all(mats[0][:3], mats[1][:3], mats[2][:3], x, 1)
     gg, ug = g.cpu().numpy().astype(np.float64), u.cpu().numpy().astype(np.float64)
     assert rel_err(gg, gref) <= TOL and rel_err(ug, uref) <= TOL
     hr = O.swiglu(gg, ug).view(np.float16).astype(np.float64)
@@ -250,7 +251,8 @@ def test_full_size_mlp_pass_70b(torch, dg):
     assert np.all(np.abs(hg - hr) <= ulp + 1e-12)
     yv = y.cpu().numpy()
     assert rel_err(yv, gemv_q_all(*mats[2][:3], hbits, 1)) <= TOL
-    assert rel_err(yv, yref) <= TOL
+    from support import activation_spread, pass_within
+    assert pass_within(yv, yref, activation_spread(mats[2][:3], hbits, href_bits), TOL)
 
 
 # ------------------------------------------------------------------ bf16 exponent coding
