@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(KArgs a)
     // issue every load, tile offsets first; table barrier; own tile and x (as in fused_q.hip)
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
     const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, false);
-    const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
+    const uint32_t start = lw_part_start(a, c.t, c.l, c.half * a.parts);   // this lane's tile row
     uint32_t xv[BATCH][2];
     const uint32_t *xg = reinterpret_cast<const uint32_t *>(a.x) + (size_t)(c.active ? c.cb : 0) * 128;
 #pragma unroll
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(KArgs a)
     if (c.active) {
         LaneDec d;
         const bool ok = lw_lane_init(d, lds, slots, c.l, a);
-        d.advance(c.half ? split : 0u);       // the second tile row starts at the split bit
+        d.advance(start);
         if (ok) {
             struct XA {
                 u32x2 v[BATCH];
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void k_decode_bf16(KArgs a)
     const uint32_t *smrow = a.sm + (size_t)c.t * 4096 + (size_t)c.half * 64 * 32 + c.l;
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
     const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, false);
-    const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
+    const uint32_t start = lw_part_start(a, c.t, c.l, c.half * a.parts);   // this lane's tile row
     uint32_t ring[2][CHUNK];
     lw_load_sm(ring[0], smrow, 0);
     LwTileRegs64 tile;
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256) void k_decode_bf16(KArgs a)
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     LaneDec d;
     if (!lw_lane_init(d, lds, slots, c.l, a)) return;
-    d.advance(c.half ? split : 0u);
+    d.advance(start);
     // the lane's restored row segment: each chunk of 16 groups (64 weights,
     // 128 bytes) is collected in registers and written as 16-byte stores
     uint4 *orow = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.out) +
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256) void k_transcode_bf16(KArgs a)
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
     const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, !EXP);   // second table: the palette index itself
-    const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
+    const uint32_t start = lw_part_start(a, c.t, c.l, c.half * a.parts);   // this lane's tile row
     LwTileRegs64 tile;
     lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256) void k_transcode_bf16(KArgs a)
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     LaneDec d;
     if (!lw_lane_init(d, lds, slots, c.l, a)) return;
-    d.advance(c.half ? split : 0u);
+    d.advance(start);
     const int r = 2 * c.l + c.half;                                   // tile row
     uint32_t *o = static_cast<uint32_t *>(a.out) + (size_t)c.t * (EXP ? 64 : 32) * 64 + r;
     struct NoAux {};

@@ -291,7 +291,7 @@ struct Shape {
 };
 
 // Layout of a new image.  Returns the header with offsets and sizes filled.
-static lw_image_header plan_image(int kind, const Shape &sh, int64_t n_words, int64_t n_verb)
+static lw_image_header plan_image(int kind, const Shape &sh, int64_t n_words, int64_t n_verb, int parts)
 {
     lw_image_header h;
     std::memset(&h, 0, sizeof(h));
@@ -305,14 +305,15 @@ static lw_image_header plan_image(int kind, const Shape &sh, int64_t n_words, in
     h.n_rb = (int32_t)sh.n_rb;
     h.n_cb = (int32_t)sh.n_cb;
     h.spl = kind == LW_Q4_PAIR ? 256 : 512;
-    h.work_groups = (int32_t)((sh.n_cb + LW_CB_PER_WG - 1) / LW_CB_PER_WG);
+    h.parts = parts;
+    h.work_groups = lw_work_groups(sh.n_cb, parts);
     h.n_verbatim = n_verb;
     uint64_t bytes[LW_REG_COUNT] = {0};
     bytes[LW_REG_TABLE] = sizeof(lw_table);
     bytes[LW_REG_GPUTAB] = sizeof(lw_gputab);
     bytes[LW_REG_TILE_OFF] = 4u * (uint64_t)(sh.n_tiles + 1);
     bytes[LW_REG_WORDS] = 4u * (uint64_t)n_words;
-    bytes[LW_REG_SPLIT] = 2u * LW_LANES * (uint64_t)sh.n_tiles;
+    bytes[LW_REG_SPLIT] = 2u * LW_LANES * (uint64_t)sh.n_tiles * (uint64_t)(2 * parts - 1);
     if (kind == LW_BF16_EXP) {
         bytes[LW_REG_PALETTE] = 16;
         bytes[LW_REG_SM] = 4u * 4096u * (uint64_t)sh.n_tiles;
@@ -322,10 +323,9 @@ static lw_image_header plan_image(int kind, const Shape &sh, int64_t n_words, in
     } else {
         bytes[LW_REG_DM] = 4u * 64u * (uint64_t)sh.n_tiles;
     }
-    // one arrival counter per row band (kernels that combine two row bands per
-    // workgroup use the first half of them), plus slack
+    // partial sums, then one arrival counter line per row band
     bytes[LW_REG_WORK] = h.work_groups > 1
-        ? lw_work_partial_bytes(h.work_groups, sh.rows) + 4u * (uint64_t)(sh.n_rb + 64) : 0;
+        ? lw_work_partial_bytes(h.work_groups, sh.rows) + lw_work_counter_bytes(sh.n_rb) : 0;
     uint64_t pos = LW_HEADER_BYTES;
     for (int r = 0; r < LW_REG_COUNT; r++) {
         h.off[r] = bytes[r] ? pos : 0;
@@ -534,7 +534,10 @@ void lw_make_plan(const lw_table &t, int min_len, int max_len, lw_plan &a)
 }
 
 // Encode every tile of a symbol source.  sym(t, l, k) gives symbol k of lane
-// l of tile t.  Two passes: lane bit counts (for the tile sizes), then words.
+// l of tile t.  Two passes: lane bit counts (for the tile sizes), then words
+// and the part starts: with P = h->parts, lane stream l of tile t is 2P parts
+// of spl/(2P) symbols (P per tile row), and split[(t*(2P-1) + k-1)*32 + l]
+// is the bit where part k >= 1 begins.
 template <class SymFn>
 static void encode_tiles(const Shape &sh, int spl, const uint8_t *lens, const uint16_t *codes,
                          SymFn sym, std::vector<uint32_t> &tile_off, int32_t &max_words,
@@ -564,12 +567,14 @@ static void encode_tiles(const Shape &sh, int spl, const uint8_t *lens, const ui
     }
     uint32_t *words = region<uint32_t>(*img, *h, LW_REG_WORDS);
     uint16_t *split = region<uint16_t>(*img, *h, LW_REG_SPLIT);
+    const int nparts = 2 * h->parts, per = spl / nparts;
     parallel_for(sh.n_tiles, [&](int64_t t) {
         uint32_t *blk = words + tile_off[t];
         for (int l = 0; l < LW_LANES; l++) {
             LaneWriter w{blk, l};
             for (int k = 0; k < spl; k++) {
-                if (k == spl / 2) split[t * LW_LANES + l] = (uint16_t)w.bits();
+                if (k > 0 && k % per == 0)
+                    split[(t * (nparts - 1) + k / per - 1) * LW_LANES + l] = (uint16_t)w.bits();
                 int s = sym(t, l, k);
                 w.put(codes[s], lens[s]);
             }
@@ -589,6 +594,20 @@ static lw_status check_shape(int64_t rows, int64_t cols, Shape &sh)
     sh.n_rb = rows / LW_TILE_ROWS;
     sh.n_cb = cols / LW_TILE_COLS;
     sh.n_tiles = sh.n_rb * sh.n_cb;
+    return LW_OK;
+}
+
+// Parts per tile row: 0 picks the largest of 8, 4, 2, 1 that keeps the
+// matrix within LW_PART_UNITS decoding units (tiles x parts), else 1, 2, 4
+// or 8 as asked.
+static lw_status choose_parts(const Shape &sh, int &parts)
+{
+    if (parts == 0) {
+        parts = 8;
+        while (parts > 1 && sh.n_tiles * parts > LW_PART_UNITS) parts /= 2;
+        return LW_OK;
+    }
+    if (parts != 1 && parts != 2 && parts != 4 && parts != 8) return lw_fail(LW_E_ARG, "parts must be 0, 1, 2, 4 or 8");
     return LW_OK;
 }
 
@@ -623,7 +642,7 @@ static lw_status user_table(int n_alpha, const std::vector<uint64_t> &hist, cons
 }
 
 static lw_status build_q(int kind, int64_t rows, int64_t cols, const uint8_t *q, const uint16_t *d,
-                         const uint16_t *m, const uint8_t *user_lens, int code, lw_bundle **out)
+                         const uint16_t *m, const uint8_t *user_lens, int code, int parts, lw_bundle **out)
 {
     if (!out) return lw_fail(LW_E_ARG, "out is null");
     *out = nullptr;
@@ -632,6 +651,7 @@ static lw_status build_q(int kind, int64_t rows, int64_t cols, const uint8_t *q,
     Shape sh;
     lw_status st = check_shape(rows, cols, sh);
     if (st) return st;
+    if ((st = choose_parts(sh, parts))) return st;
     const int qmax = kind == LW_Q4_PAIR ? 15 : 63;
     const int n_alpha = kind == LW_Q4_PAIR ? 256 : 64;
     const int spl = kind == LW_Q4_PAIR ? 256 : 512;
@@ -679,7 +699,7 @@ static lw_status build_q(int kind, int64_t rows, int64_t cols, const uint8_t *q,
         std::vector<uint32_t> tile_off;
         int32_t max_words = 0;
         encode_tiles(sh, spl, lens, codes, sym, tile_off, max_words, nullptr, nullptr);
-        lw_image_header h = plan_image(kind, sh, tile_off[sh.n_tiles], 0);
+        lw_image_header h = plan_image(kind, sh, tile_off[sh.n_tiles], 0, parts);
         h.n_sym = n_sym;
         h.max_words = max_words;
         h.code = user_lens ? LW_CODE_LENS : code;
@@ -712,13 +732,13 @@ static lw_status build_q(int kind, int64_t rows, int64_t cols, const uint8_t *q,
 extern "C" lw_status lw_bundle_build_q(int kind, int64_t rows, int64_t cols, const uint8_t *q,
                                        const uint16_t *d, const uint16_t *m, lw_bundle **out)
 {
-    return build_q(kind, rows, cols, q, d, m, nullptr, LW_CODE_HUFFMAN, out);
+    return build_q(kind, rows, cols, q, d, m, nullptr, LW_CODE_HUFFMAN, 0, out);
 }
 
 extern "C" lw_status lw_bundle_build_q_compact(int kind, int64_t rows, int64_t cols, const uint8_t *q,
                                                const uint16_t *d, const uint16_t *m, lw_bundle **out)
 {
-    return build_q(kind, rows, cols, q, d, m, nullptr, LW_CODE_COMPACT, out);
+    return build_q(kind, rows, cols, q, d, m, nullptr, LW_CODE_COMPACT, 0, out);
 }
 
 extern "C" lw_status lw_bundle_build_q_lens(int kind, int64_t rows, int64_t cols, const uint8_t *q,
@@ -729,10 +749,30 @@ extern "C" lw_status lw_bundle_build_q_lens(int kind, int64_t rows, int64_t cols
         if (out) *out = nullptr;
         return lw_fail(LW_E_ARG, "lens is null");
     }
-    return build_q(kind, rows, cols, q, d, m, lens, LW_CODE_LENS, out);
+    return build_q(kind, rows, cols, q, d, m, lens, LW_CODE_LENS, 0, out);
 }
 
-static lw_status build_bf16(int64_t rows, int64_t cols, const uint16_t *w, int code, lw_bundle **out)
+// Options: the code (lens for LW_CODE_LENS) and the parts per tile row.
+static lw_status check_opts(const lw_build_opts *o, lw_bundle **out)
+{
+    if (out) *out = nullptr;
+    if (!o) return lw_fail(LW_E_ARG, "opts is null");
+    if (o->code < LW_CODE_HUFFMAN || o->code > LW_CODE_LENS) return lw_fail(LW_E_ARG, "unknown code kind");
+    if (o->code == LW_CODE_LENS && !o->lens) return lw_fail(LW_E_ARG, "lens is null");
+    return LW_OK;
+}
+
+extern "C" lw_status lw_bundle_build_q_opts(int kind, int64_t rows, int64_t cols, const uint8_t *q,
+                                            const uint16_t *d, const uint16_t *m, const lw_build_opts *opts,
+                                            lw_bundle **out)
+{
+    lw_status st = check_opts(opts, out);
+    if (st) return st;
+    return build_q(kind, rows, cols, q, d, m, opts->code == LW_CODE_LENS ? opts->lens : nullptr, opts->code,
+                   opts->parts, out);
+}
+
+static lw_status build_bf16(int64_t rows, int64_t cols, const uint16_t *w, int code, int parts, lw_bundle **out)
 {
     if (!out) return lw_fail(LW_E_ARG, "out is null");
     *out = nullptr;
@@ -740,6 +780,7 @@ static lw_status build_bf16(int64_t rows, int64_t cols, const uint16_t *w, int c
     Shape sh;
     lw_status st = check_shape(rows, cols, sh);
     if (st) return st;
+    if ((st = choose_parts(sh, parts))) return st;
     try {
         // exponent histogram -> palette: top 16 by (count desc, exponent asc)
         std::vector<std::vector<uint64_t>> part(sh.n_rb, std::vector<uint64_t>(256, 0));
@@ -818,7 +859,7 @@ static lw_status build_bf16(int64_t rows, int64_t cols, const uint16_t *w, int c
         std::vector<uint32_t> tile_off;
         int32_t max_words = 0;
         encode_tiles(sh, 512, lens, codes, sym, tile_off, max_words, nullptr, nullptr);
-        lw_image_header h = plan_image(LW_BF16_EXP, sh, tile_off[sh.n_tiles], n_verb);
+        lw_image_header h = plan_image(LW_BF16_EXP, sh, tile_off[sh.n_tiles], n_verb, parts);
         h.n_sym = n_sym;
         h.max_words = max_words;
         h.n_pal = n_pal;
@@ -871,12 +912,24 @@ static lw_status build_bf16(int64_t rows, int64_t cols, const uint16_t *w, int c
 
 extern "C" lw_status lw_bundle_build_bf16(int64_t rows, int64_t cols, const uint16_t *w, lw_bundle **out)
 {
-    return build_bf16(rows, cols, w, LW_CODE_HUFFMAN, out);
+    return build_bf16(rows, cols, w, LW_CODE_HUFFMAN, 0, out);
 }
 
 extern "C" lw_status lw_bundle_build_bf16_compact(int64_t rows, int64_t cols, const uint16_t *w, lw_bundle **out)
 {
-    return build_bf16(rows, cols, w, LW_CODE_COMPACT, out);
+    return build_bf16(rows, cols, w, LW_CODE_COMPACT, 0, out);
+}
+
+extern "C" lw_status lw_bundle_build_bf16_opts(int64_t rows, int64_t cols, const uint16_t *w,
+                                               const lw_build_opts *opts, lw_bundle **out)
+{
+    if (opts && opts->code == LW_CODE_LENS) {
+        if (out) *out = nullptr;
+        return lw_fail(LW_E_UNSUPPORTED, "bf16 bundles take the Huffman or compact code");
+    }
+    lw_status st = check_opts(opts, out);
+    if (st) return st;
+    return build_bf16(rows, cols, w, opts->code, opts->parts, out);
 }
 
 // ----------------------------------------------------------------- validate
@@ -928,7 +981,9 @@ static lw_status validate_image(const uint8_t *img, size_t bytes)
     if (h.bytes[LW_REG_TABLE] != sizeof(lw_table) || h.bytes[LW_REG_GPUTAB] != sizeof(lw_gputab))
         return lw_fail(LW_E_FORMAT, "table region size");
     if (h.bytes[LW_REG_TILE_OFF] != 4u * (uint64_t)(h.n_tiles + 1)) return lw_fail(LW_E_FORMAT, "tile_off size");
-    if (h.bytes[LW_REG_SPLIT] != 2u * LW_LANES * (uint64_t)h.n_tiles) return lw_fail(LW_E_FORMAT, "split size");
+    if (h.parts != 1 && h.parts != 2 && h.parts != 4 && h.parts != 8) return lw_fail(LW_E_FORMAT, "bad parts per row");
+    if (h.bytes[LW_REG_SPLIT] != 2u * LW_LANES * (uint64_t)h.n_tiles * (uint64_t)(2 * h.parts - 1))
+        return lw_fail(LW_E_FORMAT, "split size");
     if (h.kind != LW_BF16_EXP && h.bytes[LW_REG_DM] != 256u * (uint64_t)h.n_tiles)
         return lw_fail(LW_E_FORMAT, "dm size");
     if (h.kind == LW_BF16_EXP &&
@@ -983,14 +1038,23 @@ static lw_status validate_image(const uint8_t *img, size_t bytes)
         wmax = std::max<int32_t>(wmax, (int32_t)((to[i + 1] - to[i]) / 32));
     }
     if ((uint64_t)to[h.n_tiles] * 4u != h.bytes[LW_REG_WORDS]) return lw_fail(LW_E_FORMAT, "words size");
-    // a lane's second tile row starts inside its stream, after at least one bit per symbol of the first
+    // each part of a lane stream starts inside the stream, 1 to 11 bits per
+    // symbol after the start of the part before it
     const uint16_t *sp = reinterpret_cast<const uint16_t *>(img + h.off[LW_REG_SPLIT]);
-    for (int64_t i = 0; i < h.n_tiles; i++)
+    const int nparts = 2 * h.parts;
+    const uint32_t per = (uint32_t)(h.spl / nparts);
+    for (int64_t i = 0; i < h.n_tiles; i++) {
+        const uint32_t lane_words = (to[i + 1] - to[i]) / 32u;
         for (int l = 0; l < LW_LANES; l++) {
-            const uint32_t v = sp[i * LW_LANES + l];
-            if (v < (uint32_t)h.spl / 2 || v > 32u * ((to[i + 1] - to[i]) / 32u) || v > (uint32_t)(h.spl / 2) * LW_MAXLEN)
-                return lw_fail(LW_E_FORMAT, "split outside the lane stream");
+            uint32_t prev = 0;
+            for (int k = 1; k < nparts; k++) {
+                const uint32_t v = sp[(i * (nparts - 1) + k - 1) * LW_LANES + l];
+                if (v < prev + per || v > prev + per * LW_MAXLEN || v > 32u * lane_words)
+                    return lw_fail(LW_E_FORMAT, "part start outside the lane stream");
+                prev = v;
+            }
         }
+    }
     if (wmax != h.max_words) return lw_fail(LW_E_FORMAT, "max_words mismatch");
     // a lane can hold at most symbols_per_lane codes of 11 bits
     if ((int64_t)wmax * 32 > (int64_t)h.spl * LW_MAXLEN + 31) return lw_fail(LW_E_FORMAT, "tile longer than possible");
@@ -1006,9 +1070,9 @@ static lw_status validate_image(const uint8_t *img, size_t bytes)
         if ((int64_t)vs[h.n_tiles] != h.n_verbatim) return lw_fail(LW_E_FORMAT, "verbatim count");
         if (h.n_pal < 1 || h.n_pal > 16 || nsym > h.n_pal) return lw_fail(LW_E_FORMAT, "palette size");
     }
-    int32_t groups = (int32_t)((h.n_cb + LW_CB_PER_WG - 1) / LW_CB_PER_WG);
+    const int32_t groups = lw_work_groups(h.n_cb, h.parts);
     if (h.work_groups != groups) return lw_fail(LW_E_FORMAT, "workspace groups");
-    if (groups > 1 && h.bytes[LW_REG_WORK] < lw_work_partial_bytes(groups, h.rows) + 4u * (uint64_t)h.n_rb)
+    if (groups > 1 && h.bytes[LW_REG_WORK] < lw_work_partial_bytes(groups, h.rows) + lw_work_counter_bytes(h.n_rb))
         return lw_fail(LW_E_FORMAT, "workspace too small");
     return LW_OK;
 }
@@ -1058,6 +1122,7 @@ extern "C" lw_status lw_bundle_get_info(const lw_bundle *b, lw_bundle_info *info
     info->min_len = h.min_len;
     info->max_len = h.max_len;
     info->max_words = h.max_words;
+    info->parts = h.parts;
     info->n_palette = h.n_pal;
     info->n_verbatim = h.n_verbatim;
     const lw_table *t = reinterpret_cast<const lw_table *>(b->image.data() + h.off[LW_REG_TABLE]);

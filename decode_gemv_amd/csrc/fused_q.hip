@@ -2,20 +2,27 @@
 // decode-only kernels for 4-bit pair and 6-bit single codes, gfx950.
 //
 // Work split ("LazyWeights", section "2 . Code them": a 64x256 tile is 32
-// lanes of two rows): one wavefront per tile.  Lane l < 32 decodes lane
-// stream l from its first bit (tile row 2l); lane l + 32 decodes the same
-// stream from its split bit (tile row 2l+1, where the bundle records that it
-// starts).  So every lane runs one serial chain of 128 (Q4) or 256 (Q6)
-// symbols, there are twice as many wavefronts to hide each other's latency,
-// and all 64 lanes consume the same activation pair at each step (x is read
-// once per wavefront from LDS).  A workgroup of four wavefronts (sixteen,
-// whole rows, when a row band has 13 to 16 column blocks) covers that many
-// consecutive column blocks of one row band; workgroups of different column
-// groups are combined by a fixed-order reduction through the bundle's
-// workspace (the last workgroup to arrive sums the partials in group order),
-// so the result is deterministic.  When the whole grid is resident at once,
-// each wavefront lowers its issue priority as its decode progresses, so the
-// wavefronts sharing a SIMD finish together.
+// lanes of two rows; Fig. 3 caption: recorded offsets let a decoder start
+// without the rest).  The bundle records where each of P parts of a tile row
+// starts in its lane stream (P = 1, 2, 4 or 8, chosen when the bundle is
+// built), and one wavefront decodes one part of a tile: lane l < 32 decodes
+// lane stream l's part in tile row 2l, lane l + 32 the same part of row
+// 2l+1.  So every lane runs one serial chain of 128/P (Q4) or 256/P (Q6)
+// symbols, and all 64 lanes consume the same activation pair at each step
+// (x is read once per wavefront from LDS).  The parts of one tile share its
+// staged words.  More parts shorten the chains of small matrices and spread
+// a large one evenly over the SIMDs (3584 tiles in two parts are seven
+// wavefronts on every SIMD of 256 CUs, where whole rows leave some SIMDs four
+// and others three or none).
+// A workgroup holds whole column blocks of one row band: in parts, eight
+// wavefronts (four tiles in two parts, two in four, one in eight); in whole
+// rows, sixteen (a whole row band of 13 to 16 column blocks, when there are
+// enough row bands to fill the chip), fourteen or four.  Workgroups of
+// different column groups are combined by a fixed-order reduction through
+// the bundle's workspace (the last workgroup to arrive sums the partials in
+// group order), so the result is deterministic.  When the whole grid is resident at once, each wavefront
+// lowers its issue priority as its decode progresses, so the wavefronts
+// sharing a SIMD finish together.
 //
 // Dequantisation w = d*q - m per 256-weight super-block (one tile row) is
 // applied after the dot product: y = d * sum(q x) - m * sum(x).
@@ -31,26 +38,29 @@ struct LdsLayout {
     uint32_t x, tiles, flag, total;
 };
 
-__host__ __device__ inline LdsLayout lds_layout(int batch, int max_words, bool decode_only, int waves = WAVES)
+// staged tiles: one per `parts` wavefronts
+__host__ __device__ inline LdsLayout lds_layout(int batch, int max_words, bool decode_only, int waves = WAVES,
+                                                int parts = 1)
 {
     LdsLayout L;
     L.x = LW_TAB_BYTES;
     const uint32_t xbytes = decode_only ? 0u : (uint32_t)(waves * batch * 128 * 4);
     L.tiles = L.x + xbytes;
-    const uint32_t tiles = (uint32_t)(waves * (max_words + 3) * 128);
+    const uint32_t tiles = (uint32_t)((waves / parts) * (max_words + 3) * 128);
     const uint32_t red = (uint32_t)(waves * batch * 64 * 4);
     L.flag = L.tiles + (tiles > red ? tiles : red);
     L.total = L.flag + 16;
     return L;
 }
 
-// Identity of a lane within the grid.
+// Identity of a lane within the grid: wavefront w of a workgroup decodes
+// part p = w % parts of the tile in its slot ts = w / parts.
 struct LaneCtx {
-    int wave, lane, half, l, g, cb, rb, t;
+    int wave, lane, half, l, g, cb, rb, t, ts, p;
     bool active;
 };
 
-LW_DEV LaneCtx lane_ctx(const KArgs &a, int waves = WAVES)
+LW_DEV LaneCtx lane_ctx(const KArgs &a, int waves = WAVES, int parts = 1)
 {
     LaneCtx c;
     c.wave = (int)lw_wave_id();
@@ -59,25 +69,29 @@ LW_DEV LaneCtx lane_ctx(const KArgs &a, int waves = WAVES)
     c.l = c.lane & 31;                    // lane stream of the tile
     c.g = blockIdx.x;
     c.rb = blockIdx.y;
-    c.cb = c.g * waves + c.wave;
+    c.ts = c.wave / parts;
+    c.p = c.wave % parts;
+    c.cb = c.g * (waves / parts) + c.ts;
     c.active = c.cb < a.n_cb;
     c.t = c.rb * a.n_cb + (c.active ? c.cb : 0);
     return c;
 }
 
-// WPG wavefronts per workgroup cover WPG consecutive column blocks of one row
-// band; with WPG >= K/256 a workgroup holds whole rows and the reduction
-// stays in LDS.
-template <int KIND, int PLAN, int BATCH, int WPG>
+// WPG wavefronts per workgroup decode P parts of WPG/P consecutive column
+// blocks of one row band; when they cover whole rows the reduction stays in
+// LDS.
+template <int KIND, int PLAN, int BATCH, int WPG, int P>
 __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    static_assert(WPG % P == 0, "whole tiles per workgroup");
     constexpr int SPL = KIND == LW_Q4_PAIR ? 256 : 512;
-    const LdsLayout L = lds_layout(BATCH, a.max_words, false, WPG);
-    const LaneCtx c = lane_ctx(a, WPG);
+    constexpr int NG = SPL / 8 / P;       // groups of four symbols per part of a tile row
+    const LdsLayout L = lds_layout(BATCH, a.max_words, false, WPG, P);
+    const LaneCtx c = lane_ctx(a, WPG, P);
     const int S = a.max_words + 3;
     const uint32_t xs_addr = (uint32_t)(size_t)(lds + L.x) + 4u * (uint32_t)(c.wave * BATCH * 128);
-    uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
+    uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.ts * S * 32;
 
     // Issue every global load first (unconditionally: an inactive wavefront
     // reads tile 0 and drops it), tile offsets first since the tile words
@@ -88,7 +102,8 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
     const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, false);
     const uint32_t dm = a.dm[(size_t)c.t * 64 + 2 * c.l + c.half];   // (d, m) of this lane's tile row
-    const uint32_t split = a.split[(size_t)c.t * 32 + c.l];          // second-row start
+    // this lane's part: bundle part half * parts + p * (parts / P)
+    const uint32_t start = lw_part_start(a, c.t, c.l, c.half * a.parts + c.p * (a.parts / P));
     uint32_t xv[BATCH][2];
     const uint32_t *xg = reinterpret_cast<const uint32_t *>(a.x) + (size_t)(c.active ? c.cb : 0) * 128;
 #pragma unroll
@@ -102,17 +117,28 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
     // is requested at once) reaches the barrier late and stalls all of
     // them, about 5 % on a 16-block row band; with four wavefronts the
     // order makes no difference.
+    // In parts, the tile's first wavefront stages it for all of them, and
+    // one barrier then covers the table and the tiles.
     LwTileRegs64 tile;
-    if constexpr (WPG <= WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
-    __syncthreads();                      // the decoder table is complete
-    if constexpr (WPG > WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
+    if constexpr (P > 1) {
+        if (c.p == 0) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
+        lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
+        if (c.p == 0) lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
+    } else {
+        if constexpr (WPG <= WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
+        lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
+        __syncthreads();                  // the decoder table is complete
+        if constexpr (WPG > WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
+    }
 #pragma unroll
     for (int b = 0; b < BATCH; b++) {
         *(lw_lds_w32 *)(size_t)(xs_addr + 4u * (b * 128 + c.lane)) = xv[b][0];
         *(lw_lds_w32 *)(size_t)(xs_addr + 4u * (b * 128 + c.lane + 64)) = xv[b][1];
     }
-    lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
+    if constexpr (P > 1)
+        __syncthreads();                  // the table and every tile of the workgroup are complete
+    else
+        lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
 
     float acc[BATCH];
 #pragma unroll
@@ -121,8 +147,8 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
     if (c.active) {
         LaneDec d;
         const bool ok = lw_lane_init(d, lds, slots, c.l, a);
-        d.advance(c.half ? split : 0u);       // the second tile row starts at the split bit
-        constexpr int NG = SPL / 8;       // groups of four symbols per tile row
+        d.advance(start);
+        const int g0 = c.p * NG;          // first group of this part within the tile row
         if (ok) {
             // activations of one group: Q4 four pairs, Q6 two pairs (four columns) per batch row
             typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -136,10 +162,10 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
 #pragma unroll
                 for (int b = 0; b < BATCH; b++) {
                     if constexpr (KIND == LW_Q4_PAIR) {
-                        const uint32_t ad = xs_addr + (uint32_t)(b * 512 + 16 * g);
+                        const uint32_t ad = xs_addr + (uint32_t)(b * 512 + 16 * (g0 + g));
                         r.v[b] = *(__attribute__((address_space(3))) const u32x4 *)(size_t)ad;
                     } else {
-                        const uint32_t ad = xs_addr + (uint32_t)(b * 512 + 8 * g);
+                        const uint32_t ad = xs_addr + (uint32_t)(b * 512 + 8 * (g0 + g));
                         const u32x2 t = *(__attribute__((address_space(3))) const u32x2 *)(size_t)ad;
                         r.v[b] = u32x4{t.x, t.y, 0u, 0u};
                     }
@@ -168,13 +194,15 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
         }
     }
 
-    // dequantise: y_row = d * sum(q x) - m * sum(x) for this tile row (the
-    // column block's activation sum is taken here, off the decode's start)
+    // dequantise: y_row = d * sum(q x) - m * sum(x) over this part's columns
+    // of the tile row (the activation sum is taken here, off the decode's
+    // start; lane i holds the column pairs i and i + 64)
+    const bool in0 = c.lane / (128 / P) == c.p, in1 = (c.lane + 64) / (128 / P) == c.p;
     float sx[BATCH];
 #pragma unroll
     for (int b = 0; b < BATCH; b++)
-        sx[b] = lw_wave_sum(lw_half_lo(xv[b][0]) + lw_half_hi(xv[b][0]) + lw_half_lo(xv[b][1]) +
-                            lw_half_hi(xv[b][1]));
+        sx[b] = lw_wave_sum((in0 ? lw_half_lo(xv[b][0]) + lw_half_hi(xv[b][0]) : 0.f) +
+                            (in1 ? lw_half_lo(xv[b][1]) + lw_half_hi(xv[b][1]) : 0.f));
     float val[BATCH];
 #pragma unroll
     for (int b = 0; b < BATCH; b++) val[b] = c.active ? lw_half_lo(dm) * acc[b] - lw_half_hi(dm) * sx[b] : 0.f;
@@ -203,7 +231,7 @@ __global__ __launch_bounds__(256) void k_decode_q(KArgs a)
     // issue, then store (as in k_gemv_q)
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
     const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, true);
-    const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
+    const uint32_t start = lw_part_start(a, c.t, c.l, c.half * a.parts);   // this lane's tile row
     LwTileRegs64 tile;
     lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
@@ -212,7 +240,7 @@ __global__ __launch_bounds__(256) void k_decode_q(KArgs a)
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     LaneDec d;
     if (!lw_lane_init(d, lds, slots, c.l, a)) return;
-    d.advance(c.half ? split : 0u);
+    d.advance(start);
     const int64_t row_bytes = KIND == LW_Q4_PAIR ? a.cols / 2 : a.cols;
     constexpr int NG = SPL / 8;           // groups of four symbols per tile row
     // The lane's restored row segment (4 bytes per group) is collected in
@@ -246,33 +274,45 @@ __global__ __launch_bounds__(256) void k_decode_q(KArgs a)
     if (a.lane_bits && c.half) a.lane_bits[(size_t)c.t * 32 + c.l] = d.bitpos();
 }
 
-template <int KIND, int PLAN, int BATCH, int WPG>
+template <int KIND, int PLAN, int BATCH, int WPG, int P = 1>
 hipError_t launch_gemv_wpg(const KArgs &a0, hipStream_t s)
 {
     KArgs a = a0;
-    a.groups = (a.n_cb + WPG - 1) / WPG;  // column groups combined through the workspace (none if 1)
-    a.ramp = lw_resident_ramp((int64_t)a.n_rb * a.n_cb);
-    const LdsLayout L = lds_layout(BATCH, a.max_words, false, WPG);
+    constexpr int TPW = WPG / P;          // column blocks per workgroup
+    a.groups = (a.n_cb + TPW - 1) / TPW;  // column groups combined through the workspace (none if 1)
+    if (a.groups > 1 && a.groups > lw_work_groups(a.n_cb, a.parts)) return hipErrorInvalidValue;
+    a.ramp = lw_resident_ramp((int64_t)a.n_rb * a.n_cb * P);
+    const LdsLayout L = lds_layout(BATCH, a.max_words, false, WPG, P);
     dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
-    auto kern = k_gemv_q<KIND, PLAN, BATCH, WPG>;
-    hipError_t e = lw_allow_lds<k_gemv_q<KIND, PLAN, BATCH, WPG>>();
+    auto kern = k_gemv_q<KIND, PLAN, BATCH, WPG, P>;
+    hipError_t e = lw_allow_lds<k_gemv_q<KIND, PLAN, BATCH, WPG, P>>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, grid, dim3(64 * WPG), L.total, s, a);
     return hipGetLastError();
 }
 
-// Whole rows per workgroup (16 wavefronts, no cross-workgroup reduction) when
-// a row band has 13..16 column blocks and the tiles fit in LDS; 14 wavefronts
-// (a few column groups, every wavefront active) when the column blocks are a
-// multiple of 14 (K = 14336 and 28672; plans of at most eight comparisons) and the whole grid is
+// Bundles in parts (matrices of up to 2048 tiles) decode every recorded part
+// in eight-wavefront workgroups (measured best at 16 to 2048 tiles).  In whole
+// rows: 16 wavefronts, no cross-workgroup reduction, when a row band has
+// 13..16 column blocks, the tiles fit in LDS and there are at least 128 row
+// bands (fewer leave most CUs idle: 1024x4096 takes 16.1 us so, 9.9 us in
+// four-wavefront groups); 14 wavefronts (a few column groups, every
+// wavefront active) when the column blocks are a multiple of 14 (K = 14336
+// and 28672; plans of at most eight comparisons) and the whole grid is
 // resident at once (with several generations, workgroups this large free
 // their CU only all together: 8 % slower on 8192x28672); else four.
 template <int KIND, int PLAN, int BATCH>
 hipError_t launch_gemv_q(const KArgs &a, hipStream_t s)
 {
+    const uint32_t lds = (uint32_t)lw_device_lds_bytes();
+    if (a.parts == 2 && lds_layout(BATCH, a.max_words, false, 8, 2).total <= lds)
+        return launch_gemv_wpg<KIND, PLAN, BATCH, 8, 2>(a, s);
+    if (a.parts == 4 && lds_layout(BATCH, a.max_words, false, 8, 4).total <= lds)
+        return launch_gemv_wpg<KIND, PLAN, BATCH, 8, 4>(a, s);
+    if (a.parts == 8 && lds_layout(BATCH, a.max_words, false, 8, 8).total <= lds)
+        return launch_gemv_wpg<KIND, PLAN, BATCH, 8, 8>(a, s);
     if constexpr (BATCH <= 4) {
-        const uint32_t lds = (uint32_t)lw_device_lds_bytes();
-        if (a.n_cb > 12 && a.n_cb <= 16 && lds_layout(BATCH, a.max_words, false, 16).total <= lds)
+        if (a.n_cb > 12 && a.n_cb <= 16 && a.n_rb >= 128 && lds_layout(BATCH, a.max_words, false, 16).total <= lds)
             return launch_gemv_wpg<KIND, PLAN, BATCH, 16>(a, s);
         if constexpr (PLAN != LW_P_GEN) {
             if (a.n_cb > 16 && a.n_cb % 14 == 0 && lw_resident_ramp((int64_t)a.n_rb * a.n_cb) &&

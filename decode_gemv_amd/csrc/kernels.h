@@ -15,7 +15,7 @@
 struct KArgs {
     const uint32_t *words;       // interleaved lane words
     const uint32_t *tile_off;    // [n_tiles+1]
-    const uint16_t *split;       // [n_tiles][32] first bit of each lane's second tile row
+    const uint16_t *split;       // [n_tiles][2*parts-1][32] first bit of each part of a lane stream
     const uint32_t *dm;          // [n_tiles][64] d | m << 16 (Q4/Q6)
     const lw_gputab *tab;        // derived tables
     const uint32_t *sm;          // bf16 sign+mantissa words
@@ -31,6 +31,7 @@ struct KArgs {
     int32_t *vrank;              // bf16 transcode: verbatim store index of each (tile, segment, row), or -1
     int64_t rows, cols;
     int32_t n_rb, n_cb, groups, batch, max_words, min_len, max_len;
+    int32_t parts;               // parts per tile row with a recorded start (1, 2, 4 or 8)
     uint32_t pal0;               // bf16: exponent of palette index 0
     // Limit comparison by sums of absolute differences (see lane_decode.hpp).
     // c8[j], c8m1[j]: the byte thresholds of SAD pair j (t and t - 1 per

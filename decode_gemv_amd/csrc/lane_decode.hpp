@@ -516,6 +516,17 @@ LW_DEV void lw_ramp(int on, int g)
     if (g == 3 * NG / 4) lw_progress_priority<0>(on);
 }
 
+// Bit of lane stream l of tile t where bundle part k begins (0 <= k <
+// 2 * a.parts; parts 0 .. a.parts-1 cover the first tile row, the rest the
+// second; part 0 begins at bit 0).  The load is unconditional (index
+// clamped), so it can be issued with the kernel's other prologue loads.
+LW_DEV uint32_t lw_part_start(const KArgs &a, int64_t t, int l, int k)
+{
+    const size_t np1 = (size_t)(2 * a.parts - 1);
+    const uint32_t v = a.split[((size_t)t * np1 + (size_t)(k > 0 ? k - 1 : 0)) * 32 + (size_t)l];
+    return k > 0 ? v : 0u;
+}
+
 // Set up a lane's decoder on its staged tile.  Returns false (the kernel must
 // then produce nothing) unless the LDS base is 256-byte aligned (the shift
 // amounts s = A >> 1 then carry a bias lb/2 + PBASE/2 that is a multiple of
@@ -546,11 +557,17 @@ LW_DEV bool lw_lane_init(LaneDec &d, uint8_t *lds, const uint32_t *slots, int l,
 // RS floats between consecutive (wave, b) runs) and either write y (one
 // column group) or take part in the split-column reduction.  The partials
 // travel through the bundle's workspace as device-scope atomic exchanges,
-// which are performed at the coherence point
-// of all XCDs without an L2 writeback; each workgroup then bumps the arrival
-// counter of its rows (index ctr), and the last one to arrive reads the
-// partials back with device-scope atomic loads and adds them in group order
-// (deterministic), then re-arms the counter for the next call.
+// which are performed at the coherence point of all XCDs without an L2
+// writeback; each workgroup then bumps the arrival counter of its rows
+// (index ctr), and the last one to arrive reads the partials back with
+// device-scope atomic loads, then re-arms the counter for the next call.
+// The last arrival's loads are all in flight at once -- T consecutive
+// threads per output (T a power of two, at most 8, as the workgroup's
+// threads allow), each loading only its own groups (every T-th, summed in
+// group order), the T sums then combined by a butterfly -- so the reduction
+// costs three round trips to the coherence point (publish, count, gather)
+// however many groups there are.  The order of the additions is fixed by the group count and the
+// workgroup size alone, so the result is deterministic.
 template <int BATCH, int ROWS = 128, int RS = ROWS>
 LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g, int ctr, int waves,
                            uint32_t *last_flag)
@@ -571,33 +588,41 @@ LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's exchanges are performed
     __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&a.count[ctr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t old = __hip_atomic_fetch_add(&a.count[(size_t)ctr * LW_COUNTER_STRIDE], 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
         *last_flag = (old == (uint32_t)a.groups - 1u) ? 1u : 0u;
     }
     __syncthreads();
     if (!*last_flag) return;
-    for (int i = threadIdx.x; i < BATCH * ROWS; i += blockDim.x) {
+    // T threads per output (consecutive lanes of one wavefront)
+    const int per = (int)blockDim.x / (BATCH * ROWS);
+    const int T = per >= 8 ? 8 : per >= 4 ? 4 : per >= 2 ? 2 : 1;
+    const int q = threadIdx.x % T;
+    const size_t gstride = (size_t)LW_BATCH_MAX * a.rows;
+    for (int i = threadIdx.x / T; i < BATCH * ROWS; i += blockDim.x / T) {
         const int b = i / ROWS, row = i % ROWS;
-        if (b >= a.batch) break;
-        if (row0 + row >= a.rows) continue;
-        // eight groups' partials are requested together (clamped indices, so
-        // every load is unconditional) and then added in group order
-        const float *pp = &a.part[(size_t)b * a.rows + row0 + row];
-        const size_t gstride = (size_t)LW_BATCH_MAX * a.rows;
+        const bool ok = b < a.batch && row0 + row < a.rows;
+        const float *pp = &a.part[(size_t)(ok ? b : 0) * a.rows + (ok ? row0 + row : 0)];
+        const int ng = ok ? a.groups : 0;
         float v = 0.f;
-        for (int g0 = 0; g0 < a.groups; g0 += 8) {
-            float t[8];
+        for (int g0 = q; g0 < ng; g0 += 16 * T) {
+            // only the loads this thread needs: a load per group, all in flight together
+            float t[16];
 #pragma unroll
-            for (int k = 0; k < 8; k++)
-                t[k] = __hip_atomic_load(pp + (size_t)min(g0 + k, a.groups - 1) * gstride, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
+            for (int k = 0; k < 16; k++)
+                t[k] = g0 + k * T < ng ? __hip_atomic_load(pp + (size_t)(g0 + k * T) * gstride, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT)
+                                       : 0.f;
 #pragma unroll
-            for (int k = 0; k < 8; k++)
-                if (g0 + k < a.groups) v += t[k];
+            for (int k = 0; k < 16; k++)
+                if (g0 + k * T < ng) v += t[k];
         }
-        a.y[(size_t)b * a.rows + row0 + row] = v;
+        // the T sums of this output, in the same butterfly order in every lane
+        for (int o = 1; o < T; o <<= 1) v += __shfl_xor(v, o, 64);
+        if (ok && q == 0) a.y[(size_t)b * a.rows + row0 + row] = v;
     }
-    if (threadIdx.x == 0) __hip_atomic_store(&a.count[ctr], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&a.count[(size_t)ctr * LW_COUNTER_STRIDE], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 #endif

@@ -14,7 +14,7 @@
 #include "lw.h"
 
 #define LW_MAGIC 0x3142574Cu       /* "LWB1" */
-#define LW_VERSION 2u
+#define LW_VERSION 3u
 #define LW_MAXLEN 11               /* "LazyWeights", 2 . Code them: 11-bit codes */
 #define LW_TILE_ROWS 64            /* a 64x256 tile is 32 lanes of two rows */
 #define LW_TILE_COLS 256
@@ -23,7 +23,14 @@
 #define LW_HEADER_BYTES 512
 #define LW_BATCH_MAX 16             /* largest batch of the fused kernels */
 #define LW_GEMM_BATCH_MAX 65536     /* largest batch of lw_gemm */
-#define LW_CB_PER_WG 4             /* column blocks one workgroup covers (one per wave) */
+#define LW_CB_PER_WG 4             /* decoding units (wavefronts) of the smallest workgroup */
+/* Decoding units (tiles x parts per tile row) the default part count stays
+ * within: four wavefronts on each of the 1024 SIMDs of 256 compute units.
+ * Measured on MI355X at batch 1, matrices of 16 to 2048 tiles run fastest
+ * with the most parts that keep tiles x parts <= 4096 (e.g. 1024x4096: 6.2 us
+ * in eight parts against 16.1 us in whole rows); from about 3584 tiles whole
+ * rows in one part are as fast or faster, and need no extra starts. */
+#define LW_PART_UNITS 4096
 
 typedef struct {
     uint32_t magic;
@@ -48,6 +55,8 @@ typedef struct {
     uint64_t twin_bytes;
     uint64_t off[LW_REG_COUNT];
     uint64_t bytes[LW_REG_COUNT];
+    int32_t parts;                 /* parts per tile row whose starts LW_REG_SPLIT holds: 1, 2, 4 or 8 */
+    int32_t reserved;
 } lw_image_header;
 
 /* LW_REG_TABLE: the canonical decoder table of the matrix. */
@@ -112,11 +121,25 @@ void lw_make_plan(const lw_table &t, int min_len, int max_len, lw_plan &p);
 
 static inline uint64_t lw_align_up(uint64_t v) { return (v + LW_ALIGN - 1) & ~(uint64_t)(LW_ALIGN - 1); }
 
+/* Column groups the workspace holds partials for: a row band's tiles x parts
+ * over the smallest workgroup (every launch combines at most this many). */
+static inline int32_t lw_work_groups(int64_t n_cb, int32_t parts)
+{
+    return (int32_t)((n_cb * parts + LW_CB_PER_WG - 1) / LW_CB_PER_WG);
+}
+
 /* workspace layout: partial sums [work_groups][LW_BATCH_MAX][rows] f32, then
- * one u32 arrival counter per row band (rows / 64) */
+ * one u32 arrival counter per row band (rows / 64), each on its own 256-byte
+ * line (LW_COUNTER_STRIDE u32 apart), so that the read-modify-writes of
+ * different row bands never queue on one line */
+#define LW_COUNTER_STRIDE 64
 static inline uint64_t lw_work_partial_bytes(int32_t groups, int64_t rows)
 {
     return (uint64_t)groups * LW_BATCH_MAX * (uint64_t)rows * 4u;
+}
+static inline uint64_t lw_work_counter_bytes(int64_t n_rb)
+{
+    return (uint64_t)n_rb * LW_COUNTER_STRIDE * 4u;
 }
 
 #endif

@@ -129,7 +129,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_mfma(KArgs a)
     // issue every load, tile offsets first; table barrier; own tile (as in fused_q.hip)
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
     const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, false);
-    const uint32_t split = a.split[(size_t)c.t * 32 + c.l];
+    const uint32_t start = lw_part_start(a, c.t, c.l, c.half * a.parts);   // this lane's tile row
     LwTileRegs64 tile;
     if constexpr (WPG <= WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_mfma(KArgs a)
     if (c.active) {
         LaneDec d;
         const bool ok = lw_lane_init(d, lds, slots, c.l, a);
-        d.advance(c.half ? split : 0u);       // the second tile row starts at the split bit
+        d.advance(start);
         if (ok) {
             u32x2 xcur = load_x(0);
             uint32_t gw[4];                   // the current group's 16-bit weights, two per word

@@ -104,6 +104,7 @@ static KArgs make_args(const lw_dev_bundle *db)
     a.n_cb = db->h.n_cb;
     a.groups = db->h.work_groups;
     a.max_words = db->h.max_words;
+    a.parts = db->h.parts;
     a.min_len = db->h.min_len;
     a.max_len = db->h.max_len;
     return a;

@@ -42,7 +42,11 @@ class lw_bundle_info(C.Structure):
                 ("n_verbatim", C.c_int64), ("count_per_len", C.c_uint16 * 12),
                 ("region_offset", C.c_uint64 * LW_REG_COUNT), ("region_bytes", C.c_uint64 * LW_REG_COUNT),
                 ("image_bytes", C.c_uint64), ("coded_bytes", C.c_uint64), ("twin_bytes", C.c_uint64),
-                ("code", C.c_int32), ("reserved", C.c_int32)]
+                ("code", C.c_int32), ("parts", C.c_int32)]
+
+
+class lw_build_opts(C.Structure):
+    _fields_ = [("code", C.c_int32), ("parts", C.c_int32), ("lens", C.c_void_p)]
 
 
 def _load():
@@ -58,6 +62,8 @@ def _load():
         "lw_bundle_build_q": (st, [i32, i64, i64, P, P, P, C.POINTER(P)]),
         "lw_bundle_build_q_compact": (st, [i32, i64, i64, P, P, P, C.POINTER(P)]),
         "lw_bundle_build_q_lens": (st, [i32, i64, i64, P, P, P, P, C.POINTER(P)]),
+        "lw_bundle_build_q_opts": (st, [i32, i64, i64, P, P, P, C.POINTER(lw_build_opts), C.POINTER(P)]),
+        "lw_bundle_build_bf16_opts": (st, [i64, i64, P, C.POINTER(lw_build_opts), C.POINTER(P)]),
         "lw_bundle_build_bf16": (st, [i64, i64, P, C.POINTER(P)]),
         "lw_bundle_build_bf16_compact": (st, [i64, i64, P, C.POINTER(P)]),
         "lw_bundle_load": (st, [P, C.c_size_t, C.POINTER(P)]),
@@ -157,11 +163,7 @@ def lw_bundle_build_q_compact(kind: int, codes: np.ndarray, d: np.ndarray, m: np
     return Bundle(out.value)
 
 
-def lw_bundle_build_q_lens(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray, lens: np.ndarray) -> Bundle:
-    rows, cols = codes.shape
-    codes, pc = _np(codes, np.uint8)
-    d, pd = _np(d, np.uint16)
-    m, pm = _np(m, np.uint16)
+def _lens_u8(kind: int, lens):
     n = 256 if kind == LW_Q4_PAIR else 64
     lens = np.asarray(lens)
     # the C side takes one byte per length: refuse what a cast would wrap or truncate
@@ -171,9 +173,41 @@ def lw_bundle_build_q_lens(kind: int, codes: np.ndarray, d: np.ndarray, m: np.nd
         raise ValueError(f"lens must hold {n} lengths")
     if lens.size and (lens.min() < 0 or lens.max() > 11):
         raise ValueError("code lengths must lie in 0..11")
-    lens, pl = _np(lens, np.uint8)
+    return _np(lens, np.uint8)
+
+
+def lw_bundle_build_q_lens(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray, lens: np.ndarray) -> Bundle:
+    rows, cols = codes.shape
+    codes, pc = _np(codes, np.uint8)
+    d, pd = _np(d, np.uint16)
+    m, pm = _np(m, np.uint16)
+    lens, pl = _lens_u8(kind, lens)
     out = C.c_void_p()
     _check(_L.lw_bundle_build_q_lens(kind, rows, cols, pc, pd, pm, pl, C.byref(out)))
+    return Bundle(out.value)
+
+
+def lw_bundle_build_q_opts(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray,
+                           code: int = LW_CODE_HUFFMAN, parts: int = 0, lens=None) -> Bundle:
+    rows, cols = codes.shape
+    codes, pc = _np(codes, np.uint8)
+    d, pd = _np(d, np.uint16)
+    m, pm = _np(m, np.uint16)
+    opts = lw_build_opts(code=code, parts=parts, lens=None)
+    if lens is not None:
+        lens, pl = _lens_u8(kind, lens)
+        opts.lens = pl
+    out = C.c_void_p()
+    _check(_L.lw_bundle_build_q_opts(kind, rows, cols, pc, pd, pm, C.byref(opts), C.byref(out)))
+    return Bundle(out.value)
+
+
+def lw_bundle_build_bf16_opts(w: np.ndarray, code: int = LW_CODE_HUFFMAN, parts: int = 0) -> Bundle:
+    rows, cols = w.shape
+    w, pw = _np(w, np.uint16)
+    opts = lw_build_opts(code=code, parts=parts, lens=None)
+    out = C.c_void_p()
+    _check(_L.lw_bundle_build_bf16_opts(rows, cols, pw, C.byref(opts), C.byref(out)))
     return Bundle(out.value)
 
 

@@ -106,8 +106,11 @@ typedef enum {
     LW_REG_VB_BITS = 7,    /* u32 [n_tiles][8], bit 4i+s marks segment s of tile row i verbatim (bf16) */
     LW_REG_VB_START = 8,   /* u32 [n_tiles+1] verbatim segments before each tile (bf16) */
     LW_REG_VERBATIM = 9,   /* u16 [n_verbatim][64] raw bf16 segments (bf16) */
-    LW_REG_SPLIT = 10,     /* u16 [n_tiles][32]: bits of lane l's first tile row (row 2l); its second
-                              row (2l+1) starts at that bit of the lane stream */
+    LW_REG_SPLIT = 10,     /* u16 [n_tiles][2P-1][32], P = lw_bundle_info.parts: lane stream l of a
+                              tile is 2P parts of equal symbol count, P per tile row (row 2l, then
+                              2l+1), and entry [t][k-1][l] is the bit where part k >= 1 begins, so
+                              any part decodes on its own ("LazyWeights", Fig. 3 caption: per-tile
+                              offsets let every tile start independently; here every part) */
     LW_REG_WORK = 11,      /* device workspace of the split-column reduction (zero in the image) */
     LW_REG_COUNT = 12
 } lw_region;
@@ -128,14 +131,23 @@ typedef struct {
     uint64_t region_offset[LW_REG_COUNT]; /* byte offset of each region inside the image */
     uint64_t region_bytes[LW_REG_COUNT];  /* byte size of each region (0 if absent) */
     uint64_t image_bytes;      /* size of the device image = bytes lw_bundle_upload copies/needs */
-    uint64_t coded_bytes;      /* bytes a fused GEMV must read for the weights: words + tile_off +
+    uint64_t coded_bytes;      /* bytes a fused GEMV must read for the weights: words + tile_off + split +
                                   table + dm (Q4/Q6) or + sm + vb_bits + vb_start + verbatim +
                                   palette (bf16); excludes x, y and the workspace */
     uint64_t twin_bytes;       /* the fixed-width equivalent: rows*cols*bits/8 + rows*cols/256*4
                                   (bf16: rows*cols*2, the dense matrix) */
     int32_t code;              /* lw_code: how the code lengths were chosen */
-    int32_t reserved;
+    int32_t parts;             /* parts per tile row with a recorded start (LW_REG_SPLIT): 1, 2, 4, 8 */
 } lw_bundle_info;
+
+/* Build options (lw_bundle_build_q_opts, lw_bundle_build_bf16_opts). */
+typedef struct {
+    int32_t code;              /* lw_code; LW_CODE_LENS (Q4/Q6 only) takes the lengths in lens */
+    int32_t parts;             /* parts per tile row whose starts are recorded: 1, 2, 4 or 8; 0 lets the
+                                  library choose the largest that keeps tiles x parts <= 4096 (four
+                                  wavefronts per SIMD of a 256-CU MI355X), else 1 */
+    const uint8_t *lens;       /* LW_CODE_LENS: as in lw_bundle_build_q_lens; else ignored */
+} lw_build_opts;
 
 /* ---------------------------------------------------------------- host side */
 
@@ -172,6 +184,17 @@ lw_status lw_bundle_build_q_compact(int kind, int64_t rows, int64_t cols, const 
 lw_status lw_bundle_build_q_lens(int kind, int64_t rows, int64_t cols, const uint8_t *codes,
                                  const uint16_t *d, const uint16_t *m, const uint8_t *lens, lw_bundle **out);
 
+/* As lw_bundle_build_q with explicit options: the code (lw_build_opts.code,
+ * lens) and the parts per tile row.  More parts let more wavefronts decode
+ * one tile at once (shorter serial chains, work spread evenly over the SIMDs)
+ * for 2 bytes per extra part start per lane stream.  The other builders pick
+ * parts = 0.  opts is read, not retained.
+ * Errors: as lw_bundle_build_q_lens, LW_E_ARG for a null opts, an unknown
+ * code or parts outside 0, 1, 2, 4, 8. */
+lw_status lw_bundle_build_q_opts(int kind, int64_t rows, int64_t cols, const uint8_t *codes,
+                                 const uint16_t *d, const uint16_t *m, const lw_build_opts *opts,
+                                 lw_bundle **out);
+
 /* Build a bf16 exponent-coded bundle ("Unweight", exponent palette and
  * verbatim rows; the palette indices coded with the optimal prefix code of at
  * most 11 bits, LW_CODE_HUFFMAN).  w: host bf16 bits [rows][cols].  Errors as
@@ -180,6 +203,12 @@ lw_status lw_bundle_build_bf16(int64_t rows, int64_t cols, const uint16_t *w, lw
 
 /* As lw_bundle_build_bf16 with the compact code (LW_CODE_COMPACT). */
 lw_status lw_bundle_build_bf16_compact(int64_t rows, int64_t cols, const uint16_t *w, lw_bundle **out);
+
+/* As lw_bundle_build_bf16 with explicit options (code HUFFMAN or COMPACT,
+ * parts as in lw_bundle_build_q_opts).  Errors: as lw_bundle_build_bf16,
+ * LW_E_ARG for bad options, LW_E_UNSUPPORTED for LW_CODE_LENS. */
+lw_status lw_bundle_build_bf16_opts(int64_t rows, int64_t cols, const uint16_t *w, const lw_build_opts *opts,
+                                    lw_bundle **out);
 
 /* Re-create a bundle from an image (as returned by lw_bundle_image); the image
  * is copied and validated.  Errors: LW_E_ARG, LW_E_FORMAT, LW_E_TABLE. */

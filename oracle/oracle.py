@@ -268,6 +268,32 @@ def row_split(syms: np.ndarray, spl: int, lens: np.ndarray) -> np.ndarray:
     return np.asarray(lens, dtype=np.int64)[s].sum(axis=2).astype(np.uint16).ravel()
 
 
+# Decoding units (tiles x parts per tile row) the default part count stays within.
+PART_UNITS = 4096
+
+
+def default_parts(n_tiles: int) -> int:
+    """Parts per tile row when the caller leaves it open: the largest of 8, 4,
+    2 that keeps n_tiles * parts <= PART_UNITS, else 1."""
+    for p in (8, 4, 2):
+        if n_tiles * p <= PART_UNITS:
+            return p
+    return 1
+
+
+def part_starts(syms: np.ndarray, spl: int, lens: np.ndarray, parts: int) -> np.ndarray:
+    """Each lane stream cut into 2*parts runs of spl/(2*parts) symbols (parts
+    per tile row): for k = 1 .. 2*parts-1, the bit where run k begins (the
+    total length of the runs before it).  u16 [n_tiles][2*parts-1][32]; with
+    parts = 1 this is row_split."""
+    s = np.asarray(syms).reshape(-1, 32, spl)
+    L = np.asarray(lens, dtype=np.int64)[s]                     # [tiles][lane][symbol]
+    per = spl // (2 * parts)
+    ends = np.cumsum(L, axis=2)[:, :, per - 1::per]             # bits through the end of each run
+    starts = ends[:, :, :2 * parts - 1]                         # run k starts where run k-1 ends
+    return starts.transpose(0, 2, 1).astype(np.uint16).ravel()
+
+
 def code_lengths(counts, code: str = "huffman") -> np.ndarray:
     """The bundle's code lengths: "huffman" (the default) is the optimal
     prefix code with lengths <= 11, the length-limited Huffman table of
@@ -281,9 +307,10 @@ def code_lengths(counts, code: str = "huffman") -> np.ndarray:
 
 
 def build_bundle_q(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray, code: str = "huffman",
-                   lens=None) -> dict:
-    """Quantised bundle: per-matrix table, tile offsets, interleaved words, dm.
-    `lens` (one length per symbol), when given, replaces the chosen code's."""
+                   lens=None, parts: int = 0) -> dict:
+    """Quantised bundle: per-matrix table, tile offsets, interleaved words, dm,
+    part starts.  `lens` (one length per symbol), when given, replaces the
+    chosen code's; parts 0 takes default_parts."""
     R, Cc = codes.shape
     if R % 64 or Cc % 256:
         raise ValueError("shape must be a multiple of 64x256")
@@ -293,9 +320,10 @@ def build_bundle_q(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray, c
     lens = code_lengths(counts, code) if lens is None else np.ascontiguousarray(lens, dtype=np.uint8)
     tab = canonical(lens)
     tile_off, words, lane_bits = encode_tiles(syms, spl, lens, tab["codes"])
+    parts = parts or default_parts((R // 64) * (Cc // 256))
     return dict(kind=kind, rows=R, cols=Cc, spl=spl, counts=counts, table=tab,
                 tile_off=tile_off, words=words, lane_bits=lane_bits, dm=pack_dm(d, m),
-                split=row_split(syms, spl, lens))
+                parts=parts, split=part_starts(syms, spl, lens, parts))
 
 
 def decode_bundle_q(b: dict, bitwise: bool = False):
@@ -318,7 +346,7 @@ def symbolise_bf16(w: np.ndarray, palette: np.ndarray, n_pal: int, vb_bits: np.n
     return syms
 
 
-def build_bundle_bf16(w: np.ndarray, code: str = "huffman") -> dict:
+def build_bundle_bf16(w: np.ndarray, code: str = "huffman", parts: int = 0) -> dict:
     R, Cc = w.shape
     if R % 64 or Cc % 256:
         raise ValueError("shape must be a multiple of 64x256")
@@ -342,7 +370,7 @@ def build_bundle_bf16(w: np.ndarray, code: str = "huffman") -> dict:
     return dict(kind=BF16, rows=R, cols=Cc, spl=512, counts=counts, table=tab, palette=palette,
                 n_pal=n_pal, vb_bits=vb_bits, vb_start=vb_start, verbatim=verbatim[:nv * 64],
                 n_verbatim=nv, tile_off=tile_off, words=words, lane_bits=lane_bits, sm=sm,
-                split=row_split(syms, 512, lens))
+                parts=parts or default_parts(nt), split=part_starts(syms, 512, lens, parts or default_parts(nt)))
 
 
 def decode_bundle_bf16(b: dict, bitwise: bool = False):

@@ -41,6 +41,7 @@ def _compare_q(kind, codes, d, m, code="huffman"):
     assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_WORDS, np.uint32), ob["words"])
     assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_DM, np.uint32), ob["dm"])
     assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_SPLIT, np.uint16), ob["split"])
+    assert info["parts"] == ob["parts"] == O.default_parts(info["n_tiles"])
     W = np.diff(ob["tile_off"].astype(np.int64)) // 32
     assert info["max_words"] == W.max()
     assert info["coded_bytes"] == (ob["words"].nbytes + ob["tile_off"].nbytes + ob["dm"].nbytes +
@@ -84,7 +85,59 @@ def test_builder_with_given_lengths_matches_oracle(kind, law, seed):
         assert np.array_equal(t[k], tab[k]), k
     assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_TILE_OFF, np.uint32), tile_off)
     assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_WORDS, np.uint32), words)
-    assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_SPLIT, np.uint16), O.row_split(syms, spl, lens))
+    parts = O.default_parts((192 // 64) * (1280 // 256))
+    assert dg.lw_bundle_get_info(pb)["parts"] == parts
+    assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_SPLIT, np.uint16), O.part_starts(syms, spl, lens, parts))
+
+
+@pytest.mark.parametrize("parts", [1, 2, 4, 8])
+def test_builder_parts_match_oracle(parts):
+    """Explicit parts per tile row: the part starts (and everything else)
+    equal the oracle's for Q4, Q6 and bf16, with either code."""
+    for kind, qmax, mu, sc in ((dg.LW_Q4_PAIR, 15, 7.5, 1.8), (dg.LW_Q6_SINGLE, 63, 31.5, 5.0)):
+        codes, d, m, _ = synth.gen_q_custom(128, 768, 90 + parts, qmax=qmax, mu=mu, scale=sc)
+        for code, cname in ((dg.LW_CODE_HUFFMAN, "huffman"), (dg.LW_CODE_COMPACT, "compact")):
+            ob = O.build_bundle_q(kind, codes, d, m, code=cname, parts=parts)
+            pb = dg.lw_bundle_build_q_opts(kind, codes, d, m, code=code, parts=parts)
+            dg.lw_bundle_validate(pb)
+            info = dg.lw_bundle_get_info(pb)
+            assert info["parts"] == parts and info["code"] == code
+            assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_WORDS, np.uint32), ob["words"])
+            sp = dg.lw_bundle_region(pb, dg.LW_REG_SPLIT, np.uint16)
+            assert sp.size == info["n_tiles"] * 32 * (2 * parts - 1)
+            assert np.array_equal(sp, ob["split"])
+            assert info["coded_bytes"] == (ob["words"].nbytes + ob["tile_off"].nbytes + ob["dm"].nbytes +
+                                           ob["split"].nbytes + 608)
+    w, _ = synth.gen_bf16_custom(128, 768, 95 + parts, outlier_frac=0.01)
+    ob = O.build_bundle_bf16(w, parts=parts)
+    pb = dg.lw_bundle_build_bf16_opts(w, parts=parts)
+    assert dg.lw_bundle_get_info(pb)["parts"] == parts
+    assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_SPLIT, np.uint16), ob["split"])
+    # lengths given through the options match lw_bundle_build_q_lens
+    codes, d, m, _ = synth.gen_q_custom(64, 512, 97)
+    lens = O.package_merge(O.histogram(O.symbolise_q(O.Q4, codes), 256))
+    a = dg.lw_bundle_build_q_opts(dg.LW_Q4_PAIR, codes, d, m, code=dg.LW_CODE_LENS, parts=parts, lens=lens)
+    ob = O.build_bundle_q(O.Q4, codes, d, m, lens=lens, parts=parts)
+    assert np.array_equal(dg.lw_bundle_region(a, dg.LW_REG_SPLIT, np.uint16), ob["split"])
+    assert np.array_equal(dg.lw_bundle_region(a, dg.LW_REG_WORDS, np.uint32), ob["words"])
+
+
+def test_build_options_rejected():
+    codes, d, m, _ = synth.gen_q_custom(64, 256, 98)
+    for parts in (3, 16, -1):
+        with pytest.raises(dg.LwError) as e:
+            dg.lw_bundle_build_q_opts(dg.LW_Q4_PAIR, codes, d, m, parts=parts)
+        assert e.value.status == dg.LW_E_ARG
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_bundle_build_q_opts(dg.LW_Q4_PAIR, codes, d, m, code=7)
+    assert e.value.status == dg.LW_E_ARG
+    with pytest.raises(dg.LwError) as e:               # LENS without lengths
+        dg.lw_bundle_build_q_opts(dg.LW_Q4_PAIR, codes, d, m, code=dg.LW_CODE_LENS)
+    assert e.value.status == dg.LW_E_ARG
+    w, _ = synth.gen_bf16_custom(64, 256, 99)
+    with pytest.raises(dg.LwError) as e:
+        dg.lw_bundle_build_bf16_opts(w, code=dg.LW_CODE_LENS)
+    assert e.value.status == dg.LW_E_UNSUPPORTED
 
 
 def test_given_lengths_rejected():
@@ -219,7 +272,7 @@ def test_load_round_trip():
 
 
 @pytest.mark.parametrize("what", ["magic", "truncate", "len12", "kraft", "tile_off", "tile_off_end",
-                                  "shape", "region", "split"])
+                                  "shape", "region", "split", "split_order", "parts"])
 def test_corrupt_images_rejected(what):
     b, img, info = _image()
     img = img.copy()
@@ -254,7 +307,16 @@ def test_corrupt_images_rejected(what):
         hdr[104 // 8 + dg.LW_REG_WORDS] = len(img) + 4096
     elif what == "split":
         sp = img[off[dg.LW_REG_SPLIT]:].view(np.uint16)
-        sp[5] = 0xFFFF                # second row starting past the lane's words
+        sp[5] = 0xFFFF                # a part starting past the lane's words
+    elif what == "split_order":
+        assert info["parts"] > 1
+        sp = img[off[dg.LW_REG_SPLIT]:].view(np.uint16)
+        sp[32 + 3] = sp[3]            # part 2 of lane 3 starting where part 1 does
+    elif what == "parts":
+        hdr = img[:512].view(np.int32)
+        # the parts field follows the region offset and size arrays (bytes 104 .. 296)
+        assert hdr[296 // 4] == info["parts"]
+        hdr[296 // 4] = 3
     with pytest.raises(dg.LwError) as e:
         dg.lw_bundle_load(img)
     assert e.value.status == expect, (what, e.value)

@@ -331,6 +331,57 @@ def test_gemv_mfma_small(torch, dg, case, batch):
     assert np.array_equal(y, _run_gemv(dg, torch, db, x, batch, rows))
 
 
+# ------------------------------------------------------------------ parts per tile row
+
+PARTS_Q = [
+    # column blocks: five (four-wavefront groups), fourteen (fourteen-wavefront
+    # groups), sixteen (whole rows), eight and thirteen
+    ("q4", 192, 1280, "normal", 131), ("q4", 128, 3584, "laplace", 132), ("q4", 64, 4096, "normal", 133),
+    ("q6", 128, 2048, "normal", 134), ("q6", 64, 3328, "normal", 135),
+]
+
+
+@pytest.mark.parametrize("parts", [1, 2, 4, 8])
+@pytest.mark.parametrize("case", PARTS_Q, ids=lambda c: "-".join(map(str, c)))
+def test_parts_q(torch, dg, case, parts):
+    """Bundles with 1, 2, 4 and 8 recorded parts per tile row: decode-only
+    bit-exact (and per-lane bit counts), the VALU GEMV at batch 1, 2, 4 and 7
+    and the matrix-core GEMV at batch 16 within tolerance and repeatable."""
+    kind_s, rows, cols, law, seed = case
+    say("parts", case, parts)
+    kind = dg.LW_Q4_PAIR if kind_s == "q4" else dg.LW_Q6_SINGLE
+    codes, d, m, x = _gen_small(*case)
+    b = dg.lw_bundle_build_q_opts(kind, codes, d, m, parts=parts)
+    info = dg.lw_bundle_get_info(b)
+    assert info["parts"] == parts
+    db = _upload(dg, torch, b)
+    q, bits = _decode_q(dg, torch, db, kind, rows, cols, info["n_tiles"])
+    assert np.array_equal(q, codes)
+    _, obits = O.decode_bundle_q(O.build_bundle_q(kind, codes, d, m, parts=parts))
+    assert np.array_equal(bits, obits)
+    for batch in (1, 2, 4, 7, 16):
+        y = _run_gemv(dg, torch, db, x, batch, rows)
+        assert rel_err(y, O.gemv_q(codes, d, m, x, batch)) <= TOL, batch
+        assert np.array_equal(y, _run_gemv(dg, torch, db, x, batch, rows)), batch
+
+
+@pytest.mark.parametrize("parts", [1, 2, 8])
+@pytest.mark.parametrize("case", [(128, 1280, 0.02, 211), (64, 4096, 0.0, 212)], ids=lambda c: "-".join(map(str, c)))
+def test_parts_bf16(torch, dg, case, parts):
+    rows, cols, frac, seed = case
+    say("bf16 parts", case, parts)
+    w, x = synth.gen_bf16_custom(rows, cols, seed, outlier_frac=frac)
+    b = dg.lw_bundle_build_bf16_opts(w, parts=parts)
+    info = dg.lw_bundle_get_info(b)
+    assert info["parts"] == parts
+    db = _upload(dg, torch, b)
+    w2, _ = _decode_bf16(dg, torch, db, rows, cols, info["n_tiles"])
+    assert np.array_equal(w2, w)
+    for batch in (1, 3, 16):
+        y = _run_gemv(dg, torch, db, x, batch, rows)
+        assert rel_err(y, O.gemv_bf16(w, x, batch)) <= TOL, batch
+
+
 PLAN_NAMES = {0: "compact", 1: "r2", 2: "r2k", 3: "r2x2", 4: "gen"}
 
 

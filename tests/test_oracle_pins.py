@@ -392,35 +392,49 @@ def _bitwise_from(bits, start, n, code_map):
     return syms, pos
 
 
+@pytest.mark.parametrize("parts", [1, 2, 4, 8])
 @pytest.mark.parametrize("case", ["q4", "q6", "bf16"])
-def test_row_split_marks_second_row(case):
-    # the split of lane l is where its second tile row starts: decoding the
-    # first half from bit 0 ends there, and decoding from there yields the
-    # second row's symbols (checked with a bit-at-a-time decoder)
+def test_part_starts_mark_runs(case, parts):
+    # with 2*parts runs of spl/(2*parts) symbols per lane stream (parts per
+    # tile row), the recorded start of run k is where decoding run k-1 from
+    # its own start ends, and decoding from there yields exactly run k's
+    # symbols (checked with a bit-at-a-time decoder); with one part per row
+    # the only start is the second tile row's
     if case == "bf16":
         w, _ = synth.gen_bf16_custom(64, 512, 77, outlier_frac=0.01)
-        b = O.build_bundle_bf16(w)
+        b = O.build_bundle_bf16(w, parts=parts)
         spl = 512
         syms = O.symbolise_bf16(w, b["palette"], b["n_pal"], b["vb_bits"])
     else:
         kind = O.Q4 if case == "q4" else O.Q6
         codes, d, m, _ = synth.gen_q_custom(64, 512, 78, qmax=15 if case == "q4" else 63,
                                             mu=7.5 if case == "q4" else 31.5, scale=1.8 if case == "q4" else 5.0)
-        b = O.build_bundle_q(kind, codes, d, m)
+        b = O.build_bundle_q(kind, codes, d, m, parts=parts)
         spl = b["spl"]
         syms = O.symbolise_q(kind, codes)
+    assert b["parts"] == parts
     syms = syms.reshape(-1, 32, spl)
     lens, cw = b["table"]["lens"], b["table"]["codes"]
     code_map = {(int(lens[s]), int(cw[s])): s for s in range(len(lens)) if lens[s] > 0}
-    split = b["split"].reshape(-1, 32)
+    nrun, per = 2 * parts, spl // (2 * parts)
+    starts = b["split"].reshape(syms.shape[0], nrun - 1, 32)
+    if parts == 1:
+        assert np.array_equal(b["split"], O.row_split(syms.ravel(), spl, lens))
     for t in range(syms.shape[0]):
         for l in (0, 5, 17, 31):
             bits = _lane_bits(b["words"], b["tile_off"], t, l)
-            first, end = _bitwise_from(bits, 0, spl // 2, code_map)
-            assert end == split[t, l]
-            assert first == list(syms[t, l, :spl // 2])
-            second, _ = _bitwise_from(bits, int(split[t, l]), spl // 2, code_map)
-            assert second == list(syms[t, l, spl // 2:])
+            pos = 0
+            for k in range(nrun):
+                if k:
+                    assert pos == starts[t, k - 1, l]
+                run, pos = _bitwise_from(bits, int(starts[t, k - 1, l]) if k else 0, per, code_map)
+                assert run == list(syms[t, l, k * per:(k + 1) * per])
+
+
+def test_default_parts_rule():
+    # the largest of 8, 4, 2 that keeps tiles x parts within 4096 units, else 1
+    assert [O.default_parts(n) for n in (1, 16, 512, 513, 1024, 1025, 2048, 2049, 3584, 14336)] == \
+        [8, 8, 8, 4, 4, 2, 2, 1, 1, 1]
 
 
 def test_double_to_half_matches_numpy_rounding():
