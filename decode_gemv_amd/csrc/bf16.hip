@@ -30,14 +30,14 @@ struct LdsLayout {
     uint32_t x, tiles, flag, total;
 };
 
-__host__ __device__ inline LdsLayout lds_layout(int batch, int max_words, bool decode_only)
+__host__ __device__ inline LdsLayout lds_layout(int batch, int max_words, bool decode_only, int waves = WAVES)
 {
     LdsLayout L;
     L.x = LW_TAB_BYTES;
-    const uint32_t xbytes = decode_only ? 0u : (uint32_t)(WAVES * batch * 128 * 4);
+    const uint32_t xbytes = decode_only ? 0u : (uint32_t)(waves * batch * 128 * 4);
     L.tiles = L.x + xbytes;
-    const uint32_t tiles = (uint32_t)(WAVES * (max_words + 3) * 128);
-    const uint32_t red = (uint32_t)(WAVES * batch * 64 * 4);
+    const uint32_t tiles = (uint32_t)(waves * (max_words + 3) * 128);
+    const uint32_t red = (uint32_t)(waves * batch * 64 * 4);
     L.flag = L.tiles + (tiles > red ? tiles : red);
     L.total = L.flag + 16;
     return L;
@@ -50,7 +50,7 @@ struct LaneCtx {
     bool active;
 };
 
-LW_DEV LaneCtx lane_ctx(const KArgs &a)
+LW_DEV LaneCtx lane_ctx(const KArgs &a, int waves = WAVES)
 {
     LaneCtx c;
     c.wave = (int)lw_wave_id();
@@ -59,7 +59,7 @@ LW_DEV LaneCtx lane_ctx(const KArgs &a)
     c.l = c.lane & 31;
     c.g = blockIdx.x;
     c.rb = blockIdx.y;
-    c.cb = c.g * WAVES + c.wave;
+    c.cb = c.g * waves + c.wave;
     c.active = c.cb < a.n_cb;
     c.t = c.rb * a.n_cb + (c.active ? c.cb : 0);
     return c;
@@ -92,12 +92,14 @@ LW_DEV void lw_load_sm(uint32_t (&dst)[CHUNK], const uint32_t *smrow, int chunk)
     for (int i = 0; i < CHUNK; i++) dst[i] = smrow[(chunk * CHUNK + i) * 32];
 }
 
-template <int PLAN, int BATCH>
-__global__ __launch_bounds__(256) void k_gemv_bf16(KArgs a)
+// WPG wavefronts per workgroup, one column block each: four, or sixteen
+// (whole rows, the reduction in LDS) as in fused_q.hip.
+template <int PLAN, int BATCH, int WPG>
+__global__ __launch_bounds__(64 * WPG) void k_gemv_bf16(KArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const LdsLayout L = lds_layout(BATCH, a.max_words, false);
-    const LaneCtx c = lane_ctx(a);
+    const LdsLayout L = lds_layout(BATCH, a.max_words, false, WPG);
+    const LaneCtx c = lane_ctx(a, WPG);
     const int S = a.max_words + 3;
     const uint32_t xs_addr = (uint32_t)(size_t)(lds + L.x) + 4u * (uint32_t)(c.wave * BATCH * 128);
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
@@ -117,10 +119,12 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(KArgs a)
     }
     uint32_t ring[2][CHUNK];
     lw_load_sm(ring[0], smrow, 0);
+    // whole-row workgroups request their tiles after the table barrier (see fused_q.hip)
     LwTileRegs64 tile;
-    lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
+    if constexpr (WPG <= WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
     __syncthreads();                      // the decoder table is complete
+    if constexpr (WPG > WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
 #pragma unroll
     for (int b = 0; b < BATCH; b++) {
         *(lw_lds_w32 *)(size_t)(xs_addr + 4u * (b * 128 + c.lane)) = xv[b][0];
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(KArgs a)
     for (int b = 0; b < BATCH; b++) red[(c.wave * BATCH + b) * 64 + 2 * c.l + c.half] = c.active ? acc[b] : 0.f;
     __syncthreads();
     uint32_t *last_flag = reinterpret_cast<uint32_t *>(lds + L.flag);
-    lw_finish_rows<BATCH, 64>(a, red, (int64_t)c.rb * 64, c.g, c.rb, WAVES, last_flag);
+    lw_finish_rows<BATCH, 64>(a, red, (int64_t)c.rb * 64, c.g, c.rb, WPG, last_flag);
 }
 
 // Decode only: rebuild the bf16 matrix [rows][cols].
@@ -341,7 +345,7 @@ template <int PLAN, bool EXP>
 hipError_t launch_transcode(const KArgs &a, hipStream_t s)
 {
     const LdsLayout L = lds_layout(1, a.max_words, true);
-    dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
+    dim3 grid((unsigned)((a.n_cb + WAVES - 1) / WAVES), (unsigned)a.n_rb);
     hipError_t e = lw_allow_lds<k_transcode_bf16<PLAN, EXP>>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_transcode_bf16<PLAN, EXP>), grid, dim3(256), L.total, s, a);
@@ -354,23 +358,39 @@ hipError_t transcode_mode(const KArgs &a, bool exponents, hipStream_t s)
     return exponents ? launch_transcode<PLAN, true>(a, s) : launch_transcode<PLAN, false>(a, s);
 }
 
-template <int PLAN, int BATCH>
-hipError_t launch_gemv(const KArgs &a0, hipStream_t s)
+template <int PLAN, int BATCH, int WPG>
+hipError_t launch_gemv_wpg(const KArgs &a0, hipStream_t s)
 {
     KArgs a = a0;
+    a.groups = (a.n_cb + WPG - 1) / WPG;  // column groups combined through the workspace (none if 1)
     a.ramp = lw_resident_ramp((int64_t)a.n_rb * a.n_cb);
-    const LdsLayout L = lds_layout(BATCH, a.max_words, false);
+    const LdsLayout L = lds_layout(BATCH, a.max_words, false, WPG);
     dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
-    auto kern = k_gemv_bf16<PLAN, BATCH>;
-    hipError_t e = lw_allow_lds<k_gemv_bf16<PLAN, BATCH>>();
+    auto kern = k_gemv_bf16<PLAN, BATCH, WPG>;
+    hipError_t e = lw_allow_lds<k_gemv_bf16<PLAN, BATCH, WPG>>();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, grid, dim3(256), L.total, s, a);
+    hipLaunchKernelGGL(kern, grid, dim3(64 * WPG), L.total, s, a);
     return hipGetLastError();
 }
 
-template <int PLAN>
-hipError_t launch_decode(const KArgs &a, hipStream_t s)
+// Whole rows (sixteen wavefronts) under the 4- and 6-bit kernels'
+// conditions: 13..16 column blocks, at least 128 row bands, tiles in LDS.
+template <int PLAN, int BATCH>
+hipError_t launch_gemv(const KArgs &a, hipStream_t s)
 {
+    if constexpr (BATCH <= 4) {
+        if (a.n_cb > 12 && a.n_cb <= 16 && a.n_rb >= 128 &&
+            lds_layout(BATCH, a.max_words, false, 16).total <= (uint32_t)lw_device_lds_bytes())
+            return launch_gemv_wpg<PLAN, BATCH, 16>(a, s);
+    }
+    return launch_gemv_wpg<PLAN, BATCH, WAVES>(a, s);
+}
+
+template <int PLAN>
+hipError_t launch_decode(const KArgs &a0, hipStream_t s)
+{
+    KArgs a = a0;
+    a.groups = (a.n_cb + WAVES - 1) / WAVES;
     const LdsLayout L = lds_layout(1, a.max_words, true);
     dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
     auto kern = k_decode_bf16<PLAN>;

@@ -327,7 +327,7 @@ template <int KIND, int PLAN>
 hipError_t launch_decode_q(const KArgs &a, hipStream_t s)
 {
     const LdsLayout L = lds_layout(1, a.max_words, true);
-    dim3 grid((unsigned)a.groups, (unsigned)a.n_rb);
+    dim3 grid((unsigned)((a.n_cb + WAVES - 1) / WAVES), (unsigned)a.n_rb);   // one column block per wavefront
     auto kern = k_decode_q<KIND, PLAN>;
     hipError_t e = lw_allow_lds<k_decode_q<KIND, PLAN>>();
     if (e != hipSuccess) return e;
