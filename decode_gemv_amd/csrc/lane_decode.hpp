@@ -556,11 +556,13 @@ LW_DEV bool lw_lane_init(LaneDec &d, uint8_t *lds, const uint32_t *slots, int l,
 // Sum the per-wave partials of the workgroup's ROWS rows (red[wave][b][row],
 // RS floats between consecutive (wave, b) runs) and either write y (one
 // column group) or take part in the split-column reduction.  The partials
-// travel through the bundle's workspace as device-scope atomic exchanges,
-// which are performed at the coherence point of all XCDs without an L2
-// writeback; each workgroup then bumps the arrival counter of its rows
-// (index ctr), and the last one to arrive reads the partials back with
-// device-scope atomic loads, then re-arms the counter for the next call.
+// travel through the bundle's workspace as device-scope atomic stores,
+// which are written through to the coherence point of all XCDs (no L2
+// writeback of other data is needed); once each thread's stores are
+// acknowledged (vmcnt 0) and the workgroup has met at a barrier, the
+// workgroup bumps the arrival counter of its rows (index ctr), and the last
+// one to arrive reads the partials back with device-scope atomic loads, then
+// re-arms the counter for the next call.
 // The last arrival's loads are all in flight at once -- T consecutive
 // threads per output (T a power of two, at most 8, as the workgroup's
 // threads allow), each loading only its own groups (every T-th, summed in
@@ -580,12 +582,12 @@ LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g
         if (row0 + row < a.rows) {
             if (a.groups == 1) a.y[(size_t)b * a.rows + row0 + row] = v;
             else
-                (void)__hip_atomic_exchange(&a.part[((size_t)g * LW_BATCH_MAX + b) * a.rows + row0 + row], v,
-                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&a.part[((size_t)g * LW_BATCH_MAX + b) * a.rows + row0 + row], v,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
     if (a.groups == 1) return;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's exchanges are performed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's stores are acknowledged
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t old = __hip_atomic_fetch_add(&a.count[(size_t)ctr * LW_COUNTER_STRIDE], 1u, __ATOMIC_RELAXED,
