@@ -177,6 +177,37 @@ def test_canonical_prefix_free_and_ordered(seed):
     assert kraft_sum(lens) == 2048
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_canonical_equals_greedy_search(seed):
+    """The canonical assignment (RFC 1951, section 3.2.2: codes of one length
+    consecutive in symbol order, shorter lengths first) found by search
+    instead of the recurrence: in (length, symbol) order, each symbol takes
+    the smallest code of its length that no earlier code is a prefix of and
+    that lies above every earlier code left-justified to 11 bits.  Random
+    length vectors, complete and incomplete (Kraft sum below 1)."""
+    rng = np.random.default_rng(300 + seed)
+    for trial in range(60):
+        n = int(rng.integers(1, 13))
+        while True:
+            lens = np.zeros(16, np.uint8)
+            lens[rng.choice(16, n, replace=False)] = rng.integers(1, 12, n)
+            if kraft_sum(lens) <= 2048:
+                break
+        tab = O.canonical(lens)
+        taken = []
+        for sym in sorted(np.flatnonzero(lens), key=lambda s: (int(lens[s]), s)):
+            L = int(lens[sym])
+            floor = max((int(c, 2) << (11 - len(c)) for c in taken), default=-1)
+            for v in range(1 << L):
+                c = format(v, f"0{L}b")
+                if (int(c, 2) << (11 - L)) > floor and not any(c.startswith(t) or t.startswith(c) for t in taken):
+                    break
+            else:
+                raise AssertionError("no code left")
+            taken.append(c)
+            assert _bitstr(tab["codes"][sym], L) == c, (lens.tolist(), sym)
+
+
 # ------------------------------------------------------------------ streams
 
 def _bundle_bits_by_hand(syms, spl, lens, codes, nt):
