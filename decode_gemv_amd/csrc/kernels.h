@@ -95,7 +95,6 @@ hipError_t lw_launch_transcode_bf16(const KArgs &a, SadPlan p, bool exponents, h
 hipError_t lw_launch_swiglu(const float *g, const float *u, uint16_t *h, int64_t n, hipStream_t s);
 hipError_t lw_launch_twin(const uint8_t *twin, const uint32_t *dm, int64_t rows, int64_t cols,
                           const uint16_t *x, float *y, int batch, hipStream_t s);
-hipError_t lw_launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t lw_launch_read_probe(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
 hipError_t lw_launch_recon(bool exponents, const uint32_t *src, const uint32_t *sm, const int32_t *vrank,
                            const uint32_t *vb_start, const uint16_t *verbatim, int64_t n_verbatim,
