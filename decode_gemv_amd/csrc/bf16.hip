@@ -27,7 +27,7 @@ constexpr int WAVES = 4;
 constexpr int CHUNK = 16;                 // groups of four columns per sm prefetch chunk
 
 struct LdsLayout {
-    uint32_t x, tiles, flag, total;
+    uint32_t x, tiles, total;
 };
 
 __host__ __device__ inline LdsLayout lds_layout(int batch, int max_words, bool decode_only, int waves = WAVES)
@@ -38,8 +38,7 @@ __host__ __device__ inline LdsLayout lds_layout(int batch, int max_words, bool d
     L.tiles = L.x + xbytes;
     const uint32_t tiles = (uint32_t)(waves * (max_words + 3) * 128);
     const uint32_t red = (uint32_t)(waves * batch * 64 * 4);
-    L.flag = L.tiles + (tiles > red ? tiles : red);
-    L.total = L.flag + 16;
+    L.total = L.tiles + (tiles > red ? tiles : red);
     return L;
 }
 
@@ -201,8 +200,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_bf16(KArgs a)
 #pragma unroll
     for (int b = 0; b < BATCH; b++) red[(c.wave * BATCH + b) * 64 + 2 * c.l + c.half] = c.active ? acc[b] : 0.f;
     __syncthreads();
-    uint32_t *last_flag = reinterpret_cast<uint32_t *>(lds + L.flag);
-    lw_finish_rows<BATCH, 64>(a, red, (int64_t)c.rb * 64, c.g, c.rb, WPG, last_flag);
+    lw_finish_rows<BATCH, 64>(a, red, (int64_t)c.rb * 64, c.g, WPG);
 }
 
 // Decode only: rebuild the bf16 matrix [rows][cols].

@@ -323,9 +323,8 @@ static lw_image_header plan_image(int kind, const Shape &sh, int64_t n_words, in
     } else {
         bytes[LW_REG_DM] = 4u * 64u * (uint64_t)sh.n_tiles;
     }
-    // partial sums, then one arrival counter line per row band
-    bytes[LW_REG_WORK] = h.work_groups > 1
-        ? lw_work_partial_bytes(h.work_groups, sh.rows) + lw_work_counter_bytes(sh.n_rb) : 0;
+    // the pair slots of the split-column reduction
+    bytes[LW_REG_WORK] = lw_work_bytes(h.work_groups, sh.rows);
     uint64_t pos = LW_HEADER_BYTES;
     for (int r = 0; r < LW_REG_COUNT; r++) {
         h.off[r] = bytes[r] ? pos : 0;
@@ -1072,7 +1071,7 @@ static lw_status validate_image(const uint8_t *img, size_t bytes)
     }
     const int32_t groups = lw_work_groups(h.n_cb, h.parts);
     if (h.work_groups != groups) return lw_fail(LW_E_FORMAT, "workspace groups");
-    if (groups > 1 && h.bytes[LW_REG_WORK] < lw_work_partial_bytes(groups, h.rows) + lw_work_counter_bytes(h.n_rb))
+    if (h.bytes[LW_REG_WORK] < lw_work_bytes(groups, h.rows))
         return lw_fail(LW_E_FORMAT, "workspace too small");
     return LW_OK;
 }

@@ -35,7 +35,7 @@ namespace {
 constexpr int WAVES = 4;                 // wavefronts per workgroup (one column block each), by default
 
 struct LdsLayout {
-    uint32_t x, tiles, flag, total;
+    uint32_t x, tiles, total;
 };
 
 // staged tiles: one per `parts` wavefronts
@@ -48,8 +48,7 @@ __host__ __device__ inline LdsLayout lds_layout(int batch, int max_words, bool d
     L.tiles = L.x + xbytes;
     const uint32_t tiles = (uint32_t)((waves / parts) * (max_words + 3) * 128);
     const uint32_t red = (uint32_t)(waves * batch * 64 * 4);
-    L.flag = L.tiles + (tiles > red ? tiles : red);
-    L.total = L.flag + 16;
+    L.total = L.tiles + (tiles > red ? tiles : red);
     return L;
 }
 
@@ -213,8 +212,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
     for (int b = 0; b < BATCH; b++) red[(c.wave * BATCH + b) * 64 + 2 * c.l + c.half] = val[b];
     __syncthreads();
 
-    uint32_t *last_flag = reinterpret_cast<uint32_t *>(lds + L.flag);
-    lw_finish_rows<BATCH, 64>(a, red, (int64_t)c.rb * 64, c.g, c.rb, WPG, last_flag);
+    lw_finish_rows<BATCH, 64>(a, red, (int64_t)c.rb * 64, c.g, WPG);
 }
 
 

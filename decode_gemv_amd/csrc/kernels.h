@@ -24,8 +24,7 @@ struct KArgs {
     const uint16_t *verbatim;    // bf16 raw segments
     const uint16_t *x;           // [batch][cols] fp16 or bf16 bits
     float *y;                    // [batch][rows]
-    float *part;                 // workspace partials [groups][16][rows]
-    uint32_t *count;             // workspace arrival counters
+    float *part;                 // workspace: pair slots of the reduction tree [groups-1][16][rows]
     void *out;                   // decode-only output
     uint32_t *lane_bits;         // decode-only optional per-lane bit counts
     int32_t *vrank;              // bf16 transcode: verbatim store index of each (tile, segment, row), or -1

@@ -554,77 +554,77 @@ LW_DEV bool lw_lane_init(LaneDec &d, uint8_t *lds, const uint32_t *slots, int l,
 }
 
 // Sum the per-wave partials of the workgroup's ROWS rows (red[wave][b][row],
-// RS floats between consecutive (wave, b) runs) and either write y (one
-// column group) or take part in the split-column reduction.  The partials
-// travel through the bundle's workspace as device-scope atomic stores,
-// which are written through to the coherence point of all XCDs (no L2
-// writeback of other data is needed); once each thread's stores are
-// acknowledged (vmcnt 0) and the workgroup has met at a barrier, the
-// workgroup bumps the arrival counter of its rows (index ctr), and the last
-// one to arrive reads the partials back with device-scope atomic loads, then
-// re-arms the counter for the next call.
-// The last arrival's loads are all in flight at once -- T consecutive
-// threads per output (T a power of two, at most 8, as the workgroup's
-// threads allow), each loading only its own groups (every T-th, summed in
-// group order), the T sums then combined by a butterfly -- so the reduction
-// costs three round trips to the coherence point (publish, count, gather)
-// however many groups there are.  The order of the additions is fixed by the group count and the
-// workgroup size alone, so the result is deterministic.
+// RS floats between consecutive (wave, b) runs) and write y, or, when the
+// row band's columns are split over a.groups workgroups, combine the groups'
+// sums by a pairwise exchange tree in the bundle's workspace.
+//
+// Group g is leaf g of a binary tree over the groups (a node without a
+// sibling at some level passes its value up unchanged).  For each output,
+// the two members of a pair meet in one workspace slot, which holds 0 when
+// empty: each swaps its value into the slot with one device-scope atomic
+// exchange.  The one that gets 0 back arrives first and is done; the other
+// gets its partner's value, empties the slot again and carries the sum one
+// level up.  The single atomic read-modify-write on the slot is the only
+// synchronisation, so no thread ever waits for another, and every slot is
+// empty again when the call ends (both members of every pair always come).
+// Floating-point addition is commutative, so each pair's sum, and the whole
+// tree's, does not depend on which member arrives first: the result is
+// deterministic.  A value of +0.0 travels as -0.0 (the empty slot's bits are
+// those of +0.0), so an output whose sum is zero may be written as -0.0.
+// A thread's outputs (at most KMAX) go up the tree together, their exchanges
+// in flight at once: ceil(log2(groups)) round trips to the coherence point.
 template <int BATCH, int ROWS = 128, int RS = ROWS>
-LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g, int ctr, int waves,
-                           uint32_t *last_flag)
+LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g, int waves)
 {
-    for (int i = threadIdx.x; i < BATCH * ROWS; i += blockDim.x) {
+    constexpr int KMAX = (BATCH * ROWS + 255) / 256;   // outputs per thread (workgroups have at least 256 threads)
+    float v[KMAX];
+    int64_t at[KMAX];                                    // the output's index in y, or -1
+#pragma unroll
+    for (int k = 0; k < KMAX; k++) {
+        const int i = (int)threadIdx.x + k * (int)blockDim.x;
         const int b = i / ROWS, row = i % ROWS;
-        if (b >= a.batch) break;
-        float v = 0.f;
-        for (int w = 0; w < waves; w++) v += red[(w * BATCH + b) * RS + row];
-        if (row0 + row < a.rows) {
-            if (a.groups == 1) a.y[(size_t)b * a.rows + row0 + row] = v;
-            else
-                __hip_atomic_store(&a.part[((size_t)g * LW_BATCH_MAX + b) * a.rows + row0 + row], v,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool ok = i < BATCH * ROWS && b < a.batch && row0 + row < a.rows;
+        float s = 0.f;
+        if (ok)
+            for (int w = 0; w < waves; w++) s += red[(w * BATCH + b) * RS + row];
+        v[k] = s;
+        at[k] = ok ? (int64_t)b * a.rows + row0 + row : -1;
+    }
+    if (a.groups > 1) {
+        uint32_t *slots = reinterpret_cast<uint32_t *>(a.part);
+        const size_t stride = (size_t)LW_BATCH_MAX * (size_t)a.rows;   // one slot: [LW_BATCH_MAX][rows]
+        int node = g, n = a.groups, base = 0;
+        while (n > 1) {                                  // the same steps in every thread of the workgroup
+            if ((node ^ 1) < n) {
+                uint32_t *slot = slots + (size_t)(base + (node >> 1)) * stride;
+                uint32_t mine[KMAX], other[KMAX];
+#pragma unroll
+                for (int k = 0; k < KMAX; k++) {
+                    mine[k] = __builtin_bit_cast(uint32_t, v[k]);
+                    if (mine[k] == 0u) mine[k] = 0x80000000u;
+                    other[k] = at[k] >= 0 ? __hip_atomic_exchange(slot + at[k], mine[k], __ATOMIC_RELAXED,
+                                                                  __HIP_MEMORY_SCOPE_AGENT)
+                                          : 0u;
+                }
+#pragma unroll
+                for (int k = 0; k < KMAX; k++) {
+                    if (at[k] < 0) continue;
+                    if (other[k] == 0u) {
+                        at[k] = -1;                      // first of the pair: the partner carries on
+                    } else {
+                        __hip_atomic_store(slot + at[k], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        v[k] = __builtin_bit_cast(float, mine[k]) + __builtin_bit_cast(float, other[k]);
+                    }
+                }
+            }
+            base += n >> 1;                              // pair slots used at this level
+            node >>= 1;
+            n = (n + 1) >> 1;
         }
     }
-    if (a.groups == 1) return;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's stores are acknowledged
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&a.count[(size_t)ctr * LW_COUNTER_STRIDE], 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        *last_flag = (old == (uint32_t)a.groups - 1u) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (!*last_flag) return;
-    // T threads per output (consecutive lanes of one wavefront)
-    const int per = (int)blockDim.x / (BATCH * ROWS);
-    const int T = per >= 8 ? 8 : per >= 4 ? 4 : per >= 2 ? 2 : 1;
-    const int q = threadIdx.x % T;
-    const size_t gstride = (size_t)LW_BATCH_MAX * a.rows;
-    for (int i = threadIdx.x / T; i < BATCH * ROWS; i += blockDim.x / T) {
-        const int b = i / ROWS, row = i % ROWS;
-        const bool ok = b < a.batch && row0 + row < a.rows;
-        const float *pp = &a.part[(size_t)(ok ? b : 0) * a.rows + (ok ? row0 + row : 0)];
-        const int ng = ok ? a.groups : 0;
-        float v = 0.f;
-        for (int g0 = q; g0 < ng; g0 += 16 * T) {
-            // only the loads this thread needs: a load per group, all in flight together
-            float t[16];
 #pragma unroll
-            for (int k = 0; k < 16; k++)
-                t[k] = g0 + k * T < ng ? __hip_atomic_load(pp + (size_t)(g0 + k * T) * gstride, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT)
-                                       : 0.f;
-#pragma unroll
-            for (int k = 0; k < 16; k++)
-                if (g0 + k * T < ng) v += t[k];
-        }
-        // the T sums of this output, in the same butterfly order in every lane
-        for (int o = 1; o < T; o <<= 1) v += __shfl_xor(v, o, 64);
-        if (ok && q == 0) a.y[(size_t)b * a.rows + row0 + row] = v;
-    }
-    if (threadIdx.x == 0)
-        __hip_atomic_store(&a.count[(size_t)ctr * LW_COUNTER_STRIDE], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int k = 0; k < KMAX; k++)
+        if (at[k] >= 0) a.y[at[k]] = v[k];
 }
 
 #endif

@@ -14,7 +14,7 @@
 #include "lw.h"
 
 #define LW_MAGIC 0x3142574Cu       /* "LWB1" */
-#define LW_VERSION 3u
+#define LW_VERSION 4u
 #define LW_MAXLEN 11               /* "LazyWeights", 2 . Code them: 11-bit codes */
 #define LW_TILE_ROWS 64            /* a 64x256 tile is 32 lanes of two rows */
 #define LW_TILE_COLS 256
@@ -128,18 +128,12 @@ static inline int32_t lw_work_groups(int64_t n_cb, int32_t parts)
     return (int32_t)((n_cb * parts + LW_CB_PER_WG - 1) / LW_CB_PER_WG);
 }
 
-/* workspace layout: partial sums [work_groups][LW_BATCH_MAX][rows] f32, then
- * one u32 arrival counter per row band (rows / 64), each on its own 256-byte
- * line (LW_COUNTER_STRIDE u32 apart), so that the read-modify-writes of
- * different row bands never queue on one line */
-#define LW_COUNTER_STRIDE 64
-static inline uint64_t lw_work_partial_bytes(int32_t groups, int64_t rows)
+/* workspace layout: the pair slots of the split-column reduction's exchange
+ * tree, [groups - 1][LW_BATCH_MAX][rows] f32 (combining G groups takes G - 1
+ * pair slots), all zero (empty) between calls */
+static inline uint64_t lw_work_bytes(int32_t groups, int64_t rows)
 {
-    return (uint64_t)groups * LW_BATCH_MAX * (uint64_t)rows * 4u;
-}
-static inline uint64_t lw_work_counter_bytes(int64_t n_rb)
-{
-    return (uint64_t)n_rb * LW_COUNTER_STRIDE * 4u;
+    return groups > 1 ? (uint64_t)(groups - 1) * LW_BATCH_MAX * (uint64_t)rows * 4u : 0u;
 }
 
 #endif

@@ -95,9 +95,7 @@ static KArgs make_args(const lw_dev_bundle *db)
     a.vb_bits = dev_region<uint32_t>(db, LW_REG_VB_BITS);
     a.vb_start = dev_region<uint32_t>(db, LW_REG_VB_START);
     a.verbatim = dev_region<uint16_t>(db, LW_REG_VERBATIM);
-    uint8_t *work = dev_region<uint8_t>(db, LW_REG_WORK);
-    a.part = reinterpret_cast<float *>(work);
-    a.count = work ? reinterpret_cast<uint32_t *>(work + lw_work_partial_bytes(db->h.work_groups, db->h.rows)) : nullptr;
+    a.part = dev_region<float>(db, LW_REG_WORK);
     a.rows = db->h.rows;
     a.cols = db->h.cols;
     a.n_rb = db->h.n_rb;
@@ -156,8 +154,8 @@ static lw_status require_regions(const lw_dev_bundle *db, int op, const char *wh
     return LW_OK;
 }
 
-// Launch the GEMV kernel of a bundle's kind and the batch; a.part and
-// a.count name the split-column reduction's scratch.
+// Launch the GEMV kernel of a bundle's kind and the batch; a.part names the
+// split-column reduction's pair slots.
 static lw_status gemv_launch(const lw_dev_bundle *db, KArgs &a, const void *x, float *y, int batch, hipStream_t s)
 {
     a.x = static_cast<const uint16_t *>(x);
@@ -186,21 +184,18 @@ extern "C" lw_status lw_gemv(const lw_dev_bundle *db, const void *x, float *y, i
 }
 
 // ------------------------------------------------ lw_gemv without a workspace
-// The split-column reduction's partial sums and arrival counters live in a
-// file-scope device array instead of the bundle's workspace region.  Each
-// device holds its own copy of the array; host code uses only the address
-// hipGetSymbolAddress returns for the current device (the array's name is a
-// host-side stand-in there), looked up once per device.
+// The split-column reduction's pair slots live in a file-scope device array
+// instead of the bundle's workspace region.  Each device holds its own copy
+// of the array; host code uses only the address hipGetSymbolAddress returns
+// for the current device (the array's name is a host-side stand-in there),
+// looked up once per device.  The slots must be empty (zero) when a call
+// starts: the array starts zeroed, and every call leaves each slot it used
+// empty again (both members of every pair always arrive), so no clearing
+// launch is needed.
 #define LW_NOALLOC_SCRATCH_BYTES (16u << 20)
 static __device__ __align__(256) uint8_t scratch[LW_NOALLOC_SCRATCH_BYTES];
 
 namespace {
-
-__global__ __launch_bounds__(256) void k_zero_u32(uint32_t *p, uint32_t n)
-{
-    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
-    if (i < n) p[i] = 0u;
-}
 
 struct DeviceScratch {
     std::once_flag once;
@@ -237,7 +232,7 @@ extern "C" lw_status lw_gemv_noalloc(const lw_dev_bundle *db, const void *x, flo
     if ((st = require_regions(db, LW_OP_GEMV, "lw_gemv_noalloc", 1u << LW_REG_WORK))) return st;
     KArgs a = make_args(db);
     hipStream_t s = (hipStream_t)stream;
-    const uint64_t need = db->h.bytes[LW_REG_WORK];   // partial sums + counters (0: no split reduction)
+    const uint64_t need = db->h.bytes[LW_REG_WORK];   // pair slots (0: no split reduction)
     if (need > LW_NOALLOC_SCRATCH_BYTES)
         return lw_fail(LW_E_UNSUPPORTED, "the split-column reduction of this bundle needs " + std::to_string(need) +
                                              " bytes of scratch, more than the " +
@@ -247,14 +242,7 @@ extern "C" lw_status lw_gemv_noalloc(const lw_dev_bundle *db, const void *x, flo
         uint8_t *sp = nullptr;
         hipError_t e = device_scratch(&sp);
         if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
-        const uint64_t pbytes = lw_work_partial_bytes(db->h.work_groups, db->h.rows);
         a.part = reinterpret_cast<float *>(sp);
-        a.count = reinterpret_cast<uint32_t *>(sp + pbytes);
-        // the arrival counters must start at zero: the array keeps the last call's contents
-        const uint32_t nctr = (uint32_t)((need - pbytes) / 4u);
-        hipLaunchKernelGGL(k_zero_u32, dim3((nctr + 255u) / 256u), dim3(256), 0, s, a.count, nctr);
-        e = hipGetLastError();
-        if (e != hipSuccess) return hip_fail(e, "scratch counter clear");
     }
     return gemv_launch(db, a, x, y, batch, s);
 }

@@ -258,22 +258,24 @@ void lw_dev_bundle_free(lw_dev_bundle *db);
  *   1 <= batch <= 16; batch >= 8 uses the matrix-core (MFMA) kernel.
  * The split-column reduction uses the bundle's workspace: calls on one
  * uploaded bundle must not overlap in time (use one stream per bundle).
- * Summation order is fixed, so results are deterministic.
+ * Results are deterministic: the column groups' sums meet pairwise in a
+ * fixed tree, and each pair's sum does not depend on which arrives first (an
+ * output whose sum is zero may be written as -0.0).
  * Errors: LW_E_ARG, LW_E_UNSUPPORTED, LW_E_DEVICE. */
 lw_status lw_gemv(const lw_dev_bundle *db, const void *x, float *y, int batch, void *stream);
 
 /* lw_gemv for callers that cannot allocate device memory or reserve a
  * workspace (code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation): the same kernels and results as lw_gemv, with the
- * split-column reduction's partial sums and arrival counters taken from a
- * scratch array the library holds per device (16 MiB, held until the process
- * ends) instead of the bundle's workspace region.  Nothing is allocated; the
- * counters are cleared by a small kernel on `stream` before the GEMV.
- * Calls that overlap in time on one device share that array and race: run
- * them on one stream, or order them.  Arguments as lw_gemv.
+ * split-column reduction's pair slots taken from a scratch array the library
+ * holds per device (16 MiB, zero at load, held until the process ends)
+ * instead of the bundle's workspace region.  Nothing is allocated and nothing
+ * is launched besides the GEMV: every call leaves the slots it used empty
+ * (zero) again.  Calls that overlap in time on one device share that array
+ * and race: run them on one stream, or order them.  Arguments as lw_gemv.
  * Errors: as lw_gemv; LW_E_UNSUPPORTED when the bundle's reduction needs more
- * scratch than 16 MiB (groups * 16 * rows * 4 bytes of partial sums plus the
- * counters; lw_bundle_info.region_bytes[LW_REG_WORK] gives it). */
+ * scratch than 16 MiB ((groups - 1) * 16 * rows * 4 bytes of pair slots;
+ * lw_bundle_info.region_bytes[LW_REG_WORK] gives it). */
 lw_status lw_gemv_noalloc(const lw_dev_bundle *db, const void *x, float *y, int batch, void *stream);
 
 /* Decode only: restore the fixed-width codes ("3 . Decode on demand": the unit

@@ -1,9 +1,9 @@
 """HIP graph capture of the C-ABI calls: a captured lw_gemv / lw_twin_gemv /
 lw_decode_only must give, on every replay, exactly what the eager call gives.
 
-The split-column reduction keeps arrival counters in the bundle's workspace
-and re-arms them inside the kernel (no memset node), so repeated replays are
-the case under test.  Between replays the program does its own eager work
+The split-column reduction meets in pair slots of the bundle's workspace and
+leaves them empty again inside the kernel (no memset node), so repeated
+replays are the case under test.  Between replays the program does its own eager work
 (other launches on the same bundle) and synchronises, as bench.py does.
 """
 import numpy as np

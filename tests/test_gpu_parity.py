@@ -331,6 +331,24 @@ def test_gemv_mfma_small(torch, dg, case, batch):
     assert np.array_equal(y, _run_gemv(dg, torch, db, x, batch, rows))
 
 
+
+# whole-row layouts of the matrix-core kernel (sixteen wavefronts a workgroup:
+# 128 row bands of 13 to 16 column blocks, bundles in one part)
+MFMA_WHOLE = [("q4", 8192, 3328, "normal", 311), ("q6", 8192, 4096, "laplace", 312)]
+
+
+@pytest.mark.parametrize("case", MFMA_WHOLE, ids=lambda c: "-".join(map(str, c)))
+def test_gemv_mfma_whole_rows(torch, dg, case):
+    kind_s, rows, cols, law, seed = case
+    kind = dg.LW_Q4_PAIR if kind_s == "q4" else dg.LW_Q6_SINGLE
+    codes, d, m, x = _gen_small(*case)
+    db = _upload(dg, torch, dg.lw_bundle_build_q_opts(kind, codes, d, m, parts=1))
+    for batch in (8, 16):
+        say("mfma whole rows", case, batch)
+        y = _run_gemv(dg, torch, db, x, batch, rows)
+        assert rel_err(y, gemv_q_all(codes, d, m, x, batch)) <= TOL
+        assert np.array_equal(y, _run_gemv(dg, torch, db, x, batch, rows))
+
 # ------------------------------------------------------------------ parts per tile row
 
 PARTS_Q = [

@@ -69,9 +69,9 @@ def test_noalloc_repeated_and_6bit(torch, dg):
 
 
 def test_noalloc_refuses_oversized_reduction(torch, dg):
-    # 4736 x 57344: 224 column blocks, 56 groups x 16 x 4736 rows x 4 B = 17 MB of
-    # partial sums, more than the 16 MiB array: refused before any launch
-    rows, cols = 4736, 57344
+    # 4800 x 57344: 224 column blocks, 56 groups, 55 pair slots x 16 x 4800 rows
+    # x 4 B = 16.9 MB, more than the 16 MiB array: refused before any launch
+    rows, cols = 4800, 57344
     codes = np.full((rows, cols), 8, np.uint8)
     d = np.full((rows, cols // 256), 0x2000, np.uint16)
     b = dg.lw_bundle_build_q(dg.LW_Q4_PAIR, codes, d, d)
