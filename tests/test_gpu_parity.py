@@ -202,7 +202,9 @@ def _q6_matrix(i):
 @pytest.mark.parametrize("i", [0, 1, 2], ids=["gate", "up", "down"])
 def test_full_size_q6(torch, dg, i):
     """Each 70B MLP matrix (gate and up 28672x8192, down 8192x28672): decode
-    bit-exact and every GEMV row against the oracle."""
+    bit-exact and every GEMV row against the oracle, at batch 1 and at batch
+    16 (the matrix-core kernel, whose column groups -- 8 for gate and up, 28
+    for down -- meet in a three- or five-level exchange tree)."""
     mat = synth.WORKLOADS["q6_mlp_70b"][i]
     say("full", mat.name)
     codes, d, m, x = _q6_matrix(i)
@@ -212,8 +214,10 @@ def test_full_size_q6(torch, dg, i):
     q, _ = _decode_q(dg, torch, db, dg.LW_Q6_SINGLE, mat.rows, mat.cols, info["n_tiles"])
     assert np.array_equal(q, codes)
     del q
-    y = _run_gemv(dg, torch, db, x, 1, mat.rows)
-    assert rel_err(y, gemv_q_all(codes, d, m, x, 1)) <= TOL
+    for batch in (1, 16):
+        say("full gemv", mat.name, batch)
+        y = _run_gemv(dg, torch, db, x, batch, mat.rows)
+        assert rel_err(y, gemv_q_all(codes, d, m, x, batch)) <= TOL
 
 
 def test_full_size_mlp_pass_70b(torch, dg):
