@@ -4,23 +4,23 @@
 // "Unweight", section "How reconstructive matmul works").
 //
 // At batch >= 8 the product is a real dense contraction, and a lane's decoded
-// group is already a matrix-core operand.  Lane l + 32*half decodes tile row
-// 2l + half (one wavefront per part of a tile, as in fused_q.hip); after a
-// group of four symbols it holds that row's weights at K consecutive columns
-// (K = 8 for 4-bit pairs, 4 for 6-bit codes and bf16 exponents), which is
-// exactly its B operand of v_mfma_f32_32x32x{16,8} for B[k][n], n = l,
-// k = K*half + e.  The activations go in as a block-diagonal A:
-//   A[2b + h][K*h' + e] = x[b][col + e] when h == h', else 0,
+// weights are already a matrix-core operand.  Lane l + 32*half decodes tile
+// row 2l + half (one wavefront per part of a tile, as in fused_q.hip); after
+// one group of four symbols (4-bit pairs) or two (6-bit codes, bf16
+// exponents) it holds that row's weights at 8 consecutive columns, which is
+// exactly its B operand of v_mfma_f32_32x32x16_{f16,bf16} for B[k][n], n = l,
+// k = 8*half + e.  The activations go in as a block-diagonal A:
+//   A[2b + h][8h' + e] = x[b][col + e] when h == h', else 0,
 // so D[2b + h][n] accumulates x[b] . W[row 2n + h]: batch row b against both
-// rows of the lane pair.  One matrix instruction per group replaces any
+// rows of the lane pair.  One matrix instruction per 8 columns replaces any
 // staging of the decoded weights through LDS; half of A is zero, which the
-// matrix cores absorb (a 32x32x16 a group is about a tenth of the SIMD's
-// issue time for decoding that group).  Each lane fetches its A fragments
-// straight from global memory, 16 bytes a load (one 4-bit group's, two of
-// the others'), three or four groups ahead (lanes off the diagonal, and batch
-// rows past the call's batch, read a line of zeros).
-// MFMA 32x32 lane layout: A lane i = A[i%32][K(i/32) ..], B lane i =
-// B[K(i/32) ..][i%32], D lane i register j = D[8(j/4) + 4(i/32) + j%4][i%32].
+// matrix cores absorb (a 32x32x16 per 8 columns is about a tenth of the
+// SIMD's issue time for decoding them).  Each lane fetches its A fragments
+// straight from global memory, 16 bytes (8 columns) a load, three or four
+// groups ahead (lanes off the diagonal, and batch rows past the call's batch,
+// read a line of zeros).
+// MFMA 32x32x16 lane layout: A lane i = A[i%32][8(i/32) ..], B lane i =
+// B[8(i/32) ..][i%32], D lane i register j = D[8(j/4) + 4(i/32) + j%4][i%32].
 //
 // Dequantisation (4- and 6-bit) uses y = d * (W q x) - m * sum(x) per tile
 // row; the activation sums come from the A fragments as they pass (4-bit) or
@@ -41,9 +41,8 @@ constexpr int WAVES = 4;
 constexpr int NB = 16;                     // batch rows of the matrix-core tile
 constexpr int RED_RS = 65;                 // floats per (wavefront, batch) run of the partial sums
 
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef short s4 __attribute__((ext_vector_type(4)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f16x __attribute__((ext_vector_type(16)));   // one lane's 32x32 accumulator block
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -52,23 +51,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // row's columns, 512 bytes, never written.
 __device__ __attribute__((aligned(16))) uint32_t lw_zero_x[128] = {};
 
-// D += A B: 32x32x16 on 16-byte fragments (4-bit pairs), 32x32x8 on 8-byte
-// ones (6-bit codes in fp16, bf16 weights)
+// D += A B on 16-byte fragments: eight columns of fp16 (4- and 6-bit codes)
+// or bf16 weights
 template <int KIND>
 LW_DEV f16x mfma32(u32x4 a, u32x4 b, f16x acc)
 {
-    static_assert(KIND == LW_Q4_PAIR, "16-byte fragments carry 4-bit pairs");
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), acc, 0, 0, 0);
-}
-
-template <int KIND>
-LW_DEV f16x mfma32(u32x2 a, u32x2 b, f16x acc)
-{
     if constexpr (KIND == LW_BF16_EXP)
-        return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b), acc, 0, 0,
-                                                         0);
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), acc, 0, 0, 0);
     else
-        return __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4, a), __builtin_bit_cast(h4, b), acc, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), acc, 0, 0, 0);
 }
 
 struct LdsLayout {
@@ -118,10 +109,9 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_mfma(KArgs a)
     static_assert(WPG % P == 0, "whole tiles per workgroup");
     static_assert(P == 1 || KIND != LW_BF16_EXP, "bf16 tiles are decoded in whole rows");
     constexpr bool Q4 = KIND == LW_Q4_PAIR, BF = KIND == LW_BF16_EXP;
-    typedef typename std::conditional<Q4, u32x4, u32x2>::type frag;   // one group's operand fragment
     constexpr int NG = (Q4 ? 32 : 64) / P;   // groups of four symbols per part of a tile row
     constexpr int PCOLS = 256 / P;           // columns per part
-    constexpr int GPL = Q4 ? 1 : 2;          // groups per 16-byte activation load
+    constexpr int GPL = Q4 ? 1 : 2;          // groups per matrix instruction and per 16-byte activation load
     constexpr int NL = NG / GPL;             // activation loads per part
     constexpr int DIST = Q4 ? 3 : 2;         // loads between an A fragment's load and its first use
     const LdsLayout L = lds_layout(a.max_words, WPG, P);
@@ -195,59 +185,60 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_mfma(KArgs a)
             u32x4 xr[DIST + 1];           // ring of activation loads, indexed by load (a compile-time constant)
 #pragma unroll
             for (int q = 0; q < DIST; q++) xr[q] = xp[q];
-            uint32_t gw[4];               // the group's weights, two 16-bit ones per word
-            // A group's weights and its A fragment into the matrix cores.
+            uint32_t gw[4];               // eight columns' weights, two 16-bit ones per word
+            // A group's weights into the B fragment; after the last group of
+            // a fragment (every group for Q4, every second one for Q6 and
+            // bf16), the matrix instruction with its A fragment.
             // pay: the symbol's payload (Q4 a pair of fp16 codes; Q6 one
             // fp16 code, in the low half for even symbols and the high half
             // for odd ones; bf16 the exponent bits, placed likewise); smw:
             // bf16 sign+mantissa bytes of the group's four columns.
-            auto put = [&](int j, uint32_t pay, uint32_t smw, const frag &xv) {
+            auto put = [&](int g, int j, uint32_t pay, uint32_t smw, const u32x4 &xv) {
                 if constexpr (Q4) {
                     gw[j] = pay;
-                } else if constexpr (BF) {
-                    if (j & 1) {
-                        const uint32_t spread = __builtin_amdgcn_perm(smw, smw, j == 1 ? 0x01010000u : 0x03030202u);
-                        gw[j >> 1] = (spread & 0x807F807Fu) | gw[j >> 1] | pay;
-                    } else {
-                        gw[j >> 1] = pay;
-                    }
                 } else {
-                    if (j & 1) gw[j >> 1] |= pay;
-                    else gw[j >> 1] = pay;
+                    const int w = 2 * (g & 1) + (j >> 1);
+                    if constexpr (BF) {
+                        if (j & 1) {
+                            const uint32_t spread = __builtin_amdgcn_perm(smw, smw, j == 1 ? 0x01010000u : 0x03030202u);
+                            gw[w] = (spread & 0x807F807Fu) | gw[w] | pay;
+                        } else {
+                            gw[w] = pay;
+                        }
+                    } else {
+                        if (j & 1) gw[w] |= pay;
+                        else gw[w] = pay;
+                    }
                 }
-                if (j == 3) {
+                if (j == 3 && g % GPL == GPL - 1) {
+                    acc = mfma32<KIND>(xv, u32x4{gw[0], gw[1], gw[2], gw[3]}, acc);
                     if constexpr (Q4) {
-                        acc = mfma32<KIND>(xv, u32x4{gw[0], gw[1], gw[2], gw[3]}, acc);
 #pragma unroll
                         for (int w = 0; w < 4; w++) sxq = lw_dot2(xv[w], 0x3C003C00u, sxq);
-                    } else {
-                        acc = mfma32<KIND>(xv, u32x2{gw[0], gw[1]}, acc);
                     }
                 }
             };
             // the A fragment of group g (loaded DIST loads earlier); at the
             // first group of a load, issues the load DIST further on
-            auto next_x = [&](int g) -> frag {
+            auto next_x = [&](int g) -> u32x4 {
                 lw_ramp<NG>(a.ramp, g);
                 const int q = g / GPL;
                 if (g % GPL == 0 && q + DIST < NL) xr[(q + DIST) % (DIST + 1)] = xp[q + DIST];
-                const u32x4 v = xr[q % (DIST + 1)];
-                if constexpr (Q4) return v;
-                else return (g & 1) ? u32x2{v.z, v.w} : u32x2{v.x, v.y};
+                return xr[q % (DIST + 1)];
             };
             auto pay_off = [](int j) { return (!Q4 && (j & 1)) ? (LW_TPAY_HI - LW_TPAY) : 0u; };
             if constexpr (BF) {
                 // sign+mantissa words stream in 16-group chunks, as in the VALU kernel
                 const uint32_t *smrow = a.sm + (size_t)c.t * 4096 + (size_t)c.half * 64 * 32 + c.l;
                 struct XA {
-                    frag x;
+                    u32x4 x;
                     uint32_t sm;
                 };
                 uint32_t ring[2][16];
                 auto run_chunk = [&](int ch, const uint32_t (&cur)[16]) {
                     lw_decode_pipelined<PLAN, 16, XA, true>(
                         d, a, pay_off, [&](int g) { return XA{next_x(16 * ch + g), cur[g]}; },
-                        [&](int, int j, uint32_t pay, const XA &x) { put(j, pay, x.sm, x.x); });
+                        [&](int g, int j, uint32_t pay, const XA &x) { put(16 * ch + g, j, pay, x.sm, x.x); });
                 };
 #pragma unroll
                 for (int i = 0; i < 16; i++) ring[0][i] = smrow[i * 32];
@@ -263,11 +254,11 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_mfma(KArgs a)
                 }
             } else {
                 struct XA {
-                    frag x;
+                    u32x4 x;
                 };
                 lw_decode_pipelined<PLAN, NG, XA, true>(
                     d, a, pay_off, [&](int g) { return XA{next_x(g)}; },
-                    [&](int, int j, uint32_t pay, const XA &x) { put(j, pay, 0u, x.x); });
+                    [&](int g, int j, uint32_t pay, const XA &x) { put(g, j, pay, 0u, x.x); });
             }
         } else {                           // unusable LDS base: poison the output
 #pragma unroll
