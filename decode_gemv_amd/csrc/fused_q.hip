@@ -216,6 +216,145 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
 }
 
 
+// Balanced layout (bundles in parts, batch 1..4).  With U = 4K + 2 tiles per
+// CU (14336x4096 and 4096x14336 on 256 CUs: 3584 tiles, U = 14), whole
+// tiles give some SIMDs K + 1 tiles of work and others K.  Here one
+// workgroup per CU takes U consecutive tiles in row-major order with 4K + 4
+// wavefronts: wavefronts 0 .. 4K-1 decode tiles 0 .. 4K-1 whole, and
+// wavefronts 4K .. 4K+3 decode the two halves (recorded parts) of tiles 4K
+// and 4K+1.  A workgroup's wavefronts w, w+4, w+8, ... share a SIMD, so every
+// SIMD gets K + 1/2 tiles.  Every wavefront stages its tile in its own slot
+// after the table barrier, as in the whole-row layout, so it starts decoding
+// when its own tile is in (one shared staging would need a barrier after the
+// slowest tile of the workgroup); the second request of a split tile's lines
+// is served by the CU's L2.  A workgroup's tiles span at most two row bands (U <= the
+// column blocks); each row band's sums meet those of the other workgroups
+// holding its tiles in the exchange tree (leaf = workgroup - the band's
+// first workgroup).
+__host__ __device__ inline LdsLayout lds_layout_bal(int batch, int max_words, int waves, int tiles_per_wg)
+{
+    LdsLayout L;
+    L.x = LW_TAB_BYTES;
+    L.tiles = L.x + (uint32_t)(waves * batch * 128 * 4);
+    const uint32_t tiles = (uint32_t)(tiles_per_wg * (max_words + 3) * 128);
+    const uint32_t red = (uint32_t)(waves * batch * 64 * 4);
+    L.total = L.tiles + (tiles > red ? tiles : red);
+    return L;
+}
+
+template <int KIND, int PLAN, int BATCH, int K>
+__global__ __launch_bounds__(64 * (4 * K + 4)) void k_gemv_bal(KArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr int WPG = 4 * K + 4, U = 4 * K + 2;   // wavefronts and tiles of a workgroup
+    constexpr int SPL = KIND == LW_Q4_PAIR ? 256 : 512;
+    constexpr int NG = SPL / 8;           // groups of four symbols per tile row (half tiles: NG / 2)
+    const LdsLayout L = lds_layout_bal(BATCH, a.max_words, WPG, WPG);
+    const int wave = (int)lw_wave_id(), lane = threadIdx.x & 63, half = lane >> 5, l = lane & 31;
+    const bool split = wave >= 4 * K;     // a half-tile wavefront
+    const int j = split ? 4 * K + ((wave - 4 * K) >> 1) : wave;   // tile slot within the workgroup
+    const int p = split ? ((wave - 4 * K) & 1) : 0;                  // half of the tile row
+    const int64_t T0 = (int64_t)blockIdx.x * U;                      // the workgroup's first tile
+    const int64_t t = T0 + j;             // tiles are in row-major order: t = rb * n_cb + cb
+    const int rb = (int)(t / a.n_cb), cb = (int)(t % a.n_cb);
+    const int S = a.max_words + 3;
+    const uint32_t xs_addr = (uint32_t)(size_t)(lds + L.x) + 4u * (uint32_t)(wave * BATCH * 128);
+    uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + wave * S * 32;
+
+    // Issue every global load first (as in k_gemv_q); the tile loads go out
+    // after the table barrier, as in the sixteen-wavefront whole-row layout.
+    const uint32_t w0 = a.tile_off[t], w1 = a.tile_off[t + 1];
+    const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, false);
+    const uint32_t dm = a.dm[(size_t)t * 64 + 2 * l + half];
+    const uint32_t start = lw_part_start(a, t, l, half * a.parts + p * (a.parts / 2));
+    uint32_t xv[BATCH][2];
+    const uint32_t *xg = reinterpret_cast<const uint32_t *>(a.x) + (size_t)cb * 128;
+#pragma unroll
+    for (int b = 0; b < BATCH; b++) {
+        xv[b][0] = xg[(size_t)b * (a.cols / 2) + lane];
+        xv[b][1] = xg[(size_t)b * (a.cols / 2) + lane + 64];
+    }
+    lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
+    __syncthreads();                      // the decoder table is complete
+    LwTileRegs64 tile;
+    lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, lane, tile);
+#pragma unroll
+    for (int b = 0; b < BATCH; b++) {
+        *(lw_lds_w32 *)(size_t)(xs_addr + 4u * (b * 128 + lane)) = xv[b][0];
+        *(lw_lds_w32 *)(size_t)(xs_addr + 4u * (b * 128 + lane + 64)) = xv[b][1];
+    }
+    lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, lane, tile);
+
+    float acc[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; b++) acc[b] = 0.f;
+    {
+        LaneDec d;
+        const bool ok = lw_lane_init(d, lds, slots, l, a);
+        d.advance(start);
+        const int g0 = p * (NG / 2);      // first group of this wavefront's columns
+        if (ok) {
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            struct XA {
+                u32x4 v[BATCH];
+            };
+            auto fetch_x = [&](int g) {
+                XA r;
+#pragma unroll
+                for (int b = 0; b < BATCH; b++) {
+                    if constexpr (KIND == LW_Q4_PAIR) {
+                        const uint32_t ad = xs_addr + (uint32_t)(b * 512 + 16 * (g0 + g));
+                        r.v[b] = *(__attribute__((address_space(3))) const u32x4 *)(size_t)ad;
+                    } else {
+                        const uint32_t ad = xs_addr + (uint32_t)(b * 512 + 8 * (g0 + g));
+                        const u32x2 t2 = *(__attribute__((address_space(3))) const u32x2 *)(size_t)ad;
+                        r.v[b] = u32x4{t2.x, t2.y, 0u, 0u};
+                    }
+                }
+                return r;
+            };
+            auto use = [&](int, int jj, uint32_t pay, const XA &x) {
+#pragma unroll
+                for (int b = 0; b < BATCH; b++) {
+                    uint32_t xp;
+                    if constexpr (KIND == LW_Q4_PAIR)
+                        xp = jj == 0 ? x.v[b].x : jj == 1 ? x.v[b].y : jj == 2 ? x.v[b].z : x.v[b].w;
+                    else
+                        xp = jj < 2 ? x.v[b].x : x.v[b].y;
+                    acc[b] = lw_dot2(pay, xp, acc[b]);
+                }
+            };
+            auto pay_off = [](int jj) { return (KIND != LW_Q4_PAIR && (jj & 1)) ? (LW_TPAY_HI - LW_TPAY) : 0u; };
+            if (split)
+                lw_decode_pipelined<PLAN, NG / 2, XA, true>(
+                    d, a, pay_off, [&](int g) { lw_ramp<NG / 2>(a.ramp, g); return fetch_x(g); }, use);
+            else
+                lw_decode_pipelined<PLAN, NG, XA, true>(
+                    d, a, pay_off, [&](int g) { lw_ramp<NG>(a.ramp, g); return fetch_x(g); }, use);
+        } else {                           // unusable LDS base: poison the output
+#pragma unroll
+            for (int b = 0; b < BATCH; b++) acc[b] = __builtin_nanf("");
+        }
+    }
+
+    // dequantise over this wavefront's columns (lane i holds the column pairs i and i + 64)
+    const bool in0 = !split || p == 0, in1 = !split || p == 1;
+    float sx[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; b++)
+        sx[b] = lw_wave_sum((in0 ? lw_half_lo(xv[b][0]) + lw_half_hi(xv[b][0]) : 0.f) +
+                            (in1 ? lw_half_lo(xv[b][1]) + lw_half_hi(xv[b][1]) : 0.f));
+    __syncthreads();                      // tiles no longer read: reuse for the partial sums
+    float *red = reinterpret_cast<float *>(lds + L.tiles);
+#pragma unroll
+    for (int b = 0; b < BATCH; b++)
+        red[(wave * BATCH + b) * 64 + 2 * l + half] = lw_half_lo(dm) * acc[b] - lw_half_hi(dm) * sx[b];
+    __syncthreads();
+
+    lw_finish_balanced<BATCH, 64, K>(a, red);
+}
+
 // Decode only: restore the fixed-width codes (Q4 packed nibbles, Q6 bytes).
 template <int KIND, int PLAN>
 __global__ __launch_bounds__(256) void k_decode_q(KArgs a)
@@ -299,8 +438,45 @@ hipError_t launch_gemv_wpg(const KArgs &a0, hipStream_t s)
     return hipGetLastError();
 }
 
-// Bundles in parts (matrices of up to 2048 tiles) decode every recorded part
-// in eight-wavefront workgroups (measured best at 16 to 2048 tiles).  In whole
+template <int KIND, int PLAN, int BATCH, int K>
+hipError_t launch_gemv_bal(const KArgs &a0, hipStream_t s)
+{
+    KArgs a = a0;
+    constexpr int WPG = 4 * K + 4;
+    a.ramp = 1;                           // one workgroup per CU: the whole grid is resident
+    const LdsLayout L = lds_layout_bal(BATCH, a.max_words, WPG, WPG);
+    auto kern = k_gemv_bal<KIND, PLAN, BATCH, K>;
+    hipError_t e = lw_allow_lds<k_gemv_bal<KIND, PLAN, BATCH, K>>();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)a.n_rb * a.n_cb / (4 * K + 2))), dim3(64 * WPG), L.total, s, a);
+    return hipGetLastError();
+}
+
+// The balanced layout applies when the tiles are U = 4K + 2 per CU (K = 1..3),
+// the bundle records half-row starts (parts >= 2), a workgroup's tiles span
+// at most two row bands, the staged tiles fit in LDS and the workspace holds
+// the widest band's tree.  Returns hipErrorNotSupported otherwise.
+template <int KIND, int PLAN, int BATCH>
+hipError_t try_gemv_bal(const KArgs &a, hipStream_t s)
+{
+    const int cus = lw_device_cu_count();
+    const int64_t tiles = (int64_t)a.n_rb * a.n_cb;
+    if (cus <= 0 || a.parts < 2 || tiles % cus) return hipErrorNotSupported;
+    const int64_t U = tiles / cus;
+    if (U % 4 != 2 || U < 6 || U > 14 || a.n_cb < U) return hipErrorNotSupported;
+    if (lds_layout_bal(BATCH, a.max_words, (int)U + 2, (int)U + 2).total > (uint32_t)lw_device_lds_bytes())
+        return hipErrorNotSupported;
+    if ((a.n_cb + U - 1) / U + 1 > lw_work_groups(a.n_cb, a.parts)) return hipErrorNotSupported;
+    if (U == 6) return launch_gemv_bal<KIND, PLAN, BATCH, 1>(a, s);
+    if (U == 10) return launch_gemv_bal<KIND, PLAN, BATCH, 2>(a, s);
+    return launch_gemv_bal<KIND, PLAN, BATCH, 3>(a, s);
+}
+
+// At batch 1..4 the balanced layout goes first where it applies (bundles in
+// parts with 4K + 2 tiles per CU; 4096x14336: 19.2 against 20.4-20.8 us in
+// fourteen-wavefront groups).  Bundles in parts for their size (up to 2048
+// tiles) decode every recorded part in eight-wavefront workgroups (measured
+// best at 16 to 2048 tiles); other bundles are decoded in whole rows.  In whole
 // rows: 16 wavefronts, no cross-workgroup reduction, when a row band has
 // 13..16 column blocks, the tiles fit in LDS and there are at least 128 row
 // bands (fewer leave most CUs idle: 1024x4096 takes 16.1 us so, 9.9 us in
@@ -313,11 +489,18 @@ template <int KIND, int PLAN, int BATCH>
 hipError_t launch_gemv_q(const KArgs &a, hipStream_t s)
 {
     const uint32_t lds = (uint32_t)lw_device_lds_bytes();
-    if (a.parts == 2 && lds_layout(BATCH, a.max_words, false, 8, 2).total <= lds)
+    if constexpr (BATCH <= 4) {
+        const hipError_t e = try_gemv_bal<KIND, PLAN, BATCH>(a, s);
+        if (e != hipErrorNotSupported) return e;
+    }
+    // the eight-wavefront part layouts serve the bundles the part rule puts
+    // in parts for their size (tiles x parts within LW_PART_UNITS)
+    const bool small = (int64_t)a.n_rb * a.n_cb * a.parts <= LW_PART_UNITS;
+    if (small && a.parts == 2 && lds_layout(BATCH, a.max_words, false, 8, 2).total <= lds)
         return launch_gemv_wpg<KIND, PLAN, BATCH, 8, 2>(a, s);
-    if (a.parts == 4 && lds_layout(BATCH, a.max_words, false, 8, 4).total <= lds)
+    if (small && a.parts == 4 && lds_layout(BATCH, a.max_words, false, 8, 4).total <= lds)
         return launch_gemv_wpg<KIND, PLAN, BATCH, 8, 4>(a, s);
-    if (a.parts == 8 && lds_layout(BATCH, a.max_words, false, 8, 8).total <= lds)
+    if (small && a.parts == 8 && lds_layout(BATCH, a.max_words, false, 8, 8).total <= lds)
         return launch_gemv_wpg<KIND, PLAN, BATCH, 8, 8>(a, s);
     if constexpr (BATCH <= 4) {
         if (a.n_cb > 12 && a.n_cb <= 16 && a.n_rb >= 128 && lds_layout(BATCH, a.max_words, false, 16).total <= lds)

@@ -573,6 +573,47 @@ LW_DEV bool lw_lane_init(LaneDec &d, uint8_t *lds, const uint32_t *slots, int l,
 // those of +0.0), so an output whose sum is zero may be written as -0.0.
 // A thread's outputs (at most KMAX) go up the tree together, their exchanges
 // in flight at once: ceil(log2(groups)) round trips to the coherence point.
+// The exchange tree of the split-column reduction (see lw_finish_rows): this
+// thread's outputs v[k] (at their indices at[k] in y, -1 for none) enter as
+// leaf `node` of a tree over n leaves and go up level by level, their
+// exchanges in flight at once.  On return at[k] is -1 where this thread
+// arrived first at some pair (its partner carries the sum on); the outputs
+// left in at[] hold their complete sums.
+template <int KMAX>
+LW_DEV void lw_tree_combine(const KArgs &a, int node, int n, float (&v)[KMAX], int64_t (&at)[KMAX])
+{
+    uint32_t *slots = reinterpret_cast<uint32_t *>(a.part);
+    const size_t stride = (size_t)LW_BATCH_MAX * (size_t)a.rows;   // one slot: [LW_BATCH_MAX][rows]
+    int base = 0;
+    while (n > 1) {
+        if ((node ^ 1) < n) {
+            uint32_t *slot = slots + (size_t)(base + (node >> 1)) * stride;
+            uint32_t mine[KMAX], other[KMAX];
+#pragma unroll
+            for (int k = 0; k < KMAX; k++) {
+                mine[k] = __builtin_bit_cast(uint32_t, v[k]);
+                if (mine[k] == 0u) mine[k] = 0x80000000u;
+                other[k] = at[k] >= 0 ? __hip_atomic_exchange(slot + at[k], mine[k], __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT)
+                                      : 0u;
+            }
+#pragma unroll
+            for (int k = 0; k < KMAX; k++) {
+                if (at[k] < 0) continue;
+                if (other[k] == 0u) {
+                    at[k] = -1;                          // first of the pair: the partner carries on
+                } else {
+                    __hip_atomic_store(slot + at[k], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    v[k] = __builtin_bit_cast(float, mine[k]) + __builtin_bit_cast(float, other[k]);
+                }
+            }
+        }
+        base += n >> 1;                                  // pair slots used at this level
+        node >>= 1;
+        n = (n + 1) >> 1;
+    }
+}
+
 template <int BATCH, int ROWS = 128, int RS = ROWS>
 LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g, int waves)
 {
@@ -590,37 +631,55 @@ LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g
         v[k] = s;
         at[k] = ok ? (int64_t)b * a.rows + row0 + row : -1;
     }
-    if (a.groups > 1) {
-        uint32_t *slots = reinterpret_cast<uint32_t *>(a.part);
-        const size_t stride = (size_t)LW_BATCH_MAX * (size_t)a.rows;   // one slot: [LW_BATCH_MAX][rows]
-        int node = g, n = a.groups, base = 0;
-        while (n > 1) {                                  // the same steps in every thread of the workgroup
-            if ((node ^ 1) < n) {
-                uint32_t *slot = slots + (size_t)(base + (node >> 1)) * stride;
-                uint32_t mine[KMAX], other[KMAX];
+    if (a.groups > 1) lw_tree_combine<KMAX>(a, g, a.groups, v, at);
 #pragma unroll
-                for (int k = 0; k < KMAX; k++) {
-                    mine[k] = __builtin_bit_cast(uint32_t, v[k]);
-                    if (mine[k] == 0u) mine[k] = 0x80000000u;
-                    other[k] = at[k] >= 0 ? __hip_atomic_exchange(slot + at[k], mine[k], __ATOMIC_RELAXED,
-                                                                  __HIP_MEMORY_SCOPE_AGENT)
-                                          : 0u;
-                }
+    for (int k = 0; k < KMAX; k++)
+        if (at[k] >= 0) a.y[at[k]] = v[k];
+}
+
+// Finish of the balanced layouts (fused_q.hip, mfma.hip): workgroup k holds
+// tiles [kU, kU + U) in row-major order, U = 4K + 2, with wavefronts 0 ..
+// 4K-1 on tiles 0 .. 4K-1 and wavefronts 4K + i on tile 4K + i/2.  Its tiles
+// cover row band rb0 from slot 0 and, when the band ends inside, band rb0 + 1
+// from slot jb.  Each (band, batch row, row) output sums red[wave][b][row]
+// (RS floats between (wave, b) runs) over the band's wavefronts in wavefront
+// order, then meets the other workgroups holding the band's tiles in the
+// exchange tree (leaf = k - the band's first workgroup).  A thread's KMAX
+// outputs are consecutive, so they share a band.
+template <int BATCH, int RS, int K>
+LW_DEV void lw_finish_balanced(const KArgs &a, const float *red)
+{
+    constexpr int U = 4 * K + 2, WPG = 4 * K + 4, NOUT = 2 * BATCH * 64;
+    constexpr int KMIN = (NOUT + 64 * WPG - 1) / (64 * WPG);   // outputs per thread, rounded up to a power of two
+    constexpr int KMAX = KMIN <= 1 ? 1 : KMIN <= 2 ? 2 : KMIN <= 4 ? 4 : 8;
+    static_assert((BATCH * 64) % KMAX == 0 && 64 * WPG * KMAX >= NOUT, "a thread's outputs share a band");
+    const int64_t T0 = (int64_t)blockIdx.x * U;
+    const int rb0 = (int)(T0 / a.n_cb);
+    const int jb = (int)((int64_t)(rb0 + 1) * a.n_cb - T0);   // first slot of the next band (>= U: none)
+    const int s = (int)(threadIdx.x * KMAX) / (BATCH * 64);   // band of this thread's outputs: rb0 + s
+    const int band = rb0 + s;
+    float v[KMAX];
+    int64_t at[KMAX];
+    bool any = false;
 #pragma unroll
-                for (int k = 0; k < KMAX; k++) {
-                    if (at[k] < 0) continue;
-                    if (other[k] == 0u) {
-                        at[k] = -1;                      // first of the pair: the partner carries on
-                    } else {
-                        __hip_atomic_store(slot + at[k], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        v[k] = __builtin_bit_cast(float, mine[k]) + __builtin_bit_cast(float, other[k]);
-                    }
-                }
+    for (int k = 0; k < KMAX; k++) {
+        const int i = (int)threadIdx.x * KMAX + k;
+        const int b = (i / 64) % BATCH, r = i % 64;
+        const bool ok = i < NOUT && b < a.batch && (s == 0 || jb < U) && band < a.n_rb;
+        float sum = 0.f;
+        if (ok)
+            for (int w = 0; w < WPG; w++) {
+                const int jw = w < 4 * K ? w : 4 * K + ((w - 4 * K) >> 1);
+                if ((jw >= jb) == (s == 1)) sum += red[(w * BATCH + b) * RS + r];
             }
-            base += n >> 1;                              // pair slots used at this level
-            node >>= 1;
-            n = (n + 1) >> 1;
-        }
+        v[k] = sum;
+        at[k] = ok ? (int64_t)b * a.rows + (int64_t)band * 64 + r : -1;
+        any = any || ok;
+    }
+    if (any) {
+        // the workgroups holding this band's tiles
+        const int64_t f = (int64_t)band * a.n_cb / U, e = ((int64_t)band * a.n_cb + a.n_cb - 1) / U;
+        if (e > f) lw_tree_combine<KMAX>(a, (int)(blockIdx.x - f), (int)(e - f + 1), v, at);
     }
 #pragma unroll
     for (int k = 0; k < KMAX; k++)

@@ -30,7 +30,9 @@
 // kernel.  Workgroups have the VALU kernel's shapes: eight wavefronts on
 // bundles in parts, sixteen (whole rows) for 13 to 16 column blocks and at
 // least 128 row bands, fourteen when the column blocks are a multiple of 14
-// and the whole grid is resident at once, else four.
+// and the whole grid is resident at once, else four (a balanced layout as in
+// fused_q.hip measured no faster at batch 8 and 16: 24.7-25.0 against 25.0 us
+// on 4096x14336).
 #include <type_traits>
 
 #include "lane_decode.hpp"
@@ -325,9 +327,12 @@ hipError_t launch(const KArgs &a, hipStream_t s)
 {
     const uint32_t lds = (uint32_t)lw_device_lds_bytes();
     if constexpr (KIND != LW_BF16_EXP) {
-        if (a.parts == 2 && lds_layout(a.max_words, 8, 2).total <= lds) return launch_wpg<KIND, PLAN, 8, 2>(a, s);
-        if (a.parts == 4 && lds_layout(a.max_words, 8, 4).total <= lds) return launch_wpg<KIND, PLAN, 8, 4>(a, s);
-        if (a.parts == 8 && lds_layout(a.max_words, 8, 8).total <= lds) return launch_wpg<KIND, PLAN, 8, 8>(a, s);
+        // part layouts for the bundles in parts for their size, as the VALU kernel
+        if ((int64_t)a.n_rb * a.n_cb * a.parts <= LW_PART_UNITS) {
+            if (a.parts == 2 && lds_layout(a.max_words, 8, 2).total <= lds) return launch_wpg<KIND, PLAN, 8, 2>(a, s);
+            if (a.parts == 4 && lds_layout(a.max_words, 8, 4).total <= lds) return launch_wpg<KIND, PLAN, 8, 4>(a, s);
+            if (a.parts == 8 && lds_layout(a.max_words, 8, 8).total <= lds) return launch_wpg<KIND, PLAN, 8, 8>(a, s);
+        }
     }
     if (a.n_cb > 12 && a.n_cb <= 16 && a.n_rb >= 128 && lds_layout(a.max_words, 16, 1).total <= lds)
         return launch_wpg<KIND, PLAN, 16, 1>(a, s);

@@ -353,6 +353,27 @@ def test_gemv_mfma_whole_rows(torch, dg, case):
         assert rel_err(y, gemv_q_all(codes, d, m, x, batch)) <= TOL
         assert np.array_equal(y, _run_gemv(dg, torch, db, x, batch, rows))
 
+
+# balanced layout: 3584 tiles (14 per CU on 256 CUs), bundles in two parts --
+# whole tiles on twelve wavefronts of a CU and tile halves on four, each row
+# band meeting the other workgroups holding its tiles; batch 1..4 on the
+# VALU kernel, and 8 and 16 on the matrix cores' whole-row layouts over the
+# same two-part bundles
+BALANCED = [("q4", 14336, 4096, "normal", 321), ("q4", 4096, 14336, "laplace", 322), ("q6", 4096, 14336, "normal", 323)]
+
+
+@pytest.mark.parametrize("case", BALANCED, ids=lambda c: "-".join(map(str, c)))
+def test_gemv_balanced_layout(torch, dg, case):
+    kind_s, rows, cols, law, seed = case
+    kind = dg.LW_Q4_PAIR if kind_s == "q4" else dg.LW_Q6_SINGLE
+    codes, d, m, x = _gen_small(*case)
+    db = _upload(dg, torch, dg.lw_bundle_build_q_opts(kind, codes, d, m, parts=2))
+    for batch in ((1, 2, 4, 8, 16) if kind_s == "q4" else (1, 16)):
+        say("balanced", case, batch)
+        y = _run_gemv(dg, torch, db, x, batch, rows)
+        assert rel_err(y, gemv_q_all(codes, d, m, x, batch)) <= TOL
+        assert np.array_equal(y, _run_gemv(dg, torch, db, x, batch, rows))
+
 # ------------------------------------------------------------------ parts per tile row
 
 PARTS_Q = [
