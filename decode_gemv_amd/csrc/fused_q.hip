@@ -227,10 +227,10 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
 // after the table barrier, as in the whole-row layout, so it starts decoding
 // when its own tile is in (one shared staging would need a barrier after the
 // slowest tile of the workgroup); the second request of a split tile's lines
-// is served by the CU's L2.  A workgroup's tiles span at most two row bands (U <= the
-// column blocks); each row band's sums meet those of the other workgroups
-// holding its tiles in the exchange tree (leaf = workgroup - the band's
-// first workgroup).
+// is served by the CU's L2.  A workgroup's tiles span at most two row bands
+// (U <= the column blocks); each row band's sums meet those of the other
+// workgroups holding its tiles in the exchange tree (leaf = workgroup - the
+// band's first workgroup).
 __host__ __device__ inline LdsLayout lds_layout_bal(int batch, int max_words, int waves, int tiles_per_wg)
 {
     LdsLayout L;
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(64 * (4 * K + 4)) void k_gemv_bal(KArgs a)
     const int p = split ? ((wave - 4 * K) & 1) : 0;                  // half of the tile row
     const int64_t T0 = (int64_t)blockIdx.x * U;                      // the workgroup's first tile
     const int64_t t = T0 + j;             // tiles are in row-major order: t = rb * n_cb + cb
-    const int rb = (int)(t / a.n_cb), cb = (int)(t % a.n_cb);
+    const int cb = (int)(t % a.n_cb);
     const int S = a.max_words + 3;
     const uint32_t xs_addr = (uint32_t)(size_t)(lds + L.x) + 4u * (uint32_t)(wave * BATCH * 128);
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + wave * S * 32;

@@ -459,7 +459,8 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
     LW_FENCE();
     issue_params(1);
     LW_FENCE();
-#pragma unroll(UNROLL_ALL ? NG : 1)
+    constexpr int UNROLL = UNROLL_ALL ? NG : 1;
+#pragma unroll UNROLL
     for (int g = 2; g < NG; g += 2) {
         decode_group(0);       // group g (even)
         LW_FENCE();
