@@ -27,6 +27,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -52,14 +53,23 @@ def kernel_source(kind_name: str, batch: int) -> str:
     return "mfma.hip" if batch >= 8 else "fused_q.hip"
 
 
+def _code_text(text: str) -> str:
+    """Source text without comments, whitespace runs collapsed: an edit to a
+    comment leaves the digest of the code unchanged."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return re.sub(r"\s+", " ", text).strip()
+
+
 def sources_digest(kernel_file: str) -> str:
-    """Digest of the dominant kernel's sources: a recorded traffic figure is
-    only reported while the kernel it was measured on is unchanged."""
+    """Digest of the dominant kernel's sources (their code, comments left
+    out): a recorded traffic figure is only reported while the kernel it was
+    measured on is unchanged."""
     h = hashlib.sha256()
     for name in sorted(SHARED_SOURCES + (kernel_file,)):
         h.update(name.encode())
-        with open(os.path.join(ROOT, "decode_gemv_amd", "csrc", name), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "decode_gemv_amd", "csrc", name), encoding="utf-8") as fh:
+            h.update(_code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

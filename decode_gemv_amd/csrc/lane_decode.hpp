@@ -554,32 +554,28 @@ LW_DEV bool lw_lane_init(LaneDec &d, uint8_t *lds, const uint32_t *slots, int l,
     return (lb & 255u) == 0 && lb + LW_CSEL < 0xFF00u;
 }
 
-// Sum the per-wave partials of the workgroup's ROWS rows (red[wave][b][row],
-// RS floats between consecutive (wave, b) runs) and write y, or, when the
-// row band's columns are split over a.groups workgroups, combine the groups'
-// sums by a pairwise exchange tree in the bundle's workspace.
-//
-// Group g is leaf g of a binary tree over the groups (a node without a
-// sibling at some level passes its value up unchanged).  For each output,
-// the two members of a pair meet in one workspace slot, which holds 0 when
-// empty: each swaps its value into the slot with one device-scope atomic
-// exchange.  The one that gets 0 back arrives first and is done; the other
-// gets its partner's value, empties the slot again and carries the sum one
-// level up.  The single atomic read-modify-write on the slot is the only
+// The exchange tree of the split-column reduction.  When a row band's
+// columns are split over several workgroups (column groups), their sums are
+// combined in a binary tree over the groups (a node without a sibling at
+// some level passes its value up unchanged).  For each output, the two
+// members of a pair meet in one slot of the bundle's workspace, which holds
+// 0 when empty: each swaps its value into the slot with one device-scope
+// atomic exchange.  The one that gets 0 back arrives first and is done; the
+// other gets its partner's value, empties the slot again and carries the sum
+// one level up.  The single atomic read-modify-write on the slot is the only
 // synchronisation, so no thread ever waits for another, and every slot is
 // empty again when the call ends (both members of every pair always come).
 // Floating-point addition is commutative, so each pair's sum, and the whole
 // tree's, does not depend on which member arrives first: the result is
 // deterministic.  A value of +0.0 travels as -0.0 (the empty slot's bits are
 // those of +0.0), so an output whose sum is zero may be written as -0.0.
-// A thread's outputs (at most KMAX) go up the tree together, their exchanges
-// in flight at once: ceil(log2(groups)) round trips to the coherence point.
-// The exchange tree of the split-column reduction (see lw_finish_rows): this
-// thread's outputs v[k] (at their indices at[k] in y, -1 for none) enter as
-// leaf `node` of a tree over n leaves and go up level by level, their
-// exchanges in flight at once.  On return at[k] is -1 where this thread
-// arrived first at some pair (its partner carries the sum on); the outputs
-// left in at[] hold their complete sums.
+//
+// This thread's outputs v[k] (at their indices at[k] in y, -1 for none)
+// enter as leaf `node` of a tree over n leaves and go up level by level,
+// their exchanges in flight at once: ceil(log2(n)) round trips to the
+// coherence point.  On return at[k] is -1 where this thread arrived first at
+// some pair (its partner carries the sum on); the outputs left in at[] hold
+// their complete sums.
 template <int KMAX>
 LW_DEV void lw_tree_combine(const KArgs &a, int node, int n, float (&v)[KMAX], int64_t (&at)[KMAX])
 {
@@ -615,6 +611,10 @@ LW_DEV void lw_tree_combine(const KArgs &a, int node, int n, float (&v)[KMAX], i
     }
 }
 
+// Sum the per-wave partials of the workgroup's ROWS rows (red[wave][b][row],
+// RS floats between consecutive (wave, b) runs) and write y, or, when the
+// row band's columns are split over a.groups workgroups, combine the groups'
+// sums in the exchange tree (leaf g).
 template <int BATCH, int ROWS = 128, int RS = ROWS>
 LW_DEV void lw_finish_rows(const KArgs &a, const float *red, int64_t row0, int g, int waves)
 {
