@@ -405,23 +405,28 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
     // (compact tables) or bias - len_j with bias = lb/2 + 512 a multiple of
     // 64, so the running sum t of the s before symbol j is -o modulo 64.
     // Symbols 1 and 2 sit at most 22 bits in: one alignbit by t (which reads
-    // t mod 32 = 32 - o) takes their peek.  Symbol 3 can sit 33 bits in,
-    // past one alignment, so it takes a 64-bit shift by -t.
+    // t mod 32 = 32 - o) takes their peek, all 32 bits of it from the window.
+    // Symbol 3 can sit 33 bits in, past one alignment; its peek is symbol
+    // 2's advanced by symbol 2's length (an alignbit of (peek, 0) by s, whose
+    // low five bits are 32 - len), which leaves 32 - len >= 21 bits from the
+    // window: every plan reads at most the top 16 bits of a peek.
     auto decode_group = [&](int q) {
         const uint32_t sh = d.un;
         const uint32_t hi = __builtin_amdgcn_alignbit(wa, wb, sh), lo = __builtin_amdgcn_alignbit(wb, wc, sh);
-        uint32_t t = 0;
+        uint32_t t = 0, prev = 0, sprev = 0;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             uint32_t peek;
             if (j == 0) peek = hi;
             else if (j < 3) peek = __builtin_amdgcn_alignbit(hi, lo, t);
-            else peek = (uint32_t)((((uint64_t)hi << 32 | lo) << ((0u - t) & 63u)) >> 32);
+            else peek = __builtin_amdgcn_alignbit(prev, 0u, sprev);
             const uint32_t Aj = lw_count<PLAN>(peek, d.k, d.xk, a);
             const uint32_t s = CMP ? __builtin_amdgcn_perm(a.lut_hi, d.lut_lo, Aj) : Aj >> 1;
             A[q][j] = Aj;
             code[q][j] = peek >> (s & 31u);
             t += s;
+            prev = peek;
+            sprev = s;
         }
         if constexpr (CMP)
             d.un += t;                    // t = -sum(len) exactly
