@@ -107,7 +107,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_bf16(KArgs a)
 
     // issue every load, tile offsets first; table barrier; own tile and x (as in fused_q.hip)
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-    const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, false);
+    const LwTabRegs tr = lw_tab_fetch<PLAN>(a, false);
     const uint32_t start = lw_part_start(a, c.t, c.l, c.half * a.parts);   // this lane's tile row
     uint32_t xv[BATCH][2];
     const uint32_t *xg = reinterpret_cast<const uint32_t *>(a.x) + (size_t)(c.active ? c.cb : 0) * 128;
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_bf16(KArgs a)
     // whole-row workgroups request their tiles after the table barrier (see fused_q.hip)
     LwTileRegs64 tile;
     if constexpr (WPG <= WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
+    lw_tab_put<PLAN>(lds, tr, a);
     __syncthreads();                      // the decoder table is complete
     if constexpr (WPG > WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
 #pragma unroll
@@ -214,13 +214,13 @@ __global__ __launch_bounds__(256) void k_decode_bf16(KArgs a)
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
     const uint32_t *smrow = a.sm + (size_t)c.t * 4096 + (size_t)c.half * 64 * 32 + c.l;
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-    const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, false);
+    const LwTabRegs tr = lw_tab_fetch<PLAN>(a, false);
     const uint32_t start = lw_part_start(a, c.t, c.l, c.half * a.parts);   // this lane's tile row
     uint32_t ring[2][CHUNK];
     lw_load_sm(ring[0], smrow, 0);
     LwTileRegs64 tile;
     lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
+    lw_tab_put<PLAN>(lds, tr, a);
     __syncthreads();
     if (!c.active) return;
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
@@ -288,11 +288,11 @@ __global__ __launch_bounds__(256) void k_transcode_bf16(KArgs a)
     const int S = a.max_words + 3;
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-    const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, !EXP);   // second table: the palette index itself
+    const LwTabRegs tr = lw_tab_fetch<PLAN>(a, !EXP);   // second table: the palette index itself
     const uint32_t start = lw_part_start(a, c.t, c.l, c.half * a.parts);   // this lane's tile row
     LwTileRegs64 tile;
     lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
+    lw_tab_put<PLAN>(lds, tr, a);
     __syncthreads();
     if (!c.active) return;
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);

@@ -393,6 +393,78 @@ static void fill_gputab(int kind, const lw_table &t, const uint8_t *palette, lw_
     }
 }
 
+// Residue packing of the limits of lengths L[0..n) into two SAD byte pairs:
+// a limit c with c mod 8 = r compares floor((p + k)/8) with (c + k)/8,
+// k = 8 - r, on a byte taken from the peek plus k << 21 (a saturating add),
+// or with `sub` floor((p - r)/8) with (c - r)/8 on a byte taken from the
+// peek minus r << 21 (saturating at 0; this form also takes limits above
+// 2040, where (c + k)/8 would be 256, and needs c - r >= 8); the residue-0
+// limits compare the top byte.  Residue limits of pair j sit in its top bytes
+// (3, 2, ..), read from the peek plus k_j; the residue-0 limits fill bytes
+// 0.. of pair 0, then of pair 1.  One residue: its limits split over both
+// pairs, which share one register.  Unused lanes compare 0 with 0 and
+// contribute nothing.  Writes c8, c8m1, xk and xsel of a and returns the
+// number of residues besides 0 (0..2), or -1 when the limits do not fit.
+static int pack_residues(const lw_table &t, const int *L, int n, lw_plan &a, bool sub)
+{
+    if (n > 8) return -1;
+    int thr[8], zero[8], rl[2][8], nz = 0, nrl[2] = {0, 0}, rv[2] = {0, 0}, nres = 0;
+    for (int i = 0; i < n; i++) {
+        const uint32_t c = t.limit[L[i]];
+        const int r = (int)(c & 7u);
+        thr[i] = sub ? (int)((c - (uint32_t)r) >> 3) : (int)((c + (uint32_t)((8 - r) & 7)) >> 3);   // exact
+        if (thr[i] < 1 || thr[i] > 255) return -1;
+        if (!r) {
+            zero[nz++] = i;
+            continue;
+        }
+        int q = -1;
+        for (int j = 0; j < nres; j++)
+            if (rv[j] == r) q = j;
+        if (q < 0) {
+            if (nres == 2) return -1;
+            q = nres;
+            rv[nres++] = r;
+        }
+        rl[q][nrl[q]++] = i;
+    }
+    int pres[2] = {0, 0}, plist[2][8], pn[2] = {0, 0};
+    if (nres == 1) {
+        pres[0] = pres[1] = rv[0];
+        for (int i = 0; i < nrl[0]; i++) {
+            const int j = i & 1;
+            plist[j][pn[j]++] = rl[0][i];
+        }
+    } else if (nres == 2) {
+        for (int j = 0; j < 2; j++) {
+            pres[j] = rv[j];
+            for (int i = 0; i < nrl[j]; i++) plist[j][pn[j]++] = rl[j][i];
+        }
+    }
+    const int extra = std::max(pn[0], pn[1]);
+    if (extra > 4 || nz > 2 * (4 - extra)) return -1;
+    a.c8[0] = a.c8[1] = a.c8m1[0] = a.c8m1[1] = 0;
+    for (int j = 0; j < 2; j++)
+        for (int i = 0; i < pn[j]; i++) {
+            const int b = 3 - i;
+            a.c8[j] |= (uint32_t)thr[plist[j][i]] << (8 * b);
+            a.c8m1[j] |= (uint32_t)(thr[plist[j][i]] - 1) << (8 * b);
+        }
+    for (int i = 0; i < nz; i++) {
+        const int j = i / (4 - extra), b = i % (4 - extra);
+        a.c8[j] |= (uint32_t)thr[zero[i]] << (8 * b);
+        a.c8m1[j] |= (uint32_t)(thr[zero[i]] - 1) << (8 * b);
+    }
+    for (int j = 0; j < 2; j++) {
+        const int k = sub ? pres[j] : (8 - pres[j]) & 7;
+        a.xk[j] = (uint32_t)k << 21;
+        uint32_t sel = 0;
+        for (int b = 0; b < 4; b++) sel |= (k && b >= 4 - extra ? 7u : 3u) << (8 * b);
+        a.xsel[j] = sel;
+    }
+    return nres;
+}
+
 // Limit comparisons packed for the SAD counting of lane_decode.hpp.
 // Compact tables (at most four used lengths, the three shorter <= 8): the
 // limits of the used lengths but the longest, in byte lanes (top 8 peek bits
@@ -400,12 +472,13 @@ static void fill_gputab(int kind, const lw_table &t, const uint8_t *palette, lw_
 // compare every length min_len .. max_len-1 (an absent length repeats the
 // previous limit), so the length is min_len + count:
 //   - up to eight limits whose residues mod 8 take at most two values besides
-//     0 go to two SAD byte pairs (residue plans): a limit c with c mod 8 = r
-//     compares floor((p + k)/8) with (c + k)/8, k = 8 - r, on a byte taken
-//     from the peek plus k << 21; the residue-0 limits compare the top byte;
+//     0 go to two SAD byte pairs (residue plans, pack_residues);
+//   - when these do not fit but the used lengths but the longest (at most
+//     seven) do, with at most one residue in the subtracting form, the
+//     sparse plan compares only those, and the count r indexes the used
+//     lengths through a byte table (the length of count r in byte 7 - r);
 //   - anything else takes the general plan (lengths <= 8 in byte lanes, 9 and
 //     10 in 16-bit lanes against the top 16 window bits).
-// Unused lanes compare 0 with 0 and contribute nothing.
 void lw_make_plan(const lw_table &t, int min_len, int max_len, lw_plan &a)
 {
     std::memset(&a, 0, sizeof(a));
@@ -439,75 +512,24 @@ void lw_make_plan(const lw_table &t, int min_len, int max_len, lw_plan &a)
         return;
     }
     const int n = max_len - min_len;          // comparisons: lengths min_len .. max_len - 1
-    a.sad_k = LW_PLAN_PBASE - 2u * (uint32_t)min_len - (uint32_t)n;
-    // residue plans: per limit its residue mod 8 and its byte threshold
-    int thr[LW_MAXLEN + 1], zero[LW_MAXLEN + 1], rl[2][LW_MAXLEN + 1], nz = 0, nrl[2] = {0, 0}, rv[2] = {0, 0};
-    int nres = 0;
-    bool fits = n <= 8;
-    for (int i = 0; i < n && fits; i++) {
-        const uint32_t c = t.limit[min_len + i];
-        const int r = (int)(c & 7u);
-        thr[i] = (int)((c + (uint32_t)((8 - r) & 7)) >> 3);   // exact: c + k is a multiple of 8
-        if (thr[i] < 1 || thr[i] > 255) {
-            fits = false;
-            break;
-        }
-        if (!r) {
-            zero[nz++] = i;
-            continue;
-        }
-        int q = -1;
-        for (int j = 0; j < nres; j++)
-            if (rv[j] == r) q = j;
-        if (q < 0) {
-            if (nres == 2) {
-                fits = false;
-                break;
-            }
-            q = nres;
-            rv[nres++] = r;
-        }
-        rl[q][nrl[q]++] = i;
+    int dense[LW_MAXLEN + 1];
+    for (int i = 0; i < n; i++) dense[i] = min_len + i;
+    a.sad_k = LW_PLAN_PBASE - 2u * (uint32_t)min_len - (uint32_t)n;   // residue and general plans
+    const int nres = pack_residues(t, dense, n, a, false);
+    if (nres >= 0) {
+        a.plan = nres == 0 ? LW_P_R2 : nres == 1 ? LW_P_R2K : LW_P_R2X2;
+        return;
     }
-    if (fits) {
-        // residue limits of pair j sit in its top bytes (3, 2, ..), read from
-        // the peek plus k_j; the residue-0 limits fill bytes 0.. of pair 0,
-        // then of pair 1, read from the top peek byte.  One residue: its
-        // limits split over both pairs, which share one register.
-        int pres[2] = {0, 0}, plist[2][LW_MAXLEN + 1], pn[2] = {0, 0};
-        if (nres == 1) {
-            pres[0] = pres[1] = rv[0];
-            for (int i = 0; i < nrl[0]; i++) {
-                const int j = i & 1;
-                plist[j][pn[j]++] = rl[0][i];
-            }
-        } else if (nres == 2) {
-            for (int j = 0; j < 2; j++) {
-                pres[j] = rv[j];
-                for (int i = 0; i < nrl[j]; i++) plist[j][pn[j]++] = rl[j][i];
-            }
-        }
-        const int extra = std::max(pn[0], pn[1]);
-        if (extra <= 4 && nz <= 2 * (4 - extra)) {
-            for (int j = 0; j < 2; j++)
-                for (int i = 0; i < pn[j]; i++) {
-                    const int b = 3 - i;
-                    a.c8[j] |= (uint32_t)thr[plist[j][i]] << (8 * b);
-                    a.c8m1[j] |= (uint32_t)(thr[plist[j][i]] - 1) << (8 * b);
-                }
-            for (int i = 0; i < nz; i++) {
-                const int j = i / (4 - extra), b = i % (4 - extra);
-                a.c8[j] |= (uint32_t)thr[zero[i]] << (8 * b);
-                a.c8m1[j] |= (uint32_t)(thr[zero[i]] - 1) << (8 * b);
-            }
-            for (int j = 0; j < 2; j++) {
-                const int k = (8 - pres[j]) & 7;
-                a.xk[j] = (uint32_t)k << 21;
-                uint32_t sel = 0;
-                for (int b = 0; b < 4; b++) sel |= (k && b >= 4 - extra ? 7u : 3u) << (8 * b);
-                a.xsel[j] = sel;
-            }
-            a.plan = nres == 0 ? LW_P_R2 : nres == 1 ? LW_P_R2K : LW_P_R2X2;
+    if (nu <= 8 && nu < n + 1) {
+        const int sres = pack_residues(t, used, nu - 1, a, true);
+        if (sres == 0 || sres == 1) {
+            uint64_t lut = 0;
+            for (int r = 0; r < nu; r++) lut |= (uint64_t)((256 - used[r]) & 0xFF) << (8 * (7 - r));
+            a.lut_lo = (uint32_t)lut;
+            a.lut_hi = (uint32_t)(lut >> 32);
+            a.ncmp = nu - 1;
+            a.sad_k = LW_PLAN_SBASE - (uint32_t)(nu - 1);
+            a.plan = LW_P_S2K;
             return;
         }
     }

@@ -207,7 +207,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
     // stores its own tile and activations and starts decoding as soon as its
     // own data is in (a wavefront's LDS operations complete in order).
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-    const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, false);
+    const LwTabRegs tr = lw_tab_fetch<PLAN>(a, false);
     lw_u32x2 dlo, dhi;                    // (d, m) of the tile rows whose sums this lane ends with
     MfDot<KIND, BATCH>::dm_rows(a, c.t, dlo, dhi);
     // this lane's part: bundle part half * parts + p * (parts / P)
@@ -231,11 +231,11 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
     LwTileRegs64 tile;
     if constexpr (P > 1) {
         if (c.p == 0) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-        lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
+        lw_tab_put<PLAN>(lds, tr, a);
         if (c.p == 0) lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     } else {
         if constexpr (WPG <= WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-        lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
+        lw_tab_put<PLAN>(lds, tr, a);
         __syncthreads();                  // the decoder table is complete
         if constexpr (WPG > WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
     }
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(64 * (4 * K + 4)) void k_gemv_bal(KArgs a)
     // Issue every global load first (as in k_gemv_q); the tile loads go out
     // after the table barrier, as in the sixteen-wavefront whole-row layout.
     const uint32_t w0 = a.tile_off[t], w1 = a.tile_off[t + 1];
-    const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, false);
+    const LwTabRegs tr = lw_tab_fetch<PLAN>(a, false);
     lw_u32x2 dlo, dhi;
     MfDot<KIND, BATCH>::dm_rows(a, t, dlo, dhi);
     const uint32_t start = lw_part_start(a, t, l, half * a.parts + p * (a.parts / 2));
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(64 * (4 * K + 4)) void k_gemv_bal(KArgs a)
         xv[b][0] = xg[(size_t)b * (a.cols / 2) + lane];
         xv[b][1] = xg[(size_t)b * (a.cols / 2) + lane + 64];
     }
-    lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
+    lw_tab_put<PLAN>(lds, tr, a);
     if (threadIdx.x < ZERO_BYTES / 4) *(lw_lds_w32 *)(size_t)(zero_addr + 4u * threadIdx.x) = 0u;
     __syncthreads();                      // the decoder table and the zero block are complete
     LwTileRegs64 tile;
@@ -401,11 +401,11 @@ __global__ __launch_bounds__(256) void k_decode_q(KArgs a)
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.wave * S * 32;
     // issue, then store (as in k_gemv_q)
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-    const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, true);
+    const LwTabRegs tr = lw_tab_fetch<PLAN>(a, true);
     const uint32_t start = lw_part_start(a, c.t, c.l, c.half * a.parts);   // this lane's tile row
     LwTileRegs64 tile;
     lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-    lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
+    lw_tab_put<PLAN>(lds, tr, a);
     __syncthreads();
     if (!c.active) return;
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);

@@ -63,6 +63,9 @@ struct KArgs {
 //   LW_P_R2X2     two residues besides 0: each SAD pair has its own register
 //   LW_P_GEN      anything else (more than 8 comparisons): two byte pairs on
 //                 the top byte and one 16-bit pair on the top 16 bits
+//   LW_P_S2K      tables with absent lengths whose used lengths fit where the
+//                 full range does not: as R2K over the used lengths only, the
+//                 length of count r from a byte table indexed by A / 2
 struct SadPlan {
     int plan;
 };
@@ -79,6 +82,7 @@ inline hipError_t lw_with_plan(SadPlan p, F f)
     case LW_P_R2K: return f(std::integral_constant<int, LW_P_R2K>{});
     case LW_P_R2X2: return f(std::integral_constant<int, LW_P_R2X2>{});
     case LW_P_GEN: return f(std::integral_constant<int, LW_P_GEN>{});
+    case LW_P_S2K: return f(std::integral_constant<int, LW_P_S2K>{});
     }
     return hipErrorInvalidValue;
 }

@@ -49,6 +49,17 @@
 // second byte (at least 13) makes 0xFF, and its two zero upper bytes pick
 // table byte 0, which holds 0xFF.  So the shift is s = -len exactly: its low
 // five bits are 32 - len, and the lengths of a group sum without a mask.
+//
+// Sparse plan (a table with absent lengths, whose used lengths fit two SAD
+// pairs with one residue where the whole length range does not: the bf16
+// exponent tables).  The pairs compare the limits of the used lengths only
+// (a residue r on the peek minus r << 21, saturating at 0: p >= c exactly
+// when floor((p - r)/8) >= (c - r)/8, which holds for limits up to 2047),
+// and A = SBASE - 2r for r limits passed: the LDS address of that count's
+// base entry.  The low byte of A >> 1 is 7 - r, a v_perm_b32 selector into
+// an 8-byte table of -len mod 256 per count; the shift's upper bytes are
+// other table bytes, which shifts ignore, and the low byte of a group's sum
+// of shifts, sign-extended, is -sum(len) (at most 44).
 #ifndef LW_LANE_DECODE_HPP
 #define LW_LANE_DECODE_HPP
 
@@ -129,6 +140,7 @@ inline hipError_t lw_allow_lds()
 #define LW_TPAY 1024u        // payload per canonical index, u32[256]
 #define LW_TPAY_HI 2048u     // second payload, u32[256]
 #define LW_CSEL LW_PLAN_CSEL     // compact tables: selector of count r CSEL - 2r, its base entry at CSEL + 1 - 2r
+#define LW_SBASE LW_PLAN_SBASE   // sparse plan: base entry of count r at SBASE - 2r
 #define LW_TAB_BYTES 3584u
 
 LW_DEV uint32_t lw_wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -214,13 +226,18 @@ struct LwTabRegs {
 // whether a plan indexes the compact tables (length from a byte table)
 template <int PLAN>
 constexpr bool lw_compact() { return PLAN == LW_P_COMPACT; }
+// whether a plan counts the used lengths only (length from a byte table)
+template <int PLAN>
+constexpr bool lw_sparse() { return PLAN == LW_P_S2K; }
 
 // thread tid (< 256) fetches payload entry tid of both tables and length
 // entry min(tid, max_len - min_len) (compact tables: the base of count
-// min(tid, ncmp), from the kernel arguments).  Loads and stores are
-// unconditional: a load the compiler sinks into a divergent branch is
-// waited on together with every load issued before it.
-template <bool CMP>
+// min(tid, ncmp), from the kernel arguments; the sparse plan: the base of
+// the length that count min(tid, ncmp) stands for, byte 7 - count of the
+// byte table).  Loads and stores are unconditional: a load the compiler
+// sinks into a divergent branch is waited on together with every load
+// issued before it.
+template <int PLAN>
 LW_DEV LwTabRegs lw_tab_fetch(const KArgs &a, bool symval_second)
 {
     LwTabRegs r;
@@ -228,16 +245,20 @@ LW_DEV LwTabRegs lw_tab_fetch(const KArgs &a, bool symval_second)
     const lw_gputab *g = a.tab;
     r.pay = g->payload[tid & 255];
     r.pay2 = symval_second ? g->symval[tid & 255] : g->payload_hi[tid & 255];
-    if constexpr (CMP) {
+    if constexpr (lw_compact<PLAN>()) {
         const int i = min(tid, a.ncmp);
         r.ent = i == 0 ? a.cbase[0] : i == 1 ? a.cbase[1] : i == 2 ? a.cbase[2] : a.cbase[3];
+    } else if constexpr (lw_sparse<PLAN>()) {
+        const int i = min(tid, a.ncmp);   // ncmp <= 7
+        const uint32_t nb = i < 4 ? a.lut_hi >> (8 * (3 - i)) : a.lut_lo >> (8 * (7 - i));   // -len mod 256
+        r.ent = g->base[((256u - (nb & 0xFFu)) & 0xFFu) - (uint32_t)a.min_len];
     } else {
         r.ent = g->base[min(tid, a.max_len - a.min_len)];   // threads past the last entry repeat it
     }
     return r;
 }
 
-template <bool CMP>
+template <int PLAN>
 LW_DEV void lw_tab_put(uint8_t *lds, const LwTabRegs &r, const KArgs &a)
 {
     const uint32_t lb = (uint32_t)(size_t)lds;
@@ -245,8 +266,10 @@ LW_DEV void lw_tab_put(uint8_t *lds, const LwTabRegs &r, const KArgs &a)
     *(lw_lds_w32 *)(size_t)(lb + LW_TPAY + 4u * (tid & 255)) = r.pay;
     *(lw_lds_w32 *)(size_t)(lb + LW_TPAY_HI + 4u * (tid & 255)) = r.pay2;
     const int16_t v = (int16_t)((int32_t)lb + (int32_t)LW_TPAY + 4 * r.ent);   // repeated stores write the same value
-    if constexpr (CMP)
+    if constexpr (lw_compact<PLAN>())
         *(lw_lds_w16 *)(size_t)(lb + LW_CSEL + 1u - 2u * (uint32_t)min(tid, a.ncmp)) = v;
+    else if constexpr (lw_sparse<PLAN>())
+        *(lw_lds_w16 *)(size_t)(lb + LW_SBASE - 2u * (uint32_t)min(tid, a.ncmp)) = v;
     else
         *(lw_lds_w16 *)(size_t)(lb + LW_PBASE - 2u * (uint32_t)(a.min_len + min(tid, a.max_len - a.min_len))) = v;
 }
@@ -336,6 +359,14 @@ LW_DEV uint32_t lw_add_sat(uint32_t v, uint32_t k)
     return r;
 }
 
+// peek - k, saturating at 0 (one v_sub_u32 with the clamp bit)
+LW_DEV uint32_t lw_sub_sat(uint32_t v, uint32_t k)
+{
+    uint32_t r;
+    asm("v_sub_u32_e64 %0, %1, %2 clamp" : "=v"(r) : "v"(v), "v"(k));
+    return r;
+}
+
 // Count the limits the window's peek has passed; returns A = lb + PBASE - 2*len
 // (compact tables: A = lb + CSEL - 2r for r limits passed).  xk holds the
 // residue plans' additive constants in vector registers (see LaneDec).
@@ -360,6 +391,8 @@ LW_DEV uint32_t lw_count(uint32_t hi, uint32_t k, const uint32_t (&xk)[2], const
         uint32_t x1, x2;
         if constexpr (PLAN == LW_P_R2) {
             x1 = __builtin_amdgcn_perm(hi, hi, 0x03030303u);
+        } else if constexpr (PLAN == LW_P_S2K) {
+            x1 = __builtin_amdgcn_perm(lw_sub_sat(hi, xk[0]), hi, a.xsel[0]);   // the residue subtracted
         } else {
             x1 = __builtin_amdgcn_perm(lw_add_sat(hi, xk[0]), hi, a.xsel[0]);
         }
@@ -390,7 +423,7 @@ template <int PLAN, int NG, class Aux, bool UNROLL_ALL = false, class PayOff, cl
 LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetch fetch, Use use)
 {
     static_assert(NG % 2 == 0 && NG >= 4, "groups must be even");
-    constexpr bool CMP = lw_compact<PLAN>();
+    constexpr bool CMP = lw_compact<PLAN>(), SPR = lw_sparse<PLAN>();
     uint32_t wa, wb, wc;
     uint32_t code[2][4], A[2][4], base[2][4], pay[2][4];
     Aux aux[2];
@@ -421,7 +454,9 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
             else if (j < 3) peek = __builtin_amdgcn_alignbit(hi, lo, t);
             else peek = __builtin_amdgcn_alignbit(prev, 0u, sprev);
             const uint32_t Aj = lw_count<PLAN>(peek, d.k, d.xk, a);
-            const uint32_t s = CMP ? __builtin_amdgcn_perm(a.lut_hi, d.lut_lo, Aj) : Aj >> 1;
+            const uint32_t s = CMP   ? __builtin_amdgcn_perm(a.lut_hi, d.lut_lo, Aj)
+                               : SPR ? __builtin_amdgcn_perm(a.lut_hi, d.lut_lo, Aj >> 1)
+                                     : Aj >> 1;
             A[q][j] = Aj;
             code[q][j] = peek >> (s & 31u);
             t += s;
@@ -430,6 +465,8 @@ LW_DEV void lw_decode_pipelined(LaneDec &d, const KArgs &a, PayOff pay_off, Fetc
         }
         if constexpr (CMP)
             d.un += t;                    // t = -sum(len) exactly
+        else if constexpr (SPR)
+            d.un += (uint32_t)((int32_t)(t << 24) >> 24);   // the low byte of t is -sum(len) mod 256, sum <= 44
         else
             d.un += t - d.ubias;          // t - ubias = -sum(len)
     };
@@ -534,12 +571,12 @@ LW_DEV uint32_t lw_part_start(const KArgs &a, int64_t t, int l, int k)
 }
 
 // Set up a lane's decoder on its staged tile.  Returns false (the kernel must
-// then produce nothing) unless the LDS base is 256-byte aligned (the shift
+// then produce nothing) unless the LDS base is 512-byte aligned (the shift
 // amounts s = A >> 1 then carry a bias lb/2 + PBASE/2 that is a multiple of
-// 64, which both the 32-bit shifts and the 64-bit window offset need, and
-// the low byte of a compact table's A is its byte-table selector) and low
-// enough that the selector's second byte stays a 0xFF selector and its
-// upper bytes stay zero.
+// 64, which both the 32-bit shifts and the 64-bit window offset need, the
+// low byte of a compact table's A is its byte-table selector, and that of
+// the sparse plan's A >> 1) and low enough that the compact selector's
+// second byte stays a 0xFF selector and its upper bytes stay zero.
 LW_DEV bool lw_lane_init(LaneDec &d, uint8_t *lds, const uint32_t *slots, int l, const KArgs &a)
 {
     const uint32_t lb = (uint32_t)(size_t)lds;
@@ -556,7 +593,7 @@ LW_DEV bool lw_lane_init(LaneDec &d, uint8_t *lds, const uint32_t *slots, int l,
     // slower rate on gfx950).
     asm volatile("" : "+v"(d.k), "+v"(d.lut_lo), "+v"(d.xk[0]), "+v"(d.xk[1]));
     d.ubias = 4u * (lb / 2u + LW_PBASE / 2u);
-    return (lb & 255u) == 0 && lb + LW_CSEL < 0xFF00u;
+    return (lb & 511u) == 0 && lb + LW_CSEL < 0xFF00u;
 }
 
 // The exchange tree of the split-column reduction.  When a row band's

@@ -102,12 +102,15 @@ typedef struct {
 } lw_gputab;
 
 /* LDS byte offsets the plans' accumulator offsets are relative to: the
- * length entries sit at PBASE - 2*len, the compact tables' at CSEL + 1 - 2r. */
+ * length entries sit at PBASE - 2*len, the compact tables' at CSEL + 1 - 2r,
+ * the sparse plan's at SBASE - 2r (SBASE / 2 = 7 mod 256, so that the low
+ * byte of A / 2 is the byte-table selector 7 - r). */
 #define LW_PLAN_PBASE 1024u
 #define LW_PLAN_CSEL 0xD07u
+#define LW_PLAN_SBASE 526u
 
 /* Comparison plans (lane_decode.hpp): see kernels.h. */
-enum { LW_P_COMPACT = 0, LW_P_R2 = 1, LW_P_R2K = 2, LW_P_R2X2 = 3, LW_P_GEN = 4 };
+enum { LW_P_COMPACT = 0, LW_P_R2 = 1, LW_P_R2K = 2, LW_P_R2X2 = 3, LW_P_GEN = 4, LW_P_S2K = 5 };
 
 /* Regions each kind of kernel reads (bundle.cpp): a bit mask over lw_region.
  * LW_OP_ANY is the union over every kernel of the kind (what a valid image

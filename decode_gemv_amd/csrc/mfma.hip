@@ -124,7 +124,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_mfma(KArgs a)
 
     // Issue every global load first, tile offsets first (as in fused_q.hip).
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
-    const LwTabRegs tr = lw_tab_fetch<lw_compact<PLAN>()>(a, false);
+    const LwTabRegs tr = lw_tab_fetch<PLAN>(a, false);
     const uint32_t start = lw_part_start(a, c.t, c.l, c.half * a.parts + c.p * (a.parts / P));
     // (d, m) of tile rows 2l and 2l + 1, the two rows of this lane's D column
     u32x2 dm2 = u32x2{0u, 0u};
@@ -150,12 +150,12 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_mfma(KArgs a)
     if constexpr (P > 1) {
         // the tile's first wavefront stages it; one barrier covers the table and the tiles
         if (c.p == 0) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-        lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
+        lw_tab_put<PLAN>(lds, tr, a);
         if (c.p == 0) lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
         __syncthreads();
     } else {
         if constexpr (WPG <= WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
-        lw_tab_put<lw_compact<PLAN>()>(lds, tr, a);
+        lw_tab_put<PLAN>(lds, tr, a);
         __syncthreads();                  // the decoder table is complete
         if constexpr (WPG > WAVES) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
         lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);

@@ -8,8 +8,9 @@ bytes to gather and which thresholds to compare (the plan stored with the
 derived GPU tables).
 
 These tests take the plan a bundle carries and evaluate, on the CPU, the
-instruction sequence the kernels issue (v_perm_b32, v_add_u32 with clamp,
-v_sad_u8, v_sad_u16, written here from their instruction-set definitions)
+instruction sequence the kernels issue (v_perm_b32, v_add_u32 and v_sub_u32
+with clamp, v_sad_u8, v_sad_u16, written here from their instruction-set
+definitions)
 for every 11-bit peek followed by arbitrary stream bits.  The result must
 equal the length the canonical table defines (the first length whose limit
 exceeds the peek), on the workloads' tables and on random complete codes that
@@ -22,8 +23,8 @@ import decode_gemv_amd as dg
 import synth
 from support import codes_over, plan_of, random_complete_lengths
 
-PBASE, CSEL = 1024, 0xD07
-PLANS = {0: "compact", 1: "r2", 2: "r2k", 3: "r2x2", 4: "gen"}
+PBASE, CSEL, SBASE = 1024, 0xD07, 526
+PLANS = {0: "compact", 1: "r2", 2: "r2k", 3: "r2x2", 4: "gen", 5: "s2k"}
 M32 = 0xFFFFFFFF
 
 
@@ -67,6 +68,10 @@ def v_add_u32_clamp(a, b):
     return np.minimum(np.asarray(a, np.int64) + int(b), M32)
 
 
+def v_sub_u32_clamp(a, b):
+    return np.maximum(np.asarray(a, np.int64) - int(b), 0)
+
+
 # ------------------------------------------------------------ the stored plan
 
 def kernel_count(pl, hi):
@@ -87,6 +92,8 @@ def kernel_count(pl, hi):
     else:
         if P == 1:
             x1 = v_perm_b32(hi, hi, 0x03030303)
+        elif P == 5:
+            x1 = v_perm_b32(v_sub_u32_clamp(hi, pl["xk"][0]), hi, pl["xsel"][0])
         else:
             x1 = v_perm_b32(v_add_u32_clamp(hi, pl["xk"][0]), hi, pl["xsel"][0])
         x2 = v_perm_b32(v_add_u32_clamp(hi, pl["xk"][1]), hi, pl["xsel"][1]) if P == 3 else x1
@@ -130,6 +137,16 @@ def check_bundle(bundle, rng, junk_draws=3):
             for i in range(0, end, max(1, end // 64)):
                 s = int(v_perm_b32(pl["lut_hi"], pl["lut_lo"], int(A[i])))
                 assert s == (-int(got[i])) & M32, (i, hex(s), got[i], hex(lut))
+        elif pl["plan"] == 5:
+            # sparse: the count r of used-length limits passed, A = SBASE - 2r;
+            # the low byte of the shift perm(lut, A >> 1) is -len mod 256
+            used = [L for L in range(1, 12) if t["count"][L]]
+            r = (SBASE - A) // 2
+            assert np.array_equal(A, SBASE - 2 * r) and r.min() >= 0 and r.max() < len(used)
+            got = np.array(used)[r]
+            for i in range(0, end, max(1, end // 64)):
+                sh = int(v_perm_b32(pl["lut_hi"], pl["lut_lo"], int(A[i]) >> 1))
+                assert sh & 0xFF == (-int(got[i])) & 0xFF, (i, hex(sh), got[i])
         else:
             assert np.all((PBASE - A) % 2 == 0)
             got = (PBASE - A) // 2
@@ -153,6 +170,31 @@ def test_plans_of_workload_tables():
     assert seen[("q4_up_14336x4096", "lw_bundle_build_q")] in ("r2k", "r2x2", "r2")
     assert seen[("q6_mlp_70b", "lw_bundle_build_q")] in ("r2k", "r2x2", "r2")
     assert seen[("q4_up_14336x4096", "lw_bundle_build_q_compact")] == "compact"
+    # the bf16 exponent table (lengths 2..7, 9, 11) compares its used lengths only
+    assert seen["bf16"] == "s2k"
+
+
+def test_sparse_group_shift_sum():
+    """The sparse plan's shifts carry other table bytes above their low byte;
+    a group's four shifts summed, low byte sign-extended, is -sum(len), and
+    each shift's low five bits are 32 - len (what the decoder relies on)."""
+    w, _ = synth.gen_bf16(synth.WORKLOADS["bf16_up_14336x4096"][0], rows=128, cols=1024)
+    b = dg.lw_bundle_build_bf16(w)
+    pl, t = plan_of(b), table_of(b)
+    assert pl["plan"] == 5
+    used = [L for L in range(1, 12) if t["count"][L]]
+    n = len(used)
+    shift = [int(v_perm_b32(pl["lut_hi"], pl["lut_lo"], (SBASE - 2 * r) >> 1)) for r in range(n)]
+    for r in range(n):
+        assert shift[r] & 31 == (32 - used[r]) & 31
+    for r0 in range(n):
+        for r1 in range(n):
+            for r2 in range(n):
+                for r3 in range(n):
+                    tt = (shift[r0] + shift[r1] + shift[r2] + shift[r3]) & M32
+                    low = tt & 0xFF
+                    sext = low - 256 if low >= 128 else low
+                    assert sext == -(used[r0] + used[r1] + used[r2] + used[r3])
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -175,10 +217,11 @@ def test_plans_of_random_complete_codes(seed):
 
 
 def test_every_plan_is_reached():
-    """The random tables of the test above, the workloads and a few crafted
-    ones reach all five plans, so each plan's arithmetic is pinned."""
+    """The random tables of the test above and the bf16 workload's table
+    reach all six plans, so each plan's arithmetic is pinned."""
     rng = np.random.default_rng(99)
-    seen = set()
+    w, _ = synth.gen_bf16(synth.WORKLOADS["bf16_up_14336x4096"][0], rows=64, cols=256)
+    seen = {PLANS[check_bundle(dg.lw_bundle_build_bf16(w), rng, junk_draws=2)]}
     for trial in range(300):
         kind = dg.LW_Q4_PAIR
         n_sym = int(rng.integers(2, 257))
@@ -190,7 +233,7 @@ def test_every_plan_is_reached():
         if PLANS[pl] not in seen:
             check_bundle(b, rng, junk_draws=2)
             seen.add(PLANS[pl])
-        if len(seen) == 5:
+        if len(seen) == len(PLANS):
             break
     assert seen == set(PLANS.values()), seen
 
