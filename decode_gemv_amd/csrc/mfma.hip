@@ -1,4 +1,4 @@
-// mfma.hip -- fused decode + GEMM for batch 5..16 (bf16: 2..16) on the matrix cores of
+// mfma.hip -- fused decode + GEMM for batch 5..16 (bf16: 4..16) on the matrix cores of
 // gfx950 ("LazyWeights" bundle, decoded as in lane_decode.hpp; feeding the
 // matrix cores from on-chip data follows the reconstructive matmul idea of
 // "Unweight", section "How reconstructive matmul works").
