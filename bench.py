@@ -48,9 +48,9 @@ SHARED_SOURCES = ("lane_decode.hpp", "kernels.h", "lw_internal.h", "bundle.cpp",
 
 def kernel_source(kind_name: str, batch: int) -> str:
     """Source file of the kernel that dominates a workload's step: the
-    32x32 matrix-core kernel from batch 5 (bf16: 4), else the decode kernel
-    of the bundle's kind."""
-    if batch >= (4 if kind_name == "bf16" else 5):
+    matrix-core kernel from batch 8, else the decode kernel of the bundle's
+    kind."""
+    if batch >= 8:
         return "mfma.hip"
     return "bf16.hip" if kind_name == "bf16" else "fused_q.hip"
 

@@ -625,11 +625,14 @@ static lw_status check_shape(int64_t rows, int64_t cols, Shape &sh)
 // blocks (10 or 14 tiles per CU of a 256-CU MI355X with no whole-row layout:
 // the half-row starts let every SIMD carry the same work).  Else 1, 2, 4 or
 // 8 as asked.
-static lw_status choose_parts(const Shape &sh, int &parts)
+static lw_status choose_parts(const Shape &sh, int &parts, bool quantised)
 {
     if (parts == 0) {
         parts = 8;
         while (parts > 1 && sh.n_tiles * parts > LW_PART_UNITS) parts /= 2;
+        if (parts == 1 && quantised && sh.n_tiles > LW_PART_UNITS / 2 && sh.n_tiles <= LW_PART_UNITS &&
+            sh.n_tiles % 512 == 0 && (sh.n_tiles / 512) % 2 == 1 && sh.n_cb > 16)
+            parts = 2;
         return LW_OK;
     }
     if (parts != 1 && parts != 2 && parts != 4 && parts != 8) return lw_fail(LW_E_ARG, "parts must be 0, 1, 2, 4 or 8");
@@ -676,7 +679,7 @@ static lw_status build_q(int kind, int64_t rows, int64_t cols, const uint8_t *q,
     Shape sh;
     lw_status st = check_shape(rows, cols, sh);
     if (st) return st;
-    if ((st = choose_parts(sh, parts))) return st;
+    if ((st = choose_parts(sh, parts, true))) return st;
     const int qmax = kind == LW_Q4_PAIR ? 15 : 63;
     const int n_alpha = kind == LW_Q4_PAIR ? 256 : 64;
     const int spl = kind == LW_Q4_PAIR ? 256 : 512;
@@ -805,7 +808,7 @@ static lw_status build_bf16(int64_t rows, int64_t cols, const uint16_t *w, int c
     Shape sh;
     lw_status st = check_shape(rows, cols, sh);
     if (st) return st;
-    if ((st = choose_parts(sh, parts))) return st;
+    if ((st = choose_parts(sh, parts, false))) return st;
     try {
         // exponent histogram -> palette: top 16 by (count desc, exponent asc)
         std::vector<std::vector<uint64_t>> part(sh.n_rb, std::vector<uint64_t>(256, 0));

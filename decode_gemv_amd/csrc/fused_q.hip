@@ -1,4 +1,4 @@
-// fused_q.hip -- fused decode + dequantise + GEMV (batch 1..4) and
+// fused_q.hip -- fused decode + dequantise + GEMV (batch 1..7, VALU) and
 // decode-only kernels for 4-bit pair and 6-bit single codes, gfx950.
 //
 // Work split ("LazyWeights", section "2 . Code them": a 64x256 tile is 32
@@ -8,8 +8,9 @@
 // built), and one wavefront decodes one part of a tile: lane l < 32 decodes
 // lane stream l's part in tile row 2l, lane l + 32 the same part of row
 // 2l+1.  So every lane runs one serial chain of 128/P (Q4) or 256/P (Q6)
-// symbols, and each group's weights go to the matrix cores from registers
-// (MfDot).  The parts of one tile share its staged words.  More parts shorten the chains of small matrices and spread
+// symbols, and all 64 lanes consume the same activation pair at each step
+// (x is read once per wavefront from LDS).  The parts of one tile share its
+// staged words.  More parts shorten the chains of small matrices and spread
 // a large one evenly over the SIMDs (3584 tiles in two parts are seven
 // wavefronts on every SIMD of 256 CUs, where whole rows leave some SIMDs four
 // and others three or none).
@@ -33,21 +34,17 @@ namespace {
 constexpr int WAVES = 4;                 // wavefronts per workgroup (one column block each), by default
 
 struct LdsLayout {
-    uint32_t x, zero, tiles, total;
+    uint32_t x, tiles, total;
 };
 
-constexpr uint32_t ZERO_BYTES = 512;     // the A fragments of lanes off the diagonal (see MfDot)
-
-// the decoder table, each wavefront's activations, a block of zeros, then
-// the staged tiles (one per `parts` wavefronts), reused for the partial sums
+// staged tiles: one per `parts` wavefronts
 __host__ __device__ inline LdsLayout lds_layout(int batch, int max_words, bool decode_only, int waves = WAVES,
                                                 int parts = 1)
 {
     LdsLayout L;
     L.x = LW_TAB_BYTES;
     const uint32_t xbytes = decode_only ? 0u : (uint32_t)(waves * batch * 128 * 4);
-    L.zero = L.x + xbytes;
-    L.tiles = L.zero + (decode_only ? 0u : ZERO_BYTES);
+    L.tiles = L.x + xbytes;
     const uint32_t tiles = (uint32_t)((waves / parts) * (max_words + 3) * 128);
     const uint32_t red = (uint32_t)(waves * batch * 64 * 4);
     L.total = L.tiles + (tiles > red ? tiles : red);
@@ -78,111 +75,6 @@ LW_DEV LaneCtx lane_ctx(const KArgs &a, int waves = WAVES, int parts = 1)
     return c;
 }
 
-// Matrix-core dot products at batch 1..4 (the decoded weights go to the
-// matrix cores straight from registers, as in "Unweight", section "How
-// reconstructive matmul works").  v_mfma_f32_16x16x32_f16 takes from lane
-// i = 16 kg + n the fragments A[i % 16][8 kg + e] and B[8 kg + e][n], e < 8,
-// and returns D[4 kg + j][n] in its register j.  After one group of four
-// 4-bit pair symbols (two groups of 6-bit codes) a decoding lane holds its
-// tile row's weights at 8 consecutive columns: its B fragment.  Decoding lane
-// l + 32 h holds tile row 2l + h, so lane 16 kg + n holds row
-//     r(kg, n) = 32 (kg & 1) + 2n + (kg >> 1).
-// A is block-diagonal: A[4b + kg][8 kg' + e] = x[b][col + e] when kg' == kg
-// and b < batch, else 0, so the sum over k never mixes rows and
-//     D[4b + kg][n] = x[b] . W[r(kg, n)][col .. col + 8).
-// Lanes off the diagonal read their A fragments from a block of zeros in LDS
-// at the offsets the activations have, so every fragment read is one LDS
-// load with a constant offset.  One matrix instruction per 8 columns takes
-// the place of 4 (4-bit) or 8 (6-bit) v_dot2 per batch row, and the matrix
-// cores run beside the decode's VALU work.
-typedef _Float16 lw_h8 __attribute__((ext_vector_type(8)));
-typedef float lw_f4 __attribute__((ext_vector_type(4)));
-typedef uint32_t lw_u32x2 __attribute__((ext_vector_type(2)));
-
-template <int KIND, int BATCH>
-struct MfDot {
-    static_assert(BATCH >= 1 && BATCH <= 4, "sixteen rows of A: four batch rows of four lane groups");
-    static constexpr bool Q4 = KIND == LW_Q4_PAIR;
-    static constexpr uint32_t XG = Q4 ? 16u : 8u;   // activation bytes per group of four symbols
-    lw_f4 d;
-    uint32_t gw[4];                       // the B fragment being filled
-    uint32_t xa;                          // LDS address of this lane's A fragment at group 0
-
-    // xs: the wavefront's activations (batch row b at xs + 512 b); zero: the
-    // zero block; g0: the first group of the columns decoded
-    LW_DEV void init(uint32_t xs, uint32_t zero, int g0)
-    {
-        const int lane = threadIdx.x & 63, m = lane & 15, kg = lane >> 4, b = m >> 2;
-        const bool diag = (m & 3) == kg && b < BATCH;
-        xa = (diag ? xs + 512u * (uint32_t)b : zero) + XG * (uint32_t)g0;
-        d = lw_f4{0.f, 0.f, 0.f, 0.f};
-    }
-    // the A fragment for the matrix instruction after group g (every 4-bit
-    // group, every odd 6-bit group)
-    LW_DEV lw_u32x4 frag(int g) const
-    {
-        if (!Q4 && (g & 1) == 0) return lw_u32x4{0u, 0u, 0u, 0u};
-        return *(const lw_lds_w128 *)(size_t)(xa + XG * (uint32_t)(Q4 ? g : g - 1));
-    }
-    // symbol j of group g (pay: a 4-bit pair's two fp16 codes; a 6-bit code
-    // in the low half for even j, the high half for odd j)
-    LW_DEV void put(int g, int j, uint32_t pay, const lw_u32x4 &xf)
-    {
-        if constexpr (Q4) {
-            gw[j] = pay;
-        } else {
-            const int w = 2 * (g & 1) + (j >> 1);
-            gw[w] = (j & 1) ? (gw[w] | pay) : pay;
-        }
-        if (j == 3 && (Q4 || (g & 1)))
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(lw_h8, xf),
-                                                       __builtin_bit_cast(lw_h8, lw_u32x4{gw[0], gw[1], gw[2], gw[3]}),
-                                                       d, 0, 0, 0);
-    }
-    LW_DEV void poison() { d = lw_f4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")}; }
-    // (d, m) of the rows this lane's results belong to: rows 2n, 2n + 1 and 32 + 2n, 33 + 2n of tile t
-    static LW_DEV void dm_rows(const KArgs &a, int64_t t, lw_u32x2 &lo, lw_u32x2 &hi)
-    {
-        const int n = threadIdx.x & 15;
-        lo = *reinterpret_cast<const lw_u32x2 *>(a.dm + (size_t)t * 64 + 2 * n);
-        hi = *reinterpret_cast<const lw_u32x2 *>(a.dm + (size_t)t * 64 + 32 + 2 * n);
-    }
-    // dequantised partial sums into red[wave][b][row]: lane 16 b + n, register
-    // kg, holds batch row b against row r(kg, n); sx is batch row b's
-    // activation sum over the decoded columns
-    LW_DEV void store(float *red, int wave, bool active, const lw_u32x2 &lo, const lw_u32x2 &hi, float sx) const
-    {
-        const int lane = threadIdx.x & 63, b = lane >> 4, n = lane & 15;
-        if (b >= BATCH) return;
-#pragma unroll
-        for (int kg = 0; kg < 4; kg++) {
-            const uint32_t w = kg == 0 ? lo.x : kg == 1 ? hi.x : kg == 2 ? lo.y : hi.y;
-            red[(wave * BATCH + b) * 64 + 32 * (kg & 1) + 2 * n + (kg >> 1)] =
-                active ? lw_half_lo(w) * d[kg] - lw_half_hi(w) * sx : 0.f;
-        }
-    }
-};
-
-// The activation sum, over the decoded columns, of the batch row whose
-// results this lane stores (MfDot::store: lane 16 b + n): lane i holds the
-// column pairs i and i + 64 of every batch row (xv), in0 / in1 say whether
-// they are among the decoded columns.  Selected value by value: a select
-// chain over an array's elements is folded into one indexed load, which
-// keeps the array in scratch memory.
-template <int BATCH>
-LW_DEV float lw_batch_xsum(const uint32_t (&xv)[BATCH][2], bool in0, bool in1)
-{
-    const int mine = (threadIdx.x & 63) >> 4;
-    float s = 0.f;
-#pragma unroll
-    for (int b = 0; b < BATCH; b++) {
-        const float v = lw_wave_sum((in0 ? lw_half_lo(xv[b][0]) + lw_half_hi(xv[b][0]) : 0.f) +
-                                    (in1 ? lw_half_lo(xv[b][1]) + lw_half_hi(xv[b][1]) : 0.f));
-        s = mine == b ? v : s;
-    }
-    return s;
-}
-
 // WPG wavefronts per workgroup decode P parts of WPG/P consecutive column
 // blocks of one row band; when they cover whole rows the reduction stays in
 // LDS.
@@ -197,7 +89,6 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
     const LaneCtx c = lane_ctx(a, WPG, P);
     const int S = a.max_words + 3;
     const uint32_t xs_addr = (uint32_t)(size_t)(lds + L.x) + 4u * (uint32_t)(c.wave * BATCH * 128);
-    const uint32_t zero_addr = (uint32_t)(size_t)(lds + L.zero);
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + c.ts * S * 32;
 
     // Issue every global load first (unconditionally: an inactive wavefront
@@ -208,8 +99,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
     // own data is in (a wavefront's LDS operations complete in order).
     const uint32_t w0 = a.tile_off[c.t], w1 = a.tile_off[c.t + 1];
     const LwTabRegs tr = lw_tab_fetch<PLAN>(a, false);
-    lw_u32x2 dlo, dhi;                    // (d, m) of the tile rows whose sums this lane ends with
-    MfDot<KIND, BATCH>::dm_rows(a, c.t, dlo, dhi);
+    const uint32_t dm = a.dm[(size_t)c.t * 64 + 2 * c.l + c.half];   // (d, m) of this lane's tile row
     // this lane's part: bundle part half * parts + p * (parts / P)
     const uint32_t start = lw_part_start(a, c.t, c.l, c.half * a.parts + c.p * (a.parts / P));
     uint32_t xv[BATCH][2];
@@ -227,7 +117,6 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
     // order makes no difference.
     // In parts, the tile's first wavefront stages it for all of them, and
     // one barrier then covers the table and the tiles.
-    if (threadIdx.x < ZERO_BYTES / 4) *(lw_lds_w32 *)(size_t)(zero_addr + 4u * threadIdx.x) = 0u;
     LwTileRegs64 tile;
     if constexpr (P > 1) {
         if (c.p == 0) lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, c.lane, tile);
@@ -249,22 +138,57 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
     else
         lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, c.lane, tile);
 
-    MfDot<KIND, BATCH> mf;
-    mf.init(xs_addr, zero_addr, c.p * NG);   // from the first group of this part within the tile row
+    float acc[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; b++) acc[b] = 0.f;
+
     if (c.active) {
         LaneDec d;
         const bool ok = lw_lane_init(d, lds, slots, c.l, a);
         d.advance(start);
+        const int g0 = c.p * NG;          // first group of this part within the tile row
         if (ok) {
-            struct XF {
-                lw_u32x4 v;
+            // activations of one group: Q4 four pairs, Q6 two pairs (four columns) per batch row
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            struct XA {
+                u32x4 v[BATCH];
             };
-            lw_decode_pipelined<PLAN, NG, XF, true>(
-                d, a, [](int j) { return (KIND != LW_Q4_PAIR && (j & 1)) ? (LW_TPAY_HI - LW_TPAY) : 0u; },
-                [&](int g) { lw_ramp<NG>(a.ramp, g); return XF{mf.frag(g)}; },
-                [&](int g, int j, uint32_t pay, const XF &x) { mf.put(g, j, pay, x.v); });
+            auto fetch = [&](int g) {
+                lw_ramp<NG>(a.ramp, g);
+                XA r;
+#pragma unroll
+                for (int b = 0; b < BATCH; b++) {
+                    if constexpr (KIND == LW_Q4_PAIR) {
+                        const uint32_t ad = xs_addr + (uint32_t)(b * 512 + 16 * (g0 + g));
+                        r.v[b] = *(__attribute__((address_space(3))) const u32x4 *)(size_t)ad;
+                    } else {
+                        const uint32_t ad = xs_addr + (uint32_t)(b * 512 + 8 * (g0 + g));
+                        const u32x2 t = *(__attribute__((address_space(3))) const u32x2 *)(size_t)ad;
+                        r.v[b] = u32x4{t.x, t.y, 0u, 0u};
+                    }
+                }
+                return r;
+            };
+            auto use = [&](int, int j, uint32_t pay, const XA &x) {
+#pragma unroll
+                for (int b = 0; b < BATCH; b++) {
+                    uint32_t xp;
+                    if constexpr (KIND == LW_Q4_PAIR)
+                        xp = j == 0 ? x.v[b].x : j == 1 ? x.v[b].y : j == 2 ? x.v[b].z : x.v[b].w;
+                    else
+                        xp = j < 2 ? x.v[b].x : x.v[b].y;
+                    acc[b] = lw_dot2(pay, xp, acc[b]);
+                }
+            };
+            if constexpr (KIND == LW_Q4_PAIR)
+                lw_decode_pipelined<PLAN, NG, XA, true>(d, a, [](int) { return 0u; }, fetch, use);
+            else
+                lw_decode_pipelined<PLAN, NG, XA, true>(
+                    d, a, [](int j) { return (j & 1) ? (LW_TPAY_HI - LW_TPAY) : 0u; }, fetch, use);
         } else {                           // unusable LDS base: poison the output
-            mf.poison();
+#pragma unroll
+            for (int b = 0; b < BATCH; b++) acc[b] = __builtin_nanf("");
         }
     }
 
@@ -272,17 +196,26 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_q(KArgs a)
     // of the tile row (the activation sum is taken here, off the decode's
     // start; lane i holds the column pairs i and i + 64)
     const bool in0 = c.lane / (128 / P) == c.p, in1 = (c.lane + 64) / (128 / P) == c.p;
-    const float sx = lw_batch_xsum<BATCH>(xv, in0, in1);
+    float sx[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; b++)
+        sx[b] = lw_wave_sum((in0 ? lw_half_lo(xv[b][0]) + lw_half_hi(xv[b][0]) : 0.f) +
+                            (in1 ? lw_half_lo(xv[b][1]) + lw_half_hi(xv[b][1]) : 0.f));
+    float val[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; b++) val[b] = c.active ? lw_half_lo(dm) * acc[b] - lw_half_hi(dm) * sx[b] : 0.f;
     __syncthreads();                      // tiles no longer read: reuse for the reduction
     float *red = reinterpret_cast<float *>(lds + L.tiles);
-    mf.store(red, c.wave, c.active, dlo, dhi, sx);   // red[wave][b][row], row within the tile's 64 rows
+    // red[wave][b][row], row = 2l + half within the tile's 64 rows
+#pragma unroll
+    for (int b = 0; b < BATCH; b++) red[(c.wave * BATCH + b) * 64 + 2 * c.l + c.half] = val[b];
     __syncthreads();
 
     lw_finish_rows<BATCH, 64>(a, red, (int64_t)c.rb * 64, c.g, WPG);
 }
 
 
-// Balanced layout (bundles in parts).  With U = 4K + 2 tiles per
+// Balanced layout (bundles in parts, batch 1..4).  With U = 4K + 2 tiles per
 // CU (14336x4096 and 4096x14336 on 256 CUs: 3584 tiles, U = 14), whole
 // tiles give some SIMDs K + 1 tiles of work and others K.  Here one
 // workgroup per CU takes U consecutive tiles in row-major order with 4K + 4
@@ -301,8 +234,7 @@ __host__ __device__ inline LdsLayout lds_layout_bal(int batch, int max_words, in
 {
     LdsLayout L;
     L.x = LW_TAB_BYTES;
-    L.zero = L.x + (uint32_t)(waves * batch * 128 * 4);
-    L.tiles = L.zero + ZERO_BYTES;
+    L.tiles = L.x + (uint32_t)(waves * batch * 128 * 4);
     const uint32_t tiles = (uint32_t)(tiles_per_wg * (max_words + 3) * 128);
     const uint32_t red = (uint32_t)(waves * batch * 64 * 4);
     L.total = L.tiles + (tiles > red ? tiles : red);
@@ -326,15 +258,13 @@ __global__ __launch_bounds__(64 * (4 * K + 4)) void k_gemv_bal(KArgs a)
     const int cb = (int)(t % a.n_cb);
     const int S = a.max_words + 3;
     const uint32_t xs_addr = (uint32_t)(size_t)(lds + L.x) + 4u * (uint32_t)(wave * BATCH * 128);
-    const uint32_t zero_addr = (uint32_t)(size_t)(lds + L.zero);
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + L.tiles) + wave * S * 32;
 
     // Issue every global load first (as in k_gemv_q); the tile loads go out
     // after the table barrier, as in the sixteen-wavefront whole-row layout.
     const uint32_t w0 = a.tile_off[t], w1 = a.tile_off[t + 1];
     const LwTabRegs tr = lw_tab_fetch<PLAN>(a, false);
-    lw_u32x2 dlo, dhi;
-    MfDot<KIND, BATCH>::dm_rows(a, t, dlo, dhi);
+    const uint32_t dm = a.dm[(size_t)t * 64 + 2 * l + half];
     const uint32_t start = lw_part_start(a, t, l, half * a.parts + p * (a.parts / 2));
     uint32_t xv[BATCH][2];
     const uint32_t *xg = reinterpret_cast<const uint32_t *>(a.x) + (size_t)cb * 128;
@@ -344,8 +274,7 @@ __global__ __launch_bounds__(64 * (4 * K + 4)) void k_gemv_bal(KArgs a)
         xv[b][1] = xg[(size_t)b * (a.cols / 2) + lane + 64];
     }
     lw_tab_put<PLAN>(lds, tr, a);
-    if (threadIdx.x < ZERO_BYTES / 4) *(lw_lds_w32 *)(size_t)(zero_addr + 4u * threadIdx.x) = 0u;
-    __syncthreads();                      // the decoder table and the zero block are complete
+    __syncthreads();                      // the decoder table is complete
     LwTileRegs64 tile;
     lw_tile_fetch64(a.words, w0, (w1 - w0) >> 5, lane, tile);
 #pragma unroll
@@ -355,35 +284,71 @@ __global__ __launch_bounds__(64 * (4 * K + 4)) void k_gemv_bal(KArgs a)
     }
     lw_tile_put64(slots, a.words, w0, (w1 - w0) >> 5, lane, tile);
 
-    MfDot<KIND, BATCH> mf;
-    mf.init(xs_addr, zero_addr, p * (NG / 2));   // from the first group of this wavefront's columns
+    float acc[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; b++) acc[b] = 0.f;
     {
         LaneDec d;
         const bool ok = lw_lane_init(d, lds, slots, l, a);
         d.advance(start);
+        const int g0 = p * (NG / 2);      // first group of this wavefront's columns
         if (ok) {
-            struct XF {
-                lw_u32x4 v;
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            struct XA {
+                u32x4 v[BATCH];
             };
-            auto use = [&](int g, int jj, uint32_t pay, const XF &x) { mf.put(g, jj, pay, x.v); };
+            auto fetch_x = [&](int g) {
+                XA r;
+#pragma unroll
+                for (int b = 0; b < BATCH; b++) {
+                    if constexpr (KIND == LW_Q4_PAIR) {
+                        const uint32_t ad = xs_addr + (uint32_t)(b * 512 + 16 * (g0 + g));
+                        r.v[b] = *(__attribute__((address_space(3))) const u32x4 *)(size_t)ad;
+                    } else {
+                        const uint32_t ad = xs_addr + (uint32_t)(b * 512 + 8 * (g0 + g));
+                        const u32x2 t2 = *(__attribute__((address_space(3))) const u32x2 *)(size_t)ad;
+                        r.v[b] = u32x4{t2.x, t2.y, 0u, 0u};
+                    }
+                }
+                return r;
+            };
+            auto use = [&](int, int jj, uint32_t pay, const XA &x) {
+#pragma unroll
+                for (int b = 0; b < BATCH; b++) {
+                    uint32_t xp;
+                    if constexpr (KIND == LW_Q4_PAIR)
+                        xp = jj == 0 ? x.v[b].x : jj == 1 ? x.v[b].y : jj == 2 ? x.v[b].z : x.v[b].w;
+                    else
+                        xp = jj < 2 ? x.v[b].x : x.v[b].y;
+                    acc[b] = lw_dot2(pay, xp, acc[b]);
+                }
+            };
             auto pay_off = [](int jj) { return (KIND != LW_Q4_PAIR && (jj & 1)) ? (LW_TPAY_HI - LW_TPAY) : 0u; };
             if (split)
-                lw_decode_pipelined<PLAN, NG / 2, XF, true>(
-                    d, a, pay_off, [&](int g) { lw_ramp<NG / 2>(a.ramp, g); return XF{mf.frag(g)}; }, use);
+                lw_decode_pipelined<PLAN, NG / 2, XA, true>(
+                    d, a, pay_off, [&](int g) { lw_ramp<NG / 2>(a.ramp, g); return fetch_x(g); }, use);
             else
-                lw_decode_pipelined<PLAN, NG, XF, true>(
-                    d, a, pay_off, [&](int g) { lw_ramp<NG>(a.ramp, g); return XF{mf.frag(g)}; }, use);
+                lw_decode_pipelined<PLAN, NG, XA, true>(
+                    d, a, pay_off, [&](int g) { lw_ramp<NG>(a.ramp, g); return fetch_x(g); }, use);
         } else {                           // unusable LDS base: poison the output
-            mf.poison();
+#pragma unroll
+            for (int b = 0; b < BATCH; b++) acc[b] = __builtin_nanf("");
         }
     }
 
     // dequantise over this wavefront's columns (lane i holds the column pairs i and i + 64)
     const bool in0 = !split || p == 0, in1 = !split || p == 1;
-    const float sx = lw_batch_xsum<BATCH>(xv, in0, in1);
+    float sx[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; b++)
+        sx[b] = lw_wave_sum((in0 ? lw_half_lo(xv[b][0]) + lw_half_hi(xv[b][0]) : 0.f) +
+                            (in1 ? lw_half_lo(xv[b][1]) + lw_half_hi(xv[b][1]) : 0.f));
     __syncthreads();                      // tiles no longer read: reuse for the partial sums
     float *red = reinterpret_cast<float *>(lds + L.tiles);
-    mf.store(red, wave, true, dlo, dhi, sx);
+#pragma unroll
+    for (int b = 0; b < BATCH; b++)
+        red[(wave * BATCH + b) * 64 + 2 * l + half] = lw_half_lo(dm) * acc[b] - lw_half_hi(dm) * sx[b];
     __syncthreads();
 
     lw_finish_balanced<BATCH, 64, K>(a, red);
@@ -506,7 +471,7 @@ hipError_t try_gemv_bal(const KArgs &a, hipStream_t s)
     return launch_gemv_bal<KIND, PLAN, BATCH, 3>(a, s);
 }
 
-// The balanced layout goes first where it applies (bundles in
+// At batch 1..4 the balanced layout goes first where it applies (bundles in
 // parts with 4K + 2 tiles per CU; 4096x14336: 19.2 against 20.4-20.8 us in
 // fourteen-wavefront groups).  Bundles in parts for their size (up to 2048
 // tiles) decode every recorded part in eight-wavefront workgroups (measured
@@ -523,8 +488,10 @@ template <int KIND, int PLAN, int BATCH>
 hipError_t launch_gemv_q(const KArgs &a, hipStream_t s)
 {
     const uint32_t lds = (uint32_t)lw_device_lds_bytes();
-    const hipError_t e = try_gemv_bal<KIND, PLAN, BATCH>(a, s);
-    if (e != hipErrorNotSupported) return e;
+    if constexpr (BATCH <= 4) {
+        const hipError_t e = try_gemv_bal<KIND, PLAN, BATCH>(a, s);
+        if (e != hipErrorNotSupported) return e;
+    }
     // the eight-wavefront part layouts serve the bundles the part rule puts
     // in parts for their size (tiles x parts within LW_PART_UNITS)
     const bool small = (int64_t)a.n_rb * a.n_cb * a.parts <= LW_PART_UNITS;
@@ -534,12 +501,14 @@ hipError_t launch_gemv_q(const KArgs &a, hipStream_t s)
         return launch_gemv_wpg<KIND, PLAN, BATCH, 8, 4>(a, s);
     if (small && a.parts == 8 && lds_layout(BATCH, a.max_words, false, 8, 8).total <= lds)
         return launch_gemv_wpg<KIND, PLAN, BATCH, 8, 8>(a, s);
-    if (a.n_cb > 12 && a.n_cb <= 16 && a.n_rb >= 128 && lds_layout(BATCH, a.max_words, false, 16).total <= lds)
-        return launch_gemv_wpg<KIND, PLAN, BATCH, 16>(a, s);
-    if constexpr (PLAN != LW_P_GEN) {
-        if (a.n_cb > 16 && a.n_cb % 14 == 0 && lw_resident_ramp((int64_t)a.n_rb * a.n_cb) &&
-            lds_layout(BATCH, a.max_words, false, 14).total <= lds)
-            return launch_gemv_wpg<KIND, PLAN, BATCH, 14>(a, s);
+    if constexpr (BATCH <= 4) {
+        if (a.n_cb > 12 && a.n_cb <= 16 && a.n_rb >= 128 && lds_layout(BATCH, a.max_words, false, 16).total <= lds)
+            return launch_gemv_wpg<KIND, PLAN, BATCH, 16>(a, s);
+        if constexpr (PLAN != LW_P_GEN) {
+            if (a.n_cb > 16 && a.n_cb % 14 == 0 && lw_resident_ramp((int64_t)a.n_rb * a.n_cb) &&
+                lds_layout(BATCH, a.max_words, false, 14).total <= lds)
+                return launch_gemv_wpg<KIND, PLAN, BATCH, 14>(a, s);
+        }
     }
     return launch_gemv_wpg<KIND, PLAN, BATCH, WAVES>(a, s);
 }
@@ -564,6 +533,9 @@ hipError_t gemv_batch(const KArgs &a, int batch, hipStream_t s)
     case 2: return launch_gemv_q<KIND, PLAN, 2>(a, s);
     case 3: return launch_gemv_q<KIND, PLAN, 3>(a, s);
     case 4: return launch_gemv_q<KIND, PLAN, 4>(a, s);
+    case 5: return launch_gemv_q<KIND, PLAN, 5>(a, s);
+    case 6: return launch_gemv_q<KIND, PLAN, 6>(a, s);
+    case 7: return launch_gemv_q<KIND, PLAN, 7>(a, s);
     }
     return hipErrorInvalidValue;
 }

@@ -1,11 +1,10 @@
-// mfma.hip -- fused decode + GEMM for batch 5..16 (bf16: 4..16) on the matrix cores of
+// mfma.hip -- fused decode + GEMM for batch 8..16 on the matrix cores of
 // gfx950 ("LazyWeights" bundle, decoded as in lane_decode.hpp; feeding the
 // matrix cores from on-chip data follows the reconstructive matmul idea of
 // "Unweight", section "How reconstructive matmul works").
 //
-// A lane's decoded weights are already a matrix-core operand (fused_q.hip
-// feeds them to 16x16x32 instructions at batch 1..4, four batch rows in one
-// instruction; here 32x32x16 ones take up to sixteen).  Lane l + 32*half decodes tile
+// At batch >= 8 the product is a real dense contraction, and a lane's decoded
+// weights are already a matrix-core operand.  Lane l + 32*half decodes tile
 // row 2l + half (one wavefront per part of a tile, as in fused_q.hip); after
 // one group of four symbols (4-bit pairs) or two (6-bit codes, bf16
 // exponents) it holds that row's weights at 8 consecutive columns, which is

@@ -163,11 +163,7 @@ static lw_status gemv_launch(const lw_dev_bundle *db, KArgs &a, const void *x, f
     a.batch = batch;
     hipError_t e;
     a.pal0 = db->h.kind == LW_BF16_EXP ? db->tab.payload[0] >> 7 : 0u;
-    // 32x32 matrix instructions from batch 5 (4-bit, 6-bit: below that the
-    // decode kernels' 16x16x32 ones) and from batch 4 for bf16 (whose decode
-    // kernel computes its products on the VALU: 47.1 against 46.5 us at
-    // batch 4, 43.4 against 44.3 at batch 2 on 14336x4096)
-    if (batch >= (db->h.kind == LW_BF16_EXP ? 4 : 5))
+    if (batch >= 8)                        // a real dense contraction: matrix cores
         e = lw_launch_gemv_mfma(a, db->h.kind, plan_of(db, a), batch, s);
     else if (db->h.kind == LW_BF16_EXP)
         e = lw_launch_gemv_bf16(a, plan_of(db, a), batch, s);

@@ -255,10 +255,7 @@ void lw_dev_bundle_free(lw_dev_bundle *db);
  * dequantise + dot product; HBM moves only coded bytes).
  *   x : device [batch][cols], fp16 (Q4/Q6) or bf16 (BF16) bits, 16-byte aligned
  *   y : device [batch][rows] fp32, overwritten, 16-byte aligned
- *   1 <= batch <= 16.  The products run on the matrix cores: 16x16x32
- *   instructions inside the decode kernel at batch 1..4 (4- and 6-bit
- *   codes), 32x32x16 ones in the matrix-core kernel from batch 5 (bf16:
- *   from batch 4; below that bf16 products run on the VALU).
+ *   1 <= batch <= 16; batch >= 8 uses the matrix-core (MFMA) kernel.
  * The split-column reduction uses the bundle's workspace: calls on one
  * uploaded bundle must not overlap in time (use one stream per bundle).
  * Results are deterministic: the column groups' sums meet pairwise in a

@@ -272,12 +272,17 @@ def row_split(syms: np.ndarray, spl: int, lens: np.ndarray) -> np.ndarray:
 PART_UNITS = 4096
 
 
-def default_parts(n_tiles: int) -> int:
+def default_parts(n_tiles: int, n_cb: int = 0, quantised: bool = False) -> int:
     """Parts per tile row when the caller leaves it open: the largest of 8, 4,
-    2 that keeps n_tiles * parts <= PART_UNITS, else 1."""
+    2 that keeps n_tiles * parts <= PART_UNITS, else 1; for 4- and 6-bit
+    codes 2 also where n_tiles is an odd multiple of 512 in (PART_UNITS / 2,
+    PART_UNITS] and a row band has more than 16 column blocks (n_cb)."""
     for p in (8, 4, 2):
         if n_tiles * p <= PART_UNITS:
             return p
+    if quantised and PART_UNITS // 2 < n_tiles <= PART_UNITS and n_tiles % 512 == 0 and (n_tiles // 512) % 2 == 1 \
+            and n_cb > 16:
+        return 2
     return 1
 
 
@@ -320,7 +325,7 @@ def build_bundle_q(kind: int, codes: np.ndarray, d: np.ndarray, m: np.ndarray, c
     lens = code_lengths(counts, code) if lens is None else np.ascontiguousarray(lens, dtype=np.uint8)
     tab = canonical(lens)
     tile_off, words, lane_bits = encode_tiles(syms, spl, lens, tab["codes"])
-    parts = parts or default_parts((R // 64) * (Cc // 256))
+    parts = parts or default_parts((R // 64) * (Cc // 256), Cc // 256, quantised=True)
     return dict(kind=kind, rows=R, cols=Cc, spl=spl, counts=counts, table=tab,
                 tile_off=tile_off, words=words, lane_bits=lane_bits, dm=pack_dm(d, m),
                 parts=parts, split=part_starts(syms, spl, lens, parts))

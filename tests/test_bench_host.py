@@ -11,13 +11,13 @@ import bench  # noqa: E402
 
 
 def test_kernel_source_follows_the_dispatch():
-    # 4- and 6-bit bundles: the decode kernel (16x16x32 matrix instructions)
-    # up to batch 4, the 32x32 matrix-core kernel from 5; bf16 from 4
+    # the decode kernel of the bundle's kind up to batch 7, the matrix-core
+    # kernel from batch 8
     for kind in ("q4", "q6"):
-        assert [bench.kernel_source(kind, b) for b in (1, 4, 5, 8, 16)] == \
-            ["fused_q.hip"] * 2 + ["mfma.hip"] * 3
-    assert [bench.kernel_source("bf16", b) for b in (1, 3, 4, 16)] == \
-        ["bf16.hip"] * 2 + ["mfma.hip"] * 2
+        assert [bench.kernel_source(kind, b) for b in (1, 4, 7, 8, 16)] == \
+            ["fused_q.hip"] * 3 + ["mfma.hip"] * 2
+    assert [bench.kernel_source("bf16", b) for b in (1, 4, 7, 8, 16)] == \
+        ["bf16.hip"] * 3 + ["mfma.hip"] * 2
 
 
 def test_code_text_ignores_comments_and_layout():

@@ -41,7 +41,7 @@ def _compare_q(kind, codes, d, m, code="huffman"):
     assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_WORDS, np.uint32), ob["words"])
     assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_DM, np.uint32), ob["dm"])
     assert np.array_equal(dg.lw_bundle_region(pb, dg.LW_REG_SPLIT, np.uint16), ob["split"])
-    assert info["parts"] == ob["parts"] == O.default_parts(info["n_tiles"])
+    assert info["parts"] == ob["parts"] == O.default_parts(info["n_tiles"], codes.shape[1] // 256, quantised=True)
     W = np.diff(ob["tile_off"].astype(np.int64)) // 32
     assert info["max_words"] == W.max()
     assert info["coded_bytes"] == (ob["words"].nbytes + ob["tile_off"].nbytes + ob["dm"].nbytes +

@@ -316,14 +316,14 @@ def test_full_size_bf16(torch, dg):
         assert rel_err(y, gemv_bf16_all(w, x, batch)) <= TOL
 
 
-# ------------------------------------------------------------------ batch >= 5: the 32x32 matrix-core kernel
+# ------------------------------------------------------------------ batch >= 8: matrix cores
 
 MFMA_CASES = [("q4", 64, 256, "normal", 301), ("q4", 192, 1280, "laplace", 302), ("q4", 320, 2304, "normal", 303),
               ("q6", 128, 768, "normal", 304), ("q6", 64, 2048, "uniform", 305)]
 
 
 @pytest.mark.parametrize("case", MFMA_CASES, ids=lambda c: "-".join(map(str, c)))
-@pytest.mark.parametrize("batch", [5, 8, 11, 16])
+@pytest.mark.parametrize("batch", [8, 11, 16])
 def test_gemv_mfma_small(torch, dg, case, batch):
     kind_s, rows, cols, law, seed = case
     say("mfma", case, batch)
@@ -356,9 +356,9 @@ def test_gemv_mfma_whole_rows(torch, dg, case):
 
 # balanced layout: 3584 tiles (14 per CU on 256 CUs), bundles in two parts --
 # whole tiles on twelve wavefronts of a CU and tile halves on four, each row
-# band meeting the other workgroups holding its tiles; batch 1..4 in the
-# balanced decode kernel (16x16x32 matrix instructions), and 8 and 16 on the
-# 32x32 matrix-core kernel's whole-row layouts over the same two-part bundles
+# band meeting the other workgroups holding its tiles; batch 1..4 on the
+# VALU kernel, and 8 and 16 on the matrix cores' whole-row layouts over the
+# same two-part bundles
 BALANCED = [("q4", 14336, 4096, "normal", 321), ("q4", 4096, 14336, "laplace", 322), ("q6", 4096, 14336, "normal", 323)]
 
 
@@ -388,9 +388,8 @@ PARTS_Q = [
 @pytest.mark.parametrize("case", PARTS_Q, ids=lambda c: "-".join(map(str, c)))
 def test_parts_q(torch, dg, case, parts):
     """Bundles with 1, 2, 4 and 8 recorded parts per tile row: decode-only
-    bit-exact (and per-lane bit counts), the GEMV at batch 1, 2 and 4 (the
-    decode kernel), 7 and 16 (the 32x32 matrix-core kernel) within tolerance
-    and repeatable."""
+    bit-exact (and per-lane bit counts), the VALU GEMV at batch 1, 2, 4 and 7
+    and the matrix-core GEMV at batch 16 within tolerance and repeatable."""
     kind_s, rows, cols, law, seed = case
     say("parts", case, parts)
     kind = dg.LW_Q4_PAIR if kind_s == "q4" else dg.LW_Q6_SINGLE
@@ -451,8 +450,7 @@ def test_each_comparison_plan(torch, dg, plan, pairs):
     code that takes it, over a matrix of several tiles with a ragged column
     group.  Decode-only restores every code with per-lane bit counts equal to
     the oracle's (its bundle built with the same lengths), and the fused GEMV
-    matches the oracle at batch 1 and 3 (the decode kernel's 16x16x32 matrix
-    instructions) and 16 (the 32x32 matrix-core kernel)."""
+    matches the oracle at batch 1 and 3 (VALU) and 16 (matrix cores)."""
     rng = np.random.default_rng(700 + 10 * plan + pairs)
     lens, syms = _table_for_plan(dg, plan, pairs, rng)
     kind = dg.LW_Q4_PAIR if pairs else dg.LW_Q6_SINGLE
@@ -500,7 +498,7 @@ def test_compact_code_bundles(torch, dg, case):
 
 
 @pytest.mark.parametrize("case", SMALL_BF16[:4], ids=lambda c: "-".join(map(str, c)))
-@pytest.mark.parametrize("batch", [4, 8, 16])
+@pytest.mark.parametrize("batch", [8, 16])
 def test_bf16_gemv_mfma_small(torch, dg, case, batch):
     rows, cols, frac, seed = case
     say("bf16 mfma", case, batch)

@@ -466,6 +466,12 @@ def test_default_parts_rule():
     # the largest of 8, 4, 2 that keeps tiles x parts within 4096 units, else 1
     assert [O.default_parts(n) for n in (1, 16, 512, 513, 1024, 1025, 2048, 2049, 3584, 14336)] == \
         [8, 8, 8, 4, 4, 2, 2, 1, 1, 1]
+    # 4- and 6-bit codes: 2 where the tiles are an odd multiple of 512 in
+    # (2048, 4096] and a row band has more than 16 column blocks
+    q = lambda n, cb: O.default_parts(n, cb, quantised=True)
+    assert [q(3584, 56), q(2560, 40), q(3584, 16), q(3072, 48), q(4096, 64), q(3584, 17), q(14336, 112)] == \
+        [2, 2, 1, 1, 1, 2, 1]
+    assert q(1024, 16) == 4 and O.default_parts(3584, 56) == 1      # bf16 keeps the tile-count rule
 
 
 def test_double_to_half_matches_numpy_rounding():
