@@ -368,7 +368,8 @@ LW_DEV uint32_t lw_sub_sat(uint32_t v, uint32_t k)
 }
 
 // Count the limits the window's peek has passed; returns A = lb + PBASE - 2*len
-// (compact tables: A = lb + CSEL - 2r for r limits passed).  xk holds the
+// (compact tables: A = lb + CSEL - 2r, the sparse plan: A = lb + SBASE - 2r,
+// for r limits passed).  xk holds the
 // residue plans' additive constants in vector registers (see LaneDec).
 template <int PLAN>
 LW_DEV uint32_t lw_count(uint32_t hi, uint32_t k, const uint32_t (&xk)[2], const KArgs &a)
